@@ -1,0 +1,458 @@
+"""CPU oracle for greedy tree verify.
+
+TEST INFRASTRUCTURE.  This package is the slow, plain reference that the HIP
+library is checked against.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import it; the library
+(``greedy_draft_tree_amd``) never does, and the two share no code.  The only
+common module is ``synth`` (seeded inputs, no arithmetic of the method).
+
+What it computes, and where the pages define it:
+
+* ``Oracle.step``: one token through the target model, the "one forward pass
+  per token" of plain greedy decoding ("Exactness", The promise).  The model
+  is a pre-norm decoder; its arithmetic is fp64 with bf16 (round to nearest
+  even) at the activation rounding points and an fp32 head output ("Exactness",
+  The one exception: near ties: the head returns fp32 logits).  ``exact=True``
+  drops every rounding point (used to pin the forward to an independent
+  library implementation).
+* ``Oracle.tree_scores``: the brute-force tree scorer.  Row i is the model's
+  scores after consuming the path root..i, i.e. the sequential decode of the
+  node's ancestor prefix ("Drafters and tree verify", The round, step 2;
+  "Algorithm and correctness contract", Target position and batching, which
+  indexes the same contexts by the child).
+* ``apply_modifiers`` / ``top2``: score modifiers as plain decoding applies
+  them to its one row ("Exactness", The promise; penalties before the other
+  filters, "Exactness", Sampling), then argmax (lowest id on an exact tie)
+  and the top-1/top-2 gap in bf16 ulps ("Exactness", The one exception).
+* ``accept_walk``: the greedy accept walk with the bonus token ("Drafters and
+  tree verify", The round, step 3).
+* ``Seq.commit``: the oracle's committed state is its token sequence; a
+  commit simply steps the accepted tokens one at a time ("Drafters and tree
+  verify", The round, step 4).  The closed form of the recurrent state
+  ("Drafters and tree verify", Tree verify through recurrent layers) is NOT
+  used here; tests check it against this loop.
+
+Every pin that holds this code to the pages and to the mathematics lives in
+``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from synth import ATTN, RECUR, ModelShape, Modifiers
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "_matvec.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C primitive with gcc (plain x86-64, OpenMP)."""
+    if force or not os.path.exists(_SO):
+        src = os.path.join(_HERE, "matvec.c")
+        tmp = _SO + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC",
+                               "-o", tmp, src])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build(force=True)
+        lib = ctypes.CDLL(_SO)
+        lib.orc_matvec_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+        lib.orc_matvec_bf16.restype = None
+        lib.orc_set_threads.argtypes = [ctypes.c_int]
+        lib.orc_get_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def set_threads(n: int) -> None:
+    _load().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().orc_get_threads())
+
+
+# ------------------------------------------------------------ numerics
+
+def bf16_round(x):
+    """Round fp64 values to the nearest bf16 value, ties to even.
+
+    bf16 keeps 8 significant bits and binary32's exponent range, so a finite
+    x is rounded on the grid of its quantum ``ulp_bf16(x)``.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    q = ulp_bf16(x)
+    return np.rint(x / q) * q
+
+
+def ulp_bf16(x):
+    """One bf16 step at x: 2**(floor(log2|x|) - 7), or 2**-133 below the
+    normal range (|x| < 2**-126, zero included)."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(x)              # x = m * 2**e with m in [0.5, 1)
+    e = np.where(x < 2.0 ** -126, -126, e - 1)
+    return np.ldexp(1.0, e - 7)
+
+
+def log_sigmoid(a):
+    return -np.logaddexp(0.0, -np.asarray(a, dtype=np.float64))
+
+
+def f32(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def bf16_bits_to_f64(u16: np.ndarray) -> np.ndarray:
+    return (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def t2u16(t: torch.Tensor) -> np.ndarray:
+    """bf16 torch tensor (CPU) -> uint16 numpy view of its bits."""
+    assert t.dtype == torch.bfloat16
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def t2f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+# ------------------------------------------------------------ the model
+
+class Oracle:
+    """The target model of a ``synth.ModelShape`` on given bf16 weights.
+
+    Weights are the spec's: every matrix is [N_out, K_in] row-major bf16;
+    a layer's ``wqkv`` stacks q heads, then k heads, then v heads.
+    """
+
+    def __init__(self, shape: ModelShape, weights: Dict[str, torch.Tensor], exact: bool = False):
+        self.s = shape
+        self.exact = exact
+        self.W = {k: t2u16(v) for k, v in weights.items()}
+        for name, arr in self.W.items():
+            assert arr.flags["C_CONTIGUOUS"], name
+        self.lib = _load()
+        D = shape.head_dim
+        # RoPE frequencies, rotate-half pairing (i, i + D/2), fp64.
+        self.inv_freq = shape.rope_theta ** (-(2.0 * np.arange(D // 2)) / D)
+
+    # rounding point: bf16 unless exact
+    def r(self, x):
+        return np.asarray(x, dtype=np.float64) if self.exact else bf16_round(x)
+
+    def matvec(self, name: str, x: np.ndarray) -> np.ndarray:
+        W = self.W[name]
+        N, K = W.shape
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        assert x.shape == (K,)
+        y = np.empty(N, dtype=np.float64)
+        self.lib.orc_matvec_bf16(W.ctypes.data, N, K, x.ctypes.data, y.ctypes.data)
+        return y
+
+    def rmsnorm(self, x: np.ndarray, wname: str) -> np.ndarray:
+        w = bf16_bits_to_f64(self.W[wname])
+        return x / math.sqrt(float(np.mean(x * x)) + self.s.eps) * w
+
+    def rope(self, x: np.ndarray, pos: int) -> np.ndarray:
+        """Rotate each head [h, D] by angle pos*inv_freq[i] on pairs (i, i+D/2)."""
+        half = self.s.head_dim // 2
+        ang = pos * self.inv_freq
+        c, s = np.cos(ang), np.sin(ang)
+        a, b = x[:, :half], x[:, half:]
+        return np.concatenate([a * c - b * s, b * c + a * s], axis=1)
+
+    def attention(self, q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+        """q [QH, D]; K, V [KVH, L, D]; grouped heads; scaled dot product,
+        softmax with max subtraction."""
+        QH, D = q.shape
+        grp = QH // K.shape[0]
+        out = np.empty_like(q)
+        for h in range(QH):
+            kv = h // grp
+            sc = K[kv] @ q[h] / math.sqrt(D)
+            p = np.exp(sc - sc.max())
+            out[h] = (p / p.sum()) @ V[kv]
+        return out
+
+    @staticmethod
+    def recur_mix(q, k, v, g, S_prev):
+        """Gated linear recurrence, one token, every head at once:
+        S = exp(g) * S_prev + k v^T, read out o = S^T q.
+        q, k, v [QH, D]; g [QH] (log of the decay); S [QH, D(k), D(v)]."""
+        S = np.exp(g)[:, None, None] * S_prev + k[:, :, None] * v[:, None, :]
+        o = np.einsum("hkv,hk->hv", S, q)
+        return o, S
+
+    def l2norm(self, x: np.ndarray) -> np.ndarray:
+        return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + self.s.eps)
+
+    def step(self, token: int, pos: int, prefix: Dict[int, Tuple[np.ndarray, np.ndarray]],
+             states: Dict[int, np.ndarray]):
+        """One token at position ``pos``.
+
+        ``prefix[l]`` is (K, V) [KVH, L, D] of every earlier position of this
+        path at attention layer l; ``states[l]`` is the recurrent state
+        [QH, D, D] before this token at recurrent layer l.  Returns
+        (logits [V], rows {l: (k, v)}, new_states {l: S}).
+        """
+        s = self.s
+        r = self.r
+        QH, KVH, D = s.n_qhead, s.n_kvhead, s.head_dim
+        x = bf16_bits_to_f64(self.W["emb"][token])
+        rows, new_states = {}, {}
+        for l, kind in enumerate(s.kinds):
+            p = f"layers.{l}."
+            xn = r(self.rmsnorm(x, p + "attn_norm"))
+            if kind == ATTN:
+                qkv = r(self.matvec(p + "wqkv", xn))
+                q = qkv[:QH * D].reshape(QH, D)
+                k = qkv[QH * D:(QH + KVH) * D].reshape(KVH, D)
+                v = qkv[(QH + KVH) * D:].reshape(KVH, D)
+                q = r(self.rope(q, pos))
+                k = r(self.rope(k, pos))
+                Kp, Vp = prefix[l]
+                Ka = np.concatenate([Kp, k[:, None, :]], axis=1)
+                Va = np.concatenate([Vp, v[:, None, :]], axis=1)
+                o = r(self.attention(q, Ka, Va).reshape(-1))
+                rows[l] = (k, v)
+            else:
+                qkv = r(self.matvec(p + "wqkv", xn))
+                q = r(self.l2norm(qkv[:QH * D].reshape(QH, D)))
+                k = r(self.l2norm(qkv[QH * D:2 * QH * D].reshape(QH, D)))
+                v = qkv[2 * QH * D:].reshape(QH, D)
+                a = r(self.matvec(p + "wa", xn))
+                o, S = self.recur_mix(q, k, v, log_sigmoid(a), states[l])
+                o = r(o.reshape(-1))
+                # the state is held in fp32 between tokens
+                new_states[l] = S if self.exact else f32(S)
+            x = r(x + r(self.matvec(p + "wo", o)))
+            hn = r(self.rmsnorm(x, p + "ffn_norm"))
+            gt = r(self.matvec(p + "wg", hn))
+            u = r(self.matvec(p + "wu", hn))
+            act = r(gt / (1.0 + np.exp(-gt)) * u)     # silu(g) * u
+            x = r(x + r(self.matvec(p + "wd", act)))
+        xf = r(self.rmsnorm(x, "final_norm"))
+        logits = self.matvec("head", xf)
+        if not self.exact:
+            logits = f32(logits)
+        return logits, rows, new_states
+
+    # -------------------------------------------------------- sequences
+
+    def new_seq(self, cap: int, history: Optional[Sequence[int]] = None,
+                kv: Optional[dict] = None, ctx_len: int = 0,
+                s0: Optional[dict] = None) -> "Seq":
+        return Seq(self, cap, history, kv, ctx_len, s0)
+
+    def tree_scores(self, seq: "Seq", parents: Sequence[int], tokens: Sequence[int],
+                    rows_wanted: Optional[Sequence[int]] = None) -> np.ndarray:
+        """Brute-force scorer: logits [n, V] of every node, each the step of
+        the node's token after the committed sequence and its ancestors.
+
+        Nodes are visited in index order (parents come first); a node's KV
+        rows and recurrent state are kept for its descendants.  With
+        ``rows_wanted`` only those nodes and their ancestors are stepped
+        (other rows are NaN).
+        """
+        n = len(parents)
+        parents = [int(p) for p in parents]
+        need = set(range(n)) if rows_wanted is None else set()
+        if rows_wanted is not None:
+            for i in rows_wanted:
+                j = int(i)
+                while j >= 0:
+                    need.add(j)
+                    j = parents[j]
+        depth = [0] * n
+        node_rows: List[Optional[dict]] = [None] * n
+        node_state: List[Optional[dict]] = [None] * n
+        out = np.full((n, self.s.vocab), np.nan)
+        for i in range(n):
+            if i > 0:
+                if not (0 <= parents[i] < i):
+                    raise ValueError("parents must precede children")
+                depth[i] = depth[parents[i]] + 1
+            if i not in need:
+                continue
+            anc = []
+            j = parents[i]
+            while j >= 0:
+                anc.append(j)
+                j = parents[j]
+            anc.reverse()
+            prefix = {}
+            for l, kind in enumerate(self.s.kinds):
+                if kind != ATTN:
+                    continue
+                K0, V0 = seq.K[l][:, :seq.ctx_len], seq.V[l][:, :seq.ctx_len]
+                if anc:
+                    Kt = np.stack([node_rows[a][l][0] for a in anc], axis=1)
+                    Vt = np.stack([node_rows[a][l][1] for a in anc], axis=1)
+                    K0 = np.concatenate([K0, Kt], axis=1)
+                    V0 = np.concatenate([V0, Vt], axis=1)
+                prefix[l] = (K0, V0)
+            st = seq.S if parents[i] < 0 else node_state[parents[i]]
+            logits, rows, new_st = self.step(int(tokens[i]), seq.ctx_len + depth[i], prefix, st)
+            out[i] = logits
+            node_rows[i] = rows
+            node_state[i] = new_st
+        return out
+
+
+class Seq:
+    """Committed state of one request: its KV rows, recurrent states and
+    token history (prompt and every committed token)."""
+
+    def __init__(self, model: Oracle, cap: int, history=None, kv=None, ctx_len=0, s0=None):
+        s = model.s
+        self.m = model
+        self.cap = cap
+        self.ctx_len = ctx_len
+        self.history: List[int] = [] if history is None else [int(t) for t in history]
+        self.K, self.V, self.S = {}, {}, {}
+        for l, kind in enumerate(s.kinds):
+            if kind == ATTN:
+                K = np.zeros((s.n_kvhead, cap, s.head_dim))
+                V = np.zeros((s.n_kvhead, cap, s.head_dim))
+                if kv is not None and ctx_len > 0:
+                    K[:, :ctx_len] = t2f64(kv[(l, "k")][:, :ctx_len])
+                    V[:, :ctx_len] = t2f64(kv[(l, "v")][:, :ctx_len])
+                self.K[l], self.V[l] = K, V
+            else:
+                if s0 is not None:
+                    self.S[l] = t2f64(s0[l])
+                else:
+                    self.S[l] = np.zeros((s.n_qhead, s.head_dim, s.head_dim))
+
+    def step(self, token: int) -> np.ndarray:
+        """Append one token: its KV rows and states become committed."""
+        if self.ctx_len >= self.cap:
+            raise ValueError("sequence capacity exceeded")
+        prefix = {l: (self.K[l][:, :self.ctx_len], self.V[l][:, :self.ctx_len]) for l in self.K}
+        logits, rows, new_st = self.m.step(int(token), self.ctx_len, prefix, self.S)
+        for l in self.K:
+            self.K[l][:, self.ctx_len] = rows[l][0]
+            self.V[l][:, self.ctx_len] = rows[l][1]
+        self.S.update(new_st)
+        self.ctx_len += 1
+        self.history.append(int(token))
+        return logits
+
+    def commit(self, tokens: Sequence[int]) -> Optional[np.ndarray]:
+        last = None
+        for t in tokens:
+            last = self.step(t)
+        return last
+
+
+# ------------------------------------------------------------ scores
+
+def apply_modifiers(logits: np.ndarray, prior: Sequence[int], mods: Optional[Modifiers]) -> np.ndarray:
+    """Modified fp32 scores of one row: repetition penalty over ``prior``
+    (l/theta for l>0, else l*theta), then logit_bias, then the allow-mask
+    (disallowed ids score -inf).  fp32 arithmetic, as the decision is taken
+    on the fp32 logits."""
+    s = np.asarray(logits, dtype=np.float64).astype(np.float32)
+    if mods is None:
+        return s
+    th = np.float32(mods.rep_penalty)
+    if mods.rep_penalty != 1.0 and len(prior):
+        ids = np.unique(np.asarray(prior, dtype=np.int64))
+        v = s[ids]
+        s[ids] = np.where(v > 0, v / th, v * th).astype(np.float32)
+    if len(mods.bias_ids):
+        s[mods.bias_ids] = (s[mods.bias_ids] + mods.bias_vals.astype(np.float32)).astype(np.float32)
+    if mods.allow_bits is not None:
+        ids = np.arange(s.shape[0])
+        allowed = (mods.allow_bits[ids // 32] >> (ids % 32).astype(np.uint32)) & 1
+        s[allowed == 0] = np.float32(-np.inf)
+    return s
+
+
+def top2(scores: np.ndarray) -> Tuple[int, float, float, float]:
+    """(argmax, top-1, top-2, gap in bf16 ulps of top-1).  The argmax is the
+    lowest id among equal maxima; top-2 is the best score among the other
+    ids (equal to top-1 on an exact tie)."""
+    s = np.asarray(scores, dtype=np.float64)
+    a = int(np.argmax(s))
+    l1 = float(s[a])
+    rest = np.concatenate([s[:a], s[a + 1:]])
+    l2 = float(rest.max()) if rest.size else -np.inf
+    if l2 == -np.inf:
+        gap = np.inf
+    else:
+        gap = (l1 - l2) / float(ulp_bf16(l1))
+    return a, l1, l2, gap
+
+
+def path_tokens(parents: Sequence[int], tokens: Sequence[int], i: int) -> List[int]:
+    out = []
+    while i >= 0:
+        out.append(int(tokens[i]))
+        i = int(parents[i])
+    return out[::-1]
+
+
+def tree_decisions(logits: np.ndarray, parents, tokens, history: Sequence[int],
+                   mods: Optional[Modifiers] = None):
+    """Per-row (argmax, gap) on modified scores; a row's prior tokens are
+    the history plus its path root..node."""
+    n = len(parents)
+    am = np.zeros(n, dtype=np.int32)
+    gap = np.zeros(n)
+    for i in range(n):
+        prior = list(history) + path_tokens(parents, tokens, i)
+        a, _, _, g = top2(apply_modifiers(logits[i], prior, mods))
+        am[i], gap[i] = a, g
+    return am, gap
+
+
+def accept_walk(parents: Sequence[int], tokens: Sequence[int], argmax: Sequence[int]):
+    """From the root, take the model's token and move to the child that
+    carries it; stop where none does and keep the model's token there.
+    Returns (path node indices, emitted tokens); len(emitted) == len(path)."""
+    n = len(parents)
+    kids: List[List[int]] = [[] for _ in range(n)]
+    for i in range(1, n):
+        kids[int(parents[i])].append(i)
+    cur = 0
+    path, emitted = [0], []
+    while True:
+        g = int(argmax[cur])
+        emitted.append(g)
+        nxt = [c for c in kids[cur] if int(tokens[c]) == g]
+        if not nxt:
+            break
+        cur = nxt[0]
+        path.append(cur)
+    return path, emitted
+
+
+def greedy(seq: Seq, first: int, k: int, mods: Optional[Modifiers] = None):
+    """Plain greedy decoding: feed ``first``, then k-1 argmax tokens.
+    Returns (tokens emitted [k], gaps [k]); ``seq`` ends having consumed
+    ``first`` and the first k-1 emitted tokens."""
+    out, gaps = [], []
+    t = first
+    for i in range(k):
+        logits = seq.step(t)
+        a, _, _, g = top2(apply_modifiers(logits, seq.history, mods))
+        out.append(a)
+        gaps.append(g)
+        t = a
+    return out, gaps
