@@ -1,0 +1,95 @@
+// Internal interface between the host runtime (tv_runtime.cpp) and the gfx950
+// kernels (tv_kernels.hip).  Not part of the public C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tv {
+
+constexpr int kMaxRows = 32;   // rows of one pass
+constexpr int kMaxGroup = 8;   // query heads per KV head
+constexpr int kAttnSplit = 256; // cache keys per attention workgroup
+constexpr int kAttnChunk = 64;  // keys staged in LDS at a time
+
+// Candidate pair of a top-2 search: best (v1, i1) and runner-up (v2, i2),
+// ordered by value, then by lower token id.
+struct Top2 {
+    float v1;
+    int i1;
+    float v2;
+    int i2;
+};
+
+// Score modifiers of one request of the pass (device arrays or null).
+struct HeadMods {
+    const uint32_t *hist_bits;  // [ceil(V/32)] prior tokens (history + committed)
+    const float *bias;          // [V] dense logit_bias (0 where none)
+    const uint32_t *allow_bits; // [ceil(V/32)] allowed ids
+    float rep;                  // repetition penalty (1 = off)
+    int pad[3];
+};
+
+// Per-pass metadata, copied to the device once per verify.
+struct PassMeta {
+    int tok[kMaxRows];
+    int depth[kMaxRows];
+    uint32_t anc[kMaxRows];      // ancestor-or-self bits, request-local indices
+    int row_req[kMaxRows];       // request slot of each row
+    int path_len[kMaxRows];      // tokens on root..row
+    int path_tok[kMaxRows * kMaxRows];
+    HeadMods mods[kMaxRows];     // per request slot
+};
+
+enum Epi { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3 };
+
+struct GemmArgs {
+    const uint16_t *X;  // [M, K] bf16 activations, row stride ldx
+    int ldx;
+    const uint16_t *W;  // [N, K] bf16 weights
+    const uint16_t *W2; // [N, K] second weights (SwiGLU up)
+    int M, N, K;
+    uint16_t *Y;        // bf16 out (or residual in/out), row stride ldy
+    int ldy;
+    float *Yf;          // fp32 out (head), row stride ldyf
+    int ldyf;
+    Top2 *part;         // head: [ceil(N/32)][32] per-tile candidates
+    const PassMeta *meta; // head modifiers (null: none)
+    int mods_on;
+};
+
+struct AttnArgs {
+    const uint16_t *Q;  // rotated queries, rows row0.., [rows, n_qhead*D]
+    const uint16_t *Kc; // cache [n_kvhead][cap][D]
+    const uint16_t *Vc;
+    const PassMeta *meta;
+    float *po;          // partials [n_kvhead][ns][kMaxRows*kMaxGroup][D]
+    float *pm;          // [n_kvhead][ns][kMaxRows*kMaxGroup]
+    float *pl;
+    int row0, n, ctx, cap, G, n_qhead, ns, n_ctx_split;
+    float scale;
+};
+
+struct RopeArgs {
+    const uint16_t *qkv; // [rows, (QH+2KVH)*D]
+    uint16_t *q_out;     // [rows, QH*D]
+    uint16_t *Kc, *Vc;   // cache [KVH][cap][D]
+    const float *cosT, *sinT; // [max_pos][D/2]
+    const PassMeta *meta;
+    int row0, n, ctx, cap, QH, KVH, D;
+};
+
+// launch wrappers (tv_kernels.hip); each returns hipGetLastError()
+hipError_t launch_embed(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H,
+                        uint16_t *X);
+hipError_t launch_rmsnorm(hipStream_t s, const uint16_t *X, const uint16_t *w, int M, int H,
+                          float eps, uint16_t *Y);
+hipError_t launch_gemm(hipStream_t s, int epi, const GemmArgs &a);
+hipError_t launch_rope_kv(hipStream_t s, const RopeArgs &a);
+hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a);
+hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t *out);
+hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M, int32_t *argmax,
+                              float *gap, float *top);
+hipError_t launch_commit_kv(hipStream_t s, uint16_t *const *kv_ptrs, int n_layers, int KVH,
+                            int cap, int D, int ctx, const int *path, int path_len);
+
+} // namespace tv

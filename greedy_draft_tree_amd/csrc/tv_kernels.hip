@@ -1,0 +1,623 @@
+// gfx950 kernels of the tree-verify pass.
+//
+// Numerics of the target model (the same readings the CPU oracle takes, in
+// its own code): bf16 storage of weights, activations and KV; fp32
+// accumulation; bf16 round-to-nearest-even after every projection but the
+// head, after each residual add, after RMSNorm, after RoPE and after SwiGLU;
+// the head accumulates and returns fp32 ("Exactness", The one exception:
+// near ties: the head returns fp32 logits and every matrix-product kernel
+// fixes its reduction order by the weight's shape, never by the row count).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "tv_internal.h"
+
+namespace tv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bfround(float f) { return bf2f(f2bf(f)); }
+
+__device__ __forceinline__ bf16x8 as_bf8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(a), as_bf8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// Row index inside a 32x32 MFMA output tile held by accumulator r of a lane
+// in half `hf` (lanes 0-31: hf 0, lanes 32-63: hf 1); the column is lane%32.
+__device__ __forceinline__ int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
+
+// Strict order of top-2 candidates: higher value, then lower id.
+__device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
+    return a > b || (a == b && ia < ib);
+}
+
+__device__ __forceinline__ void top2_insert(float &v1, int &i1, float &v2, int &i2, float s, int id) {
+    if (better(s, id, v1, i1)) {
+        v2 = v1; i2 = i1; v1 = s; i1 = id;
+    } else if (better(s, id, v2, i2)) {
+        v2 = s; i2 = id;
+    }
+}
+
+__device__ __forceinline__ void top2_merge(float &v1, int &i1, float &v2, int &i2, float w1, int j1,
+                                           float w2, int j2) {
+    if (better(w1, j1, v1, i1)) {
+        if (better(v1, i1, w2, j2)) { v2 = v1; i2 = i1; } else { v2 = w2; i2 = j2; }
+        v1 = w1; i1 = j1;
+    } else if (better(w1, j1, v2, i2)) {
+        v2 = w1; i2 = j1;
+    }
+}
+
+// ------------------------------------------------------------------ embed
+
+__global__ __launch_bounds__(256) void k_embed(const uint16_t *__restrict__ emb,
+                                               const PassMeta *__restrict__ meta, int H,
+                                               uint16_t *__restrict__ X) {
+    const int m = blockIdx.x;
+    const uint16_t *src = emb + (size_t)meta->tok[m] * H;
+    uint16_t *dst = X + (size_t)m * H;
+    for (int k = threadIdx.x * 8; k < H; k += 256 * 8)
+        *reinterpret_cast<uint4 *>(dst + k) = ld16(src + k);
+}
+
+// ---------------------------------------------------------------- rmsnorm
+// y = bf16(x / sqrt(mean(x^2) + eps) * w), one workgroup per row; the sum of
+// squares is reduced in a fixed order.
+
+__global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t *__restrict__ X,
+                                                 const uint16_t *__restrict__ w, int H, float eps,
+                                                 uint16_t *__restrict__ Y) {
+    __shared__ float red[256];
+    const int m = blockIdx.x, t = threadIdx.x;
+    const uint16_t *x = X + (size_t)m * H;
+    float ss = 0.f;
+    for (int k = t; k < H; k += 256) {
+        float v = bf2f(x[k]);
+        ss += v * v;
+    }
+    red[t] = ss;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (t < o) red[t] += red[t + o];
+        __syncthreads();
+    }
+    const float scale = 1.0f / sqrtf(red[0] / (float)H + eps);
+    uint16_t *y = Y + (size_t)m * H;
+    for (int k = t; k < H; k += 256) y[k] = f2bf(bf2f(x[k]) * scale * bf2f(w[k]));
+}
+
+// ------------------------------------------------------------ skinny GEMM
+// Y[m, n] = sum_k X[m, k] W[n, k] for M <= 32 activation rows.
+//
+// One workgroup owns a 32-row tile of W and splits K between its WK waves;
+// each wave streams its weight rows with 16-byte loads and feeds
+// v_mfma_f32_32x32x16_bf16 with weights as the A operand (row = lane%32) and
+// activations as B (column = lane%32, zero beyond M).  A lane covers 32
+// consecutive k of its row per 64-wide step (two lanes read one 128-byte
+// line), which fixes the k order of every output by K alone: M only decides
+// which B columns are zero, so a row's result does not depend on how many
+// other rows share the pass, nor on its column slot.  The WK partial tiles
+// are summed in wave order through LDS.
+template <int EPI, int WK>
+__global__ __launch_bounds__(64 * WK) void k_gemm(GemmArgs g) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    constexpr int U = DUAL ? 2 : 4;   // 64-wide k steps loaded per burst
+    constexpr int NACC = DUAL ? 2 : 1;
+    __shared__ float red[(WK > 1 ? WK - 1 : 1) * NACC * 16 * 64];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hf = lane >> 5, c = lane & 31;
+    const int tile = blockIdx.x;
+    const int row = tile * 32 + c;
+    const int K = g.K;
+    const int nsteps = (K + 63) >> 6;
+    const int s0 = (nsteps * wave) / WK, s1 = (nsteps * (wave + 1)) / WK;
+    const bool rok = row < g.N;
+    const bool cok = c < g.M;
+    const uint16_t *wr = g.W + (size_t)(rok ? row : 0) * K;
+    const uint16_t *wr2 = DUAL ? g.W2 + (size_t)(rok ? row : 0) * K : nullptr;
+    const uint16_t *xr = g.X + (size_t)(cok ? c : 0) * g.ldx;
+    const uint4 z = {0u, 0u, 0u, 0u};
+
+    f32x16 acc = {}, acc2 = {};
+    for (int s = s0; s < s1; s += U) {
+        uint4 a[U][4], b[U][4], a2[DUAL ? U : 1][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k0 = (s + u) * 64 + hf * 32;
+            const bool sok = (s + u) < s1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k = k0 + q * 8;
+                const bool kok = sok && k < K;
+                a[u][q] = (kok && rok) ? ld16(wr + k) : z;
+                b[u][q] = (kok && cok) ? ld16(xr + k) : z;
+                if constexpr (DUAL) a2[u][q] = (kok && rok) ? ld16(wr2 + k) : z;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc = mfma32(a[u][q], b[u][q], acc);
+                if constexpr (DUAL) acc2 = mfma32(a2[u][q], b[u][q], acc2);
+            }
+        }
+    }
+
+    if constexpr (WK > 1) {
+        if (wave > 0) {
+            float *dst = red + (size_t)(wave - 1) * NACC * 16 * 64;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dst[r * 64 + lane] = acc[r];
+            if constexpr (DUAL) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dst[(16 + r) * 64 + lane] = acc2[r];
+            }
+        }
+        __syncthreads();
+        if (wave != 0) return;
+        for (int w = 1; w < WK; ++w) {
+            const float *src = red + (size_t)(w - 1) * NACC * 16 * 64;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] += src[r * 64 + lane];
+            if constexpr (DUAL) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc2[r] += src[(16 + r) * 64 + lane];
+            }
+        }
+    }
+
+    const int m = c;
+    if constexpr (EPI == EPI_HEAD) {
+        float v1 = -INFINITY, v2 = -INFINITY;
+        int i1 = 0x7fffffff, i2 = 0x7fffffff;
+        const bool mods = g.mods_on && cok;
+        const HeadMods *md = mods ? &g.meta->mods[g.meta->row_req[m]] : nullptr;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int n = tile * 32 + acc_row(r, hf);
+            if (!cok || n >= g.N) continue;
+            float s = acc[r];
+            g.Yf[(size_t)m * g.ldyf + n] = s;
+            if (mods) {
+                if (md->rep != 1.0f) {
+                    bool prior = md->hist_bits && ((md->hist_bits[n >> 5] >> (n & 31)) & 1u);
+                    const int L = g.meta->path_len[m];
+                    const int *pt = g.meta->path_tok + m * kMaxRows;
+                    for (int j = 0; j < L && !prior; ++j) prior = (pt[j] == n);
+                    if (prior) s = s > 0.f ? s / md->rep : s * md->rep;
+                }
+                if (md->bias) s = s + md->bias[n];
+                if (md->allow_bits && !((md->allow_bits[n >> 5] >> (n & 31)) & 1u)) s = -INFINITY;
+            }
+            top2_insert(v1, i1, v2, i2, s, n);
+        }
+        const float w1 = __shfl_xor(v1, 32), w2 = __shfl_xor(v2, 32);
+        const int j1 = __shfl_xor(i1, 32), j2 = __shfl_xor(i2, 32);
+        top2_merge(v1, i1, v2, i2, w1, j1, w2, j2);
+        if (hf == 0) g.part[(size_t)tile * 32 + m] = Top2{v1, i1, v2, i2};
+    } else {
+        if (!cok) return;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int n = tile * 32 + acc_row(r, hf);
+            if (n >= g.N) continue;
+            uint16_t *y = g.Y + (size_t)m * g.ldy + n;
+            if constexpr (EPI == EPI_BF16) {
+                *y = f2bf(acc[r]);
+            } else if constexpr (EPI == EPI_RESID) {
+                *y = f2bf(bf2f(*y) + bfround(acc[r]));
+            } else {
+                const float gt = bfround(acc[r]), up = bfround(acc2[r]);
+                *y = f2bf(gt / (1.0f + expf(-gt)) * up);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- top-2 reduce
+// One workgroup per row merges the per-tile candidates; the result is a
+// selection under a strict order, so it does not depend on the merge order.
+
+__global__ __launch_bounds__(256) void k_top2_reduce(const Top2 *__restrict__ part, int ntiles,
+                                                     int32_t *__restrict__ argmax,
+                                                     float *__restrict__ gap,
+                                                     float *__restrict__ top) {
+    __shared__ Top2 sh[256];
+    const int m = blockIdx.x, t = threadIdx.x;
+    float v1 = -INFINITY, v2 = -INFINITY;
+    int i1 = 0x7fffffff, i2 = 0x7fffffff;
+    for (int i = t; i < ntiles; i += 256) {
+        const Top2 p = part[(size_t)i * 32 + m];
+        top2_merge(v1, i1, v2, i2, p.v1, p.i1, p.v2, p.i2);
+    }
+    sh[t] = Top2{v1, i1, v2, i2};
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (t < o) {
+            Top2 a = sh[t];
+            const Top2 b = sh[t + o];
+            top2_merge(a.v1, a.i1, a.v2, a.i2, b.v1, b.i1, b.v2, b.i2);
+            sh[t] = a;
+        }
+        __syncthreads();
+    }
+    if (t == 0) {
+        const Top2 r = sh[0];
+        argmax[m] = r.i1;
+        // gap in bf16 ulps of top-1: ulp(x) = 2^(floor(log2|x|) - 7), or
+        // 2^-133 below the normal range; the difference of two fp32 values
+        // is exact in fp64.
+        float g;
+        if (r.v2 == -INFINITY) {
+            g = INFINITY;
+        } else {
+            const uint32_t e = (__float_as_uint(r.v1) >> 23) & 0xffu;
+            const int ex = (e == 0) ? -126 : (int)e - 127;
+            g = (float)(((double)r.v1 - (double)r.v2) / ldexp(1.0, ex - 7));
+        }
+        gap[m] = g;
+        top[2 * m] = r.v1;
+        top[2 * m + 1] = r.v2;
+    }
+}
+
+// ------------------------------------------------------------- RoPE + KV
+// Rotate q and k of each tree node at position ctx + depth (rotate-half
+// pairs (i, i + D/2)); k and v go to cache slot ctx + node index ("Drafters
+// and tree verify", Tree verify through recurrent layers: position = depth,
+// every node at its depth-first slot).
+
+__global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
+    const int i = blockIdx.x;
+    const int m = a.row0 + i;
+    const int D = a.D, half = D / 2;
+    const int pos = a.ctx + a.meta->depth[m];
+    const uint16_t *row = a.qkv + (size_t)m * (a.QH + 2 * a.KVH) * D;
+    const float *cs = a.cosT + (size_t)pos * half;
+    const float *sn = a.sinT + (size_t)pos * half;
+    for (int idx = threadIdx.x; idx < a.QH * half; idx += 256) {
+        const int h = idx / half, p = idx % half;
+        const float x0 = bf2f(row[h * D + p]), x1 = bf2f(row[h * D + p + half]);
+        uint16_t *o = a.q_out + (size_t)m * a.QH * D + h * D;
+        o[p] = f2bf(x0 * cs[p] - x1 * sn[p]);
+        o[p + half] = f2bf(x1 * cs[p] + x0 * sn[p]);
+    }
+    const uint16_t *kr = row + a.QH * D;
+    const uint16_t *vr = kr + a.KVH * D;
+    const size_t slot = (size_t)(a.ctx + i);
+    for (int idx = threadIdx.x; idx < a.KVH * half; idx += 256) {
+        const int h = idx / half, p = idx % half;
+        const float x0 = bf2f(kr[h * D + p]), x1 = bf2f(kr[h * D + p + half]);
+        uint16_t *o = a.Kc + ((size_t)h * a.cap + slot) * D;
+        o[p] = f2bf(x0 * cs[p] - x1 * sn[p]);
+        o[p + half] = f2bf(x1 * cs[p] + x0 * sn[p]);
+    }
+    for (int idx = threadIdx.x; idx < a.KVH * D; idx += 256) {
+        const int h = idx / D, d = idx % D;
+        a.Vc[((size_t)h * a.cap + slot) * D + d] = vr[h * D + d];
+    }
+}
+
+// ---------------------------------------------------------- tree attention
+// Grid (split, kv head).  Rows of a workgroup are the G query heads of its
+// KV head for every tree node: row r = node*G + head-in-group.  Splits
+// 0..n_ctx_split-1 each take kAttnSplit cache keys (all visible); the last
+// split takes the tree's own keys at slots ctx..ctx+n-1, key j visible to
+// node t iff j is t or an ancestor of t ("Drafters and tree verify", Tree
+// verify through recurrent layers: an attention mask of its ancestors).
+// Keys are staged in LDS 64 at a time; scores and P.V run on MFMA with an
+// online softmax per row in fp32.  P is split into bf16 high and low parts
+// (two MFMAs) so P.V keeps ~16 bits of P.  Each workgroup writes its
+// unnormalised partial (max, sum, output); the combine kernel merges splits
+// in index order.  Split boundaries depend only on ctx, so a row's result
+// does not depend on the other rows of the pass.
+
+template <int D>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+    constexpr int RMAX = 160;          // rows staged: G*n <= 160 (host checks G <= 5)
+    constexpr int CH = kAttnChunk;
+    constexpr int SSTR = CH + 4;       // fp32 stride of the score rows
+    constexpr int VSTR = CH + 8;       // bf16 stride of transposed V rows
+    constexpr int DB = D / 32;         // output column blocks
+    __shared__ __attribute__((aligned(16))) uint16_t Qs[RMAX * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[CH * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
+    __shared__ __attribute__((aligned(16))) float Ss[RMAX * SSTR];
+    __shared__ float mrow[RMAX], lrow[RMAX], arow[RMAX];
+
+    const int split = blockIdx.x, kvh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hf = lane >> 5, c = lane & 31;
+    const int G = a.G, n = a.n;
+    const int R = G * n;
+    const int RB = (R + 31) >> 5;
+    const bool tree = split >= a.n_ctx_split;
+    const int key0 = tree ? a.ctx : split * kAttnSplit;
+    const int nkeys = tree ? n : min(kAttnSplit, a.ctx - key0);
+    const int ldq = a.n_qhead * D;
+    const PassMeta *meta = a.meta;
+
+    // stage the queries of this KV head
+    for (int idx = tid; idx < RB * 32 * (D / 8); idx += 256) {
+        const int r = idx / (D / 8), p = idx % (D / 8);
+        uint4 v = {0u, 0u, 0u, 0u};
+        if (r < R) {
+            const int t = r / G, hh = r % G;
+            v = ld16(a.Q + (size_t)(a.row0 + t) * ldq + (size_t)(kvh * G + hh) * D + p * 8);
+        }
+        *reinterpret_cast<uint4 *>(Qs + r * D + p * 8) = v;
+    }
+    for (int r = tid; r < RMAX; r += 256) {
+        mrow[r] = -INFINITY;
+        lrow[r] = 0.f;
+    }
+
+    f32x16 o[2][DB];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int d = 0; d < DB; ++d) o[b][d] = (f32x16){};
+
+    const uint16_t *Kbase = a.Kc + (size_t)kvh * a.cap * D;
+    const uint16_t *Vbase = a.Vc + (size_t)kvh * a.cap * D;
+
+    for (int c0 = 0; c0 < nkeys; c0 += CH) {
+        const int cn = min(CH, nkeys - c0);
+        __syncthreads();
+        for (int idx = tid; idx < CH * (D / 8); idx += 256) {
+            const int kk = idx / (D / 8), p = idx % (D / 8);
+            uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+            if (kk < cn) {
+                const size_t off = (size_t)(key0 + c0 + kk) * D + p * 8;
+                kv = ld16(Kbase + off);
+                vv = ld16(Vbase + off);
+            }
+            *reinterpret_cast<uint4 *>(Ks + kk * D + p * 8) = kv;
+            const uint16_t *ve = reinterpret_cast<const uint16_t *>(&vv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Vt[(p * 8 + e) * VSTR + kk] = ve[e];
+        }
+        __syncthreads();
+
+        // scores of the row blocks this wave owns
+        for (int rb = wave; rb < RB; rb += 4) {
+#pragma unroll
+            for (int kb = 0; kb < CH / 32; ++kb) {
+                f32x16 s = {};
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    const uint4 qa = *reinterpret_cast<const uint4 *>(Qs + (rb * 32 + c) * D + kk * 16 + hf * 8);
+                    const uint4 kb4 = *reinterpret_cast<const uint4 *>(Ks + (kb * 32 + c) * D + kk * 16 + hf * 8);
+                    s = mfma32(qa, kb4, s);
+                }
+                const int j = kb * 32 + c;   // key within the chunk
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = rb * 32 + acc_row(r, hf);
+                    bool vis = j < cn;
+                    if (tree && vis) {
+                        const int t = min(row / G, n - 1);
+                        vis = (meta->anc[a.row0 + t] >> (c0 + j)) & 1u;
+                    }
+                    Ss[row * SSTR + j] = vis ? s[r] * a.scale : -INFINITY;
+                }
+            }
+        }
+        __syncthreads();
+
+        // online softmax, one thread per row
+        if (tid < RB * 32) {
+            const int row = tid;
+            float *sr = Ss + row * SSTR;
+            float mx = -INFINITY;
+            for (int j = 0; j < CH; ++j) mx = fmaxf(mx, sr[j]);
+            const float mold = mrow[row];
+            const float mnew = fmaxf(mold, mx);
+            float alpha, l = lrow[row];
+            if (mnew == -INFINITY) {
+                alpha = 1.f;
+                for (int j = 0; j < CH; ++j) sr[j] = 0.f;
+            } else {
+                alpha = (mold == -INFINITY) ? 0.f : expf(mold - mnew);
+                l *= alpha;
+                for (int j = 0; j < CH; ++j) {
+                    const float p = (sr[j] == -INFINITY) ? 0.f : expf(sr[j] - mnew);
+                    l += p;
+                    const uint16_t hi = f2bf(p);
+                    const uint16_t lo = f2bf(p - bf2f(hi));
+                    sr[j] = __uint_as_float((uint32_t)hi | ((uint32_t)lo << 16));
+                }
+            }
+            mrow[row] = mnew;
+            lrow[row] = l;
+            arow[row] = alpha;
+        }
+        __syncthreads();
+
+        // o = o * alpha + P V
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+            const int rb = wave + 4 * bi;
+            if (rb >= RB) break;
+            float al[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) al[r] = arow[rb * 32 + acc_row(r, hf)];
+#pragma unroll
+            for (int d = 0; d < DB; ++d)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[bi][d][r] *= al[r];
+#pragma unroll
+            for (int kk = 0; kk < CH / 16; ++kk) {
+                const float *sp = Ss + (rb * 32 + c) * SSTR + kk * 16 + hf * 8;
+                uint32_t hiw[4], low[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t p0 = __float_as_uint(sp[2 * e]), p1 = __float_as_uint(sp[2 * e + 1]);
+                    hiw[e] = (p0 & 0xffffu) | (p1 << 16);
+                    low[e] = (p0 >> 16) | (p1 & 0xffff0000u);
+                }
+                const uint4 phi = {hiw[0], hiw[1], hiw[2], hiw[3]};
+                const uint4 plo = {low[0], low[1], low[2], low[3]};
+#pragma unroll
+                for (int d = 0; d < DB; ++d) {
+                    const uint4 vb = *reinterpret_cast<const uint4 *>(Vt + (d * 32 + c) * VSTR + kk * 16 + hf * 8);
+                    o[bi][d] = mfma32(phi, vb, o[bi][d]);
+                    o[bi][d] = mfma32(plo, vb, o[bi][d]);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const int RP = kMaxRows * kMaxGroup;
+    const size_t pbase = ((size_t)kvh * a.ns + split) * RP;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+        const int rb = wave + 4 * bi;
+        if (rb >= RB) break;
+#pragma unroll
+        for (int d = 0; d < DB; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = rb * 32 + acc_row(r, hf);
+                if (row < R) a.po[(pbase + row) * D + d * 32 + c] = o[bi][d][r];
+            }
+    }
+    for (int r = tid; r < R; r += 256) {
+        a.pm[pbase + r] = mrow[r];
+        a.pl[pbase + r] = lrow[r];
+    }
+}
+
+// Merge the splits of every (node, query head) in split order.
+template <int D>
+__global__ __launch_bounds__(D) void k_attn_combine(AttnArgs a, uint16_t *__restrict__ out) {
+    const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+    const int G = a.G, kvh = h / G, row = t * G + (h % G);
+    const int RP = kMaxRows * kMaxGroup;
+    float M = -INFINITY;
+    for (int s = 0; s < a.ns; ++s) M = fmaxf(M, a.pm[((size_t)kvh * a.ns + s) * RP + row]);
+    float L = 0.f, O = 0.f;
+    for (int s = 0; s < a.ns; ++s) {
+        const size_t b = ((size_t)kvh * a.ns + s) * RP + row;
+        const float ms = a.pm[b];
+        if (ms == -INFINITY) continue;
+        const float w = expf(ms - M);
+        L += w * a.pl[b];
+        O += w * a.po[b * D + d];
+    }
+    out[(size_t)(a.row0 + t) * a.n_qhead * D + h * D + d] = f2bf(O / L);
+}
+
+// ---------------------------------------------------------------- commit
+// Gather the accepted path's KV rows: slot ctx+path[d] -> ctx+d.  One
+// workgroup per (layer, KV head) reads every moved row before writing any,
+// so the in-place move is safe in any order.
+
+__global__ __launch_bounds__(256) void k_commit_kv(uint16_t *const *__restrict__ kv_ptrs, int cap,
+                                                   int D, int ctx, const int *__restrict__ path,
+                                                   int path_len) {
+    __shared__ __attribute__((aligned(16))) uint16_t buf[2 * kMaxRows * 128];
+    const int layer = blockIdx.x, h = blockIdx.y;
+    uint16_t *Kc = kv_ptrs[2 * layer] + (size_t)h * cap * D;
+    uint16_t *Vc = kv_ptrs[2 * layer + 1] + (size_t)h * cap * D;
+    const int per = D / 8;
+    const int total = path_len * per;
+    for (int idx = threadIdx.x; idx < total; idx += 256) {
+        const int d = idx / per, p = idx % per;
+        const size_t src = (size_t)(ctx + path[d]) * D + p * 8;
+        *reinterpret_cast<uint4 *>(buf + d * D + p * 8) = ld16(Kc + src);
+        *reinterpret_cast<uint4 *>(buf + (kMaxRows + d) * D + p * 8) = ld16(Vc + src);
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < total; idx += 256) {
+        const int d = idx / per, p = idx % per;
+        if (path[d] == d) continue;
+        const size_t dst = (size_t)(ctx + d) * D + p * 8;
+        *reinterpret_cast<uint4 *>(Kc + dst) = *reinterpret_cast<const uint4 *>(buf + d * D + p * 8);
+        *reinterpret_cast<uint4 *>(Vc + dst) =
+            *reinterpret_cast<const uint4 *>(buf + (kMaxRows + d) * D + p * 8);
+    }
+}
+
+// ------------------------------------------------------------ launchers
+
+hipError_t launch_embed(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H,
+                        uint16_t *X) {
+    hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, s, emb, meta, H, X);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(hipStream_t s, const uint16_t *X, const uint16_t *w, int M, int H,
+                          float eps, uint16_t *Y) {
+    hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, s, X, w, H, eps, Y);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(hipStream_t s, int epi, const GemmArgs &a) {
+    constexpr int WK = 4;
+    const dim3 grid((a.N + 31) / 32), block(64 * WK);
+    switch (epi) {
+    case EPI_BF16: hipLaunchKernelGGL((k_gemm<EPI_BF16, WK>), grid, block, 0, s, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_gemm<EPI_RESID, WK>), grid, block, 0, s, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm<EPI_SWIGLU, WK>), grid, block, 0, s, a); break;
+    case EPI_HEAD: hipLaunchKernelGGL((k_gemm<EPI_HEAD, WK>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_kv(hipStream_t s, const RopeArgs &a) {
+    hipLaunchKernelGGL(k_rope_kv, dim3(a.n), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a) {
+    const dim3 grid(a.ns, a.n_qhead / a.G);
+    if (D == 128) hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, s, a);
+    else if (D == 64) hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t *out) {
+    const dim3 grid(a.n, a.n_qhead);
+    if (D == 128) hipLaunchKernelGGL(k_attn_combine<128>, grid, dim3(128), 0, s, a, out);
+    else if (D == 64) hipLaunchKernelGGL(k_attn_combine<64>, grid, dim3(64), 0, s, a, out);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M, int32_t *argmax,
+                              float *gap, float *top) {
+    hipLaunchKernelGGL(k_top2_reduce, dim3(M), dim3(256), 0, s, part, ntiles, argmax, gap, top);
+    return hipGetLastError();
+}
+
+hipError_t launch_commit_kv(hipStream_t s, uint16_t *const *kv_ptrs, int n_layers, int KVH, int cap,
+                            int D, int ctx, const int *path, int path_len) {
+    hipLaunchKernelGGL(k_commit_kv, dim3(n_layers, KVH), dim3(256), 0, s, kv_ptrs, cap, D, ctx, path,
+                       path_len);
+    return hipGetLastError();
+}
+
+} // namespace tv

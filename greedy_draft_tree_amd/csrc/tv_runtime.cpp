@@ -1,0 +1,760 @@
+// Host runtime of the tree-verify library: model descriptor, bound buffers,
+// per-request state, tree validation and metadata, launch sequence, accept
+// walk and commit.  Exposes the C ABI declared in include/treeverify.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/treeverify.h"
+#include "tv_internal.h"
+
+using namespace tv;
+
+namespace {
+
+struct Req {
+    int ctx_len = 0;
+    std::vector<int32_t> history;
+    std::vector<uint16_t *> K, V;  // per layer (attention layers)
+    std::vector<float *> S;        // per layer (recurrent layers)
+    // modifiers
+    float rep = 1.f;
+    bool mods_on = false;
+    std::vector<uint32_t> hist_bits;  // host copy of prior-token bits
+    uint32_t *d_hist = nullptr;
+    float *d_bias = nullptr;
+    uint32_t *d_allow = nullptr;
+    bool has_bias = false, has_allow = false;
+    // pending tree of the last verify
+    bool pending = false;
+    std::vector<int32_t> pparents, ptokens;
+    int prow0 = 0;
+    // device pointer table {K0, V0, K1, V1, ...} over attention layers
+    uint16_t **d_kvtab = nullptr;
+    bool kvtab_dirty = true;
+};
+
+struct ProfRec {
+    const char *name;
+    hipEvent_t a, b;
+};
+
+} // namespace
+
+struct tv_ctx {
+    tv_model_desc m{};
+    std::vector<int> kinds;
+    std::vector<int> attn_layers;
+    hipStream_t stream = nullptr;
+    std::string err;
+    int G = 1;
+
+    // weights
+    const uint16_t *emb = nullptr, *head = nullptr, *final_norm = nullptr;
+    std::vector<const uint16_t *> attn_norm, wqkv, wo, wa, ffn_norm, wg, wu, wd;
+
+    std::vector<Req> reqs;
+
+    // scratch (library-owned)
+    uint16_t *X = nullptr, *XN = nullptr, *QKV = nullptr, *QR = nullptr, *ATT = nullptr,
+             *ACT = nullptr;
+    float *logits = nullptr;  // [32, V] when the caller passes none
+    Top2 *part = nullptr;
+    float *po = nullptr, *pm = nullptr, *pl = nullptr;
+    float *rope_cos = nullptr, *rope_sin = nullptr;
+    PassMeta *d_meta = nullptr;
+    int32_t *d_argmax = nullptr;
+    float *d_gap = nullptr, *d_top = nullptr;
+    int32_t *d_path = nullptr;
+    // pinned host staging
+    PassMeta *h_meta = nullptr;
+    int32_t *h_argmax = nullptr;
+    float *h_gap = nullptr;
+    int32_t *h_path = nullptr;
+    int ns_max = 0;
+
+    // profiling
+    bool prof = false;
+    std::string prof_only;
+    std::vector<ProfRec> recs;
+    size_t rec_used = 0;
+    std::vector<std::pair<std::string, std::pair<double, int>>> totals;
+};
+
+namespace {
+
+int fail(tv_ctx *c, int code, const char *fmt, ...) {
+    if (c) {
+        char buf[512];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof buf, fmt, ap);
+        va_end(ap);
+        c->err = buf;
+    }
+    return code;
+}
+
+#define HIPCHECK(c, expr)                                                                   \
+    do {                                                                                    \
+        hipError_t e_ = (expr);                                                             \
+        if (e_ != hipSuccess)                                                               \
+            return fail((c), TV_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));      \
+    } while (0)
+
+size_t vocab_words(const tv_model_desc &m) { return (size_t)(m.vocab + 31) / 32; }
+
+// Record a launch with optional event timing.
+struct Launch {
+    tv_ctx *c;
+    const char *name;
+    ProfRec *rec = nullptr;
+    Launch(tv_ctx *ctx, const char *nm) : c(ctx), name(nm) {
+        if (c->prof && !strncmp(nm, c->prof_only.c_str(), c->prof_only.size())) {
+            if (c->rec_used == c->recs.size()) {
+                ProfRec r{nm, nullptr, nullptr};
+                hipEventCreate(&r.a);
+                hipEventCreate(&r.b);
+                c->recs.push_back(r);
+            }
+            rec = &c->recs[c->rec_used++];
+            rec->name = nm;
+            hipEventRecord(rec->a, c->stream);
+        }
+    }
+    void done() {
+        if (rec) hipEventRecord(rec->b, c->stream);
+    }
+};
+
+void harvest(tv_ctx *c) {
+    for (size_t i = 0; i < c->rec_used; ++i) {
+        float ms = 0.f;
+        hipEventElapsedTime(&ms, c->recs[i].a, c->recs[i].b);
+        bool found = false;
+        for (auto &t : c->totals)
+            if (t.first == c->recs[i].name) {
+                t.second.first += ms;
+                t.second.second += 1;
+                found = true;
+                break;
+            }
+        if (!found) c->totals.push_back({c->recs[i].name, {(double)ms, 1}});
+    }
+    c->rec_used = 0;
+}
+
+#define LAUNCH(c, nm, call)                                                                  \
+    do {                                                                                     \
+        Launch L_(c, nm);                                                                    \
+        hipError_t e_ = (call);                                                              \
+        L_.done();                                                                           \
+        if (e_ != hipSuccess) return fail(c, TV_EHIP, "launch %s: %s", nm, hipGetErrorString(e_)); \
+    } while (0)
+
+int check_req(tv_ctx *c, int req) {
+    if (!c) return TV_EINVAL;
+    if (req < 0 || req >= c->m.max_req) return fail(c, TV_EINVAL, "request %d out of range", req);
+    return TV_OK;
+}
+
+int check_bound(tv_ctx *c, const std::vector<int> &reqs) {
+    const tv_model_desc &m = c->m;
+    if (!c->emb || !c->head || !c->final_norm) return fail(c, TV_ESTATE, "emb/head/final_norm not bound");
+    for (int l = 0; l < m.n_layer; ++l) {
+        if (!c->attn_norm[l] || !c->wqkv[l] || !c->wo[l] || !c->ffn_norm[l] || !c->wg[l] || !c->wu[l] ||
+            !c->wd[l])
+            return fail(c, TV_ESTATE, "layer %d weights not bound", l);
+        if (c->kinds[l] == TV_LAYER_RECUR && !c->wa[l]) return fail(c, TV_ESTATE, "layer %d wa not bound", l);
+    }
+    for (int r : reqs) {
+        const Req &q = c->reqs[r];
+        for (int l = 0; l < m.n_layer; ++l) {
+            if (c->kinds[l] == TV_LAYER_ATTN && (!q.K[l] || !q.V[l]))
+                return fail(c, TV_ESTATE, "request %d layer %d KV cache not bound", r, l);
+            if (c->kinds[l] == TV_LAYER_RECUR && !q.S[l])
+                return fail(c, TV_ESTATE, "request %d layer %d state not bound", r, l);
+        }
+    }
+    return TV_OK;
+}
+
+// Tree rules ("Algorithm and correctness contract", Target position and
+// batching): parents before children, distinct sibling tokens.
+int validate_tree(tv_ctx *c, const int32_t *parents, const int32_t *tokens, int n) {
+    if (!parents || !tokens) return fail(c, TV_EINVAL, "null tree");
+    if (n < 1 || n > TV_MAX_NODES) return fail(c, TV_EINVAL, "n_nodes %d not in [1, %d]", n, TV_MAX_NODES);
+    if (parents[0] != -1) return fail(c, TV_EINVAL, "parents[0] must be -1");
+    for (int i = 0; i < n; ++i) {
+        if (tokens[i] < 0 || tokens[i] >= c->m.vocab) return fail(c, TV_EINVAL, "token %d out of range", i);
+        if (i > 0 && (parents[i] < 0 || parents[i] >= i))
+            return fail(c, TV_EINVAL, "parents[%d] = %d not in [0, %d)", i, parents[i], i);
+    }
+    for (int i = 1; i < n; ++i)
+        for (int j = 1; j < i; ++j)
+            if (parents[j] == parents[i] && tokens[j] == tokens[i])
+                return fail(c, TV_EINVAL, "sibling nodes %d and %d carry the same token", j, i);
+    return TV_OK;
+}
+
+int upload_kvtab(tv_ctx *c, Req &q) {
+    if (!q.kvtab_dirty) return TV_OK;
+    std::vector<uint16_t *> tab;
+    for (int l : c->attn_layers) {
+        tab.push_back(q.K[l]);
+        tab.push_back(q.V[l]);
+    }
+    if (!tab.empty()) {
+        if (!q.d_kvtab) HIPCHECK(c, hipMalloc(&q.d_kvtab, tab.size() * sizeof(void *)));
+        HIPCHECK(c, hipMemcpyAsync(q.d_kvtab, tab.data(), tab.size() * sizeof(void *),
+                                   hipMemcpyHostToDevice, c->stream));
+        HIPCHECK(c, hipStreamSynchronize(c->stream));
+    }
+    q.kvtab_dirty = false;
+    return TV_OK;
+}
+
+// One forward pass over `total` rows of up to 32, request after request.
+int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parents,
+             const int32_t *const *tokens, const int *n_nodes, float *logits_dev, int32_t *argmax,
+             float *gap) {
+    const tv_model_desc &m = c->m;
+    int total = 0;
+    for (int r = 0; r < n_req; ++r) {
+        int rc = check_req(c, reqs[r]);
+        if (rc) return rc;
+        for (int s = 0; s < r; ++s)
+            if (reqs[s] == reqs[r]) return fail(c, TV_EINVAL, "request %d appears twice", reqs[r]);
+        rc = validate_tree(c, parents[r], tokens[r], n_nodes[r]);
+        if (rc) return rc;
+        if (c->reqs[reqs[r]].ctx_len + n_nodes[r] > m.max_ctx)
+            return fail(c, TV_ECAPACITY, "request %d: ctx %d + %d rows > max_ctx %d", reqs[r],
+                        c->reqs[reqs[r]].ctx_len, n_nodes[r], m.max_ctx);
+        total += n_nodes[r];
+    }
+    if (total > TV_MAX_NODES) return fail(c, TV_EINVAL, "%d rows in one pass > %d", total, TV_MAX_NODES);
+    {
+        std::vector<int> rv(reqs, reqs + n_req);
+        int rc = check_bound(c, rv);
+        if (rc) return rc;
+    }
+    for (int r = 0; r < n_req; ++r) {
+        int rc = upload_kvtab(c, c->reqs[reqs[r]]);
+        if (rc) return rc;
+    }
+
+    // metadata
+    PassMeta &pm = *c->h_meta;
+    memset(&pm, 0, sizeof pm);
+    bool any_mods = false;
+    int row0 = 0;
+    std::vector<int> row0s(n_req);
+    for (int r = 0; r < n_req; ++r) {
+        const int n = n_nodes[r];
+        Req &q = c->reqs[reqs[r]];
+        row0s[r] = row0;
+        for (int i = 0; i < n; ++i) {
+            const int g = row0 + i;
+            const int p = parents[r][i];
+            pm.tok[g] = tokens[r][i];
+            pm.depth[g] = p < 0 ? 0 : pm.depth[row0 + p] + 1;
+            pm.anc[g] = (p < 0 ? 0u : pm.anc[row0 + p]) | (1u << i);
+            pm.row_req[g] = r;
+            // tokens on root..i
+            int L = 0, stack[TV_MAX_NODES];
+            for (int j = i; j >= 0; j = parents[r][j]) stack[L++] = tokens[r][j];
+            pm.path_len[g] = L;
+            for (int d = 0; d < L; ++d) pm.path_tok[g * kMaxRows + d] = stack[L - 1 - d];
+        }
+        HeadMods &hm = pm.mods[r];
+        hm.rep = q.rep;
+        hm.hist_bits = (q.mods_on && q.rep != 1.f) ? q.d_hist : nullptr;
+        hm.bias = (q.mods_on && q.has_bias) ? q.d_bias : nullptr;
+        hm.allow_bits = (q.mods_on && q.has_allow) ? q.d_allow : nullptr;
+        if (!q.mods_on) hm.rep = 1.f;
+        any_mods |= q.mods_on;
+        row0 += n;
+    }
+    const int M = total;
+    hipStream_t s = c->stream;
+    HIPCHECK(c, hipMemcpyAsync(c->d_meta, c->h_meta, sizeof(PassMeta), hipMemcpyHostToDevice, s));
+
+    const int H = m.hidden, D = m.head_dim, QH = m.n_qhead, KVH = m.n_kvhead;
+    LAUNCH(c, "embed", launch_embed(s, c->emb, c->d_meta, M, H, c->X));
+    for (int l = 0; l < m.n_layer; ++l) {
+        LAUNCH(c, "rmsnorm", launch_rmsnorm(s, c->X, c->attn_norm[l], M, H, m.eps, c->XN));
+        if (c->kinds[l] == TV_LAYER_ATTN) {
+            GemmArgs g{};
+            g.X = c->XN; g.ldx = H; g.W = c->wqkv[l]; g.M = M; g.N = (QH + 2 * KVH) * D; g.K = H;
+            g.Y = c->QKV; g.ldy = g.N;
+            LAUNCH(c, "gemm_qkv", launch_gemm(s, EPI_BF16, g));
+            for (int r = 0; r < n_req; ++r) {
+                Req &q = c->reqs[reqs[r]];
+                RopeArgs ra{};
+                ra.qkv = c->QKV; ra.q_out = c->QR; ra.Kc = q.K[l]; ra.Vc = q.V[l];
+                ra.cosT = c->rope_cos; ra.sinT = c->rope_sin; ra.meta = c->d_meta;
+                ra.row0 = row0s[r]; ra.n = n_nodes[r]; ra.ctx = q.ctx_len; ra.cap = m.max_ctx;
+                ra.QH = QH; ra.KVH = KVH; ra.D = D;
+                LAUNCH(c, "rope_kv", launch_rope_kv(s, ra));
+                AttnArgs aa{};
+                aa.Q = c->QR; aa.Kc = q.K[l]; aa.Vc = q.V[l]; aa.meta = c->d_meta;
+                aa.po = c->po; aa.pm = c->pm; aa.pl = c->pl;
+                aa.row0 = row0s[r]; aa.n = n_nodes[r]; aa.ctx = q.ctx_len; aa.cap = m.max_ctx;
+                aa.G = c->G; aa.n_qhead = QH;
+                aa.n_ctx_split = (q.ctx_len + kAttnSplit - 1) / kAttnSplit;
+                aa.ns = aa.n_ctx_split + 1;
+                aa.scale = (float)(1.0 / std::sqrt((double)D));
+                LAUNCH(c, "attn", launch_attn(s, D, aa));
+                LAUNCH(c, "attn_combine", launch_attn_combine(s, D, aa, c->ATT));
+            }
+        } else {
+            return fail(c, TV_EINVAL, "recurrent layers are not available in this build");
+        }
+        {
+            GemmArgs g{};
+            g.X = c->ATT; g.ldx = QH * D; g.W = c->wo[l]; g.M = M; g.N = H; g.K = QH * D;
+            g.Y = c->X; g.ldy = H;
+            LAUNCH(c, "gemm_o", launch_gemm(s, EPI_RESID, g));
+        }
+        LAUNCH(c, "rmsnorm", launch_rmsnorm(s, c->X, c->ffn_norm[l], M, H, m.eps, c->XN));
+        {
+            GemmArgs g{};
+            g.X = c->XN; g.ldx = H; g.W = c->wg[l]; g.W2 = c->wu[l]; g.M = M; g.N = m.ffn; g.K = H;
+            g.Y = c->ACT; g.ldy = m.ffn;
+            LAUNCH(c, "gemm_gateup", launch_gemm(s, EPI_SWIGLU, g));
+        }
+        {
+            GemmArgs g{};
+            g.X = c->ACT; g.ldx = m.ffn; g.W = c->wd[l]; g.M = M; g.N = H; g.K = m.ffn;
+            g.Y = c->X; g.ldy = H;
+            LAUNCH(c, "gemm_down", launch_gemm(s, EPI_RESID, g));
+        }
+    }
+    LAUNCH(c, "rmsnorm", launch_rmsnorm(s, c->X, c->final_norm, M, H, m.eps, c->XN));
+    float *out = logits_dev ? logits_dev : c->logits;
+    {
+        GemmArgs g{};
+        g.X = c->XN; g.ldx = H; g.W = c->head; g.M = M; g.N = m.vocab; g.K = H;
+        g.Yf = out; g.ldyf = m.vocab; g.part = c->part; g.meta = c->d_meta; g.mods_on = any_mods;
+        LAUNCH(c, "gemm_head", launch_gemm(s, EPI_HEAD, g));
+    }
+    LAUNCH(c, "top2", launch_top2_reduce(s, c->part, (m.vocab + 31) / 32, M, c->d_argmax, c->d_gap,
+                                         c->d_top));
+    HIPCHECK(c, hipMemcpyAsync(c->h_argmax, c->d_argmax, M * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    HIPCHECK(c, hipMemcpyAsync(c->h_gap, c->d_gap, M * sizeof(float), hipMemcpyDeviceToHost, s));
+    HIPCHECK(c, hipStreamSynchronize(s));
+    if (c->prof) harvest(c);
+    if (argmax) memcpy(argmax, c->h_argmax, M * sizeof(int32_t));
+    if (gap) memcpy(gap, c->h_gap, M * sizeof(float));
+
+    for (int r = 0; r < n_req; ++r) {
+        Req &q = c->reqs[reqs[r]];
+        q.pending = true;
+        q.pparents.assign(parents[r], parents[r] + n_nodes[r]);
+        q.ptokens.assign(tokens[r], tokens[r] + n_nodes[r]);
+        q.prow0 = row0s[r];
+    }
+    // a pass overwrites shared scratch: other requests' pending trees stay
+    // valid for their KV (held in their own caches) only.
+    return TV_OK;
+}
+
+void set_bit(std::vector<uint32_t> &b, int v) { b[v >> 5] |= 1u << (v & 31); }
+
+} // namespace
+
+extern "C" {
+
+int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
+    if (!md || !out) return TV_EINVAL;
+    *out = nullptr;
+    const tv_model_desc &m = *md;
+    if (m.n_layer < 1 || m.hidden < 64 || m.hidden % 64 || m.n_qhead < 1 || m.n_kvhead < 1 ||
+        m.n_qhead % m.n_kvhead || (m.head_dim != 64 && m.head_dim != 128) || m.ffn < 8 || m.ffn % 8 ||
+        m.vocab < 2 || m.max_ctx < 1 || m.max_req < 1 || !m.layer_kind || m.eps <= 0.f)
+        return TV_EINVAL;
+    if (m.n_qhead / m.n_kvhead > 5) return TV_EINVAL;  // attention stages G*32 <= 160 query rows
+    tv_ctx *c = new tv_ctx();
+    c->m = m;
+    c->kinds.assign(m.layer_kind, m.layer_kind + m.n_layer);
+    for (int l = 0; l < m.n_layer; ++l) {
+        if (c->kinds[l] != TV_LAYER_ATTN && c->kinds[l] != TV_LAYER_RECUR) {
+            delete c;
+            return TV_EINVAL;
+        }
+        if (c->kinds[l] == TV_LAYER_ATTN) c->attn_layers.push_back(l);
+    }
+    c->m.layer_kind = nullptr;
+    c->stream = (hipStream_t)stream;
+    c->G = m.n_qhead / m.n_kvhead;
+    const int L = m.n_layer;
+    c->attn_norm.assign(L, nullptr); c->wqkv.assign(L, nullptr); c->wo.assign(L, nullptr);
+    c->wa.assign(L, nullptr); c->ffn_norm.assign(L, nullptr); c->wg.assign(L, nullptr);
+    c->wu.assign(L, nullptr); c->wd.assign(L, nullptr);
+    c->reqs.resize(m.max_req);
+    for (auto &q : c->reqs) {
+        q.K.assign(L, nullptr); q.V.assign(L, nullptr); q.S.assign(L, nullptr);
+        q.hist_bits.assign(vocab_words(m), 0u);
+    }
+    auto cleanup = [&](int rc) { tv_destroy(c); return rc; };
+    const int R = kMaxRows;
+    const int H = m.hidden, D = m.head_dim;
+    const size_t qkv = (size_t)std::max((m.n_qhead + 2 * m.n_kvhead) * D, 3 * m.n_qhead * D);
+    c->ns_max = (m.max_ctx + kAttnSplit - 1) / kAttnSplit + 1;
+    const size_t RP = (size_t)kMaxRows * kMaxGroup;
+    hipError_t e = hipSuccess;
+#define ALLOC(p, bytes) if (e == hipSuccess) e = hipMalloc((void **)&(p), (bytes))
+    ALLOC(c->X, (size_t)R * H * 2);
+    ALLOC(c->XN, (size_t)R * H * 2);
+    ALLOC(c->QKV, (size_t)R * qkv * 2);
+    ALLOC(c->QR, (size_t)R * m.n_qhead * D * 2);
+    ALLOC(c->ATT, (size_t)R * m.n_qhead * D * 2);
+    ALLOC(c->ACT, (size_t)R * m.ffn * 2);
+    ALLOC(c->logits, (size_t)R * m.vocab * 4);
+    ALLOC(c->part, (size_t)((m.vocab + 31) / 32) * 32 * sizeof(Top2));
+    ALLOC(c->po, (size_t)m.n_kvhead * c->ns_max * RP * D * 4);
+    ALLOC(c->pm, (size_t)m.n_kvhead * c->ns_max * RP * 4);
+    ALLOC(c->pl, (size_t)m.n_kvhead * c->ns_max * RP * 4);
+    ALLOC(c->rope_cos, (size_t)m.max_ctx * (D / 2) * 4);
+    ALLOC(c->rope_sin, (size_t)m.max_ctx * (D / 2) * 4);
+    ALLOC(c->d_meta, sizeof(PassMeta));
+    ALLOC(c->d_argmax, R * 4);
+    ALLOC(c->d_gap, R * 4);
+    ALLOC(c->d_top, 2 * R * 4);
+    ALLOC(c->d_path, R * 4);
+#undef ALLOC
+    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_meta, sizeof(PassMeta), hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_argmax, R * 4, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_gap, R * 4, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_path, R * 4, hipHostMallocDefault);
+    if (e != hipSuccess) return cleanup(TV_EHIP);
+    // RoPE table: angle pos * theta^(-2i/D) in fp64, cos and sin rounded to fp32
+    {
+        std::vector<float> cs((size_t)m.max_ctx * (D / 2)), sn(cs.size());
+        for (int p = 0; p < m.max_ctx; ++p)
+            for (int i = 0; i < D / 2; ++i) {
+                const double ang = (double)p * std::pow((double)m.rope_theta, -2.0 * i / D);
+                cs[(size_t)p * (D / 2) + i] = (float)std::cos(ang);
+                sn[(size_t)p * (D / 2) + i] = (float)std::sin(ang);
+            }
+        e = hipMemcpy(c->rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(c->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice);
+        if (e != hipSuccess) return cleanup(TV_EHIP);
+    }
+    *out = c;
+    return TV_OK;
+}
+
+void tv_destroy(tv_ctx *c) {
+    if (!c) return;
+    if (c->stream) hipStreamSynchronize(c->stream);
+    else hipDeviceSynchronize();
+    void *dev[] = {c->X, c->XN, c->QKV, c->QR, c->ATT, c->ACT, c->logits, c->part, c->po, c->pm, c->pl,
+                   c->rope_cos, c->rope_sin, c->d_meta, c->d_argmax, c->d_gap, c->d_top, c->d_path};
+    for (void *p : dev)
+        if (p) hipFree(p);
+    for (auto &q : c->reqs) {
+        if (q.d_hist) hipFree(q.d_hist);
+        if (q.d_bias) hipFree(q.d_bias);
+        if (q.d_allow) hipFree(q.d_allow);
+        if (q.d_kvtab) hipFree(q.d_kvtab);
+    }
+    void *host[] = {c->h_meta, c->h_argmax, c->h_gap, c->h_path};
+    for (void *p : host)
+        if (p) hipHostFree(p);
+    for (auto &r : c->recs) {
+        hipEventDestroy(r.a);
+        hipEventDestroy(r.b);
+    }
+    delete c;
+}
+
+const char *tv_last_error(tv_ctx *c) { return c ? c->err.c_str() : "null context"; }
+
+int tv_bind(tv_ctx *c, const char *name, void *ptr, size_t bytes) {
+    if (!c || !name) return TV_EINVAL;
+    if (!ptr) return fail(c, TV_EINVAL, "null pointer for %s", name);
+    const tv_model_desc &m = c->m;
+    const size_t H = m.hidden, V = m.vocab, F = m.ffn, D = m.head_dim, QH = m.n_qhead, KVH = m.n_kvhead;
+    auto want = [&](size_t n) -> int {
+        if (bytes != n) return fail(c, TV_EINVAL, "%s: %zu bytes given, %zu expected", name, bytes, n);
+        return TV_OK;
+    };
+    int rc;
+    if (!strcmp(name, "emb")) { if ((rc = want(V * H * 2))) return rc; c->emb = (const uint16_t *)ptr; return TV_OK; }
+    if (!strcmp(name, "head")) { if ((rc = want(V * H * 2))) return rc; c->head = (const uint16_t *)ptr; return TV_OK; }
+    if (!strcmp(name, "final_norm")) { if ((rc = want(H * 2))) return rc; c->final_norm = (const uint16_t *)ptr; return TV_OK; }
+    int l = -1, r = -1, used = 0;
+    char field[32] = {0};
+    if (sscanf(name, "layers.%d.%31s%n", &l, field, &used) == 2 && name[used] == 0) {
+        if (l < 0 || l >= m.n_layer) return fail(c, TV_EINVAL, "%s: layer out of range", name);
+        const bool at = c->kinds[l] == TV_LAYER_ATTN;
+        const uint16_t *p = (const uint16_t *)ptr;
+        if (!strcmp(field, "attn_norm")) { if ((rc = want(H * 2))) return rc; c->attn_norm[l] = p; return TV_OK; }
+        if (!strcmp(field, "ffn_norm")) { if ((rc = want(H * 2))) return rc; c->ffn_norm[l] = p; return TV_OK; }
+        if (!strcmp(field, "wqkv")) {
+            if ((rc = want((at ? (QH + 2 * KVH) * D : 3 * QH * D) * H * 2))) return rc;
+            c->wqkv[l] = p; return TV_OK;
+        }
+        if (!strcmp(field, "wa")) {
+            if (at) return fail(c, TV_EINVAL, "%s: not a recurrent layer", name);
+            if ((rc = want(QH * H * 2))) return rc;
+            c->wa[l] = p; return TV_OK;
+        }
+        if (!strcmp(field, "wo")) { if ((rc = want(H * QH * D * 2))) return rc; c->wo[l] = p; return TV_OK; }
+        if (!strcmp(field, "wg")) { if ((rc = want(F * H * 2))) return rc; c->wg[l] = p; return TV_OK; }
+        if (!strcmp(field, "wu")) { if ((rc = want(F * H * 2))) return rc; c->wu[l] = p; return TV_OK; }
+        if (!strcmp(field, "wd")) { if ((rc = want(H * F * 2))) return rc; c->wd[l] = p; return TV_OK; }
+        return fail(c, TV_EINVAL, "unknown tensor %s", name);
+    }
+    if (sscanf(name, "req.%d.layers.%d.%31s%n", &r, &l, field, &used) == 3 && name[used] == 0) {
+        if (r < 0 || r >= m.max_req) return fail(c, TV_EINVAL, "%s: request out of range", name);
+        if (l < 0 || l >= m.n_layer) return fail(c, TV_EINVAL, "%s: layer out of range", name);
+        Req &q = c->reqs[r];
+        const bool at = c->kinds[l] == TV_LAYER_ATTN;
+        if (!strcmp(field, "k") || !strcmp(field, "v")) {
+            if (!at) return fail(c, TV_EINVAL, "%s: not an attention layer", name);
+            if ((rc = want(KVH * (size_t)m.max_ctx * D * 2))) return rc;
+            (field[0] == 'k' ? q.K[l] : q.V[l]) = (uint16_t *)ptr;
+            q.kvtab_dirty = true;
+            return TV_OK;
+        }
+        if (!strcmp(field, "state")) {
+            if (at) return fail(c, TV_EINVAL, "%s: not a recurrent layer", name);
+            if ((rc = want(QH * D * D * 4))) return rc;
+            q.S[l] = (float *)ptr;
+            return TV_OK;
+        }
+        return fail(c, TV_EINVAL, "unknown tensor %s", name);
+    }
+    return fail(c, TV_EINVAL, "unknown tensor %s", name);
+}
+
+int tv_set_history(tv_ctx *c, int req, const int32_t *ids, int n_ids, int ctx_len) {
+    int rc = check_req(c, req);
+    if (rc) return rc;
+    if (ctx_len < 0 || ctx_len > c->m.max_ctx) return fail(c, TV_ECAPACITY, "ctx_len %d out of range", ctx_len);
+    if (n_ids < 0 || (n_ids > 0 && !ids)) return fail(c, TV_EINVAL, "bad history");
+    for (int i = 0; i < n_ids; ++i)
+        if (ids[i] < 0 || ids[i] >= c->m.vocab) return fail(c, TV_EINVAL, "history id %d out of range", i);
+    Req &q = c->reqs[req];
+    q.ctx_len = ctx_len;
+    q.history.assign(ids, ids + n_ids);
+    std::fill(q.hist_bits.begin(), q.hist_bits.end(), 0u);
+    for (int i = 0; i < n_ids; ++i) set_bit(q.hist_bits, ids[i]);
+    q.pending = false;
+    if (q.d_hist) HIPCHECK(c, hipMemcpy(q.d_hist, q.hist_bits.data(), q.hist_bits.size() * 4, hipMemcpyHostToDevice));
+    return TV_OK;
+}
+
+int tv_set_modifiers(tv_ctx *c, int req, float rep, const int32_t *bias_ids, const float *bias_vals,
+                     int n_bias, const uint32_t *allow_bits) {
+    int rc = check_req(c, req);
+    if (rc) return rc;
+    const tv_model_desc &m = c->m;
+    if (!(rep > 0.f) || !std::isfinite(rep)) return fail(c, TV_EINVAL, "repetition penalty must be > 0");
+    if (n_bias < 0 || (n_bias > 0 && (!bias_ids || !bias_vals))) return fail(c, TV_EINVAL, "bad bias");
+    for (int i = 0; i < n_bias; ++i) {
+        if (bias_ids[i] < 0 || bias_ids[i] >= m.vocab) return fail(c, TV_EINVAL, "bias id out of range");
+        if (!std::isfinite(bias_vals[i])) return fail(c, TV_EINVAL, "bias value not finite");
+    }
+    Req &q = c->reqs[req];
+    const size_t W = vocab_words(m);
+    if (!q.d_hist) HIPCHECK(c, hipMalloc(&q.d_hist, W * 4));
+    if (!q.d_bias) HIPCHECK(c, hipMalloc(&q.d_bias, (size_t)m.vocab * 4));
+    if (!q.d_allow) HIPCHECK(c, hipMalloc(&q.d_allow, W * 4));
+    std::vector<float> bias(m.vocab, 0.f);
+    for (int i = 0; i < n_bias; ++i) bias[bias_ids[i]] += bias_vals[i];
+    HIPCHECK(c, hipMemcpy(q.d_bias, bias.data(), bias.size() * 4, hipMemcpyHostToDevice));
+    if (allow_bits) HIPCHECK(c, hipMemcpy(q.d_allow, allow_bits, W * 4, hipMemcpyHostToDevice));
+    HIPCHECK(c, hipMemcpy(q.d_hist, q.hist_bits.data(), W * 4, hipMemcpyHostToDevice));
+    q.rep = rep;
+    q.has_bias = n_bias > 0;
+    q.has_allow = allow_bits != nullptr;
+    q.mods_on = rep != 1.f || q.has_bias || q.has_allow;
+    return TV_OK;
+}
+
+int tv_verify_tree(tv_ctx *c, int req, const int32_t *parents, const int32_t *tokens, int n_nodes,
+                   float *logits_dev, int32_t *argmax, float *gap_ulps) {
+    if (!c) return TV_EINVAL;
+    if (!argmax) return fail(c, TV_EINVAL, "argmax output is required");
+    return run_pass(c, 1, &req, &parents, &tokens, &n_nodes, logits_dev, argmax, gap_ulps);
+}
+
+int tv_verify_trees(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parents,
+                    const int32_t *const *tokens, const int *n_nodes, float *logits_dev,
+                    int32_t *argmax, float *gap_ulps) {
+    if (!c) return TV_EINVAL;
+    if (n_req < 1 || n_req > TV_MAX_NODES || !reqs || !parents || !tokens || !n_nodes || !argmax)
+        return fail(c, TV_EINVAL, "bad joint verify arguments");
+    return run_pass(c, n_req, reqs, parents, tokens, n_nodes, logits_dev, argmax, gap_ulps);
+}
+
+int tv_accept_walk(const int32_t *parents, const int32_t *tokens, const int32_t *argmax, int n,
+                   int32_t *path, int *path_len, int32_t *emitted, int *n_emitted) {
+    if (!parents || !tokens || !argmax || !path || !path_len || !emitted || !n_emitted) return TV_EINVAL;
+    if (n < 1 || n > TV_MAX_NODES || parents[0] != -1) return TV_EINVAL;
+    for (int i = 1; i < n; ++i)
+        if (parents[i] < 0 || parents[i] >= i) return TV_EINVAL;
+    int cur = 0, len = 0;
+    path[len] = 0;
+    for (;;) {
+        const int g = argmax[cur];
+        emitted[len] = g;
+        int next = -1;
+        for (int i = cur + 1; i < n; ++i)
+            if (parents[i] == cur && tokens[i] == g) { next = i; break; }
+        ++len;
+        if (next < 0) break;
+        path[len] = next;
+        cur = next;
+    }
+    *path_len = len;
+    *n_emitted = len;
+    return TV_OK;
+}
+
+int tv_commit(tv_ctx *c, int req, const int32_t *path, int path_len) {
+    int rc = check_req(c, req);
+    if (rc) return rc;
+    Req &q = c->reqs[req];
+    if (!q.pending) return fail(c, TV_ESTATE, "request %d has no pending verify", req);
+    const int n = (int)q.pparents.size();
+    if (!path || path_len < 1 || path_len > n) return fail(c, TV_EINVAL, "path_len %d not in [1, %d]", path_len, n);
+    if (path[0] != 0) return fail(c, TV_EINVAL, "path must start at the root");
+    for (int d = 1; d < path_len; ++d)
+        if (path[d] <= 0 || path[d] >= n || q.pparents[path[d]] != path[d - 1])
+            return fail(c, TV_EINVAL, "path[%d] = %d is not a child of path[%d]", d, path[d], d - 1);
+    bool moves = false;
+    for (int d = 0; d < path_len; ++d) moves |= path[d] != d;
+    hipStream_t s = c->stream;
+    if (moves && !c->attn_layers.empty()) {
+        memcpy(c->h_path, path, path_len * sizeof(int32_t));
+        HIPCHECK(c, hipMemcpyAsync(c->d_path, c->h_path, path_len * sizeof(int32_t), hipMemcpyHostToDevice, s));
+        LAUNCH(c, "commit_kv", launch_commit_kv(s, q.d_kvtab, (int)c->attn_layers.size(), c->m.n_kvhead,
+                                                c->m.max_ctx, c->m.head_dim, q.ctx_len, c->d_path, path_len));
+    }
+    q.ctx_len += path_len;
+    for (int d = 0; d < path_len; ++d) {
+        const int t = q.ptokens[path[d]];
+        q.history.push_back(t);
+        set_bit(q.hist_bits, t);
+    }
+    if (q.mods_on && q.d_hist)
+        HIPCHECK(c, hipMemcpyAsync(q.d_hist, q.hist_bits.data(), q.hist_bits.size() * 4, hipMemcpyHostToDevice, s));
+    HIPCHECK(c, hipStreamSynchronize(s));
+    if (c->prof) harvest(c);
+    q.pending = false;
+    return TV_OK;
+}
+
+int tv_prefill(tv_ctx *c, int req, const int32_t *tokens, int n, int32_t *argmax_last) {
+    int rc = check_req(c, req);
+    if (rc) return rc;
+    if (n < 1 || !tokens) return fail(c, TV_EINVAL, "empty prompt");
+    if (c->reqs[req].ctx_len + n > c->m.max_ctx)
+        return fail(c, TV_ECAPACITY, "prompt of %d tokens does not fit", n);
+    int32_t parents[TV_MAX_NODES], path[TV_MAX_NODES], am[TV_MAX_NODES];
+    for (int i = 0; i < TV_MAX_NODES; ++i) {
+        parents[i] = i - 1;
+        path[i] = i;
+    }
+    for (int off = 0; off < n; off += TV_MAX_NODES) {
+        const int k = std::min(TV_MAX_NODES, n - off);
+        rc = tv_verify_tree(c, req, parents, tokens + off, k, nullptr, am, nullptr);
+        if (rc) return rc;
+        rc = tv_commit(c, req, path, k);
+        if (rc) return rc;
+        if (argmax_last) *argmax_last = am[k - 1];
+    }
+    return TV_OK;
+}
+
+int tv_linear(tv_ctx *c, const void *x, const void *w, int M, int N, int K, void *y, int y_fp32) {
+    if (!c) return TV_EINVAL;
+    if (!x || !w || !y) return fail(c, TV_EINVAL, "null operand");
+    if (M < 1 || M > kMaxRows || N < 1 || K < 8 || K % 8)
+        return fail(c, TV_EINVAL, "shape M=%d N=%d K=%d not supported", M, N, K);
+    if (y_fp32 && N > c->m.vocab) return fail(c, TV_EINVAL, "fp32 output needs N <= vocab");
+    GemmArgs g{};
+    g.X = (const uint16_t *)x; g.ldx = K; g.W = (const uint16_t *)w; g.M = M; g.N = N; g.K = K;
+    hipStream_t s = c->stream;
+    if (y_fp32) {
+        g.Yf = (float *)y; g.ldyf = N; g.part = c->part;
+        LAUNCH(c, "gemm_linear_f32", launch_gemm(s, EPI_HEAD, g));
+    } else {
+        g.Y = (uint16_t *)y; g.ldy = N;
+        LAUNCH(c, "gemm_linear", launch_gemm(s, EPI_BF16, g));
+    }
+    HIPCHECK(c, hipStreamSynchronize(s));
+    if (c->prof) harvest(c);
+    return TV_OK;
+}
+
+int tv_head_top2(tv_ctx *c, const void *x, int M, float *logits_dev, int32_t *argmax, float *gap) {
+    if (!c) return TV_EINVAL;
+    if (!x || !logits_dev || !argmax) return fail(c, TV_EINVAL, "null operand");
+    if (M < 1 || M > kMaxRows) return fail(c, TV_EINVAL, "M=%d not in [1, 32]", M);
+    if (!c->head) return fail(c, TV_ESTATE, "head not bound");
+    const tv_model_desc &m = c->m;
+    hipStream_t s = c->stream;
+    GemmArgs g{};
+    g.X = (const uint16_t *)x; g.ldx = m.hidden; g.W = c->head; g.M = M; g.N = m.vocab; g.K = m.hidden;
+    g.Yf = logits_dev; g.ldyf = m.vocab; g.part = c->part;
+    LAUNCH(c, "gemm_head", launch_gemm(s, EPI_HEAD, g));
+    LAUNCH(c, "top2", launch_top2_reduce(s, c->part, (m.vocab + 31) / 32, M, c->d_argmax, c->d_gap, c->d_top));
+    HIPCHECK(c, hipMemcpyAsync(c->h_argmax, c->d_argmax, M * 4, hipMemcpyDeviceToHost, s));
+    HIPCHECK(c, hipMemcpyAsync(c->h_gap, c->d_gap, M * 4, hipMemcpyDeviceToHost, s));
+    HIPCHECK(c, hipStreamSynchronize(s));
+    if (c->prof) harvest(c);
+    memcpy(argmax, c->h_argmax, M * 4);
+    if (gap) memcpy(gap, c->h_gap, M * 4);
+    return TV_OK;
+}
+
+int tv_ctx_len(tv_ctx *c, int req) {
+    int rc = check_req(c, req);
+    if (rc) return rc;
+    return c->reqs[req].ctx_len;
+}
+
+int tv_profile_enable(tv_ctx *c, int on, const char *only_prefix) {
+    if (!c) return TV_EINVAL;
+    c->prof = on != 0;
+    c->prof_only = only_prefix ? only_prefix : "";
+    return TV_OK;
+}
+
+int tv_profile_reset(tv_ctx *c) {
+    if (!c) return TV_EINVAL;
+    HIPCHECK(c, hipStreamSynchronize(c->stream));
+    harvest(c);
+    c->totals.clear();
+    return TV_OK;
+}
+
+int tv_profile_get(tv_ctx *c, const char *prefix, double *total_ms, int *count) {
+    if (!c || !prefix || !total_ms || !count) return TV_EINVAL;
+    HIPCHECK(c, hipStreamSynchronize(c->stream));
+    harvest(c);
+    double ms = 0;
+    int n = 0;
+    const size_t L = strlen(prefix);
+    for (auto &t : c->totals)
+        if (!strncmp(t.first.c_str(), prefix, L)) {
+            ms += t.second.first;
+            n += t.second.second;
+        }
+    *total_ms = ms;
+    *count = n;
+    return TV_OK;
+}
+
+} // extern "C"

@@ -1,0 +1,182 @@
+/*
+ * treeverify: the tree-verify pass of greedy speculative decoding on one
+ * MI355X (gfx950), behind a C ABI.
+ *
+ * One round ("Drafters and tree verify", The round):
+ *   tv_verify_tree  one target-model forward over a draft tree of at most 32
+ *                   nodes against the request's KV cache and recurrent state;
+ *                   fp32 logits, the argmax token and the top-1/top-2 gap at
+ *                   every node (step 2, Verify);
+ *   tv_accept_walk  the greedy walk down the tree (step 3, Accept);
+ *   tv_commit       keep the KV rows and recurrent state of the accepted path
+ *                   and drop the rest (step 4, Commit).
+ *
+ * Conventions shared by every call:
+ *   - Every call returns TV_OK (0) or a negative TV_E* code and never throws.
+ *     A failed call changes no state: validation happens before any work is
+ *     enqueued.  tv_last_error() gives a message for the last failure.
+ *   - Device memory for weights, KV caches, recurrent states and logits is
+ *     allocated by the caller and BORROWED (tv_bind); the library never frees
+ *     it.  The library allocates its own small activation scratch in
+ *     tv_create and frees it in tv_destroy.
+ *   - All device work is enqueued on the stream given to tv_create.  A call
+ *     that returns host results (argmax, gaps, path) synchronises that stream.
+ *   - Token ids are int32 in [0, vocab).  A tree is given by parents[] and
+ *     tokens[] of n_nodes entries, root included: parents[0] == -1 and
+ *     0 <= parents[i] < i (any topological order; depth-first pre-order as
+ *     the pages store it is the usual case).  tokens[0] is the root: the last
+ *     token emitted, whose KV is not cached yet.  Sibling tokens must differ
+ *     ("Algorithm and correctness contract", Target position and batching).
+ *   - Row i of a verify is the model's scores after consuming the path
+ *     root..i, at position ctx_len + depth(i) ("Drafters and tree verify",
+ *     Tree verify through recurrent layers: attention sees its ancestors
+ *     and a position equal to its depth).
+ *   - A verify writes the tree's KV rows at cache slots ctx_len + i but does
+ *     not move ctx_len; only tv_commit does.  Verifying again without a commit
+ *     discards the previous tree.
+ */
+#ifndef TREEVERIFY_H
+#define TREEVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TV_OK 0
+#define TV_EINVAL (-1)    /* bad argument, tree, path, name or size */
+#define TV_ECAPACITY (-2) /* ctx_len + rows would exceed max_ctx */
+#define TV_ESTATE (-3)    /* commit with no pending verify; unbound tensors */
+#define TV_EHIP (-4)      /* a HIP runtime call failed (message in tv_last_error) */
+
+#define TV_MAX_NODES 32   /* rows of one pass, all requests together */
+
+#define TV_LAYER_ATTN 0   /* grouped-query attention layer with RoPE */
+#define TV_LAYER_RECUR 1  /* gated linear recurrence layer */
+
+/* Shapes of the target model.  Every weight matrix is [N_out, K_in]
+ * row-major bf16.  An attention layer's wqkv stacks n_qhead, then n_kvhead,
+ * then n_kvhead heads of head_dim rows; a recurrent layer's wqkv stacks q, k
+ * and v with n_qhead heads each, and its wa is [n_qhead, hidden]. */
+typedef struct tv_model_desc {
+    int n_layer;
+    int hidden;
+    int n_qhead;
+    int n_kvhead;
+    int head_dim;       /* 64 or 128 */
+    int ffn;
+    int vocab;
+    const int *layer_kind; /* [n_layer], TV_LAYER_* (copied) */
+    float eps;          /* RMSNorm and L2-norm epsilon */
+    float rope_theta;
+    int max_ctx;        /* KV cache rows per request, tree rows included */
+    int max_req;        /* requests (independent caches) */
+} tv_model_desc;
+
+typedef struct tv_ctx tv_ctx;
+
+/* Create a context; `stream` is a hipStream_t (NULL = the null stream). */
+int tv_create(const tv_model_desc *m, void *stream, tv_ctx **out);
+void tv_destroy(tv_ctx *ctx);
+const char *tv_last_error(tv_ctx *ctx);
+
+/* Bind a caller-owned device buffer by name.  `bytes` must equal the
+ * tensor's size.  Names and layouts:
+ *   "emb" [vocab, hidden] bf16        "head" [vocab, hidden] bf16
+ *   "final_norm" [hidden] bf16
+ *   "layers.L.attn_norm", "layers.L.ffn_norm" [hidden] bf16
+ *   "layers.L.wqkv", "layers.L.wo", "layers.L.wa" (recurrent only),
+ *   "layers.L.wg", "layers.L.wu" [ffn, hidden], "layers.L.wd" [hidden, ffn]
+ *   "req.R.layers.L.k", "req.R.layers.L.v"  [n_kvhead, max_ctx, head_dim] bf16
+ *   "req.R.layers.L.state"                  [n_qhead, head_dim, head_dim] fp32
+ *     (state[h][i][j]: key index i, value index j)                          */
+int tv_bind(tv_ctx *ctx, const char *name, void *dev_ptr, size_t bytes);
+
+/* Declare request `req`'s committed context: ctx_len cache rows already
+ * hold its keys (already rotated) and values, and its recurrent states are
+ * the bound ones.  `ids` (n_ids tokens, may be NULL) is the text those rows
+ * stand for, used only by the repetition penalty.  Drops any pending tree. */
+int tv_set_history(tv_ctx *ctx, int req, const int32_t *ids, int n_ids, int ctx_len);
+
+/* Score modifiers of request `req`, applied to every verified row as plain
+ * decoding applies them to its one row ("Exactness", The promise): first a
+ * repetition penalty theta over the row's prior tokens (history, committed
+ * tokens and the row's own path; l > 0 -> l/theta, else l*theta), then
+ * logit_bias, then the allow-mask (bit v of allow_bits[v/32]; disallowed ids
+ * never win).  rep_penalty == 1, n_bias == 0 and allow_bits == NULL turn
+ * each off.  The returned logits stay the raw fp32 values; argmax and gap
+ * use the modified scores. */
+int tv_set_modifiers(tv_ctx *ctx, int req, float rep_penalty, const int32_t *bias_ids,
+                     const float *bias_vals, int n_bias, const uint32_t *allow_bits);
+
+/* Prefill: forward `n` prompt tokens as chains of at most 32 through the
+ * verify path, committing each chain whole (the prefill chunk grid,
+ * "Exactness", Caches).  *argmax_last (may be NULL) gets the argmax after
+ * the last token: the first token to emit. */
+int tv_prefill(tv_ctx *ctx, int req, const int32_t *tokens, int n, int32_t *argmax_last);
+
+/* Verify one tree for request `req`.  logits_dev: device fp32 [n_nodes,
+ * vocab] (may be NULL: then logits go to library scratch).  argmax (int32)
+ * and gap_ulps (float, may be NULL) are host arrays of n_nodes.  gap_ulps[i]
+ * = (top1 - top2) / ulp_bf16(top1) with ulp_bf16(x) = 2^(floor(log2|x|)-7)
+ * ("Exactness", The one exception: near ties); +inf when only one id is
+ * allowed. */
+int tv_verify_tree(tv_ctx *ctx, int req, const int32_t *parents, const int32_t *tokens,
+                   int n_nodes, float *logits_dev, int32_t *argmax, float *gap_ulps);
+
+/* Verify n_req trees of distinct requests in one pass ("Exactness",
+ * Parallel requests); the sum of n_nodes must be <= 32.  Rows are laid out
+ * request after request in the order given.  Each request's rows equal what
+ * its own tv_verify_tree gives, bit for bit. */
+int tv_verify_trees(tv_ctx *ctx, int n_req, const int *reqs, const int32_t *const *parents,
+                    const int32_t *const *tokens, const int *n_nodes, float *logits_dev,
+                    int32_t *argmax, float *gap_ulps);
+
+/* The greedy accept walk, host only, integers only: from the root take the
+ * model's token argmax[cur] and move to the child carrying it; stop where
+ * none does, keeping the model's token there ("Drafters and tree verify",
+ * The round, step 3).  path (node ids, root first) and emitted (tokens) are
+ * host arrays of at least n_nodes; *path_len == *n_emitted >= 1. */
+int tv_accept_walk(const int32_t *parents, const int32_t *tokens, const int32_t *argmax,
+                   int n_nodes, int32_t *path, int *path_len, int32_t *emitted, int *n_emitted);
+
+/* Commit the accepted path of request `req`'s pending tree: path[0] == 0
+ * and each path[d] a child of path[d-1].  KV rows move from slot
+ * ctx_len+path[d] to ctx_len+d ("Drafters and tree verify", Tree verify
+ * through recurrent layers: the cache holds every node at its depth-first
+ * slot and the commit gathers the accepted rows into place); each recurrent
+ * state becomes the state after the path, from the quantities the verify
+ * computed (same section, the closed form of S_path).  ctx_len grows by
+ * path_len; the path's tokens join the history. */
+int tv_commit(tv_ctx *ctx, int req, const int32_t *path, int path_len);
+
+/* Committed context length of request `req` (negative TV_E* on error). */
+int tv_ctx_len(tv_ctx *ctx, int req);
+
+/* Kernel-level calls: the pass's projection and head kernels on caller-given
+ * device operands, for per-kernel tests and bandwidth measurement.
+ * tv_linear: x [M, K] bf16 (row-major), w [N, K] bf16, M in [1, 32], K a
+ * multiple of 8; y_fp32 == 0 writes bf16(x w^T) to y [M, N] bf16, y_fp32 != 0
+ * writes the fp32 sums to y [M, N] fp32 (N <= vocab).  The k order of every
+ * output is fixed by K alone, as in the pass.
+ * tv_head_top2: the bound "head" on x [M, hidden] bf16: fp32 logits [M,
+ * vocab] to logits_dev, argmax and gap (host, M entries) as tv_verify_tree
+ * returns them, with no score modifiers.  Both synchronise the stream. */
+int tv_linear(tv_ctx *ctx, const void *x, const void *w, int M, int N, int K, void *y, int y_fp32);
+int tv_head_top2(tv_ctx *ctx, const void *x, int M, float *logits_dev, int32_t *argmax, float *gap_ulps);
+
+/* Kernel timing: with `on` != 0, launches whose kernel name starts with
+ * `only_prefix` (all launches when it is NULL or "") are bracketed by HIP
+ * events on the context's stream.  tv_profile_get returns the total
+ * milliseconds and the launch count recorded for names starting with
+ * `prefix` since the last reset (it synchronises the stream). */
+int tv_profile_enable(tv_ctx *ctx, int on, const char *only_prefix);
+int tv_profile_reset(tv_ctx *ctx);
+int tv_profile_get(tv_ctx *ctx, const char *prefix, double *total_ms, int *count);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

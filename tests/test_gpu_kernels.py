@@ -1,0 +1,148 @@
+"""Per-kernel parity of the skinny GEMM and the fp32 head (MI355X only).
+
+Inputs are seeded synthetic bf16 operands from ``synth``'s generator; the
+expected values are the oracle's fp64 dot products.
+
+* fp32 outputs: |y - y64| <= gamma_K * sum_k |x_k w_k| (Higham's bound for a
+  length-K fp32 sum, gamma_K = K u / (1 - K u), u = 2^-24), and the north
+  star's 1e-5 relative bound for the head accumulation.
+* bf16 outputs: equal to the fp64 value rounded to bf16, except where the
+  fp64 value lies within the fp32 error bound of a rounding boundary.
+* Row invariance ("Exactness", The one exception: near ties, and Parallel
+  requests): a row's result is bit-identical for every row count 1..32 and
+  every row slot.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def tv():
+    _gpu()
+    from greedy_draft_tree_amd import TreeVerifier
+    s = torch.cuda.current_stream().cuda_stream
+    t = TreeVerifier.for_shape(synth.C1, max_ctx=64, max_req=1, stream=s)
+    return t
+
+
+def _ref(x_bf16, w_bf16):
+    """fp64 products and the sum of |terms| per output, via the oracle's
+    plain matvec."""
+    m = oracle.Oracle.__new__(oracle.Oracle)
+    m.lib = oracle._load()
+    m.W = {"w": oracle.t2u16(w_bf16.cpu())}
+    wa = w_bf16.cpu().to(torch.float64).abs()
+    m.W["wa"] = oracle.t2u16(wa.to(torch.bfloat16))  # |w| is exact in bf16
+    x = x_bf16.cpu().to(torch.float64).numpy()
+    y = np.stack([m.matvec("w", x[i]) for i in range(x.shape[0])])
+    a = np.stack([m.matvec("wa", np.abs(x[i])) for i in range(x.shape[0])])
+    return y, a
+
+
+def _operands(M, N, K, seed, xstd=1.0):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    x = (torch.randn(M, K, generator=g, device="cuda") * xstd).to(torch.bfloat16)
+    w = (torch.randn(N, K, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    return x, w
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (7, 1000, 688), (32, 7168, 5120), (13, 5120, 17408),
+                                   (32, 33, 5128), (5, 40, 5120)])
+def test_linear_fp32_within_higham_bound(tv, M, N, K):
+    x, w = _operands(M, N, K, M * 7 + N)
+    y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    tv.linear(x, w, y)
+    ref, absum = _ref(x, w)
+    gam = K * U / (1 - K * U)
+    err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+    assert (err <= gam * absum + 1e-30).all(), float((err / (gam * absum + 1e-30)).max())
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 512, 256), (32, 7168, 5120), (9, 17408, 5120)])
+def test_linear_bf16_is_correctly_rounded(tv, M, N, K):
+    x, w = _operands(M, N, K, 100 + M)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tv.linear(x, w, y)
+    ref, absum = _ref(x, w)
+    want = oracle.bf16_round(ref)
+    got = y.cpu().to(torch.float64).numpy()
+    gam = K * U / (1 - K * U)
+    # where rounding differs, the fp64 value must sit within the fp32 bound of
+    # the midpoint between the two bf16 neighbours
+    bad = got != want
+    mid = (got + want) / 2
+    near = np.abs(ref - mid) <= gam * absum + 2 * U * np.abs(ref)
+    assert (~bad | near).all(), int((bad & ~near).sum())
+    assert bad.mean() < 1e-3
+
+
+def test_linear_rows_bitwise_invariant(tv):
+    N, K = 4096, 5120
+    x, w = _operands(32, N, K, 5)
+    full = torch.empty(32, N, dtype=torch.float32, device="cuda")
+    tv.linear(x, w, full)
+    rng = np.random.default_rng(0)
+    for M in (1, 2, 5, 8, 16, 17, 24, 31, 32):
+        perm = rng.permutation(32)[:M]
+        xs = x[torch.from_numpy(perm).cuda()].contiguous()
+        y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+        tv.linear(xs, w, y)
+        assert torch.equal(y, full[torch.from_numpy(perm).cuda()]), M
+        yb = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        tv.linear(xs, w, yb)
+        assert torch.equal(yb, full[torch.from_numpy(perm).cuda()].to(torch.bfloat16)), M
+
+
+@pytest.fixture(scope="module")
+def head(tv):
+    w = synth.weights(synth.C1, seed=0, device="cuda", only=["head"])["head"]
+    tv.bind("head", w)
+    return w
+
+
+def test_head_top2_c1(tv, head):
+    M = 32
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn(M, synth.C1.hidden, generator=g, device="cuda").to(torch.bfloat16)
+    logits = torch.empty(M, synth.C1.vocab, dtype=torch.float32, device="cuda")
+    am, gap = tv.head_top2(x, logits)
+    gl = logits.cpu().numpy().astype(np.float64)
+    ref, absum = _ref(x, head)
+    K = synth.C1.hidden
+    gam = K * U / (1 - K * U)
+    err = np.abs(gl - ref)
+    assert (err <= gam * absum).all()
+    # spec head bound: 1e-5 relative (to the row's largest |logit|)
+    assert (err.max(axis=1) <= 1e-5 * np.abs(ref).max(axis=1)).all()
+    for i in range(M):
+        a, l1, l2, g2 = oracle.top2(gl[i])
+        assert am[i] == a and gap[i] == np.float32(g2)
+        a64, _, _, g64 = oracle.top2(oracle.f32(ref[i]))
+        assert am[i] == a64 or g64 <= 1.0
+
+
+def test_head_rows_bitwise_invariant(tv, head):
+    g = torch.Generator(device="cuda").manual_seed(12)
+    x = torch.randn(32, synth.C1.hidden, generator=g, device="cuda").to(torch.bfloat16)
+    full = torch.empty(32, synth.C1.vocab, dtype=torch.float32, device="cuda")
+    am_full, gap_full = tv.head_top2(x, full)
+    for M, rows in ((1, [31]), (8, list(range(8, 16))), (3, [30, 0, 17])):
+        xs = x[rows].contiguous()
+        out = torch.empty(M, synth.C1.vocab, dtype=torch.float32, device="cuda")
+        am, gap = tv.head_top2(xs, out)
+        assert torch.equal(out, full[rows])
+        np.testing.assert_array_equal(am, am_full[rows])
+        np.testing.assert_array_equal(gap, gap_full[rows])

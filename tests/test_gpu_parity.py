@@ -1,0 +1,279 @@
+"""Parity of the HIP tree verify with the CPU oracle (MI355X only).
+
+Bars (spec acceptance): token and index outputs bit-exact, except
+where the oracle's top-2 gap is at most 1 bf16 ulp ("Exactness", The one
+exception: near ties); logits within 2e-2 absolute end to end (bf16
+activations).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_ATOL = 2e-2
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def check_rows(gpu_logits, gpu_argmax, gpu_gap, orc_logits, parents, tokens, history, mods=None,
+               what="", orc_exact=None):
+    """Logits close to the oracle's; the GPU's argmax and gap are exactly
+    those of its own fp32 logits; its argmax equals the oracle's unless the
+    oracle's gap is <= 1 ulp.
+
+    Logit bound per row: LOGIT_ATOL, or, when the oracle's unrounded (exact)
+    logits are given, the larger of LOGIT_ATOL and the spread that bf16
+    activation rounding itself puts on that row (max |rounded - exact|): a
+    tiny fp32 difference that lands on a bf16 rounding boundary is carried
+    forward ("Exactness", The one exception: near ties), so two correct
+    bf16 computations differ by about the rounding's own effect."""
+    n = len(parents)
+    diff = np.abs(gpu_logits[:n].astype(np.float64) - orc_logits[:n])
+    tol = np.full(n, LOGIT_ATOL)
+    if orc_exact is not None:
+        tol = np.maximum(tol, np.abs(orc_logits[:n] - orc_exact[:n]).max(axis=1))
+    worst = (diff.max(axis=1) / tol).max()
+    print(f"[{what}] max|dlogit| {diff.max():.4g} rms {np.sqrt((diff ** 2).mean()):.3g} "
+          f"tol {tol.min():.3g}..{tol.max():.3g}", flush=True)
+    assert worst <= 1.0, f"{what}: max |dlogit| {diff.max():.3g} over tolerance {tol.min():.3g}"
+    own_am, own_gap = oracle.tree_decisions(gpu_logits[:n].astype(np.float64), parents, tokens,
+                                            history, mods)
+    np.testing.assert_array_equal(gpu_argmax[:n], own_am, err_msg=f"{what}: argmax vs own logits")
+    np.testing.assert_array_equal(gpu_gap[:n], own_gap.astype(np.float32),
+                                  err_msg=f"{what}: gap vs own logits")
+    am, gap = oracle.tree_decisions(orc_logits, parents, tokens, history, mods)
+    ties = 0
+    for i in range(n):
+        if gpu_argmax[i] != am[i]:
+            assert gap[i] <= 1.0, f"{what}: row {i} argmax {gpu_argmax[i]} vs {am[i]} at gap {gap[i]:.3f} ulp"
+            ties += 1
+    return am, gap, ties
+
+
+# ------------------------------------------------------------------ C0
+
+@pytest.fixture(scope="module")
+def c0():
+    _gpu()
+    import workloads
+    wl = workloads.build(synth.C0, max_ctx=512, max_req=2, weight_device="cuda")
+    w_cpu = {k: v.cpu() for k, v in wl.weights.items()}
+    return wl, oracle.Oracle(synth.C0, w_cpu)
+
+
+def test_c0_prefill_and_tree_rows(c0):
+    wl, orc = c0
+    prompt = synth.uniform_ids(64, synth.C0.vocab, 1)
+    _say("c0 prefill 63 + tree")
+    wl.tv.set_history(0, [], 0)
+    first = wl.tv.prefill(0, prompt[:-1])
+    seq = orc.new_seq(cap=512)
+    last = seq.commit(prompt[:-1])
+    a, _, _, g = oracle.top2(last)
+    assert first == a or g <= 1.0
+    assert wl.tv.ctx_len(0) == 63
+    for seed, parents in [(2, synth.c0_tree()), (3, synth.spine_tree(32, 3)), (4, synth.chain_tree(1)),
+                          (5, synth.bush_tree(17)), (6, synth.random_tree(29, 6))]:
+        tokens = synth.tree_tokens(parents, synth.C0.vocab, seed, root_token=int(prompt[-1]))
+        _say("c0 tree", seed, len(parents))
+        am, gap = wl.tv.verify_tree(0, parents, tokens, logits=wl.logits)
+        gl = wl.logits[:len(parents)].cpu().numpy()
+        ol = orc.tree_scores(seq, parents, tokens)
+        check_rows(gl, am, gap, ol, parents, tokens, seq.history, what=f"c0 tree {seed}")
+
+
+def _greedy_drafter(orc, seq, root, parents, rng, r):
+    spine = synth.spine_nodes(parents)
+    s = orc.new_seq(cap=seq.cap)
+    s.commit(seq.history)
+    cont = oracle.greedy(s, root, len(spine) - 1)[0]
+    forced = {}
+    for d, node in enumerate(spine[1:]):
+        if rng.random() < 0.7:
+            forced[node] = cont[d]
+        else:
+            break
+    return synth.tree_tokens(parents, orc.s.vocab, 1000 + r, root, forced)
+
+
+def test_c0_32_greedy_rounds(c0):
+    """32 rounds of verify -> walk -> commit against the oracle; the emitted
+    text equals sequential greedy decoding up to near ties (after an allowed
+    divergence the oracle follows the GPU's text)."""
+    wl, orc = c0
+    prompt = synth.uniform_ids(64, synth.C0.vocab, 1)
+    wl.tv.set_history(1, [], 0)
+    root = wl.tv.prefill(1, prompt[:-1])
+    seq = orc.new_seq(cap=512)
+    seq.commit(prompt[:-1])
+    root = int(prompt[-1])
+    parents = synth.c0_tree()
+    rng = np.random.default_rng(7)
+    emitted_total, multi = 0, 0
+    for r in range(32):
+        tokens = _greedy_drafter(orc, seq, root, parents, rng, r)
+        am, gap = wl.tv.verify_tree(1, parents, tokens, logits=wl.logits)
+        ol = orc.tree_scores(seq, parents, tokens)
+        check_rows(wl.logits[:8].cpu().numpy(), am, gap, ol, parents, tokens, seq.history,
+                   what=f"c0 round {r}")
+        path, emitted = oracle.accept_walk(parents, tokens, am)
+        path2, emitted2 = __import__("greedy_draft_tree_amd").accept_walk(parents, tokens, am)
+        assert (path, emitted) == (path2, emitted2)
+        wl.tv.commit(1, path)
+        seq.commit([int(tokens[i]) for i in path])
+        assert wl.tv.ctx_len(1) == seq.ctx_len
+        emitted_total += len(emitted)
+        multi += len(emitted) > 1
+        root = emitted[-1]
+    assert emitted_total >= 32 and multi > 0
+
+
+def test_c0_wrong_drafter_one_token_per_round(c0):
+    wl, orc = c0
+    prompt = synth.uniform_ids(40, synth.C0.vocab, 2)
+    wl.tv.set_history(0, [], 0)
+    wl.tv.prefill(0, prompt[:-1])
+    seq = orc.new_seq(cap=512)
+    seq.commit(prompt[:-1])
+    root = int(prompt[-1])
+    parents = synth.c0_tree()
+    out = []
+    for r in range(6):
+        # every child of the root carries a token other than the model's own
+        s = orc.new_seq(cap=512)
+        s.commit(seq.history)
+        want = oracle.top2(s.step(root))[0]
+        tokens = synth.tree_tokens(parents, synth.C0.vocab, 50 + r, root)
+        for i in range(1, len(parents)):
+            if parents[i] == 0 and tokens[i] == want:
+                tokens[i] = (want + 1 + i) % synth.C0.vocab
+        am, gap = wl.tv.verify_tree(0, parents, tokens)
+        path, emitted = oracle.accept_walk(parents, tokens, am)
+        assert len(emitted) == 1 and path == [0]
+        wl.tv.commit(0, path)
+        seq.commit([root])
+        out.append(emitted[0])
+        root = emitted[0]
+    ref = orc.new_seq(cap=512)
+    ref.commit(prompt[:-1])
+    want, gaps = oracle.greedy(ref, int(prompt[-1]), 6)
+    for i, (a, b) in enumerate(zip(out, want)):
+        if a != b:
+            assert gaps[i] <= 1.0
+            break
+
+
+def test_c0_commit_gathers_rows_bitwise(c0):
+    wl, orc = c0
+    prompt = synth.uniform_ids(20, synth.C0.vocab, 9)
+    wl.tv.set_history(0, [], 0)
+    wl.tv.prefill(0, prompt)
+    ctx = wl.tv.ctx_len(0)
+    parents = synth.spine_tree(16, 9)
+    tokens = synth.tree_tokens(parents, synth.C0.vocab, 9, root_token=3)
+    wl.tv.verify_tree(0, parents, tokens)
+    torch.cuda.synchronize()
+    before = {k: v[:, ctx:ctx + 16].clone() for k, v in wl.kv[0].items()}
+    # a path down the spine with a leaf at the end
+    spine = synth.spine_nodes(parents)
+    path = spine[:4]
+    leaf = [i for i in range(1, 16) if parents[i] == path[-1] and i not in spine]
+    if leaf:
+        path = path + [leaf[0]]
+    wl.tv.commit(0, path)
+    torch.cuda.synchronize()
+    for k, v in wl.kv[0].items():
+        for d, node in enumerate(path):
+            assert torch.equal(v[:, ctx + d], before[k][:, node]), (k, d, node)
+    assert wl.tv.ctx_len(0) == ctx + len(path)
+
+
+def test_c0_rows_independent_of_pass(c0):
+    """A row's logits are bit-identical alone, inside a wider chain, and in a
+    joint pass with another request ("Exactness", Parallel requests;
+    "Drafters and tree verify", The length router: row i does not depend on
+    rows after i)."""
+    wl, orc = c0
+    p = synth.uniform_ids(30, synth.C0.vocab, 4)
+    for r in (0, 1):
+        wl.tv.set_history(r, [], 0)
+        wl.tv.prefill(r, p[:20 + 5 * r])
+    chain = synth.uniform_ids(24, synth.C0.vocab, 5)
+    wl.tv.verify_tree(0, synth.chain_tree(24), chain, logits=wl.logits)
+    wide = wl.logits[:24].clone()
+    wl.tv.verify_tree(0, synth.chain_tree(7), chain[:7], logits=wl.logits)
+    narrow = wl.logits[:7].clone()
+    assert torch.equal(wide[:7], narrow)
+    tree = synth.spine_tree(16, 1)
+    tt = synth.tree_tokens(tree, synth.C0.vocab, 6, root_token=11)
+    other = synth.spine_tree(16, 2)
+    ot = synth.tree_tokens(other, synth.C0.vocab, 7, root_token=12)
+    wl.tv.verify_tree(0, tree, tt, logits=wl.logits)
+    alone = wl.logits[:16].clone()
+    wl.tv.verify_trees([1, 0], [other, tree], [ot, tt], logits=wl.logits)
+    joint = wl.logits[16:32].clone()
+    assert torch.equal(alone, joint)
+    # bitwise repeatable
+    wl.tv.verify_tree(0, tree, tt, logits=wl.logits)
+    assert torch.equal(alone, wl.logits[:16])
+
+
+def test_c0_errors_leave_state(c0):
+    from greedy_draft_tree_amd import TVError, TV_EINVAL, TV_ECAPACITY, TV_ESTATE
+    wl, _ = c0
+    wl.tv.set_history(0, [], 500)
+    with pytest.raises(TVError) as e:
+        wl.tv.verify_tree(0, synth.chain_tree(16), list(range(16)))
+    assert e.value.code == TV_ECAPACITY
+    assert wl.tv.ctx_len(0) == 500
+    with pytest.raises(TVError) as e:
+        wl.tv.commit(0, [0])
+    assert e.value.code == TV_ESTATE
+    with pytest.raises(TVError) as e:
+        wl.tv.verify_tree(0, [-1, 0, 0], [1, 2, 2])
+    assert e.value.code == TV_EINVAL
+
+
+# ------------------------------------------------------------------ C1
+
+@pytest.fixture(scope="module")
+def c1():
+    _gpu()
+    import workloads
+    wl = workloads.build(synth.C1, max_ctx=8192 + 64, max_req=2, weight_device="cuda")
+    w_cpu = {k: v.cpu() for k, v in wl.weights.items()}
+    orc = oracle.Oracle(synth.C1, w_cpu)
+    orc.w_src = w_cpu
+    return wl, orc
+
+
+@pytest.mark.parametrize("n,ctx", [(8, 1024), (16, 1024), (24, 1024), (32, 1024), (16, 8192)])
+def test_c1_tree_rows(c1, n, ctx):
+    import workloads
+    wl, orc = c1
+    _say("c1", n, ctx)
+    kv = synth.kv_cache(synth.C1, ctx, seed=3, cap=ctx)
+    hist = synth.uniform_ids(ctx, synth.C1.vocab, 30)
+    workloads.load_context(wl, 0, ctx, 3, history=hist, src_kv={k: v.cuda() for k, v in kv.items()})
+    seq = orc.new_seq(cap=ctx + 32, kv=kv, ctx_len=ctx, history=hist)
+    parents = synth.spine_tree(n, 4)
+    tokens = synth.tree_tokens(parents, synth.C1.vocab, 5 + n, root_token=int(hist[-1]))
+    am, gap = wl.tv.verify_tree(0, parents, tokens, logits=wl.logits)
+    gl = wl.logits[:n].cpu().numpy()
+    ol = orc.tree_scores(seq, parents, tokens)
+    ex = oracle.Oracle(synth.C1, orc.w_src, exact=True)
+    oe = ex.tree_scores(ex.new_seq(cap=ctx + 32, kv=kv, ctx_len=ctx, history=hist), parents, tokens)
+    _, _, ties = check_rows(gl, am, gap, ol, parents, tokens, seq.history, what=f"c1 n={n} ctx={ctx}",
+                            orc_exact=oe)
+    print(f"[c1 n={n} ctx={ctx}] near-tie argmax differences: {ties}", flush=True)
