@@ -86,7 +86,9 @@ def main():
     torch.cuda.init()
     dev = torch.cuda.current_device()
     print(f"[bench] building {shape.name} ctx={ctx}", file=sys.stderr, flush=True)
-    wl = workloads.build(shape, max_ctx=ctx + 64, max_req=1, weight_device="cuda")
+    want_cpu = not a.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0
+    wl = workloads.build(shape, max_ctx=ctx + 64, max_req=1, weight_device="cuda",
+                         host_copy=want_cpu)
     kv = workloads.load_context(wl, 0, ctx, seed=3)
     tv = wl.tv
     from greedy_draft_tree_amd import accept_walk
@@ -171,7 +173,7 @@ def main():
         tv.profile_enable(False)
 
     cpu = None
-    if not a.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
+    if want_cpu:
         cpu = cpu_baseline(shape, wl, kv, ctx, trees, a.cpu_sample)
 
     out = {
@@ -209,8 +211,7 @@ def cpu_baseline(shape, wl, kv, ctx, trees, sample):
     """The CPU oracle (brute-force tree scorer) on the same trees."""
     import torch
     import oracle
-    print("[bench] cpu baseline: copying weights to host", file=sys.stderr, flush=True)
-    w_cpu = {k: v.cpu() for k, v in wl.weights.items()}
+    w_cpu = wl.host_weights
     kv_cpu = {k: v[:, :ctx].cpu() for k, v in kv.items()}
     orc = oracle.Oracle(shape, w_cpu)
     seq = orc.new_seq(cap=ctx + 40, kv=kv_cpu, ctx_len=ctx)

@@ -19,7 +19,7 @@ _lib = None
 SYMBOLS = ("tv_create", "tv_destroy", "tv_last_error", "tv_bind", "tv_set_history",
            "tv_set_modifiers", "tv_prefill", "tv_verify_tree", "tv_verify_trees",
            "tv_accept_walk", "tv_commit", "tv_ctx_len", "tv_profile_enable",
-           "tv_profile_reset", "tv_profile_get", "tv_linear", "tv_head_top2")
+           "tv_profile_reset", "tv_profile_get", "tv_linear", "tv_head_top2", "tv_pack_weight")
 
 
 class TVError(RuntimeError):
@@ -67,6 +67,7 @@ def load_library():
         "tv_profile_get": ([P, ctypes.c_char_p, P, P], I),
         "tv_linear": ([P, P, P, I, I, I, P, I], I),
         "tv_head_top2": ([P, P, I, P, P, P], I),
+        "tv_pack_weight": ([P, P, I, I], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -226,7 +227,8 @@ class TreeVerifier:
         return rc
 
     def linear(self, x, w, y) -> None:
-        """tv_linear: y = x w^T (bf16 out if y is bf16, fp32 sums if y is fp32)."""
+        """tv_linear: y = x w^T (bf16 out if y is bf16, fp32 sums if y is fp32);
+        w must have been packed with pack_weight."""
         M, K = x.shape
         N = w.shape[0]
         assert w.shape[1] == K and tuple(y.shape) == (M, N)
@@ -237,6 +239,12 @@ class TreeVerifier:
         self._check(self.lib.tv_linear(self.h, ctypes.c_void_p(x.data_ptr()),
                                        ctypes.c_void_p(w.data_ptr()), M, N, K,
                                        ctypes.c_void_p(y.data_ptr()), fp32), "tv_linear")
+
+    def pack_weight(self, w) -> None:
+        """tv_pack_weight: rearrange a row-major [N, K] bf16 tensor in place."""
+        N, K = w.shape
+        self._check(self.lib.tv_pack_weight(self.h, ctypes.c_void_p(w.data_ptr()), N, K),
+                    "tv_pack_weight")
 
     def head_top2(self, x, logits):
         """tv_head_top2 on x [M, hidden] bf16 -> (argmax, gap)."""

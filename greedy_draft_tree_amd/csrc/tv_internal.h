@@ -55,7 +55,18 @@ struct GemmArgs {
     Top2 *part;         // head: [ceil(N/32)][32] per-tile candidates
     const PassMeta *meta; // head modifiers (null: none)
     int mods_on;
+    float *partial;     // split-K partial tiles (splits > 1)
 };
+
+// k-range splits of a GEMM: a function of the weight shape only.
+inline int gemm_splits(int N, int K) {
+    const int rowblocks = ((N + 31) / 32 + 3) / 4;
+    const int nsteps = (K + 63) / 64;
+    int s = (512 + rowblocks - 1) / rowblocks;
+    const int most = nsteps / 4 > 1 ? nsteps / 4 : 1;   // at least 4 k steps per split
+    if (s > most) s = most;
+    return s < 1 ? 1 : s;
+}
 
 struct AttnArgs {
     const uint16_t *Q;  // rotated queries, rows row0.., [rows, n_qhead*D]
@@ -83,7 +94,9 @@ hipError_t launch_embed(hipStream_t s, const uint16_t *emb, const PassMeta *meta
                         uint16_t *X);
 hipError_t launch_rmsnorm(hipStream_t s, const uint16_t *X, const uint16_t *w, int M, int H,
                           float eps, uint16_t *Y);
-hipError_t launch_gemm(hipStream_t s, int epi, const GemmArgs &a);
+hipError_t launch_gemm(hipStream_t s, int epi, const GemmArgs &a, int splits);
+hipError_t launch_splitk_reduce(hipStream_t s, int epi, const GemmArgs &a, int splits);
+hipError_t launch_pack(hipStream_t s, const uint16_t *src, uint16_t *dst, int N, int K, int t0, int nt);
 hipError_t launch_rope_kv(hipStream_t s, const RopeArgs &a);
 hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a);
 hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t *out);

@@ -11,6 +11,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "tv_internal.h"
 
 namespace tv {
@@ -106,86 +108,42 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t *__restrict__ X,
 // ------------------------------------------------------------ skinny GEMM
 // Y[m, n] = sum_k X[m, k] W[n, k] for M <= 32 activation rows.
 //
-// One workgroup owns a 32-row tile of W and splits K between its WK waves;
-// each wave streams its weight rows with 16-byte loads and feeds
-// v_mfma_f32_32x32x16_bf16 with weights as the A operand (row = lane%32) and
-// activations as B (column = lane%32, zero beyond M).  A lane covers 32
-// consecutive k of its row per 64-wide step (two lanes read one 128-byte
-// line), which fixes the k order of every output by K alone: M only decides
-// which B columns are zero, so a row's result does not depend on how many
-// other rows share the pass, nor on its column slot.  The WK partial tiles
-// are summed in wave order through LDS.
-template <int EPI, int WK>
-__global__ __launch_bounds__(64 * WK) void k_gemm(GemmArgs g) {
-    constexpr bool DUAL = (EPI == EPI_SWIGLU);
-    constexpr int U = DUAL ? 2 : 4;   // 64-wide k steps loaded per burst
-    constexpr int NACC = DUAL ? 2 : 1;
-    __shared__ float red[(WK > 1 ? WK - 1 : 1) * NACC * 16 * 64];
+// Weights are stored packed (see k_pack): a tile of 32 rows is cut into
+// 64-wide k steps, and a full step is 4 KB laid out so that load q of lane l
+// reads bytes [1024q + 16l, +16): the 8 k values [32*(l/32) + 8q, +8) of row
+// l%32, exactly v_mfma_f32_32x32x16_bf16's A operand (row = lane%32).  Every
+// weight load is then one contiguous 1 KB per wave.
+//
+// A workgroup of 4 waves owns 4 consecutive tiles (128 rows) and one of S
+// k-ranges; the activations of each step (32 x 64 bf16, zero beyond M) are
+// staged once in LDS (XOR-swizzled 16-byte chunks, conflict-free reads) and
+// shared by the 4 waves as the B operand (column = lane%32).  With S > 1 each
+// workgroup writes its fp32 partial tile and k_splitk_reduce adds the S
+// partials in k-range order and applies the epilogue.
+// S depends on the weight shape only, and the k order of every output is
+// fixed by K: M only decides which B columns are zero, so a row's result is
+// the same for any row count and any row slot.
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Element offset, inside a packed tile, of the 8-element piece (q, hf) of
+// row c at step s; -1 when the piece lies beyond K or the row beyond N.
+__device__ __forceinline__ long packed_piece(int s, int q, int hf, int c, int nr, int K) {
+    const int kr = min(64, K - 64 * s);
+    if (c >= nr || 32 * hf + 8 * q >= kr) return -1;
+    const int pi = 2 * q + hf;
+    int rank = 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+        rank += (p < pi && 32 * (p & 1) + 8 * (p >> 1) < kr) ? 1 : 0;
+    return (long)64 * s * nr + (long)rank * nr * 8 + c * 8;
+}
+
+// Epilogue of one 32x32 output tile held in MFMA accumulator layout.
+template <int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, int tile, int lane, const f32x16 &acc,
+                                              const f32x16 &acc2) {
     const int hf = lane >> 5, c = lane & 31;
-    const int tile = blockIdx.x;
-    const int row = tile * 32 + c;
-    const int K = g.K;
-    const int nsteps = (K + 63) >> 6;
-    const int s0 = (nsteps * wave) / WK, s1 = (nsteps * (wave + 1)) / WK;
-    const bool rok = row < g.N;
+    const int m = c, N = g.N;
     const bool cok = c < g.M;
-    const uint16_t *wr = g.W + (size_t)(rok ? row : 0) * K;
-    const uint16_t *wr2 = DUAL ? g.W2 + (size_t)(rok ? row : 0) * K : nullptr;
-    const uint16_t *xr = g.X + (size_t)(cok ? c : 0) * g.ldx;
-    const uint4 z = {0u, 0u, 0u, 0u};
-
-    f32x16 acc = {}, acc2 = {};
-    for (int s = s0; s < s1; s += U) {
-        uint4 a[U][4], b[U][4], a2[DUAL ? U : 1][4];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k0 = (s + u) * 64 + hf * 32;
-            const bool sok = (s + u) < s1;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int k = k0 + q * 8;
-                const bool kok = sok && k < K;
-                a[u][q] = (kok && rok) ? ld16(wr + k) : z;
-                b[u][q] = (kok && cok) ? ld16(xr + k) : z;
-                if constexpr (DUAL) a2[u][q] = (kok && rok) ? ld16(wr2 + k) : z;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc = mfma32(a[u][q], b[u][q], acc);
-                if constexpr (DUAL) acc2 = mfma32(a2[u][q], b[u][q], acc2);
-            }
-        }
-    }
-
-    if constexpr (WK > 1) {
-        if (wave > 0) {
-            float *dst = red + (size_t)(wave - 1) * NACC * 16 * 64;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dst[r * 64 + lane] = acc[r];
-            if constexpr (DUAL) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) dst[(16 + r) * 64 + lane] = acc2[r];
-            }
-        }
-        __syncthreads();
-        if (wave != 0) return;
-        for (int w = 1; w < WK; ++w) {
-            const float *src = red + (size_t)(w - 1) * NACC * 16 * 64;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] += src[r * 64 + lane];
-            if constexpr (DUAL) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc2[r] += src[(16 + r) * 64 + lane];
-            }
-        }
-    }
-
-    const int m = c;
     if constexpr (EPI == EPI_HEAD) {
         float v1 = -INFINITY, v2 = -INFINITY;
         int i1 = 0x7fffffff, i2 = 0x7fffffff;
@@ -194,7 +152,7 @@ __global__ __launch_bounds__(64 * WK) void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int n = tile * 32 + acc_row(r, hf);
-            if (!cok || n >= g.N) continue;
+            if (!cok || n >= N) continue;
             float s = acc[r];
             g.Yf[(size_t)m * g.ldyf + n] = s;
             if (mods) {
@@ -219,7 +177,7 @@ __global__ __launch_bounds__(64 * WK) void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int n = tile * 32 + acc_row(r, hf);
-            if (n >= g.N) continue;
+            if (n >= N) continue;
             uint16_t *y = g.Y + (size_t)m * g.ldy + n;
             if constexpr (EPI == EPI_BF16) {
                 *y = f2bf(acc[r]);
@@ -230,6 +188,134 @@ __global__ __launch_bounds__(64 * WK) void k_gemm(GemmArgs g) {
                 *y = f2bf(gt / (1.0f + expf(-gt)) * up);
             }
         }
+    }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    constexpr int U = DUAL ? 2 : 4;      // k steps per LDS stage
+    constexpr int NACC = DUAL ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][U][32 * 64];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hf = lane >> 5, c = lane & 31;
+    const int N = g.N, K = g.K;
+    const int ntiles = (N + 31) >> 5;
+    const int tile = blockIdx.x * 4 + wave;
+    const bool tok = tile < ntiles;
+    const int nr = tok ? min(32, N - tile * 32) : 0;
+    const int nsteps = (K + 63) >> 6;
+    const int S = gridDim.y, ks = blockIdx.y;
+    const int s0 = (nsteps * ks) / S, s1 = (nsteps * (ks + 1)) / S;
+    const uint16_t *tb = g.W + (size_t)(tok ? tile : 0) * 32 * K;
+    const uint16_t *tb2 = DUAL ? g.W2 + (size_t)(tok ? tile : 0) * 32 * K : nullptr;
+    const uint4 z = {0u, 0u, 0u, 0u};
+
+    // activation staging: thread -> (row br, 16-byte chunk bc) of a step
+    const int br = tid >> 3, bc = tid & 7;
+    const uint16_t *xrow = g.X + (size_t)(br < g.M ? br : 0) * g.ldx;
+    auto stage = [&](int buf, int sf) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = sf + u, k = s * 64 + bc * 8;
+            const uint4 v = (s < s1 && br < g.M && k < K) ? ld16(xrow + k) : z;
+            *reinterpret_cast<uint4 *>(&Bs[buf][u][br * 64 + ((bc ^ (br & 7)) << 3)]) = v;
+        }
+    };
+
+    f32x16 acc = {}, acc2 = {};
+    if (s0 < s1) stage(0, s0);
+    int buf = 0;
+    for (int sg = s0; sg < s1; sg += U, buf ^= 1) {
+        uint4 a[U][4], a2[DUAL ? U : 1][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = sg + u;
+            const bool full = (nr == 32) && (s * 64 + 64 <= K);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                long off;
+                if (s >= s1 || !tok) off = -1;
+                else if (full) off = (long)s * 2048 + q * 512 + lane * 8;
+                else off = packed_piece(s, q, hf, c, nr, K);
+                a[u][q] = off >= 0 ? ld16(tb + off) : z;
+                if constexpr (DUAL) a2[u][q] = off >= 0 ? ld16(tb2 + off) : z;
+            }
+        }
+        __syncthreads();   // stage(buf) visible; everyone is done with buf^1
+        if (sg + U < s1) stage(buf ^ 1, sg + U);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ch = 4 * hf + q;
+                const uint4 b = *reinterpret_cast<const uint4 *>(&Bs[buf][u][c * 64 + ((ch ^ (c & 7)) << 3)]);
+                acc = mfma32(a[u][q], b, acc);
+                if constexpr (DUAL) acc2 = mfma32(a2[u][q], b, acc2);
+            }
+        }
+    }
+
+    if (S > 1) {
+        // partial tile in the raw accumulator layout [rowblock][ks][wave][NACC][16][64];
+        // columns beyond M are zero and stay unwritten (the reduce never reads them)
+        if (c < g.M) {
+            float *mine = g.partial + (((size_t)blockIdx.x * S + ks) * 4 + wave) * NACC * 1024;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mine[r * 64 + lane] = acc[r];
+            if constexpr (DUAL) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mine[1024 + r * 64 + lane] = acc2[r];
+            }
+        }
+        return;
+    }
+    if (tok) gemm_epilogue<EPI>(g, tile, lane, acc, acc2);
+}
+
+// Split-K finish: one workgroup per 128-row block adds the S partial tiles
+// in k-range order and applies the epilogue.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g, int S) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    constexpr int NACC = DUAL ? 2 : 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 31;
+    const int tile = blockIdx.x * 4 + wave;
+    if (tile >= (g.N + 31) / 32 || c >= g.M) return;
+    f32x16 acc = {}, acc2 = {};
+    for (int k2 = 0; k2 < S; ++k2) {
+        const float *p = g.partial + (((size_t)blockIdx.x * S + k2) * 4 + wave) * NACC * 1024;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += p[r * 64 + lane];
+        if constexpr (DUAL) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc2[r] += p[1024 + r * 64 + lane];
+        }
+    }
+    gemm_epilogue<EPI>(g, tile, lane, acc, acc2);
+}
+
+// In-place repack of a row-major [N, K] bf16 matrix into the packed tile
+// order read by k_gemm.  `src` holds a row-major copy of tiles [t0, t0+nt).
+__global__ __launch_bounds__(256) void k_pack(const uint16_t *__restrict__ src, uint16_t *__restrict__ dst,
+                                              int N, int K, int t0, int nt) {
+    const int nsteps = (K + 63) >> 6;
+    const long pieces = (long)nt * nsteps * 8 * 32;
+    for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < pieces; i += (long)gridDim.x * blockDim.x) {
+        const int c = (int)(i & 31);
+        const long j = i >> 5;
+        const int pi = (int)(j & 7);
+        const long j2 = j >> 3;
+        const int s = (int)(j2 % nsteps);
+        const int tl = (int)(j2 / nsteps);
+        const int tile = t0 + tl;
+        const int nr = min(32, N - tile * 32);
+        const int q = pi >> 1, hf = pi & 1;
+        const long off = packed_piece(s, q, hf, c, nr, K);
+        if (off < 0) continue;
+        const uint4 v = ld16(src + ((size_t)tl * 32 + c) * K + s * 64 + 32 * hf + 8 * q);
+        *reinterpret_cast<uint4 *>(dst + (size_t)tile * 32 * K + off) = v;
     }
 }
 
@@ -573,16 +659,36 @@ hipError_t launch_rmsnorm(hipStream_t s, const uint16_t *X, const uint16_t *w, i
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(hipStream_t s, int epi, const GemmArgs &a) {
-    constexpr int WK = 4;
-    const dim3 grid((a.N + 31) / 32), block(64 * WK);
+hipError_t launch_gemm(hipStream_t s, int epi, const GemmArgs &a, int splits) {
+    const int rowblocks = ((a.N + 31) / 32 + 3) / 4;
+    const dim3 grid(rowblocks, splits), block(256);
     switch (epi) {
-    case EPI_BF16: hipLaunchKernelGGL((k_gemm<EPI_BF16, WK>), grid, block, 0, s, a); break;
-    case EPI_RESID: hipLaunchKernelGGL((k_gemm<EPI_RESID, WK>), grid, block, 0, s, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm<EPI_SWIGLU, WK>), grid, block, 0, s, a); break;
-    case EPI_HEAD: hipLaunchKernelGGL((k_gemm<EPI_HEAD, WK>), grid, block, 0, s, a); break;
+    case EPI_BF16: hipLaunchKernelGGL((k_gemm<EPI_BF16>), grid, block, 0, s, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_gemm<EPI_RESID>), grid, block, 0, s, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm<EPI_SWIGLU>), grid, block, 0, s, a); break;
+    case EPI_HEAD: hipLaunchKernelGGL((k_gemm<EPI_HEAD>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(hipStream_t s, int epi, const GemmArgs &a, int splits) {
+    const int rowblocks = ((a.N + 31) / 32 + 3) / 4;
+    const dim3 grid(rowblocks), block(256);
+    switch (epi) {
+    case EPI_BF16: hipLaunchKernelGGL((k_splitk_reduce<EPI_BF16>), grid, block, 0, s, a, splits); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_splitk_reduce<EPI_RESID>), grid, block, 0, s, a, splits); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((k_splitk_reduce<EPI_SWIGLU>), grid, block, 0, s, a, splits); break;
+    case EPI_HEAD: hipLaunchKernelGGL((k_splitk_reduce<EPI_HEAD>), grid, block, 0, s, a, splits); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(hipStream_t s, const uint16_t *src, uint16_t *dst, int N, int K, int t0, int nt) {
+    const long pieces = (long)nt * ((K + 63) / 64) * 8 * 32;
+    const int grid = (int)std::min<long>((pieces + 255) / 256, 65536);
+    hipLaunchKernelGGL(k_pack, dim3(grid), dim3(256), 0, s, src, dst, N, K, t0, nt);
     return hipGetLastError();
 }
 

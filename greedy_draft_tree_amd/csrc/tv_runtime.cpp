@@ -72,6 +72,8 @@ struct tv_ctx {
     int32_t *d_argmax = nullptr;
     float *d_gap = nullptr, *d_top = nullptr;
     int32_t *d_path = nullptr;
+    float *gemm_partial = nullptr;   // split-K partial tiles
+    size_t gemm_partial_floats = 0;
     // pinned host staging
     PassMeta *h_meta = nullptr;
     int32_t *h_argmax = nullptr;
@@ -220,6 +222,51 @@ int upload_kvtab(tv_ctx *c, Req &q) {
     return TV_OK;
 }
 
+size_t gemm_partial_need(int N, int K, bool dual) {
+    const int S = gemm_splits(N, K);
+    if (S <= 1) return 0;
+    const size_t rowblocks = (size_t)((N + 31) / 32 + 3) / 4;
+    return rowblocks * S * 4 * (dual ? 2 : 1) * 1024;
+}
+
+// Rearrange a row-major [N, K] bf16 matrix in place into the packed tile
+// order of the GEMM kernel, a chunk of whole tiles at a time.
+int pack_inplace(tv_ctx *c, void *ptr, int N, int K) {
+    const int ntiles = (N + 31) / 32;
+    const size_t tile_bytes = (size_t)32 * K * 2;
+    const int per = (int)std::max<size_t>(1, ((size_t)64 << 20) / tile_bytes);
+    uint16_t *tmp = nullptr;
+    HIPCHECK(c, hipMalloc(&tmp, std::min(per, ntiles) * tile_bytes));
+    hipError_t e = hipSuccess;
+    for (int t0 = 0; t0 < ntiles && e == hipSuccess; t0 += per) {
+        const int nt = std::min(per, ntiles - t0);
+        const size_t rows = std::min((size_t)nt * 32, (size_t)N - (size_t)t0 * 32);
+        e = hipMemcpyAsync(tmp, (uint16_t *)ptr + (size_t)t0 * 32 * K, rows * K * 2, hipMemcpyDeviceToDevice,
+                           c->stream);
+        if (e == hipSuccess) e = launch_pack(c->stream, tmp, (uint16_t *)ptr, N, K, t0, nt);
+        if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    }
+    hipFree(tmp);
+    if (e != hipSuccess) return fail(c, TV_EHIP, "packing a weight failed: %s", hipGetErrorString(e));
+    return TV_OK;
+}
+
+int gemm(tv_ctx *c, const char *name, int epi, GemmArgs g) {
+    g.partial = c->gemm_partial;
+    const int S = gemm_splits(g.N, g.K);
+    if (gemm_partial_need(g.N, g.K, epi == EPI_SWIGLU) > c->gemm_partial_floats)
+        return fail(c, TV_EINVAL, "GEMM N=%d K=%d needs more split-K scratch than allocated", g.N, g.K);
+    LAUNCH(c, name, launch_gemm(c->stream, epi, g, S));
+    if (S > 1) LAUNCH(c, name, launch_splitk_reduce(c->stream, epi, g, S));
+    return TV_OK;
+}
+
+#define GEMM(c, nm, epi, g)                 \
+    do {                                    \
+        int rc_ = gemm((c), (nm), (epi), (g)); \
+        if (rc_) return rc_;                \
+    } while (0)
+
 // One forward pass over `total` rows of up to 32, request after request.
 int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parents,
              const int32_t *const *tokens, const int *n_nodes, float *logits_dev, int32_t *argmax,
@@ -293,7 +340,7 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
             GemmArgs g{};
             g.X = c->XN; g.ldx = H; g.W = c->wqkv[l]; g.M = M; g.N = (QH + 2 * KVH) * D; g.K = H;
             g.Y = c->QKV; g.ldy = g.N;
-            LAUNCH(c, "gemm_qkv", launch_gemm(s, EPI_BF16, g));
+            GEMM(c, "gemm_qkv", EPI_BF16, g);
             for (int r = 0; r < n_req; ++r) {
                 Req &q = c->reqs[reqs[r]];
                 RopeArgs ra{};
@@ -320,20 +367,20 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
             GemmArgs g{};
             g.X = c->ATT; g.ldx = QH * D; g.W = c->wo[l]; g.M = M; g.N = H; g.K = QH * D;
             g.Y = c->X; g.ldy = H;
-            LAUNCH(c, "gemm_o", launch_gemm(s, EPI_RESID, g));
+            GEMM(c, "gemm_o", EPI_RESID, g);
         }
         LAUNCH(c, "rmsnorm", launch_rmsnorm(s, c->X, c->ffn_norm[l], M, H, m.eps, c->XN));
         {
             GemmArgs g{};
             g.X = c->XN; g.ldx = H; g.W = c->wg[l]; g.W2 = c->wu[l]; g.M = M; g.N = m.ffn; g.K = H;
             g.Y = c->ACT; g.ldy = m.ffn;
-            LAUNCH(c, "gemm_gateup", launch_gemm(s, EPI_SWIGLU, g));
+            GEMM(c, "gemm_gateup", EPI_SWIGLU, g);
         }
         {
             GemmArgs g{};
             g.X = c->ACT; g.ldx = m.ffn; g.W = c->wd[l]; g.M = M; g.N = H; g.K = m.ffn;
             g.Y = c->X; g.ldy = H;
-            LAUNCH(c, "gemm_down", launch_gemm(s, EPI_RESID, g));
+            GEMM(c, "gemm_down", EPI_RESID, g);
         }
     }
     LAUNCH(c, "rmsnorm", launch_rmsnorm(s, c->X, c->final_norm, M, H, m.eps, c->XN));
@@ -342,7 +389,7 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
         GemmArgs g{};
         g.X = c->XN; g.ldx = H; g.W = c->head; g.M = M; g.N = m.vocab; g.K = H;
         g.Yf = out; g.ldyf = m.vocab; g.part = c->part; g.meta = c->d_meta; g.mods_on = any_mods;
-        LAUNCH(c, "gemm_head", launch_gemm(s, EPI_HEAD, g));
+        GEMM(c, "gemm_head", EPI_HEAD, g);
     }
     LAUNCH(c, "top2", launch_top2_reduce(s, c->part, (m.vocab + 31) / 32, M, c->d_argmax, c->d_gap,
                                          c->d_top));
@@ -366,6 +413,8 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
 }
 
 void set_bit(std::vector<uint32_t> &b, int v) { b[v >> 5] |= 1u << (v & 31); }
+
+
 
 } // namespace
 
@@ -428,6 +477,19 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     ALLOC(c->d_gap, R * 4);
     ALLOC(c->d_top, 2 * R * 4);
     ALLOC(c->d_path, R * 4);
+    {
+        const int QD = m.n_qhead * D;
+        size_t need = (size_t)8 << 20;  // room for kernel-level calls
+        need = std::max(need, gemm_partial_need((m.n_qhead + 2 * m.n_kvhead) * D, H, false));
+        need = std::max(need, gemm_partial_need(3 * QD, H, false));
+        need = std::max(need, gemm_partial_need(m.n_qhead, H, false));
+        need = std::max(need, gemm_partial_need(H, QD, false));
+        need = std::max(need, gemm_partial_need(m.ffn, H, true));
+        need = std::max(need, gemm_partial_need(H, m.ffn, false));
+        need = std::max(need, gemm_partial_need(m.vocab, H, false));
+        c->gemm_partial_floats = need;
+    }
+    ALLOC(c->gemm_partial, c->gemm_partial_floats * 4);
 #undef ALLOC
     if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_meta, sizeof(PassMeta), hipHostMallocDefault);
     if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_argmax, R * 4, hipHostMallocDefault);
@@ -456,7 +518,8 @@ void tv_destroy(tv_ctx *c) {
     if (c->stream) hipStreamSynchronize(c->stream);
     else hipDeviceSynchronize();
     void *dev[] = {c->X, c->XN, c->QKV, c->QR, c->ATT, c->ACT, c->logits, c->part, c->po, c->pm, c->pl,
-                   c->rope_cos, c->rope_sin, c->d_meta, c->d_argmax, c->d_gap, c->d_top, c->d_path};
+                   c->rope_cos, c->rope_sin, c->d_meta, c->d_argmax, c->d_gap, c->d_top, c->d_path,
+                   c->gemm_partial};
     for (void *p : dev)
         if (p) hipFree(p);
     for (auto &q : c->reqs) {
@@ -488,7 +551,13 @@ int tv_bind(tv_ctx *c, const char *name, void *ptr, size_t bytes) {
     };
     int rc;
     if (!strcmp(name, "emb")) { if ((rc = want(V * H * 2))) return rc; c->emb = (const uint16_t *)ptr; return TV_OK; }
-    if (!strcmp(name, "head")) { if ((rc = want(V * H * 2))) return rc; c->head = (const uint16_t *)ptr; return TV_OK; }
+    if (!strcmp(name, "head")) {
+        if ((rc = want(V * H * 2))) return rc;
+        if (c->head == ptr) return TV_OK;  // re-bound: already packed
+        if ((rc = pack_inplace(c, ptr, (int)V, (int)H))) return rc;
+        c->head = (const uint16_t *)ptr;
+        return TV_OK;
+    }
     if (!strcmp(name, "final_norm")) { if ((rc = want(H * 2))) return rc; c->final_norm = (const uint16_t *)ptr; return TV_OK; }
     int l = -1, r = -1, used = 0;
     char field[32] = {0};
@@ -498,19 +567,24 @@ int tv_bind(tv_ctx *c, const char *name, void *ptr, size_t bytes) {
         const uint16_t *p = (const uint16_t *)ptr;
         if (!strcmp(field, "attn_norm")) { if ((rc = want(H * 2))) return rc; c->attn_norm[l] = p; return TV_OK; }
         if (!strcmp(field, "ffn_norm")) { if ((rc = want(H * 2))) return rc; c->ffn_norm[l] = p; return TV_OK; }
-        if (!strcmp(field, "wqkv")) {
-            if ((rc = want((at ? (QH + 2 * KVH) * D : 3 * QH * D) * H * 2))) return rc;
-            c->wqkv[l] = p; return TV_OK;
-        }
+        auto mat = [&](const uint16_t *&slot, size_t n_out, size_t k_in) -> int {
+            int r2 = want(n_out * k_in * 2);
+            if (r2) return r2;
+            if (slot == p) return TV_OK;  // re-bound: already packed
+            r2 = pack_inplace(c, ptr, (int)n_out, (int)k_in);
+            if (r2) return r2;
+            slot = p;
+            return TV_OK;
+        };
+        if (!strcmp(field, "wqkv")) return mat(c->wqkv[l], at ? (QH + 2 * KVH) * D : 3 * QH * D, H);
         if (!strcmp(field, "wa")) {
             if (at) return fail(c, TV_EINVAL, "%s: not a recurrent layer", name);
-            if ((rc = want(QH * H * 2))) return rc;
-            c->wa[l] = p; return TV_OK;
+            return mat(c->wa[l], QH, H);
         }
-        if (!strcmp(field, "wo")) { if ((rc = want(H * QH * D * 2))) return rc; c->wo[l] = p; return TV_OK; }
-        if (!strcmp(field, "wg")) { if ((rc = want(F * H * 2))) return rc; c->wg[l] = p; return TV_OK; }
-        if (!strcmp(field, "wu")) { if ((rc = want(F * H * 2))) return rc; c->wu[l] = p; return TV_OK; }
-        if (!strcmp(field, "wd")) { if ((rc = want(H * F * 2))) return rc; c->wd[l] = p; return TV_OK; }
+        if (!strcmp(field, "wo")) return mat(c->wo[l], H, QH * D);
+        if (!strcmp(field, "wg")) return mat(c->wg[l], F, H);
+        if (!strcmp(field, "wu")) return mat(c->wu[l], F, H);
+        if (!strcmp(field, "wd")) return mat(c->wd[l], H, F);
         return fail(c, TV_EINVAL, "unknown tensor %s", name);
     }
     if (sscanf(name, "req.%d.layers.%d.%31s%n", &r, &l, field, &used) == 3 && name[used] == 0) {
@@ -688,14 +762,20 @@ int tv_linear(tv_ctx *c, const void *x, const void *w, int M, int N, int K, void
     hipStream_t s = c->stream;
     if (y_fp32) {
         g.Yf = (float *)y; g.ldyf = N; g.part = c->part;
-        LAUNCH(c, "gemm_linear_f32", launch_gemm(s, EPI_HEAD, g));
+        GEMM(c, "gemm_linear_f32", EPI_HEAD, g);
     } else {
         g.Y = (uint16_t *)y; g.ldy = N;
-        LAUNCH(c, "gemm_linear", launch_gemm(s, EPI_BF16, g));
+        GEMM(c, "gemm_linear", EPI_BF16, g);
     }
     HIPCHECK(c, hipStreamSynchronize(s));
     if (c->prof) harvest(c);
     return TV_OK;
+}
+
+int tv_pack_weight(tv_ctx *c, void *w, int N, int K) {
+    if (!c) return TV_EINVAL;
+    if (!w || N < 1 || K < 8 || K % 8) return fail(c, TV_EINVAL, "bad weight shape N=%d K=%d", N, K);
+    return pack_inplace(c, w, N, K);
 }
 
 int tv_head_top2(tv_ctx *c, const void *x, int M, float *logits_dev, int32_t *argmax, float *gap) {
@@ -708,7 +788,7 @@ int tv_head_top2(tv_ctx *c, const void *x, int M, float *logits_dev, int32_t *ar
     GemmArgs g{};
     g.X = (const uint16_t *)x; g.ldx = m.hidden; g.W = c->head; g.M = M; g.N = m.vocab; g.K = m.hidden;
     g.Yf = logits_dev; g.ldyf = m.vocab; g.part = c->part;
-    LAUNCH(c, "gemm_head", launch_gemm(s, EPI_HEAD, g));
+    GEMM(c, "gemm_head", EPI_HEAD, g);
     LAUNCH(c, "top2", launch_top2_reduce(s, c->part, (m.vocab + 31) / 32, M, c->d_argmax, c->d_gap, c->d_top));
     HIPCHECK(c, hipMemcpyAsync(c->h_argmax, c->d_argmax, M * 4, hipMemcpyDeviceToHost, s));
     HIPCHECK(c, hipMemcpyAsync(c->h_gap, c->d_gap, M * 4, hipMemcpyDeviceToHost, s));

@@ -91,7 +91,12 @@ const char *tv_last_error(tv_ctx *ctx);
  *   "layers.L.wg", "layers.L.wu" [ffn, hidden], "layers.L.wd" [hidden, ffn]
  *   "req.R.layers.L.k", "req.R.layers.L.v"  [n_kvhead, max_ctx, head_dim] bf16
  *   "req.R.layers.L.state"                  [n_qhead, head_dim, head_dim] fp32
- *     (state[h][i][j]: key index i, value index j)                          */
+ *     (state[h][i][j]: key index i, value index j)
+ * Weight matrices (head, wqkv, wo, wa, wg, wu, wd) are given row-major and
+ * REARRANGED IN PLACE into the library's packed tile order (see
+ * tv_pack_weight): after tv_bind their bytes are no longer row-major.
+ * Re-binding a name to the buffer it already holds does not pack it again;
+ * binding an already packed buffer under another name does.                */
 int tv_bind(tv_ctx *ctx, const char *name, void *dev_ptr, size_t bytes);
 
 /* Declare request `req`'s committed context: ctx_len cache rows already
@@ -157,7 +162,7 @@ int tv_ctx_len(tv_ctx *ctx, int req);
 
 /* Kernel-level calls: the pass's projection and head kernels on caller-given
  * device operands, for per-kernel tests and bandwidth measurement.
- * tv_linear: x [M, K] bf16 (row-major), w [N, K] bf16, M in [1, 32], K a
+ * tv_linear: x [M, K] bf16 (row-major), w [N, K] bf16 packed (tv_pack_weight), M in [1, 32], K a
  * multiple of 8; y_fp32 == 0 writes bf16(x w^T) to y [M, N] bf16, y_fp32 != 0
  * writes the fp32 sums to y [M, N] fp32 (N <= vocab).  The k order of every
  * output is fixed by K alone, as in the pass.
@@ -165,6 +170,17 @@ int tv_ctx_len(tv_ctx *ctx, int req);
  * vocab] to logits_dev, argmax and gap (host, M entries) as tv_verify_tree
  * returns them, with no score modifiers.  Both synchronise the stream. */
 int tv_linear(tv_ctx *ctx, const void *x, const void *w, int M, int N, int K, void *y, int y_fp32);
+
+/* Rearrange a row-major [N, K] bf16 device matrix in place into the packed
+ * order the projection kernels read (tv_bind does this for weights; a
+ * tv_linear operand must be packed first).  Rows are cut into tiles of 32,
+ * k into steps of 64; a full step of a full tile is 4 KB in which bytes
+ * [1024q + 16l, +16) hold row l%32, k = 32*(l/32) + 8q .. +8 of the step
+ * (q = 0..3, l = 0..63): the operand layout of one 32x32x16 bf16 matrix
+ * instruction per q.  Partial tiles and steps keep the present pieces in
+ * the same order.  Each tile stays in its row-major byte range.  Every call
+ * packs (packing twice scrambles the matrix).  Synchronises the stream. */
+int tv_pack_weight(tv_ctx *ctx, void *w, int N, int K);
 int tv_head_top2(tv_ctx *ctx, const void *x, int M, float *logits_dev, int32_t *argmax, float *gap_ulps);
 
 /* Kernel timing: with `on` != 0, launches whose kernel name starts with

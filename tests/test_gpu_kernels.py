@@ -59,13 +59,47 @@ def _operands(M, N, K, seed, xstd=1.0):
     return x, w
 
 
+def _packed_layout(w):
+    """The packed order documented in include/treeverify.h, built on the host
+    from a row-major matrix (tiles of 32 rows, steps of 64 k, pieces (q, hf)
+    of 8 k values in order 2q+hf, present pieces only)."""
+    N, K = w.shape
+    src = w.cpu().view(torch.int16).numpy()
+    out = np.empty(N * K, dtype=np.int16)
+    pos = 0
+    for t in range(0, N, 32):
+        nr = min(32, N - t)
+        for s in range(0, K, 64):
+            kr = min(64, K - s)
+            for pi in range(8):
+                q, hf = pi >> 1, pi & 1
+                k0 = 32 * hf + 8 * q
+                if k0 >= kr:
+                    continue
+                for c in range(nr):
+                    out[pos:pos + 8] = src[t + c, s + k0:s + k0 + 8]
+                    pos += 8
+    assert pos == N * K
+    return out
+
+
+@pytest.mark.parametrize("N,K", [(64, 128), (40, 200), (100, 688)])
+def test_pack_weight_matches_documented_layout(tv, N, K):
+    _, w = _operands(1, N, K, N + K)
+    want = _packed_layout(w)
+    tv.pack_weight(w)
+    got = w.cpu().view(torch.int16).numpy().reshape(-1)
+    np.testing.assert_array_equal(got, want)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (7, 1000, 688), (32, 7168, 5120), (13, 5120, 17408),
-                                   (32, 33, 5128), (5, 40, 5120)])
+                                   (32, 33, 5128), (5, 40, 5120), (32, 17408, 5120), (8, 5120, 5120)])
 def test_linear_fp32_within_higham_bound(tv, M, N, K):
     x, w = _operands(M, N, K, M * 7 + N)
+    ref, absum = _ref(x, w)
+    tv.pack_weight(w)
     y = torch.empty(M, N, dtype=torch.float32, device="cuda")
     tv.linear(x, w, y)
-    ref, absum = _ref(x, w)
     gam = K * U / (1 - K * U)
     err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
     assert (err <= gam * absum + 1e-30).all(), float((err / (gam * absum + 1e-30)).max())
@@ -74,9 +108,10 @@ def test_linear_fp32_within_higham_bound(tv, M, N, K):
 @pytest.mark.parametrize("M,N,K", [(3, 512, 256), (32, 7168, 5120), (9, 17408, 5120)])
 def test_linear_bf16_is_correctly_rounded(tv, M, N, K):
     x, w = _operands(M, N, K, 100 + M)
+    ref, absum = _ref(x, w)
+    tv.pack_weight(w)
     y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     tv.linear(x, w, y)
-    ref, absum = _ref(x, w)
     want = oracle.bf16_round(ref)
     got = y.cpu().to(torch.float64).numpy()
     gam = K * U / (1 - K * U)
@@ -92,6 +127,7 @@ def test_linear_bf16_is_correctly_rounded(tv, M, N, K):
 def test_linear_rows_bitwise_invariant(tv):
     N, K = 4096, 5120
     x, w = _operands(32, N, K, 5)
+    tv.pack_weight(w)
     full = torch.empty(32, N, dtype=torch.float32, device="cuda")
     tv.linear(x, w, full)
     rng = np.random.default_rng(0)
@@ -109,8 +145,9 @@ def test_linear_rows_bitwise_invariant(tv):
 @pytest.fixture(scope="module")
 def head(tv):
     w = synth.weights(synth.C1, seed=0, device="cuda", only=["head"])["head"]
+    host = w.cpu()
     tv.bind("head", w)
-    return w
+    return host
 
 
 def test_head_top2_c1(tv, head):

@@ -67,9 +67,8 @@ def check_rows(gpu_logits, gpu_argmax, gpu_gap, orc_logits, parents, tokens, his
 def c0():
     _gpu()
     import workloads
-    wl = workloads.build(synth.C0, max_ctx=512, max_req=2, weight_device="cuda")
-    w_cpu = {k: v.cpu() for k, v in wl.weights.items()}
-    return wl, oracle.Oracle(synth.C0, w_cpu)
+    wl = workloads.build(synth.C0, max_ctx=512, max_req=2, weight_device="cuda", host_copy=True)
+    return wl, oracle.Oracle(synth.C0, wl.host_weights)
 
 
 def test_c0_prefill_and_tree_rows(c0):
@@ -251,10 +250,9 @@ def test_c0_errors_leave_state(c0):
 def c1():
     _gpu()
     import workloads
-    wl = workloads.build(synth.C1, max_ctx=8192 + 64, max_req=2, weight_device="cuda")
-    w_cpu = {k: v.cpu() for k, v in wl.weights.items()}
-    orc = oracle.Oracle(synth.C1, w_cpu)
-    orc.w_src = w_cpu
+    wl = workloads.build(synth.C1, max_ctx=8192 + 64, max_req=2, weight_device="cuda", host_copy=True)
+    orc = oracle.Oracle(synth.C1, wl.host_weights)
+    orc.w_src = wl.host_weights
     return wl, orc
 
 

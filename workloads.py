@@ -19,22 +19,26 @@ from greedy_draft_tree_amd import TreeVerifier
 class Workload:
     shape: synth.ModelShape
     tv: TreeVerifier
-    weights: Dict[str, torch.Tensor]           # device bf16
+    weights: Dict[str, torch.Tensor]           # device bf16 (matrices packed in place by bind)
     kv: Dict[int, Dict]                        # req -> {(layer, 'k'|'v'): device tensor}
     states: Dict[int, Dict]                    # req -> {layer: device fp32 [QH, D, D]}
     max_ctx: int
     logits: torch.Tensor                       # device fp32 [32, V]
+    host_weights: Optional[Dict[str, torch.Tensor]] = None  # row-major CPU copies, taken before bind
 
 
 def build(shape: synth.ModelShape, max_ctx: int, max_req: int = 1, weight_seed: int = 0,
           weight_device: str = "cpu", weights: Optional[Dict[str, torch.Tensor]] = None,
-          device: str = "cuda") -> Workload:
+          device: str = "cuda", host_copy: bool = False) -> Workload:
     """Allocate and bind weights (drawn on ``weight_device``), zeroed KV caches
-    of ``max_ctx`` rows and zero recurrent states for ``max_req`` requests."""
+    of ``max_ctx`` rows and zero recurrent states for ``max_req`` requests.
+    Binding rearranges the weight matrices in place; ``host_copy`` keeps
+    row-major CPU copies taken before that (for the oracle)."""
     if weights is None:
         w = synth.weights(shape, seed=weight_seed, device=weight_device)
         weights = {k: v.to(device) for k, v in w.items()}
         del w
+    host = {k: v.cpu() for k, v in weights.items()} if host_copy else None
     stream = torch.cuda.current_stream().cuda_stream
     tv = TreeVerifier.for_shape(shape, max_ctx=max_ctx, max_req=max_req, stream=stream)
     for k, v in weights.items():
@@ -55,7 +59,7 @@ def build(shape: synth.ModelShape, max_ctx: int, max_req: int = 1, weight_seed: 
                 tv.bind(f"req.{r}.layers.{l}.state", t)
                 states[r][l] = t
     logits = torch.empty((32, shape.vocab), dtype=torch.float32, device=device)
-    return Workload(shape, tv, weights, kv, states, max_ctx, logits)
+    return Workload(shape, tv, weights, kv, states, max_ctx, logits, host)
 
 
 def load_context(wl: Workload, req: int, ctx: int, seed: int, history=None,
