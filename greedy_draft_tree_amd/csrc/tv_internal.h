@@ -8,7 +8,6 @@ namespace tv {
 
 constexpr int kMaxRows = 32;   // rows of one pass
 constexpr int kMaxGroup = 8;   // query heads per KV head
-constexpr int kAttnSplit = 256; // cache keys per attention workgroup
 constexpr int kAttnChunk = 64;  // keys staged in LDS at a time
 
 // Candidate pair of a top-2 search: best (v1, i1) and runner-up (v2, i2),
@@ -77,8 +76,17 @@ struct AttnArgs {
     float *pm;          // [n_kvhead][ns][kMaxRows*kMaxGroup]
     float *pl;
     int row0, n, ctx, cap, G, n_qhead, ns, n_ctx_split;
+    int span;           // cache keys per split (a multiple of kAttnChunk)
     float scale;
 };
+
+// Cache keys per attention split: about 32 splits per KV head, in whole
+// LDS chunks; a function of the context length only.
+inline int attn_span(int ctx) {
+    const int chunks = (ctx + kAttnChunk - 1) / kAttnChunk;
+    const int per = (chunks + 31) / 32;
+    return (per < 1 ? 1 : per) * kAttnChunk;
+}
 
 struct RopeArgs {
     const uint16_t *qkv; // [rows, (QH+2KVH)*D]

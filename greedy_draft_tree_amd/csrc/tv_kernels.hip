@@ -138,9 +138,10 @@ __device__ __forceinline__ long packed_piece(int s, int q, int hf, int c, int nr
 }
 
 // Epilogue of one 32x32 output tile held in MFMA accumulator layout.
+// For the head, each column's top-2 over the tile goes to top_out[column].
 template <int EPI>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, int tile, int lane, const f32x16 &acc,
-                                              const f32x16 &acc2) {
+                                              const f32x16 &acc2, Top2 *top_out) {
     const int hf = lane >> 5, c = lane & 31;
     const int m = c, N = g.N;
     const bool cok = c < g.M;
@@ -171,7 +172,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, int tile, int l
         const float w1 = __shfl_xor(v1, 32), w2 = __shfl_xor(v2, 32);
         const int j1 = __shfl_xor(i1, 32), j2 = __shfl_xor(i2, 32);
         top2_merge(v1, i1, v2, i2, w1, j1, w2, j2);
-        if (hf == 0) g.part[(size_t)tile * 32 + m] = Top2{v1, i1, v2, i2};
+        if (hf == 0) top_out[m] = Top2{v1, i1, v2, i2};
     } else {
         if (!cok) return;
 #pragma unroll
@@ -271,29 +272,55 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
         }
         return;
     }
-    if (tok) gemm_epilogue<EPI>(g, tile, lane, acc, acc2);
+    if constexpr (EPI == EPI_HEAD) {
+        // each wave's per-column top-2 goes through LDS; wave 0 merges the
+        // workgroup's 4 tiles (a selection: order-free) and stores row-major
+        // candidates part[m * rowblocks + rowblock]
+        __shared__ Top2 wt[4][32];
+        Top2 mine = {-INFINITY, 0x7fffffff, -INFINITY, 0x7fffffff};
+        if (tok) {
+            gemm_epilogue<EPI>(g, tile, lane, acc, acc2, wt[wave]);
+        } else if (hf == 0) {
+            wt[wave][c] = mine;
+        }
+        __syncthreads();
+        if (wave == 0 && hf == 0 && c < g.M) {
+            Top2 r = wt[0][c];
+            for (int w = 1; w < 4; ++w) top2_merge(r.v1, r.i1, r.v2, r.i2, wt[w][c].v1, wt[w][c].i1, wt[w][c].v2, wt[w][c].i2);
+            g.part[(size_t)c * gridDim.x + blockIdx.x] = r;
+        }
+    } else {
+        if (tok) gemm_epilogue<EPI>(g, tile, lane, acc, acc2, nullptr);
+    }
 }
 
-// Split-K finish: one workgroup per 128-row block adds the S partial tiles
-// in k-range order and applies the epilogue.
+// Split-K finish: one thread per output element adds its S partials in
+// k-range order and applies the element's epilogue.
 template <int EPI>
 __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g, int S) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
     constexpr int NACC = DUAL ? 2 : 1;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 31;
-    const int tile = blockIdx.x * 4 + wave;
-    if (tile >= (g.N + 31) / 32 || c >= g.M) return;
-    f32x16 acc = {}, acc2 = {};
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;   // ((rb*4 + wave)*16 + r)*64 + lane
+    const int lane = (int)(idx & 63), r = (int)((idx >> 6) & 15), wave = (int)((idx >> 10) & 3);
+    const long rb = idx >> 12;
+    const int c = lane & 31, hf = lane >> 5;
+    const int n = (int)((rb * 4 + wave) * 32) + acc_row(r, hf);
+    if (c >= g.M || n >= g.N) return;
+    float acc = 0.f, acc2 = 0.f;
+    const float *p = g.partial + ((size_t)rb * S * 4 + wave) * NACC * 1024 + r * 64 + lane;
     for (int k2 = 0; k2 < S; ++k2) {
-        const float *p = g.partial + (((size_t)blockIdx.x * S + k2) * 4 + wave) * NACC * 1024;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += p[r * 64 + lane];
-        if constexpr (DUAL) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc2[r] += p[1024 + r * 64 + lane];
-        }
+        acc += p[(size_t)k2 * 4 * NACC * 1024];
+        if constexpr (DUAL) acc2 += p[(size_t)k2 * 4 * NACC * 1024 + 1024];
     }
-    gemm_epilogue<EPI>(g, tile, lane, acc, acc2);
+    uint16_t *y = g.Y + (size_t)c * g.ldy + n;
+    if constexpr (EPI == EPI_BF16) {
+        *y = f2bf(acc);
+    } else if constexpr (EPI == EPI_RESID) {
+        *y = f2bf(bf2f(*y) + bfround(acc));
+    } else if constexpr (EPI == EPI_SWIGLU) {
+        const float gt = bfround(acc), up = bfround(acc2);
+        *y = f2bf(gt / (1.0f + expf(-gt)) * up);
+    }
 }
 
 // In-place repack of a row-major [N, K] bf16 matrix into the packed tile
@@ -331,8 +358,9 @@ __global__ __launch_bounds__(256) void k_top2_reduce(const Top2 *__restrict__ pa
     const int m = blockIdx.x, t = threadIdx.x;
     float v1 = -INFINITY, v2 = -INFINITY;
     int i1 = 0x7fffffff, i2 = 0x7fffffff;
+    const Top2 *row = part + (size_t)m * ntiles;
     for (int i = t; i < ntiles; i += 256) {
-        const Top2 p = part[(size_t)i * 32 + m];
+        const Top2 p = row[i];
         top2_merge(v1, i1, v2, i2, p.v1, p.i1, p.v2, p.i2);
     }
     sh[t] = Top2{v1, i1, v2, i2};
@@ -404,193 +432,170 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
 }
 
 // ---------------------------------------------------------- tree attention
-// Grid (split, kv head).  Rows of a workgroup are the G query heads of its
-// KV head for every tree node: row r = node*G + head-in-group.  Splits
-// 0..n_ctx_split-1 each take kAttnSplit cache keys (all visible); the last
-// split takes the tree's own keys at slots ctx..ctx+n-1, key j visible to
-// node t iff j is t or an ancestor of t ("Drafters and tree verify", Tree
-// verify through recurrent layers: an attention mask of its ancestors).
-// Keys are staged in LDS 64 at a time; scores and P.V run on MFMA with an
-// online softmax per row in fp32.  P is split into bf16 high and low parts
-// (two MFMAs) so P.V keeps ~16 bits of P.  Each workgroup writes its
-// unnormalised partial (max, sum, output); the combine kernel merges splits
-// in index order.  Split boundaries depend only on ctx, so a row's result
-// does not depend on the other rows of the pass.
+// Grid (split, kv head); one wave per block of 32 query rows, where row
+// r = node*G + head-in-group.  Splits 0..n_ctx_split-1 each take `span`
+// cache keys (visible to every row); the last split takes the tree's own
+// keys at slots ctx..ctx+n-1, key j visible to node t iff j is t or an
+// ancestor of t ("Drafters and tree verify", Tree verify through recurrent
+// layers: attention gets a mask of the node's ancestors).
+//
+// Scores are computed transposed, S^T = K Q^T, on MFMA (A = 32 keys from
+// LDS, B = the wave's 32 query rows kept in registers), so every lane owns
+// one query row: the online-softmax max, sum and rescale stay in the lane
+// (plus its partner lane^32).  P^T then feeds O^T = V^T P^T directly from
+// registers: the k slots of each 16-key step are permuted to the keys the
+// lane already holds, and V^T is staged in LDS with the same order.  P is
+// split into bf16 high and low parts (two MFMAs) so P.V keeps ~16 bits of P.
+// Each workgroup writes its unnormalised partial (max, sum, output); the
+// combine kernel merges splits in index order.  Split boundaries depend
+// only on ctx, so a row's result does not depend on the other rows.
 
 template <int D>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
-    constexpr int RMAX = 160;          // rows staged: G*n <= 160 (host checks G <= 5)
-    constexpr int CH = kAttnChunk;
-    constexpr int SSTR = CH + 4;       // fp32 stride of the score rows
-    constexpr int VSTR = CH + 8;       // bf16 stride of transposed V rows
-    constexpr int DB = D / 32;         // output column blocks
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[RMAX * D];
+__global__ __launch_bounds__(320) void k_attn(AttnArgs a) {
+    constexpr int CH = kAttnChunk;     // keys per LDS stage
+    constexpr int KC = D / 8;          // 16-byte chunks per key row
+    constexpr int VSTR = CH + 4;       // bf16 stride of a transposed V row
+    constexpr int NDB = D / 32;        // output dim blocks
+    constexpr int NKK = D / 16;        // dim steps of the score MFMA
     __shared__ __attribute__((aligned(16))) uint16_t Ks[CH * D];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
-    __shared__ __attribute__((aligned(16))) float Ss[RMAX * SSTR];
-    __shared__ float mrow[RMAX], lrow[RMAX], arow[RMAX];
 
     const int split = blockIdx.x, kvh = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int hf = lane >> 5, c = lane & 31;
     const int G = a.G, n = a.n;
     const int R = G * n;
-    const int RB = (R + 31) >> 5;
     const bool tree = split >= a.n_ctx_split;
-    const int key0 = tree ? a.ctx : split * kAttnSplit;
-    const int nkeys = tree ? n : min(kAttnSplit, a.ctx - key0);
-    const int ldq = a.n_qhead * D;
-    const PassMeta *meta = a.meta;
+    const int key0 = tree ? a.ctx : split * a.span;
+    const int nkeys = tree ? n : min(a.span, a.ctx - key0);
+    const int row = wave * 32 + c;             // this lane's query row
+    const bool rowok = row < R;
+    const int t = rowok ? row / G : 0, hh = rowok ? row % G : 0;
+    const uint32_t anc = a.meta->anc[a.row0 + t];
 
-    // stage the queries of this KV head
-    for (int idx = tid; idx < RB * 32 * (D / 8); idx += 256) {
-        const int r = idx / (D / 8), p = idx % (D / 8);
-        uint4 v = {0u, 0u, 0u, 0u};
-        if (r < R) {
-            const int t = r / G, hh = r % G;
-            v = ld16(a.Q + (size_t)(a.row0 + t) * ldq + (size_t)(kvh * G + hh) * D + p * 8);
-        }
-        *reinterpret_cast<uint4 *>(Qs + r * D + p * 8) = v;
-    }
-    for (int r = tid; r < RMAX; r += 256) {
-        mrow[r] = -INFINITY;
-        lrow[r] = 0.f;
-    }
-
-    f32x16 o[2][DB];
+    // the wave's 32 query rows, dims 16kk + 8hf .. +8 for each kk
+    uint4 q[NKK];
+    {
+        const uint16_t *qr = a.Q + (size_t)(a.row0 + t) * a.n_qhead * D + (size_t)(kvh * G + hh) * D;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+        for (int kk = 0; kk < NKK; ++kk)
+            q[kk] = rowok ? ld16(qr + kk * 16 + hf * 8) : uint4{0u, 0u, 0u, 0u};
+    }
+    f32x16 o[NDB];
 #pragma unroll
-        for (int d = 0; d < DB; ++d) o[b][d] = (f32x16){};
+    for (int d = 0; d < NDB; ++d) o[d] = (f32x16){};
+    float mrun = -INFINITY, lrun = 0.f;
 
-    const uint16_t *Kbase = a.Kc + (size_t)kvh * a.cap * D;
-    const uint16_t *Vbase = a.Vc + (size_t)kvh * a.cap * D;
-
+    const uint16_t *Kb = a.Kc + (size_t)kvh * a.cap * D;
+    const uint16_t *Vb = a.Vc + (size_t)kvh * a.cap * D;
     for (int c0 = 0; c0 < nkeys; c0 += CH) {
         const int cn = min(CH, nkeys - c0);
         __syncthreads();
-        for (int idx = tid; idx < CH * (D / 8); idx += 256) {
-            const int kk = idx / (D / 8), p = idx % (D / 8);
+        for (int idx = tid; idx < CH * KC; idx += nthr) {
+            const int kk = idx / KC, p = idx % KC;
             uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
             if (kk < cn) {
                 const size_t off = (size_t)(key0 + c0 + kk) * D + p * 8;
-                kv = ld16(Kbase + off);
-                vv = ld16(Vbase + off);
+                kv = ld16(Kb + off);
+                vv = ld16(Vb + off);
             }
-            *reinterpret_cast<uint4 *>(Ks + kk * D + p * 8) = kv;
+            *reinterpret_cast<uint4 *>(Ks + kk * D + ((p ^ (kk & (KC - 1))) << 3)) = kv;
             const uint16_t *ve = reinterpret_cast<const uint16_t *>(&vv);
 #pragma unroll
             for (int e = 0; e < 8; ++e) Vt[(p * 8 + e) * VSTR + kk] = ve[e];
         }
         __syncthreads();
+        if (wave * 32 >= R) continue;
 
-        // scores of the row blocks this wave owns
-        for (int rb = wave; rb < RB; rb += 4) {
+        // S^T for 2 blocks of 32 keys: lane (c, hf) holds rows=c, keys kb*32 + acc_row(r, hf)
+        f32x16 s[CH / 32];
 #pragma unroll
-            for (int kb = 0; kb < CH / 32; ++kb) {
-                f32x16 s = {};
+        for (int kb = 0; kb < CH / 32; ++kb) {
+            s[kb] = (f32x16){};
+            const int key = kb * 32 + c;
 #pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) {
-                    const uint4 qa = *reinterpret_cast<const uint4 *>(Qs + (rb * 32 + c) * D + kk * 16 + hf * 8);
-                    const uint4 kb4 = *reinterpret_cast<const uint4 *>(Ks + (kb * 32 + c) * D + kk * 16 + hf * 8);
-                    s = mfma32(qa, kb4, s);
-                }
-                const int j = kb * 32 + c;   // key within the chunk
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = rb * 32 + acc_row(r, hf);
-                    bool vis = j < cn;
-                    if (tree && vis) {
-                        const int t = min(row / G, n - 1);
-                        vis = (meta->anc[a.row0 + t] >> (c0 + j)) & 1u;
-                    }
-                    Ss[row * SSTR + j] = vis ? s[r] * a.scale : -INFINITY;
-                }
+            for (int kk = 0; kk < NKK; ++kk) {
+                const uint4 ka = *reinterpret_cast<const uint4 *>(Ks + key * D + (((2 * kk + hf) ^ (key & (KC - 1))) << 3));
+                s[kb] = mfma32(ka, q[kk], s[kb]);
             }
         }
-        __syncthreads();
-
-        // online softmax, one thread per row
-        if (tid < RB * 32) {
-            const int row = tid;
-            float *sr = Ss + row * SSTR;
-            float mx = -INFINITY;
-            for (int j = 0; j < CH; ++j) mx = fmaxf(mx, sr[j]);
-            const float mold = mrow[row];
-            const float mnew = fmaxf(mold, mx);
-            float alpha, l = lrow[row];
-            if (mnew == -INFINITY) {
-                alpha = 1.f;
-                for (int j = 0; j < CH; ++j) sr[j] = 0.f;
-            } else {
-                alpha = (mold == -INFINITY) ? 0.f : expf(mold - mnew);
-                l *= alpha;
-                for (int j = 0; j < CH; ++j) {
-                    const float p = (sr[j] == -INFINITY) ? 0.f : expf(sr[j] - mnew);
-                    l += p;
-                    const uint16_t hi = f2bf(p);
-                    const uint16_t lo = f2bf(p - bf2f(hi));
-                    sr[j] = __uint_as_float((uint32_t)hi | ((uint32_t)lo << 16));
-                }
-            }
-            mrow[row] = mnew;
-            lrow[row] = l;
-            arow[row] = alpha;
-        }
-        __syncthreads();
-
-        // o = o * alpha + P V
+        float mx = -INFINITY;
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi) {
-            const int rb = wave + 4 * bi;
-            if (rb >= RB) break;
-            float al[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) al[r] = arow[rb * 32 + acc_row(r, hf)];
-#pragma unroll
-            for (int d = 0; d < DB; ++d)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[bi][d][r] *= al[r];
-#pragma unroll
-            for (int kk = 0; kk < CH / 16; ++kk) {
-                const float *sp = Ss + (rb * 32 + c) * SSTR + kk * 16 + hf * 8;
-                uint32_t hiw[4], low[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t p0 = __float_as_uint(sp[2 * e]), p1 = __float_as_uint(sp[2 * e + 1]);
-                    hiw[e] = (p0 & 0xffffu) | (p1 << 16);
-                    low[e] = (p0 >> 16) | (p1 & 0xffff0000u);
-                }
-                const uint4 phi = {hiw[0], hiw[1], hiw[2], hiw[3]};
-                const uint4 plo = {low[0], low[1], low[2], low[3]};
-#pragma unroll
-                for (int d = 0; d < DB; ++d) {
-                    const uint4 vb = *reinterpret_cast<const uint4 *>(Vt + (d * 32 + c) * VSTR + kk * 16 + hf * 8);
-                    o[bi][d] = mfma32(phi, vb, o[bi][d]);
-                    o[bi][d] = mfma32(plo, vb, o[bi][d]);
-                }
-            }
-        }
-    }
-    __syncthreads();
-
-    const int RP = kMaxRows * kMaxGroup;
-    const size_t pbase = ((size_t)kvh * a.ns + split) * RP;
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
-        const int rb = wave + 4 * bi;
-        if (rb >= RB) break;
-#pragma unroll
-        for (int d = 0; d < DB; ++d)
+        for (int kb = 0; kb < CH / 32; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = rb * 32 + acc_row(r, hf);
-                if (row < R) a.po[(pbase + row) * D + d * 32 + c] = o[bi][d][r];
+                const int j = kb * 32 + acc_row(r, hf);   // key within the chunk
+                bool vis = j < cn && rowok;
+                if (tree && vis) vis = (anc >> (c0 + j)) & 1u;
+                const float v = vis ? s[kb][r] * a.scale : -INFINITY;
+                s[kb][r] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(mrun, mx);
+        float alpha;
+        if (mnew == -INFINITY) {
+            alpha = 1.f;
+        } else {
+            alpha = (mrun == -INFINITY) ? 0.f : expf(mrun - mnew);
+        }
+        float ls = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < CH / 32; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = (s[kb][r] == -INFINITY) ? 0.f : expf(s[kb][r] - mnew);
+                s[kb][r] = p;
+                ls += p;
+            }
+        ls += __shfl_xor(ls, 32);
+        lrun = lrun * alpha + ls;
+        mrun = mnew;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+
+        // O^T += V^T P^T over 16-key steps (kb, h): lane hf supplies keys
+        // kb*32 + 16h + {4hf..4hf+3, 8+4hf..8+4hf+3} = its accumulators r = 8h..8h+7
+#pragma unroll
+        for (int kb = 0; kb < CH / 32; ++kb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p0 = s[kb][8 * h + 2 * e], p1 = s[kb][8 * h + 2 * e + 1];
+                    const uint16_t h0 = f2bf(p0), h1 = f2bf(p1);
+                    const uint16_t l0 = f2bf(p0 - bf2f(h0)), l1 = f2bf(p1 - bf2f(h1));
+                    hw[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                    lw[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+                }
+                const uint4 phi = {hw[0], hw[1], hw[2], hw[3]}, plo = {lw[0], lw[1], lw[2], lw[3]};
+                const int k0 = kb * 32 + 16 * h + 4 * hf;
+#pragma unroll
+                for (int d = 0; d < NDB; ++d) {
+                    const uint16_t *vr = Vt + (d * 32 + c) * VSTR;
+                    const uint2 v0 = *reinterpret_cast<const uint2 *>(vr + k0);
+                    const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + k0 + 8);
+                    const uint4 va = {v0.x, v0.y, v1.x, v1.y};
+                    o[d] = mfma32(va, phi, o[d]);
+                    o[d] = mfma32(va, plo, o[d]);
+                }
             }
     }
-    for (int r = tid; r < R; r += 256) {
-        a.pm[pbase + r] = mrow[r];
-        a.pl[pbase + r] = lrow[r];
+
+    if (!rowok || hf > 1) return;
+    const int RP = kMaxRows * kMaxGroup;
+    const size_t pb = ((size_t)kvh * a.ns + split) * RP + row;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a.po[pb * D + d * 32 + acc_row(r, hf)] = o[d][r];
+    if (hf == 0) {
+        a.pm[pb] = mrun;
+        a.pl[pb] = lrun;
     }
 }
 
@@ -674,13 +679,12 @@ hipError_t launch_gemm(hipStream_t s, int epi, const GemmArgs &a, int splits) {
 
 hipError_t launch_splitk_reduce(hipStream_t s, int epi, const GemmArgs &a, int splits) {
     const int rowblocks = ((a.N + 31) / 32 + 3) / 4;
-    const dim3 grid(rowblocks), block(256);
+    const dim3 grid(rowblocks * 16), block(256);
     switch (epi) {
     case EPI_BF16: hipLaunchKernelGGL((k_splitk_reduce<EPI_BF16>), grid, block, 0, s, a, splits); break;
     case EPI_RESID: hipLaunchKernelGGL((k_splitk_reduce<EPI_RESID>), grid, block, 0, s, a, splits); break;
     case EPI_SWIGLU: hipLaunchKernelGGL((k_splitk_reduce<EPI_SWIGLU>), grid, block, 0, s, a, splits); break;
-    case EPI_HEAD: hipLaunchKernelGGL((k_splitk_reduce<EPI_HEAD>), grid, block, 0, s, a, splits); break;
-    default: return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;   // the head runs unsplit
     }
     return hipGetLastError();
 }
@@ -698,9 +702,10 @@ hipError_t launch_rope_kv(hipStream_t s, const RopeArgs &a) {
 }
 
 hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a) {
-    const dim3 grid(a.ns, a.n_qhead / a.G);
-    if (D == 128) hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, s, a);
-    else if (D == 64) hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), 0, s, a);
+    const int rb = (a.G * a.n + 31) / 32;
+    const dim3 grid(a.ns, a.n_qhead / a.G), block(64 * rb);
+    if (D == 128) hipLaunchKernelGGL(k_attn<128>, grid, block, 0, s, a);
+    else if (D == 64) hipLaunchKernelGGL(k_attn<64>, grid, block, 0, s, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -253,8 +253,9 @@ int pack_inplace(tv_ctx *c, void *ptr, int N, int K) {
 
 int gemm(tv_ctx *c, const char *name, int epi, GemmArgs g) {
     g.partial = c->gemm_partial;
-    const int S = gemm_splits(g.N, g.K);
-    if (gemm_partial_need(g.N, g.K, epi == EPI_SWIGLU) > c->gemm_partial_floats)
+    // the head's top-2 epilogue needs whole sums in the kernel: it never splits
+    const int S = epi == EPI_HEAD ? 1 : gemm_splits(g.N, g.K);
+    if (S > 1 && gemm_partial_need(g.N, g.K, epi == EPI_SWIGLU) > c->gemm_partial_floats)
         return fail(c, TV_EINVAL, "GEMM N=%d K=%d needs more split-K scratch than allocated", g.N, g.K);
     LAUNCH(c, name, launch_gemm(c->stream, epi, g, S));
     if (S > 1) LAUNCH(c, name, launch_splitk_reduce(c->stream, epi, g, S));
@@ -354,7 +355,8 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
                 aa.po = c->po; aa.pm = c->pm; aa.pl = c->pl;
                 aa.row0 = row0s[r]; aa.n = n_nodes[r]; aa.ctx = q.ctx_len; aa.cap = m.max_ctx;
                 aa.G = c->G; aa.n_qhead = QH;
-                aa.n_ctx_split = (q.ctx_len + kAttnSplit - 1) / kAttnSplit;
+                aa.span = attn_span(q.ctx_len);
+                aa.n_ctx_split = (q.ctx_len + aa.span - 1) / aa.span;
                 aa.ns = aa.n_ctx_split + 1;
                 aa.scale = (float)(1.0 / std::sqrt((double)D));
                 LAUNCH(c, "attn", launch_attn(s, D, aa));
@@ -391,8 +393,8 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
         g.Yf = out; g.ldyf = m.vocab; g.part = c->part; g.meta = c->d_meta; g.mods_on = any_mods;
         GEMM(c, "gemm_head", EPI_HEAD, g);
     }
-    LAUNCH(c, "top2", launch_top2_reduce(s, c->part, (m.vocab + 31) / 32, M, c->d_argmax, c->d_gap,
-                                         c->d_top));
+    LAUNCH(c, "top2", launch_top2_reduce(s, c->part, ((m.vocab + 31) / 32 + 3) / 4, M, c->d_argmax,
+                                         c->d_gap, c->d_top));
     HIPCHECK(c, hipMemcpyAsync(c->h_argmax, c->d_argmax, M * sizeof(int32_t), hipMemcpyDeviceToHost, s));
     HIPCHECK(c, hipMemcpyAsync(c->h_gap, c->d_gap, M * sizeof(float), hipMemcpyDeviceToHost, s));
     HIPCHECK(c, hipStreamSynchronize(s));
@@ -455,7 +457,7 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     const int R = kMaxRows;
     const int H = m.hidden, D = m.head_dim;
     const size_t qkv = (size_t)std::max((m.n_qhead + 2 * m.n_kvhead) * D, 3 * m.n_qhead * D);
-    c->ns_max = (m.max_ctx + kAttnSplit - 1) / kAttnSplit + 1;
+    c->ns_max = 32 + 1;  // at most 32 cache splits (attn_span) plus the tree split
     const size_t RP = (size_t)kMaxRows * kMaxGroup;
     hipError_t e = hipSuccess;
 #define ALLOC(p, bytes) if (e == hipSuccess) e = hipMalloc((void **)&(p), (bytes))
@@ -789,7 +791,7 @@ int tv_head_top2(tv_ctx *c, const void *x, int M, float *logits_dev, int32_t *ar
     g.X = (const uint16_t *)x; g.ldx = m.hidden; g.W = c->head; g.M = M; g.N = m.vocab; g.K = m.hidden;
     g.Yf = logits_dev; g.ldyf = m.vocab; g.part = c->part;
     GEMM(c, "gemm_head", EPI_HEAD, g);
-    LAUNCH(c, "top2", launch_top2_reduce(s, c->part, (m.vocab + 31) / 32, M, c->d_argmax, c->d_gap, c->d_top));
+    LAUNCH(c, "top2", launch_top2_reduce(s, c->part, ((m.vocab + 31) / 32 + 3) / 4, M, c->d_argmax, c->d_gap, c->d_top));
     HIPCHECK(c, hipMemcpyAsync(c->h_argmax, c->d_argmax, M * 4, hipMemcpyDeviceToHost, s));
     HIPCHECK(c, hipMemcpyAsync(c->h_gap, c->d_gap, M * 4, hipMemcpyDeviceToHost, s));
     HIPCHECK(c, hipStreamSynchronize(s));
