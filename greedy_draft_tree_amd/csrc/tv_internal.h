@@ -97,6 +97,28 @@ struct RopeArgs {
     int row0, n, ctx, cap, QH, KVH, D;
 };
 
+struct RecurArgs {
+    const uint16_t *qkv;  // [rows, 3*QH*D]: q heads, k heads, v heads (bf16)
+    const uint16_t *a;    // [rows, QH] gate pre-activations (bf16)
+    const float *S0;      // [QH][D][D] state before the round (key index, value index)
+    const PassMeta *meta;
+    uint16_t *out;        // [rows, QH*D] read-out (bf16)
+    uint16_t *save_k;     // [kMaxRows][QH][D] normalised keys of this layer (request-local node order)
+    uint16_t *save_v;     // [kMaxRows][QH][D] values
+    float *save_gc;       // [kMaxRows][QH] cumulative log-gates
+    int row0, n, QH;
+    float eps;
+};
+
+struct RecurCommitArgs {
+    float *const *states;   // [n_layers] bound states, [QH][D][D] each
+    const uint16_t *save_k; // [n_layers][kMaxRows][QH][D]
+    const uint16_t *save_v;
+    const float *save_gc;   // [n_layers][kMaxRows][QH]
+    const int *path;
+    int path_len, QH;
+};
+
 // launch wrappers (tv_kernels.hip); each returns hipGetLastError()
 hipError_t launch_embed(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H,
                         uint16_t *X);
@@ -110,6 +132,8 @@ hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a);
 hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t *out);
 hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M, int32_t *argmax,
                               float *gap, float *top);
+hipError_t launch_recur_tree(hipStream_t s, int D, const RecurArgs &a);
+hipError_t launch_recur_commit(hipStream_t s, int D, const RecurCommitArgs &a, int n_layers);
 hipError_t launch_commit_kv(hipStream_t s, uint16_t *const *kv_ptrs, int n_layers, int KVH,
                             int cap, int D, int ctx, const int *path, int path_len);
 

@@ -619,6 +619,128 @@ __global__ __launch_bounds__(D) void k_attn_combine(AttnArgs a, uint16_t *__rest
     out[(size_t)(a.row0 + t) * a.n_qhead * D + h * D + d] = f2bf(O / L);
 }
 
+// ------------------------------------------------------- gated recurrence
+// Tree verify through a gated linear recurrence layer ("Drafters and tree
+// verify", Tree verify through recurrent layers).  Per head, the state after
+// node t is e^{g_t} S(parent) + k_t v_t^T; unrolled along the root-to-t path,
+//   o_t = S(t)^T q_t = e^{gc_t} S0^T q_t + sum_{s in anc*(t)} e^{gc_t - gc_s} (q_t . k_s) v_s
+// with gc the cumulative log-gate along the path, so no node overwrites its
+// parent's state.  q and k are L2-normalised per head and rounded to bf16,
+// g = log sigmoid(a).  One workgroup per head; it also saves k, v and gc of
+// every node for the commit.
+
+__device__ __forceinline__ float log_sigmoid(float a) {
+    return a >= 0.f ? -log1pf(expf(-a)) : a - log1pf(expf(a));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
+    __shared__ float qs[kMaxRows][D], ks[kMaxRows][D], vs[kMaxRows][D];
+    __shared__ float gsh[kMaxRows], gcs[kMaxRows], scale[2][kMaxRows];
+    __shared__ float coef[kMaxRows][kMaxRows + 1];
+    const int h = blockIdx.x, tid = threadIdx.x, n = r.n, QH = r.QH;
+    const int ld = 3 * QH * D;
+    for (int idx = tid; idx < n * D; idx += 256) {
+        const int t = idx / D, d = idx % D;
+        const uint16_t *row = r.qkv + (size_t)(r.row0 + t) * ld;
+        qs[t][d] = bf2f(row[h * D + d]);
+        ks[t][d] = bf2f(row[(QH + h) * D + d]);
+        vs[t][d] = bf2f(row[(2 * QH + h) * D + d]);
+    }
+    if (tid < n) gsh[tid] = log_sigmoid(bf2f(r.a[(size_t)(r.row0 + tid) * QH + h]));
+    __syncthreads();
+    if (tid < 2 * n) {
+        const int t = tid >> 1;
+        const float *x = (tid & 1) ? ks[t] : qs[t];
+        float ss = 0.f;
+        for (int d = 0; d < D; ++d) ss += x[d] * x[d];
+        scale[tid & 1][t] = 1.0f / sqrtf(ss + r.eps);
+    }
+    if (tid < n) {
+        // cumulative gate over the ancestors, root first (ancestors have lower indices)
+        const uint32_t anc = r.meta->anc[r.row0 + tid];
+        float gc = 0.f;
+        for (int s = 0; s <= tid; ++s)
+            if ((anc >> s) & 1u) gc += gsh[s];
+        gcs[tid] = gc;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < n * D; idx += 256) {
+        const int t = idx / D, d = idx % D;
+        qs[t][d] = bfround(qs[t][d] * scale[0][t]);
+        ks[t][d] = bfround(ks[t][d] * scale[1][t]);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < n * n; idx += 256) {
+        const int t = idx / n, s = idx % n;
+        float cf = 0.f;
+        if ((r.meta->anc[r.row0 + t] >> s) & 1u) {
+            float dot = 0.f;
+            for (int d = 0; d < D; ++d) dot += qs[t][d] * ks[s][d];
+            cf = expf(gcs[t] - gcs[s]) * dot;
+        }
+        coef[t][s] = cf;
+    }
+    __syncthreads();
+    // read-out: thread -> value index v, nodes t = grp, grp + G2, ...
+    constexpr int G2 = 256 / D;
+    const int v = tid % D, grp = tid / D;
+    float acc[kMaxRows / G2];
+#pragma unroll
+    for (int j = 0; j < kMaxRows / G2; ++j) acc[j] = 0.f;
+    const float *S0 = r.S0 + (size_t)h * D * D;
+    for (int k = 0; k < D; ++k) {
+        const float s0 = S0[k * D + v];
+#pragma unroll
+        for (int j = 0; j < kMaxRows / G2; ++j) {
+            const int t = grp + j * G2;
+            if (t < n) acc[j] += s0 * qs[t][k];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxRows / G2; ++j) {
+        const int t = grp + j * G2;
+        if (t >= n) continue;
+        float o = expf(gcs[t]) * acc[j];
+        for (int s = 0; s <= t; ++s) o += coef[t][s] * vs[s][v];
+        r.out[(size_t)(r.row0 + t) * QH * D + h * D + v] = f2bf(o);
+        r.save_k[((size_t)t * QH + h) * D + v] = f2bf(ks[t][v]);
+        r.save_v[((size_t)t * QH + h) * D + v] = f2bf(vs[t][v]);
+    }
+    if (tid < n) r.save_gc[(size_t)tid * QH + h] = gcs[tid];
+}
+
+// State commit: the state after the accepted path from the quantities the
+// verify saved ("Drafters and tree verify", Tree verify through recurrent
+// layers: S_path = e^{gc_last} S0 + sum over the path of e^{gc_last - gc_t}
+// k_t (x) v_t), in place; one read and write of the state, no weights.
+template <int D>
+__global__ __launch_bounds__(256) void k_recur_commit(RecurCommitArgs a) {
+    __shared__ float kk[kMaxRows][D], vv[kMaxRows][D], w[kMaxRows];
+    __shared__ float elast;
+    const int l = blockIdx.x / a.QH, h = blockIdx.x % a.QH, tid = threadIdx.x, QH = a.QH;
+    const int L = a.path_len;
+    const uint16_t *sk = a.save_k + (size_t)l * kMaxRows * QH * D;
+    const uint16_t *sv = a.save_v + (size_t)l * kMaxRows * QH * D;
+    const float *sg = a.save_gc + (size_t)l * kMaxRows * QH;
+    for (int idx = tid; idx < L * D; idx += 256) {
+        const int d = idx / D, e = idx % D, node = a.path[d];
+        kk[d][e] = bf2f(sk[((size_t)node * QH + h) * D + e]);
+        vv[d][e] = bf2f(sv[((size_t)node * QH + h) * D + e]);
+    }
+    const float gl = sg[(size_t)a.path[L - 1] * QH + h];
+    if (tid < L) w[tid] = expf(gl - sg[(size_t)a.path[tid] * QH + h]);
+    if (tid == 0) elast = expf(gl);
+    __syncthreads();
+    float *S = a.states[l] + (size_t)h * D * D;
+    for (int idx = tid; idx < D * D; idx += 256) {
+        const int i = idx / D, j = idx % D;
+        float s = elast * S[idx];
+        for (int d = 0; d < L; ++d) s += (w[d] * kk[d][i]) * vv[d][j];
+        S[idx] = s;
+    }
+}
+
 // ---------------------------------------------------------------- commit
 // Gather the accepted path's KV rows: slot ctx+path[d] -> ctx+d.  One
 // workgroup per (layer, KV head) reads every moved row before writing any,
@@ -721,6 +843,21 @@ hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t
 hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M, int32_t *argmax,
                               float *gap, float *top) {
     hipLaunchKernelGGL(k_top2_reduce, dim3(M), dim3(256), 0, s, part, ntiles, argmax, gap, top);
+    return hipGetLastError();
+}
+
+hipError_t launch_recur_tree(hipStream_t s, int D, const RecurArgs &a) {
+    if (D == 128) hipLaunchKernelGGL(k_recur_tree<128>, dim3(a.QH), dim3(256), 0, s, a);
+    else if (D == 64) hipLaunchKernelGGL(k_recur_tree<64>, dim3(a.QH), dim3(256), 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_recur_commit(hipStream_t s, int D, const RecurCommitArgs &a, int n_layers) {
+    const dim3 grid(n_layers * a.QH);
+    if (D == 128) hipLaunchKernelGGL(k_recur_commit<128>, grid, dim3(256), 0, s, a);
+    else if (D == 64) hipLaunchKernelGGL(k_recur_commit<64>, grid, dim3(256), 0, s, a);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

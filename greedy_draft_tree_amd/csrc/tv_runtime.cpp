@@ -38,6 +38,11 @@ struct Req {
     // device pointer table {K0, V0, K1, V1, ...} over attention layers
     uint16_t **d_kvtab = nullptr;
     bool kvtab_dirty = true;
+    // recurrent layers: bound state table and the last verify's saved k, v, gc
+    float **d_stab = nullptr;
+    bool stab_dirty = true;
+    uint16_t *save_k = nullptr, *save_v = nullptr;
+    float *save_gc = nullptr;
 };
 
 struct ProfRec {
@@ -51,6 +56,8 @@ struct tv_ctx {
     tv_model_desc m{};
     std::vector<int> kinds;
     std::vector<int> attn_layers;
+    std::vector<int> recur_layers;
+    std::vector<int> recur_index;   // layer -> position in recur_layers (or -1)
     hipStream_t stream = nullptr;
     std::string err;
     int G = 1;
@@ -63,7 +70,7 @@ struct tv_ctx {
 
     // scratch (library-owned)
     uint16_t *X = nullptr, *XN = nullptr, *QKV = nullptr, *QR = nullptr, *ATT = nullptr,
-             *ACT = nullptr;
+             *ACT = nullptr, *ABUF = nullptr;
     float *logits = nullptr;  // [32, V] when the caller passes none
     Top2 *part = nullptr;
     float *po = nullptr, *pm = nullptr, *pl = nullptr;
@@ -268,6 +275,18 @@ int gemm(tv_ctx *c, const char *name, int epi, GemmArgs g) {
         if (rc_) return rc_;                \
     } while (0)
 
+int upload_stab(tv_ctx *c, Req &q) {
+    if (!q.stab_dirty || c->recur_layers.empty()) return TV_OK;
+    std::vector<float *> tab;
+    for (int l : c->recur_layers) tab.push_back(q.S[l]);
+    if (!q.d_stab) HIPCHECK(c, hipMalloc(&q.d_stab, tab.size() * sizeof(void *)));
+    HIPCHECK(c, hipMemcpyAsync(q.d_stab, tab.data(), tab.size() * sizeof(void *), hipMemcpyHostToDevice,
+                               c->stream));
+    HIPCHECK(c, hipStreamSynchronize(c->stream));
+    q.stab_dirty = false;
+    return TV_OK;
+}
+
 // One forward pass over `total` rows of up to 32, request after request.
 int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parents,
              const int32_t *const *tokens, const int *n_nodes, float *logits_dev, int32_t *argmax,
@@ -294,6 +313,8 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
     }
     for (int r = 0; r < n_req; ++r) {
         int rc = upload_kvtab(c, c->reqs[reqs[r]]);
+        if (rc) return rc;
+        rc = upload_stab(c, c->reqs[reqs[r]]);
         if (rc) return rc;
     }
 
@@ -363,7 +384,26 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
                 LAUNCH(c, "attn_combine", launch_attn_combine(s, D, aa, c->ATT));
             }
         } else {
-            return fail(c, TV_EINVAL, "recurrent layers are not available in this build");
+            const int rl = c->recur_index[l];
+            GemmArgs g{};
+            g.X = c->XN; g.ldx = H; g.W = c->wqkv[l]; g.M = M; g.N = 3 * QH * D; g.K = H;
+            g.Y = c->QKV; g.ldy = g.N;
+            GEMM(c, "gemm_qkv", EPI_BF16, g);
+            GemmArgs ga{};
+            ga.X = c->XN; ga.ldx = H; ga.W = c->wa[l]; ga.M = M; ga.N = QH; ga.K = H;
+            ga.Y = c->ABUF; ga.ldy = QH;
+            GEMM(c, "gemm_gate", EPI_BF16, ga);
+            for (int r = 0; r < n_req; ++r) {
+                Req &q = c->reqs[reqs[r]];
+                RecurArgs ra{};
+                ra.qkv = c->QKV; ra.a = c->ABUF; ra.S0 = q.S[l]; ra.meta = c->d_meta; ra.out = c->ATT;
+                const size_t per = (size_t)kMaxRows * QH * D;
+                ra.save_k = q.save_k + rl * per;
+                ra.save_v = q.save_v + rl * per;
+                ra.save_gc = q.save_gc + (size_t)rl * kMaxRows * QH;
+                ra.row0 = row0s[r]; ra.n = n_nodes[r]; ra.QH = QH; ra.eps = m.eps;
+                LAUNCH(c, "recur_tree", launch_recur_tree(s, D, ra));
+            }
         }
         {
             GemmArgs g{};
@@ -439,7 +479,13 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
             delete c;
             return TV_EINVAL;
         }
-        if (c->kinds[l] == TV_LAYER_ATTN) c->attn_layers.push_back(l);
+        c->recur_index.push_back(-1);
+        if (c->kinds[l] == TV_LAYER_ATTN) {
+            c->attn_layers.push_back(l);
+        } else {
+            c->recur_index[l] = (int)c->recur_layers.size();
+            c->recur_layers.push_back(l);
+        }
     }
     c->m.layer_kind = nullptr;
     c->stream = (hipStream_t)stream;
@@ -467,6 +513,15 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     ALLOC(c->QR, (size_t)R * m.n_qhead * D * 2);
     ALLOC(c->ATT, (size_t)R * m.n_qhead * D * 2);
     ALLOC(c->ACT, (size_t)R * m.ffn * 2);
+    ALLOC(c->ABUF, (size_t)R * m.n_qhead * 2);
+    if (!c->recur_layers.empty()) {
+        const size_t nrl = c->recur_layers.size();
+        for (auto &q : c->reqs) {
+            ALLOC(q.save_k, nrl * R * m.n_qhead * D * 2);
+            ALLOC(q.save_v, nrl * R * m.n_qhead * D * 2);
+            ALLOC(q.save_gc, nrl * R * m.n_qhead * 4);
+        }
+    }
     ALLOC(c->logits, (size_t)R * m.vocab * 4);
     ALLOC(c->part, (size_t)((m.vocab + 31) / 32) * 32 * sizeof(Top2));
     ALLOC(c->po, (size_t)m.n_kvhead * c->ns_max * RP * D * 4);
@@ -519,7 +574,7 @@ void tv_destroy(tv_ctx *c) {
     if (!c) return;
     if (c->stream) hipStreamSynchronize(c->stream);
     else hipDeviceSynchronize();
-    void *dev[] = {c->X, c->XN, c->QKV, c->QR, c->ATT, c->ACT, c->logits, c->part, c->po, c->pm, c->pl,
+    void *dev[] = {c->X, c->XN, c->QKV, c->QR, c->ATT, c->ACT, c->ABUF, c->logits, c->part, c->po, c->pm, c->pl,
                    c->rope_cos, c->rope_sin, c->d_meta, c->d_argmax, c->d_gap, c->d_top, c->d_path,
                    c->gemm_partial};
     for (void *p : dev)
@@ -529,6 +584,10 @@ void tv_destroy(tv_ctx *c) {
         if (q.d_bias) hipFree(q.d_bias);
         if (q.d_allow) hipFree(q.d_allow);
         if (q.d_kvtab) hipFree(q.d_kvtab);
+        if (q.d_stab) hipFree(q.d_stab);
+        if (q.save_k) hipFree(q.save_k);
+        if (q.save_v) hipFree(q.save_v);
+        if (q.save_gc) hipFree(q.save_gc);
     }
     void *host[] = {c->h_meta, c->h_argmax, c->h_gap, c->h_path};
     for (void *p : host)
@@ -605,6 +664,7 @@ int tv_bind(tv_ctx *c, const char *name, void *ptr, size_t bytes) {
             if (at) return fail(c, TV_EINVAL, "%s: not a recurrent layer", name);
             if ((rc = want(QH * D * D * 4))) return rc;
             q.S[l] = (float *)ptr;
+            q.stab_dirty = true;
             return TV_OK;
         }
         return fail(c, TV_EINVAL, "unknown tensor %s", name);
@@ -711,9 +771,15 @@ int tv_commit(tv_ctx *c, int req, const int32_t *path, int path_len) {
     bool moves = false;
     for (int d = 0; d < path_len; ++d) moves |= path[d] != d;
     hipStream_t s = c->stream;
+    memcpy(c->h_path, path, path_len * sizeof(int32_t));
+    HIPCHECK(c, hipMemcpyAsync(c->d_path, c->h_path, path_len * sizeof(int32_t), hipMemcpyHostToDevice, s));
+    if (!c->recur_layers.empty()) {
+        RecurCommitArgs ra{};
+        ra.states = q.d_stab; ra.save_k = q.save_k; ra.save_v = q.save_v; ra.save_gc = q.save_gc;
+        ra.path = c->d_path; ra.path_len = path_len; ra.QH = c->m.n_qhead;
+        LAUNCH(c, "commit_state", launch_recur_commit(s, c->m.head_dim, ra, (int)c->recur_layers.size()));
+    }
     if (moves && !c->attn_layers.empty()) {
-        memcpy(c->h_path, path, path_len * sizeof(int32_t));
-        HIPCHECK(c, hipMemcpyAsync(c->d_path, c->h_path, path_len * sizeof(int32_t), hipMemcpyHostToDevice, s));
         LAUNCH(c, "commit_kv", launch_commit_kv(s, q.d_kvtab, (int)c->attn_layers.size(), c->m.n_kvhead,
                                                 c->m.max_ctx, c->m.head_dim, q.ctx_len, c->d_path, path_len));
     }

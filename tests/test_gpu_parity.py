@@ -53,12 +53,25 @@ def check_rows(gpu_logits, gpu_argmax, gpu_gap, orc_logits, parents, tokens, his
     np.testing.assert_array_equal(gpu_gap[:n], own_gap.astype(np.float32),
                                   err_msg=f"{what}: gap vs own logits")
     am, gap = oracle.tree_decisions(orc_logits, parents, tokens, history, mods)
-    ties = 0
+    ties, drift = 0, 0
     for i in range(n):
         if gpu_argmax[i] != am[i]:
-            assert gap[i] <= 1.0, f"{what}: row {i} argmax {gpu_argmax[i]} vs {am[i]} at gap {gap[i]:.3f} ulp"
-            ties += 1
-    return am, gap, ties
+            if gap[i] <= 1.0:
+                ties += 1
+                continue
+            # Beyond one ulp a flip is accepted only where the row's measured
+            # bf16 drift (the oracle's own rounded-vs-exact spread, not the
+            # GPU) can explain it: two results within tol of each other can
+            # order two scores differently only when they are within 2*tol.
+            scores = oracle.apply_modifiers(orc_logits[i], list(history) +
+                                            oracle.path_tokens(parents, tokens, i), mods)
+            a, l1, l2, _ = oracle.top2(scores)
+            assert orc_exact is not None and l1 - l2 <= 2 * tol[i], \
+                f"{what}: row {i} argmax {gpu_argmax[i]} vs {am[i]} at gap {gap[i]:.3f} ulp"
+            drift += 1
+    if drift:
+        print(f"[{what}] argmax flips beyond 1 ulp within the row's bf16 drift: {drift}", flush=True)
+    return am, gap, ties + drift
 
 
 # ------------------------------------------------------------------ C0
@@ -275,3 +288,164 @@ def test_c1_tree_rows(c1, n, ctx):
     _, _, ties = check_rows(gl, am, gap, ol, parents, tokens, seq.history, what=f"c1 n={n} ctx={ctx}",
                             orc_exact=oe)
     print(f"[c1 n={n} ctx={ctx}] near-tie argmax differences: {ties}", flush=True)
+
+
+# ------------------------------------------------------------- hybrid (C3 layer mix)
+
+HYB0 = synth.scaled(synth.C0, "c0_hybrid", n_layer=4, kinds=[1, 1, 1, 0])
+
+
+@pytest.fixture(scope="module")
+def hyb0():
+    _gpu()
+    import workloads
+    wl = workloads.build(HYB0, max_ctx=256, max_req=1, weight_device="cuda", host_copy=True)
+    return wl, oracle.Oracle(HYB0, wl.host_weights)
+
+
+def _load_states(wl, req, s0):
+    for l, t in wl.states[req].items():
+        t.copy_(s0[l].cuda())
+    torch.cuda.synchronize()
+
+
+def test_hybrid_c0_rounds_and_states(hyb0):
+    """Gated-recurrence layers: per-node rows, greedy rounds with commits of
+    the accepted path's state ("Drafters and tree verify", Tree verify
+    through recurrent layers), and the committed states themselves."""
+    wl, orc = hyb0
+    s0 = synth.state0(HYB0, seed=6)
+    _load_states(wl, 0, s0)
+    wl.tv.set_history(0, [], 0)
+    prompt = synth.uniform_ids(40, HYB0.vocab, 3)
+    wl.tv.prefill(0, prompt[:-1])
+    seq = orc.new_seq(cap=256, s0=s0)
+    seq.commit(prompt[:-1])
+    root = int(prompt[-1])
+    parents = synth.c0_tree()
+    rng = np.random.default_rng(11)
+    multi = 0
+    for r in range(12):
+        tokens = _greedy_drafter(orc, seq, root, parents, rng, r)
+        am, gap = wl.tv.verify_tree(0, parents, tokens, logits=wl.logits)
+        ol = orc.tree_scores(seq, parents, tokens)
+        check_rows(wl.logits[:8].cpu().numpy(), am, gap, ol, parents, tokens, seq.history,
+                   what=f"hybrid round {r}")
+        path, emitted = oracle.accept_walk(parents, tokens, am)
+        wl.tv.commit(0, path)
+        seq.commit([int(tokens[i]) for i in path])
+        multi += len(path) > 1
+        root = emitted[-1]
+    assert multi > 0
+    torch.cuda.synchronize()
+    for l, t in wl.states[0].items():
+        got = t.cpu().numpy().astype(np.float64)
+        want = seq.S[l]
+        err = np.abs(got - want).max()
+        print(f"[hybrid state layer {l}] max|dS| {err:.3g} max|S| {np.abs(want).max():.3g}", flush=True)
+        assert err <= 2e-2 * max(1.0, np.abs(want).max()), (l, err)
+
+
+HYB4 = synth.scaled(synth.C1, "c3_layers4", n_layer=4, kinds=[1, 1, 1, 0])
+
+
+def test_hybrid_full_width_tree_and_commit():
+    """The hybrid layer mix at full width (3 recurrent + 1 attention layers,
+    hidden 5120, 40 heads x 128x128 fp32 states) with a 16-node tree at 1k
+    context, then a commit of a multi-node path."""
+    _gpu()
+    import workloads
+    ctx = 1024
+    wl = workloads.build(HYB4, max_ctx=ctx + 32, max_req=1, weight_device="cuda", host_copy=True)
+    orc = oracle.Oracle(HYB4, wl.host_weights)
+    kv = synth.kv_cache(HYB4, ctx, seed=3, cap=ctx)
+    s0 = synth.state0(HYB4, seed=6)
+    hist = synth.uniform_ids(ctx, HYB4.vocab, 30)
+    workloads.load_context(wl, 0, ctx, 3, history=hist, src_kv={k: v.cuda() for k, v in kv.items()},
+                           src_states={l: v.cuda() for l, v in s0.items()})
+    seq = orc.new_seq(cap=ctx + 32, kv=kv, ctx_len=ctx, history=hist, s0=s0)
+    parents = synth.spine_tree(16, 4)
+    tokens = synth.tree_tokens(parents, HYB4.vocab, 21, root_token=int(hist[-1]))
+    am, gap = wl.tv.verify_tree(0, parents, tokens, logits=wl.logits)
+    ol = orc.tree_scores(seq, parents, tokens)
+    ex = oracle.Oracle(HYB4, wl.host_weights, exact=True)
+    oe = ex.tree_scores(ex.new_seq(cap=ctx + 32, kv=kv, ctx_len=ctx, history=hist, s0=s0), parents, tokens)
+    check_rows(wl.logits[:16].cpu().numpy(), am, gap, ol, parents, tokens, seq.history,
+               what="c3 layers x4 n=16", orc_exact=oe)
+    spine = synth.spine_nodes(parents)
+    path = spine[:5]
+    wl.tv.commit(0, path)
+    seq.commit([int(tokens[i]) for i in path])
+    torch.cuda.synchronize()
+    for l, t in wl.states[0].items():
+        got = t.cpu().numpy().astype(np.float64)
+        err = np.abs(got - seq.S[l]).max()
+        print(f"[c3 state layer {l}] max|dS| {err:.3g}", flush=True)
+        assert err <= 2e-2 * max(1.0, np.abs(seq.S[l]).max()), (l, err)
+
+
+# ------------------------------------------------------------- C4: joint + modifiers
+
+def test_c4_joint_modifiers_wrong_drafter(c1):
+    """Two requests verified in one pass (16 rows each, ctx 1024 and 8192)
+    with per-request score modifiers on every row ("Exactness", The promise:
+    penalties, logit_bias and masks applied as plain decoding applies them;
+    Parallel requests: each request's rows equal its alone verify).  A
+    wrong-on-purpose drafter yields exactly one token per round and the
+    request's greedy text."""
+    import workloads
+    wl, orc = c1
+    ctxs = (1024, 8192)
+    seqs, kvs = [], []
+    for r, ctx in enumerate(ctxs):
+        kv = synth.kv_cache(synth.C1, ctx, seed=40 + r, cap=ctx)
+        hist = synth.uniform_ids(ctx, synth.C1.vocab, 50 + r)
+        workloads.load_context(wl, r, ctx, 0, history=hist, src_kv={k: v.cuda() for k, v in kv.items()})
+        mods = synth.modifiers(synth.C1.vocab, seed=7 + r)
+        wl.tv.set_modifiers(r, mods.rep_penalty, mods.bias_ids, mods.bias_vals, mods.allow_bits)
+        seqs.append((orc.new_seq(cap=ctx + 40, kv=kv, ctx_len=ctx, history=hist), mods))
+        kvs.append(kv)
+    roots = [int(seqs[r][0].history[-1]) for r in range(2)]
+    for rnd in range(2):
+        trees = []
+        for r in range(2):
+            seq, mods = seqs[r]
+            parents = synth.spine_tree(16, 60 + r + rnd)
+            tokens = synth.tree_tokens(parents, synth.C1.vocab, 70 + r + rnd, root_token=roots[r])
+            # wrong on purpose: the root's children never carry the model's token
+            am, _ = wl.tv.verify_tree(r, parents, tokens)
+            for i in range(1, 16):
+                if parents[i] == 0 and tokens[i] == am[0]:
+                    tokens[i] = (int(am[0]) + 1 + i) % synth.C1.vocab
+            trees.append((parents, tokens))
+        _say("c4 round", rnd)
+        am_j, gap_j = wl.tv.verify_trees([0, 1], [t[0] for t in trees], [t[1] for t in trees],
+                                         logits=wl.logits)
+        joint = wl.logits[:32].clone()
+        for r in range(2):
+            parents, tokens = trees[r]
+            seq, mods = seqs[r]
+            am_a, gap_a = wl.tv.verify_tree(r, parents, tokens, logits=wl.logits)
+            assert torch.equal(wl.logits[:16], joint[16 * r:16 * r + 16]), "joint != alone"
+            np.testing.assert_array_equal(am_a, am_j[16 * r:16 * r + 16])
+            rows = orc.tree_scores(seq, parents, tokens, rows_wanted=[0, 1, 5])
+            ok = ~np.isnan(rows[:, 0])
+            sub = [i for i in range(16) if ok[i]]
+            ex = oracle.Oracle(synth.C1, orc.w_src, exact=True)
+            es = ex.new_seq(cap=seq.cap, kv=kvs[r], ctx_len=ctxs[r], history=seq.history)
+            rows_ex = ex.tree_scores(es, parents, tokens, rows_wanted=[0, 1, 5])
+            gl = joint[16 * r:16 * r + 16].cpu().numpy().astype(np.float64)
+            tol = np.maximum(LOGIT_ATOL, np.abs(rows[sub] - rows_ex[sub]).max(axis=1))
+            assert (np.abs(gl[sub] - rows[sub]).max(axis=1) <= tol).all()
+            own_am, own_gap = oracle.tree_decisions(gl, parents, tokens, seq.history, mods)
+            np.testing.assert_array_equal(am_a, own_am)
+            np.testing.assert_array_equal(gap_a, own_gap.astype(np.float32))
+            for i in sub:
+                prior = seq.history + oracle.path_tokens(parents, tokens, i)
+                a, _, _, g = oracle.top2(oracle.apply_modifiers(rows[i], prior, mods))
+                assert am_a[i] == a or g <= 1.0, (r, i, am_a[i], a, g)
+            path, emitted = oracle.accept_walk(parents, tokens, am_a)
+            assert len(emitted) == 1 and path == [0]
+            wl.tv.commit(r, path)
+            seq.commit([roots[r]])
+            roots[r] = emitted[0]
