@@ -160,8 +160,9 @@ def main():
             for n in NS:
                 round_(n)
         kernels = {}
-        for k in ("embed", "rmsnorm", "gemm_qkv", "rope_kv", "attn_combine", "attn", "gemm_o",
-                  "gemm_gateup", "gemm_down", "gemm_head", "top2", "commit_kv"):
+        for k in ("embed_norm", "resid_norm", "gemm_qkv", "rope_kv", "attn_combine", "attn", "gemm_o",
+                  "gemm_gateup", "gemm_down", "gemm_gate", "recur_tree", "gemm_head", "top2", "commit_kv",
+                  "commit_state"):
             ms, cnt = tv.profile_get(k)
             if cnt:
                 kernels[k] = {"avg_us": round(ms / cnt * 1e3, 2), "launches": cnt}

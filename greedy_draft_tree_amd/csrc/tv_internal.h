@@ -39,7 +39,8 @@ struct PassMeta {
     HeadMods mods[kMaxRows];     // per request slot
 };
 
-enum Epi { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3 };
+// EPI_PARTIAL: write the fp32 partial sums only (a consumer kernel finishes them)
+enum Epi { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3, EPI_PARTIAL = 4 };
 
 struct GemmArgs {
     const uint16_t *X;  // [M, K] bf16 activations, row stride ldx
@@ -89,7 +90,8 @@ inline int attn_span(int ctx) {
 }
 
 struct RopeArgs {
-    const uint16_t *qkv; // [rows, (QH+2KVH)*D]
+    const float *part;   // QKV projection partial sums (row-contiguous split-K layout)
+    int S;               // its k-range splits
     uint16_t *q_out;     // [rows, QH*D]
     uint16_t *Kc, *Vc;   // cache [KVH][cap][D]
     const float *cosT, *sinT; // [max_pos][D/2]
@@ -120,10 +122,10 @@ struct RecurCommitArgs {
 };
 
 // launch wrappers (tv_kernels.hip); each returns hipGetLastError()
-hipError_t launch_embed(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H,
-                        uint16_t *X);
-hipError_t launch_rmsnorm(hipStream_t s, const uint16_t *X, const uint16_t *w, int M, int H,
-                          float eps, uint16_t *Y);
+hipError_t launch_embed_norm(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H,
+                             float eps, const uint16_t *w, uint16_t *X, uint16_t *Y);
+hipError_t launch_resid_norm(hipStream_t s, const float *P, int S, int M, int H, float eps, const uint16_t *w,
+                             uint16_t *X, uint16_t *Y);
 hipError_t launch_gemm(hipStream_t s, int epi, const GemmArgs &a, int splits);
 hipError_t launch_splitk_reduce(hipStream_t s, int epi, const GemmArgs &a, int splits);
 hipError_t launch_pack(hipStream_t s, const uint16_t *src, uint16_t *dst, int N, int K, int t0, int nt);

@@ -67,42 +67,86 @@ __device__ __forceinline__ void top2_merge(float &v1, int &i1, float &v2, int &i
     }
 }
 
-// ------------------------------------------------------------------ embed
+// ------------------------------------------------------- split-K partials
+// Projections write fp32 partial sums row-contiguously: for 128-row block
+// rb, k-range s and accumulator j (gate/up use two), element (m, n) sits at
+// partial[((rb*S + s)*NACC + j)*4096 + m*128 + n%128].  A consumer adds the S
+// partials of an element in k-range order, so every element's sum order is
+// fixed by the weight shape.
 
-__global__ __launch_bounds__(256) void k_embed(const uint16_t *__restrict__ emb,
-                                               const PassMeta *__restrict__ meta, int H,
-                                               uint16_t *__restrict__ X) {
-    const int m = blockIdx.x;
-    const uint16_t *src = emb + (size_t)meta->tok[m] * H;
-    uint16_t *dst = X + (size_t)m * H;
-    for (int k = threadIdx.x * 8; k < H; k += 256 * 8)
-        *reinterpret_cast<uint4 *>(dst + k) = ld16(src + k);
+__device__ __forceinline__ float psum(const float *__restrict__ P, int S, int nacc, int j, int m, int n) {
+    const float *p = P + ((size_t)(n >> 7) * S * nacc + j) * 4096 + (size_t)m * 128 + (n & 127);
+    const size_t st = (size_t)nacc * 4096;
+    float s = 0.f;
+    int k = 0;
+    for (; k + 4 <= S; k += 4) {   // four loads in flight, adds kept in k order
+        const float a0 = p[k * st], a1 = p[(k + 1) * st], a2 = p[(k + 2) * st], a3 = p[(k + 3) * st];
+        s += a0;
+        s += a1;
+        s += a2;
+        s += a3;
+    }
+    for (; k < S; ++k) s += p[k * st];
+    return s;
 }
 
-// ---------------------------------------------------------------- rmsnorm
-// y = bf16(x / sqrt(mean(x^2) + eps) * w), one workgroup per row; the sum of
-// squares is reduced in a fixed order.
+// ------------------------------------------------------- norms (+ residual)
+// RMSNorm: y = bf16(x / sqrt(mean(x^2) + eps) * w), one workgroup per row,
+// the sum of squares reduced in a fixed order.  k_embed_norm gathers the
+// embedding row first; k_resid_norm first finishes a residual projection,
+// x = bf16(x + bf16(sum of the partials)), and stores x.
 
-__global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t *__restrict__ X,
-                                                 const uint16_t *__restrict__ w, int H, float eps,
-                                                 uint16_t *__restrict__ Y) {
-    __shared__ float red[256];
-    const int m = blockIdx.x, t = threadIdx.x;
-    const uint16_t *x = X + (size_t)m * H;
+constexpr int kMaxHidden = 8192;
+
+constexpr int kNormThreads = 1024;
+
+__device__ __forceinline__ void norm_row(const float *xs, int H, float eps, const uint16_t *__restrict__ w,
+                                         uint16_t *__restrict__ y, float *red) {
+    const int t = threadIdx.x;
     float ss = 0.f;
-    for (int k = t; k < H; k += 256) {
-        float v = bf2f(x[k]);
-        ss += v * v;
-    }
+    for (int k = t; k < H; k += kNormThreads) ss += xs[k] * xs[k];
     red[t] = ss;
     __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
+    for (int o = kNormThreads / 2; o > 0; o >>= 1) {
         if (t < o) red[t] += red[t + o];
         __syncthreads();
     }
     const float scale = 1.0f / sqrtf(red[0] / (float)H + eps);
-    uint16_t *y = Y + (size_t)m * H;
-    for (int k = t; k < H; k += 256) y[k] = f2bf(bf2f(x[k]) * scale * bf2f(w[k]));
+    for (int k = t; k < H; k += kNormThreads) y[k] = f2bf(xs[k] * scale * bf2f(w[k]));
+}
+
+__global__ __launch_bounds__(kNormThreads) void k_embed_norm(const uint16_t *__restrict__ emb,
+                                                    const PassMeta *__restrict__ meta, int H, float eps,
+                                                    const uint16_t *__restrict__ w, uint16_t *__restrict__ X,
+                                                    uint16_t *__restrict__ Y) {
+    __shared__ float xs[kMaxHidden], red[kNormThreads];
+    const int m = blockIdx.x;
+    const uint16_t *src = emb + (size_t)meta->tok[m] * H;
+    uint16_t *dst = X + (size_t)m * H;
+    for (int k = threadIdx.x * 8; k < H; k += kNormThreads * 8) {
+        const uint4 v = ld16(src + k);
+        *reinterpret_cast<uint4 *>(dst + k) = v;
+        const uint16_t *e = reinterpret_cast<const uint16_t *>(&v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) xs[k + q] = bf2f(e[q]);
+    }
+    __syncthreads();
+    norm_row(xs, H, eps, w, Y + (size_t)m * H, red);
+}
+
+__global__ __launch_bounds__(kNormThreads) void k_resid_norm(const float *__restrict__ P, int S, int H, float eps,
+                                                    const uint16_t *__restrict__ w, uint16_t *__restrict__ X,
+                                                    uint16_t *__restrict__ Y) {
+    __shared__ float xs[kMaxHidden], red[kNormThreads];
+    const int m = blockIdx.x;
+    uint16_t *x = X + (size_t)m * H;
+    for (int k = threadIdx.x; k < H; k += kNormThreads) {
+        const uint16_t v = f2bf(bf2f(x[k]) + bfround(psum(P, S, 1, 0, m, k)));
+        x[k] = v;
+        xs[k] = bf2f(v);
+    }
+    __syncthreads();
+    norm_row(xs, H, eps, w, Y + (size_t)m * H, red);
 }
 
 // ------------------------------------------------------------ skinny GEMM
@@ -258,16 +302,15 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
         }
     }
 
-    if (S > 1) {
-        // partial tile in the raw accumulator layout [rowblock][ks][wave][NACC][16][64];
-        // columns beyond M are zero and stay unwritten (the reduce never reads them)
+    if (S > 1 || EPI == EPI_PARTIAL) {
+        // partial sums, row-contiguous (see psum); columns beyond M stay unwritten
         if (c < g.M) {
-            float *mine = g.partial + (((size_t)blockIdx.x * S + ks) * 4 + wave) * NACC * 1024;
+            float *mine = g.partial + ((size_t)blockIdx.x * S + ks) * NACC * 4096 + (size_t)c * 128 + wave * 32;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mine[r * 64 + lane] = acc[r];
+            for (int r = 0; r < 16; ++r) mine[acc_row(r, hf)] = acc[r];
             if constexpr (DUAL) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mine[1024 + r * 64 + lane] = acc2[r];
+                for (int r = 0; r < 16; ++r) mine[4096 + acc_row(r, hf)] = acc2[r];
             }
         }
         return;
@@ -298,27 +341,19 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 // k-range order and applies the element's epilogue.
 template <int EPI>
 __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g, int S) {
-    constexpr bool DUAL = (EPI == EPI_SWIGLU);
-    constexpr int NACC = DUAL ? 2 : 1;
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;   // ((rb*4 + wave)*16 + r)*64 + lane
-    const int lane = (int)(idx & 63), r = (int)((idx >> 6) & 15), wave = (int)((idx >> 10) & 3);
-    const long rb = idx >> 12;
-    const int c = lane & 31, hf = lane >> 5;
-    const int n = (int)((rb * 4 + wave) * 32) + acc_row(r, hf);
-    if (c >= g.M || n >= g.N) return;
-    float acc = 0.f, acc2 = 0.f;
-    const float *p = g.partial + ((size_t)rb * S * 4 + wave) * NACC * 1024 + r * 64 + lane;
-    for (int k2 = 0; k2 < S; ++k2) {
-        acc += p[(size_t)k2 * 4 * NACC * 1024];
-        if constexpr (DUAL) acc2 += p[(size_t)k2 * 4 * NACC * 1024 + 1024];
-    }
-    uint16_t *y = g.Y + (size_t)c * g.ldy + n;
+    constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;   // (rb*32 + m)*128 + nl
+    const int nl = (int)(idx & 127), m = (int)((idx >> 7) & 31);
+    const int n = (int)((idx >> 12) * 128) + nl;
+    if (m >= g.M || n >= g.N) return;
+    const float acc = psum(g.partial, S, NACC, 0, m, n);
+    uint16_t *y = g.Y + (size_t)m * g.ldy + n;
     if constexpr (EPI == EPI_BF16) {
         *y = f2bf(acc);
     } else if constexpr (EPI == EPI_RESID) {
         *y = f2bf(bf2f(*y) + bfround(acc));
     } else if constexpr (EPI == EPI_SWIGLU) {
-        const float gt = bfround(acc), up = bfround(acc2);
+        const float gt = bfround(acc), up = bfround(psum(g.partial, S, NACC, 1, m, n));
         *y = f2bf(gt / (1.0f + expf(-gt)) * up);
     }
 }
@@ -400,34 +435,32 @@ __global__ __launch_bounds__(256) void k_top2_reduce(const Top2 *__restrict__ pa
 // and tree verify", Tree verify through recurrent layers: position = depth,
 // every node at its depth-first slot).
 
+// Grid (node, slice): thread u of a node handles one q pair, one k pair or
+// one v element: units [0, QH*D/2) q, then KVH*D/2 k, then KVH*D v.
 __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
     const int i = blockIdx.x;
     const int m = a.row0 + i;
     const int D = a.D, half = D / 2;
+    const int u = blockIdx.y * 256 + threadIdx.x;
+    const int nq = a.QH * half, nk = a.KVH * half, nv = a.KVH * D;
+    if (u >= nq + nk + nv) return;
     const int pos = a.ctx + a.meta->depth[m];
-    const uint16_t *row = a.qkv + (size_t)m * (a.QH + 2 * a.KVH) * D;
-    const float *cs = a.cosT + (size_t)pos * half;
-    const float *sn = a.sinT + (size_t)pos * half;
-    for (int idx = threadIdx.x; idx < a.QH * half; idx += 256) {
-        const int h = idx / half, p = idx % half;
-        const float x0 = bf2f(row[h * D + p]), x1 = bf2f(row[h * D + p + half]);
-        uint16_t *o = a.q_out + (size_t)m * a.QH * D + h * D;
-        o[p] = f2bf(x0 * cs[p] - x1 * sn[p]);
-        o[p + half] = f2bf(x1 * cs[p] + x0 * sn[p]);
-    }
-    const uint16_t *kr = row + a.QH * D;
-    const uint16_t *vr = kr + a.KVH * D;
+    // projection outputs: bf16 of the partial sums (the QKV projection's rounding point)
+    auto qkv = [&](int n) { return bfround(psum(a.part, a.S, 1, 0, m, n)); };
     const size_t slot = (size_t)(a.ctx + i);
-    for (int idx = threadIdx.x; idx < a.KVH * half; idx += 256) {
-        const int h = idx / half, p = idx % half;
-        const float x0 = bf2f(kr[h * D + p]), x1 = bf2f(kr[h * D + p + half]);
-        uint16_t *o = a.Kc + ((size_t)h * a.cap + slot) * D;
-        o[p] = f2bf(x0 * cs[p] - x1 * sn[p]);
-        o[p + half] = f2bf(x1 * cs[p] + x0 * sn[p]);
-    }
-    for (int idx = threadIdx.x; idx < a.KVH * D; idx += 256) {
-        const int h = idx / D, d = idx % D;
-        a.Vc[((size_t)h * a.cap + slot) * D + d] = vr[h * D + d];
+    if (u < nq + nk) {
+        const bool isq = u < nq;
+        const int uu = isq ? u : u - nq;
+        const int h = uu / half, p = uu % half;
+        const int col = (isq ? 0 : a.QH * D) + h * D + p;
+        const float x0 = qkv(col), x1 = qkv(col + half);
+        const float c = a.cosT[(size_t)pos * half + p], s = a.sinT[(size_t)pos * half + p];
+        uint16_t *o = isq ? a.q_out + (size_t)m * a.QH * D + h * D : a.Kc + ((size_t)h * a.cap + slot) * D;
+        o[p] = f2bf(x0 * c - x1 * s);
+        o[p + half] = f2bf(x1 * c + x0 * s);
+    } else {
+        const int uu = u - nq - nk, h = uu / D, d = uu % D;
+        a.Vc[((size_t)h * a.cap + slot) * D + d] = f2bf(qkv((a.QH + a.KVH) * D + h * D + d));
     }
 }
 
@@ -602,19 +635,25 @@ __global__ __launch_bounds__(320) void k_attn(AttnArgs a) {
 // Merge the splits of every (node, query head) in split order.
 template <int D>
 __global__ __launch_bounds__(D) void k_attn_combine(AttnArgs a, uint16_t *__restrict__ out) {
+    __shared__ float ms[64], wl[64], ws[64];
     const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
     const int G = a.G, kvh = h / G, row = t * G + (h % G);
     const int RP = kMaxRows * kMaxGroup;
+    const int ns = a.ns;
+    const size_t b0 = (size_t)kvh * ns * RP + row;
+    if (d < ns) {
+        ms[d] = a.pm[b0 + (size_t)d * RP];
+        wl[d] = a.pl[b0 + (size_t)d * RP];
+    }
+    __syncthreads();
     float M = -INFINITY;
-    for (int s = 0; s < a.ns; ++s) M = fmaxf(M, a.pm[((size_t)kvh * a.ns + s) * RP + row]);
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, ms[s]);
+    if (d < ns) ws[d] = (ms[d] == -INFINITY) ? 0.f : expf(ms[d] - M);
+    __syncthreads();
     float L = 0.f, O = 0.f;
-    for (int s = 0; s < a.ns; ++s) {
-        const size_t b = ((size_t)kvh * a.ns + s) * RP + row;
-        const float ms = a.pm[b];
-        if (ms == -INFINITY) continue;
-        const float w = expf(ms - M);
-        L += w * a.pl[b];
-        O += w * a.po[b * D + d];
+    for (int s = 0; s < ns; ++s) {
+        L += ws[s] * wl[s];
+        O += ws[s] * a.po[(b0 + (size_t)s * RP) * D + d];
     }
     out[(size_t)(a.row0 + t) * a.n_qhead * D + h * D + d] = f2bf(O / L);
 }
@@ -774,15 +813,15 @@ __global__ __launch_bounds__(256) void k_commit_kv(uint16_t *const *__restrict__
 
 // ------------------------------------------------------------ launchers
 
-hipError_t launch_embed(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H,
-                        uint16_t *X) {
-    hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, s, emb, meta, H, X);
+hipError_t launch_embed_norm(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H,
+                             float eps, const uint16_t *w, uint16_t *X, uint16_t *Y) {
+    hipLaunchKernelGGL(k_embed_norm, dim3(M), dim3(kNormThreads), 0, s, emb, meta, H, eps, w, X, Y);
     return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(hipStream_t s, const uint16_t *X, const uint16_t *w, int M, int H,
-                          float eps, uint16_t *Y) {
-    hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, s, X, w, H, eps, Y);
+hipError_t launch_resid_norm(hipStream_t s, const float *P, int S, int M, int H, float eps, const uint16_t *w,
+                             uint16_t *X, uint16_t *Y) {
+    hipLaunchKernelGGL(k_resid_norm, dim3(M), dim3(kNormThreads), 0, s, P, S, H, eps, w, X, Y);
     return hipGetLastError();
 }
 
@@ -794,6 +833,7 @@ hipError_t launch_gemm(hipStream_t s, int epi, const GemmArgs &a, int splits) {
     case EPI_RESID: hipLaunchKernelGGL((k_gemm<EPI_RESID>), grid, block, 0, s, a); break;
     case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm<EPI_SWIGLU>), grid, block, 0, s, a); break;
     case EPI_HEAD: hipLaunchKernelGGL((k_gemm<EPI_HEAD>), grid, block, 0, s, a); break;
+    case EPI_PARTIAL: hipLaunchKernelGGL((k_gemm<EPI_PARTIAL>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -801,7 +841,7 @@ hipError_t launch_gemm(hipStream_t s, int epi, const GemmArgs &a, int splits) {
 
 hipError_t launch_splitk_reduce(hipStream_t s, int epi, const GemmArgs &a, int splits) {
     const int rowblocks = ((a.N + 31) / 32 + 3) / 4;
-    const dim3 grid(rowblocks * 16), block(256);
+    const dim3 grid(rowblocks * 16), block(256);   // 4096 elements per row block
     switch (epi) {
     case EPI_BF16: hipLaunchKernelGGL((k_splitk_reduce<EPI_BF16>), grid, block, 0, s, a, splits); break;
     case EPI_RESID: hipLaunchKernelGGL((k_splitk_reduce<EPI_RESID>), grid, block, 0, s, a, splits); break;
@@ -819,7 +859,8 @@ hipError_t launch_pack(hipStream_t s, const uint16_t *src, uint16_t *dst, int N,
 }
 
 hipError_t launch_rope_kv(hipStream_t s, const RopeArgs &a) {
-    hipLaunchKernelGGL(k_rope_kv, dim3(a.n), dim3(256), 0, s, a);
+    const int units = a.QH * a.D / 2 + a.KVH * a.D / 2 + a.KVH * a.D;
+    hipLaunchKernelGGL(k_rope_kv, dim3(a.n, (units + 255) / 256), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -229,11 +229,11 @@ int upload_kvtab(tv_ctx *c, Req &q) {
     return TV_OK;
 }
 
-size_t gemm_partial_need(int N, int K, bool dual) {
+size_t gemm_partial_need(int N, int K, bool dual, bool always = false) {
     const int S = gemm_splits(N, K);
-    if (S <= 1) return 0;
+    if (S <= 1 && !always) return 0;
     const size_t rowblocks = (size_t)((N + 31) / 32 + 3) / 4;
-    return rowblocks * S * 4 * (dual ? 2 : 1) * 1024;
+    return rowblocks * S * (dual ? 2 : 1) * 4096;
 }
 
 // Rearrange a row-major [N, K] bf16 matrix in place into the packed tile
@@ -268,6 +268,22 @@ int gemm(tv_ctx *c, const char *name, int epi, GemmArgs g) {
     if (S > 1) LAUNCH(c, name, launch_splitk_reduce(c->stream, epi, g, S));
     return TV_OK;
 }
+
+// A projection whose consumer finishes the sums: partials only, *S = splits.
+int gemm_partial(tv_ctx *c, const char *name, GemmArgs g, int *S) {
+    g.partial = c->gemm_partial;
+    *S = gemm_splits(g.N, g.K);
+    if (gemm_partial_need(g.N, g.K, false, true) > c->gemm_partial_floats)
+        return fail(c, TV_EINVAL, "GEMM N=%d K=%d needs more split-K scratch than allocated", g.N, g.K);
+    LAUNCH(c, name, launch_gemm(c->stream, EPI_PARTIAL, g, *S));
+    return TV_OK;
+}
+
+#define GEMMP(c, nm, g, S)                          \
+    do {                                            \
+        int rc_ = gemm_partial((c), (nm), (g), &(S)); \
+        if (rc_) return rc_;                        \
+    } while (0)
 
 #define GEMM(c, nm, epi, g)                 \
     do {                                    \
@@ -355,22 +371,25 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
     HIPCHECK(c, hipMemcpyAsync(c->d_meta, c->h_meta, sizeof(PassMeta), hipMemcpyHostToDevice, s));
 
     const int H = m.hidden, D = m.head_dim, QH = m.n_qhead, KVH = m.n_kvhead;
-    LAUNCH(c, "embed", launch_embed(s, c->emb, c->d_meta, M, H, c->X));
+    // X: residual stream; XN: normalised input of the next projection.
+    LAUNCH(c, "embed_norm", launch_embed_norm(s, c->emb, c->d_meta, M, H, m.eps, c->attn_norm[0], c->X, c->XN));
     for (int l = 0; l < m.n_layer; ++l) {
-        LAUNCH(c, "rmsnorm", launch_rmsnorm(s, c->X, c->attn_norm[l], M, H, m.eps, c->XN));
         if (c->kinds[l] == TV_LAYER_ATTN) {
             GemmArgs g{};
             g.X = c->XN; g.ldx = H; g.W = c->wqkv[l]; g.M = M; g.N = (QH + 2 * KVH) * D; g.K = H;
-            g.Y = c->QKV; g.ldy = g.N;
-            GEMM(c, "gemm_qkv", EPI_BF16, g);
+            int S = 0;
+            GEMMP(c, "gemm_qkv", g, S);
             for (int r = 0; r < n_req; ++r) {
                 Req &q = c->reqs[reqs[r]];
                 RopeArgs ra{};
-                ra.qkv = c->QKV; ra.q_out = c->QR; ra.Kc = q.K[l]; ra.Vc = q.V[l];
+                ra.part = c->gemm_partial; ra.S = S; ra.q_out = c->QR; ra.Kc = q.K[l]; ra.Vc = q.V[l];
                 ra.cosT = c->rope_cos; ra.sinT = c->rope_sin; ra.meta = c->d_meta;
                 ra.row0 = row0s[r]; ra.n = n_nodes[r]; ra.ctx = q.ctx_len; ra.cap = m.max_ctx;
                 ra.QH = QH; ra.KVH = KVH; ra.D = D;
                 LAUNCH(c, "rope_kv", launch_rope_kv(s, ra));
+            }
+            for (int r = 0; r < n_req; ++r) {
+                Req &q = c->reqs[reqs[r]];
                 AttnArgs aa{};
                 aa.Q = c->QR; aa.Kc = q.K[l]; aa.Vc = q.V[l]; aa.meta = c->d_meta;
                 aa.po = c->po; aa.pm = c->pm; aa.pl = c->pl;
@@ -408,10 +427,10 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
         {
             GemmArgs g{};
             g.X = c->ATT; g.ldx = QH * D; g.W = c->wo[l]; g.M = M; g.N = H; g.K = QH * D;
-            g.Y = c->X; g.ldy = H;
-            GEMM(c, "gemm_o", EPI_RESID, g);
+            int S = 0;
+            GEMMP(c, "gemm_o", g, S);
+            LAUNCH(c, "resid_norm", launch_resid_norm(s, c->gemm_partial, S, M, H, m.eps, c->ffn_norm[l], c->X, c->XN));
         }
-        LAUNCH(c, "rmsnorm", launch_rmsnorm(s, c->X, c->ffn_norm[l], M, H, m.eps, c->XN));
         {
             GemmArgs g{};
             g.X = c->XN; g.ldx = H; g.W = c->wg[l]; g.W2 = c->wu[l]; g.M = M; g.N = m.ffn; g.K = H;
@@ -421,11 +440,12 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
         {
             GemmArgs g{};
             g.X = c->ACT; g.ldx = m.ffn; g.W = c->wd[l]; g.M = M; g.N = H; g.K = m.ffn;
-            g.Y = c->X; g.ldy = H;
-            GEMM(c, "gemm_down", EPI_RESID, g);
+            int S = 0;
+            GEMMP(c, "gemm_down", g, S);
+            const uint16_t *next = l + 1 < m.n_layer ? c->attn_norm[l + 1] : c->final_norm;
+            LAUNCH(c, "resid_norm", launch_resid_norm(s, c->gemm_partial, S, M, H, m.eps, next, c->X, c->XN));
         }
     }
-    LAUNCH(c, "rmsnorm", launch_rmsnorm(s, c->X, c->final_norm, M, H, m.eps, c->XN));
     float *out = logits_dev ? logits_dev : c->logits;
     {
         GemmArgs g{};
@@ -471,6 +491,7 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
         m.vocab < 2 || m.max_ctx < 1 || m.max_req < 1 || !m.layer_kind || m.eps <= 0.f)
         return TV_EINVAL;
     if (m.n_qhead / m.n_kvhead > 5) return TV_EINVAL;  // attention stages G*32 <= 160 query rows
+    if (m.hidden > 8192) return TV_EINVAL;              // norm kernels hold one row in LDS
     tv_ctx *c = new tv_ctx();
     c->m = m;
     c->kinds.assign(m.layer_kind, m.layer_kind + m.n_layer);
@@ -537,12 +558,12 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     {
         const int QD = m.n_qhead * D;
         size_t need = (size_t)8 << 20;  // room for kernel-level calls
-        need = std::max(need, gemm_partial_need((m.n_qhead + 2 * m.n_kvhead) * D, H, false));
+        need = std::max(need, gemm_partial_need((m.n_qhead + 2 * m.n_kvhead) * D, H, false, true));
         need = std::max(need, gemm_partial_need(3 * QD, H, false));
         need = std::max(need, gemm_partial_need(m.n_qhead, H, false));
-        need = std::max(need, gemm_partial_need(H, QD, false));
+        need = std::max(need, gemm_partial_need(H, QD, false, true));
         need = std::max(need, gemm_partial_need(m.ffn, H, true));
-        need = std::max(need, gemm_partial_need(H, m.ffn, false));
+        need = std::max(need, gemm_partial_need(H, m.ffn, false, true));
         need = std::max(need, gemm_partial_need(m.vocab, H, false));
         c->gemm_partial_floats = need;
     }
