@@ -40,6 +40,14 @@ __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
+// Weight streams are read once per pass: nontemporal loads keep them from
+// displacing the activations every workgroup re-reads from the caches.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const uint16_t *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return uint4{v.x, v.y, v.z, v.w};
+}
+
 // Row index inside a 32x32 MFMA output tile held by accumulator r of a lane
 // in half `hf` (lanes 0-31: hf 0, lanes 32-63: hf 1); the column is lane%32.
 __device__ __forceinline__ int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
@@ -284,8 +292,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
                 if (s >= s1 || !tok) off = -1;
                 else if (full) off = (long)s * 2048 + q * 512 + lane * 8;
                 else off = packed_piece(s, q, hf, c, nr, K);
-                a[u][q] = off >= 0 ? ld16(tb + off) : z;
-                if constexpr (DUAL) a2[u][q] = off >= 0 ? ld16(tb2 + off) : z;
+                a[u][q] = off >= 0 ? ld16_stream(tb + off) : z;
+                if constexpr (DUAL) a2[u][q] = off >= 0 ? ld16_stream(tb2 + off) : z;
             }
         }
         __syncthreads();   // stage(buf) visible; everyone is done with buf^1
