@@ -98,63 +98,79 @@ __device__ __forceinline__ float psum(const float *__restrict__ P, int S, int na
     return s;
 }
 
-// ------------------------------------------------------- norms (+ residual)
-// RMSNorm: y = bf16(x / sqrt(mean(x^2) + eps) * w), one workgroup per row,
-// the sum of squares reduced in a fixed order.  k_embed_norm gathers the
-// embedding row first; k_resid_norm first finishes a residual projection,
-// x = bf16(x + bf16(sum of the partials)), and stores x.
+// --------------------------------------------- residual stream + RMSNorm
+// RMSNorm is y = bf16(x / sqrt(mean(x^2) + eps) * w).  The residual kernels
+// below write x and, per row, kNormParts partial sums of squares over fixed
+// slices (each reduced in a fixed order); k_norm_apply adds the slices in
+// order, forms the row's scale and writes y.  Both are wide grids (many
+// workgroups per row).
+// k_embed_ss gathers the embedding row; k_resid_ss finishes a residual
+// projection, x = bf16(x + bf16(sum of the partials)).
 
-constexpr int kMaxHidden = 8192;
-
-constexpr int kNormThreads = 1024;
-
-__device__ __forceinline__ void norm_row(const float *xs, int H, float eps, const uint16_t *__restrict__ w,
-                                         uint16_t *__restrict__ y, float *red) {
+__device__ __forceinline__ void slice_ss(float ss, float *red, float *out) {
     const int t = threadIdx.x;
-    float ss = 0.f;
-    for (int k = t; k < H; k += kNormThreads) ss += xs[k] * xs[k];
     red[t] = ss;
     __syncthreads();
-    for (int o = kNormThreads / 2; o > 0; o >>= 1) {
+    for (int o = 128; o > 0; o >>= 1) {
         if (t < o) red[t] += red[t + o];
         __syncthreads();
     }
-    const float scale = 1.0f / sqrtf(red[0] / (float)H + eps);
-    for (int k = t; k < H; k += kNormThreads) y[k] = f2bf(xs[k] * scale * bf2f(w[k]));
+    if (t == 0) *out = red[0];
 }
 
-__global__ __launch_bounds__(kNormThreads) void k_embed_norm(const uint16_t *__restrict__ emb,
-                                                    const PassMeta *__restrict__ meta, int H, float eps,
-                                                    const uint16_t *__restrict__ w, uint16_t *__restrict__ X,
-                                                    uint16_t *__restrict__ Y) {
-    __shared__ float xs[kMaxHidden], red[kNormThreads];
-    const int m = blockIdx.x;
+__global__ __launch_bounds__(256) void k_embed_ss(const uint16_t *__restrict__ emb, const PassMeta *__restrict__ meta,
+                                                  int H, uint16_t *__restrict__ X, float *__restrict__ ssp) {
+    __shared__ float red[256];
+    const int m = blockIdx.x, part = blockIdx.y;
+    const int k0 = (H * part) / kNormParts, k1 = (H * (part + 1)) / kNormParts;
     const uint16_t *src = emb + (size_t)meta->tok[m] * H;
     uint16_t *dst = X + (size_t)m * H;
-    for (int k = threadIdx.x * 8; k < H; k += kNormThreads * 8) {
-        const uint4 v = ld16(src + k);
-        *reinterpret_cast<uint4 *>(dst + k) = v;
-        const uint16_t *e = reinterpret_cast<const uint16_t *>(&v);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) xs[k + q] = bf2f(e[q]);
+    float ss = 0.f;
+    for (int k = k0 + threadIdx.x; k < k1; k += 256) {
+        const uint16_t v = src[k];
+        dst[k] = v;
+        const float f = bf2f(v);
+        ss += f * f;
     }
-    __syncthreads();
-    norm_row(xs, H, eps, w, Y + (size_t)m * H, red);
+    slice_ss(ss, red, ssp + m * kNormParts + part);
 }
 
-__global__ __launch_bounds__(kNormThreads) void k_resid_norm(const float *__restrict__ P, int S, int H, float eps,
-                                                    const uint16_t *__restrict__ w, uint16_t *__restrict__ X,
+__global__ __launch_bounds__(256) void k_norm_apply(const uint16_t *__restrict__ X, const float *__restrict__ ssp,
+                                                    const uint16_t *__restrict__ w, int H, float eps,
                                                     uint16_t *__restrict__ Y) {
-    __shared__ float xs[kMaxHidden], red[kNormThreads];
-    const int m = blockIdx.x;
+    const int m = blockIdx.y;
+    const int k = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (k >= H) return;
+    float ss = 0.f;
+    for (int p = 0; p < kNormParts; ++p) ss += ssp[m * kNormParts + p];
+    const float scale = 1.0f / sqrtf(ss / (float)H + eps);
+    const uint4 xv = ld16(X + (size_t)m * H + k), wv = ld16(w + k);
+    const uint16_t *xe = reinterpret_cast<const uint16_t *>(&xv);
+    const uint16_t *we = reinterpret_cast<const uint16_t *>(&wv);
+    uint32_t yw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint16_t lo = f2bf(bf2f(xe[2 * e]) * scale * bf2f(we[2 * e]));
+        const uint16_t hi = f2bf(bf2f(xe[2 * e + 1]) * scale * bf2f(we[2 * e + 1]));
+        yw[e] = (uint32_t)lo | ((uint32_t)hi << 16);
+    }
+    *reinterpret_cast<uint4 *>(Y + (size_t)m * H + k) = uint4{yw[0], yw[1], yw[2], yw[3]};
+}
+
+__global__ __launch_bounds__(256) void k_resid_ss(const float *__restrict__ P, int S, int H, uint16_t *__restrict__ X,
+                                                  float *__restrict__ ssp) {
+    __shared__ float red[256];
+    const int m = blockIdx.x, part = blockIdx.y;
+    const int k0 = (H * part) / kNormParts, k1 = (H * (part + 1)) / kNormParts;
     uint16_t *x = X + (size_t)m * H;
-    for (int k = threadIdx.x; k < H; k += kNormThreads) {
+    float ss = 0.f;
+    for (int k = k0 + threadIdx.x; k < k1; k += 256) {
         const uint16_t v = f2bf(bf2f(x[k]) + bfround(psum(P, S, 1, 0, m, k)));
         x[k] = v;
-        xs[k] = bf2f(v);
+        const float f = bf2f(v);
+        ss += f * f;
     }
-    __syncthreads();
-    norm_row(xs, H, eps, w, Y + (size_t)m * H, red);
+    slice_ss(ss, red, ssp + m * kNormParts + part);
 }
 
 // ------------------------------------------------------------ skinny GEMM
@@ -207,7 +223,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, int tile, int l
             const int n = tile * 32 + acc_row(r, hf);
             if (!cok || n >= N) continue;
             float s = acc[r];
-            g.Yf[(size_t)m * g.ldyf + n] = s;
             if (mods) {
                 if (md->rep != 1.0f) {
                     bool prior = md->hist_bits && ((md->hist_bits[n >> 5] >> (n & 31)) & 1u);
@@ -265,20 +280,31 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     const uint16_t *tb2 = DUAL ? g.W2 + (size_t)(tok ? tile : 0) * 32 * K : nullptr;
     const uint4 z = {0u, 0u, 0u, 0u};
 
-    // activation staging: thread -> (row br, 16-byte chunk bc) of a step
+    // activation staging: thread -> (row br, 16-byte chunk bc) of a step.  The
+    // next group's activations are loaded with this group's weights and
+    // written to LDS after this group's MFMAs, so their latency overlaps.
     const int br = tid >> 3, bc = tid & 7;
     const uint16_t *xrow = g.X + (size_t)(br < g.M ? br : 0) * g.ldx;
-    auto stage = [&](int buf, int sf) {
+    auto bload = [&](uint4 (&bv)[U], int sf) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int s = sf + u, k = s * 64 + bc * 8;
-            const uint4 v = (s < s1 && br < g.M && k < K) ? ld16(xrow + k) : z;
-            *reinterpret_cast<uint4 *>(&Bs[buf][u][br * 64 + ((bc ^ (br & 7)) << 3)]) = v;
+            bv[u] = (s < s1 && br < g.M && k < K) ? ld16(xrow + k) : z;
         }
+    };
+    auto bstore = [&](int buf, const uint4 (&bv)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            *reinterpret_cast<uint4 *>(&Bs[buf][u][br * 64 + ((bc ^ (br & 7)) << 3)]) = bv[u];
     };
 
     f32x16 acc = {}, acc2 = {};
-    if (s0 < s1) stage(0, s0);
+    if (s0 < s1) {
+        uint4 bv[U];
+        bload(bv, s0);
+        bstore(0, bv);
+    }
+    __syncthreads();
     int buf = 0;
     for (int sg = s0; sg < s1; sg += U, buf ^= 1) {
         uint4 a[U][4], a2[DUAL ? U : 1][4];
@@ -296,8 +322,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
                 if constexpr (DUAL) a2[u][q] = off >= 0 ? ld16_stream(tb2 + off) : z;
             }
         }
-        __syncthreads();   // stage(buf) visible; everyone is done with buf^1
-        if (sg + U < s1) stage(buf ^ 1, sg + U);
+        const bool more = sg + U < s1;
+        uint4 bn[U];
+        if (more) bload(bn, sg + U);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -308,6 +335,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
                 if constexpr (DUAL) acc2 = mfma32(a2[u][q], b, acc2);
             }
         }
+        if (more) bstore(buf ^ 1, bn);
+        __syncthreads();
     }
 
     if (S > 1 || EPI == EPI_PARTIAL) {
@@ -324,6 +353,26 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
         return;
     }
     if constexpr (EPI == EPI_HEAD) {
+        // fp32 logits leave through LDS so each row's 128 values are stored as
+        // one contiguous 512-byte run (the loop's last barrier freed Bs)
+        float *lt = reinterpret_cast<float *>(&Bs[0][0][0]);   // [32 rows][128]
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lt[c * 128 + wave * 32 + acc_row(r, hf)] = acc[r];
+        __syncthreads();
+        for (int idx = tid; idx < g.M * 32; idx += 256) {
+            const int mm = idx >> 5, q4 = idx & 31;
+            const int n0 = blockIdx.x * 128 + q4 * 4;
+            const float4 v = *reinterpret_cast<const float4 *>(lt + mm * 128 + q4 * 4);
+            float *dst = g.Yf + (size_t)mm * g.ldyf + n0;
+            if (n0 + 3 < N && (g.ldyf & 3) == 0) {
+                *reinterpret_cast<float4 *>(dst) = v;
+            } else {
+                if (n0 < N) dst[0] = v.x;
+                if (n0 + 1 < N) dst[1] = v.y;
+                if (n0 + 2 < N) dst[2] = v.z;
+                if (n0 + 3 < N) dst[3] = v.w;
+            }
+        }
         // each wave's per-column top-2 goes through LDS; wave 0 merges the
         // workgroup's 4 tiles (a selection: order-free) and stores row-major
         // candidates part[m * rowblocks + rowblock]
@@ -821,15 +870,20 @@ __global__ __launch_bounds__(256) void k_commit_kv(uint16_t *const *__restrict__
 
 // ------------------------------------------------------------ launchers
 
-hipError_t launch_embed_norm(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H,
-                             float eps, const uint16_t *w, uint16_t *X, uint16_t *Y) {
-    hipLaunchKernelGGL(k_embed_norm, dim3(M), dim3(kNormThreads), 0, s, emb, meta, H, eps, w, X, Y);
+hipError_t launch_embed_ss(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H, uint16_t *X,
+                           float *ss) {
+    hipLaunchKernelGGL(k_embed_ss, dim3(M, kNormParts), dim3(256), 0, s, emb, meta, H, X, ss);
     return hipGetLastError();
 }
 
-hipError_t launch_resid_norm(hipStream_t s, const float *P, int S, int M, int H, float eps, const uint16_t *w,
-                             uint16_t *X, uint16_t *Y) {
-    hipLaunchKernelGGL(k_resid_norm, dim3(M), dim3(kNormThreads), 0, s, P, S, H, eps, w, X, Y);
+hipError_t launch_norm_apply(hipStream_t s, const uint16_t *X, const float *ss, const uint16_t *w, int M, int H,
+                             float eps, uint16_t *Y) {
+    hipLaunchKernelGGL(k_norm_apply, dim3((H / 8 + 255) / 256, M), dim3(256), 0, s, X, ss, w, H, eps, Y);
+    return hipGetLastError();
+}
+
+hipError_t launch_resid_ss(hipStream_t s, const float *P, int S, int M, int H, uint16_t *X, float *ss) {
+    hipLaunchKernelGGL(k_resid_ss, dim3(M, kNormParts), dim3(256), 0, s, P, S, H, X, ss);
     return hipGetLastError();
 }
 

@@ -72,6 +72,7 @@ struct tv_ctx {
     uint16_t *X = nullptr, *XN = nullptr, *QKV = nullptr, *QR = nullptr, *ATT = nullptr,
              *ACT = nullptr, *ABUF = nullptr;
     float *logits = nullptr;  // [32, V] when the caller passes none
+    float *SS = nullptr;      // [32][kNormParts] sum-of-squares slices of X
     Top2 *part = nullptr;
     float *po = nullptr, *pm = nullptr, *pl = nullptr;
     float *rope_cos = nullptr, *rope_sin = nullptr;
@@ -371,12 +372,29 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
     HIPCHECK(c, hipMemcpyAsync(c->d_meta, c->h_meta, sizeof(PassMeta), hipMemcpyHostToDevice, s));
 
     const int H = m.hidden, D = m.head_dim, QH = m.n_qhead, KVH = m.n_kvhead;
-    // X: residual stream; XN: normalised input of the next projection.
-    LAUNCH(c, "embed_norm", launch_embed_norm(s, c->emb, c->d_meta, M, H, m.eps, c->attn_norm[0], c->X, c->XN));
+    // X: residual stream; SS: its per-row sum-of-squares slices.  Projections
+    // that consume RMSNorm(X) apply the norm while staging X.
+    LAUNCH(c, "embed_ss", launch_embed_ss(s, c->emb, c->d_meta, M, H, c->X, c->SS));
+    // XN = RMSNorm(X) with weights w, from X and its sum-of-squares slices
+    const uint16_t *xn_w = nullptr;
+    auto normed = [&](GemmArgs &g, const uint16_t *w) -> int {
+        if (xn_w != w) {
+            LAUNCH(c, "norm", launch_norm_apply(s, c->X, c->SS, w, M, H, m.eps, c->XN));
+            xn_w = w;
+        }
+        g.X = c->XN; g.ldx = H;
+        return TV_OK;
+    };
+#define NORMED(g, w)                 \
+    do {                             \
+        int rc_ = normed((g), (w));  \
+        if (rc_) return rc_;         \
+    } while (0)
     for (int l = 0; l < m.n_layer; ++l) {
         if (c->kinds[l] == TV_LAYER_ATTN) {
             GemmArgs g{};
-            g.X = c->XN; g.ldx = H; g.W = c->wqkv[l]; g.M = M; g.N = (QH + 2 * KVH) * D; g.K = H;
+            NORMED(g, c->attn_norm[l]);
+            g.W = c->wqkv[l]; g.M = M; g.N = (QH + 2 * KVH) * D; g.K = H;
             int S = 0;
             GEMMP(c, "gemm_qkv", g, S);
             for (int r = 0; r < n_req; ++r) {
@@ -405,11 +423,13 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
         } else {
             const int rl = c->recur_index[l];
             GemmArgs g{};
-            g.X = c->XN; g.ldx = H; g.W = c->wqkv[l]; g.M = M; g.N = 3 * QH * D; g.K = H;
+            NORMED(g, c->attn_norm[l]);
+            g.W = c->wqkv[l]; g.M = M; g.N = 3 * QH * D; g.K = H;
             g.Y = c->QKV; g.ldy = g.N;
             GEMM(c, "gemm_qkv", EPI_BF16, g);
             GemmArgs ga{};
-            ga.X = c->XN; ga.ldx = H; ga.W = c->wa[l]; ga.M = M; ga.N = QH; ga.K = H;
+            NORMED(ga, c->attn_norm[l]);
+            ga.W = c->wa[l]; ga.M = M; ga.N = QH; ga.K = H;
             ga.Y = c->ABUF; ga.ldy = QH;
             GEMM(c, "gemm_gate", EPI_BF16, ga);
             for (int r = 0; r < n_req; ++r) {
@@ -429,11 +449,13 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
             g.X = c->ATT; g.ldx = QH * D; g.W = c->wo[l]; g.M = M; g.N = H; g.K = QH * D;
             int S = 0;
             GEMMP(c, "gemm_o", g, S);
-            LAUNCH(c, "resid_norm", launch_resid_norm(s, c->gemm_partial, S, M, H, m.eps, c->ffn_norm[l], c->X, c->XN));
+            LAUNCH(c, "resid_ss", launch_resid_ss(s, c->gemm_partial, S, M, H, c->X, c->SS));
+            xn_w = nullptr;
         }
         {
             GemmArgs g{};
-            g.X = c->XN; g.ldx = H; g.W = c->wg[l]; g.W2 = c->wu[l]; g.M = M; g.N = m.ffn; g.K = H;
+            NORMED(g, c->ffn_norm[l]);
+            g.W = c->wg[l]; g.W2 = c->wu[l]; g.M = M; g.N = m.ffn; g.K = H;
             g.Y = c->ACT; g.ldy = m.ffn;
             GEMM(c, "gemm_gateup", EPI_SWIGLU, g);
         }
@@ -442,14 +464,15 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
             g.X = c->ACT; g.ldx = m.ffn; g.W = c->wd[l]; g.M = M; g.N = H; g.K = m.ffn;
             int S = 0;
             GEMMP(c, "gemm_down", g, S);
-            const uint16_t *next = l + 1 < m.n_layer ? c->attn_norm[l + 1] : c->final_norm;
-            LAUNCH(c, "resid_norm", launch_resid_norm(s, c->gemm_partial, S, M, H, m.eps, next, c->X, c->XN));
+            LAUNCH(c, "resid_ss", launch_resid_ss(s, c->gemm_partial, S, M, H, c->X, c->SS));
+            xn_w = nullptr;
         }
     }
     float *out = logits_dev ? logits_dev : c->logits;
     {
         GemmArgs g{};
-        g.X = c->XN; g.ldx = H; g.W = c->head; g.M = M; g.N = m.vocab; g.K = H;
+        NORMED(g, c->final_norm);
+        g.W = c->head; g.M = M; g.N = m.vocab; g.K = H;
         g.Yf = out; g.ldyf = m.vocab; g.part = c->part; g.meta = c->d_meta; g.mods_on = any_mods;
         GEMM(c, "gemm_head", EPI_HEAD, g);
     }
@@ -535,6 +558,7 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     ALLOC(c->ATT, (size_t)R * m.n_qhead * D * 2);
     ALLOC(c->ACT, (size_t)R * m.ffn * 2);
     ALLOC(c->ABUF, (size_t)R * m.n_qhead * 2);
+    ALLOC(c->SS, (size_t)R * kNormParts * 4);
     if (!c->recur_layers.empty()) {
         const size_t nrl = c->recur_layers.size();
         for (auto &q : c->reqs) {
@@ -595,7 +619,7 @@ void tv_destroy(tv_ctx *c) {
     if (!c) return;
     if (c->stream) hipStreamSynchronize(c->stream);
     else hipDeviceSynchronize();
-    void *dev[] = {c->X, c->XN, c->QKV, c->QR, c->ATT, c->ACT, c->ABUF, c->logits, c->part, c->po, c->pm, c->pl,
+    void *dev[] = {c->X, c->XN, c->QKV, c->QR, c->ATT, c->ACT, c->ABUF, c->SS, c->logits, c->part, c->po, c->pm, c->pl,
                    c->rope_cos, c->rope_sin, c->d_meta, c->d_argmax, c->d_gap, c->d_top, c->d_path,
                    c->gemm_partial};
     for (void *p : dev)
@@ -811,9 +835,9 @@ int tv_commit(tv_ctx *c, int req, const int32_t *path, int path_len) {
         set_bit(q.hist_bits, t);
     }
     if (q.mods_on && q.d_hist)
-        HIPCHECK(c, hipMemcpyAsync(q.d_hist, q.hist_bits.data(), q.hist_bits.size() * 4, hipMemcpyHostToDevice, s));
-    HIPCHECK(c, hipStreamSynchronize(s));
-    if (c->prof) harvest(c);
+        HIPCHECK(c, hipMemcpy(q.d_hist, q.hist_bits.data(), q.hist_bits.size() * 4, hipMemcpyHostToDevice));
+    // No synchronisation: the commit is stream-ordered before the next verify,
+    // which synchronises; the pinned path buffer is rewritten only after that.
     q.pending = false;
     return TV_OK;
 }

@@ -20,7 +20,9 @@
  *     it.  The library allocates its own small activation scratch in
  *     tv_create and frees it in tv_destroy.
  *   - All device work is enqueued on the stream given to tv_create.  A call
- *     that returns host results (argmax, gaps, path) synchronises that stream.
+ *     that returns host results (argmax, gaps) synchronises that stream;
+ *     tv_commit only enqueues (its effects are ordered before later work on
+ *     the stream).
  *   - Token ids are int32 in [0, vocab).  A tree is given by parents[] and
  *     tokens[] of n_nodes entries, root included: parents[0] == -1 and
  *     0 <= parents[i] < i (any topological order; depth-first pre-order as
