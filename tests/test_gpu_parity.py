@@ -449,3 +449,57 @@ def test_c4_joint_modifiers_wrong_drafter(c1):
             wl.tv.commit(r, path)
             seq.commit([roots[r]])
             roots[r] = emitted[0]
+
+
+# ------------------------------------------------------------- edge cases
+
+def test_c0_edges_capacity_single_row_three_requests(c0):
+    """Degenerate and boundary cases: a one-node tree (the root alone), a
+    verify that fills the cache to max_ctx exactly, three requests in one
+    pass (8 + 8 + 16 rows), and an empty tree (rejected)."""
+    from greedy_draft_tree_amd import TVError, TV_EINVAL
+    wl, orc = c0
+    cap = wl.max_ctx
+    # cache filled to the last row: ctx = cap - 32, then a 32-row chain
+    ctx = cap - 32
+    kv = synth.kv_cache(synth.C0, ctx, seed=13, cap=ctx)
+    import workloads
+    workloads.load_context(wl, 0, ctx, 0, src_kv={k: v.cuda() for k, v in kv.items()})
+    seq = orc.new_seq(cap=cap, kv=kv, ctx_len=ctx)
+    chain = synth.chain_tree(32)
+    toks = synth.uniform_ids(32, synth.C0.vocab, 14)
+    am, gap = wl.tv.verify_tree(0, chain, toks, logits=wl.logits)
+    ol = orc.tree_scores(seq, chain, toks)
+    check_rows(wl.logits[:32].cpu().numpy(), am, gap, ol, chain, toks, seq.history, what="c0 at capacity")
+    first_row = wl.logits[0].cpu().numpy().copy()
+    wl.tv.commit(0, list(range(32)))
+    assert wl.tv.ctx_len(0) == cap
+    # the root alone
+    workloads.load_context(wl, 0, ctx, 0, src_kv={k: v.cuda() for k, v in kv.items()})
+    am1, gap1 = wl.tv.verify_tree(0, [-1], [int(toks[0])], logits=wl.logits)
+    # the root's row is bitwise the same whether or not 31 more rows follow it
+    assert np.array_equal(wl.logits[0].cpu().numpy(), first_row) and am1[0] == am[0]
+    # empty tree
+    with pytest.raises(TVError) as e:
+        wl.tv.verify_tree(0, [], [])
+    assert e.value.code == TV_EINVAL
+
+
+def test_c0_three_requests_joint_equal_alone(c0):
+    import workloads
+    wl3 = workloads.build(synth.C0, max_ctx=256, max_req=3, weights=None, weight_device="cuda")
+    trees = []
+    for r, (n, seed) in enumerate([(8, 1), (8, 2), (16, 3)]):
+        p = synth.uniform_ids(20 + r, synth.C0.vocab, 70 + r)
+        wl3.tv.set_history(r, [], 0)
+        wl3.tv.prefill(r, p)
+        par = synth.random_tree(n, seed)
+        trees.append((par, synth.tree_tokens(par, synth.C0.vocab, 80 + r, root_token=int(p[-1]))))
+    wl3.tv.verify_trees([2, 0, 1], [trees[2][0], trees[0][0], trees[1][0]],
+                        [trees[2][1], trees[0][1], trees[1][1]], logits=wl3.logits)
+    joint = wl3.logits[:32].clone()
+    offs = {2: 0, 0: 16, 1: 24}
+    for r in range(3):
+        n = len(trees[r][0])
+        wl3.tv.verify_tree(r, trees[r][0], trees[r][1], logits=wl3.logits)
+        assert torch.equal(wl3.logits[:n], joint[offs[r]:offs[r] + n]), r
