@@ -57,6 +57,7 @@ struct GemmArgs {
     const PassMeta *meta; // head modifiers (null: none)
     int mods_on;
     float *partial;     // split-K partial tiles (splits > 1)
+    const void *zeros;  // >= 16 zero bytes (activation staging beyond M or K)
 };
 
 // k-range splits of a GEMM: a function of the weight shape only.

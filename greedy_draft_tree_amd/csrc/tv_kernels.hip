@@ -280,33 +280,34 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     const uint16_t *tb2 = DUAL ? g.W2 + (size_t)(tok ? tile : 0) * 32 * K : nullptr;
     const uint4 z = {0u, 0u, 0u, 0u};
 
-    // activation staging: thread -> (row br, 16-byte chunk bc) of a step.  The
-    // next group's activations are loaded with this group's weights and
-    // written to LDS after this group's MFMAs, so their latency overlaps.
-    const int br = tid >> 3, bc = tid & 7;
+    // Activation staging with direct global->LDS loads: thread t fills bytes
+    // [16t, 16t+16) of a step's 4 KB block, i.e. row br = t/8, slot sw = t%8,
+    // with the row's 16-byte chunk sw ^ (br & 7) (the XOR swizzle that makes
+    // the B-operand reads conflict-free); rows beyond M and k beyond K read a
+    // zero block.  The next group's loads are issued first in each group (the
+    // buffer they fill was released by the previous group's barrier), ahead
+    // of the weight loads, and waited for at the group's barrier.
+    const int br = tid >> 3, bsw = (tid & 7) ^ (br & 7);
     const uint16_t *xrow = g.X + (size_t)(br < g.M ? br : 0) * g.ldx;
-    auto bload = [&](uint4 (&bv)[U], int sf) {
+    typedef __attribute__((address_space(3))) uint8_t lds_byte;
+    auto bissue = [&](int buf, int sf) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int s = sf + u, k = s * 64 + bc * 8;
-            bv[u] = (s < s1 && br < g.M && k < K) ? ld16(xrow + k) : z;
+            const int s = sf + u, k = s * 64 + bsw * 8;
+            const bool ok = s < s1 && br < g.M && k < K;
+            const void *src = ok ? static_cast<const void *>(xrow + k) : static_cast<const void *>(g.zeros);
+            lds_byte *dst = (lds_byte *)(&Bs[buf][u][0]) + wave * 1024;
+            __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
         }
-    };
-    auto bstore = [&](int buf, const uint4 (&bv)[U]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            *reinterpret_cast<uint4 *>(&Bs[buf][u][br * 64 + ((bc ^ (br & 7)) << 3)]) = bv[u];
     };
 
     f32x16 acc = {}, acc2 = {};
-    if (s0 < s1) {
-        uint4 bv[U];
-        bload(bv, s0);
-        bstore(0, bv);
-    }
+    if (s0 < s1) bissue(0, s0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int buf = 0;
     for (int sg = s0; sg < s1; sg += U, buf ^= 1) {
+        if (sg + U < s1) bissue(buf ^ 1, sg + U);
         uint4 a[U][4], a2[DUAL ? U : 1][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -322,9 +323,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
                 if constexpr (DUAL) a2[u][q] = off >= 0 ? ld16_stream(tb2 + off) : z;
             }
         }
-        const bool more = sg + U < s1;
-        uint4 bn[U];
-        if (more) bload(bn, sg + U);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -335,7 +333,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
                 if constexpr (DUAL) acc2 = mfma32(a2[u][q], b, acc2);
             }
         }
-        if (more) bstore(buf ^ 1, bn);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads into buf^1 have landed
         __syncthreads();
     }
 

@@ -73,6 +73,7 @@ struct tv_ctx {
              *ACT = nullptr, *ABUF = nullptr;
     float *logits = nullptr;  // [32, V] when the caller passes none
     float *SS = nullptr;      // [32][kNormParts] sum-of-squares slices of X
+    void *zeros = nullptr;    // 256 zero bytes
     Top2 *part = nullptr;
     float *po = nullptr, *pm = nullptr, *pl = nullptr;
     float *rope_cos = nullptr, *rope_sin = nullptr;
@@ -261,6 +262,7 @@ int pack_inplace(tv_ctx *c, void *ptr, int N, int K) {
 
 int gemm(tv_ctx *c, const char *name, int epi, GemmArgs g) {
     g.partial = c->gemm_partial;
+    g.zeros = c->zeros;
     // the head's top-2 epilogue needs whole sums in the kernel: it never splits
     const int S = epi == EPI_HEAD ? 1 : gemm_splits(g.N, g.K);
     if (S > 1 && gemm_partial_need(g.N, g.K, epi == EPI_SWIGLU) > c->gemm_partial_floats)
@@ -273,6 +275,7 @@ int gemm(tv_ctx *c, const char *name, int epi, GemmArgs g) {
 // A projection whose consumer finishes the sums: partials only, *S = splits.
 int gemm_partial(tv_ctx *c, const char *name, GemmArgs g, int *S) {
     g.partial = c->gemm_partial;
+    g.zeros = c->zeros;
     *S = gemm_splits(g.N, g.K);
     if (gemm_partial_need(g.N, g.K, false, true) > c->gemm_partial_floats)
         return fail(c, TV_EINVAL, "GEMM N=%d K=%d needs more split-K scratch than allocated", g.N, g.K);
@@ -559,6 +562,8 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     ALLOC(c->ACT, (size_t)R * m.ffn * 2);
     ALLOC(c->ABUF, (size_t)R * m.n_qhead * 2);
     ALLOC(c->SS, (size_t)R * kNormParts * 4);
+    ALLOC(c->zeros, 256);
+    if (e == hipSuccess) e = hipMemset(c->zeros, 0, 256);
     if (!c->recur_layers.empty()) {
         const size_t nrl = c->recur_layers.size();
         for (auto &q : c->reqs) {
@@ -619,7 +624,7 @@ void tv_destroy(tv_ctx *c) {
     if (!c) return;
     if (c->stream) hipStreamSynchronize(c->stream);
     else hipDeviceSynchronize();
-    void *dev[] = {c->X, c->XN, c->QKV, c->QR, c->ATT, c->ACT, c->ABUF, c->SS, c->logits, c->part, c->po, c->pm, c->pl,
+    void *dev[] = {c->X, c->XN, c->QKV, c->QR, c->ATT, c->ACT, c->ABUF, c->SS, c->zeros, c->logits, c->part, c->po, c->pm, c->pl,
                    c->rope_cos, c->rope_sin, c->d_meta, c->d_argmax, c->d_gap, c->d_top, c->d_path,
                    c->gemm_partial};
     for (void *p : dev)
