@@ -9,7 +9,6 @@ namespace tv {
 constexpr int kMaxRows = 32;   // rows of one pass
 constexpr int kMaxGroup = 8;   // query heads per KV head
 constexpr int kAttnChunk = 64;  // keys staged in LDS at a time
-constexpr int kNormParts = 8;   // sum-of-squares slices per row of the residual stream
 
 // Candidate pair of a top-2 search: best (v1, i1) and runner-up (v2, i2),
 // ordered by value, then by lower token id.
@@ -124,11 +123,12 @@ struct RecurCommitArgs {
 };
 
 // launch wrappers (tv_kernels.hip); each returns hipGetLastError()
-hipError_t launch_embed_ss(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H, uint16_t *X,
-                           float *ss);
-hipError_t launch_norm_apply(hipStream_t s, const uint16_t *X, const float *ss, const uint16_t *w, int M, int H,
-                             float eps, uint16_t *Y);
-hipError_t launch_resid_ss(hipStream_t s, const float *P, int S, int M, int H, uint16_t *X, float *ss);
+// X = embedding rows of the pass's tokens, Y = RMSNorm(X) with weights w
+hipError_t launch_embed_norm(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H,
+                             const uint16_t *w, float eps, uint16_t *X, uint16_t *Y);
+// X = bf16(X + bf16(sum of the S split-K partials P)), Y = RMSNorm(X) with weights w
+hipError_t launch_resid_norm(hipStream_t s, const float *P, int S, int M, int H, const uint16_t *w, float eps,
+                             uint16_t *X, uint16_t *Y);
 hipError_t launch_gemm(hipStream_t s, int epi, const GemmArgs &a, int splits);
 hipError_t launch_splitk_reduce(hipStream_t s, int epi, const GemmArgs &a, int splits);
 hipError_t launch_pack(hipStream_t s, const uint16_t *src, uint16_t *dst, int N, int K, int t0, int nt);

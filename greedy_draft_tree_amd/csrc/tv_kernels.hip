@@ -99,78 +99,128 @@ __device__ __forceinline__ float psum(const float *__restrict__ P, int S, int na
 }
 
 // --------------------------------------------- residual stream + RMSNorm
-// RMSNorm is y = bf16(x / sqrt(mean(x^2) + eps) * w).  The residual kernels
-// below write x and, per row, kNormParts partial sums of squares over fixed
-// slices (each reduced in a fixed order); k_norm_apply adds the slices in
-// order, forms the row's scale and writes y.  Both are wide grids (many
-// workgroups per row).
-// k_embed_ss gathers the embedding row; k_resid_ss finishes a residual
-// projection, x = bf16(x + bf16(sum of the partials)).
+// RMSNorm is y = bf16(x / sqrt(mean(x^2) + eps) * w).  One workgroup of 1024
+// threads owns one row: it forms the row's new residual stream x (the
+// embedding row, or x + bf16(sum of a projection's split-K partials)),
+// writes it, reduces its sum of squares in a fixed order and writes the
+// normalised row y for the next projection.  Each thread holds up to two
+// runs of 4 columns (hidden <= 8192).
 
-__device__ __forceinline__ void slice_ss(float ss, float *red, float *out) {
-    const int t = threadIdx.x;
-    red[t] = ss;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (t < o) red[t] += red[t + o];
-        __syncthreads();
-    }
-    if (t == 0) *out = red[0];
-}
+constexpr int kRowThreads = 1024;
+enum RowMode { ROW_EMBED = 0, ROW_RESID = 1 };
 
-__global__ __launch_bounds__(256) void k_embed_ss(const uint16_t *__restrict__ emb, const PassMeta *__restrict__ meta,
-                                                  int H, uint16_t *__restrict__ X, float *__restrict__ ssp) {
-    __shared__ float red[256];
-    const int m = blockIdx.x, part = blockIdx.y;
-    const int k0 = (H * part) / kNormParts, k1 = (H * (part + 1)) / kNormParts;
-    const uint16_t *src = emb + (size_t)meta->tok[m] * H;
-    uint16_t *dst = X + (size_t)m * H;
+__device__ __forceinline__ float4 ld_f4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+
+template <int MODE>
+__global__ __launch_bounds__(kRowThreads) void k_row_norm(const uint16_t *__restrict__ emb,
+                                                          const PassMeta *__restrict__ meta,
+                                                          const float *__restrict__ P, int S, int H,
+                                                          const uint16_t *__restrict__ w, float eps,
+                                                          uint16_t *__restrict__ X, uint16_t *__restrict__ Y) {
+    __shared__ float red[kRowThreads / 64];
+    const int m = blockIdx.x, t = threadIdx.x;
+    const int units = H >> 2;
+    uint16_t *xr = X + (size_t)m * H;
+    float x[2][4];
     float ss = 0.f;
-    for (int k = k0 + threadIdx.x; k < k1; k += 256) {
-        const uint16_t v = src[k];
-        dst[k] = v;
-        const float f = bf2f(v);
-        ss += f * f;
-    }
-    slice_ss(ss, red, ssp + m * kNormParts + part);
-}
-
-__global__ __launch_bounds__(256) void k_norm_apply(const uint16_t *__restrict__ X, const float *__restrict__ ssp,
-                                                    const uint16_t *__restrict__ w, int H, float eps,
-                                                    uint16_t *__restrict__ Y) {
-    const int m = blockIdx.y;
-    const int k = (blockIdx.x * 256 + threadIdx.x) * 8;
-    if (k >= H) return;
-    float ss = 0.f;
-    for (int p = 0; p < kNormParts; ++p) ss += ssp[m * kNormParts + p];
-    const float scale = 1.0f / sqrtf(ss / (float)H + eps);
-    const uint4 xv = ld16(X + (size_t)m * H + k), wv = ld16(w + k);
-    const uint16_t *xe = reinterpret_cast<const uint16_t *>(&xv);
-    const uint16_t *we = reinterpret_cast<const uint16_t *>(&wv);
-    uint32_t yw[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const uint16_t lo = f2bf(bf2f(xe[2 * e]) * scale * bf2f(we[2 * e]));
-        const uint16_t hi = f2bf(bf2f(xe[2 * e + 1]) * scale * bf2f(we[2 * e + 1]));
-        yw[e] = (uint32_t)lo | ((uint32_t)hi << 16);
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[j][e] = 0.f;
     }
-    *reinterpret_cast<uint4 *>(Y + (size_t)m * H + k) = uint4{yw[0], yw[1], yw[2], yw[3]};
-}
-
-__global__ __launch_bounds__(256) void k_resid_ss(const float *__restrict__ P, int S, int H, uint16_t *__restrict__ X,
-                                                  float *__restrict__ ssp) {
-    __shared__ float red[256];
-    const int m = blockIdx.x, part = blockIdx.y;
-    const int k0 = (H * part) / kNormParts, k1 = (H * (part + 1)) / kNormParts;
-    uint16_t *x = X + (size_t)m * H;
-    float ss = 0.f;
-    for (int k = k0 + threadIdx.x; k < k1; k += 256) {
-        const uint16_t v = f2bf(bf2f(x[k]) + bfround(psum(P, S, 1, 0, m, k)));
-        x[k] = v;
-        const float f = bf2f(v);
-        ss += f * f;
+    if constexpr (MODE == ROW_EMBED) {
+        const uint16_t *src = emb + (size_t)meta->tok[m] * H;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int u = t + j * kRowThreads;
+            if (u < units) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(src + 4 * u);
+                *reinterpret_cast<uint2 *>(xr + 4 * u) = v;
+                const uint16_t *ve = reinterpret_cast<const uint16_t *>(&v);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[j][e] = bf2f(ve[e]);
+            }
+        }
+    } else {
+        // partial (s, m, n) sits at ((n/128)*S + s)*4096 + m*128 + n%128
+        float4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        const float *pp[2];
+        bool ok[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = 4 * (t + j * kRowThreads);
+            ok[j] = n < H;
+            pp[j] = P + ((size_t)(ok[j] ? n >> 7 : 0) * S) * 4096 + (size_t)m * 128 + (n & 127);
+        }
+        for (int s0 = 0; s0 < S; s0 += 8) {   // eight splits of both runs in flight, adds in split order
+            float4 v[2][8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    v[j][i] = (ok[j] && s0 + i < S) ? ld_f4(pp[j] + (size_t)(s0 + i) * 4096)
+                                                    : float4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (s0 + i < S) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        acc[j].x += v[j][i].x;
+                        acc[j].y += v[j][i].y;
+                        acc[j].z += v[j][i].z;
+                        acc[j].w += v[j][i].w;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int u = t + j * kRowThreads;
+            if (u < units) {
+                const uint2 ov = *reinterpret_cast<const uint2 *>(xr + 4 * u);
+                const uint16_t *oe = reinterpret_cast<const uint16_t *>(&ov);
+                const float a4[4] = {acc[j].x, acc[j].y, acc[j].z, acc[j].w};
+                uint16_t ne[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ne[e] = f2bf(bf2f(oe[e]) + bfround(a4[e]));
+                    x[j][e] = bf2f(ne[e]);
+                }
+                *reinterpret_cast<uint2 *>(xr + 4 * u) =
+                    uint2{(uint32_t)ne[0] | ((uint32_t)ne[1] << 16), (uint32_t)ne[2] | ((uint32_t)ne[3] << 16)};
+            }
+        }
     }
-    slice_ss(ss, red, ssp + m * kNormParts + part);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += x[j][e] * x[j][e];
+    }
+    // fixed-order reduction: within each wave by xor shuffles, then the
+    // waves' sums in wave order
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((t & 63) == 0) red[t >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kRowThreads / 64; ++i) tot += red[i];
+    const float scale = 1.0f / sqrtf(tot / (float)H + eps);
+    uint16_t *yr = Y + (size_t)m * H;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int u = t + j * kRowThreads;
+        if (u < units) {
+            const uint2 wv = *reinterpret_cast<const uint2 *>(w + 4 * u);
+            const uint16_t *we = reinterpret_cast<const uint16_t *>(&wv);
+            uint16_t ye[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ye[e] = f2bf(x[j][e] * scale * bf2f(we[e]));
+            *reinterpret_cast<uint2 *>(yr + 4 * u) =
+                uint2{(uint32_t)ye[0] | ((uint32_t)ye[1] << 16), (uint32_t)ye[2] | ((uint32_t)ye[3] << 16)};
+        }
+    }
 }
 
 // ------------------------------------------------------------ skinny GEMM
@@ -868,20 +918,19 @@ __global__ __launch_bounds__(256) void k_commit_kv(uint16_t *const *__restrict__
 
 // ------------------------------------------------------------ launchers
 
-hipError_t launch_embed_ss(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H, uint16_t *X,
-                           float *ss) {
-    hipLaunchKernelGGL(k_embed_ss, dim3(M, kNormParts), dim3(256), 0, s, emb, meta, H, X, ss);
+hipError_t launch_embed_norm(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H,
+                             const uint16_t *w, float eps, uint16_t *X, uint16_t *Y) {
+    if (H % 4 || H > 8 * kRowThreads) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_row_norm<ROW_EMBED>, dim3(M), dim3(kRowThreads), 0, s, emb, meta, nullptr, 0, H, w, eps,
+                       X, Y);
     return hipGetLastError();
 }
 
-hipError_t launch_norm_apply(hipStream_t s, const uint16_t *X, const float *ss, const uint16_t *w, int M, int H,
-                             float eps, uint16_t *Y) {
-    hipLaunchKernelGGL(k_norm_apply, dim3((H / 8 + 255) / 256, M), dim3(256), 0, s, X, ss, w, H, eps, Y);
-    return hipGetLastError();
-}
-
-hipError_t launch_resid_ss(hipStream_t s, const float *P, int S, int M, int H, uint16_t *X, float *ss) {
-    hipLaunchKernelGGL(k_resid_ss, dim3(M, kNormParts), dim3(256), 0, s, P, S, H, X, ss);
+hipError_t launch_resid_norm(hipStream_t s, const float *P, int S, int M, int H, const uint16_t *w, float eps,
+                             uint16_t *X, uint16_t *Y) {
+    if (H % 4 || H > 8 * kRowThreads || S < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_row_norm<ROW_RESID>, dim3(M), dim3(kRowThreads), 0, s, nullptr, nullptr, P, S, H, w, eps,
+                       X, Y);
     return hipGetLastError();
 }
 

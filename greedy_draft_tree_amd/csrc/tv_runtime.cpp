@@ -72,7 +72,6 @@ struct tv_ctx {
     uint16_t *X = nullptr, *XN = nullptr, *QKV = nullptr, *QR = nullptr, *ATT = nullptr,
              *ACT = nullptr, *ABUF = nullptr;
     float *logits = nullptr;  // [32, V] when the caller passes none
-    float *SS = nullptr;      // [32][kNormParts] sum-of-squares slices of X
     void *zeros = nullptr;    // 256 zero bytes
     Top2 *part = nullptr;
     float *po = nullptr, *pm = nullptr, *pl = nullptr;
@@ -375,16 +374,12 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
     HIPCHECK(c, hipMemcpyAsync(c->d_meta, c->h_meta, sizeof(PassMeta), hipMemcpyHostToDevice, s));
 
     const int H = m.hidden, D = m.head_dim, QH = m.n_qhead, KVH = m.n_kvhead;
-    // X: residual stream; SS: its per-row sum-of-squares slices.  Projections
-    // that consume RMSNorm(X) apply the norm while staging X.
-    LAUNCH(c, "embed_ss", launch_embed_ss(s, c->emb, c->d_meta, M, H, c->X, c->SS));
-    // XN = RMSNorm(X) with weights w, from X and its sum-of-squares slices
-    const uint16_t *xn_w = nullptr;
+    // X: residual stream; XN = RMSNorm(X) with the weights of the next
+    // projection that reads it (xn_w), written by the kernel that updates X.
+    const uint16_t *xn_w = c->attn_norm[0];
+    LAUNCH(c, "embed_norm", launch_embed_norm(s, c->emb, c->d_meta, M, H, xn_w, m.eps, c->X, c->XN));
     auto normed = [&](GemmArgs &g, const uint16_t *w) -> int {
-        if (xn_w != w) {
-            LAUNCH(c, "norm", launch_norm_apply(s, c->X, c->SS, w, M, H, m.eps, c->XN));
-            xn_w = w;
-        }
+        if (xn_w != w) return fail(c, TV_ESTATE, "internal: normalised rows hold another norm");
         g.X = c->XN; g.ldx = H;
         return TV_OK;
     };
@@ -452,8 +447,8 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
             g.X = c->ATT; g.ldx = QH * D; g.W = c->wo[l]; g.M = M; g.N = H; g.K = QH * D;
             int S = 0;
             GEMMP(c, "gemm_o", g, S);
-            LAUNCH(c, "resid_ss", launch_resid_ss(s, c->gemm_partial, S, M, H, c->X, c->SS));
-            xn_w = nullptr;
+            xn_w = c->ffn_norm[l];
+            LAUNCH(c, "resid_norm", launch_resid_norm(s, c->gemm_partial, S, M, H, xn_w, m.eps, c->X, c->XN));
         }
         {
             GemmArgs g{};
@@ -467,8 +462,8 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
             g.X = c->ACT; g.ldx = m.ffn; g.W = c->wd[l]; g.M = M; g.N = H; g.K = m.ffn;
             int S = 0;
             GEMMP(c, "gemm_down", g, S);
-            LAUNCH(c, "resid_ss", launch_resid_ss(s, c->gemm_partial, S, M, H, c->X, c->SS));
-            xn_w = nullptr;
+            xn_w = l + 1 < m.n_layer ? c->attn_norm[l + 1] : c->final_norm;
+            LAUNCH(c, "resid_norm", launch_resid_norm(s, c->gemm_partial, S, M, H, xn_w, m.eps, c->X, c->XN));
         }
     }
     float *out = logits_dev ? logits_dev : c->logits;
@@ -517,7 +512,7 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
         m.vocab < 2 || m.max_ctx < 1 || m.max_req < 1 || !m.layer_kind || m.eps <= 0.f)
         return TV_EINVAL;
     if (m.n_qhead / m.n_kvhead > 5) return TV_EINVAL;  // attention stages G*32 <= 160 query rows
-    if (m.hidden > 8192) return TV_EINVAL;              // norm kernels hold one row in LDS
+    if (m.hidden > 8192) return TV_EINVAL;              // a norm workgroup holds one row
     tv_ctx *c = new tv_ctx();
     c->m = m;
     c->kinds.assign(m.layer_kind, m.layer_kind + m.n_layer);
@@ -561,7 +556,6 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     ALLOC(c->ATT, (size_t)R * m.n_qhead * D * 2);
     ALLOC(c->ACT, (size_t)R * m.ffn * 2);
     ALLOC(c->ABUF, (size_t)R * m.n_qhead * 2);
-    ALLOC(c->SS, (size_t)R * kNormParts * 4);
     ALLOC(c->zeros, 256);
     if (e == hipSuccess) e = hipMemset(c->zeros, 0, 256);
     if (!c->recur_layers.empty()) {
@@ -624,7 +618,7 @@ void tv_destroy(tv_ctx *c) {
     if (!c) return;
     if (c->stream) hipStreamSynchronize(c->stream);
     else hipDeviceSynchronize();
-    void *dev[] = {c->X, c->XN, c->QKV, c->QR, c->ATT, c->ACT, c->ABUF, c->SS, c->zeros, c->logits, c->part, c->po, c->pm, c->pl,
+    void *dev[] = {c->X, c->XN, c->QKV, c->QR, c->ATT, c->ACT, c->ABUF, c->zeros, c->logits, c->part, c->po, c->pm, c->pl,
                    c->rope_cos, c->rope_sin, c->d_meta, c->d_argmax, c->d_gap, c->d_top, c->d_path,
                    c->gemm_partial};
     for (void *p : dev)
