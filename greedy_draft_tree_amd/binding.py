@@ -83,27 +83,37 @@ def exported_symbols() -> Dict[str, bool]:
 
 
 def _i32(a) -> np.ndarray:
+    if type(a) is np.ndarray and a.dtype == np.int32 and a.flags.c_contiguous:
+        return a
     return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
 
 
-def _ptr(a: np.ndarray):
-    return ctypes.c_void_p(a.ctypes.data)
+def _ptr(a: np.ndarray) -> int:
+    """Address of an array's data (ctypes passes an int as void*)."""
+    return a.__array_interface__["data"][0]
+
+
+# output buffers of accept_walk, reused across calls (results are copied out)
+_walk_path = np.zeros(TV_MAX_NODES, np.int32)
+_walk_emit = np.zeros(TV_MAX_NODES, np.int32)
+_walk_len = (ctypes.c_int32 * 2)()
+_walk_ptrs = (_ptr(_walk_path), _ptr(_walk_emit), ctypes.addressof(_walk_len),
+              ctypes.addressof(_walk_len) + 4)
 
 
 def accept_walk(parents: Sequence[int], tokens: Sequence[int], argmax: Sequence[int]
                 ) -> Tuple[list, list]:
     """tv_accept_walk: (path node ids, emitted tokens)."""
-    lib = load_library()
+    lib = _lib if _lib is not None else load_library()
     p, t, a = _i32(parents), _i32(tokens), _i32(argmax)
     n = len(p)
-    path = np.zeros(max(n, 1), np.int32)
-    emitted = np.zeros(max(n, 1), np.int32)
-    plen, nem = ctypes.c_int(0), ctypes.c_int(0)
-    rc = lib.tv_accept_walk(_ptr(p), _ptr(t), _ptr(a), n, _ptr(path), ctypes.byref(plen),
-                            _ptr(emitted), ctypes.byref(nem))
+    if n > TV_MAX_NODES or len(t) != n or len(a) < n:
+        raise TVError(TV_EINVAL, "tv_accept_walk: bad tree size")
+    pp, pe, pl, pn = _walk_ptrs
+    rc = lib.tv_accept_walk(_ptr(p), _ptr(t), _ptr(a), n, pp, pl, pe, pn)
     if rc != TV_OK:
         raise TVError(rc, "tv_accept_walk: invalid tree")
-    return path[:plen.value].tolist(), emitted[:nem.value].tolist()
+    return _walk_path[:_walk_len[0]].tolist(), _walk_emit[:_walk_len[1]].tolist()
 
 
 class TreeVerifier:
@@ -117,6 +127,10 @@ class TreeVerifier:
         d = _Desc(n_layer, hidden, n_qhead, n_kvhead, head_dim, ffn, vocab, self._kinds,
                   eps, rope_theta, max_ctx, max_req)
         self.vocab, self.max_ctx, self.max_req = vocab, max_ctx, max_req
+        # per-call result buffers of tv_verify_tree (copied out on return)
+        self._am = np.zeros(TV_MAX_NODES, np.int32)
+        self._gap = np.zeros(TV_MAX_NODES, np.float32)
+        self._am_ptr, self._gap_ptr = _ptr(self._am), _ptr(self._gap)
         h = ctypes.c_void_p()
         rc = self.lib.tv_create(ctypes.byref(d), ctypes.c_void_p(stream or 0), ctypes.byref(h))
         if rc != TV_OK:
@@ -183,16 +197,15 @@ class TreeVerifier:
         ``logits``: optional device fp32 tensor with room for [n, vocab]."""
         p, t = _i32(parents), _i32(tokens)
         n = int(p.size)
-        am = np.zeros(max(n, 1), np.int32)
-        gap = np.zeros(max(n, 1), np.float32)
         lp = None
         if logits is not None:
             if logits.numel() < n * self.vocab or not logits.is_contiguous():
                 raise ValueError("logits tensor too small or not contiguous")
-            lp = ctypes.c_void_p(logits.data_ptr())
-        self._check(self.lib.tv_verify_tree(self.h, req, _ptr(p), _ptr(t), n, lp, _ptr(am),
-                                            _ptr(gap)), "tv_verify_tree")
-        return am[:n], gap[:n]
+            lp = logits.data_ptr()
+        rc = self.lib.tv_verify_tree(self.h, req, _ptr(p), _ptr(t), n, lp, self._am_ptr, self._gap_ptr)
+        if rc != TV_OK:
+            self._check(rc, "tv_verify_tree")
+        return self._am[:n].copy(), self._gap[:n].copy()
 
     def verify_trees(self, reqs: Sequence[int], parents: Sequence, tokens: Sequence, logits=None):
         """tv_verify_trees: rows request after request."""
@@ -218,7 +231,9 @@ class TreeVerifier:
 
     def commit(self, req: int, path: Sequence[int]) -> None:
         p = _i32(path)
-        self._check(self.lib.tv_commit(self.h, req, _ptr(p), int(p.size)), "tv_commit")
+        rc = self.lib.tv_commit(self.h, req, _ptr(p), int(p.size))
+        if rc != TV_OK:
+            self._check(rc, "tv_commit")
 
     def ctx_len(self, req: int) -> int:
         rc = self.lib.tv_ctx_len(self.h, req)

@@ -113,13 +113,19 @@ struct RecurArgs {
     float eps;
 };
 
+// An accepted path, passed to the commit kernels by value.
+struct PathArg {
+    int len;
+    int node[kMaxRows];
+};
+
 struct RecurCommitArgs {
     float *const *states;   // [n_layers] bound states, [QH][D][D] each
     const uint16_t *save_k; // [n_layers][kMaxRows][QH][D]
     const uint16_t *save_v;
     const float *save_gc;   // [n_layers][kMaxRows][QH]
-    const int *path;
-    int path_len, QH;
+    PathArg path;
+    int QH;
 };
 
 // launch wrappers (tv_kernels.hip); each returns hipGetLastError()
@@ -135,11 +141,14 @@ hipError_t launch_pack(hipStream_t s, const uint16_t *src, uint16_t *dst, int N,
 hipError_t launch_rope_kv(hipStream_t s, const RopeArgs &a);
 hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a);
 hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t *out);
-hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M, int32_t *argmax,
-                              float *gap, float *top);
+// argmax and gap may be device-visible host memory (written directly)
+hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M, int32_t *argmax, float *gap);
 hipError_t launch_recur_tree(hipStream_t s, int D, const RecurArgs &a);
+// one thread stores v to *flag (device-visible host memory) once every
+// earlier kernel on the stream has finished
+hipError_t launch_signal(hipStream_t s, volatile int *flag, int v);
 hipError_t launch_recur_commit(hipStream_t s, int D, const RecurCommitArgs &a, int n_layers);
 hipError_t launch_commit_kv(hipStream_t s, uint16_t *const *kv_ptrs, int n_layers, int KVH,
-                            int cap, int D, int ctx, const int *path, int path_len);
+                            int cap, int D, int ctx, const PathArg &path);
 
 } // namespace tv

@@ -19,6 +19,7 @@ namespace tv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
@@ -413,7 +414,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
             const float4 v = *reinterpret_cast<const float4 *>(lt + mm * 128 + q4 * 4);
             float *dst = g.Yf + (size_t)mm * g.ldyf + n0;
             if (n0 + 3 < N && (g.ldyf & 3) == 0) {
-                *reinterpret_cast<float4 *>(dst) = v;
+                // streaming store: the logits are not read again by this pass
+                __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4 *>(dst));
             } else {
                 if (n0 < N) dst[0] = v.x;
                 if (n0 + 1 < N) dst[1] = v.y;
@@ -492,8 +494,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t *__restrict__ src, 
 
 __global__ __launch_bounds__(256) void k_top2_reduce(const Top2 *__restrict__ part, int ntiles,
                                                      int32_t *__restrict__ argmax,
-                                                     float *__restrict__ gap,
-                                                     float *__restrict__ top) {
+                                                     float *__restrict__ gap) {
     __shared__ Top2 sh[256];
     const int m = blockIdx.x, t = threadIdx.x;
     float v1 = -INFINITY, v2 = -INFINITY;
@@ -529,8 +530,6 @@ __global__ __launch_bounds__(256) void k_top2_reduce(const Top2 *__restrict__ pa
             g = (float)(((double)r.v1 - (double)r.v2) / ldexp(1.0, ex - 7));
         }
         gap[m] = g;
-        top[2 * m] = r.v1;
-        top[2 * m + 1] = r.v2;
     }
 }
 
@@ -863,17 +862,17 @@ __global__ __launch_bounds__(256) void k_recur_commit(RecurCommitArgs a) {
     __shared__ float kk[kMaxRows][D], vv[kMaxRows][D], w[kMaxRows];
     __shared__ float elast;
     const int l = blockIdx.x / a.QH, h = blockIdx.x % a.QH, tid = threadIdx.x, QH = a.QH;
-    const int L = a.path_len;
+    const int L = a.path.len;
     const uint16_t *sk = a.save_k + (size_t)l * kMaxRows * QH * D;
     const uint16_t *sv = a.save_v + (size_t)l * kMaxRows * QH * D;
     const float *sg = a.save_gc + (size_t)l * kMaxRows * QH;
     for (int idx = tid; idx < L * D; idx += 256) {
-        const int d = idx / D, e = idx % D, node = a.path[d];
+        const int d = idx / D, e = idx % D, node = a.path.node[d];
         kk[d][e] = bf2f(sk[((size_t)node * QH + h) * D + e]);
         vv[d][e] = bf2f(sv[((size_t)node * QH + h) * D + e]);
     }
-    const float gl = sg[(size_t)a.path[L - 1] * QH + h];
-    if (tid < L) w[tid] = expf(gl - sg[(size_t)a.path[tid] * QH + h]);
+    const float gl = sg[(size_t)a.path.node[L - 1] * QH + h];
+    if (tid < L) w[tid] = expf(gl - sg[(size_t)a.path.node[tid] * QH + h]);
     if (tid == 0) elast = expf(gl);
     __syncthreads();
     float *S = a.states[l] + (size_t)h * D * D;
@@ -891,8 +890,8 @@ __global__ __launch_bounds__(256) void k_recur_commit(RecurCommitArgs a) {
 // so the in-place move is safe in any order.
 
 __global__ __launch_bounds__(256) void k_commit_kv(uint16_t *const *__restrict__ kv_ptrs, int cap,
-                                                   int D, int ctx, const int *__restrict__ path,
-                                                   int path_len) {
+                                                   int D, int ctx, PathArg path) {
+    const int path_len = path.len;
     __shared__ __attribute__((aligned(16))) uint16_t buf[2 * kMaxRows * 128];
     const int layer = blockIdx.x, h = blockIdx.y;
     uint16_t *Kc = kv_ptrs[2 * layer] + (size_t)h * cap * D;
@@ -901,19 +900,24 @@ __global__ __launch_bounds__(256) void k_commit_kv(uint16_t *const *__restrict__
     const int total = path_len * per;
     for (int idx = threadIdx.x; idx < total; idx += 256) {
         const int d = idx / per, p = idx % per;
-        const size_t src = (size_t)(ctx + path[d]) * D + p * 8;
+        const size_t src = (size_t)(ctx + path.node[d]) * D + p * 8;
         *reinterpret_cast<uint4 *>(buf + d * D + p * 8) = ld16(Kc + src);
         *reinterpret_cast<uint4 *>(buf + (kMaxRows + d) * D + p * 8) = ld16(Vc + src);
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < total; idx += 256) {
         const int d = idx / per, p = idx % per;
-        if (path[d] == d) continue;
+        if (path.node[d] == d) continue;
         const size_t dst = (size_t)(ctx + d) * D + p * 8;
         *reinterpret_cast<uint4 *>(Kc + dst) = *reinterpret_cast<const uint4 *>(buf + d * D + p * 8);
         *reinterpret_cast<uint4 *>(Vc + dst) =
             *reinterpret_cast<const uint4 *>(buf + (kMaxRows + d) * D + p * 8);
     }
+}
+
+// Completion flag of a pass: stream order puts it after the results.
+__global__ void k_signal(volatile int *flag, int v) {
+    if (threadIdx.x == 0) *flag = v;
 }
 
 // ------------------------------------------------------------ launchers
@@ -990,9 +994,13 @@ hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t
     return hipGetLastError();
 }
 
-hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M, int32_t *argmax,
-                              float *gap, float *top) {
-    hipLaunchKernelGGL(k_top2_reduce, dim3(M), dim3(256), 0, s, part, ntiles, argmax, gap, top);
+hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M, int32_t *argmax, float *gap) {
+    hipLaunchKernelGGL(k_top2_reduce, dim3(M), dim3(256), 0, s, part, ntiles, argmax, gap);
+    return hipGetLastError();
+}
+
+hipError_t launch_signal(hipStream_t s, volatile int *flag, int v) {
+    hipLaunchKernelGGL(k_signal, dim3(1), dim3(64), 0, s, flag, v);
     return hipGetLastError();
 }
 
@@ -1004,6 +1012,7 @@ hipError_t launch_recur_tree(hipStream_t s, int D, const RecurArgs &a) {
 }
 
 hipError_t launch_recur_commit(hipStream_t s, int D, const RecurCommitArgs &a, int n_layers) {
+    if (a.path.len < 1 || a.path.len > kMaxRows) return hipErrorInvalidValue;
     const dim3 grid(n_layers * a.QH);
     if (D == 128) hipLaunchKernelGGL(k_recur_commit<128>, grid, dim3(256), 0, s, a);
     else if (D == 64) hipLaunchKernelGGL(k_recur_commit<64>, grid, dim3(256), 0, s, a);
@@ -1012,9 +1021,9 @@ hipError_t launch_recur_commit(hipStream_t s, int D, const RecurCommitArgs &a, i
 }
 
 hipError_t launch_commit_kv(hipStream_t s, uint16_t *const *kv_ptrs, int n_layers, int KVH, int cap,
-                            int D, int ctx, const int *path, int path_len) {
-    hipLaunchKernelGGL(k_commit_kv, dim3(n_layers, KVH), dim3(256), 0, s, kv_ptrs, cap, D, ctx, path,
-                       path_len);
+                            int D, int ctx, const PathArg &path) {
+    if (path.len < 1 || path.len > kMaxRows) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_commit_kv, dim3(n_layers, KVH), dim3(256), 0, s, kv_ptrs, cap, D, ctx, path);
     return hipGetLastError();
 }
 

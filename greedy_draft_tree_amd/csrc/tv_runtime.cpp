@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -77,16 +78,20 @@ struct tv_ctx {
     float *po = nullptr, *pm = nullptr, *pl = nullptr;
     float *rope_cos = nullptr, *rope_sin = nullptr;
     PassMeta *d_meta = nullptr;
-    int32_t *d_argmax = nullptr;
-    float *d_gap = nullptr, *d_top = nullptr;
-    int32_t *d_path = nullptr;
     float *gemm_partial = nullptr;   // split-K partial tiles
     size_t gemm_partial_floats = 0;
     // pinned host staging
     PassMeta *h_meta = nullptr;
+    // per-row results of a pass, written by the top-2 kernel straight into
+    // coherent pinned host memory (hd_*: the same memory seen from the GPU)
     int32_t *h_argmax = nullptr;
     float *h_gap = nullptr;
-    int32_t *h_path = nullptr;
+    int32_t *hd_argmax = nullptr;
+    float *hd_gap = nullptr;
+    // completion flag of the last pass (coherent pinned host memory)
+    int *h_flag = nullptr;
+    int *hd_flag = nullptr;
+    int pass_seq = 0;
     int ns_max = 0;
 
     // profiling
@@ -158,6 +163,32 @@ void harvest(tv_ctx *c) {
         if (!found) c->totals.push_back({c->recs[i].name, {(double)ms, 1}});
     }
     c->rec_used = 0;
+}
+
+// Wait for the pass's completion flag: spin on the host copy (lower wake-up
+// latency than a stream synchronisation), polling the stream now and then so
+// that a failed or drained stream ends the wait.  With event profiling on,
+// synchronise the stream so the events can be read.
+int wait_pass(tv_ctx *c, int seq) {
+    if (c->prof) {
+        HIPCHECK(c, hipStreamSynchronize(c->stream));
+        harvest(c);
+    }
+    volatile int *f = c->h_flag;
+    for (long it = 1;; ++it) {
+        if (*f == seq) break;
+        if ((it & 4095) == 0) {
+            const hipError_t q = hipStreamQuery(c->stream);
+            if (q == hipSuccess) {
+                if (*f == seq) break;
+                return fail(c, TV_EHIP, "pass finished without its completion flag");
+            }
+            if (q != hipErrorNotReady) return fail(c, TV_EHIP, "stream failed: %s", hipGetErrorString(q));
+        }
+        __builtin_ia32_pause();
+    }
+    std::atomic_thread_fence(std::memory_order_acquire);
+    return TV_OK;
 }
 
 #define LAUNCH(c, nm, call)                                                                  \
@@ -474,12 +505,14 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
         g.Yf = out; g.ldyf = m.vocab; g.part = c->part; g.meta = c->d_meta; g.mods_on = any_mods;
         GEMM(c, "gemm_head", EPI_HEAD, g);
     }
-    LAUNCH(c, "top2", launch_top2_reduce(s, c->part, ((m.vocab + 31) / 32 + 3) / 4, M, c->d_argmax,
-                                         c->d_gap, c->d_top));
-    HIPCHECK(c, hipMemcpyAsync(c->h_argmax, c->d_argmax, M * sizeof(int32_t), hipMemcpyDeviceToHost, s));
-    HIPCHECK(c, hipMemcpyAsync(c->h_gap, c->d_gap, M * sizeof(float), hipMemcpyDeviceToHost, s));
-    HIPCHECK(c, hipStreamSynchronize(s));
-    if (c->prof) harvest(c);
+    LAUNCH(c, "top2", launch_top2_reduce(s, c->part, ((m.vocab + 31) / 32 + 3) / 4, M, c->hd_argmax,
+                                         c->hd_gap));
+    const int seq = ++c->pass_seq;
+    LAUNCH(c, "signal", launch_signal(s, c->hd_flag, seq));
+    {
+        const int rc = wait_pass(c, seq);
+        if (rc) return rc;
+    }
     if (argmax) memcpy(argmax, c->h_argmax, M * sizeof(int32_t));
     if (gap) memcpy(gap, c->h_gap, M * sizeof(float));
 
@@ -574,10 +607,6 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     ALLOC(c->rope_cos, (size_t)m.max_ctx * (D / 2) * 4);
     ALLOC(c->rope_sin, (size_t)m.max_ctx * (D / 2) * 4);
     ALLOC(c->d_meta, sizeof(PassMeta));
-    ALLOC(c->d_argmax, R * 4);
-    ALLOC(c->d_gap, R * 4);
-    ALLOC(c->d_top, 2 * R * 4);
-    ALLOC(c->d_path, R * 4);
     {
         const int QD = m.n_qhead * D;
         size_t need = (size_t)8 << 20;  // room for kernel-level calls
@@ -593,9 +622,14 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     ALLOC(c->gemm_partial, c->gemm_partial_floats * 4);
 #undef ALLOC
     if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_meta, sizeof(PassMeta), hipHostMallocDefault);
-    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_argmax, R * 4, hipHostMallocDefault);
-    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_gap, R * 4, hipHostMallocDefault);
-    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_path, R * 4, hipHostMallocDefault);
+    const unsigned res_flags = hipHostMallocCoherent | hipHostMallocMapped;
+    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_argmax, R * 4, res_flags);
+    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_gap, R * 4, res_flags);
+    if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&c->hd_argmax, c->h_argmax, 0);
+    if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&c->hd_gap, c->h_gap, 0);
+    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_flag, 64, res_flags);
+    if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&c->hd_flag, c->h_flag, 0);
+    if (e == hipSuccess) *(volatile int *)c->h_flag = 0;
     if (e != hipSuccess) return cleanup(TV_EHIP);
     // RoPE table: angle pos * theta^(-2i/D) in fp64, cos and sin rounded to fp32
     {
@@ -619,8 +653,7 @@ void tv_destroy(tv_ctx *c) {
     if (c->stream) hipStreamSynchronize(c->stream);
     else hipDeviceSynchronize();
     void *dev[] = {c->X, c->XN, c->QKV, c->QR, c->ATT, c->ACT, c->ABUF, c->zeros, c->logits, c->part, c->po, c->pm, c->pl,
-                   c->rope_cos, c->rope_sin, c->d_meta, c->d_argmax, c->d_gap, c->d_top, c->d_path,
-                   c->gemm_partial};
+                   c->rope_cos, c->rope_sin, c->d_meta, c->gemm_partial};
     for (void *p : dev)
         if (p) hipFree(p);
     for (auto &q : c->reqs) {
@@ -633,7 +666,7 @@ void tv_destroy(tv_ctx *c) {
         if (q.save_v) hipFree(q.save_v);
         if (q.save_gc) hipFree(q.save_gc);
     }
-    void *host[] = {c->h_meta, c->h_argmax, c->h_gap, c->h_path};
+    void *host[] = {c->h_meta, c->h_argmax, c->h_gap, c->h_flag};
     for (void *p : host)
         if (p) hipHostFree(p);
     for (auto &r : c->recs) {
@@ -815,17 +848,18 @@ int tv_commit(tv_ctx *c, int req, const int32_t *path, int path_len) {
     bool moves = false;
     for (int d = 0; d < path_len; ++d) moves |= path[d] != d;
     hipStream_t s = c->stream;
-    memcpy(c->h_path, path, path_len * sizeof(int32_t));
-    HIPCHECK(c, hipMemcpyAsync(c->d_path, c->h_path, path_len * sizeof(int32_t), hipMemcpyHostToDevice, s));
+    PathArg pa{};
+    pa.len = path_len;
+    for (int d = 0; d < path_len; ++d) pa.node[d] = path[d];
     if (!c->recur_layers.empty()) {
         RecurCommitArgs ra{};
         ra.states = q.d_stab; ra.save_k = q.save_k; ra.save_v = q.save_v; ra.save_gc = q.save_gc;
-        ra.path = c->d_path; ra.path_len = path_len; ra.QH = c->m.n_qhead;
+        ra.path = pa; ra.QH = c->m.n_qhead;
         LAUNCH(c, "commit_state", launch_recur_commit(s, c->m.head_dim, ra, (int)c->recur_layers.size()));
     }
     if (moves && !c->attn_layers.empty()) {
         LAUNCH(c, "commit_kv", launch_commit_kv(s, q.d_kvtab, (int)c->attn_layers.size(), c->m.n_kvhead,
-                                                c->m.max_ctx, c->m.head_dim, q.ctx_len, c->d_path, path_len));
+                                                c->m.max_ctx, c->m.head_dim, q.ctx_len, pa));
     }
     q.ctx_len += path_len;
     for (int d = 0; d < path_len; ++d) {
@@ -836,7 +870,7 @@ int tv_commit(tv_ctx *c, int req, const int32_t *path, int path_len) {
     if (q.mods_on && q.d_hist)
         HIPCHECK(c, hipMemcpy(q.d_hist, q.hist_bits.data(), q.hist_bits.size() * 4, hipMemcpyHostToDevice));
     // No synchronisation: the commit is stream-ordered before the next verify,
-    // which synchronises; the pinned path buffer is rewritten only after that.
+    // which synchronises (the path travels as a kernel argument).
     q.pending = false;
     return TV_OK;
 }
@@ -901,11 +935,13 @@ int tv_head_top2(tv_ctx *c, const void *x, int M, float *logits_dev, int32_t *ar
     g.X = (const uint16_t *)x; g.ldx = m.hidden; g.W = c->head; g.M = M; g.N = m.vocab; g.K = m.hidden;
     g.Yf = logits_dev; g.ldyf = m.vocab; g.part = c->part;
     GEMM(c, "gemm_head", EPI_HEAD, g);
-    LAUNCH(c, "top2", launch_top2_reduce(s, c->part, ((m.vocab + 31) / 32 + 3) / 4, M, c->d_argmax, c->d_gap, c->d_top));
-    HIPCHECK(c, hipMemcpyAsync(c->h_argmax, c->d_argmax, M * 4, hipMemcpyDeviceToHost, s));
-    HIPCHECK(c, hipMemcpyAsync(c->h_gap, c->d_gap, M * 4, hipMemcpyDeviceToHost, s));
-    HIPCHECK(c, hipStreamSynchronize(s));
-    if (c->prof) harvest(c);
+    LAUNCH(c, "top2", launch_top2_reduce(s, c->part, ((m.vocab + 31) / 32 + 3) / 4, M, c->hd_argmax, c->hd_gap));
+    const int seq = ++c->pass_seq;
+    LAUNCH(c, "signal", launch_signal(s, c->hd_flag, seq));
+    {
+        const int rc2 = wait_pass(c, seq);
+        if (rc2) return rc2;
+    }
     memcpy(argmax, c->h_argmax, M * 4);
     if (gap) memcpy(gap, c->h_gap, M * 4);
     return TV_OK;
