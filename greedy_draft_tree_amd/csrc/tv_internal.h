@@ -59,11 +59,13 @@ struct GemmArgs {
     const void *zeros;  // >= 16 zero bytes (activation staging beyond M or K)
 };
 
-// k-range splits of a GEMM: a function of the weight shape only.
+// k-range splits of a GEMM: a function of the weight shape only.  The most
+// splits that keep the grid within 512 workgroups (two per CU of the 256, so
+// no CU holds a third while others idle), at least 4 k steps each.
 inline int gemm_splits(int N, int K) {
     const int rowblocks = ((N + 31) / 32 + 3) / 4;
     const int nsteps = (K + 63) / 64;
-    int s = (512 + rowblocks - 1) / rowblocks;
+    int s = 512 / rowblocks;
     const int most = nsteps / 4 > 1 ? nsteps / 4 : 1;   // at least 4 k steps per split
     if (s > most) s = most;
     return s < 1 ? 1 : s;

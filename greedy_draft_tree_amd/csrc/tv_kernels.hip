@@ -100,14 +100,14 @@ __device__ __forceinline__ float psum(const float *__restrict__ P, int S, int na
 }
 
 // --------------------------------------------- residual stream + RMSNorm
-// RMSNorm is y = bf16(x / sqrt(mean(x^2) + eps) * w).  One workgroup of 1024
-// threads owns one row: it forms the row's new residual stream x (the
-// embedding row, or x + bf16(sum of a projection's split-K partials)),
-// writes it, reduces its sum of squares in a fixed order and writes the
-// normalised row y for the next projection.  Each thread holds up to two
-// runs of 4 columns (hidden <= 8192).
+// RMSNorm is y = bf16(x / sqrt(mean(x^2) + eps) * w).  One workgroup owns one
+// row, one thread 8 consecutive columns (hidden <= 8192): it forms the row's
+// new residual stream x (the embedding row, or x + bf16(sum of a
+// projection's split-K partials)), writes it, reduces the sum of squares in
+// a fixed order and writes the normalised row y for the next projection.
 
 constexpr int kRowThreads = 1024;
+constexpr int kRowSplits = 12;   // split-K partials in flight per thread
 enum RowMode { ROW_EMBED = 0, ROW_RESID = 1 };
 
 __device__ __forceinline__ float4 ld_f4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
@@ -120,84 +120,57 @@ __global__ __launch_bounds__(kRowThreads) void k_row_norm(const uint16_t *__rest
                                                           uint16_t *__restrict__ X, uint16_t *__restrict__ Y) {
     __shared__ float red[kRowThreads / 64];
     const int m = blockIdx.x, t = threadIdx.x;
-    const int units = H >> 2;
+    const int n0 = 8 * t;
+    const bool ok = n0 < H;
+    const uint4 z = {0u, 0u, 0u, 0u};
     uint16_t *xr = X + (size_t)m * H;
-    float x[2][4];
+    const uint4 wv = ok ? ld16(w + n0) : z;
+    float x[8];
+    if constexpr (MODE == ROW_EMBED) {
+        const uint4 v = ok ? ld16(emb + (size_t)meta->tok[m] * H + n0) : z;
+        if (ok) *reinterpret_cast<uint4 *>(xr + n0) = v;
+        const uint16_t *ve = reinterpret_cast<const uint16_t *>(&v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = bf2f(ve[e]);
+    } else {
+        const uint4 ov = ok ? ld16(xr + n0) : z;
+        // partial (s, m, n) sits at ((n/128)*S + s)*4096 + m*128 + n%128; a
+        // thread's 8 columns share one 128-column block
+        const float *pp = P + (size_t)(ok ? n0 >> 7 : 0) * S * 4096 + (size_t)m * 128 + (n0 & 127);
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        for (int s0 = 0; s0 < S; s0 += kRowSplits) {   // loads of kRowSplits splits in flight, adds in split order
+            float4 v[kRowSplits][2];
+#pragma unroll
+            for (int i = 0; i < kRowSplits; ++i) {
+                const bool in = ok && s0 + i < S;
+                v[i][0] = in ? ld_f4(pp + (size_t)(s0 + i) * 4096) : float4{0.f, 0.f, 0.f, 0.f};
+                v[i][1] = in ? ld_f4(pp + (size_t)(s0 + i) * 4096 + 4) : float4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int i = 0; i < kRowSplits; ++i) {
+                if (s0 + i < S) {
+                    acc[0] += v[i][0].x; acc[1] += v[i][0].y; acc[2] += v[i][0].z; acc[3] += v[i][0].w;
+                    acc[4] += v[i][1].x; acc[5] += v[i][1].y; acc[6] += v[i][1].z; acc[7] += v[i][1].w;
+                }
+            }
+        }
+        const uint16_t *oe = reinterpret_cast<const uint16_t *>(&ov);
+        uint32_t nw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint16_t lo = f2bf(bf2f(oe[2 * e]) + bfround(acc[2 * e]));
+            const uint16_t hi = f2bf(bf2f(oe[2 * e + 1]) + bfround(acc[2 * e + 1]));
+            x[2 * e] = bf2f(lo);
+            x[2 * e + 1] = bf2f(hi);
+            nw[e] = (uint32_t)lo | ((uint32_t)hi << 16);
+        }
+        if (ok) *reinterpret_cast<uint4 *>(xr + n0) = uint4{nw[0], nw[1], nw[2], nw[3]};
+    }
     float ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[j][e] = 0.f;
-    }
-    if constexpr (MODE == ROW_EMBED) {
-        const uint16_t *src = emb + (size_t)meta->tok[m] * H;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int u = t + j * kRowThreads;
-            if (u < units) {
-                const uint2 v = *reinterpret_cast<const uint2 *>(src + 4 * u);
-                *reinterpret_cast<uint2 *>(xr + 4 * u) = v;
-                const uint16_t *ve = reinterpret_cast<const uint16_t *>(&v);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[j][e] = bf2f(ve[e]);
-            }
-        }
-    } else {
-        // partial (s, m, n) sits at ((n/128)*S + s)*4096 + m*128 + n%128
-        float4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        const float *pp[2];
-        bool ok[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = 4 * (t + j * kRowThreads);
-            ok[j] = n < H;
-            pp[j] = P + ((size_t)(ok[j] ? n >> 7 : 0) * S) * 4096 + (size_t)m * 128 + (n & 127);
-        }
-        for (int s0 = 0; s0 < S; s0 += 8) {   // eight splits of both runs in flight, adds in split order
-            float4 v[2][8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    v[j][i] = (ok[j] && s0 + i < S) ? ld_f4(pp[j] + (size_t)(s0 + i) * 4096)
-                                                    : float4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (s0 + i < S) {
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        acc[j].x += v[j][i].x;
-                        acc[j].y += v[j][i].y;
-                        acc[j].z += v[j][i].z;
-                        acc[j].w += v[j][i].w;
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int u = t + j * kRowThreads;
-            if (u < units) {
-                const uint2 ov = *reinterpret_cast<const uint2 *>(xr + 4 * u);
-                const uint16_t *oe = reinterpret_cast<const uint16_t *>(&ov);
-                const float a4[4] = {acc[j].x, acc[j].y, acc[j].z, acc[j].w};
-                uint16_t ne[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ne[e] = f2bf(bf2f(oe[e]) + bfround(a4[e]));
-                    x[j][e] = bf2f(ne[e]);
-                }
-                *reinterpret_cast<uint2 *>(xr + 4 * u) =
-                    uint2{(uint32_t)ne[0] | ((uint32_t)ne[1] << 16), (uint32_t)ne[2] | ((uint32_t)ne[3] << 16)};
-            }
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ss += x[j][e] * x[j][e];
-    }
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
     // fixed-order reduction: within each wave by xor shuffles, then the
     // waves' sums in wave order
 #pragma unroll
@@ -205,23 +178,19 @@ __global__ __launch_bounds__(kRowThreads) void k_row_norm(const uint16_t *__rest
     if ((t & 63) == 0) red[t >> 6] = ss;
     __syncthreads();
     float tot = 0.f;
-#pragma unroll
-    for (int i = 0; i < kRowThreads / 64; ++i) tot += red[i];
+    const int nw_ = blockDim.x >> 6;
+    for (int i = 0; i < nw_; ++i) tot += red[i];
     const float scale = 1.0f / sqrtf(tot / (float)H + eps);
-    uint16_t *yr = Y + (size_t)m * H;
+    if (!ok) return;
+    const uint16_t *we = reinterpret_cast<const uint16_t *>(&wv);
+    uint32_t yw[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int u = t + j * kRowThreads;
-        if (u < units) {
-            const uint2 wv = *reinterpret_cast<const uint2 *>(w + 4 * u);
-            const uint16_t *we = reinterpret_cast<const uint16_t *>(&wv);
-            uint16_t ye[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ye[e] = f2bf(x[j][e] * scale * bf2f(we[e]));
-            *reinterpret_cast<uint2 *>(yr + 4 * u) =
-                uint2{(uint32_t)ye[0] | ((uint32_t)ye[1] << 16), (uint32_t)ye[2] | ((uint32_t)ye[3] << 16)};
-        }
+    for (int e = 0; e < 4; ++e) {
+        const uint16_t lo = f2bf(x[2 * e] * scale * bf2f(we[2 * e]));
+        const uint16_t hi = f2bf(x[2 * e + 1] * scale * bf2f(we[2 * e + 1]));
+        yw[e] = (uint32_t)lo | ((uint32_t)hi << 16);
     }
+    *reinterpret_cast<uint4 *>(Y + (size_t)m * H + n0) = uint4{yw[0], yw[1], yw[2], yw[3]};
 }
 
 // ------------------------------------------------------------ skinny GEMM
@@ -495,28 +464,37 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t *__restrict__ src, 
 __global__ __launch_bounds__(256) void k_top2_reduce(const Top2 *__restrict__ part, int ntiles,
                                                      int32_t *__restrict__ argmax,
                                                      float *__restrict__ gap) {
-    __shared__ Top2 sh[256];
-    const int m = blockIdx.x, t = threadIdx.x;
+    // top-2 selection is order-free (ties go to the lower id), so the
+    // candidates may be merged in any grouping
+    __shared__ Top2 sh[4];
+    const int m = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
     float v1 = -INFINITY, v2 = -INFINITY;
     int i1 = 0x7fffffff, i2 = 0x7fffffff;
     const Top2 *row = part + (size_t)m * ntiles;
-    for (int i = t; i < ntiles; i += 256) {
-        const Top2 p = row[i];
-        top2_merge(v1, i1, v2, i2, p.v1, p.i1, p.v2, p.i2);
-    }
-    sh[t] = Top2{v1, i1, v2, i2};
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (t < o) {
-            Top2 a = sh[t];
-            const Top2 b = sh[t + o];
-            top2_merge(a.v1, a.i1, a.v2, a.i2, b.v1, b.i1, b.v2, b.i2);
-            sh[t] = a;
+    for (int base = 0; base < ntiles; base += 8 * 256) {   // eight loads in flight per thread
+        float4 p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int idx = base + i * 256 + t;
+            p[i] = idx < ntiles ? *reinterpret_cast<const float4 *>(row + idx)
+                                : float4{-INFINITY, __int_as_float(0x7fffffff), -INFINITY, __int_as_float(0x7fffffff)};
         }
-        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            top2_merge(v1, i1, v2, i2, p[i].x, __float_as_int(p[i].y), p[i].z, __float_as_int(p[i].w));
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float w1 = __shfl_xor(v1, o), w2 = __shfl_xor(v2, o);
+        const int j1 = __shfl_xor(i1, o), j2 = __shfl_xor(i2, o);
+        top2_merge(v1, i1, v2, i2, w1, j1, w2, j2);
+    }
+    if (lane == 0) sh[wave] = Top2{v1, i1, v2, i2};
+    __syncthreads();
     if (t == 0) {
-        const Top2 r = sh[0];
+        Top2 r = sh[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) top2_merge(r.v1, r.i1, r.v2, r.i2, sh[w].v1, sh[w].i1, sh[w].v2, sh[w].i2);
         argmax[m] = r.i1;
         // gap in bf16 ulps of top-1: ulp(x) = 2^(floor(log2|x|) - 7), or
         // 2^-133 below the normal range; the difference of two fp32 values
@@ -629,18 +607,32 @@ __global__ __launch_bounds__(320) void k_attn(AttnArgs a) {
     for (int c0 = 0; c0 < nkeys; c0 += CH) {
         const int cn = min(CH, nkeys - c0);
         __syncthreads();
-        for (int idx = tid; idx < CH * KC; idx += nthr) {
-            const int kk = idx / KC, p = idx % KC;
-            uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-            if (kk < cn) {
-                const size_t off = (size_t)(key0 + c0 + kk) * D + p * 8;
-                kv = ld16(Kb + off);
-                vv = ld16(Vb + off);
-            }
-            *reinterpret_cast<uint4 *>(Ks + kk * D + ((p ^ (kk & (KC - 1))) << 3)) = kv;
-            const uint16_t *ve = reinterpret_cast<const uint16_t *>(&vv);
+        // stage the chunk: every load of a pass is issued before any store
+        for (int base = 0; base < CH * KC; base += 8 * nthr) {
+            uint4 kv[8], vv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Vt[(p * 8 + e) * VSTR + kk] = ve[e];
+            for (int i = 0; i < 8; ++i) {
+                const int idx = base + i * nthr + tid;
+                const int kk = idx / KC, p = idx % KC;
+                kv[i] = uint4{0u, 0u, 0u, 0u};
+                vv[i] = uint4{0u, 0u, 0u, 0u};
+                if (idx < CH * KC && kk < cn) {
+                    const size_t off = (size_t)(key0 + c0 + kk) * D + p * 8;
+                    kv[i] = ld16(Kb + off);
+                    vv[i] = ld16(Vb + off);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int idx = base + i * nthr + tid;
+                if (idx < CH * KC) {
+                    const int kk = idx / KC, p = idx % KC;
+                    *reinterpret_cast<uint4 *>(Ks + kk * D + ((p ^ (kk & (KC - 1))) << 3)) = kv[i];
+                    const uint16_t *ve = reinterpret_cast<const uint16_t *>(&vv[i]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) Vt[(p * 8 + e) * VSTR + kk] = ve[e];
+                }
+            }
         }
         __syncthreads();
         if (wave * 32 >= R) continue;
@@ -755,9 +747,17 @@ __global__ __launch_bounds__(D) void k_attn_combine(AttnArgs a, uint16_t *__rest
     if (d < ns) ws[d] = (ms[d] == -INFINITY) ? 0.f : expf(ms[d] - M);
     __syncthreads();
     float L = 0.f, O = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        L += ws[s] * wl[s];
-        O += ws[s] * a.po[(b0 + (size_t)s * RP) * D + d];
+    for (int s0 = 0; s0 < ns; s0 += 8) {   // eight splits' loads in flight, adds in split order
+        float pv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] = s0 + i < ns ? a.po[(b0 + (size_t)(s0 + i) * RP) * D + d] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (s0 + i < ns) {
+                L += ws[s0 + i] * wl[s0 + i];
+                O += ws[s0 + i] * pv[i];
+            }
+        }
     }
     out[(size_t)(a.row0 + t) * a.n_qhead * D + h * D + d] = f2bf(O / L);
 }
@@ -922,19 +922,21 @@ __global__ void k_signal(volatile int *flag, int v) {
 
 // ------------------------------------------------------------ launchers
 
+static int row_threads(int H) { return ((H / 8 + 63) / 64) * 64; }
+
 hipError_t launch_embed_norm(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H,
                              const uint16_t *w, float eps, uint16_t *X, uint16_t *Y) {
-    if (H % 4 || H > 8 * kRowThreads) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_row_norm<ROW_EMBED>, dim3(M), dim3(kRowThreads), 0, s, emb, meta, nullptr, 0, H, w, eps,
-                       X, Y);
+    if (H % 8 || H > 8 * kRowThreads) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_row_norm<ROW_EMBED>, dim3(M), dim3(row_threads(H)), 0, s, emb, meta, nullptr, 0, H, w,
+                       eps, X, Y);
     return hipGetLastError();
 }
 
 hipError_t launch_resid_norm(hipStream_t s, const float *P, int S, int M, int H, const uint16_t *w, float eps,
                              uint16_t *X, uint16_t *Y) {
-    if (H % 4 || H > 8 * kRowThreads || S < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_row_norm<ROW_RESID>, dim3(M), dim3(kRowThreads), 0, s, nullptr, nullptr, P, S, H, w, eps,
-                       X, Y);
+    if (H % 8 || H > 8 * kRowThreads || S < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_row_norm<ROW_RESID>, dim3(M), dim3(row_threads(H)), 0, s, nullptr, nullptr, P, S, H, w,
+                       eps, X, Y);
     return hipGetLastError();
 }
 
