@@ -3,25 +3,39 @@
 One step is one pass of the whole hot path for each tree size n in
 {8, 16, 24, 32}: tree verify (one target-model forward over the tree against
 the KV cache, fp32 logits, argmax and top-2 gap per node), the greedy accept
-walk, and the commit of the accepted path's KV rows.  After each commit the
-request's context is reset to ``ctx`` (host metadata only), so every round
-runs at the same context length.  The draft trees carry the model's own
-greedy tokens along their spine (learned in warm-up), so the accept walk
-takes the whole spine and the commit moves real rows; branches are uniform
-ids.
+walk, and the commit of the accepted path's KV rows (and recurrent states).
+After each commit the request's context is reset to ``ctx`` (host metadata
+only), so every round runs at the same context length.  The draft trees carry
+the model's own greedy tokens along their spine (learned in warm-up), so the
+accept walk takes the spine and the commit moves real rows; branches are
+uniform ids.
+
+Configurations (``--config``; the default c1 is the headline workload):
+
+* c1: one 5120-wide decoder layer + fp32 head, trees n = 8/16/24/32.
+* c2: 64 such layers.
+* c3: the 64-layer hybrid (48 gated-recurrence + 16 attention layers), n = 16.
+* c4: c2 with two requests of 16 rows each in one joint pass (contexts
+  ``ctx`` and ``--ctx2``), score modifiers on both (repetition penalty 1.1,
+  64 biased ids, a 50% allow mask) and a drafter that is always wrong, so
+  every round commits one token per request.
 
 Inputs are synthetic and resident in HBM before timing: N(0, 0.02) bf16
-weights drawn on the device, an N(0, 1) bf16 KV cache of ``ctx`` rows.
+weights drawn on the device, N(0, 1) bf16 KV caches (and N(0, 1) fp32
+recurrent states) of ``ctx`` rows.
 
-``value`` is the whole step's algorithmic HBM bytes (weights once per
-verify, KV read, tree KV write, logits write, committed rows moved) divided
-by its wall time.  ``roofline`` reports the dominant kernel (the fp32 head)
-timed with HIP events on the library's stream during the timed region.
-``cpu_baseline`` times the CPU oracle on the same trees.
+``value`` is the whole step's algorithmic HBM bytes (weights once per verify,
+KV and state reads, tree KV written, logits written, committed rows and
+states moved) divided by its wall time.  ``roofline`` reports the dominant
+kernel (the fp32 head for c1; the gate/up projection, which takes the most
+time summed over layers, for the stacks) timed with HIP events on the
+library's stream during the timed region.  ``cpu_baseline`` times the CPU
+oracle on the same trees (c1 and c2).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +46,7 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 NS = (8, 16, 24, 32)
 MIN_CPU_S = 10.0     # the CPU baseline repeats its sample for at least this long
+ATTN, RECUR = 0, 1   # layer kinds (as in synth)
 
 
 def parse():
@@ -39,8 +54,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c1", choices=["c1", "c2"])
+    ap.add_argument("--config", default="c1", choices=["c1", "c2", "c3", "c4"])
     ap.add_argument("--ctx", type=int, default=1024)
+    ap.add_argument("--ctx2", type=int, default=8192, help="second request's context (c4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", default="full",
                     help="'full' = the same four trees; 'n8' = one 8-node tree")
@@ -51,29 +67,38 @@ def parse():
     return ap.parse_args()
 
 
-def model_bytes(shape, n, ctx, path_len):
-    """Algorithmic HBM bytes of one verify + commit (see module docstring)."""
+def model_bytes(shape, n, ctxs, path_lens, mods=False):
+    """Algorithmic HBM bytes of one verify (n rows per request, requests with
+    contexts ``ctxs``) and the commits of ``path_lens`` (module docstring)."""
     H, V, F = shape.hidden, shape.vocab, shape.ffn
     D, QH, KVH = shape.head_dim, shape.n_qhead, shape.n_kvhead
-    b = 0
-    b += n * H * 2                                  # embedding rows
+    rows = n * len(ctxs)
+    b = rows * H * 2                                    # embedding rows
     for kind in shape.kinds:
-        b += 2 * H * 2                              # two norm vectors
-        b += shape.qkv_rows * H * 2                 # wqkv
-        b += H * QH * D * 2                         # wo
-        b += 3 * F * H * 2                          # wg, wu, wd
-        b += 2 * ctx * KVH * D * 2                  # cache K and V read
-        b += 2 * n * KVH * D * 2                    # tree K and V written
-        b += 2 * 2 * path_len * KVH * D * 2         # committed rows read + written
-    b += H * 2 + V * H * 2                          # final norm, head
-    b += n * V * 4                                  # fp32 logits
+        b += 2 * H * 2                                  # two norm vectors
+        if kind == ATTN:
+            b += shape.qkv_rows * H * 2                 # wqkv
+            for ctx, pl in zip(ctxs, path_lens):
+                b += 2 * ctx * KVH * D * 2              # cache K and V read
+                b += 2 * n * KVH * D * 2                # tree K and V written
+                b += 2 * 2 * pl * KVH * D * 2           # committed rows read + written
+        else:
+            b += shape.rqkv_rows * H * 2 + QH * H * 2   # wqkv, gate projection
+            for _ in ctxs:
+                b += QH * D * D * 4                     # state read by the verify
+                b += 2 * QH * D * D * 4                 # state read + written by the commit
+        b += H * QH * D * 2                             # wo
+        b += 3 * F * H * 2                              # wg, wu, wd
+    b += H * 2 + V * H * 2                              # final norm, head
+    b += rows * V * 4                                   # fp32 logits
+    if mods:
+        b += len(ctxs) * (V * 4 + 2 * ((V + 31) // 32) * 4)   # bias, allow and history bits
     return b
 
 
 def committed_traffic():
     """Per-launch HBM bytes of the head kernel from the committed rocprofv3
     counter summary, if the kernel source it was taken on is unchanged."""
-    import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     summ = os.path.join(here, "profiles", "gemm_head_c1_layer_ctx1024_counters.md")
     src = os.path.join(here, "greedy_draft_tree_amd", "csrc", "tv_kernels.hip")
@@ -93,8 +118,43 @@ def committed_traffic():
         return None
 
 
-def head_bytes(shape, n):
-    return shape.vocab * shape.hidden * 2 + n * shape.vocab * 4 + n * shape.hidden * 2
+def head_bytes(shape, rows):
+    return shape.vocab * shape.hidden * 2 + rows * shape.vocab * 4 + rows * shape.hidden * 2
+
+
+def gateup_bytes(shape, rows):
+    return 2 * shape.ffn * shape.hidden * 2 + rows * shape.hidden * 2
+
+
+def learn_spine(tv, parents, tokens, req=0):
+    """Put the model's own greedy token on each spine node (depth by depth)."""
+    import synth
+    n = len(parents)
+    spine = synth.spine_nodes(parents)
+    for d in range(len(spine) - 1):
+        am, _ = tv.verify_tree(req, parents, tokens)
+        want = int(am[spine[d]])
+        sib = {int(tokens[j]) for j in range(1, n) if parents[j] == parents[spine[d + 1]]
+               and j != spine[d + 1]}
+        if want in sib:
+            break
+        tokens[spine[d + 1]] = want
+    return tokens
+
+
+def make_wrong(parents, tokens, argmax, vocab):
+    """Change every node whose token equals its parent's argmax, keeping
+    sibling tokens distinct: the walk then accepts nothing past the root."""
+    tokens = tokens.copy()
+    for j in range(1, len(parents)):
+        p = parents[j]
+        if tokens[j] == argmax[p]:
+            sib = {int(tokens[i]) for i in range(1, len(parents)) if parents[i] == p and i != j}
+            t = (int(argmax[p]) + 1) % vocab
+            while t in sib or t == argmax[p]:
+                t = (t + 1) % vocab
+            tokens[j] = t
+    return tokens
 
 
 def main():
@@ -106,9 +166,13 @@ def main():
     import torch
     import synth
     import workloads
+    from greedy_draft_tree_amd import accept_walk
 
-    shape = synth.C1 if a.config == "c1" else synth.C2
-    ctx = a.ctx
+    shape = {"c1": synth.C1, "c2": synth.C2, "c3": synth.C3, "c4": synth.C2}[a.config]
+    ns = {"c1": NS, "c2": NS, "c3": (16,), "c4": (16,)}[a.config]
+    ctxs = [a.ctx, a.ctx2] if a.config == "c4" else [a.ctx]
+    n_req = len(ctxs)
+    mods_on = a.config == "c4"
     torch.cuda.init()
     if a.copy_probe:
         src_t = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB
@@ -116,98 +180,146 @@ def main():
         dst_t.copy_(src_t)
         torch.cuda.synchronize()
         del src_t, dst_t
-    print(f"[bench] building {shape.name} ctx={ctx}", file=sys.stderr, flush=True)
-    want_cpu = not a.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0
-    wl = workloads.build(shape, max_ctx=ctx + 64, max_req=1, weight_device="cuda",
+    print(f"[bench] building {shape.name} ctx={ctxs}", file=sys.stderr, flush=True)
+    want_cpu = (not a.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0
+                and a.config in ("c1", "c2"))
+    wl = workloads.build(shape, max_ctx=max(ctxs) + 64, max_req=n_req, weight_device="cuda",
                          host_copy=want_cpu)
-    kv = workloads.load_context(wl, 0, ctx, seed=3)
+    hist = []
+    kv = None
+    for r, ctx in enumerate(ctxs):
+        h = synth.uniform_ids(ctx, shape.vocab, 40 + r) if mods_on else []
+        kvr = workloads.load_context(wl, r, ctx, seed=3 + r, history=h, state_seed=6)
+        if r == 0:
+            kv = kvr
+        hist.append(h)
     tv = wl.tv
-    from greedy_draft_tree_amd import accept_walk
+    if mods_on:
+        for r in range(n_req):
+            md = synth.modifiers(shape.vocab, 7 + r)
+            tv.set_modifiers(r, md.rep_penalty, md.bias_ids, md.bias_vals, md.allow_bits)
 
-    # trees: spine carries the model's own greedy tokens (learned in warm-up)
+    # trees: spine carries the model's own greedy tokens (learned in warm-up);
+    # c4's drafter is wrong at every node instead
     trees = {}
-    for n in NS:
-        parents = synth.spine_tree(n, 4)
-        tokens = synth.tree_tokens(parents, shape.vocab, 5 + n, root_token=17)
-        spine = synth.spine_nodes(parents)
-        for d in range(len(spine) - 1):
-            am, _ = tv.verify_tree(0, parents, tokens)
-            want = int(am[spine[d]])
-            sib = {int(tokens[j]) for j in range(1, n) if parents[j] == parents[spine[d + 1]]
-                   and j != spine[d + 1]}
-            if want in sib:
-                break
-            tokens[spine[d + 1]] = want
-        trees[n] = (parents, tokens)
+    for n in ns:
+        per_req = []
+        for r in range(n_req):
+            parents = synth.spine_tree(n, 4)
+            tokens = synth.tree_tokens(parents, shape.vocab, 5 + n + 100 * r, root_token=17 + r)
+            if mods_on:
+                for _ in range(4):   # a changed token changes its subtree's rows: repeat until stable
+                    am, _ = tv.verify_tree(r, parents, tokens)
+                    fixed = make_wrong(parents, tokens, am, shape.vocab)
+                    if np.array_equal(fixed, tokens):
+                        break
+                    tokens = fixed
+            else:
+                tokens = learn_spine(tv, parents, tokens, r)
+            per_req.append((parents, tokens))
+        trees[n] = per_req
     print("[bench] trees ready", file=sys.stderr, flush=True)
+    reqs = list(range(n_req))
 
     def round_(n):
-        parents, tokens = trees[n]
-        am, _ = tv.verify_tree(0, parents, tokens, logits=wl.logits)
-        path, _ = accept_walk(parents, tokens, am)
-        tv.commit(0, path)
-        tv.set_history(0, [], ctx)
-        return len(path)
+        per_req = trees[n]
+        if n_req == 1:
+            parents, tokens = per_req[0]
+            am, _ = tv.verify_tree(0, parents, tokens, logits=wl.logits)
+            ams = [am]
+        else:
+            am, _ = tv.verify_trees(reqs, [p for p, _ in per_req], [t for _, t in per_req],
+                                    logits=wl.logits)
+            ams = [am[r * n:(r + 1) * n] for r in range(n_req)]
+        lens = []
+        for r in range(n_req):
+            parents, tokens = per_req[r]
+            path, _ = accept_walk(parents, tokens, ams[r])
+            tv.commit(r, path)
+            tv.set_history(r, hist[r], ctxs[r])
+            lens.append(len(path))
+        return lens
 
     for _ in range(a.warmup):
-        for n in NS:
+        for n in ns:
             round_(n)
-    path_lens = {n: round_(n) for n in NS}
 
+    kern = "gemm_head" if a.config == "c1" else "gemm_gateup"
     tv.profile_reset()
-    tv.profile_enable(True, "gemm_head")
-    per_n = {n: [] for n in NS}
+    tv.profile_enable(True, kern)
+    per_n = {n: [] for n in ns}
+    lens_seen = {n: [] for n in ns}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(a.steps):
-        for n in NS:
+        for n in ns:
             s = time.perf_counter()
-            round_(n)
+            lens = round_(n)
             per_n[n].append(time.perf_counter() - s)
+            lens_seen[n].append(lens)
     torch.cuda.synchronize()
     total = time.perf_counter() - t0
-    head_ms, head_cnt = tv.profile_get("gemm_head")
+    k_ms, k_cnt = tv.profile_get(kern)
     tv.profile_enable(False)
 
-    step_bytes = sum(model_bytes(shape, n, ctx, path_lens[n]) for n in NS)
-    value = step_bytes * a.steps / total / 1e9
+    all_bytes = sum(model_bytes(shape, n, ctxs, lens, mods_on) for n in ns for lens in lens_seen[n])
+    step_bytes = all_bytes // a.steps
+    value = all_bytes / total / 1e9
     per = {}
-    for n in NS:
+    for n in ns:
         ms = float(np.median(per_n[n]) * 1e3)
-        by = model_bytes(shape, n, ctx, path_lens[n])
-        per[str(n)] = {"ms_median": round(ms, 4), "ms_min": round(float(np.min(per_n[n]) * 1e3), 4),
-                       "GBps": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / HBM_PEAK_GBS, 4),
-                       "rows_per_s": round(n / ms * 1e3, 1), "bytes": by, "path_len": path_lens[n]}
-    ratio = per["16"]["ms_median"] / per["8"]["ms_median"]
-    head_avg_ms = head_ms / max(head_cnt, 1)
-    hb = np.mean([head_bytes(shape, n) for n in NS])
-    achieved = hb / (head_avg_ms * 1e-3) / 1e9
+        plen = [float(np.mean([l[r] for l in lens_seen[n]])) for r in range(n_req)]
+        by = model_bytes(shape, n, ctxs, [int(round(x)) for x in plen], mods_on)
+        key = str(n) if n_req == 1 else "+".join([str(n)] * n_req)
+        per[key] = {"ms_median": round(ms, 4), "ms_min": round(float(np.min(per_n[n]) * 1e3), 4),
+                    "GBps": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / HBM_PEAK_GBS, 4),
+                    "rows_per_s": round(n * n_req / ms * 1e3, 1), "bytes": by,
+                    "path_len": plen[0] if n_req == 1 else plen}
+    ratio = per["16"]["ms_median"] / per["8"]["ms_median"] if "8" in per and "16" in per else None
+    k_avg_ms = k_ms / max(k_cnt, 1)
+    if kern == "gemm_head":
+        kb = float(np.mean([head_bytes(shape, n * n_req) for n in ns]))
+        kname = "gemm_head (k_gemm<EPI_HEAD>)"
+    else:
+        kb = float(np.mean([gateup_bytes(shape, n * n_req) for n in ns]))
+        kname = "gemm_gateup (k_gemm<EPI_SWIGLU>, split-K partials)"
+    achieved = kb / (k_avg_ms * 1e-3) / 1e9
 
     kernels = None
     if a.kernel_breakdown:
         tv.profile_reset()
         tv.profile_enable(True, "")
         for _ in range(5):
-            for n in NS:
+            for n in ns:
                 round_(n)
         kernels = {}
-        for k in ("embed_norm", "resid_norm", "gemm_qkv", "rope_kv", "attn_combine", "attn", "gemm_o",
-                  "gemm_gateup", "gemm_down", "gemm_gate", "recur_tree", "gemm_head", "top2", "commit_kv",
-                  "commit_state"):
+        for k in ("embed_norm", "resid_norm", "gemm_qkv", "rope_kv", "attn", "attn_combine", "gemm_o",
+                  "gemm_gateup", "splitk_finish", "gemm_down", "gemm_gate", "recur_tree", "gemm_head",
+                  "top2", "signal", "commit_kv", "commit_state"):
             ms, cnt = tv.profile_get(k)
             if cnt:
                 kernels[k] = {"avg_us": round(ms / cnt * 1e3, 2), "launches": cnt}
-        if "attn" in kernels and "attn_combine" in kernels:
-            ms, cnt = tv.profile_get("attn")
-            ms2, cnt2 = tv.profile_get("attn_combine")
-            kernels["attn"] = {"avg_us": round((ms - ms2) / max(cnt - cnt2, 1) * 1e3, 2),
-                               "launches": cnt - cnt2}
+        # prefix counts: "attn" also matches "attn_combine", "gemm_gate" also "gemm_gateup"
+        for k, sub in (("attn", "attn_combine"), ("gemm_gate", "gemm_gateup")):
+            if k in kernels and sub in kernels:
+                ms, cnt = tv.profile_get(k)
+                ms2, cnt2 = tv.profile_get(sub)
+                if cnt > cnt2:
+                    kernels[k] = {"avg_us": round((ms - ms2) / (cnt - cnt2) * 1e3, 2), "launches": cnt - cnt2}
+                else:
+                    del kernels[k]
         tv.profile_enable(False)
 
     cpu = None
     if want_cpu:
-        cpu = cpu_baseline(shape, wl, kv, ctx, trees, a.cpu_sample)
+        cpu = cpu_baseline(shape, wl, kv, ctxs[0], {n: trees[n][0] for n in ns}, a.cpu_sample, ns)
 
+    wname = {"c1": "c1_layer: 1 x", "c2": "c2_stack64: 64 x",
+             "c3": "c3_hybrid64: 48 recurrent + 16 attention layers x", "c4": "c4 on c2_stack64: 64 x"}[a.config]
+    desc = (f"{wname} (hidden {shape.hidden}, {shape.n_qhead}q/{shape.n_kvhead}kv heads x {shape.head_dim}, "
+            f"SwiGLU {shape.ffn}) + fp32 head V={shape.vocab}; KV cache {'/'.join(map(str, ctxs))} rows; "
+            f"one step = verify+accept+commit of trees n={','.join(map(str, ns))}"
+            + (" for 2 requests in one pass, modifiers on, wrong drafter" if a.config == "c4" else ""))
     out = {
         "metric": "ms per tree verify + achieved HBM GB/s at 8/16/24/32 nodes, 1k ctx, 1 GPU",
         "value": round(value, 2),
@@ -221,18 +333,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{shape.name}: {shape.n_layer} x (hidden {shape.hidden}, "
-                               f"{shape.n_qhead}q/{shape.n_kvhead}kv heads x {shape.head_dim}, "
-                               f"SwiGLU {shape.ffn}) + fp32 head V={shape.vocab}; KV cache {ctx} rows; "
-                               f"one step = verify+accept+commit of trees n=8,16,24,32",
-                   "ctx": ctx, "tree_nodes": list(NS), "step_bytes": step_bytes},
+        "config": {"workload": desc, "ctx": ctxs[0] if n_req == 1 else ctxs, "tree_nodes": list(ns),
+                   "requests": n_req, "step_bytes": step_bytes},
         "per_n": per,
-        "ratio_16_over_8": round(ratio, 4),
+        "ratio_16_over_8": round(ratio, 4) if ratio else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": committed_traffic() if a.config == "c1" else None,
-                     "kernel": "gemm_head (k_gemm<EPI_HEAD>)", "avg_us": round(head_avg_ms * 1e3, 2),
-                     "bytes_per_launch": int(hb), "launches": head_cnt},
+                     "traffic": committed_traffic() if (a.config == "c1" and a.ctx == 1024) else None,
+                     "kernel": kname, "avg_us": round(k_avg_ms * 1e3, 2),
+                     "bytes_per_launch": int(kb), "launches": k_cnt},
         "cpu_baseline": cpu,
     }
     if kernels:
@@ -240,22 +349,21 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(shape, wl, kv, ctx, trees, sample):
+def cpu_baseline(shape, wl, kv, ctx, trees, sample, ns):
     """The CPU oracle (brute-force tree scorer) on the same trees."""
-    import torch
     import oracle
     w_cpu = wl.host_weights
     kv_cpu = {k: v[:, :ctx].cpu() for k, v in kv.items()}
     orc = oracle.Oracle(shape, w_cpu)
     seq = orc.new_seq(cap=ctx + 40, kv=kv_cpu, ctx_len=ctx)
-    ns = NS if sample == "full" else (8,)
+    ns = ns if sample == "full" else (8,)
     t0 = time.perf_counter()
     by, trees_done, passes = 0, 0, 0
     while True:   # whole passes over the sample until at least MIN_CPU_S seconds
         for n in ns:
             parents, tokens = trees[n]
             orc.tree_scores(seq, parents, tokens)
-            by += model_bytes(shape, n, ctx, 1)
+            by += model_bytes(shape, n, [ctx], [1])
             trees_done += 1
         passes += 1
         print(f"[bench] cpu baseline pass {passes} done", file=sys.stderr, flush=True)

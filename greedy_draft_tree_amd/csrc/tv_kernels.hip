@@ -778,26 +778,64 @@ __device__ __forceinline__ float log_sigmoid(float a) {
 
 template <int D>
 __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
-    __shared__ float qs[kMaxRows][D], ks[kMaxRows][D], vs[kMaxRows][D];
+    // grid (head, value slice): a workgroup produces value columns
+    // [v0, v0 + VW) of its head for every node; the small per-head setup
+    // (norms, cumulative gates, the node-node coefficients) is repeated by
+    // the head's slices.
+    constexpr int VS = kRecurSlices;
+    constexpr int VW = D / VS;             // value columns per workgroup
+    constexpr int DP = D + 1;              // padded row stride: column walks hit distinct banks
+    constexpr int NG = 256 / VW;           // node groups in the read-out
+    constexpr int RJ = kMaxRows / NG;      // nodes per thread in the read-out
+    __shared__ float qs[kMaxRows][DP], ks[kMaxRows][DP];
+    __shared__ float vsm[kMaxRows][VW];
+    __shared__ float s0[D][VW];            // S0 rows (key index) restricted to this slice's value columns
     __shared__ float gsh[kMaxRows], gcs[kMaxRows], scale[2][kMaxRows];
     __shared__ float coef[kMaxRows][kMaxRows + 1];
-    const int h = blockIdx.x, tid = threadIdx.x, n = r.n, QH = r.QH;
+    const int h = blockIdx.x, v0 = blockIdx.y * VW, tid = threadIdx.x, n = r.n, QH = r.QH;
+    const int lane = tid & 63, wave = tid >> 6;
     const int ld = 3 * QH * D;
+
+    // state slice: every load in flight before the stores
+    {
+        constexpr int NV = D * VW / 4;     // float4 pieces
+        constexpr int PER = (NV + 255) / 256;
+        const float *S0 = r.S0 + (size_t)h * D * D + v0;
+        float4 tmp[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = tid + i * 256;
+            tmp[i] = idx < NV ? *reinterpret_cast<const float4 *>(S0 + (size_t)(idx / (VW / 4)) * D + 4 * (idx % (VW / 4)))
+                              : float4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = tid + i * 256;
+            if (idx < NV) *reinterpret_cast<float4 *>(&s0[idx / (VW / 4)][4 * (idx % (VW / 4))]) = tmp[i];
+        }
+    }
+#pragma unroll 4
     for (int idx = tid; idx < n * D; idx += 256) {
         const int t = idx / D, d = idx % D;
         const uint16_t *row = r.qkv + (size_t)(r.row0 + t) * ld;
         qs[t][d] = bf2f(row[h * D + d]);
         ks[t][d] = bf2f(row[(QH + h) * D + d]);
-        vs[t][d] = bf2f(row[(2 * QH + h) * D + d]);
+    }
+    for (int idx = tid; idx < n * VW; idx += 256) {
+        const int t = idx / VW, c = idx % VW;
+        vsm[t][c] = bf2f(r.qkv[(size_t)(r.row0 + t) * ld + (2 * QH + h) * D + v0 + c]);
     }
     if (tid < n) gsh[tid] = log_sigmoid(bf2f(r.a[(size_t)(r.row0 + tid) * QH + h]));
     __syncthreads();
-    if (tid < 2 * n) {
-        const int t = tid >> 1;
-        const float *x = (tid & 1) ? ks[t] : qs[t];
+    // L2 norms of q and k rows: one wave per vector, shuffle reduction
+    for (int vec = wave; vec < 2 * n; vec += 4) {
+        const float *x = (vec & 1) ? ks[vec >> 1] : qs[vec >> 1];
         float ss = 0.f;
-        for (int d = 0; d < D; ++d) ss += x[d] * x[d];
-        scale[tid & 1][t] = 1.0f / sqrtf(ss + r.eps);
+#pragma unroll
+        for (int d = lane; d < D; d += 64) ss += x[d] * x[d];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        if (lane == 0) scale[vec & 1][vec >> 1] = 1.0f / sqrtf(ss + r.eps);
     }
     if (tid < n) {
         // cumulative gate over the ancestors, root first (ancestors have lower indices)
@@ -825,32 +863,33 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
         coef[t][s] = cf;
     }
     __syncthreads();
-    // read-out: thread -> value index v, nodes t = grp, grp + G2, ...
-    constexpr int G2 = 256 / D;
-    const int v = tid % D, grp = tid / D;
-    float acc[kMaxRows / G2];
+    // read-out: thread -> value column c, nodes t = grp, grp + NG, ...
+    const int c = tid % VW, grp = tid / VW;
+    float acc[RJ];
 #pragma unroll
-    for (int j = 0; j < kMaxRows / G2; ++j) acc[j] = 0.f;
-    const float *S0 = r.S0 + (size_t)h * D * D;
+    for (int j = 0; j < RJ; ++j) acc[j] = 0.f;
+#pragma unroll 8
     for (int k = 0; k < D; ++k) {
-        const float s0 = S0[k * D + v];
+        const float sv = s0[k][c];
 #pragma unroll
-        for (int j = 0; j < kMaxRows / G2; ++j) {
-            const int t = grp + j * G2;
-            if (t < n) acc[j] += s0 * qs[t][k];
-        }
+        for (int j = 0; j < RJ; ++j) acc[j] += sv * qs[grp + j * NG][k];
     }
 #pragma unroll
-    for (int j = 0; j < kMaxRows / G2; ++j) {
-        const int t = grp + j * G2;
+    for (int j = 0; j < RJ; ++j) {
+        const int t = grp + j * NG;
         if (t >= n) continue;
         float o = expf(gcs[t]) * acc[j];
-        for (int s = 0; s <= t; ++s) o += coef[t][s] * vs[s][v];
-        r.out[(size_t)(r.row0 + t) * QH * D + h * D + v] = f2bf(o);
-        r.save_k[((size_t)t * QH + h) * D + v] = f2bf(ks[t][v]);
-        r.save_v[((size_t)t * QH + h) * D + v] = f2bf(vs[t][v]);
+        for (int s = 0; s <= t; ++s) o += coef[t][s] * vsm[s][c];
+        r.out[(size_t)(r.row0 + t) * QH * D + h * D + v0 + c] = f2bf(o);
+        r.save_v[((size_t)t * QH + h) * D + v0 + c] = f2bf(vsm[t][c]);
     }
-    if (tid < n) r.save_gc[(size_t)tid * QH + h] = gcs[tid];
+    if (blockIdx.y == 0) {
+        for (int idx = tid; idx < n * D; idx += 256) {
+            const int t = idx / D, d = idx % D;
+            r.save_k[((size_t)t * QH + h) * D + d] = f2bf(ks[t][d]);
+        }
+        if (tid < n) r.save_gc[(size_t)tid * QH + h] = gcs[tid];
+    }
 }
 
 // State commit: the state after the accepted path from the quantities the
@@ -1007,8 +1046,9 @@ hipError_t launch_signal(hipStream_t s, volatile int *flag, int v) {
 }
 
 hipError_t launch_recur_tree(hipStream_t s, int D, const RecurArgs &a) {
-    if (D == 128) hipLaunchKernelGGL(k_recur_tree<128>, dim3(a.QH), dim3(256), 0, s, a);
-    else if (D == 64) hipLaunchKernelGGL(k_recur_tree<64>, dim3(a.QH), dim3(256), 0, s, a);
+    if (a.n < 1 || a.n > kMaxRows) return hipErrorInvalidValue;
+    if (D == 128) hipLaunchKernelGGL(k_recur_tree<128>, dim3(a.QH, kRecurSlices), dim3(256), 0, s, a);
+    else if (D == 64) hipLaunchKernelGGL(k_recur_tree<64>, dim3(a.QH, kRecurSlices), dim3(256), 0, s, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -298,7 +298,7 @@ int gemm(tv_ctx *c, const char *name, int epi, GemmArgs g) {
     if (S > 1 && gemm_partial_need(g.N, g.K, epi == EPI_SWIGLU) > c->gemm_partial_floats)
         return fail(c, TV_EINVAL, "GEMM N=%d K=%d needs more split-K scratch than allocated", g.N, g.K);
     LAUNCH(c, name, launch_gemm(c->stream, epi, g, S));
-    if (S > 1) LAUNCH(c, name, launch_splitk_reduce(c->stream, epi, g, S));
+    if (S > 1) LAUNCH(c, "splitk_finish", launch_splitk_reduce(c->stream, epi, g, S));
     return TV_OK;
 }
 
