@@ -104,8 +104,10 @@ struct RopeArgs {
 };
 
 struct RecurArgs {
-    const uint16_t *qkv;  // [rows, 3*QH*D]: q heads, k heads, v heads (bf16)
-    const uint16_t *a;    // [rows, QH] gate pre-activations (bf16)
+    const float *qkv_part; // split-K partials of the [rows, 3*QH*D] projection (q heads, k heads, v heads)
+    int qkv_S;             // its k-range splits
+    const float *a_part;   // split-K partials of the [rows, QH] gate pre-activations
+    int a_S;
     const float *S0;      // [QH][D][D] state before the round (key index, value index)
     const PassMeta *meta;
     uint16_t *out;        // [rows, QH*D] read-out (bf16)
@@ -144,12 +146,16 @@ hipError_t launch_pack(hipStream_t s, const uint16_t *src, uint16_t *dst, int N,
 hipError_t launch_rope_kv(hipStream_t s, const RopeArgs &a);
 hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a);
 hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t *out);
-// argmax and gap may be device-visible host memory (written directly)
-hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M, int32_t *argmax, float *gap);
+// Per-row result of a pass: argmax and the gap's bits, written by one 8-byte
+// store into device-visible host memory.  The host fills the records with
+// kResultEmpty before a pass and waits until every row's record has changed.
+struct RowResult {
+    int32_t argmax;
+    uint32_t gap_bits;
+};
+constexpr uint32_t kGapEmpty = 0x7fc0deadu;   // a NaN pattern no gap takes
+hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M, RowResult *res);
 hipError_t launch_recur_tree(hipStream_t s, int D, const RecurArgs &a);
-// one thread stores v to *flag (device-visible host memory) once every
-// earlier kernel on the stream has finished
-hipError_t launch_signal(hipStream_t s, volatile int *flag, int v);
 hipError_t launch_recur_commit(hipStream_t s, int D, const RecurCommitArgs &a, int n_layers);
 hipError_t launch_commit_kv(hipStream_t s, uint16_t *const *kv_ptrs, int n_layers, int KVH,
                             int cap, int D, int ctx, const PathArg &path);

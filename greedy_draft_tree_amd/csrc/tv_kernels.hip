@@ -238,21 +238,32 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, int tile, int l
         int i1 = 0x7fffffff, i2 = 0x7fffffff;
         const bool mods = g.mods_on && cok;
         const HeadMods *md = mods ? &g.meta->mods[g.meta->row_req[m]] : nullptr;
+        // modifiers over this tile's 32 columns as bit masks: word `tile` of
+        // the vocabulary bitsets covers exactly columns tile*32 .. +31
+        uint32_t prior = 0u, allow = 0xffffffffu;
+        float rep = 1.0f;
+        if (mods) {
+            rep = md->rep;
+            if (rep != 1.0f) {
+                if (md->hist_bits) prior = md->hist_bits[tile];
+                const int L = g.meta->path_len[m];
+                const int *pt = g.meta->path_tok + m * kMaxRows;
+                for (int j = 0; j < L; ++j) {
+                    const unsigned col = (unsigned)(pt[j] - tile * 32);
+                    if (col < 32u) prior |= 1u << col;
+                }
+            }
+            if (md->allow_bits) allow = md->allow_bits[tile];
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int n = tile * 32 + acc_row(r, hf);
+            const int col = acc_row(r, hf), n = tile * 32 + col;
             if (!cok || n >= N) continue;
             float s = acc[r];
             if (mods) {
-                if (md->rep != 1.0f) {
-                    bool prior = md->hist_bits && ((md->hist_bits[n >> 5] >> (n & 31)) & 1u);
-                    const int L = g.meta->path_len[m];
-                    const int *pt = g.meta->path_tok + m * kMaxRows;
-                    for (int j = 0; j < L && !prior; ++j) prior = (pt[j] == n);
-                    if (prior) s = s > 0.f ? s / md->rep : s * md->rep;
-                }
+                if ((prior >> col) & 1u) s = s > 0.f ? s / rep : s * rep;
                 if (md->bias) s = s + md->bias[n];
-                if (md->allow_bits && !((md->allow_bits[n >> 5] >> (n & 31)) & 1u)) s = -INFINITY;
+                if (!((allow >> col) & 1u)) s = -INFINITY;
             }
             top2_insert(v1, i1, v2, i2, s, n);
         }
@@ -462,8 +473,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t *__restrict__ src, 
 // selection under a strict order, so it does not depend on the merge order.
 
 __global__ __launch_bounds__(256) void k_top2_reduce(const Top2 *__restrict__ part, int ntiles,
-                                                     int32_t *__restrict__ argmax,
-                                                     float *__restrict__ gap) {
+                                                     RowResult *__restrict__ res) {
     // top-2 selection is order-free (ties go to the lower id), so the
     // candidates may be merged in any grouping
     __shared__ Top2 sh[4];
@@ -495,7 +505,6 @@ __global__ __launch_bounds__(256) void k_top2_reduce(const Top2 *__restrict__ pa
         Top2 r = sh[0];
 #pragma unroll
         for (int w = 1; w < 4; ++w) top2_merge(r.v1, r.i1, r.v2, r.i2, sh[w].v1, sh[w].i1, sh[w].v2, sh[w].i2);
-        argmax[m] = r.i1;
         // gap in bf16 ulps of top-1: ulp(x) = 2^(floor(log2|x|) - 7), or
         // 2^-133 below the normal range; the difference of two fp32 values
         // is exact in fp64.
@@ -507,7 +516,9 @@ __global__ __launch_bounds__(256) void k_top2_reduce(const Top2 *__restrict__ pa
             const int ex = (e == 0) ? -126 : (int)e - 127;
             g = (float)(((double)r.v1 - (double)r.v2) / ldexp(1.0, ex - 7));
         }
-        gap[m] = g;
+        // argmax and gap leave together in one 8-byte store
+        *reinterpret_cast<volatile uint64_t *>(res + m) =
+            ((uint64_t)__float_as_uint(g) << 32) | (uint64_t)(uint32_t)r.i1;
     }
 }
 
@@ -794,7 +805,6 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     __shared__ float coef[kMaxRows][kMaxRows + 1];
     const int h = blockIdx.x, v0 = blockIdx.y * VW, tid = threadIdx.x, n = r.n, QH = r.QH;
     const int lane = tid & 63, wave = tid >> 6;
-    const int ld = 3 * QH * D;
 
     // state slice: every load in flight before the stores
     {
@@ -814,18 +824,19 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
             if (idx < NV) *reinterpret_cast<float4 *>(&s0[idx / (VW / 4)][4 * (idx % (VW / 4))]) = tmp[i];
         }
     }
-#pragma unroll 4
+    // projection outputs: the split-K partials summed in k-range order and
+    // rounded to bf16 (the projection's output rounding)
+#pragma unroll 2
     for (int idx = tid; idx < n * D; idx += 256) {
         const int t = idx / D, d = idx % D;
-        const uint16_t *row = r.qkv + (size_t)(r.row0 + t) * ld;
-        qs[t][d] = bf2f(row[h * D + d]);
-        ks[t][d] = bf2f(row[(QH + h) * D + d]);
+        qs[t][d] = bfround(psum(r.qkv_part, r.qkv_S, 1, 0, r.row0 + t, h * D + d));
+        ks[t][d] = bfround(psum(r.qkv_part, r.qkv_S, 1, 0, r.row0 + t, (QH + h) * D + d));
     }
     for (int idx = tid; idx < n * VW; idx += 256) {
         const int t = idx / VW, c = idx % VW;
-        vsm[t][c] = bf2f(r.qkv[(size_t)(r.row0 + t) * ld + (2 * QH + h) * D + v0 + c]);
+        vsm[t][c] = bfround(psum(r.qkv_part, r.qkv_S, 1, 0, r.row0 + t, (2 * QH + h) * D + v0 + c));
     }
-    if (tid < n) gsh[tid] = log_sigmoid(bf2f(r.a[(size_t)(r.row0 + tid) * QH + h]));
+    if (tid < n) gsh[tid] = log_sigmoid(bfround(psum(r.a_part, r.a_S, 1, 0, r.row0 + tid, h)));
     __syncthreads();
     // L2 norms of q and k rows: one wave per vector, shuffle reduction
     for (int vec = wave; vec < 2 * n; vec += 4) {
@@ -954,11 +965,6 @@ __global__ __launch_bounds__(256) void k_commit_kv(uint16_t *const *__restrict__
     }
 }
 
-// Completion flag of a pass: stream order puts it after the results.
-__global__ void k_signal(volatile int *flag, int v) {
-    if (threadIdx.x == 0) *flag = v;
-}
-
 // ------------------------------------------------------------ launchers
 
 static int row_threads(int H) { return ((H / 8 + 63) / 64) * 64; }
@@ -1035,13 +1041,8 @@ hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t
     return hipGetLastError();
 }
 
-hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M, int32_t *argmax, float *gap) {
-    hipLaunchKernelGGL(k_top2_reduce, dim3(M), dim3(256), 0, s, part, ntiles, argmax, gap);
-    return hipGetLastError();
-}
-
-hipError_t launch_signal(hipStream_t s, volatile int *flag, int v) {
-    hipLaunchKernelGGL(k_signal, dim3(1), dim3(64), 0, s, flag, v);
+hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M, RowResult *res) {
+    hipLaunchKernelGGL(k_top2_reduce, dim3(M), dim3(256), 0, s, part, ntiles, res);
     return hipGetLastError();
 }
 

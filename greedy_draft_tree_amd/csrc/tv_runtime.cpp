@@ -70,8 +70,7 @@ struct tv_ctx {
     std::vector<Req> reqs;
 
     // scratch (library-owned)
-    uint16_t *X = nullptr, *XN = nullptr, *QKV = nullptr, *QR = nullptr, *ATT = nullptr,
-             *ACT = nullptr, *ABUF = nullptr;
+    uint16_t *X = nullptr, *XN = nullptr, *QR = nullptr, *ATT = nullptr, *ACT = nullptr;
     float *logits = nullptr;  // [32, V] when the caller passes none
     void *zeros = nullptr;    // 256 zero bytes
     Top2 *part = nullptr;
@@ -82,16 +81,11 @@ struct tv_ctx {
     size_t gemm_partial_floats = 0;
     // pinned host staging
     PassMeta *h_meta = nullptr;
-    // per-row results of a pass, written by the top-2 kernel straight into
-    // coherent pinned host memory (hd_*: the same memory seen from the GPU)
-    int32_t *h_argmax = nullptr;
-    float *h_gap = nullptr;
-    int32_t *hd_argmax = nullptr;
-    float *hd_gap = nullptr;
-    // completion flag of the last pass (coherent pinned host memory)
-    int *h_flag = nullptr;
-    int *hd_flag = nullptr;
-    int pass_seq = 0;
+    // per-row results of a pass (RowResult), written by the top-2 kernel
+    // straight into coherent pinned host memory (hd_res: the same memory
+    // seen from the GPU)
+    RowResult *h_res = nullptr;
+    RowResult *hd_res = nullptr;
     int ns_max = 0;
 
     // profiling
@@ -165,23 +159,37 @@ void harvest(tv_ctx *c) {
     c->rec_used = 0;
 }
 
-// Wait for the pass's completion flag: spin on the host copy (lower wake-up
-// latency than a stream synchronisation), polling the stream now and then so
-// that a failed or drained stream ends the wait.  With event profiling on,
-// synchronise the stream so the events can be read.
-int wait_pass(tv_ctx *c, int seq) {
+// Mark the result records of rows [0, M) empty (before enqueueing a pass).
+void clear_results(tv_ctx *c, int M) {
+    volatile RowResult *r = c->h_res;
+    for (int m = 0; m < M; ++m) {
+        r[m].argmax = -1;
+        r[m].gap_bits = kGapEmpty;
+    }
+    std::atomic_thread_fence(std::memory_order_release);
+}
+
+// Wait until the top-2 kernel has filled every row's record: spin on the
+// pinned host copy (lower wake-up latency than a stream synchronisation),
+// polling the stream now and then so that a failed or drained stream ends
+// the wait.  With event profiling on, synchronise the stream so the events
+// can be read.
+int wait_results(tv_ctx *c, int M) {
     if (c->prof) {
         HIPCHECK(c, hipStreamSynchronize(c->stream));
         harvest(c);
     }
-    volatile int *f = c->h_flag;
+    volatile RowResult *r = c->h_res;
+    int m = 0;
     for (long it = 1;; ++it) {
-        if (*f == seq) break;
+        while (m < M && r[m].argmax != -1 && r[m].gap_bits != kGapEmpty) ++m;
+        if (m == M) break;
         if ((it & 4095) == 0) {
             const hipError_t q = hipStreamQuery(c->stream);
             if (q == hipSuccess) {
-                if (*f == seq) break;
-                return fail(c, TV_EHIP, "pass finished without its completion flag");
+                while (m < M && r[m].argmax != -1 && r[m].gap_bits != kGapEmpty) ++m;
+                if (m == M) break;
+                return fail(c, TV_EHIP, "pass finished without the result of row %d", m);
             }
             if (q != hipErrorNotReady) return fail(c, TV_EHIP, "stream failed: %s", hipGetErrorString(q));
         }
@@ -189,6 +197,14 @@ int wait_pass(tv_ctx *c, int seq) {
     }
     std::atomic_thread_fence(std::memory_order_acquire);
     return TV_OK;
+}
+
+// Copy the records out: argmax[m] and gap[m] (either may be null).
+void read_results(tv_ctx *c, int M, int32_t *argmax, float *gap) {
+    for (int m = 0; m < M; ++m) {
+        if (argmax) argmax[m] = c->h_res[m].argmax;
+        if (gap) memcpy(gap + m, &c->h_res[m].gap_bits, 4);
+    }
 }
 
 #define LAUNCH(c, nm, call)                                                                  \
@@ -302,12 +318,13 @@ int gemm(tv_ctx *c, const char *name, int epi, GemmArgs g) {
     return TV_OK;
 }
 
-// A projection whose consumer finishes the sums: partials only, *S = splits.
-int gemm_partial(tv_ctx *c, const char *name, GemmArgs g, int *S) {
-    g.partial = c->gemm_partial;
+// A projection whose consumer finishes the sums: partials only (at float
+// offset `off` of the split-K scratch), *S = splits.
+int gemm_partial(tv_ctx *c, const char *name, GemmArgs g, int *S, size_t off = 0) {
+    g.partial = c->gemm_partial + off;
     g.zeros = c->zeros;
     *S = gemm_splits(g.N, g.K);
-    if (gemm_partial_need(g.N, g.K, false, true) > c->gemm_partial_floats)
+    if (off + gemm_partial_need(g.N, g.K, false, true) > c->gemm_partial_floats)
         return fail(c, TV_EINVAL, "GEMM N=%d K=%d needs more split-K scratch than allocated", g.N, g.K);
     LAUNCH(c, name, launch_gemm(c->stream, EPI_PARTIAL, g, *S));
     return TV_OK;
@@ -402,6 +419,7 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
     }
     const int M = total;
     hipStream_t s = c->stream;
+    clear_results(c, M);
     HIPCHECK(c, hipMemcpyAsync(c->d_meta, c->h_meta, sizeof(PassMeta), hipMemcpyHostToDevice, s));
 
     const int H = m.hidden, D = m.head_dim, QH = m.n_qhead, KVH = m.n_kvhead;
@@ -451,20 +469,28 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
             }
         } else {
             const int rl = c->recur_index[l];
+            // q/k/v and gate projections leave split-K partials (the gate's
+            // after the qkv ones); the read-out kernel finishes both
             GemmArgs g{};
             NORMED(g, c->attn_norm[l]);
             g.W = c->wqkv[l]; g.M = M; g.N = 3 * QH * D; g.K = H;
-            g.Y = c->QKV; g.ldy = g.N;
-            GEMM(c, "gemm_qkv", EPI_BF16, g);
+            int Sq = 0;
+            GEMMP(c, "gemm_qkv", g, Sq);
+            const size_t a_off = gemm_partial_need(g.N, g.K, false, true);
             GemmArgs ga{};
             NORMED(ga, c->attn_norm[l]);
             ga.W = c->wa[l]; ga.M = M; ga.N = QH; ga.K = H;
-            ga.Y = c->ABUF; ga.ldy = QH;
-            GEMM(c, "gemm_gate", EPI_BF16, ga);
+            int Sa = 0;
+            {
+                const int rc_ = gemm_partial(c, "gemm_gate", ga, &Sa, a_off);
+                if (rc_) return rc_;
+            }
             for (int r = 0; r < n_req; ++r) {
                 Req &q = c->reqs[reqs[r]];
                 RecurArgs ra{};
-                ra.qkv = c->QKV; ra.a = c->ABUF; ra.S0 = q.S[l]; ra.meta = c->d_meta; ra.out = c->ATT;
+                ra.qkv_part = c->gemm_partial; ra.qkv_S = Sq;
+                ra.a_part = c->gemm_partial + a_off; ra.a_S = Sa;
+                ra.S0 = q.S[l]; ra.meta = c->d_meta; ra.out = c->ATT;
                 const size_t per = (size_t)kMaxRows * QH * D;
                 ra.save_k = q.save_k + rl * per;
                 ra.save_v = q.save_v + rl * per;
@@ -505,16 +531,12 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
         g.Yf = out; g.ldyf = m.vocab; g.part = c->part; g.meta = c->d_meta; g.mods_on = any_mods;
         GEMM(c, "gemm_head", EPI_HEAD, g);
     }
-    LAUNCH(c, "top2", launch_top2_reduce(s, c->part, ((m.vocab + 31) / 32 + 3) / 4, M, c->hd_argmax,
-                                         c->hd_gap));
-    const int seq = ++c->pass_seq;
-    LAUNCH(c, "signal", launch_signal(s, c->hd_flag, seq));
+    LAUNCH(c, "top2", launch_top2_reduce(s, c->part, ((m.vocab + 31) / 32 + 3) / 4, M, c->hd_res));
     {
-        const int rc = wait_pass(c, seq);
+        const int rc = wait_results(c, M);
         if (rc) return rc;
     }
-    if (argmax) memcpy(argmax, c->h_argmax, M * sizeof(int32_t));
-    if (gap) memcpy(gap, c->h_gap, M * sizeof(float));
+    read_results(c, M, argmax, gap);
 
     for (int r = 0; r < n_req; ++r) {
         Req &q = c->reqs[reqs[r]];
@@ -577,18 +599,15 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     auto cleanup = [&](int rc) { tv_destroy(c); return rc; };
     const int R = kMaxRows;
     const int H = m.hidden, D = m.head_dim;
-    const size_t qkv = (size_t)std::max((m.n_qhead + 2 * m.n_kvhead) * D, 3 * m.n_qhead * D);
     c->ns_max = 32 + 1;  // at most 32 cache splits (attn_span) plus the tree split
     const size_t RP = (size_t)kMaxRows * kMaxGroup;
     hipError_t e = hipSuccess;
 #define ALLOC(p, bytes) if (e == hipSuccess) e = hipMalloc((void **)&(p), (bytes))
     ALLOC(c->X, (size_t)R * H * 2);
     ALLOC(c->XN, (size_t)R * H * 2);
-    ALLOC(c->QKV, (size_t)R * qkv * 2);
     ALLOC(c->QR, (size_t)R * m.n_qhead * D * 2);
     ALLOC(c->ATT, (size_t)R * m.n_qhead * D * 2);
     ALLOC(c->ACT, (size_t)R * m.ffn * 2);
-    ALLOC(c->ABUF, (size_t)R * m.n_qhead * 2);
     ALLOC(c->zeros, 256);
     if (e == hipSuccess) e = hipMemset(c->zeros, 0, 256);
     if (!c->recur_layers.empty()) {
@@ -611,8 +630,8 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
         const int QD = m.n_qhead * D;
         size_t need = (size_t)8 << 20;  // room for kernel-level calls
         need = std::max(need, gemm_partial_need((m.n_qhead + 2 * m.n_kvhead) * D, H, false, true));
-        need = std::max(need, gemm_partial_need(3 * QD, H, false));
-        need = std::max(need, gemm_partial_need(m.n_qhead, H, false));
+        // a recurrent layer keeps its qkv and gate partials side by side
+        need = std::max(need, gemm_partial_need(3 * QD, H, false, true) + gemm_partial_need(m.n_qhead, H, false, true));
         need = std::max(need, gemm_partial_need(H, QD, false, true));
         need = std::max(need, gemm_partial_need(m.ffn, H, true));
         need = std::max(need, gemm_partial_need(H, m.ffn, false, true));
@@ -623,13 +642,8 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
 #undef ALLOC
     if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_meta, sizeof(PassMeta), hipHostMallocDefault);
     const unsigned res_flags = hipHostMallocCoherent | hipHostMallocMapped;
-    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_argmax, R * 4, res_flags);
-    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_gap, R * 4, res_flags);
-    if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&c->hd_argmax, c->h_argmax, 0);
-    if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&c->hd_gap, c->h_gap, 0);
-    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_flag, 64, res_flags);
-    if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&c->hd_flag, c->h_flag, 0);
-    if (e == hipSuccess) *(volatile int *)c->h_flag = 0;
+    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_res, R * sizeof(RowResult), res_flags);
+    if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&c->hd_res, c->h_res, 0);
     if (e != hipSuccess) return cleanup(TV_EHIP);
     // RoPE table: angle pos * theta^(-2i/D) in fp64, cos and sin rounded to fp32
     {
@@ -652,7 +666,7 @@ void tv_destroy(tv_ctx *c) {
     if (!c) return;
     if (c->stream) hipStreamSynchronize(c->stream);
     else hipDeviceSynchronize();
-    void *dev[] = {c->X, c->XN, c->QKV, c->QR, c->ATT, c->ACT, c->ABUF, c->zeros, c->logits, c->part, c->po, c->pm, c->pl,
+    void *dev[] = {c->X, c->XN, c->QR, c->ATT, c->ACT, c->zeros, c->logits, c->part, c->po, c->pm, c->pl,
                    c->rope_cos, c->rope_sin, c->d_meta, c->gemm_partial};
     for (void *p : dev)
         if (p) hipFree(p);
@@ -666,7 +680,7 @@ void tv_destroy(tv_ctx *c) {
         if (q.save_v) hipFree(q.save_v);
         if (q.save_gc) hipFree(q.save_gc);
     }
-    void *host[] = {c->h_meta, c->h_argmax, c->h_gap, c->h_flag};
+    void *host[] = {c->h_meta, c->h_res};
     for (void *p : host)
         if (p) hipHostFree(p);
     for (auto &r : c->recs) {
@@ -934,16 +948,14 @@ int tv_head_top2(tv_ctx *c, const void *x, int M, float *logits_dev, int32_t *ar
     GemmArgs g{};
     g.X = (const uint16_t *)x; g.ldx = m.hidden; g.W = c->head; g.M = M; g.N = m.vocab; g.K = m.hidden;
     g.Yf = logits_dev; g.ldyf = m.vocab; g.part = c->part;
+    clear_results(c, M);
     GEMM(c, "gemm_head", EPI_HEAD, g);
-    LAUNCH(c, "top2", launch_top2_reduce(s, c->part, ((m.vocab + 31) / 32 + 3) / 4, M, c->hd_argmax, c->hd_gap));
-    const int seq = ++c->pass_seq;
-    LAUNCH(c, "signal", launch_signal(s, c->hd_flag, seq));
+    LAUNCH(c, "top2", launch_top2_reduce(s, c->part, ((m.vocab + 31) / 32 + 3) / 4, M, c->hd_res));
     {
-        const int rc2 = wait_pass(c, seq);
+        const int rc2 = wait_results(c, M);
         if (rc2) return rc2;
     }
-    memcpy(argmax, c->h_argmax, M * 4);
-    if (gap) memcpy(gap, c->h_gap, M * 4);
+    read_results(c, M, argmax, gap);
     return TV_OK;
 }
 
