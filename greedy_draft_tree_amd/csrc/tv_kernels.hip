@@ -23,12 +23,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// fp32 -> bf16, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even (NaN stays NaN): gfx950's
+// v_cvt_pk_bf16_f32, which equals the textbook rounding (add 0x7fff plus the
+// lowest kept bit, truncate) on every non-NaN input.
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// two values at once: a in the low half, b in the high half
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 __device__ __forceinline__ float bfround(float f) { return bf2f(f2bf(f)); }
@@ -577,14 +581,16 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
 // only on ctx, so a row's result does not depend on the other rows.
 
 template <int D>
-__global__ __launch_bounds__(320) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(64 * (kAttnComputeWaves + kAttnLoaderWaves)) void k_attn(AttnArgs a) {
     constexpr int CH = kAttnChunk;     // keys per LDS stage
     constexpr int KC = D / 8;          // 16-byte chunks per key row
     constexpr int VSTR = CH + 4;       // bf16 stride of a transposed V row
     constexpr int NDB = D / 32;        // output dim blocks
     constexpr int NKK = D / 16;        // dim steps of the score MFMA
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[CH * D];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
+    // two LDS stages: while the compute waves use one, the loader waves fill
+    // the other with the next chunk of keys
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][CH * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VSTR];
 
     const int split = blockIdx.x, kvh = blockIdx.y;
     const int tid = threadIdx.x, nthr = blockDim.x;
@@ -592,13 +598,52 @@ __global__ __launch_bounds__(320) void k_attn(AttnArgs a) {
     const int hf = lane >> 5, c = lane & 31;
     const int G = a.G, n = a.n;
     const int R = G * n;
+    const int cw = (R + 31) >> 5;              // compute waves; any further waves only load
+    const bool loaders = nthr > cw * 64;
     const bool tree = split >= a.n_ctx_split;
     const int key0 = tree ? a.ctx : split * a.span;
     const int nkeys = tree ? n : min(a.span, a.ctx - key0);
-    const int row = wave * 32 + c;             // this lane's query row
-    const bool rowok = row < R;
+    const int nch = (nkeys + CH - 1) / CH;
+    const int row = wave * 32 + c;             // this lane's query row (compute waves)
+    const bool rowok = wave < cw && row < R;
     const int t = rowok ? row / G : 0, hh = rowok ? row % G : 0;
     const uint32_t anc = a.meta->anc[a.row0 + t];
+
+    const uint16_t *Kb = a.Kc + (size_t)kvh * a.cap * D;
+    const uint16_t *Vb = a.Vc + (size_t)kvh * a.cap * D;
+    // stage the chunk of keys starting at c0 into buffer buf, by threads
+    // [0, nt) of a group (tg = this thread's index in it); every load of a
+    // pass (SB pieces of K and of V per thread) is issued before any store
+    constexpr int SB = 4;
+    auto stage = [&](int c0, int buf, int tg, int nt) {
+        const int cn = min(CH, nkeys - c0);
+        for (int base = 0; base < CH * KC; base += SB * nt) {
+            uint4 kv[SB], vv[SB];
+#pragma unroll
+            for (int i = 0; i < SB; ++i) {
+                const int idx = base + i * nt + tg;
+                const int kk = idx / KC, p = idx % KC;
+                kv[i] = uint4{0u, 0u, 0u, 0u};
+                vv[i] = uint4{0u, 0u, 0u, 0u};
+                if (idx < CH * KC && kk < cn) {
+                    const size_t off = (size_t)(key0 + c0 + kk) * D + p * 8;
+                    kv[i] = ld16(Kb + off);
+                    vv[i] = ld16(Vb + off);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < SB; ++i) {
+                const int idx = base + i * nt + tg;
+                if (idx < CH * KC) {
+                    const int kk = idx / KC, p = idx % KC;
+                    *reinterpret_cast<uint4 *>(Ks[buf] + kk * D + ((p ^ (kk & (KC - 1))) << 3)) = kv[i];
+                    const uint16_t *ve = reinterpret_cast<const uint16_t *>(&vv[i]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) Vt[buf][(p * 8 + e) * VSTR + kk] = ve[e];
+                }
+            }
+        }
+    };
 
     // the wave's 32 query rows, dims 16kk + 8hf .. +8 for each kk
     uint4 q[NKK];
@@ -611,119 +656,103 @@ __global__ __launch_bounds__(320) void k_attn(AttnArgs a) {
     f32x16 o[NDB];
 #pragma unroll
     for (int d = 0; d < NDB; ++d) o[d] = (f32x16){};
-    float mrun = -INFINITY, lrun = 0.f;
+    float mrun = -INFINITY, lrun = 0.f;   // running max (base-2 units) and sum
+    const float scale2 = a.scale * 1.4426950408889634f;
 
-    const uint16_t *Kb = a.Kc + (size_t)kvh * a.cap * D;
-    const uint16_t *Vb = a.Vc + (size_t)kvh * a.cap * D;
-    for (int c0 = 0; c0 < nkeys; c0 += CH) {
-        const int cn = min(CH, nkeys - c0);
-        __syncthreads();
-        // stage the chunk: every load of a pass is issued before any store
-        for (int base = 0; base < CH * KC; base += 8 * nthr) {
-            uint4 kv[8], vv[8];
+    if (nch > 0) stage(0, 0, tid, nthr);      // the first chunk: every thread
+    __syncthreads();
+    for (int ci = 0; ci < nch; ++ci) {
+        const int buf = ci & 1, c0 = ci * CH;
+        if (wave >= cw) {
+            if (ci + 1 < nch) stage(c0 + CH, buf ^ 1, tid - cw * 64, nthr - cw * 64);   // loader waves
+        } else if (wave * 32 < R) {
+            const int cn = min(CH, nkeys - c0);
+            const uint16_t *Kl = Ks[buf];
+            const uint16_t *Vl = Vt[buf];
+            // S^T for 2 blocks of 32 keys: lane (c, hf) holds rows=c, keys kb*32 + acc_row(r, hf)
+            f32x16 s[CH / 32];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int idx = base + i * nthr + tid;
-                const int kk = idx / KC, p = idx % KC;
-                kv[i] = uint4{0u, 0u, 0u, 0u};
-                vv[i] = uint4{0u, 0u, 0u, 0u};
-                if (idx < CH * KC && kk < cn) {
-                    const size_t off = (size_t)(key0 + c0 + kk) * D + p * 8;
-                    kv[i] = ld16(Kb + off);
-                    vv[i] = ld16(Vb + off);
+            for (int kb = 0; kb < CH / 32; ++kb) {
+                s[kb] = (f32x16){};
+                const int key = kb * 32 + c;
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const uint4 ka = *reinterpret_cast<const uint4 *>(Kl + key * D + (((2 * kk + hf) ^ (key & (KC - 1))) << 3));
+                    s[kb] = mfma32(ka, q[kk], s[kb]);
                 }
             }
+            // visible keys of the chunk as a bit mask: inside the range, and
+            // for the tree's own keys an ancestor-or-self of this row
+            uint64_t vis = cn >= 64 ? ~0ull : ((1ull << cn) - 1ull);
+            if (tree) vis &= (uint64_t)anc;   // the tree's keys are one chunk (c0 = 0)
+            if (!rowok) vis = 0ull;
+            // scores in base-2 units: softmax(x * scale) = 2^(x * scale * log2 e - max)
+            float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int idx = base + i * nthr + tid;
-                if (idx < CH * KC) {
-                    const int kk = idx / KC, p = idx % KC;
-                    *reinterpret_cast<uint4 *>(Ks + kk * D + ((p ^ (kk & (KC - 1))) << 3)) = kv[i];
-                    const uint16_t *ve = reinterpret_cast<const uint16_t *>(&vv[i]);
+            for (int kb = 0; kb < CH / 32; ++kb)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) Vt[(p * 8 + e) * VSTR + kk] = ve[e];
+                for (int r = 0; r < 16; ++r) {
+                    const int j = kb * 32 + acc_row(r, hf);   // key within the chunk
+                    const float v = ((vis >> j) & 1ull) ? s[kb][r] * scale2 : -INFINITY;
+                    s[kb][r] = v;
+                    mx = fmaxf(mx, v);
                 }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mnew = fmaxf(mrun, mx);
+            float alpha;
+            if (mnew == -INFINITY) {
+                alpha = 1.f;
+            } else {
+                alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mnew);
             }
+            float ls = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < CH / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = (s[kb][r] == -INFINITY) ? 0.f : exp2f(s[kb][r] - mnew);
+                    s[kb][r] = p;
+                    ls += p;
+                }
+            ls += __shfl_xor(ls, 32);
+            lrun = lrun * alpha + ls;
+            mrun = mnew;
+#pragma unroll
+            for (int d = 0; d < NDB; ++d)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+
+            // O^T += V^T P^T over 16-key steps (kb, h): lane hf supplies keys
+            // kb*32 + 16h + {4hf..4hf+3, 8+4hf..8+4hf+3} = its accumulators r = 8h..8h+7
+#pragma unroll
+            for (int kb = 0; kb < CH / 32; ++kb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t hw[4], lw[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float p0 = s[kb][8 * h + 2 * e], p1 = s[kb][8 * h + 2 * e + 1];
+                        hw[e] = f2bf2(p0, p1);
+                        lw[e] = f2bf2(p0 - __uint_as_float(hw[e] << 16), p1 - __uint_as_float(hw[e] & 0xffff0000u));
+                    }
+                    const uint4 phi = {hw[0], hw[1], hw[2], hw[3]}, plo = {lw[0], lw[1], lw[2], lw[3]};
+                    const int k0 = kb * 32 + 16 * h + 4 * hf;
+#pragma unroll
+                    for (int d = 0; d < NDB; ++d) {
+                        const uint16_t *vr = Vl + (d * 32 + c) * VSTR;
+                        const uint2 v0 = *reinterpret_cast<const uint2 *>(vr + k0);
+                        const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + k0 + 8);
+                        const uint4 va = {v0.x, v0.y, v1.x, v1.y};
+                        o[d] = mfma32(va, phi, o[d]);
+                        o[d] = mfma32(va, plo, o[d]);
+                    }
+                }
         }
         __syncthreads();
-        if (wave * 32 >= R) continue;
-
-        // S^T for 2 blocks of 32 keys: lane (c, hf) holds rows=c, keys kb*32 + acc_row(r, hf)
-        f32x16 s[CH / 32];
-#pragma unroll
-        for (int kb = 0; kb < CH / 32; ++kb) {
-            s[kb] = (f32x16){};
-            const int key = kb * 32 + c;
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const uint4 ka = *reinterpret_cast<const uint4 *>(Ks + key * D + (((2 * kk + hf) ^ (key & (KC - 1))) << 3));
-                s[kb] = mfma32(ka, q[kk], s[kb]);
-            }
+        if (!loaders && ci + 1 < nch) {   // no loader waves: stage the next chunk in turn
+            stage(c0 + CH, buf ^ 1, tid, nthr);
+            __syncthreads();
         }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < CH / 32; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int j = kb * 32 + acc_row(r, hf);   // key within the chunk
-                bool vis = j < cn && rowok;
-                if (tree && vis) vis = (anc >> (c0 + j)) & 1u;
-                const float v = vis ? s[kb][r] * a.scale : -INFINITY;
-                s[kb][r] = v;
-                mx = fmaxf(mx, v);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrun, mx);
-        float alpha;
-        if (mnew == -INFINITY) {
-            alpha = 1.f;
-        } else {
-            alpha = (mrun == -INFINITY) ? 0.f : expf(mrun - mnew);
-        }
-        float ls = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < CH / 32; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = (s[kb][r] == -INFINITY) ? 0.f : expf(s[kb][r] - mnew);
-                s[kb][r] = p;
-                ls += p;
-            }
-        ls += __shfl_xor(ls, 32);
-        lrun = lrun * alpha + ls;
-        mrun = mnew;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-
-        // O^T += V^T P^T over 16-key steps (kb, h): lane hf supplies keys
-        // kb*32 + 16h + {4hf..4hf+3, 8+4hf..8+4hf+3} = its accumulators r = 8h..8h+7
-#pragma unroll
-        for (int kb = 0; kb < CH / 32; ++kb)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint32_t hw[4], lw[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p0 = s[kb][8 * h + 2 * e], p1 = s[kb][8 * h + 2 * e + 1];
-                    const uint16_t h0 = f2bf(p0), h1 = f2bf(p1);
-                    const uint16_t l0 = f2bf(p0 - bf2f(h0)), l1 = f2bf(p1 - bf2f(h1));
-                    hw[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                    lw[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-                }
-                const uint4 phi = {hw[0], hw[1], hw[2], hw[3]}, plo = {lw[0], lw[1], lw[2], lw[3]};
-                const int k0 = kb * 32 + 16 * h + 4 * hf;
-#pragma unroll
-                for (int d = 0; d < NDB; ++d) {
-                    const uint16_t *vr = Vt + (d * 32 + c) * VSTR;
-                    const uint2 v0 = *reinterpret_cast<const uint2 *>(vr + k0);
-                    const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + k0 + 8);
-                    const uint4 va = {v0.x, v0.y, v1.x, v1.y};
-                    o[d] = mfma32(va, phi, o[d]);
-                    o[d] = mfma32(va, plo, o[d]);
-                }
-            }
     }
 
     if (!rowok || hf > 1) return;
@@ -755,7 +784,8 @@ __global__ __launch_bounds__(D) void k_attn_combine(AttnArgs a, uint16_t *__rest
     __syncthreads();
     float M = -INFINITY;
     for (int s = 0; s < ns; ++s) M = fmaxf(M, ms[s]);
-    if (d < ns) ws[d] = (ms[d] == -INFINITY) ? 0.f : expf(ms[d] - M);
+    // split maxima are in base-2 units (scores times log2 e)
+    if (d < ns) ws[d] = (ms[d] == -INFINITY) ? 0.f : exp2f(ms[d] - M);
     __syncthreads();
     float L = 0.f, O = 0.f;
     for (int s0 = 0; s0 < ns; s0 += 8) {   // eight splits' loads in flight, adds in split order
@@ -1025,8 +1055,11 @@ hipError_t launch_rope_kv(hipStream_t s, const RopeArgs &a) {
 }
 
 hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a) {
-    const int rb = (a.G * a.n + 31) / 32;
-    const dim3 grid(a.ns, a.n_qhead / a.G), block(64 * rb);
+    const int rb = (a.G * a.n + 31) / 32;   // compute waves
+    if (rb > kAttnComputeWaves) return hipErrorInvalidValue;
+    // loader waves only when a split spans more than one chunk of keys
+    const int lw = a.span > kAttnChunk ? kAttnLoaderWaves : 0;
+    const dim3 grid(a.ns, a.n_qhead / a.G), block(64 * (rb + lw));
     if (D == 128) hipLaunchKernelGGL(k_attn<128>, grid, block, 0, s, a);
     else if (D == 64) hipLaunchKernelGGL(k_attn<64>, grid, block, 0, s, a);
     else return hipErrorInvalidValue;
