@@ -223,10 +223,11 @@ def main():
 
     def round_(n):
         per_req = trees[n]
-        if n_req == 1:
+        if n_req == 1:   # verify, accept walk and commit in one library call
             parents, tokens = per_req[0]
-            am, _ = tv.verify_tree(0, parents, tokens, logits=wl.logits)
-            ams = [am]
+            _, _, path, _ = tv.round(0, parents, tokens, logits=wl.logits)
+            tv.set_history(0, hist[0], ctxs[0])
+            return [len(path)]
         else:
             am, _ = tv.verify_trees(reqs, [p for p, _ in per_req], [t for _, t in per_req],
                                     logits=wl.logits)

@@ -18,7 +18,7 @@ _lib = None
 # every symbol include/treeverify.h declares
 SYMBOLS = ("tv_create", "tv_destroy", "tv_last_error", "tv_bind", "tv_set_history",
            "tv_set_modifiers", "tv_prefill", "tv_verify_tree", "tv_verify_trees",
-           "tv_accept_walk", "tv_commit", "tv_ctx_len", "tv_profile_enable",
+           "tv_accept_walk", "tv_commit", "tv_round", "tv_ctx_len", "tv_profile_enable",
            "tv_profile_reset", "tv_profile_get", "tv_linear", "tv_head_top2", "tv_pack_weight")
 
 
@@ -61,6 +61,7 @@ def load_library():
         "tv_verify_trees": ([P, I, P, P, P, P, P, P, P], I),
         "tv_accept_walk": ([P, P, P, I, P, P, P, P], I),
         "tv_commit": ([P, I, P, I], I),
+        "tv_round": ([P, I, P, P, I, P, P, P, P, P, P, P], I),
         "tv_ctx_len": ([P, I], I),
         "tv_profile_enable": ([P, I, ctypes.c_char_p], I),
         "tv_profile_reset": ([P], I),
@@ -131,6 +132,11 @@ class TreeVerifier:
         self._am = np.zeros(TV_MAX_NODES, np.int32)
         self._gap = np.zeros(TV_MAX_NODES, np.float32)
         self._am_ptr, self._gap_ptr = _ptr(self._am), _ptr(self._gap)
+        self._path = np.zeros(TV_MAX_NODES, np.int32)
+        self._emit = np.zeros(TV_MAX_NODES, np.int32)
+        self._lens = (ctypes.c_int32 * 2)()
+        self._path_ptr, self._emit_ptr = _ptr(self._path), _ptr(self._emit)
+        self._lens_ptr = ctypes.addressof(self._lens)
         h = ctypes.c_void_p()
         rc = self.lib.tv_create(ctypes.byref(d), ctypes.c_void_p(stream or 0), ctypes.byref(h))
         if rc != TV_OK:
@@ -234,6 +240,23 @@ class TreeVerifier:
         rc = self.lib.tv_commit(self.h, req, _ptr(p), int(p.size))
         if rc != TV_OK:
             self._check(rc, "tv_commit")
+
+    def round(self, req: int, parents, tokens, logits=None):
+        """tv_round: verify, accept walk and commit in one call ->
+        (argmax, gap, path, emitted)."""
+        p, t = _i32(parents), _i32(tokens)
+        n = int(p.size)
+        lp = None
+        if logits is not None:
+            if logits.numel() < n * self.vocab or not logits.is_contiguous():
+                raise ValueError("logits tensor too small or not contiguous")
+            lp = logits.data_ptr()
+        rc = self.lib.tv_round(self.h, req, _ptr(p), _ptr(t), n, lp, self._am_ptr, self._gap_ptr,
+                               self._path_ptr, self._lens_ptr, self._emit_ptr, self._lens_ptr + 4)
+        if rc != TV_OK:
+            self._check(rc, "tv_round")
+        return (self._am[:n].copy(), self._gap[:n].copy(), self._path[:self._lens[0]].tolist(),
+                self._emit[:self._lens[1]].tolist())
 
     def ctx_len(self, req: int) -> int:
         rc = self.lib.tv_ctx_len(self.h, req)

@@ -889,6 +889,18 @@ int tv_commit(tv_ctx *c, int req, const int32_t *path, int path_len) {
     return TV_OK;
 }
 
+int tv_round(tv_ctx *c, int req, const int32_t *parents, const int32_t *tokens, int n_nodes,
+             float *logits_dev, int32_t *argmax, float *gap_ulps, int32_t *path, int *path_len,
+             int32_t *emitted, int *n_emitted) {
+    if (!c) return TV_EINVAL;
+    if (!path || !path_len || !emitted || !n_emitted) return fail(c, TV_EINVAL, "null output");
+    int rc = tv_verify_tree(c, req, parents, tokens, n_nodes, logits_dev, argmax, gap_ulps);
+    if (rc) return rc;
+    rc = tv_accept_walk(parents, tokens, argmax, n_nodes, path, path_len, emitted, n_emitted);
+    if (rc) return fail(c, rc, "accept walk rejected the tree");
+    return tv_commit(c, req, path, *path_len);
+}
+
 int tv_prefill(tv_ctx *c, int req, const int32_t *tokens, int n, int32_t *argmax_last) {
     int rc = check_req(c, req);
     if (rc) return rc;

@@ -159,6 +159,16 @@ int tv_accept_walk(const int32_t *parents, const int32_t *tokens, const int32_t 
  * path_len; the path's tokens join the history. */
 int tv_commit(tv_ctx *ctx, int req, const int32_t *path, int path_len);
 
+/* One whole round for request `req` ("Drafters and tree verify", The round:
+ * verify, accept, commit): tv_verify_tree, then tv_accept_walk on its
+ * argmax, then tv_commit of the accepted path, in one call.  Arguments as
+ * for those calls; path and emitted are host arrays of at least n_nodes
+ * (argmax and gap_ulps too; gap_ulps may be NULL).  On a verify error nothing
+ * is committed; the results equal those of the three calls made in turn. */
+int tv_round(tv_ctx *ctx, int req, const int32_t *parents, const int32_t *tokens, int n_nodes,
+             float *logits_dev, int32_t *argmax, float *gap_ulps, int32_t *path, int *path_len,
+             int32_t *emitted, int *n_emitted);
+
 /* Committed context length of request `req` (negative TV_E* on error). */
 int tv_ctx_len(tv_ctx *ctx, int req);
 

@@ -241,6 +241,46 @@ def test_c0_rows_independent_of_pass(c0):
     assert torch.equal(alone, wl.logits[:16])
 
 
+def test_c0_round_equals_separate_calls(c0):
+    """tv_round (verify, accept walk, commit in one call) gives what the three
+    calls give in turn, bit for bit, and leaves the same cache and context
+    ("Drafters and tree verify", The round)."""
+    from greedy_draft_tree_amd import accept_walk
+    wl, orc = c0
+    prompt = synth.uniform_ids(40, synth.C0.vocab, 21)
+    for r in (0, 1):
+        wl.tv.set_history(r, [], 0)
+        wl.tv.prefill(r, prompt[:-1])
+    seq = orc.new_seq(cap=512)
+    seq.commit(prompt[:-1])
+    root = int(prompt[-1])
+    parents = synth.c0_tree()
+    rng = np.random.default_rng(5)
+    multi = 0
+    for k in range(6):
+        tokens = _greedy_drafter(orc, seq, root, parents, rng, k)
+        _say("round vs separate calls", k)
+        am0, gap0 = wl.tv.verify_tree(0, parents, tokens, logits=wl.logits)
+        l0 = wl.logits[:len(parents)].clone()
+        path0, em0 = accept_walk(parents, tokens, am0)
+        wl.tv.commit(0, path0)
+        am1, gap1, path1, em1 = wl.tv.round(1, parents, tokens, logits=wl.logits)
+        l1 = wl.logits[:len(parents)].clone()
+        np.testing.assert_array_equal(am0, am1)
+        np.testing.assert_array_equal(gap0.view(np.uint32), gap1.view(np.uint32))
+        assert path0 == path1 and em0 == em1
+        assert torch.equal(l0, l1)
+        seq.commit([int(tokens[i]) for i in path0])
+        root = em0[-1]
+        multi += len(path0) > 1
+    assert multi > 0
+    assert wl.tv.ctx_len(0) == wl.tv.ctx_len(1)
+    ctx = wl.tv.ctx_len(0)
+    torch.cuda.synchronize()
+    for key in wl.kv[0]:
+        assert torch.equal(wl.kv[0][key][:, :ctx], wl.kv[1][key][:, :ctx]), key
+
+
 def test_c0_errors_leave_state(c0):
     from greedy_draft_tree_amd import TVError, TV_EINVAL, TV_ECAPACITY, TV_ESTATE
     wl, _ = c0
