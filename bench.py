@@ -296,7 +296,7 @@ def main():
         kernels = {}
         for k in ("embed_norm", "resid_norm", "gemm_qkv", "rope_kv", "attn", "attn_combine", "gemm_o",
                   "gemm_gateup", "splitk_finish", "gemm_down", "gemm_gate", "recur_tree", "gemm_head",
-                  "top2", "signal", "commit_kv", "commit_state"):
+                  "top2", "commit_kv", "commit_state"):
             ms, cnt = tv.profile_get(k)
             if cnt:
                 kernels[k] = {"avg_us": round(ms / cnt * 1e3, 2), "launches": cnt}

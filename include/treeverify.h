@@ -9,7 +9,8 @@
  *                   every node (step 2, Verify);
  *   tv_accept_walk  the greedy walk down the tree (step 3, Accept);
  *   tv_commit       keep the KV rows and recurrent state of the accepted path
- *                   and drop the rest (step 4, Commit).
+ *                   and drop the rest (step 4, Commit);
+ *   tv_round        the three in one call.
  *
  * Conventions shared by every call:
  *   - Every call returns TV_OK (0) or a negative TV_E* code and never throws.
@@ -20,7 +21,9 @@
  *     it.  The library allocates its own small activation scratch in
  *     tv_create and frees it in tv_destroy.
  *   - All device work is enqueued on the stream given to tv_create.  A call
- *     that returns host results (argmax, gaps) synchronises that stream;
+ *     that returns host results (argmax, gaps) returns once its last kernel
+ *     has finished, so all work enqueued on the stream before it is complete
+ *     (the results reach pinned host memory directly from the GPU);
  *     tv_commit only enqueues (its effects are ordered before later work on
  *     the stream).
  *   - Token ids are int32 in [0, vocab).  A tree is given by parents[] and
