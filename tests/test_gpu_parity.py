@@ -309,7 +309,9 @@ def c1():
     return wl, orc
 
 
-@pytest.mark.parametrize("n,ctx", [(8, 1024), (16, 1024), (24, 1024), (32, 1024), (16, 8192)])
+# ctx 3000: attention splits of two 64-key chunks each (the second staged by
+# the loader waves) and a last split of 56 keys
+@pytest.mark.parametrize("n,ctx", [(8, 1024), (16, 1024), (24, 1024), (32, 1024), (16, 8192), (32, 3000)])
 def test_c1_tree_rows(c1, n, ctx):
     import workloads
     wl, orc = c1
