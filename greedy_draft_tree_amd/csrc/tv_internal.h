@@ -49,7 +49,9 @@ struct GemmArgs {
     const uint16_t *X;  // [M, K] bf16 activations, row stride ldx
     int ldx;
     const uint16_t *W;  // [N, K] bf16 weights
-    const uint16_t *W2; // [N, K] second weights (SwiGLU up)
+    const uint16_t *W2; // [N, K] second weights (SwiGLU up); for partials: rows N1.. (see N1)
+    int N1;             // partials only: rows [0, N1) come from W and [N1, N) from W2
+                        // (N1 a multiple of 32; 0 = all rows from W)
     int M, N, K;
     uint16_t *Y;        // bf16 out (or residual in/out), row stride ldy
     int ldy;
@@ -116,6 +118,7 @@ struct RecurArgs {
     uint16_t *save_k;     // [kMaxRows][QH][D] normalised keys of this layer (request-local node order)
     uint16_t *save_v;     // [kMaxRows][QH][D] values
     float *save_gc;       // [kMaxRows][QH] cumulative log-gates
+    int a_col;             // column of head 0's gate in a_part's layout
     int row0, n, QH;
     float eps;
 };

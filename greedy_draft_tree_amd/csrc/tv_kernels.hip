@@ -311,7 +311,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     const int nsteps = (K + 63) >> 6;
     const int S = gridDim.y, ks = blockIdx.y;
     const int s0 = (nsteps * ks) / S, s1 = (nsteps * (ks + 1)) / S;
-    const uint16_t *tb = g.W + (size_t)(tok ? tile : 0) * 32 * K;
+    // partials of two stacked matrices: tiles from N1/32 on read W2
+    const int t1 = (EPI == EPI_PARTIAL && g.N1 > 0) ? (g.N1 >> 5) : ntiles;
+    const uint16_t *tb = tile < t1 ? g.W + (size_t)(tok ? tile : 0) * 32 * K
+                                   : g.W2 + (size_t)(tile - t1) * 32 * K;
     const uint16_t *tb2 = DUAL ? g.W2 + (size_t)(tok ? tile : 0) * 32 * K : nullptr;
     const uint4 z = {0u, 0u, 0u, 0u};
 
@@ -866,7 +869,7 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
         const int t = idx / VW, c = idx % VW;
         vsm[t][c] = bfround(psum(r.qkv_part, r.qkv_S, 1, 0, r.row0 + t, (2 * QH + h) * D + v0 + c));
     }
-    if (tid < n) gsh[tid] = log_sigmoid(bfround(psum(r.a_part, r.a_S, 1, 0, r.row0 + tid, h)));
+    if (tid < n) gsh[tid] = log_sigmoid(bfround(psum(r.a_part, r.a_S, 1, 0, r.row0 + tid, r.a_col + h)));
     __syncthreads();
     // L2 norms of q and k rows: one wave per vector, shuffle reduction
     for (int vec = wave; vec < 2 * n; vec += 4) {

@@ -469,27 +469,19 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
             }
         } else {
             const int rl = c->recur_index[l];
-            // q/k/v and gate projections leave split-K partials (the gate's
-            // after the qkv ones); the read-out kernel finishes both
+            // one projection over the q/k/v rows stacked on the gate rows
+            // leaves split-K partials; the read-out kernel finishes them
             GemmArgs g{};
             NORMED(g, c->attn_norm[l]);
-            g.W = c->wqkv[l]; g.M = M; g.N = 3 * QH * D; g.K = H;
+            g.W = c->wqkv[l]; g.W2 = c->wa[l]; g.N1 = 3 * QH * D;
+            g.M = M; g.N = 3 * QH * D + QH; g.K = H;
             int Sq = 0;
             GEMMP(c, "gemm_qkv", g, Sq);
-            const size_t a_off = gemm_partial_need(g.N, g.K, false, true);
-            GemmArgs ga{};
-            NORMED(ga, c->attn_norm[l]);
-            ga.W = c->wa[l]; ga.M = M; ga.N = QH; ga.K = H;
-            int Sa = 0;
-            {
-                const int rc_ = gemm_partial(c, "gemm_gate", ga, &Sa, a_off);
-                if (rc_) return rc_;
-            }
             for (int r = 0; r < n_req; ++r) {
                 Req &q = c->reqs[reqs[r]];
                 RecurArgs ra{};
                 ra.qkv_part = c->gemm_partial; ra.qkv_S = Sq;
-                ra.a_part = c->gemm_partial + a_off; ra.a_S = Sa;
+                ra.a_part = c->gemm_partial; ra.a_S = Sq; ra.a_col = 3 * QH * D;
                 ra.S0 = q.S[l]; ra.meta = c->d_meta; ra.out = c->ATT;
                 const size_t per = (size_t)kMaxRows * QH * D;
                 ra.save_k = q.save_k + rl * per;
@@ -630,8 +622,7 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
         const int QD = m.n_qhead * D;
         size_t need = (size_t)8 << 20;  // room for kernel-level calls
         need = std::max(need, gemm_partial_need((m.n_qhead + 2 * m.n_kvhead) * D, H, false, true));
-        // a recurrent layer keeps its qkv and gate partials side by side
-        need = std::max(need, gemm_partial_need(3 * QD, H, false, true) + gemm_partial_need(m.n_qhead, H, false, true));
+        need = std::max(need, gemm_partial_need(3 * QD + m.n_qhead, H, false, true));   // recurrent qkv + gate
         need = std::max(need, gemm_partial_need(H, QD, false, true));
         need = std::max(need, gemm_partial_need(m.ffn, H, true));
         need = std::max(need, gemm_partial_need(H, m.ffn, false, true));
