@@ -208,13 +208,17 @@ __global__ __launch_bounds__(kRowThreads) void k_row_norm(const uint16_t *__rest
 //
 // A workgroup of 4 waves owns 4 consecutive tiles (128 rows) and one of S
 // k-ranges; the activations of each step (32 x 64 bf16, zero beyond M) are
-// staged once in LDS (XOR-swizzled 16-byte chunks, conflict-free reads) and
-// shared by the 4 waves as the B operand (column = lane%32).  With S > 1 each
-// workgroup writes its fp32 partial tile and k_splitk_reduce adds the S
-// partials in k-range order and applies the epilogue.
-// S depends on the weight shape only, and the k order of every output is
-// fixed by K: M only decides which B columns are zero, so a row's result is
-// the same for any row count and any row slot.
+// staged once in LDS by direct global-to-LDS loads (XOR-swizzled 16-byte
+// chunks, conflict-free reads) and shared by the 4 waves as the B operand
+// (column = lane%32).  With S > 1 (or for partial-only launches) each
+// workgroup writes its fp32 partial tile; a consumer (k_splitk_reduce, the
+// RoPE kernel, the row-norm kernel or the recurrent read-out) adds the S
+// partials in k-range order.  S is the most splits that keep the grid within
+// 512 workgroups, a function of the weight shape only, and the k order of
+// every output is fixed by K: M only decides which B columns are zero, so a
+// row's result is the same for any row count and any row slot.  A partial
+// launch may read two stacked matrices (rows [0, N1) from W, the rest from
+// W2), which lets one launch serve the recurrent layer's q/k/v and gate.
 
 // Element offset, inside a packed tile, of the 8-element piece (q, hf) of
 // row c at step s; -1 when the piece lies beyond K or the row beyond N.
@@ -579,9 +583,13 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
 // registers: the k slots of each 16-key step are permuted to the keys the
 // lane already holds, and V^T is staged in LDS with the same order.  P is
 // split into bf16 high and low parts (two MFMAs) so P.V keeps ~16 bits of P.
-// Each workgroup writes its unnormalised partial (max, sum, output); the
-// combine kernel merges splits in index order.  Split boundaries depend
-// only on ctx, so a row's result does not depend on the other rows.
+// The softmax runs in base 2 (scores times scale * log2 e, exp2).  When a
+// split spans several 64-key chunks, two extra loader waves stage the next
+// chunk into the second LDS buffer while the compute waves use the first.
+// Each workgroup writes its unnormalised partial (max in base-2 units, sum,
+// output); the combine kernel merges splits in index order.  Split
+// boundaries depend only on ctx, so a row's result does not depend on the
+// other rows.
 
 template <int D>
 __global__ __launch_bounds__(64 * (kAttnComputeWaves + kAttnLoaderWaves)) void k_attn(AttnArgs a) {
