@@ -26,6 +26,11 @@ What it computes, and where the pages define it:
   and the top-1/top-2 gap in bf16 ulps ("Exactness", The one exception).
 * ``accept_walk``: the greedy accept walk with the bonus token ("Drafters and
   tree verify", The round, step 3).
+* ``sample_keys`` / ``sampled_tree_decisions`` / ``sampled``: the sampled
+  request.  The token at sequence index t is the argmax of the modified
+  scores divided by the temperature plus Gumbel noise keyed by (seed, t)
+  ("Exactness", Sampling; "Drafters and tree verify", Sampling); the noise
+  comes from Philox4x32-10, written from its published definition.
 * ``Seq.commit``: the oracle's committed state is its token sequence; a
   commit simply steps the accepted tokens one at a time ("Drafters and tree
   verify", The round, step 4).  The closed form of the recurrent state
@@ -452,6 +457,130 @@ def greedy(seq: Seq, first: int, k: int, mods: Optional[Modifiers] = None):
     for i in range(k):
         logits = seq.step(t)
         a, _, _, g = top2(apply_modifiers(logits, seq.history, mods))
+        out.append(a)
+        gaps.append(g)
+        t = a
+    return out, gaps
+
+
+# ------------------------------------------------------------ sampling
+#
+# A sampled request (temperature T > 0) draws the token at sequence index t
+# as the argmax of log p_t + G_t, where p_t is the distribution of the
+# modified scores divided by T and G_t a vector of standard Gumbel noise
+# from a generator keyed by (seed, t) ("Exactness", Sampling; "Drafters and
+# tree verify", Sampling).  log p_t differs from scores/T by one constant
+# per row, so the argmax is taken over fp32(fp32(scores / T) + G) directly.
+#
+# Sequence indices count from 0 at the first prompt token: a verify row
+# whose node sits at position ctx_len + depth scores the token at index
+# ctx_len + depth + 1, and plain decoding that has consumed c tokens draws
+# index c.
+#
+# The generator is Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel
+# random numbers: as easy as 1, 2, 3", SC 2011): a 128-bit counter, a
+# 64-bit key, ten rounds.  Vocabulary id v takes word v % 4 of the block at
+# counter (v // 4, t, 0, 0) under key (seed low word, seed high word); the
+# word x becomes u = (x + 1/2) / 2^32, strictly inside (0, 1), and
+# G = -log(-log u) is evaluated in fp64 and rounded to fp32.
+
+_PH_M0, _PH_M1 = 0xD2511F53, 0xCD9E8D57    # round multipliers
+_PH_W0, _PH_W1 = 0x9E3779B9, 0xBB67AE85    # key schedule increments
+_U32 = 0xFFFFFFFF
+
+
+class Sampling:
+    """Temperature and 64-bit seed of one sampled request (T > 0)."""
+
+    def __init__(self, temperature: float, seed: int):
+        if not (temperature > 0 and math.isfinite(temperature)):
+            raise ValueError("temperature must be positive and finite")
+        self.temperature = float(temperature)
+        self.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+
+
+def philox4x32_10(ctr: Sequence[int], key: Sequence[int]) -> List[int]:
+    """One Philox4x32-10 block, scalar: four 32-bit words of counter, two of
+    key.  Each round multiplies words 0 and 2 by the two round constants,
+    crosses the high halves of the products with words 1 and 3 and the key,
+    and keeps the low halves; the key then advances by the Weyl increments."""
+    c = [int(w) & _U32 for w in ctr]
+    k0, k1 = int(key[0]) & _U32, int(key[1]) & _U32
+    for _ in range(10):
+        p0 = _PH_M0 * c[0]
+        p1 = _PH_M1 * c[2]
+        c = [((p1 >> 32) ^ c[1] ^ k0) & _U32, p1 & _U32,
+             ((p0 >> 32) ^ c[3] ^ k1) & _U32, p0 & _U32]
+        k0, k1 = (k0 + _PH_W0) & _U32, (k1 + _PH_W1) & _U32
+    return c
+
+
+def philox_words(seed: int, t: int, n: int) -> np.ndarray:
+    """Words 0..n-1 of the stream (seed, t): word v is word v % 4 of the
+    block at counter (v // 4, t, 0, 0).  The same rounds as philox4x32_10,
+    one numpy lane per block."""
+    nb = (n + 3) // 4
+    c0 = np.arange(nb, dtype=np.uint64)
+    c1 = np.full(nb, int(t) & _U32, dtype=np.uint64)
+    c2 = np.zeros(nb, dtype=np.uint64)
+    c3 = np.zeros(nb, dtype=np.uint64)
+    k0, k1 = int(seed) & _U32, (int(seed) >> 32) & _U32
+    m = np.uint64(_U32)
+    for _ in range(10):
+        p0 = np.uint64(_PH_M0) * c0
+        p1 = np.uint64(_PH_M1) * c2
+        c0, c1, c2, c3 = ((p1 >> np.uint64(32)) ^ c1 ^ np.uint64(k0)) & m, p1 & m, \
+                         ((p0 >> np.uint64(32)) ^ c3 ^ np.uint64(k1)) & m, p0 & m
+        k0, k1 = (k0 + _PH_W0) & _U32, (k1 + _PH_W1) & _U32
+    return np.stack([c0, c1, c2, c3], axis=1).reshape(-1)[:n].astype(np.uint32)
+
+
+def gumbel(seed: int, t: int, n: int) -> np.ndarray:
+    """fp32 standard Gumbel noise G_t of the stream (seed, t), n values."""
+    u = (philox_words(seed, t, n).astype(np.float64) + 0.5) * 2.0 ** -32
+    return (-np.log(-np.log(u))).astype(np.float32)
+
+
+def sample_keys(scores: np.ndarray, smp: Sampling, t: int) -> np.ndarray:
+    """fp32 keys fp32(fp32(scores / T) + G_t) of one row; their argmax
+    (lowest id on an exact tie) is the draw.  -inf scores stay -inf."""
+    s = np.asarray(scores, dtype=np.float32)
+    return (s / np.float32(smp.temperature) + gumbel(smp.seed, t, s.shape[0])).astype(np.float32)
+
+
+def node_depths(parents: Sequence[int]) -> List[int]:
+    d = [0] * len(parents)
+    for i in range(1, len(parents)):
+        d[i] = d[int(parents[i])] + 1
+    return d
+
+
+def sampled_tree_decisions(logits: np.ndarray, parents, tokens, history: Sequence[int], ctx_len: int,
+                           smp: Sampling, mods: Optional[Modifiers] = None):
+    """Per-row (draw, gap) of a sampled request: row i draws the token at
+    index ctx_len + depth(i) + 1 from its modified scores.  The gap is the
+    top-1/top-2 key difference in bf16 ulps of the top key."""
+    n = len(parents)
+    dep = node_depths(parents)
+    am = np.zeros(n, dtype=np.int32)
+    gap = np.zeros(n)
+    for i in range(n):
+        prior = list(history) + path_tokens(parents, tokens, i)
+        keys = sample_keys(apply_modifiers(logits[i], prior, mods), smp, ctx_len + dep[i] + 1)
+        a, _, _, g = top2(keys)
+        am[i], gap[i] = a, g
+    return am, gap
+
+
+def sampled(seq: Seq, first: int, k: int, smp: Sampling, mods: Optional[Modifiers] = None):
+    """Plain sampled decoding: feed ``first``, then k-1 drawn tokens; the
+    draw after c consumed tokens is index c.  Returns (tokens [k], gaps)."""
+    out, gaps = [], []
+    t = first
+    for _ in range(k):
+        logits = seq.step(t)
+        keys = sample_keys(apply_modifiers(logits, seq.history, mods), smp, seq.ctx_len)
+        a, _, _, g = top2(keys)
         out.append(a)
         gaps.append(g)
         t = a
