@@ -17,7 +17,7 @@ _lib = None
 
 # every symbol include/treeverify.h declares
 SYMBOLS = ("tv_create", "tv_destroy", "tv_last_error", "tv_bind", "tv_set_history",
-           "tv_set_modifiers", "tv_prefill", "tv_verify_tree", "tv_verify_trees",
+           "tv_set_modifiers", "tv_set_sampling", "tv_prefill", "tv_verify_tree", "tv_verify_trees",
            "tv_accept_walk", "tv_commit", "tv_round", "tv_ctx_len", "tv_profile_enable",
            "tv_profile_reset", "tv_profile_get", "tv_linear", "tv_head_top2", "tv_pack_weight")
 
@@ -56,6 +56,7 @@ def load_library():
         "tv_bind": ([P, ctypes.c_char_p, P, S], I),
         "tv_set_history": ([P, I, P, I, I], I),
         "tv_set_modifiers": ([P, I, F, P, P, I, P], I),
+        "tv_set_sampling": ([P, I, F, ctypes.c_uint64], I),
         "tv_prefill": ([P, I, P, I, P], I),
         "tv_verify_tree": ([P, I, P, P, I, P, P, P], I),
         "tv_verify_trees": ([P, I, P, P, P, P, P, P, P], I),
@@ -190,6 +191,11 @@ class TreeVerifier:
             self.h, req, float(rep_penalty), _ptr(ids) if ids.size else None,
             _ptr(vals) if vals.size else None, int(ids.size),
             _ptr(bits) if bits is not None else None), "tv_set_modifiers")
+
+    def set_sampling(self, req: int, temperature: float, seed: int = 0) -> None:
+        """tv_set_sampling: temperature 0 is greedy."""
+        self._check(self.lib.tv_set_sampling(self.h, req, float(temperature),
+                                             int(seed) & 0xFFFFFFFFFFFFFFFF), "tv_set_sampling")
 
     def prefill(self, req: int, tokens: Sequence[int]) -> int:
         t = _i32(tokens)

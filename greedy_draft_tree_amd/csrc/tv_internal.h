@@ -28,7 +28,8 @@ struct HeadMods {
     const float *bias;          // [V] dense logit_bias (0 where none)
     const uint32_t *allow_bits; // [ceil(V/32)] allowed ids
     float rep;                  // repetition penalty (1 = off)
-    int pad[3];
+    float temp;                 // sampling temperature (0 = greedy)
+    uint32_t seed_lo, seed_hi;  // sampling seed: the Philox key
 };
 
 // Per-pass metadata, copied to the device once per verify.
@@ -39,6 +40,7 @@ struct PassMeta {
     int row_req[kMaxRows];       // request slot of each row
     int path_len[kMaxRows];      // tokens on root..row
     int path_tok[kMaxRows * kMaxRows];
+    int draw_t[kMaxRows];        // sequence index of the token each row draws
     HeadMods mods[kMaxRows];     // per request slot
 };
 
@@ -58,8 +60,8 @@ struct GemmArgs {
     float *Yf;          // fp32 out (head), row stride ldyf
     int ldyf;
     Top2 *part;         // head: [ceil(N/32)][32] per-tile candidates
-    const PassMeta *meta; // head modifiers (null: none)
-    int mods_on;
+    const PassMeta *meta; // head modifiers and sampling (null: none)
+    int mods_on;          // some request of the pass has modifiers or samples
     float *partial;     // split-K partial tiles (splits > 1)
     const void *zeros;  // >= 16 zero bytes (activation staging beyond M or K)
 };

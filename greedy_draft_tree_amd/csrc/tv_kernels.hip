@@ -62,21 +62,99 @@ __device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
     return a > b || (a == b && ia < ib);
 }
 
+// Both written as selects: with branches the compiler keeps (v1, i1, v2,
+// i2) in a private array and updates it by a computed index (scratch memory).
 __device__ __forceinline__ void top2_insert(float &v1, int &i1, float &v2, int &i2, float s, int id) {
-    if (better(s, id, v1, i1)) {
-        v2 = v1; i2 = i1; v1 = s; i1 = id;
-    } else if (better(s, id, v2, i2)) {
-        v2 = s; i2 = id;
-    }
+    const bool b1 = better(s, id, v1, i1), b2 = better(s, id, v2, i2);
+    const float n2 = b1 ? v1 : (b2 ? s : v2);
+    const int m2 = b1 ? i1 : (b2 ? id : i2);
+    v1 = b1 ? s : v1;
+    i1 = b1 ? id : i1;
+    v2 = n2;
+    i2 = m2;
 }
 
 __device__ __forceinline__ void top2_merge(float &v1, int &i1, float &v2, int &i2, float w1, int j1,
                                            float w2, int j2) {
-    if (better(w1, j1, v1, i1)) {
-        if (better(v1, i1, w2, j2)) { v2 = v1; i2 = i1; } else { v2 = w2; i2 = j2; }
-        v1 = w1; i1 = j1;
-    } else if (better(w1, j1, v2, i2)) {
-        v2 = w1; i2 = j1;
+    const bool a1 = better(w1, j1, v1, i1);
+    // a1: the new runner-up is the better of (v1, w2); else the better of (w1, v2)
+    const bool x = a1 ? better(v1, i1, w2, j2) : better(w1, j1, v2, i2);
+    const float n2 = a1 ? (x ? v1 : w2) : (x ? w1 : v2);
+    const int m2 = a1 ? (x ? i1 : j2) : (x ? j1 : i2);
+    v1 = a1 ? w1 : v1;
+    i1 = a1 ? j1 : i1;
+    v2 = n2;
+    i2 = m2;
+}
+
+// ------------------------------------------------------------ sampling
+// A sampled row draws the argmax of fp32(fp32(score / T) + G), G standard
+// Gumbel noise keyed by (seed, t), t the sequence index of the drawn token:
+// the Gumbel-max trick ("Exactness", Sampling; "Drafters and tree verify",
+// Sampling).  The noise generator is Philox4x32-10 (Salmon, Moraes, Dror and
+// Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011): vocabulary
+// id v takes word v % 4 of the block at counter (v / 4, t, 0, 0) under key
+// (seed low word, seed high word), so an aligned quad of ids is one block.
+
+struct U32x4 {
+    uint32_t w[4];
+};
+
+__device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;   // round multipliers of the definition
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c0 = n0;
+        c1 = (uint32_t)p1;
+        c2 = n2;
+        c3 = (uint32_t)p0;
+        k0 += 0x9E3779B9u;   // key schedule increments of the definition
+        k1 += 0xBB67AE85u;
+    }
+    return U32x4{{c0, c1, c2, c3}};
+}
+
+// G = -log(-log(u)) with u = (x + 1/2) / 2^32, exact in fp64 and strictly
+// inside (0, 1); the logs run in fp64 and G is rounded once to fp32.
+__device__ __forceinline__ float gumbel_of(uint32_t x) {
+    const double u = ((double)x + 0.5) * 0x1p-32;
+    return (float)(-log(-log(u)));
+}
+
+// Modified score of the aligned quad n0..n0+3 (n0 < N) of row m, in place:
+// repetition penalty over the prior tokens (history bits, and `pathq`, the
+// row's path tokens among the quad in its low 4 bits), logit_bias, the
+// allow-mask, then for a sampled request score / T + G.
+__device__ __forceinline__ void score_quad(const PassMeta *meta, int m, int n0, int N, uint32_t pathq,
+                                           float s[4]) {
+    const HeadMods &md = meta->mods[meta->row_req[m]];
+    const int w = n0 >> 5, b = n0 & 31;   // the quad lies inside vocabulary word w
+    if (md.rep != 1.0f) {
+        const uint32_t prior = ((md.hist_bits ? md.hist_bits[w] : 0u) >> b) | pathq;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if ((prior >> j) & 1u) s[j] = s[j] > 0.f ? s[j] / md.rep : s[j] * md.rep;
+    }
+    if (md.bias) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (n0 + j < N) s[j] = s[j] + md.bias[n0 + j];
+    }
+    if (md.allow_bits) {
+        const uint32_t allow = md.allow_bits[w] >> b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (!((allow >> j) & 1u)) s[j] = -INFINITY;
+    }
+    if (md.temp > 0.f) {
+        const U32x4 x = philox4x32_10((uint32_t)(n0 >> 2), (uint32_t)meta->draw_t[m], 0u, 0u, md.seed_lo,
+                                      md.seed_hi);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[j] = s[j] / md.temp + gumbel_of(x.w[j]);
     }
 }
 
@@ -233,67 +311,26 @@ __device__ __forceinline__ long packed_piece(int s, int q, int hf, int c, int nr
     return (long)64 * s * nr + (long)rank * nr * 8 + c * 8;
 }
 
-// Epilogue of one 32x32 output tile held in MFMA accumulator layout.
-// For the head, each column's top-2 over the tile goes to top_out[column].
+// Epilogue of one 32x32 output tile held in MFMA accumulator layout (all
+// epilogues but the head's).
 template <int EPI>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, int tile, int lane, const f32x16 &acc,
-                                              const f32x16 &acc2, Top2 *top_out) {
+                                              const f32x16 &acc2) {
     const int hf = lane >> 5, c = lane & 31;
     const int m = c, N = g.N;
-    const bool cok = c < g.M;
-    if constexpr (EPI == EPI_HEAD) {
-        float v1 = -INFINITY, v2 = -INFINITY;
-        int i1 = 0x7fffffff, i2 = 0x7fffffff;
-        const bool mods = g.mods_on && cok;
-        const HeadMods *md = mods ? &g.meta->mods[g.meta->row_req[m]] : nullptr;
-        // modifiers over this tile's 32 columns as bit masks: word `tile` of
-        // the vocabulary bitsets covers exactly columns tile*32 .. +31
-        uint32_t prior = 0u, allow = 0xffffffffu;
-        float rep = 1.0f;
-        if (mods) {
-            rep = md->rep;
-            if (rep != 1.0f) {
-                if (md->hist_bits) prior = md->hist_bits[tile];
-                const int L = g.meta->path_len[m];
-                const int *pt = g.meta->path_tok + m * kMaxRows;
-                for (int j = 0; j < L; ++j) {
-                    const unsigned col = (unsigned)(pt[j] - tile * 32);
-                    if (col < 32u) prior |= 1u << col;
-                }
-            }
-            if (md->allow_bits) allow = md->allow_bits[tile];
-        }
+    if (c >= g.M) return;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int col = acc_row(r, hf), n = tile * 32 + col;
-            if (!cok || n >= N) continue;
-            float s = acc[r];
-            if (mods) {
-                if ((prior >> col) & 1u) s = s > 0.f ? s / rep : s * rep;
-                if (md->bias) s = s + md->bias[n];
-                if (!((allow >> col) & 1u)) s = -INFINITY;
-            }
-            top2_insert(v1, i1, v2, i2, s, n);
-        }
-        const float w1 = __shfl_xor(v1, 32), w2 = __shfl_xor(v2, 32);
-        const int j1 = __shfl_xor(i1, 32), j2 = __shfl_xor(i2, 32);
-        top2_merge(v1, i1, v2, i2, w1, j1, w2, j2);
-        if (hf == 0) top_out[m] = Top2{v1, i1, v2, i2};
-    } else {
-        if (!cok) return;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int n = tile * 32 + acc_row(r, hf);
-            if (n >= N) continue;
-            uint16_t *y = g.Y + (size_t)m * g.ldy + n;
-            if constexpr (EPI == EPI_BF16) {
-                *y = f2bf(acc[r]);
-            } else if constexpr (EPI == EPI_RESID) {
-                *y = f2bf(bf2f(*y) + bfround(acc[r]));
-            } else {
-                const float gt = bfround(acc[r]), up = bfround(acc2[r]);
-                *y = f2bf(gt / (1.0f + expf(-gt)) * up);
-            }
+    for (int r = 0; r < 16; ++r) {
+        const int n = tile * 32 + acc_row(r, hf);
+        if (n >= N) continue;
+        uint16_t *y = g.Y + (size_t)m * g.ldy + n;
+        if constexpr (EPI == EPI_BF16) {
+            *y = f2bf(acc[r]);
+        } else if constexpr (EPI == EPI_RESID) {
+            *y = f2bf(bf2f(*y) + bfround(acc[r]));
+        } else {
+            const float gt = bfround(acc[r]), up = bfround(acc2[r]);
+            *y = f2bf(gt / (1.0f + expf(-gt)) * up);
         }
     }
 }
@@ -304,6 +341,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     constexpr int U = DUAL ? 2 : 4;      // k steps per LDS stage
     constexpr int NACC = DUAL ? 2 : 1;
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][U][32 * 64];
+    __shared__ uint32_t pbits[EPI == EPI_HEAD ? kMaxRows * 4 : 1];   // head: path tokens per row
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hf = lane >> 5, c = lane & 31;
@@ -344,6 +382,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     };
 
     f32x16 acc = {}, acc2 = {};
+    if (EPI == EPI_HEAD && tid < kMaxRows * 4) pbits[tid] = 0u;
     if (s0 < s1) bissue(0, s0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -398,7 +437,22 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
         float *lt = reinterpret_cast<float *>(&Bs[0][0][0]);   // [32 rows][128]
 #pragma unroll
         for (int r = 0; r < 16; ++r) lt[c * 128 + wave * 32 + acc_row(r, hf)] = acc[r];
+        if (g.mods_on) {
+            // each row's path tokens among this workgroup's 128 columns, for
+            // the repetition penalty (pbits was cleared before the k loop)
+            for (int i = tid; i < g.M * kMaxRows; i += 256) {
+                const int mm = i / kMaxRows, j = i % kMaxRows;
+                if (j < g.meta->path_len[mm]) {
+                    const unsigned col = (unsigned)(g.meta->path_tok[mm * kMaxRows + j] - (int)blockIdx.x * 128);
+                    if (col < 128u) atomicOr(&pbits[mm * 4 + (col >> 5)], 1u << (col & 31));
+                }
+            }
+        }
         __syncthreads();
+        // one aligned quad of columns per thread and step: store the logits,
+        // score them, and reduce row mm's top-2 over the 32 lanes (half a
+        // wave) that hold its 128 columns; the lowest lane writes the
+        // workgroup's candidates part[mm * rowblocks + rowblock]
         for (int idx = tid; idx < g.M * 32; idx += 256) {
             const int mm = idx >> 5, q4 = idx & 31;
             const int n0 = blockIdx.x * 128 + q4 * 4;
@@ -413,25 +467,24 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
                 if (n0 + 2 < N) dst[2] = v.z;
                 if (n0 + 3 < N) dst[3] = v.w;
             }
-        }
-        // each wave's per-column top-2 goes through LDS; wave 0 merges the
-        // workgroup's 4 tiles (a selection: order-free) and stores row-major
-        // candidates part[m * rowblocks + rowblock]
-        __shared__ Top2 wt[4][32];
-        Top2 mine = {-INFINITY, 0x7fffffff, -INFINITY, 0x7fffffff};
-        if (tok) {
-            gemm_epilogue<EPI>(g, tile, lane, acc, acc2, wt[wave]);
-        } else if (hf == 0) {
-            wt[wave][c] = mine;
-        }
-        __syncthreads();
-        if (wave == 0 && hf == 0 && c < g.M) {
-            Top2 r = wt[0][c];
-            for (int w = 1; w < 4; ++w) top2_merge(r.v1, r.i1, r.v2, r.i2, wt[w][c].v1, wt[w][c].i1, wt[w][c].v2, wt[w][c].i2);
-            g.part[(size_t)c * gridDim.x + blockIdx.x] = r;
+            float sc[4] = {v.x, v.y, v.z, v.w};
+            if (g.mods_on && n0 < N)
+                score_quad(g.meta, mm, n0, N, (pbits[mm * 4 + (q4 >> 3)] >> ((q4 & 7) * 4)) & 15u, sc);
+            float v1 = -INFINITY, v2 = -INFINITY;
+            int i1 = 0x7fffffff, i2 = 0x7fffffff;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (n0 + j < N) top2_insert(v1, i1, v2, i2, sc[j], n0 + j);
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) {
+                const float w1 = __shfl_xor(v1, o), w2 = __shfl_xor(v2, o);
+                const int j1 = __shfl_xor(i1, o), j2 = __shfl_xor(i2, o);
+                top2_merge(v1, i1, v2, i2, w1, j1, w2, j2);
+            }
+            if (q4 == 0) g.part[(size_t)mm * gridDim.x + blockIdx.x] = Top2{v1, i1, v2, i2};
         }
     } else {
-        if (tok) gemm_epilogue<EPI>(g, tile, lane, acc, acc2, nullptr);
+        if (tok) gemm_epilogue<EPI>(g, tile, lane, acc, acc2);
     }
 }
 

@@ -32,6 +32,9 @@ struct Req {
     float *d_bias = nullptr;
     uint32_t *d_allow = nullptr;
     bool has_bias = false, has_allow = false;
+    // sampling (temp 0: greedy)
+    float temp = 0.f;
+    uint64_t seed = 0;
     // pending tree of the last verify
     bool pending = false;
     std::vector<int32_t> pparents, ptokens;
@@ -402,6 +405,7 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
             pm.depth[g] = p < 0 ? 0 : pm.depth[row0 + p] + 1;
             pm.anc[g] = (p < 0 ? 0u : pm.anc[row0 + p]) | (1u << i);
             pm.row_req[g] = r;
+            pm.draw_t[g] = q.ctx_len + pm.depth[g] + 1;
             // tokens on root..i
             int L = 0, stack[TV_MAX_NODES];
             for (int j = i; j >= 0; j = parents[r][j]) stack[L++] = tokens[r][j];
@@ -414,7 +418,10 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
         hm.bias = (q.mods_on && q.has_bias) ? q.d_bias : nullptr;
         hm.allow_bits = (q.mods_on && q.has_allow) ? q.d_allow : nullptr;
         if (!q.mods_on) hm.rep = 1.f;
-        any_mods |= q.mods_on;
+        hm.temp = q.temp;
+        hm.seed_lo = (uint32_t)q.seed;
+        hm.seed_hi = (uint32_t)(q.seed >> 32);
+        any_mods |= q.mods_on || q.temp > 0.f;
         row0 += n;
     }
     const int M = total;
@@ -796,6 +803,17 @@ int tv_set_modifiers(tv_ctx *c, int req, float rep, const int32_t *bias_ids, con
     q.has_bias = n_bias > 0;
     q.has_allow = allow_bits != nullptr;
     q.mods_on = rep != 1.f || q.has_bias || q.has_allow;
+    return TV_OK;
+}
+
+int tv_set_sampling(tv_ctx *c, int req, float temperature, uint64_t seed) {
+    int rc = check_req(c, req);
+    if (rc) return rc;
+    if (!(temperature >= 0.f) || !std::isfinite(temperature))
+        return fail(c, TV_EINVAL, "temperature must be finite and >= 0");
+    Req &q = c->reqs[req];
+    q.temp = temperature;
+    q.seed = seed;
     return TV_OK;
 }
 

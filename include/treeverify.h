@@ -7,7 +7,9 @@
  *                   nodes against the request's KV cache and recurrent state;
  *                   fp32 logits, the argmax token and the top-1/top-2 gap at
  *                   every node (step 2, Verify);
- *   tv_accept_walk  the greedy walk down the tree (step 3, Accept);
+ *   tv_accept_walk  the walk down the tree (step 3, Accept), over the argmax
+ *                   of greedy rows or the draw of sampled ones
+ *                   (tv_set_sampling);
  *   tv_commit       keep the KV rows and recurrent state of the accepted path
  *                   and drop the rest (step 4, Commit);
  *   tv_round        the three in one call.
@@ -120,6 +122,24 @@ int tv_set_history(tv_ctx *ctx, int req, const int32_t *ids, int n_ids, int ctx_
  * use the modified scores. */
 int tv_set_modifiers(tv_ctx *ctx, int req, float rep_penalty, const int32_t *bias_ids,
                      const float *bias_vals, int n_bias, const uint32_t *allow_bits);
+
+/* Make request `req` a sampled request ("Exactness", Sampling; "Drafters and
+ * tree verify", Sampling), or greedy again with temperature == 0 (the state
+ * at tv_create).  A sampled row's "argmax" is then the target's own draw: the
+ * argmax of fp32(fp32(score / temperature) + G), score the row's modified
+ * score and G standard Gumbel noise keyed by (seed, t), t the sequence index
+ * of the drawn token (indices count from 0 at the first prompt token; row i
+ * draws index ctx_len + depth(i) + 1).  That is an exact draw from
+ * softmax(score / temperature), and the accept walk keeps a drafted token
+ * exactly while the draw lands on it, so a seed gives the same text for any
+ * drafter.  The noise: Philox4x32-10 (Salmon et al., "Parallel random
+ * numbers: as easy as 1, 2, 3", SC 2011), vocabulary id v taking word v % 4
+ * of the block at counter (v / 4, t, 0, 0) under key (seed & 0xffffffff,
+ * seed >> 32); a word x gives u = (x + 1/2) / 2^32 and G = -log(-log u) in
+ * fp64, rounded to fp32.  gap_ulps then measures the two best noisy scores.
+ * The setting stays with the request slot until changed.  Errors: TV_EINVAL
+ * for a negative, NaN or infinite temperature or a bad request slot. */
+int tv_set_sampling(tv_ctx *ctx, int req, float temperature, uint64_t seed);
 
 /* Prefill: forward `n` prompt tokens as chains of at most 32 through the
  * verify path, committing each chain whole (the prefill chunk grid,
