@@ -20,6 +20,10 @@ Configurations (``--config``; the default c1 is the headline workload):
   64 biased ids, a 50% allow mask) and a drafter that is always wrong, so
   every round commits one token per request.
 
+``--temperature T`` (> 0) makes every request a sampled one (seeded
+Gumbel-max draws in the head kernel); the spine then carries the request's
+own draws.  The bytes are the same as greedy: the noise is generated, not read.
+
 Inputs are synthetic and resident in HBM before timing: N(0, 0.02) bf16
 weights drawn on the device, N(0, 1) bf16 KV caches (and N(0, 1) fp32
 recurrent states) of ``ctx`` rows.
@@ -57,6 +61,9 @@ def parse():
     ap.add_argument("--config", default="c1", choices=["c1", "c2", "c3", "c4"])
     ap.add_argument("--ctx", type=int, default=1024)
     ap.add_argument("--ctx2", type=int, default=8192, help="second request's context (c4)")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="> 0: every request samples (seeded Gumbel-max draws); 0 = greedy")
+    ap.add_argument("--seed", type=int, default=42, help="sampling seed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", default="full",
                     help="'full' = the same four trees; 'n8' = one 8-node tree")
@@ -127,7 +134,8 @@ def gateup_bytes(shape, rows):
 
 
 def learn_spine(tv, parents, tokens, req=0):
-    """Put the model's own greedy token on each spine node (depth by depth)."""
+    """Put the model's own token (the argmax, or a sampled request's draw)
+    on each spine node, depth by depth."""
     import synth
     n = len(parents)
     spine = synth.spine_nodes(parents)
@@ -198,6 +206,9 @@ def main():
         for r in range(n_req):
             md = synth.modifiers(shape.vocab, 7 + r)
             tv.set_modifiers(r, md.rep_penalty, md.bias_ids, md.bias_vals, md.allow_bits)
+    if a.temperature > 0:
+        for r in range(n_req):
+            tv.set_sampling(r, a.temperature, a.seed + r)
 
     # trees: spine carries the model's own greedy tokens (learned in warm-up);
     # c4's drafter is wrong at every node instead
@@ -320,7 +331,8 @@ def main():
     desc = (f"{wname} (hidden {shape.hidden}, {shape.n_qhead}q/{shape.n_kvhead}kv heads x {shape.head_dim}, "
             f"SwiGLU {shape.ffn}) + fp32 head V={shape.vocab}; KV cache {'/'.join(map(str, ctxs))} rows; "
             f"one step = verify+accept+commit of trees n={','.join(map(str, ns))}"
-            + (" for 2 requests in one pass, modifiers on, wrong drafter" if a.config == "c4" else ""))
+            + (" for 2 requests in one pass, modifiers on, wrong drafter" if a.config == "c4" else "")
+            + (f"; sampled requests (temperature {a.temperature}, seed {a.seed})" if a.temperature > 0 else ""))
     out = {
         "metric": "ms per tree verify + achieved HBM GB/s at 8/16/24/32 nodes, 1k ctx, 1 GPU",
         "value": round(value, 2),
@@ -335,7 +347,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": desc, "ctx": ctxs[0] if n_req == 1 else ctxs, "tree_nodes": list(ns),
-                   "requests": n_req, "step_bytes": step_bytes},
+                   "requests": n_req, "step_bytes": step_bytes,
+                   "sampling": {"temperature": a.temperature, "seed": a.seed} if a.temperature > 0 else None},
         "per_n": per,
         "ratio_16_over_8": round(ratio, 4) if ratio else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
