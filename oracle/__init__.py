@@ -36,6 +36,11 @@ What it computes, and where the pages define it:
   verify", The round, step 4).  The closed form of the recurrent state
   ("Drafters and tree verify", Tree verify through recurrent layers) is NOT
   used here; tests check it against this loop.
+* Recurrent layers come in two kinds: a gated linear recurrence
+  (``recur_mix``: S = e^g S_parent + k v^T) and the gated delta rule of the
+  pages' Gated DeltaNet layers (``delta_mix``: S = e^g (I - beta k k^T)
+  S_parent + beta k v^T, beta = sigmoid of a second projection), both
+  stepped one token at a time.
 
 Every pin that holds this code to the pages and to the mathematics lives in
 ``tests/test_oracle_*.py``.
@@ -51,7 +56,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 import torch
 
-from synth import ATTN, RECUR, ModelShape, Modifiers
+from synth import ATTN, DELTA, RECUR, ModelShape, Modifiers
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "_matvec.so")
@@ -116,6 +121,10 @@ def ulp_bf16(x):
 
 def log_sigmoid(a):
     return -np.logaddexp(0.0, -np.asarray(a, dtype=np.float64))
+
+
+def sigmoid(a):
+    return np.exp(log_sigmoid(a))
 
 
 def f32(x):
@@ -203,6 +212,20 @@ class Oracle:
         o = np.einsum("hkv,hk->hv", S, q)
         return o, S
 
+    @staticmethod
+    def delta_mix(q, k, v, g, beta, S_prev):
+        """Gated delta rule, one token, every head at once (Yang, Kautz and
+        Hatamizadeh, "Gated Delta Networks: Improving Mamba2 with Delta
+        Rule", ICLR 2025): the state first decays by alpha = exp(g), then
+        the value it returns for key k is moved a fraction beta of the way
+        to v:  S = alpha (I - beta k k^T) S_prev + beta k v^T  (key index
+        first), read out o = S^T q.  q, k, v [QH, D]; g, beta [QH]."""
+        kS = np.einsum("hk,hkv->hv", k, S_prev)              # S_prev^T k
+        S = np.exp(g)[:, None, None] * (S_prev - beta[:, None, None] * k[:, :, None] * kS[:, None, :]) \
+            + beta[:, None, None] * k[:, :, None] * v[:, None, :]
+        o = np.einsum("hkv,hk->hv", S, q)
+        return o, S
+
     def l2norm(self, x: np.ndarray) -> np.ndarray:
         return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + self.s.eps)
 
@@ -241,7 +264,11 @@ class Oracle:
                 k = r(self.l2norm(qkv[QH * D:2 * QH * D].reshape(QH, D)))
                 v = qkv[2 * QH * D:].reshape(QH, D)
                 a = r(self.matvec(p + "wa", xn))
-                o, S = self.recur_mix(q, k, v, log_sigmoid(a), states[l])
+                if kind == RECUR:
+                    o, S = self.recur_mix(q, k, v, log_sigmoid(a), states[l])
+                else:
+                    # gate rows, then write-strength rows
+                    o, S = self.delta_mix(q, k, v, log_sigmoid(a[:QH]), sigmoid(a[QH:]), states[l])
                 o = r(o.reshape(-1))
                 # the state is held in fp32 between tokens
                 new_states[l] = S if self.exact else f32(S)

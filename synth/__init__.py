@@ -28,7 +28,8 @@ import torch
 
 # Layer kinds.
 ATTN = 0
-RECUR = 1
+RECUR = 1    # gated linear recurrence
+DELTA = 2    # gated delta rule
 
 
 @dataclasses.dataclass(frozen=True)
@@ -43,7 +44,7 @@ class ModelShape:
     head_dim: int
     ffn: int
     vocab: int
-    kinds: Tuple[int, ...]  # per layer: ATTN or RECUR
+    kinds: Tuple[int, ...]  # per layer: ATTN, RECUR or DELTA
     eps: float = 1e-6
     rope_theta: float = 1e4
 
@@ -69,8 +70,12 @@ C1 = _shape("c1_layer", 1, 5120, 40, 8, 128, 17408, 151936)
 C2 = _shape("c2_stack64", 64, 5120, 40, 8, 128, 17408, 151936)
 C3 = _shape("c3_hybrid64", 64, 5120, 40, 8, 128, 17408, 151936,
             kinds=[RECUR if (l % 4) != 3 else ATTN for l in range(64)])
+# c3 with gated delta-rule layers in place of the plain gated recurrence: the
+# pages' 48 Gated DeltaNet + 16 attention layers
+C3D = _shape("c3d_delta64", 64, 5120, 40, 8, 128, 17408, 151936,
+             kinds=[DELTA if (l % 4) != 3 else ATTN for l in range(64)])
 
-SHAPES = {s.name: s for s in (C0, C1, C2, C3)}
+SHAPES = {s.name: s for s in (C0, C1, C2, C3, C3D)}
 
 
 def scaled(shape: ModelShape, name: str, n_layer: Optional[int] = None,
@@ -100,7 +105,9 @@ def weight_names(shape: ModelShape) -> List[Tuple[str, Tuple[int, ...], str]]:
             out.append((p + "wqkv", (shape.qkv_rows, H), "normal"))
         else:
             out.append((p + "wqkv", (shape.rqkv_rows, H), "normal"))
-            out.append((p + "wa", (shape.n_qhead, H), "normal"))
+            # gate rows; a delta layer stacks its write-strength rows under them
+            rows = shape.n_qhead if k == RECUR else 2 * shape.n_qhead
+            out.append((p + "wa", (rows, H), "normal"))
         out.append((p + "wo", (H, QD), "normal"))
         out.append((p + "ffn_norm", (H,), "ones"))
         out.append((p + "wg", (shape.ffn, H), "normal"))
@@ -177,7 +184,7 @@ def state0(shape: ModelShape, seed: int, device="cpu", layers: Optional[Sequence
     """Synthetic N(0,1) fp32 start state [QH, D, D] per recurrent layer."""
     out = {}
     for l, k in enumerate(shape.kinds):
-        if k != RECUR or (layers is not None and l not in layers):
+        if k == ATTN or (layers is not None and l not in layers):
             continue
         g = _gen(seed * 1_000_003 + l, device)
         out[l] = torch.randn((shape.n_qhead, shape.head_dim, shape.head_dim),
