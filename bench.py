@@ -15,6 +15,8 @@ Configurations (``--config``; the default c1 is the headline workload):
 * c1: one 5120-wide decoder layer + fp32 head, trees n = 8/16/24/32.
 * c2: 64 such layers.
 * c3: the 64-layer hybrid (48 gated-recurrence + 16 attention layers), n = 16.
+* c3d: c3 with gated delta-rule (Gated DeltaNet) layers in place of the plain
+  gated recurrence, n = 16.
 * c4: c2 with two requests of 16 rows each in one joint pass (contexts
   ``ctx`` and ``--ctx2``), score modifiers on both (repetition penalty 1.1,
   64 biased ids, a 50% allow mask) and a drafter that is always wrong, so
@@ -50,7 +52,7 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 NS = (8, 16, 24, 32)
 MIN_CPU_S = 10.0     # the CPU baseline repeats its sample for at least this long
-ATTN, RECUR = 0, 1   # layer kinds (as in synth)
+ATTN, RECUR, DELTA = 0, 1, 2   # layer kinds (as in synth)
 
 
 def parse():
@@ -58,7 +60,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c1", choices=["c1", "c2", "c3", "c4"])
+    ap.add_argument("--config", default="c1", choices=["c1", "c2", "c3", "c3d", "c4"])
     ap.add_argument("--ctx", type=int, default=1024)
     ap.add_argument("--ctx2", type=int, default=8192, help="second request's context (c4)")
     ap.add_argument("--temperature", type=float, default=0.0,
@@ -90,7 +92,8 @@ def model_bytes(shape, n, ctxs, path_lens, mods=False):
                 b += 2 * n * KVH * D * 2                # tree K and V written
                 b += 2 * 2 * pl * KVH * D * 2           # committed rows read + written
         else:
-            b += shape.rqkv_rows * H * 2 + QH * H * 2   # wqkv, gate projection
+            b += shape.rqkv_rows * H * 2                # wqkv
+            b += (2 if kind == DELTA else 1) * QH * H * 2   # gate (and write-strength) projection
             for _ in ctxs:
                 b += QH * D * D * 4                     # state read by the verify
                 b += 2 * QH * D * D * 4                 # state read + written by the commit
@@ -176,8 +179,8 @@ def main():
     import workloads
     from greedy_draft_tree_amd import accept_walk
 
-    shape = {"c1": synth.C1, "c2": synth.C2, "c3": synth.C3, "c4": synth.C2}[a.config]
-    ns = {"c1": NS, "c2": NS, "c3": (16,), "c4": (16,)}[a.config]
+    shape = {"c1": synth.C1, "c2": synth.C2, "c3": synth.C3, "c3d": synth.C3D, "c4": synth.C2}[a.config]
+    ns = {"c1": NS, "c2": NS, "c3": (16,), "c3d": (16,), "c4": (16,)}[a.config]
     ctxs = [a.ctx, a.ctx2] if a.config == "c4" else [a.ctx]
     n_req = len(ctxs)
     mods_on = a.config == "c4"
@@ -327,7 +330,9 @@ def main():
         cpu = cpu_baseline(shape, wl, kv, ctxs[0], {n: trees[n][0] for n in ns}, a.cpu_sample, ns)
 
     wname = {"c1": "c1_layer: 1 x", "c2": "c2_stack64: 64 x",
-             "c3": "c3_hybrid64: 48 recurrent + 16 attention layers x", "c4": "c4 on c2_stack64: 64 x"}[a.config]
+             "c3": "c3_hybrid64: 48 recurrent + 16 attention layers x",
+             "c3d": "c3d_delta64: 48 gated delta-rule + 16 attention layers x",
+             "c4": "c4 on c2_stack64: 64 x"}[a.config]
     desc = (f"{wname} (hidden {shape.hidden}, {shape.n_qhead}q/{shape.n_kvhead}kv heads x {shape.head_dim}, "
             f"SwiGLU {shape.ffn}) + fp32 head V={shape.vocab}; KV cache {'/'.join(map(str, ctxs))} rows; "
             f"one step = verify+accept+commit of trees n={','.join(map(str, ns))}"

@@ -9,7 +9,7 @@ import numpy as np
 
 TV_OK, TV_EINVAL, TV_ECAPACITY, TV_ESTATE, TV_EHIP = 0, -1, -2, -3, -4
 TV_MAX_NODES = 32
-TV_LAYER_ATTN, TV_LAYER_RECUR = 0, 1
+TV_LAYER_ATTN, TV_LAYER_RECUR, TV_LAYER_DELTA = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtreeverify.so")

@@ -112,15 +112,16 @@ struct RopeArgs {
 struct RecurArgs {
     const float *qkv_part; // split-K partials of the [rows, 3*QH*D] projection (q heads, k heads, v heads)
     int qkv_S;             // its k-range splits
-    const float *a_part;   // split-K partials of the [rows, QH] gate pre-activations
-    int a_S;
+    const float *a_part;   // split-K partials of the gate pre-activations [rows, QH] (a delta
+    int a_S;               // layer: then the write-strength pre-activations [rows, QH])
     const float *S0;      // [QH][D][D] state before the round (key index, value index)
     const PassMeta *meta;
     uint16_t *out;        // [rows, QH*D] read-out (bf16)
     uint16_t *save_k;     // [kMaxRows][QH][D] normalised keys of this layer (request-local node order)
-    uint16_t *save_v;     // [kMaxRows][QH][D] values
+    float *save_v;        // [kMaxRows][QH][D] values (a delta layer: pseudo-values u)
     float *save_gc;       // [kMaxRows][QH] cumulative log-gates
-    int a_col;             // column of head 0's gate in a_part's layout
+    int a_col;             // column of head 0's gate in a_part's layout (its write strength: a_col + QH)
+    int delta;             // gated delta rule instead of the plain gated recurrence
     int row0, n, QH;
     float eps;
 };
@@ -134,7 +135,7 @@ struct PathArg {
 struct RecurCommitArgs {
     float *const *states;   // [n_layers] bound states, [QH][D][D] each
     const uint16_t *save_k; // [n_layers][kMaxRows][QH][D]
-    const uint16_t *save_v;
+    const float *save_v;    // [n_layers][kMaxRows][QH][D] values or pseudo-values
     const float *save_gc;   // [n_layers][kMaxRows][QH]
     PathArg path;
     int QH;

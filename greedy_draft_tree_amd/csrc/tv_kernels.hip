@@ -876,12 +876,24 @@ __global__ __launch_bounds__(D) void k_attn_combine(AttnArgs a, uint16_t *__rest
 // parent's state.  q and k are L2-normalised per head and rounded to bf16,
 // g = log sigmoid(a).  One workgroup per head; it also saves k, v and gc of
 // every node for the commit.
+//
+// Gated delta rule (the pages' Gated DeltaNet layers; Yang, Kautz and
+// Hatamizadeh, ICLR 2025): S(t) = e^{g_t} (I - b_t k_t k_t^T) S(parent)
+// + b_t k_t v_t^T with write strength b = sigmoid(.).  Written as
+// S(t) = e^{g_t} S(parent) + k_t u_t^T it is the same recurrence with the
+// pseudo-value u_t in place of v_t, where
+//   u_t + sum_{s strict ancestor of t} b_t e^{gc_t - gc_s} (k_t . k_s) u_s
+//       = b_t (v_t - e^{gc_t} S0^T k_t):
+// a unit lower-triangular system whose off-diagonal part is ancestor-masked
+// ("Drafters and tree verify", Tree verify through recurrent layers), solved
+// by forward substitution in node order; u replaces v in the read-out and
+// in what the commit saves.
 
 __device__ __forceinline__ float log_sigmoid(float a) {
     return a >= 0.f ? -log1pf(expf(-a)) : a - log1pf(expf(a));
 }
 
-template <int D>
+template <int D, bool DELTA>
 __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     // grid (head, value slice): a workgroup produces value columns
     // [v0, v0 + VW) of its head for every node; the small per-head setup
@@ -897,6 +909,9 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     __shared__ float s0[D][VW];            // S0 rows (key index) restricted to this slice's value columns
     __shared__ float gsh[kMaxRows], gcs[kMaxRows], scale[2][kMaxRows];
     __shared__ float coef[kMaxRows][kMaxRows + 1];
+    // delta rule: write strengths and b_t e^{gc_t - gc_s} (k_t . k_s) for strict ancestors s
+    __shared__ float bsh[DELTA ? kMaxRows : 1];
+    __shared__ float akk[DELTA ? kMaxRows : 1][kMaxRows + 1];
     const int h = blockIdx.x, v0 = blockIdx.y * VW, tid = threadIdx.x, n = r.n, QH = r.QH;
     const int lane = tid & 63, wave = tid >> 6;
 
@@ -930,7 +945,13 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
         const int t = idx / VW, c = idx % VW;
         vsm[t][c] = bfround(psum(r.qkv_part, r.qkv_S, 1, 0, r.row0 + t, (2 * QH + h) * D + v0 + c));
     }
-    if (tid < n) gsh[tid] = log_sigmoid(bfround(psum(r.a_part, r.a_S, 1, 0, r.row0 + tid, r.a_col + h)));
+    if (tid < n) {
+        gsh[tid] = log_sigmoid(bfround(psum(r.a_part, r.a_S, 1, 0, r.row0 + tid, r.a_col + h)));
+        if constexpr (DELTA) {
+            const float b = bfround(psum(r.a_part, r.a_S, 1, 0, r.row0 + tid, r.a_col + QH + h));
+            bsh[tid] = 1.0f / (1.0f + expf(-b));
+        }
+    }
     __syncthreads();
     // L2 norms of q and k rows: one wave per vector, shuffle reduction
     for (int vec = wave; vec < 2 * n; vec += 4) {
@@ -959,25 +980,60 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     __syncthreads();
     for (int idx = tid; idx < n * n; idx += 256) {
         const int t = idx / n, s = idx % n;
-        float cf = 0.f;
+        float cf = 0.f, ck = 0.f;
         if ((r.meta->anc[r.row0 + t] >> s) & 1u) {
             float dot = 0.f;
             for (int d = 0; d < D; ++d) dot += qs[t][d] * ks[s][d];
-            cf = expf(gcs[t] - gcs[s]) * dot;
+            const float decay = expf(gcs[t] - gcs[s]);
+            cf = decay * dot;
+            if constexpr (DELTA) {
+                if (s != t) {
+                    float dk = 0.f;
+                    for (int d = 0; d < D; ++d) dk += ks[t][d] * ks[s][d];
+                    ck = bsh[t] * decay * dk;
+                }
+            }
         }
         coef[t][s] = cf;
+        if constexpr (DELTA) akk[t][s] = ck;
     }
     __syncthreads();
     // read-out: thread -> value column c, nodes t = grp, grp + NG, ...
     const int c = tid % VW, grp = tid / VW;
-    float acc[RJ];
+    float acc[RJ], acck[DELTA ? RJ : 1];
 #pragma unroll
     for (int j = 0; j < RJ; ++j) acc[j] = 0.f;
+    if constexpr (DELTA) {
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) acck[j] = 0.f;
+    }
 #pragma unroll 8
     for (int k = 0; k < D; ++k) {
         const float sv = s0[k][c];
 #pragma unroll
-        for (int j = 0; j < RJ; ++j) acc[j] += sv * qs[grp + j * NG][k];
+        for (int j = 0; j < RJ; ++j) {
+            acc[j] += sv * qs[grp + j * NG][k];
+            if constexpr (DELTA) acck[j] += sv * ks[grp + j * NG][k];
+        }
+    }
+    if constexpr (DELTA) {
+        // right-hand side b_t (v_t - e^{gc_t} S0^T k_t), in place of v
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) {
+            const int t = grp + j * NG;
+            if (t < n) vsm[t][c] = bsh[t] * (vsm[t][c] - expf(gcs[t]) * acck[j]);
+        }
+        __syncthreads();
+        // forward substitution, one thread per value column: ancestors have
+        // lower indices, so u_s is final when node t needs it
+        if (tid < VW) {
+            for (int t = 1; t < n; ++t) {
+                float x = vsm[t][tid];
+                for (int s2 = 0; s2 < t; ++s2) x -= akk[t][s2] * vsm[s2][tid];
+                vsm[t][tid] = x;
+            }
+        }
+        __syncthreads();
     }
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
@@ -986,7 +1042,7 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
         float o = expf(gcs[t]) * acc[j];
         for (int s = 0; s <= t; ++s) o += coef[t][s] * vsm[s][c];
         r.out[(size_t)(r.row0 + t) * QH * D + h * D + v0 + c] = f2bf(o);
-        r.save_v[((size_t)t * QH + h) * D + v0 + c] = f2bf(vsm[t][c]);
+        r.save_v[((size_t)t * QH + h) * D + v0 + c] = vsm[t][c];
     }
     if (blockIdx.y == 0) {
         for (int idx = tid; idx < n * D; idx += 256) {
@@ -1000,7 +1056,8 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
 // State commit: the state after the accepted path from the quantities the
 // verify saved ("Drafters and tree verify", Tree verify through recurrent
 // layers: S_path = e^{gc_last} S0 + sum over the path of e^{gc_last - gc_t}
-// k_t (x) v_t), in place; one read and write of the state, no weights.
+// k_t (x) u_t, u = v for the plain gated recurrence), in place; one read and
+// write of the state, no weights.
 template <int D>
 __global__ __launch_bounds__(256) void k_recur_commit(RecurCommitArgs a) {
     __shared__ float kk[kMaxRows][D], vv[kMaxRows][D], w[kMaxRows];
@@ -1008,12 +1065,12 @@ __global__ __launch_bounds__(256) void k_recur_commit(RecurCommitArgs a) {
     const int l = blockIdx.x / a.QH, h = blockIdx.x % a.QH, tid = threadIdx.x, QH = a.QH;
     const int L = a.path.len;
     const uint16_t *sk = a.save_k + (size_t)l * kMaxRows * QH * D;
-    const uint16_t *sv = a.save_v + (size_t)l * kMaxRows * QH * D;
+    const float *sv = a.save_v + (size_t)l * kMaxRows * QH * D;
     const float *sg = a.save_gc + (size_t)l * kMaxRows * QH;
     for (int idx = tid; idx < L * D; idx += 256) {
         const int d = idx / D, e = idx % D, node = a.path.node[d];
         kk[d][e] = bf2f(sk[((size_t)node * QH + h) * D + e]);
-        vv[d][e] = bf2f(sv[((size_t)node * QH + h) * D + e]);
+        vv[d][e] = sv[((size_t)node * QH + h) * D + e];
     }
     const float gl = sg[(size_t)a.path.node[L - 1] * QH + h];
     if (tid < L) w[tid] = expf(gl - sg[(size_t)a.path.node[tid] * QH + h]);
@@ -1145,8 +1202,11 @@ hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M
 
 hipError_t launch_recur_tree(hipStream_t s, int D, const RecurArgs &a) {
     if (a.n < 1 || a.n > kMaxRows) return hipErrorInvalidValue;
-    if (D == 128) hipLaunchKernelGGL(k_recur_tree<128>, dim3(a.QH, kRecurSlices), dim3(256), 0, s, a);
-    else if (D == 64) hipLaunchKernelGGL(k_recur_tree<64>, dim3(a.QH, kRecurSlices), dim3(256), 0, s, a);
+    const dim3 grid(a.QH, kRecurSlices), block(256);
+    if (D == 128 && a.delta) hipLaunchKernelGGL((k_recur_tree<128, true>), grid, block, 0, s, a);
+    else if (D == 128) hipLaunchKernelGGL((k_recur_tree<128, false>), grid, block, 0, s, a);
+    else if (D == 64 && a.delta) hipLaunchKernelGGL((k_recur_tree<64, true>), grid, block, 0, s, a);
+    else if (D == 64) hipLaunchKernelGGL((k_recur_tree<64, false>), grid, block, 0, s, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

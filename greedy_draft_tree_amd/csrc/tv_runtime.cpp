@@ -45,7 +45,8 @@ struct Req {
     // recurrent layers: bound state table and the last verify's saved k, v, gc
     float **d_stab = nullptr;
     bool stab_dirty = true;
-    uint16_t *save_k = nullptr, *save_v = nullptr;
+    uint16_t *save_k = nullptr;
+    float *save_v = nullptr;   // values, or a delta layer's pseudo-values (fp32)
     float *save_gc = nullptr;
 };
 
@@ -231,14 +232,14 @@ int check_bound(tv_ctx *c, const std::vector<int> &reqs) {
         if (!c->attn_norm[l] || !c->wqkv[l] || !c->wo[l] || !c->ffn_norm[l] || !c->wg[l] || !c->wu[l] ||
             !c->wd[l])
             return fail(c, TV_ESTATE, "layer %d weights not bound", l);
-        if (c->kinds[l] == TV_LAYER_RECUR && !c->wa[l]) return fail(c, TV_ESTATE, "layer %d wa not bound", l);
+        if (c->kinds[l] != TV_LAYER_ATTN && !c->wa[l]) return fail(c, TV_ESTATE, "layer %d wa not bound", l);
     }
     for (int r : reqs) {
         const Req &q = c->reqs[r];
         for (int l = 0; l < m.n_layer; ++l) {
             if (c->kinds[l] == TV_LAYER_ATTN && (!q.K[l] || !q.V[l]))
                 return fail(c, TV_ESTATE, "request %d layer %d KV cache not bound", r, l);
-            if (c->kinds[l] == TV_LAYER_RECUR && !q.S[l])
+            if (c->kinds[l] != TV_LAYER_ATTN && !q.S[l])
                 return fail(c, TV_ESTATE, "request %d layer %d state not bound", r, l);
         }
     }
@@ -477,18 +478,20 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
         } else {
             const int rl = c->recur_index[l];
             // one projection over the q/k/v rows stacked on the gate rows
-            // leaves split-K partials; the read-out kernel finishes them
+            // (and a delta layer's write-strength rows) leaves split-K
+            // partials; the read-out kernel finishes them
+            const bool delta = c->kinds[l] == TV_LAYER_DELTA;
             GemmArgs g{};
             NORMED(g, c->attn_norm[l]);
             g.W = c->wqkv[l]; g.W2 = c->wa[l]; g.N1 = 3 * QH * D;
-            g.M = M; g.N = 3 * QH * D + QH; g.K = H;
+            g.M = M; g.N = 3 * QH * D + (delta ? 2 : 1) * QH; g.K = H;
             int Sq = 0;
             GEMMP(c, "gemm_qkv", g, Sq);
             for (int r = 0; r < n_req; ++r) {
                 Req &q = c->reqs[reqs[r]];
                 RecurArgs ra{};
                 ra.qkv_part = c->gemm_partial; ra.qkv_S = Sq;
-                ra.a_part = c->gemm_partial; ra.a_S = Sq; ra.a_col = 3 * QH * D;
+                ra.a_part = c->gemm_partial; ra.a_S = Sq; ra.a_col = 3 * QH * D; ra.delta = delta;
                 ra.S0 = q.S[l]; ra.meta = c->d_meta; ra.out = c->ATT;
                 const size_t per = (size_t)kMaxRows * QH * D;
                 ra.save_k = q.save_k + rl * per;
@@ -571,7 +574,7 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     c->m = m;
     c->kinds.assign(m.layer_kind, m.layer_kind + m.n_layer);
     for (int l = 0; l < m.n_layer; ++l) {
-        if (c->kinds[l] != TV_LAYER_ATTN && c->kinds[l] != TV_LAYER_RECUR) {
+        if (c->kinds[l] != TV_LAYER_ATTN && c->kinds[l] != TV_LAYER_RECUR && c->kinds[l] != TV_LAYER_DELTA) {
             delete c;
             return TV_EINVAL;
         }
@@ -613,7 +616,7 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
         const size_t nrl = c->recur_layers.size();
         for (auto &q : c->reqs) {
             ALLOC(q.save_k, nrl * R * m.n_qhead * D * 2);
-            ALLOC(q.save_v, nrl * R * m.n_qhead * D * 2);
+            ALLOC(q.save_v, nrl * R * m.n_qhead * D * 4);
             ALLOC(q.save_gc, nrl * R * m.n_qhead * 4);
         }
     }
@@ -629,7 +632,7 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
         const int QD = m.n_qhead * D;
         size_t need = (size_t)8 << 20;  // room for kernel-level calls
         need = std::max(need, gemm_partial_need((m.n_qhead + 2 * m.n_kvhead) * D, H, false, true));
-        need = std::max(need, gemm_partial_need(3 * QD + m.n_qhead, H, false, true));   // recurrent qkv + gate
+        need = std::max(need, gemm_partial_need(3 * QD + 2 * m.n_qhead, H, false, true));   // recurrent qkv + gate (+ write strength)
         need = std::max(need, gemm_partial_need(H, QD, false, true));
         need = std::max(need, gemm_partial_need(m.ffn, H, true));
         need = std::max(need, gemm_partial_need(H, m.ffn, false, true));
@@ -729,7 +732,7 @@ int tv_bind(tv_ctx *c, const char *name, void *ptr, size_t bytes) {
         if (!strcmp(field, "wqkv")) return mat(c->wqkv[l], at ? (QH + 2 * KVH) * D : 3 * QH * D, H);
         if (!strcmp(field, "wa")) {
             if (at) return fail(c, TV_EINVAL, "%s: not a recurrent layer", name);
-            return mat(c->wa[l], QH, H);
+            return mat(c->wa[l], c->kinds[l] == TV_LAYER_DELTA ? 2 * QH : QH, H);
         }
         if (!strcmp(field, "wo")) return mat(c->wo[l], H, QH * D);
         if (!strcmp(field, "wg")) return mat(c->wg[l], F, H);

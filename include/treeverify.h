@@ -62,11 +62,19 @@ extern "C" {
 
 #define TV_LAYER_ATTN 0   /* grouped-query attention layer with RoPE */
 #define TV_LAYER_RECUR 1  /* gated linear recurrence layer */
+#define TV_LAYER_DELTA 2  /* gated delta-rule layer (Gated DeltaNet, "Drafters and
+                             tree verify", Tree verify through recurrent layers) */
 
 /* Shapes of the target model.  Every weight matrix is [N_out, K_in]
  * row-major bf16.  An attention layer's wqkv stacks n_qhead, then n_kvhead,
  * then n_kvhead heads of head_dim rows; a recurrent layer's wqkv stacks q, k
- * and v with n_qhead heads each, and its wa is [n_qhead, hidden]. */
+ * and v with n_qhead heads each.  wa of a TV_LAYER_RECUR layer is
+ * [n_qhead, hidden]: the log-gate g = log sigmoid(x wa^T) of each head, the
+ * state S = e^g S_parent + k v^T.  wa of a TV_LAYER_DELTA layer is
+ * [2 n_qhead, hidden]: the gate rows, then the write-strength rows
+ * b = sigmoid(x wb^T); its state follows the gated delta rule
+ * S = e^g (I - b k k^T) S_parent + b k v^T (key index first).  Both read
+ * out o = S^T q with q and k L2-normalised per head. */
 typedef struct tv_model_desc {
     int n_layer;
     int hidden;
@@ -94,7 +102,7 @@ const char *tv_last_error(tv_ctx *ctx);
  *   "emb" [vocab, hidden] bf16        "head" [vocab, hidden] bf16
  *   "final_norm" [hidden] bf16
  *   "layers.L.attn_norm", "layers.L.ffn_norm" [hidden] bf16
- *   "layers.L.wqkv", "layers.L.wo", "layers.L.wa" (recurrent only),
+ *   "layers.L.wqkv", "layers.L.wo", "layers.L.wa" (recurrent and delta only),
  *   "layers.L.wg", "layers.L.wu" [ffn, hidden], "layers.L.wd" [hidden, ffn]
  *   "req.R.layers.L.k", "req.R.layers.L.v"  [n_kvhead, max_ctx, head_dim] bf16
  *   "req.R.layers.L.state"                  [n_qhead, head_dim, head_dim] fp32

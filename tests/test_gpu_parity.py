@@ -334,15 +334,18 @@ def test_c1_tree_rows(c1, n, ctx):
 
 # ------------------------------------------------------------- hybrid (C3 layer mix)
 
-HYB0 = synth.scaled(synth.C0, "c0_hybrid", n_layer=4, kinds=[1, 1, 1, 0])
+# three recurrent layers (plain gated recurrence or gated delta rule) + one attention layer
+HYB0 = {k: synth.scaled(synth.C0, name, n_layer=4, kinds=[k, k, k, synth.ATTN])
+        for k, name in ((synth.RECUR, "c0_hybrid"), (synth.DELTA, "c0_delta"))}
 
 
-@pytest.fixture(scope="module")
-def hyb0():
+@pytest.fixture(scope="module", params=[synth.RECUR, synth.DELTA], ids=["gated", "delta"])
+def hyb0(request):
     _gpu()
     import workloads
-    wl = workloads.build(HYB0, max_ctx=256, max_req=1, weight_device="cuda", host_copy=True)
-    return wl, oracle.Oracle(HYB0, wl.host_weights)
+    shape = HYB0[request.param]
+    wl = workloads.build(shape, max_ctx=256, max_req=1, weight_device="cuda", host_copy=True)
+    return wl, oracle.Oracle(shape, wl.host_weights)
 
 
 def _load_states(wl, req, s0):
@@ -352,14 +355,16 @@ def _load_states(wl, req, s0):
 
 
 def test_hybrid_c0_rounds_and_states(hyb0):
-    """Gated-recurrence layers: per-node rows, greedy rounds with commits of
-    the accepted path's state ("Drafters and tree verify", Tree verify
+    """Recurrent layers (gated recurrence, or the gated delta rule with its
+    ancestor-masked pseudo-values): per-node rows, greedy rounds with commits
+    of the accepted path's state ("Drafters and tree verify", Tree verify
     through recurrent layers), and the committed states themselves."""
     wl, orc = hyb0
-    s0 = synth.state0(HYB0, seed=6)
+    s0 = synth.state0(orc.s, seed=6)
+    _say("hybrid rounds", orc.s.name)
     _load_states(wl, 0, s0)
     wl.tv.set_history(0, [], 0)
-    prompt = synth.uniform_ids(40, HYB0.vocab, 3)
+    prompt = synth.uniform_ids(40, orc.s.vocab, 3)
     wl.tv.prefill(0, prompt[:-1])
     seq = orc.new_seq(cap=256, s0=s0)
     seq.commit(prompt[:-1])
@@ -384,36 +389,40 @@ def test_hybrid_c0_rounds_and_states(hyb0):
         got = t.cpu().numpy().astype(np.float64)
         want = seq.S[l]
         err = np.abs(got - want).max()
-        print(f"[hybrid state layer {l}] max|dS| {err:.3g} max|S| {np.abs(want).max():.3g}", flush=True)
+        print(f"[{orc.s.name} state layer {l}] max|dS| {err:.3g} max|S| {np.abs(want).max():.3g}", flush=True)
         assert err <= 2e-2 * max(1.0, np.abs(want).max()), (l, err)
 
 
-HYB4 = synth.scaled(synth.C1, "c3_layers4", n_layer=4, kinds=[1, 1, 1, 0])
+HYB4 = {k: synth.scaled(synth.C1, name, n_layer=4, kinds=[k, k, k, synth.ATTN])
+        for k, name in ((synth.RECUR, "c3_layers4"), (synth.DELTA, "c3d_layers4"))}
 
 
-def test_hybrid_full_width_tree_and_commit():
+@pytest.mark.parametrize("kind", [synth.RECUR, synth.DELTA], ids=["gated", "delta"])
+def test_hybrid_full_width_tree_and_commit(kind):
     """The hybrid layer mix at full width (3 recurrent + 1 attention layers,
     hidden 5120, 40 heads x 128x128 fp32 states) with a 16-node tree at 1k
     context, then a commit of a multi-node path."""
     _gpu()
     import workloads
+    HYB4_ = HYB4[kind]
+    _say("hybrid full width", HYB4_.name)
     ctx = 1024
-    wl = workloads.build(HYB4, max_ctx=ctx + 32, max_req=1, weight_device="cuda", host_copy=True)
-    orc = oracle.Oracle(HYB4, wl.host_weights)
-    kv = synth.kv_cache(HYB4, ctx, seed=3, cap=ctx)
-    s0 = synth.state0(HYB4, seed=6)
-    hist = synth.uniform_ids(ctx, HYB4.vocab, 30)
+    wl = workloads.build(HYB4_, max_ctx=ctx + 32, max_req=1, weight_device="cuda", host_copy=True)
+    orc = oracle.Oracle(HYB4_, wl.host_weights)
+    kv = synth.kv_cache(HYB4_, ctx, seed=3, cap=ctx)
+    s0 = synth.state0(HYB4_, seed=6)
+    hist = synth.uniform_ids(ctx, HYB4_.vocab, 30)
     workloads.load_context(wl, 0, ctx, 3, history=hist, src_kv={k: v.cuda() for k, v in kv.items()},
                            src_states={l: v.cuda() for l, v in s0.items()})
     seq = orc.new_seq(cap=ctx + 32, kv=kv, ctx_len=ctx, history=hist, s0=s0)
     parents = synth.spine_tree(16, 4)
-    tokens = synth.tree_tokens(parents, HYB4.vocab, 21, root_token=int(hist[-1]))
+    tokens = synth.tree_tokens(parents, HYB4_.vocab, 21, root_token=int(hist[-1]))
     am, gap = wl.tv.verify_tree(0, parents, tokens, logits=wl.logits)
     ol = orc.tree_scores(seq, parents, tokens)
-    ex = oracle.Oracle(HYB4, wl.host_weights, exact=True)
+    ex = oracle.Oracle(HYB4_, wl.host_weights, exact=True)
     oe = ex.tree_scores(ex.new_seq(cap=ctx + 32, kv=kv, ctx_len=ctx, history=hist, s0=s0), parents, tokens)
     check_rows(wl.logits[:16].cpu().numpy(), am, gap, ol, parents, tokens, seq.history,
-               what="c3 layers x4 n=16", orc_exact=oe)
+               what=f"{HYB4_.name} n=16", orc_exact=oe)
     spine = synth.spine_nodes(parents)
     path = spine[:5]
     wl.tv.commit(0, path)
@@ -422,7 +431,7 @@ def test_hybrid_full_width_tree_and_commit():
     for l, t in wl.states[0].items():
         got = t.cpu().numpy().astype(np.float64)
         err = np.abs(got - seq.S[l]).max()
-        print(f"[c3 state layer {l}] max|dS| {err:.3g}", flush=True)
+        print(f"[{HYB4_.name} state layer {l}] max|dS| {err:.3g}", flush=True)
         assert err <= 2e-2 * max(1.0, np.abs(seq.S[l]).max()), (l, err)
 
 
