@@ -110,17 +110,17 @@ struct RopeArgs {
 };
 
 struct RecurArgs {
-    const float *qkv_part; // split-K partials of the [rows, 3*QH*D] projection (q heads, k heads, v heads)
+    const float *qkv_part; // split-K partials of the stacked projection: q heads, k heads, v heads
+                           // (3*QH*D columns), then from column a_col the gate pre-activations
+                           // [QH] and, for a delta layer, the write-strength pre-activations [QH]
     int qkv_S;             // its k-range splits
-    const float *a_part;   // split-K partials of the gate pre-activations [rows, QH] (a delta
-    int a_S;               // layer: then the write-strength pre-activations [rows, QH])
     const float *S0;      // [QH][D][D] state before the round (key index, value index)
     const PassMeta *meta;
     uint16_t *out;        // [rows, QH*D] read-out (bf16)
     uint16_t *save_k;     // [kMaxRows][QH][D] normalised keys of this layer (request-local node order)
     float *save_v;        // [kMaxRows][QH][D] values (a delta layer: pseudo-values u)
     float *save_gc;       // [kMaxRows][QH] cumulative log-gates
-    int a_col;             // column of head 0's gate in a_part's layout (its write strength: a_col + QH)
+    int a_col;             // column of head 0's gate (its write strength: a_col + QH)
     int delta;             // gated delta rule instead of the plain gated recurrence
     int row0, n, QH;
     float eps;

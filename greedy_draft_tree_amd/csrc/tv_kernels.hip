@@ -893,153 +893,279 @@ __device__ __forceinline__ float log_sigmoid(float a) {
     return a >= 0.f ? -log1pf(expf(-a)) : a - log1pf(expf(a));
 }
 
+// Split-K sums of U elements at once: every split's load of the U elements
+// is issued before any add (4 splits per round), and each element's adds stay
+// in k-range order, as in psum.
+template <int U>
+__device__ __forceinline__ void psum_batch(const float *__restrict__ P, int S, const int (&m)[U],
+                                           const int (&col)[U], const bool (&ok)[U], float (&out)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) out[u] = 0.f;
+    for (int k0 = 0; k0 < S; k0 += 4) {
+        float l[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float *p = P + ((size_t)(col[u] >> 7) * S + k0) * 4096 + (size_t)m[u] * 128 + (col[u] & 127);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) l[u][j] = (ok[u] && k0 + j < S) ? p[(size_t)j * 4096] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (k0 + j < S) out[u] += l[u][j];
+        }
+    }
+}
+
+// Eight consecutive fp32 values as bf16 (exact when they are bf16 values).
+__device__ __forceinline__ uint4 pack_bf8(const float *x) {
+    return uint4{f2bf2(x[0], x[1]), f2bf2(x[2], x[3]), f2bf2(x[4], x[5]), f2bf2(x[6], x[7])};
+}
+
 template <int D, bool DELTA>
 __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     // grid (head, value slice): a workgroup produces value columns
     // [v0, v0 + VW) of its head for every node; the small per-head setup
     // (norms, cumulative gates, the node-node coefficients) is repeated by
-    // the head's slices.
+    // the head's slices.  The three small products of the read-out run on
+    // MFMA (v_mfma_f32_32x32x16_bf16, nodes and value columns padded to 32):
+    // Q K^T and K K^T with exact bf16 operands (q and k are bf16 values), and
+    // S0^T Q, S0^T K with the fp32 state split into bf16 hi + lo parts
+    // (|S0 - hi - lo| <= 2^-17 |S0|).
     constexpr int VS = kRecurSlices;
-    constexpr int VW = D / VS;             // value columns per workgroup
-    constexpr int DP = D + 1;              // padded row stride: column walks hit distinct banks
-    constexpr int NG = 256 / VW;           // node groups in the read-out
-    constexpr int RJ = kMaxRows / NG;      // nodes per thread in the read-out
-    __shared__ float qs[kMaxRows][DP], ks[kMaxRows][DP];
-    __shared__ float vsm[kMaxRows][VW];
-    __shared__ float s0[D][VW];            // S0 rows (key index) restricted to this slice's value columns
+    constexpr int VW = D / VS;             // value columns per workgroup (<= 32)
+    constexpr int DP = D + 1;              // padded fp32 row stride
+    constexpr int BP = D + 8;              // padded bf16 row stride (16-byte rows, spread banks)
+    constexpr int KB = D / 16;             // MFMA k blocks
+    static_assert(VW <= 32 && D % 16 == 0, "slice shape");
+    __shared__ float qs[kMaxRows][DP], ks[kMaxRows][DP];            // raw projections
+    __shared__ __attribute__((aligned(16))) uint16_t qb[kMaxRows][BP], kb[kMaxRows][BP];   // normalised, bf16
+    __shared__ __attribute__((aligned(16))) uint16_t s0h[VW][BP], s0l[VW][BP];  // S0 slice, transposed, hi/lo
+    __shared__ float vsm[kMaxRows][VW];    // v, then (delta) the right-hand side and u
+    __shared__ float accq[kMaxRows][VW + 1], acck[DELTA ? kMaxRows : 1][VW + 1];   // S0^T q_t, S0^T k_t
     __shared__ float gsh[kMaxRows], gcs[kMaxRows], scale[2][kMaxRows];
+    __shared__ uint32_t ancs[kMaxRows];    // ancestor-or-self bits of each node
     __shared__ float coef[kMaxRows][kMaxRows + 1];
     // delta rule: write strengths and b_t e^{gc_t - gc_s} (k_t . k_s) for strict ancestors s
     __shared__ float bsh[DELTA ? kMaxRows : 1];
-    __shared__ float akk[DELTA ? kMaxRows : 1][kMaxRows + 1];
+    __shared__ __attribute__((aligned(16))) float akk[DELTA ? kMaxRows : 1][kMaxRows];
     const int h = blockIdx.x, v0 = blockIdx.y * VW, tid = threadIdx.x, n = r.n, QH = r.QH;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = tid >> 6, hf = lane >> 5, l32 = lane & 31;
 
-    // state slice: every load in flight before the stores
+    // state slice (every load in flight first); stored transposed as bf16
+    // hi + lo after the projection loads below are issued
+    constexpr int NV = D * VW / 4;         // float4 pieces
+    constexpr int PER = (NV + 255) / 256;
+    float4 st[PER];
     {
-        constexpr int NV = D * VW / 4;     // float4 pieces
-        constexpr int PER = (NV + 255) / 256;
         const float *S0 = r.S0 + (size_t)h * D * D + v0;
-        float4 tmp[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int idx = tid + i * 256;
-            tmp[i] = idx < NV ? *reinterpret_cast<const float4 *>(S0 + (size_t)(idx / (VW / 4)) * D + 4 * (idx % (VW / 4)))
-                              : float4{0.f, 0.f, 0.f, 0.f};
+            st[i] = idx < NV ? *reinterpret_cast<const float4 *>(S0 + (size_t)(idx / (VW / 4)) * D + 4 * (idx % (VW / 4)))
+                             : float4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    // projection outputs: split-K partials summed in k-range order, rounded
+    // to bf16 (the projection's output rounding).  Each batch sums 8 q and 8
+    // k elements per thread; the first also this slice's v columns (up to 4
+    // per thread) and the node's gate (and write strength), so one round of
+    // loads covers up to 16 nodes
+    constexpr int UQ = 8, UV = kMaxRows * VW / 256, UB = 2 * UQ + UV + 2;
+    static_assert(UV * 256 == kMaxRows * VW, "v elements per thread");
+    if (tid < n) ancs[tid] = r.meta->anc[r.row0 + tid];
+    for (int base = 0; base < n * D; base += UQ * 256) {
+        int mm[UB], cc[UB];
+        bool ok[UB];
+        float o[UB];
+#pragma unroll
+        for (int u = 0; u < UQ; ++u) {
+            const int idx = base + u * 256 + tid;
+            ok[u] = ok[UQ + u] = idx < n * D;
+            mm[u] = mm[UQ + u] = r.row0 + (idx < n * D ? idx / D : 0);
+            cc[u] = h * D + idx % D;
+            cc[UQ + u] = (QH + h) * D + idx % D;
         }
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int idx = tid + i * 256;
-            if (idx < NV) *reinterpret_cast<float4 *>(&s0[idx / (VW / 4)][4 * (idx % (VW / 4))]) = tmp[i];
+        for (int u = 0; u < UV; ++u) {
+            const int idx = u * 256 + tid;
+            ok[2 * UQ + u] = base == 0 && idx < n * VW;
+            mm[2 * UQ + u] = r.row0 + (idx < n * VW ? idx / VW : 0);
+            cc[2 * UQ + u] = (2 * QH + h) * D + v0 + idx % VW;
+        }
+        ok[UB - 2] = base == 0 && tid < n;
+        ok[UB - 1] = DELTA && base == 0 && tid < n;
+        mm[UB - 2] = mm[UB - 1] = r.row0 + (tid < n ? tid : 0);
+        cc[UB - 2] = r.a_col + h;
+        cc[UB - 1] = r.a_col + QH + h;
+        psum_batch<UB>(r.qkv_part, r.qkv_S, mm, cc, ok, o);
+#pragma unroll
+        for (int u = 0; u < UQ; ++u) {
+            const int idx = base + u * 256 + tid;
+            if (idx < n * D) {
+                qs[idx / D][idx % D] = bfround(o[u]);
+                ks[idx / D][idx % D] = bfround(o[UQ + u]);
+            }
+        }
+        if (base == 0) {
+#pragma unroll
+            for (int u = 0; u < UV; ++u) {
+                const int idx = u * 256 + tid;
+                if (idx < n * VW) vsm[idx / VW][idx % VW] = bfround(o[2 * UQ + u]);
+            }
+            if (tid < n) {
+                gsh[tid] = log_sigmoid(bfround(o[UB - 2]));
+                if constexpr (DELTA) bsh[tid] = 1.0f / (1.0f + expf(-bfround(o[UB - 1])));
+            }
         }
     }
-    // projection outputs: the split-K partials summed in k-range order and
-    // rounded to bf16 (the projection's output rounding)
-#pragma unroll 2
-    for (int idx = tid; idx < n * D; idx += 256) {
-        const int t = idx / D, d = idx % D;
-        qs[t][d] = bfround(psum(r.qkv_part, r.qkv_S, 1, 0, r.row0 + t, h * D + d));
-        ks[t][d] = bfround(psum(r.qkv_part, r.qkv_S, 1, 0, r.row0 + t, (QH + h) * D + d));
-    }
-    for (int idx = tid; idx < n * VW; idx += 256) {
-        const int t = idx / VW, c = idx % VW;
-        vsm[t][c] = bfround(psum(r.qkv_part, r.qkv_S, 1, 0, r.row0 + t, (2 * QH + h) * D + v0 + c));
-    }
-    if (tid < n) {
-        gsh[tid] = log_sigmoid(bfround(psum(r.a_part, r.a_S, 1, 0, r.row0 + tid, r.a_col + h)));
-        if constexpr (DELTA) {
-            const float b = bfround(psum(r.a_part, r.a_S, 1, 0, r.row0 + tid, r.a_col + QH + h));
-            bsh[tid] = 1.0f / (1.0f + expf(-b));
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int idx = tid + i * 256;
+        if (idx < NV) {
+            const int k = idx / (VW / 4), c0 = 4 * (idx % (VW / 4));
+            const float x[4] = {st[i].x, st[i].y, st[i].z, st[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint16_t hi = f2bf(x[e]);
+                s0h[c0 + e][k] = hi;
+                s0l[c0 + e][k] = f2bf(x[e] - bf2f(hi));
+            }
         }
     }
     __syncthreads();
-    // L2 norms of q and k rows: one wave per vector, shuffle reduction
-    for (int vec = wave; vec < 2 * n; vec += 4) {
-        const float *x = (vec & 1) ? ks[vec >> 1] : qs[vec >> 1];
+    // L2 norms of q and k rows: 8 lanes per vector (lane p takes elements
+    // p, p + 8, ...), then a fixed xor-shuffle tree over the 8
+    for (int base = 0; base < 2 * n * 8; base += 256) {
+        const int vec = (base + tid) >> 3, p = tid & 7;
         float ss = 0.f;
+        if (vec < 2 * n) {
+            const float *x = (vec & 1) ? ks[vec >> 1] : qs[vec >> 1];
 #pragma unroll
-        for (int d = lane; d < D; d += 64) ss += x[d] * x[d];
+            for (int d = p; d < D; d += 8) ss += x[d] * x[d];
+        }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-        if (lane == 0) scale[vec & 1][vec >> 1] = 1.0f / sqrtf(ss + r.eps);
+        for (int o = 4; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        if (p == 0 && vec < 2 * n) scale[vec & 1][vec >> 1] = 1.0f / sqrtf(ss + r.eps);
     }
     if (tid < n) {
         // cumulative gate over the ancestors, root first (ancestors have lower indices)
-        const uint32_t anc = r.meta->anc[r.row0 + tid];
+        const uint32_t anc = ancs[tid];
         float gc = 0.f;
-        for (int s = 0; s <= tid; ++s)
-            if ((anc >> s) & 1u) gc += gsh[s];
+#pragma unroll
+        for (int s = 0; s < kMaxRows; ++s)
+            if (s <= tid && ((anc >> s) & 1u)) gc += gsh[s];
         gcs[tid] = gc;
     }
     __syncthreads();
-    for (int idx = tid; idx < n * D; idx += 256) {
-        const int t = idx / D, d = idx % D;
-        qs[t][d] = bfround(qs[t][d] * scale[0][t]);
-        ks[t][d] = bfround(ks[t][d] * scale[1][t]);
+    // normalised q and k, rounded to bf16; rows beyond n are zero (MFMA padding)
+    for (int idx = tid; idx < kMaxRows * (D / 8); idx += 256) {
+        const int t = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
+        uint4 wq = {0u, 0u, 0u, 0u}, wk = {0u, 0u, 0u, 0u};
+        if (t < n) {
+            float xq[8], xk[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                xq[e] = qs[t][d0 + e] * scale[0][t];
+                xk[e] = ks[t][d0 + e] * scale[1][t];
+            }
+            wq = pack_bf8(xq);
+            wk = pack_bf8(xk);
+        }
+        *reinterpret_cast<uint4 *>(&qb[t][d0]) = wq;
+        *reinterpret_cast<uint4 *>(&kb[t][d0]) = wk;
     }
     __syncthreads();
-    for (int idx = tid; idx < n * n; idx += 256) {
-        const int t = idx / n, s = idx % n;
-        float cf = 0.f, ck = 0.f;
-        if ((r.meta->anc[r.row0 + t] >> s) & 1u) {
-            float dot = 0.f;
-            for (int d = 0; d < D; ++d) dot += qs[t][d] * ks[s][d];
-            const float decay = expf(gcs[t] - gcs[s]);
-            cf = decay * dot;
-            if constexpr (DELTA) {
-                if (s != t) {
-                    float dk = 0.f;
-                    for (int d = 0; d < D; ++d) dk += ks[t][d] * ks[s][d];
-                    ck = bsh[t] * decay * dk;
+    // the small products, one wave each: lane (hf, j = lane % 32) supplies k
+    // slots 16*kk + 8*hf + 0..7 of A row j and of B column j; accumulator r
+    // holds row acc_row(r, hf) of column j
+    const uint4 z = {0u, 0u, 0u, 0u};
+    if (wave == 0 || (DELTA && wave == 1)) {
+        // coef (wave 0): e^{gc_t - gc_s} (q_t . k_s) over ancestors-or-self s;
+        // akk (wave 1): b_t e^{gc_t - gc_s} (k_t . k_s) over strict ancestors
+        const uint16_t(*A)[BP] = wave == 0 ? qb : kb;
+        f32x16 acc = {};
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+            const uint4 a = *reinterpret_cast<const uint4 *>(&A[l32][16 * kk + 8 * hf]);
+            const uint4 b = *reinterpret_cast<const uint4 *>(&kb[l32][16 * kk + 8 * hf]);
+            acc = mfma32(a, b, acc);
+        }
+        const int s = l32;
+        if (s < n) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int t = acc_row(rr, hf);
+                if (t >= n) continue;
+                const bool anc = (ancs[t] >> s) & 1u;
+                const float decay = expf(gcs[t] - gcs[s]);
+                if (wave == 0) {
+                    coef[t][s] = anc ? decay * acc[rr] : 0.f;
+                } else if constexpr (DELTA) {
+                    akk[t][s] = (anc && s != t) ? bsh[t] * decay * acc[rr] : 0.f;
                 }
             }
         }
-        coef[t][s] = cf;
-        if constexpr (DELTA) akk[t][s] = ck;
+    } else if (wave == 2 || (DELTA && wave == 3)) {
+        // S0^T q_t (wave 2) and S0^T k_t (wave 3) for this slice's columns:
+        // A row = value column (S0 transposed), B column = node
+        const uint16_t(*B)[BP] = wave == 2 ? qb : kb;
+        f32x16 acc = {};
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+            const uint4 b = *reinterpret_cast<const uint4 *>(&B[l32][16 * kk + 8 * hf]);
+            const uint4 ah = l32 < VW ? *reinterpret_cast<const uint4 *>(&s0h[l32][16 * kk + 8 * hf]) : z;
+            const uint4 al = l32 < VW ? *reinterpret_cast<const uint4 *>(&s0l[l32][16 * kk + 8 * hf]) : z;
+            acc = mfma32(ah, b, acc);
+            acc = mfma32(al, b, acc);
+        }
+        const int t = l32;
+        if (t < n) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int c = acc_row(rr, hf);
+                if (c >= VW) continue;
+                if (wave == 2) accq[t][c] = acc[rr];
+                else if constexpr (DELTA) acck[t][c] = acc[rr];
+            }
+        }
     }
     __syncthreads();
-    // read-out: thread -> value column c, nodes t = grp, grp + NG, ...
-    const int c = tid % VW, grp = tid / VW;
-    float acc[RJ], acck[DELTA ? RJ : 1];
-#pragma unroll
-    for (int j = 0; j < RJ; ++j) acc[j] = 0.f;
-    if constexpr (DELTA) {
-#pragma unroll
-        for (int j = 0; j < RJ; ++j) acck[j] = 0.f;
-    }
-#pragma unroll 8
-    for (int k = 0; k < D; ++k) {
-        const float sv = s0[k][c];
-#pragma unroll
-        for (int j = 0; j < RJ; ++j) {
-            acc[j] += sv * qs[grp + j * NG][k];
-            if constexpr (DELTA) acck[j] += sv * ks[grp + j * NG][k];
-        }
-    }
     if constexpr (DELTA) {
         // right-hand side b_t (v_t - e^{gc_t} S0^T k_t), in place of v
-#pragma unroll
-        for (int j = 0; j < RJ; ++j) {
-            const int t = grp + j * NG;
-            if (t < n) vsm[t][c] = bsh[t] * (vsm[t][c] - expf(gcs[t]) * acck[j]);
+        for (int idx = tid; idx < n * VW; idx += 256) {
+            const int t = idx / VW, c = idx % VW;
+            vsm[t][c] = bsh[t] * (vsm[t][c] - expf(gcs[t]) * acck[t][c]);
         }
         __syncthreads();
-        // forward substitution, one thread per value column: ancestors have
-        // lower indices, so u_s is final when node t needs it
+        // forward substitution, one lane per value column, u in registers
+        // (ancestors have lower indices, so u_s is final when node t needs it)
         if (tid < VW) {
-            for (int t = 1; t < n; ++t) {
+            float u[kMaxRows];
+#pragma unroll
+            for (int t = 0; t < kMaxRows; ++t) {
+                if (t >= n) break;
                 float x = vsm[t][tid];
-                for (int s2 = 0; s2 < t; ++s2) x -= akk[t][s2] * vsm[s2][tid];
+#pragma unroll
+                for (int s4 = 0; s4 < t; s4 += 4) {
+                    const float4 a4 = *reinterpret_cast<const float4 *>(&akk[t][s4]);
+                    x -= a4.x * u[s4];
+                    if (s4 + 1 < t) x -= a4.y * u[s4 + 1];
+                    if (s4 + 2 < t) x -= a4.z * u[s4 + 2];
+                    if (s4 + 3 < t) x -= a4.w * u[s4 + 3];
+                }
+                u[t] = x;
                 vsm[t][tid] = x;
             }
         }
         __syncthreads();
     }
-#pragma unroll
-    for (int j = 0; j < RJ; ++j) {
-        const int t = grp + j * NG;
-        if (t >= n) continue;
-        float o = expf(gcs[t]) * acc[j];
+    // read-out o_t = e^{gc_t} S0^T q_t + sum over ancestors-or-self s of
+    // coef[t][s] u_s (u = v for the plain recurrence)
+    for (int idx = tid; idx < n * VW; idx += 256) {
+        const int t = idx / VW, c = idx % VW;
+        float o = expf(gcs[t]) * accq[t][c];
         for (int s = 0; s <= t; ++s) o += coef[t][s] * vsm[s][c];
         r.out[(size_t)(r.row0 + t) * QH * D + h * D + v0 + c] = f2bf(o);
         r.save_v[((size_t)t * QH + h) * D + v0 + c] = vsm[t][c];
@@ -1047,7 +1173,7 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     if (blockIdx.y == 0) {
         for (int idx = tid; idx < n * D; idx += 256) {
             const int t = idx / D, d = idx % D;
-            r.save_k[((size_t)t * QH + h) * D + d] = f2bf(ks[t][d]);
+            r.save_k[((size_t)t * QH + h) * D + d] = kb[t][d];
         }
         if (tid < n) r.save_gc[(size_t)tid * QH + h] = gcs[tid];
     }

@@ -491,7 +491,7 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
                 Req &q = c->reqs[reqs[r]];
                 RecurArgs ra{};
                 ra.qkv_part = c->gemm_partial; ra.qkv_S = Sq;
-                ra.a_part = c->gemm_partial; ra.a_S = Sq; ra.a_col = 3 * QH * D; ra.delta = delta;
+                ra.a_col = 3 * QH * D; ra.delta = delta;
                 ra.S0 = q.S[l]; ra.meta = c->d_meta; ra.out = c->ATT;
                 const size_t per = (size_t)kMaxRows * QH * D;
                 ra.save_k = q.save_k + rl * per;
