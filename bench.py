@@ -66,6 +66,11 @@ def parse():
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="> 0: every request samples (seeded Gumbel-max draws); 0 = greedy")
     ap.add_argument("--seed", type=int, default=42, help="sampling seed")
+    ap.add_argument("--prices", action="store_true",
+                    help="instead of the bench line, print a verify price file (StairCut's stair tables) "
+                         "for rows 1..32, chain and tree, at the --price-ctx lengths")
+    ap.add_argument("--price-ctx", default="1024,8192,32768")
+    ap.add_argument("--price-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", default="full",
                     help="'full' = the same four trees; 'n8' = one 8-node tree")
@@ -182,6 +187,8 @@ def main():
     shape = {"c1": synth.C1, "c2": synth.C2, "c3": synth.C3, "c3d": synth.C3D, "c4": synth.C2}[a.config]
     ns = {"c1": NS, "c2": NS, "c3": (16,), "c3d": (16,), "c4": (16,)}[a.config]
     ctxs = [a.ctx, a.ctx2] if a.config == "c4" else [a.ctx]
+    if a.prices:
+        return prices_main(a, shape)
     n_req = len(ctxs)
     mods_on = a.config == "c4"
     torch.cuda.init()
@@ -366,6 +373,32 @@ def main():
     if kernels:
         out["kernels"] = kernels
     print(json.dumps(out), flush=True)
+
+
+def prices_main(a, shape):
+    """StairCut's verify price file for this workload on this GPU: median
+    wall time of a verify (host call to host results) by context length,
+    kind and rows, in the pages' stair-table format (one JSON line)."""
+    import torch
+    import workloads
+    from greedy_draft_tree_amd.staircut import measure_prices
+    lens = [int(x) for x in a.price_ctx.split(",")]
+    torch.cuda.init()
+    print(f"[bench] building {shape.name} for prices at {lens}", file=sys.stderr, flush=True)
+    wl = workloads.build(shape, max_ctx=max(lens) + 64, max_req=1, weight_device="cuda")
+    workloads.load_context(wl, 0, max(lens), seed=3, state_seed=6)
+    t0 = time.perf_counter()
+    table, steps = {}, []
+    for L in lens:   # one length at a time, with progress
+        part = measure_prices(wl.tv, 0, [L], reps=a.price_reps)
+        table[str(L)] = part[str(L)]
+        steps.append(part["step_ms"])
+        print(f"[bench] prices at ctx {L} done ({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+    table["step_ms"] = float(np.median(steps))
+    table["measured"] = (f"bench.py --prices --config {a.config}: median of {a.price_reps} verifies per count "
+                         f"(host call to host results) on one MI355X, {time.strftime('%Y-%m-%d')}")
+    table["workload"] = shape.name
+    print(json.dumps(table), flush=True)
 
 
 def cpu_baseline(shape, wl, kv, ctx, trees, sample, ns):

@@ -9,6 +9,7 @@ import numpy as np
 
 TV_OK, TV_EINVAL, TV_ECAPACITY, TV_ESTATE, TV_EHIP = 0, -1, -2, -3, -4
 TV_MAX_NODES = 32
+TV_MAX_CANDIDATE = 256
 TV_LAYER_ATTN, TV_LAYER_RECUR, TV_LAYER_DELTA = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -19,7 +20,8 @@ _lib = None
 SYMBOLS = ("tv_create", "tv_destroy", "tv_last_error", "tv_bind", "tv_set_history",
            "tv_set_modifiers", "tv_set_sampling", "tv_prefill", "tv_verify_tree", "tv_verify_trees",
            "tv_accept_walk", "tv_commit", "tv_round", "tv_ctx_len", "tv_profile_enable",
-           "tv_profile_reset", "tv_profile_get", "tv_linear", "tv_head_top2", "tv_pack_weight")
+           "tv_profile_reset", "tv_profile_get", "tv_linear", "tv_head_top2", "tv_pack_weight",
+           "tv_staircut")
 
 
 class TVError(RuntimeError):
@@ -70,6 +72,7 @@ def load_library():
         "tv_linear": ([P, P, P, I, I, I, P, I], I),
         "tv_head_top2": ([P, P, I, P, P, P], I),
         "tv_pack_weight": ([P, P, I, I], I),
+        "tv_staircut": ([P, P, P, I, P, P, F, F, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

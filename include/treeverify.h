@@ -200,6 +200,32 @@ int tv_round(tv_ctx *ctx, int req, const int32_t *parents, const int32_t *tokens
              float *logits_dev, int32_t *argmax, float *gap_ulps, int32_t *path, int *path_len,
              int32_t *emitted, int *n_emitted);
 
+/* StairCut ("Drafters and tree verify", StairCut), host only: cut a
+ * candidate tree to the node count that maximises expected committed tokens
+ * per millisecond, (1 + min(sum of q over the kept nodes, their number)) /
+ * (verify price of the rows + draft_ms + commit_ms).
+ *   parents, q: n_nodes entries (1 <= n_nodes <= TV_MAX_CANDIDATE), node 0
+ *     the root (the last emitted token, parents[0] == -1, q[0] unused),
+ *     0 <= parents[i] < i; q[i] >= 0 is node i's path probability, capped
+ *     at 1 by the caller.
+ *   order: the n_nodes-1 drafted nodes in the drafter's score order (a
+ *     permutation of 1..n_nodes-1); each is admitted with the ancestors it
+ *     needs.  q and order may be NULL when n_nodes == 1 (the root alone).
+ *   price_tree_ms, price_chain_ms: verify price in ms by row count, index
+ *     1..TV_MAX_NODES (index 0 unused); the chain table prices a cut whose
+ *     nodes form one path.
+ * A cut ends at 7, 15, 23 or 31 nodes (8, 16, 24 or 32 rows: the longest
+ * admission prefix within that many nodes) or at the whole candidate when it
+ * has at most 31; among equal scores the smaller cut wins.  keep (host, at
+ * least 32 entries) receives the kept node ids in increasing order, root
+ * first; *n_keep their number (the rows of the verify); *score (may be
+ * NULL) the cut's tokens per ms.  TV_EINVAL on a malformed candidate, a
+ * non-finite price or cost, or a non-positive total price. */
+#define TV_MAX_CANDIDATE 256
+int tv_staircut(const int32_t *parents, const float *q, const int32_t *order, int n_nodes,
+                const float *price_tree_ms, const float *price_chain_ms, float draft_ms, float commit_ms,
+                int32_t *keep, int *n_keep, float *score);
+
 /* Committed context length of request `req` (negative TV_E* on error). */
 int tv_ctx_len(tv_ctx *ctx, int req);
 

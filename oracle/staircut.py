@@ -62,7 +62,11 @@ def staircut(parents: Sequence[int], q: Sequence[float], order: Sequence[int],
     for k in sorted(ends, key=lambda k: (len(prefixes[k]), k)):
         s = prefixes[k]
         nodes = len(s) - 1
-        gain = 1.0 + min(sum(float(q[i]) for i in s if i != 0), float(nodes))
+        qsum = 0.0
+        for i in sorted(s):                        # node order
+            if i != 0:
+                qsum += float(q[i])
+        gain = 1.0 + min(qsum, float(nodes))
         table = price_chain if is_chain(parents, s) else price_tree
         score = gain / (float(table[nodes + 1]) + draft_ms + commit_ms)
         if best is None or score > best:
