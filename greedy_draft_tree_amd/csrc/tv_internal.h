@@ -45,7 +45,8 @@ struct PassMeta {
 };
 
 // EPI_PARTIAL: write the fp32 partial sums only (a consumer kernel finishes them)
-enum Epi { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3, EPI_PARTIAL = 4 };
+// EPI_F32 (dense GEMM only): the fp32 sums
+enum Epi { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3, EPI_PARTIAL = 4, EPI_F32 = 5 };
 
 struct GemmArgs {
     const uint16_t *X;  // [M, K] bf16 activations, row stride ldx
@@ -150,6 +151,8 @@ hipError_t launch_resid_norm(hipStream_t s, const float *P, int S, int M, int H,
                              uint16_t *X, uint16_t *Y);
 hipError_t launch_gemm(hipStream_t s, int epi, const GemmArgs &a, int splits);
 hipError_t launch_splitk_reduce(hipStream_t s, int epi, const GemmArgs &a, int splits);
+// many activation rows (M > 32): X [M, K] row stride ldx, epilogues BF16, RESID, SWIGLU, F32
+hipError_t launch_gemm_dense(hipStream_t s, int epi, const GemmArgs &a);
 hipError_t launch_pack(hipStream_t s, const uint16_t *src, uint16_t *dst, int N, int K, int t0, int nt);
 hipError_t launch_rope_kv(hipStream_t s, const RopeArgs &a);
 hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a);

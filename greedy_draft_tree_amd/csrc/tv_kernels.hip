@@ -488,6 +488,142 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     }
 }
 
+// ------------------------------------------------------------ dense GEMM
+// Y[m, n] = sum_k X[m, k] W[n, k] for many activation rows (prefill
+// chunks).  The same packed weights and LDS staging as k_gemm, but a
+// workgroup covers MG groups of 32 activation rows (grid.x, fastest, so the
+// workgroups that share a weight block run together and its second and later
+// reads hit the caches) and each wave reuses its weight tile across all of
+// them: weights are read once per 32*MG rows and each k step carries MG
+// MFMAs per weight load.  No split-K: the grid has enough workgroups.
+template <int EPI, int MG>
+__global__ __launch_bounds__(256) void k_gemm_dense(GemmArgs g) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    constexpr int U = 2;   // k steps per LDS stage
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][U][MG][32 * 64];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hf = lane >> 5, c = lane & 31;
+    const int N = g.N, K = g.K;
+    const int ntiles = (N + 31) >> 5;
+    const int tile = blockIdx.y * 4 + wave;
+    const bool tok = tile < ntiles;
+    const int nr = tok ? min(32, N - tile * 32) : 0;
+    const int nsteps = (K + 63) >> 6;
+    const int m0 = blockIdx.x * 32 * MG;
+    const uint16_t *tb = g.W + (size_t)(tok ? tile : 0) * 32 * K;
+    const uint16_t *tb2 = DUAL ? g.W2 + (size_t)(tok ? tile : 0) * 32 * K : nullptr;
+    const uint4 z = {0u, 0u, 0u, 0u};
+
+    const int br = tid >> 3, bsw = (tid & 7) ^ (br & 7);
+    typedef __attribute__((address_space(3))) uint8_t lds_byte;
+    auto bissue = [&](int buf, int sf) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int gi = 0; gi < MG; ++gi) {
+                const int s = sf + u, k = s * 64 + bsw * 8, row = m0 + gi * 32 + br;
+                const bool ok = s < nsteps && row < g.M && k < K;
+                const void *src = ok ? static_cast<const void *>(g.X + (size_t)row * g.ldx + k)
+                                     : static_cast<const void *>(g.zeros);
+                lds_byte *dst = (lds_byte *)(&Bs[buf][u][gi][0]) + wave * 1024;
+                __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+            }
+        }
+    };
+
+    f32x16 acc[MG], acc2[DUAL ? MG : 1];
+#pragma unroll
+    for (int gi = 0; gi < MG; ++gi) acc[gi] = f32x16{};
+    if constexpr (DUAL) {
+#pragma unroll
+        for (int gi = 0; gi < MG; ++gi) acc2[gi] = f32x16{};
+    }
+    bissue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int buf = 0;
+    for (int sg = 0; sg < nsteps; sg += U, buf ^= 1) {
+        if (sg + U < nsteps) bissue(buf ^ 1, sg + U);
+        uint4 a[U][4], a2[DUAL ? U : 1][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = sg + u;
+            const bool full = (nr == 32) && (s * 64 + 64 <= K);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                long off;
+                if (s >= nsteps || !tok) off = -1;
+                else if (full) off = (long)s * 2048 + q * 512 + lane * 8;
+                else off = packed_piece(s, q, hf, c, nr, K);
+                a[u][q] = off >= 0 ? ld16(tb + off) : z;
+                if constexpr (DUAL) a2[u][q] = off >= 0 ? ld16(tb2 + off) : z;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ch = 4 * hf + q;
+#pragma unroll
+                for (int gi = 0; gi < MG; ++gi) {
+                    const uint4 b = *reinterpret_cast<const uint4 *>(&Bs[buf][u][gi][c * 64 + ((ch ^ (c & 7)) << 3)]);
+                    acc[gi] = mfma32(a[u][q], b, acc[gi]);
+                    if constexpr (DUAL) acc2[gi] = mfma32(a2[u][q], b, acc2[gi]);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    if (!tok) return;
+    // epilogue: accumulators r = 4j..4j+3 hold 4 consecutive output columns
+#pragma unroll
+    for (int gi = 0; gi < MG; ++gi) {
+        const int m = m0 + gi * 32 + c;
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n0 = tile * 32 + 8 * j + 4 * hf;
+            float v[4], v2[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = acc[gi][4 * j + e];
+                if constexpr (DUAL) v2[e] = acc2[gi][4 * j + e];
+            }
+            if constexpr (EPI == EPI_F32) {
+                float *y = g.Yf + (size_t)m * g.ldyf + n0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n0 + e < N) y[e] = v[e];
+            } else {
+                uint16_t *y = g.Y + (size_t)m * g.ldy + n0;
+                uint16_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (n0 + e >= N) continue;
+                    if constexpr (EPI == EPI_BF16) {
+                        o[e] = f2bf(v[e]);
+                    } else if constexpr (EPI == EPI_RESID) {
+                        o[e] = f2bf(bf2f(y[e]) + bfround(v[e]));
+                    } else {
+                        const float gt = bfround(v[e]), up = bfround(v2[e]);
+                        o[e] = f2bf(gt / (1.0f + expf(-gt)) * up);
+                    }
+                }
+                if (n0 + 3 < N && (g.ldy & 3) == 0) {
+                    *reinterpret_cast<uint2 *>(y) = uint2{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                                                          (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n0 + e < N) y[e] = o[e];
+                }
+            }
+        }
+    }
+}
+
 // Split-K finish: one thread per output element adds its S partials in
 // k-range order and applies the element's epilogue.
 template <int EPI>
@@ -1271,6 +1407,24 @@ hipError_t launch_gemm(hipStream_t s, int epi, const GemmArgs &a, int splits) {
     case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm<EPI_SWIGLU>), grid, block, 0, s, a); break;
     case EPI_HEAD: hipLaunchKernelGGL((k_gemm<EPI_HEAD>), grid, block, 0, s, a); break;
     case EPI_PARTIAL: hipLaunchKernelGGL((k_gemm<EPI_PARTIAL>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_dense(hipStream_t s, int epi, const GemmArgs &a) {
+    if (a.M < 1 || a.N < 1 || a.K < 8 || a.K % 8) return hipErrorInvalidValue;
+    const int wblocks = ((a.N + 31) / 32 + 3) / 4;
+    const dim3 block(256);
+    switch (epi) {
+    case EPI_BF16:
+        hipLaunchKernelGGL((k_gemm_dense<EPI_BF16, 4>), dim3((a.M + 127) / 128, wblocks), block, 0, s, a); break;
+    case EPI_RESID:
+        hipLaunchKernelGGL((k_gemm_dense<EPI_RESID, 4>), dim3((a.M + 127) / 128, wblocks), block, 0, s, a); break;
+    case EPI_F32:
+        hipLaunchKernelGGL((k_gemm_dense<EPI_F32, 4>), dim3((a.M + 127) / 128, wblocks), block, 0, s, a); break;
+    case EPI_SWIGLU:
+        hipLaunchKernelGGL((k_gemm_dense<EPI_SWIGLU, 2>), dim3((a.M + 63) / 64, wblocks), block, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

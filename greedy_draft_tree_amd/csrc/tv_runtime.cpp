@@ -938,13 +938,18 @@ int tv_prefill(tv_ctx *c, int req, const int32_t *tokens, int n, int32_t *argmax
 int tv_linear(tv_ctx *c, const void *x, const void *w, int M, int N, int K, void *y, int y_fp32) {
     if (!c) return TV_EINVAL;
     if (!x || !w || !y) return fail(c, TV_EINVAL, "null operand");
-    if (M < 1 || M > kMaxRows || N < 1 || K < 8 || K % 8)
+    if (M < 1 || N < 1 || K < 8 || K % 8)
         return fail(c, TV_EINVAL, "shape M=%d N=%d K=%d not supported", M, N, K);
-    if (y_fp32 && N > c->m.vocab) return fail(c, TV_EINVAL, "fp32 output needs N <= vocab");
+    if (y_fp32 && M <= kMaxRows && N > c->m.vocab) return fail(c, TV_EINVAL, "fp32 output needs N <= vocab");
     GemmArgs g{};
     g.X = (const uint16_t *)x; g.ldx = K; g.W = (const uint16_t *)w; g.M = M; g.N = N; g.K = K;
+    g.zeros = c->zeros;
     hipStream_t s = c->stream;
-    if (y_fp32) {
+    if (M > kMaxRows) {   // many rows: the dense (prefill) GEMM
+        if (y_fp32) { g.Yf = (float *)y; g.ldyf = N; }
+        else { g.Y = (uint16_t *)y; g.ldy = N; }
+        LAUNCH(c, "gemm_dense", launch_gemm_dense(s, y_fp32 ? EPI_F32 : EPI_BF16, g));
+    } else if (y_fp32) {
         g.Yf = (float *)y; g.ldyf = N; g.part = c->part;
         GEMM(c, "gemm_linear_f32", EPI_HEAD, g);
     } else {

@@ -231,10 +231,12 @@ int tv_ctx_len(tv_ctx *ctx, int req);
 
 /* Kernel-level calls: the pass's projection and head kernels on caller-given
  * device operands, for per-kernel tests and bandwidth measurement.
- * tv_linear: x [M, K] bf16 (row-major), w [N, K] bf16 packed (tv_pack_weight), M in [1, 32], K a
+ * tv_linear: x [M, K] bf16 (row-major), w [N, K] bf16 packed (tv_pack_weight), M >= 1, K a
  * multiple of 8; y_fp32 == 0 writes bf16(x w^T) to y [M, N] bf16, y_fp32 != 0
- * writes the fp32 sums to y [M, N] fp32 (N <= vocab).  The k order of every
- * output is fixed by (N, K) and the output kind alone, never by M.
+ * writes the fp32 sums to y [M, N] fp32 (N <= vocab when M <= 32).  M <= 32
+ * runs the verify pass's skinny kernel: the k order of every output is fixed
+ * by (N, K) and the output kind alone, never by M.  M > 32 runs the dense
+ * (prefill) kernel, whose k order is fixed by K alone.
  * tv_head_top2: the bound "head" on x [M, hidden] bf16: fp32 logits [M,
  * vocab] to logits_dev, argmax and gap (host, M entries) as tv_verify_tree
  * returns them, with no score modifiers.  Both synchronise the stream. */

@@ -185,3 +185,44 @@ def test_head_rows_bitwise_invariant(tv, head):
         assert torch.equal(out, full[rows])
         np.testing.assert_array_equal(am, am_full[rows])
         np.testing.assert_array_equal(gap, gap_full[rows])
+
+
+# ------------------------------------------------------------ dense (prefill) GEMM
+
+@pytest.mark.parametrize("M,N,K", [(33, 512, 256), (130, 1056, 1024), (300, 5120, 5120), (97, 17408, 512)])
+def test_dense_linear_fp32_and_bf16(tv, M, N, K):
+    """More than 32 rows run the dense kernel: fp32 sums within Higham's
+    bound, bf16 outputs correctly rounded up to that bound."""
+    x, w = _operands(M, N, K, 300 + M)
+    ref, absum = _ref(x, w)
+    tv.pack_weight(w)
+    gam = K * U / (1 - K * U)
+    y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    tv.linear(x, w, y)
+    err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+    assert (err <= gam * absum + 1e-30).all(), float((err / (gam * absum + 1e-30)).max())
+    yb = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tv.linear(x, w, yb)
+    want = oracle.bf16_round(ref)
+    got = yb.cpu().to(torch.float64).numpy()
+    bad = got != want
+    mid = (got + want) / 2
+    near = np.abs(ref - mid) <= gam * absum + 2 * U * np.abs(ref)
+    assert (~bad | near).all(), int((bad & ~near).sum())
+    # the bf16 output is the fp32 sum rounded once
+    assert torch.equal(yb, y.to(torch.bfloat16))
+
+
+def test_dense_linear_rows_bitwise_invariant(tv):
+    """A row's dense result does not depend on the row count or its slot."""
+    N, K = 2048, 1024
+    x, w = _operands(300, N, K, 7)
+    tv.pack_weight(w)
+    full = torch.empty(300, N, dtype=torch.float32, device="cuda")
+    tv.linear(x, w, full)
+    rng = np.random.default_rng(1)
+    for M in (33, 64, 127, 129, 257):
+        perm = torch.from_numpy(rng.permutation(300)[:M]).cuda()
+        y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+        tv.linear(x[perm].contiguous(), w, y)
+        assert torch.equal(y, full[perm]), M
