@@ -18,7 +18,7 @@ _lib = None
 
 # every symbol include/treeverify.h declares
 SYMBOLS = ("tv_create", "tv_destroy", "tv_last_error", "tv_bind", "tv_set_history",
-           "tv_set_modifiers", "tv_set_sampling", "tv_prefill", "tv_verify_tree", "tv_verify_trees",
+           "tv_set_modifiers", "tv_set_sampling", "tv_prefill", "tv_prefill_dense", "tv_verify_tree", "tv_verify_trees",
            "tv_accept_walk", "tv_commit", "tv_round", "tv_ctx_len", "tv_profile_enable",
            "tv_profile_reset", "tv_profile_get", "tv_linear", "tv_head_top2", "tv_pack_weight",
            "tv_staircut")
@@ -60,6 +60,7 @@ def load_library():
         "tv_set_modifiers": ([P, I, F, P, P, I, P], I),
         "tv_set_sampling": ([P, I, F, ctypes.c_uint64], I),
         "tv_prefill": ([P, I, P, I, P], I),
+        "tv_prefill_dense": ([P, I, P, I, I, P], I),
         "tv_verify_tree": ([P, I, P, P, I, P, P, P], I),
         "tv_verify_trees": ([P, I, P, P, P, P, P, P, P], I),
         "tv_accept_walk": ([P, P, P, I, P, P, P, P], I),
@@ -205,6 +206,15 @@ class TreeVerifier:
         out = ctypes.c_int32(0)
         self._check(self.lib.tv_prefill(self.h, req, _ptr(t), int(t.size), ctypes.byref(out)),
                     "tv_prefill")
+        return int(out.value)
+
+    def prefill_dense(self, req: int, tokens: Sequence[int], chunk: int = 512) -> int:
+        """tv_prefill_dense: the prompt on the dense prefill kernels, chunked
+        on the grid of multiples of `chunk`; returns the last row's token."""
+        t = _i32(tokens)
+        out = ctypes.c_int32(0)
+        self._check(self.lib.tv_prefill_dense(self.h, req, _ptr(t), int(t.size), int(chunk), ctypes.byref(out)),
+                    "tv_prefill_dense")
         return int(out.value)
 
     def verify_tree(self, req: int, parents, tokens, logits=None):

@@ -90,15 +90,23 @@ struct AttnArgs {
     int row0, n, ctx, cap, G, n_qhead, ns, n_ctx_split;
     int span;           // cache keys per split (a multiple of kAttnChunk)
     float scale;
+    // prefill (zrows > 0): grid.z blocks of zrows consecutive rows of one
+    // chain; block z covers rows [z*zrows, min(M, (z+1)*zrows)) at cache
+    // slots ctx + row, sees ctx + z*zrows cache keys before it, and sizes its
+    // own splits from that; ns is then the partial stride (the most splits
+    // any block has, plus one)
+    int zrows, M;
+    int ztarget;        // prefill: splits of the cache keys per block (about)
 };
 
-// Cache keys per attention split: about 32 splits per KV head, in whole
-// LDS chunks; a function of the context length only.
-inline int attn_span(int ctx) {
+// Cache keys per attention split for about `splits` splits, in whole LDS
+// chunks.  A verify takes 32 (a function of the context length only).
+__host__ __device__ inline int attn_span_n(int ctx, int splits) {
     const int chunks = (ctx + kAttnChunk - 1) / kAttnChunk;
-    const int per = (chunks + 31) / 32;
+    const int per = (chunks + splits - 1) / splits;
     return (per < 1 ? 1 : per) * kAttnChunk;
 }
+__host__ __device__ inline int attn_span(int ctx) { return attn_span_n(ctx, 32); }
 
 struct RopeArgs {
     const float *part;   // QKV projection partial sums (row-contiguous split-K layout)
@@ -157,6 +165,13 @@ hipError_t launch_pack(hipStream_t s, const uint16_t *src, uint16_t *dst, int N,
 hipError_t launch_rope_kv(hipStream_t s, const RopeArgs &a);
 hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a);
 hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t *out);
+// prefill row kernels on M rows: X = emb[tok] (when tok is given), Y = RMSNorm(X) with weights w
+hipError_t launch_norm_dense(hipStream_t s, const int32_t *tok, const uint16_t *emb, uint16_t *X, const uint16_t *w,
+                             float eps, uint16_t *Y, int M, int H);
+// prefill RoPE on the dense QKV output qkv [M, ldq] bf16: rows at positions and cache slots pos0 + i
+hipError_t launch_rope_dense(hipStream_t s, const uint16_t *qkv, int ldq, int M, int pos0, int QH, int KVH, int D,
+                             const float *cosT, const float *sinT, uint16_t *q_out, uint16_t *Kc, uint16_t *Vc,
+                             int cap);
 // Per-row result of a pass: argmax and the gap's bits, written by one 8-byte
 // store into device-visible host memory.  The host fills the records with
 // kResultEmpty before a pass and waits until every row's record has changed.

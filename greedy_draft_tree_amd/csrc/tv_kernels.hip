@@ -757,6 +757,74 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
     }
 }
 
+// Prefill RoPE: the same rotation on the dense QKV projection's bf16
+// output; row i of the chunk is at position and cache slot pos0 + i.
+__global__ __launch_bounds__(256) void k_rope_dense(const uint16_t *__restrict__ qkv, int ldq, int pos0, int QH,
+                                                    int KVH, int D, const float *__restrict__ cosT,
+                                                    const float *__restrict__ sinT, uint16_t *__restrict__ q_out,
+                                                    uint16_t *__restrict__ Kc, uint16_t *__restrict__ Vc, int cap) {
+    const int i = blockIdx.x, half = D / 2;
+    const int u = blockIdx.y * 256 + threadIdx.x;
+    const int nq = QH * half, nk = KVH * half, nv = KVH * D;
+    if (u >= nq + nk + nv) return;
+    const int pos = pos0 + i;
+    const uint16_t *x = qkv + (size_t)i * ldq;
+    if (u < nq + nk) {
+        const bool isq = u < nq;
+        const int uu = isq ? u : u - nq;
+        const int h = uu / half, p = uu % half;
+        const int col = (isq ? 0 : QH * D) + h * D + p;
+        const float x0 = bf2f(x[col]), x1 = bf2f(x[col + half]);
+        const float c = cosT[(size_t)pos * half + p], s = sinT[(size_t)pos * half + p];
+        uint16_t *o = isq ? q_out + (size_t)i * QH * D + h * D : Kc + ((size_t)h * cap + pos) * D;
+        o[p] = f2bf(x0 * c - x1 * s);
+        o[p + half] = f2bf(x1 * c + x0 * s);
+    } else {
+        const int uu = u - nq - nk, h = uu / D, d = uu % D;
+        Vc[((size_t)h * cap + pos) * D + d] = x[(QH + KVH) * D + h * D + d];
+    }
+}
+
+// Prefill RMSNorm of M rows (one workgroup per row, one thread per 8
+// columns, the same fixed reduction order as k_row_norm); with `tok` the
+// rows are first gathered from the embedding into X.
+__global__ __launch_bounds__(1024) void k_norm_dense(const int32_t *__restrict__ tok, const uint16_t *__restrict__ emb,
+                                                     uint16_t *X, const uint16_t *__restrict__ w, float eps,
+                                                     uint16_t *__restrict__ Y, int H) {
+    __shared__ float red[16];
+    const int m = blockIdx.x, t = threadIdx.x, n0 = 8 * t;
+    const bool ok = n0 < H;
+    const uint4 zz = {0u, 0u, 0u, 0u};
+    uint4 v;
+    if (tok) {
+        v = ok ? ld16(emb + (size_t)tok[m] * H + n0) : zz;
+        if (ok) *reinterpret_cast<uint4 *>(X + (size_t)m * H + n0) = v;
+    } else {
+        v = ok ? ld16(X + (size_t)m * H + n0) : zz;
+    }
+    const uint4 wv = ok ? ld16(w + n0) : zz;
+    const uint16_t *ve = reinterpret_cast<const uint16_t *>(&v);
+    float x[8], ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        x[e] = bf2f(ve[e]);
+        ss += x[e] * x[e];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((t & 63) == 0) red[t >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += red[i];
+    const float scale = 1.0f / sqrtf(tot / (float)H + eps);
+    if (!ok) return;
+    const uint16_t *we = reinterpret_cast<const uint16_t *>(&wv);
+    uint32_t yw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) yw[e] = f2bf2(x[2 * e] * scale * bf2f(we[2 * e]), x[2 * e + 1] * scale * bf2f(we[2 * e + 1]));
+    *reinterpret_cast<uint4 *>(Y + (size_t)m * H + n0) = uint4{yw[0], yw[1], yw[2], yw[3]};
+}
+
 // ---------------------------------------------------------- tree attention
 // Grid (split, kv head); one wave per block of 32 query rows, where row
 // r = node*G + head-in-group.  Splits 0..n_ctx_split-1 each take `span`
@@ -792,22 +860,34 @@ __global__ __launch_bounds__(64 * (kAttnComputeWaves + kAttnLoaderWaves)) void k
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][CH * D];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VSTR];
 
-    const int split = blockIdx.x, kvh = blockIdx.y;
+    const int split = blockIdx.x, kvh = blockIdx.y, z = blockIdx.z;
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int hf = lane >> 5, c = lane & 31;
-    const int G = a.G, n = a.n;
+    const int G = a.G;
+    // this block's rows, context and splits (a prefill block of a chain, or the pass's tree)
+    int n = a.n, row0 = a.row0, ctx = a.ctx, span = a.span, nsplit = a.n_ctx_split;
+    if (a.zrows > 0) {
+        row0 = z * a.zrows;
+        n = min(a.zrows, a.M - row0);
+        ctx = a.ctx + row0;
+        span = attn_span_n(ctx, a.ztarget);
+        nsplit = (ctx + span - 1) / span;
+        if (split > nsplit) return;            // a block with fewer splits: the whole workgroup leaves
+    }
     const int R = G * n;
     const int cw = (R + 31) >> 5;              // compute waves; any further waves only load
     const bool loaders = nthr > cw * 64;
-    const bool tree = split >= a.n_ctx_split;
-    const int key0 = tree ? a.ctx : split * a.span;
-    const int nkeys = tree ? n : min(a.span, a.ctx - key0);
+    const bool tree = split >= nsplit;
+    const int key0 = tree ? ctx : split * span;
+    const int nkeys = tree ? n : min(span, ctx - key0);
     const int nch = (nkeys + CH - 1) / CH;
     const int row = wave * 32 + c;             // this lane's query row (compute waves)
     const bool rowok = wave < cw && row < R;
     const int t = rowok ? row / G : 0, hh = rowok ? row % G : 0;
-    const uint32_t anc = a.meta->anc[a.row0 + t];
+    // keys of the block's own rows visible to row t: its ancestors and itself
+    // (a prefill chain: rows 0..t)
+    const uint32_t anc = a.zrows > 0 ? (t >= 31 ? 0xffffffffu : ((2u << t) - 1u)) : a.meta->anc[a.row0 + t];
 
     const uint16_t *Kb = a.Kc + (size_t)kvh * a.cap * D;
     const uint16_t *Vb = a.Vc + (size_t)kvh * a.cap * D;
@@ -848,7 +928,7 @@ __global__ __launch_bounds__(64 * (kAttnComputeWaves + kAttnLoaderWaves)) void k
     // the wave's 32 query rows, dims 16kk + 8hf .. +8 for each kk
     uint4 q[NKK];
     {
-        const uint16_t *qr = a.Q + (size_t)(a.row0 + t) * a.n_qhead * D + (size_t)(kvh * G + hh) * D;
+        const uint16_t *qr = a.Q + (size_t)(row0 + t) * a.n_qhead * D + (size_t)(kvh * G + hh) * D;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk)
             q[kk] = rowok ? ld16(qr + kk * 16 + hf * 8) : uint4{0u, 0u, 0u, 0u};
@@ -957,7 +1037,7 @@ __global__ __launch_bounds__(64 * (kAttnComputeWaves + kAttnLoaderWaves)) void k
 
     if (!rowok || hf > 1) return;
     const int RP = kMaxRows * kMaxGroup;
-    const size_t pb = ((size_t)kvh * a.ns + split) * RP + row;
+    const size_t pb = (((size_t)z * gridDim.y + kvh) * a.ns + split) * RP + row;
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
 #pragma unroll
@@ -972,11 +1052,17 @@ __global__ __launch_bounds__(64 * (kAttnComputeWaves + kAttnLoaderWaves)) void k
 template <int D>
 __global__ __launch_bounds__(D) void k_attn_combine(AttnArgs a, uint16_t *__restrict__ out) {
     __shared__ float ms[64], wl[64], ws[64];
-    const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+    const int t = blockIdx.x, h = blockIdx.y, z = blockIdx.z, d = threadIdx.x;
     const int G = a.G, kvh = h / G, row = t * G + (h % G);
     const int RP = kMaxRows * kMaxGroup;
-    const int ns = a.ns;
-    const size_t b0 = (size_t)kvh * ns * RP + row;
+    int ns = a.ns, row0 = a.row0;
+    if (a.zrows > 0) {   // a prefill block: its own split count
+        row0 = z * a.zrows;
+        if (row0 + t >= a.M) return;
+        const int ctx = a.ctx + row0, span = attn_span_n(ctx, a.ztarget);
+        ns = (ctx + span - 1) / span + 1;
+    }
+    const size_t b0 = (((size_t)z * (a.n_qhead / G) + kvh) * a.ns) * RP + row;
     if (d < ns) {
         ms[d] = a.pm[b0 + (size_t)d * RP];
         wl[d] = a.pl[b0 + (size_t)d * RP];
@@ -1000,7 +1086,7 @@ __global__ __launch_bounds__(D) void k_attn_combine(AttnArgs a, uint16_t *__rest
             }
         }
     }
-    out[(size_t)(a.row0 + t) * a.n_qhead * D + h * D + d] = f2bf(O / L);
+    out[(size_t)(row0 + t) * a.n_qhead * D + h * D + d] = f2bf(O / L);
 }
 
 // ------------------------------------------------------- gated recurrence
@@ -1455,12 +1541,31 @@ hipError_t launch_rope_kv(hipStream_t s, const RopeArgs &a) {
     return hipGetLastError();
 }
 
+hipError_t launch_rope_dense(hipStream_t s, const uint16_t *qkv, int ldq, int M, int pos0, int QH, int KVH, int D,
+                             const float *cosT, const float *sinT, uint16_t *q_out, uint16_t *Kc, uint16_t *Vc,
+                             int cap) {
+    if (M < 1 || pos0 + M > cap) return hipErrorInvalidValue;
+    const int units = QH * D / 2 + KVH * D / 2 + KVH * D;
+    hipLaunchKernelGGL(k_rope_dense, dim3(M, (units + 255) / 256), dim3(256), 0, s, qkv, ldq, pos0, QH, KVH, D, cosT,
+                       sinT, q_out, Kc, Vc, cap);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_dense(hipStream_t s, const int32_t *tok, const uint16_t *emb, uint16_t *X, const uint16_t *w,
+                             float eps, uint16_t *Y, int M, int H) {
+    if (M < 1 || H % 8 || H > 8 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_norm_dense, dim3(M), dim3(row_threads(H)), 0, s, tok, emb, X, w, eps, Y, H);
+    return hipGetLastError();
+}
+
 hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a) {
     const int rb = (a.G * a.n + 31) / 32;   // compute waves
     if (rb > kAttnComputeWaves) return hipErrorInvalidValue;
     // loader waves only when a split spans more than one chunk of keys
     const int lw = a.span > kAttnChunk ? kAttnLoaderWaves : 0;
-    const dim3 grid(a.ns, a.n_qhead / a.G), block(64 * (rb + lw));
+    const int nz = a.zrows > 0 ? (a.M + a.zrows - 1) / a.zrows : 1;
+    if (a.zrows > 0 && (a.zrows > kMaxRows || a.M < 1)) return hipErrorInvalidValue;
+    const dim3 grid(a.ns, a.n_qhead / a.G, nz), block(64 * (rb + lw));
     if (D == 128) hipLaunchKernelGGL(k_attn<128>, grid, block, 0, s, a);
     else if (D == 64) hipLaunchKernelGGL(k_attn<64>, grid, block, 0, s, a);
     else return hipErrorInvalidValue;
@@ -1468,7 +1573,7 @@ hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a) {
 }
 
 hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t *out) {
-    const dim3 grid(a.n, a.n_qhead);
+    const dim3 grid(a.n, a.n_qhead, a.zrows > 0 ? (a.M + a.zrows - 1) / a.zrows : 1);
     if (D == 128) hipLaunchKernelGGL(k_attn_combine<128>, grid, dim3(128), 0, s, a, out);
     else if (D == 64) hipLaunchKernelGGL(k_attn_combine<64>, grid, dim3(64), 0, s, a, out);
     else return hipErrorInvalidValue;

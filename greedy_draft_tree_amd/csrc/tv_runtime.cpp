@@ -77,6 +77,11 @@ struct tv_ctx {
     uint16_t *X = nullptr, *XN = nullptr, *QR = nullptr, *ATT = nullptr, *ACT = nullptr;
     float *logits = nullptr;  // [32, V] when the caller passes none
     void *zeros = nullptr;    // 256 zero bytes
+    // dense prefill scratch (allocated on first use, for pf_rows rows)
+    int pf_rows = 0;
+    uint16_t *pX = nullptr, *pXN = nullptr, *pQKV = nullptr, *pQR = nullptr, *pATT = nullptr, *pACT = nullptr;
+    int32_t *pTok = nullptr, *h_tok = nullptr;
+    float *ppo = nullptr, *ppm = nullptr, *ppl = nullptr;
     Top2 *part = nullptr;
     float *po = nullptr, *pm = nullptr, *pl = nullptr;
     float *rope_cos = nullptr, *rope_sin = nullptr;
@@ -668,7 +673,8 @@ void tv_destroy(tv_ctx *c) {
     if (c->stream) hipStreamSynchronize(c->stream);
     else hipDeviceSynchronize();
     void *dev[] = {c->X, c->XN, c->QR, c->ATT, c->ACT, c->zeros, c->logits, c->part, c->po, c->pm, c->pl,
-                   c->rope_cos, c->rope_sin, c->d_meta, c->gemm_partial};
+                   c->rope_cos, c->rope_sin, c->d_meta, c->gemm_partial, c->pX, c->pXN, c->pQKV, c->pQR,
+                   c->pATT, c->pACT, c->pTok, c->ppo, c->ppm, c->ppl};
     for (void *p : dev)
         if (p) hipFree(p);
     for (auto &q : c->reqs) {
@@ -681,7 +687,7 @@ void tv_destroy(tv_ctx *c) {
         if (q.save_v) hipFree(q.save_v);
         if (q.save_gc) hipFree(q.save_gc);
     }
-    void *host[] = {c->h_meta, c->h_res};
+    void *host[] = {c->h_meta, c->h_res, c->h_tok};
     for (void *p : host)
         if (p) hipHostFree(p);
     for (auto &r : c->recs) {
@@ -911,6 +917,179 @@ int tv_round(tv_ctx *c, int req, const int32_t *parents, const int32_t *tokens, 
     rc = tv_accept_walk(parents, tokens, argmax, n_nodes, path, path_len, emitted, n_emitted);
     if (rc) return fail(c, rc, "accept walk rejected the tree");
     return tv_commit(c, req, path, *path_len);
+}
+
+// ------------------------------------------------------------ dense prefill
+namespace {
+
+constexpr int kPrefillMaxChunk = 2048;
+constexpr int kPrefillBlock = 32;   // rows of one attention block (a chain)
+
+// Target splits of the cache keys per attention block: about 1024
+// workgroups over all blocks and KV heads (at least one split each, at most
+// 32 as in a verify, so a combine merges at most 33 partials).
+int prefill_splits(int nz, int KVH) { return std::min(32, std::max(1, 1024 / (nz * KVH))); }
+
+int ensure_prefill(tv_ctx *c, int rows) {
+    if (c->pf_rows >= rows) return TV_OK;
+    const tv_model_desc &m = c->m;
+    void *old[] = {c->pX, c->pXN, c->pQKV, c->pQR, c->pATT, c->pACT, c->pTok, c->ppo, c->ppm, c->ppl};
+    for (void *p : old)
+        if (p) hipFree(p);
+    if (c->h_tok) hipHostFree(c->h_tok);
+    c->pX = c->pXN = c->pQKV = c->pQR = c->pATT = c->pACT = nullptr;
+    c->pTok = c->h_tok = nullptr;
+    c->ppo = c->ppm = c->ppl = nullptr;
+    c->pf_rows = 0;
+    const size_t R = (size_t)rows, H = m.hidden, D = m.head_dim, QH = m.n_qhead, KVH = m.n_kvhead;
+    // attention partials: blocks x KV heads x (splits + 1) x query rows
+    size_t slots = 0;
+    const int nz = (rows + kPrefillBlock - 1) / kPrefillBlock;
+    for (int z = 1; z <= nz; ++z) slots = std::max(slots, (size_t)z * KVH * (prefill_splits(z, (int)KVH) + 1));
+    const size_t RP = (size_t)kMaxRows * kMaxGroup;
+    hipError_t e = hipSuccess;
+#define ALLOC(p, bytes) if (e == hipSuccess) e = hipMalloc((void **)&(p), (bytes))
+    ALLOC(c->pX, R * H * 2);
+    ALLOC(c->pXN, R * H * 2);
+    ALLOC(c->pQKV, R * (QH + 2 * KVH) * D * 2);
+    ALLOC(c->pQR, R * QH * D * 2);
+    ALLOC(c->pATT, R * QH * D * 2);
+    ALLOC(c->pACT, R * m.ffn * 2);
+    ALLOC(c->pTok, R * 4);
+    ALLOC(c->ppo, slots * RP * D * 4);
+    ALLOC(c->ppm, slots * RP * 4);
+    ALLOC(c->ppl, slots * RP * 4);
+    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_tok, R * 4, hipHostMallocDefault);
+#undef ALLOC
+    if (e != hipSuccess) return fail(c, TV_EHIP, "prefill scratch for %d rows: %s", rows, hipGetErrorString(e));
+    c->pf_rows = rows;
+    return TV_OK;
+}
+
+// One chunk of m prompt rows at positions pos.. of request q: every layer on
+// the dense kernels; the KV rows land in the cache at their slots.
+int prefill_chunk(tv_ctx *c, Req &q, const int32_t *tokens, int m, int pos) {
+    const tv_model_desc &md = c->m;
+    hipStream_t s = c->stream;
+    const int H = md.hidden, D = md.head_dim, QH = md.n_qhead, KVH = md.n_kvhead;
+    // the staging buffer may still feed the previous chunk's copy
+    HIPCHECK(c, hipStreamSynchronize(s));
+    memcpy(c->h_tok, tokens, (size_t)m * 4);
+    HIPCHECK(c, hipMemcpyAsync(c->pTok, c->h_tok, (size_t)m * 4, hipMemcpyHostToDevice, s));
+    LAUNCH(c, "pf_embed_norm", launch_norm_dense(s, c->pTok, c->emb, c->pX, c->attn_norm[0], md.eps, c->pXN, m, H));
+    const int nz = (m + kPrefillBlock - 1) / kPrefillBlock;
+    const int target = prefill_splits(nz, KVH);
+    for (int l = 0; l < md.n_layer; ++l) {
+        GemmArgs g{};
+        g.X = c->pXN; g.ldx = H; g.W = c->wqkv[l]; g.M = m; g.N = (QH + 2 * KVH) * D; g.K = H;
+        g.Y = c->pQKV; g.ldy = g.N; g.zeros = c->zeros;
+        LAUNCH(c, "pf_gemm_qkv", launch_gemm_dense(s, EPI_BF16, g));
+        LAUNCH(c, "pf_rope", launch_rope_dense(s, c->pQKV, g.N, m, pos, QH, KVH, D, c->rope_cos, c->rope_sin,
+                                               c->pQR, q.K[l], q.V[l], md.max_ctx));
+        AttnArgs aa{};
+        aa.Q = c->pQR; aa.Kc = q.K[l]; aa.Vc = q.V[l]; aa.meta = c->d_meta;
+        aa.po = c->ppo; aa.pm = c->ppm; aa.pl = c->ppl;
+        aa.row0 = 0; aa.n = std::min(m, kPrefillBlock); aa.ctx = pos; aa.cap = md.max_ctx; aa.G = c->G;
+        aa.n_qhead = QH; aa.ns = target + 1; aa.ztarget = target;
+        // the longest split any block has decides whether loader waves run
+        aa.span = attn_span_n(pos + (nz - 1) * kPrefillBlock, target);
+        aa.n_ctx_split = 0;
+        aa.scale = (float)(1.0 / std::sqrt((double)D));
+        aa.zrows = kPrefillBlock; aa.M = m;
+        LAUNCH(c, "pf_attn", launch_attn(s, D, aa));
+        aa.n = kPrefillBlock;
+        LAUNCH(c, "pf_attn_combine", launch_attn_combine(s, D, aa, c->pATT));
+        GemmArgs go{};
+        go.X = c->pATT; go.ldx = QH * D; go.W = c->wo[l]; go.M = m; go.N = H; go.K = QH * D;
+        go.Y = c->pX; go.ldy = H; go.zeros = c->zeros;
+        LAUNCH(c, "pf_gemm_o", launch_gemm_dense(s, EPI_RESID, go));
+        LAUNCH(c, "pf_norm", launch_norm_dense(s, nullptr, nullptr, c->pX, c->ffn_norm[l], md.eps, c->pXN, m, H));
+        GemmArgs gu{};
+        gu.X = c->pXN; gu.ldx = H; gu.W = c->wg[l]; gu.W2 = c->wu[l]; gu.M = m; gu.N = md.ffn; gu.K = H;
+        gu.Y = c->pACT; gu.ldy = md.ffn; gu.zeros = c->zeros;
+        LAUNCH(c, "pf_gemm_gateup", launch_gemm_dense(s, EPI_SWIGLU, gu));
+        GemmArgs gd{};
+        gd.X = c->pACT; gd.ldx = md.ffn; gd.W = c->wd[l]; gd.M = m; gd.N = H; gd.K = md.ffn;
+        gd.Y = c->pX; gd.ldy = H; gd.zeros = c->zeros;
+        LAUNCH(c, "pf_gemm_down", launch_gemm_dense(s, EPI_RESID, gd));
+        const uint16_t *nw = l + 1 < md.n_layer ? c->attn_norm[l + 1] : c->final_norm;
+        LAUNCH(c, "pf_norm", launch_norm_dense(s, nullptr, nullptr, c->pX, nw, md.eps, c->pXN, m, H));
+    }
+    return TV_OK;
+}
+
+} // namespace
+
+int tv_prefill_dense(tv_ctx *c, int req, const int32_t *tokens, int n, int chunk, int32_t *argmax_last) {
+    int rc = check_req(c, req);
+    if (rc) return rc;
+    const tv_model_desc &m = c->m;
+    if (n < 1 || !tokens) return fail(c, TV_EINVAL, "empty prompt");
+    if (chunk < kPrefillBlock || chunk > kPrefillMaxChunk || chunk % kPrefillBlock)
+        return fail(c, TV_EINVAL, "chunk %d must be a multiple of %d in [%d, %d]", chunk, kPrefillBlock,
+                    kPrefillBlock, kPrefillMaxChunk);
+    if (!c->recur_layers.empty())
+        return fail(c, TV_EINVAL, "dense prefill runs attention layers only (use tv_prefill)");
+    for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= m.vocab) return fail(c, TV_EINVAL, "token %d out of range", i);
+    Req &q = c->reqs[req];
+    if (q.ctx_len + n > m.max_ctx) return fail(c, TV_ECAPACITY, "prompt of %d tokens does not fit", n);
+    {
+        std::vector<int> rv{req};
+        rc = check_bound(c, rv);
+        if (rc) return rc;
+    }
+    rc = ensure_prefill(c, chunk);
+    if (rc) return rc;
+    q.pending = false;
+    int done = 0;
+    while (done < n) {
+        // the chunk grid: chunks end at multiples of `chunk` positions
+        const int pos = q.ctx_len;
+        const int k = std::min(n - done, chunk - pos % chunk);
+        rc = prefill_chunk(c, q, tokens + done, k, pos);
+        if (rc) return rc;
+        q.ctx_len += k;
+        for (int i = 0; i < k; ++i) {
+            q.history.push_back(tokens[done + i]);
+            set_bit(q.hist_bits, tokens[done + i]);
+        }
+        done += k;
+        if (done == n && argmax_last) {
+            // the last row's token: the head (with the request's modifiers
+            // and sampling) on that row only
+            if (q.d_hist)
+                HIPCHECK(c, hipMemcpy(q.d_hist, q.hist_bits.data(), q.hist_bits.size() * 4, hipMemcpyHostToDevice));
+            PassMeta &pm = *c->h_meta;
+            memset(&pm, 0, sizeof pm);
+            pm.row_req[0] = 0;
+            pm.draw_t[0] = q.ctx_len;
+            HeadMods &hm = pm.mods[0];
+            hm.rep = q.mods_on ? q.rep : 1.f;
+            hm.hist_bits = (q.mods_on && q.rep != 1.f) ? q.d_hist : nullptr;
+            hm.bias = (q.mods_on && q.has_bias) ? q.d_bias : nullptr;
+            hm.allow_bits = (q.mods_on && q.has_allow) ? q.d_allow : nullptr;
+            hm.temp = q.temp;
+            hm.seed_lo = (uint32_t)q.seed;
+            hm.seed_hi = (uint32_t)(q.seed >> 32);
+            hipStream_t s = c->stream;
+            clear_results(c, 1);
+            HIPCHECK(c, hipMemcpyAsync(c->d_meta, c->h_meta, sizeof(PassMeta), hipMemcpyHostToDevice, s));
+            GemmArgs g{};
+            g.X = c->pXN + (size_t)(k - 1) * m.hidden; g.ldx = m.hidden;
+            g.W = c->head; g.M = 1; g.N = m.vocab; g.K = m.hidden;
+            g.Yf = c->logits; g.ldyf = m.vocab; g.part = c->part; g.meta = c->d_meta;
+            g.mods_on = q.mods_on || q.temp > 0.f; g.zeros = c->zeros;
+            GEMM(c, "gemm_head", EPI_HEAD, g);
+            LAUNCH(c, "top2", launch_top2_reduce(s, c->part, ((m.vocab + 31) / 32 + 3) / 4, 1, c->hd_res));
+            rc = wait_results(c, 1);
+            if (rc) return rc;
+            float gap;
+            read_results(c, 1, argmax_last, &gap);
+        }
+    }
+    if (!argmax_last) HIPCHECK(c, hipStreamSynchronize(c->stream));
+    return TV_OK;
 }
 
 int tv_prefill(tv_ctx *c, int req, const int32_t *tokens, int n, int32_t *argmax_last) {

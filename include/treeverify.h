@@ -155,6 +155,20 @@ int tv_set_sampling(tv_ctx *ctx, int req, float temperature, uint64_t seed);
  * the last token: the first token to emit. */
 int tv_prefill(tv_ctx *ctx, int req, const int32_t *tokens, int n, int32_t *argmax_last);
 
+/* Dense prefill: the prompt's rows in chunks of up to `chunk` rows through
+ * the MFMA-bound prefill kernels (one GEMM over all of a chunk's rows per
+ * projection, attention in blocks of 32 rows).  The chunk grid is fixed by
+ * absolute position: chunks end at multiples of `chunk` ("Exactness",
+ * Caches: snapshots lie on the prefill chunk grid and a resumed request
+ * forwards the rest of its prompt on the same grid), so a request resumed at
+ * a grid point from the cache rows a cold prefill left there computes the
+ * same arithmetic, bit for bit.  `chunk` is a multiple of 32 in [32, 2048].
+ * Attention layers only (TV_EINVAL for a model with recurrent layers; use
+ * tv_prefill).  Rows are committed as they go: ctx_len grows by n and the
+ * tokens join the history.  *argmax_last (may be NULL) gets the last row's
+ * token (with the request's modifiers and sampling), as tv_prefill. */
+int tv_prefill_dense(tv_ctx *ctx, int req, const int32_t *tokens, int n, int chunk, int32_t *argmax_last);
+
 /* Verify one tree for request `req`.  logits_dev: device fp32 [n_nodes,
  * vocab] (may be NULL: then logits go to library scratch).  argmax (int32)
  * and gap_ulps (float, may be NULL) are host arrays of n_nodes.  gap_ulps[i]

@@ -1,0 +1,204 @@
+"""Dense (MFMA) prefill on the chunk grid (MI355X only).
+
+"Exactness", Caches: snapshots are taken on the prefill chunk grid and a
+resumed request forwards the rest of its prompt on the same grid, so it
+computes the same arithmetic as a cold prefill: bit for bit.
+
+* The last row's token and the cache rows a dense prefill leaves agree with
+  the oracle's sequential decode of the prompt (tokens up to near ties; the
+  rows through the verify that reads them, within the logit tolerance).
+* A prompt prefilled in two calls that split on a grid point, and a request
+  resumed from a snapshot of the cache rows at a grid point, equal the cold
+  prefill bit for bit (cache rows, last token, and the logits of a verify
+  that follows).
+* The dense and the chained (32-row) prefill continue with the same tokens
+  up to near ties.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_ATOL = 2e-2
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def c0():
+    _gpu()
+    import workloads
+    wl = workloads.build(synth.C0, max_ctx=512, max_req=3, weight_device="cuda", host_copy=True)
+    return wl, oracle.Oracle(synth.C0, wl.host_weights)
+
+
+def _kv(wl, req, n):
+    return {k: v[:, :n].clone() for k, v in wl.kv[req].items()}
+
+
+@pytest.mark.parametrize("n,chunk", [(200, 64), (37, 32), (300, 128), (64, 64)])
+def test_c0_dense_prefill_against_oracle(c0, n, chunk):
+    wl, orc = c0
+    prompt = synth.uniform_ids(n + 1, synth.C0.vocab, 40 + n)
+    _say("c0 dense prefill", n, chunk)
+    wl.tv.set_history(0, [], 0)
+    first = wl.tv.prefill_dense(0, prompt[:-1], chunk=chunk)
+    assert wl.tv.ctx_len(0) == n
+    seq = orc.new_seq(cap=512)
+    last = seq.commit(prompt[:-1])
+    a, _, _, g = oracle.top2(last)
+    assert first == a or g <= 1.0, (first, a, g)
+    # cache rows: bf16 values within a few bf16 steps of the oracle's
+    for (l, nm), t in wl.kv[0].items():
+        got = t[:, :n].float().cpu().numpy().astype(np.float64)
+        want = (seq.K if nm == "k" else seq.V)[l][:, :n]
+        err = np.abs(got - want)
+        tol = 2.0 ** -6 * np.maximum(1.0, np.abs(want))
+        assert (err <= tol).mean() > 0.999 and err.max() < 0.1, (l, nm, float(err.max()))
+    # a verify that reads those rows, against the oracle's tree rows
+    parents = synth.c0_tree()
+    tokens = synth.tree_tokens(parents, synth.C0.vocab, 7, root_token=int(prompt[-1]))
+    am, gap = wl.tv.verify_tree(0, parents, tokens, logits=wl.logits)
+    ol = orc.tree_scores(seq, parents, tokens)
+    gl = wl.logits[:len(parents)].cpu().numpy().astype(np.float64)
+    assert np.abs(gl - ol).max() <= LOGIT_ATOL, float(np.abs(gl - ol).max())
+    oam, ogap = oracle.tree_decisions(ol, parents, tokens, seq.history)
+    for i in range(len(parents)):
+        assert am[i] == oam[i] or ogap[i] <= 1.0
+
+
+def test_c0_resume_on_the_grid_is_bitwise_cold(c0):
+    wl, _ = c0
+    chunk, n = 64, 230
+    prompt = synth.uniform_ids(n + 1, synth.C0.vocab, 77)
+    _say("c0 resume on the grid")
+    # cold
+    wl.tv.set_history(0, [], 0)
+    cold_first = wl.tv.prefill_dense(0, prompt[:-1], chunk=chunk)
+    cold = _kv(wl, 0, n)
+    # the same prompt in two calls split on a grid point
+    wl.tv.set_history(1, [], 0)
+    wl.tv.prefill_dense(1, prompt[:128], chunk=chunk)
+    split_first = wl.tv.prefill_dense(1, prompt[128:n], chunk=chunk)
+    assert split_first == cold_first
+    for key, t in _kv(wl, 1, n).items():
+        assert torch.equal(t, cold[key]), key
+    # resumed from a snapshot of the rows at grid point 192
+    for key, t in wl.kv[2].items():
+        t.zero_()
+        t[:, :192].copy_(cold[key][:, :192])
+    wl.tv.set_history(2, prompt[:192].tolist(), 192)
+    res_first = wl.tv.prefill_dense(2, prompt[192:n], chunk=chunk)
+    assert res_first == cold_first
+    for key, t in _kv(wl, 2, n).items():
+        assert torch.equal(t, cold[key]), key
+    # and the logits of a verify that follows
+    parents = synth.random_tree(16, 3)
+    tokens = synth.tree_tokens(parents, synth.C0.vocab, 9, root_token=int(prompt[-1]))
+    outs = []
+    for r in (0, 2):
+        wl.tv.verify_tree(r, parents, tokens, logits=wl.logits)
+        outs.append(wl.logits[:16].clone())
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_c0_dense_and_chained_prefill_agree(c0):
+    wl, orc = c0
+    n = 150
+    prompt = synth.uniform_ids(n + 1, synth.C0.vocab, 91)
+    wl.tv.set_history(0, [], 0)
+    a = wl.tv.prefill_dense(0, prompt[:-1], chunk=64)
+    wl.tv.set_history(1, [], 0)
+    b = wl.tv.prefill(1, prompt[:-1])
+    seq = orc.new_seq(cap=512)
+    last = seq.commit(prompt[:-1])
+    o, _, _, g = oracle.top2(last)
+    assert (a == o or g <= 1.0) and (b == o or g <= 1.0)
+    for key in wl.kv[0]:
+        d = (wl.kv[0][key][:, :n].float() - wl.kv[1][key][:, :n].float()).abs().max().item()
+        assert d < 0.1, (key, d)
+
+
+def test_c0_dense_prefill_errors(c0):
+    from greedy_draft_tree_amd import TVError, TV_EINVAL, TV_ECAPACITY
+    wl, _ = c0
+    wl.tv.set_history(0, [], 0)
+    for chunk in (16, 48, 4096):
+        with pytest.raises(TVError) as e:
+            wl.tv.prefill_dense(0, [1, 2, 3], chunk=chunk)
+        assert e.value.code == TV_EINVAL
+    with pytest.raises(TVError) as e:
+        wl.tv.prefill_dense(0, [5] * 600, chunk=64)
+    assert e.value.code == TV_ECAPACITY
+    with pytest.raises(TVError):
+        wl.tv.prefill_dense(0, [synth.C0.vocab], chunk=64)
+    assert wl.tv.ctx_len(0) == 0
+
+
+def test_c0_dense_prefill_sampled_last_token(c0):
+    """A sampled request's prefill returns its draw at the index after the
+    prompt, as plain sampled decoding does."""
+    wl, orc = c0
+    n = 90
+    prompt = synth.uniform_ids(n, synth.C0.vocab, 13)
+    smp = oracle.Sampling(0.9, 4242)
+    wl.tv.set_history(0, [], 0)
+    wl.tv.set_sampling(0, smp.temperature, smp.seed)
+    try:
+        got = wl.tv.prefill_dense(0, prompt, chunk=64)
+    finally:
+        wl.tv.set_sampling(0, 0.0)
+    seq = orc.new_seq(cap=512)
+    last = seq.commit(prompt)
+    keys = oracle.sample_keys(oracle.apply_modifiers(last, seq.history, None), smp, n)
+    a, l1, l2, _ = oracle.top2(keys)
+    assert got == a or l1 - l2 <= 2 * LOGIT_ATOL / smp.temperature
+
+
+def test_hybrid_model_rejects_dense_prefill():
+    _gpu()
+    import workloads
+    from greedy_draft_tree_amd import TVError, TV_EINVAL
+    shape = synth.scaled(synth.C0, "c0_hybrid_pf", n_layer=2, kinds=[synth.RECUR, synth.ATTN])
+    wl = workloads.build(shape, max_ctx=128, max_req=1, weight_device="cuda")
+    wl.tv.set_history(0, [], 0)
+    with pytest.raises(TVError) as e:
+        wl.tv.prefill_dense(0, [1, 2, 3], chunk=32)
+    assert e.value.code == TV_EINVAL
+
+
+def test_c1_width_dense_prefill():
+    """Full width (hidden 5120, 40 q heads, ffn 17408, the fp32 head): 96
+    prompt rows in chunks of 64 against the oracle, then a verify."""
+    _gpu()
+    import workloads
+    wl = workloads.build(synth.C1, max_ctx=256, max_req=1, weight_device="cuda", host_copy=True)
+    orc = oracle.Oracle(synth.C1, wl.host_weights)
+    n = 96
+    prompt = synth.uniform_ids(n + 1, synth.C1.vocab, 5)
+    _say("c1 width dense prefill", n)
+    wl.tv.set_history(0, [], 0)
+    first = wl.tv.prefill_dense(0, prompt[:-1], chunk=64)
+    seq = orc.new_seq(cap=256)
+    last = seq.commit(prompt[:-1])
+    a, _, _, g = oracle.top2(last)
+    assert first == a or g <= 2.0, (first, a, g)
+    parents = synth.spine_tree(8, 2)
+    tokens = synth.tree_tokens(parents, synth.C1.vocab, 3, root_token=int(prompt[-1]))
+    am, gap = wl.tv.verify_tree(0, parents, tokens, logits=wl.logits)
+    ol = orc.tree_scores(seq, parents, tokens)
+    gl = wl.logits[:8].cpu().numpy().astype(np.float64)
+    err = np.abs(gl - ol).max()
+    print(f"[c1 dense prefill] verify max|dlogit| {err:.4g}", flush=True)
+    assert err <= 0.1, err
