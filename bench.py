@@ -70,6 +70,9 @@ def parse():
                     help="instead of the bench line, print a verify price file (StairCut's stair tables) "
                          "for rows 1..32, chain and tree, at the --price-ctx lengths")
     ap.add_argument("--price-ctx", default="1024,8192,32768")
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="instead of the bench line, time a dense prefill of this many tokens (one JSON line)")
+    ap.add_argument("--chunk", type=int, default=512, help="dense prefill chunk (rows)")
     ap.add_argument("--price-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", default="full",
@@ -189,6 +192,8 @@ def main():
     ctxs = [a.ctx, a.ctx2] if a.config == "c4" else [a.ctx]
     if a.prices:
         return prices_main(a, shape)
+    if a.prefill:
+        return prefill_main(a, shape)
     n_req = len(ctxs)
     mods_on = a.config == "c4"
     torch.cuda.init()
@@ -369,6 +374,97 @@ def main():
                      "kernel": kname, "avg_us": round(k_avg_ms * 1e3, 2),
                      "bytes_per_launch": int(kb), "launches": k_cnt},
         "cpu_baseline": cpu,
+    }
+    if kernels:
+        out["kernels"] = kernels
+    print(json.dumps(out), flush=True)
+
+
+def prefill_main(a, shape):
+    """Dense prefill throughput: a prompt of --prefill uniform tokens through
+    tv_prefill_dense in chunks of --chunk rows (attention-only workloads),
+    with the dense gate/up GEMM's MFMA roofline and the chained (32-row)
+    prefill timed once beside it."""
+    import torch
+    import synth
+    import workloads
+    n, chunk = a.prefill, a.chunk
+    torch.cuda.init()
+    print(f"[bench] building {shape.name} for a {n}-token prefill", file=sys.stderr, flush=True)
+    wl = workloads.build(shape, max_ctx=n + 64, max_req=1, weight_device="cuda")
+    tv = wl.tv
+    prompt = synth.uniform_ids(n, shape.vocab, 5)
+
+    def once():
+        tv.set_history(0, [], 0)
+        return tv.prefill_dense(0, prompt, chunk=chunk)
+
+    for _ in range(a.warmup):
+        once()
+    print("[bench] warm", file=sys.stderr, flush=True)
+    tv.profile_reset()
+    tv.profile_enable(True, "pf_gemm_gateup")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        once()
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    k_ms, k_cnt = tv.profile_get("pf_gemm_gateup")
+    tv.profile_enable(False)
+    kernels = None
+    if a.kernel_breakdown:
+        tv.profile_reset()
+        tv.profile_enable(True, "")
+        once()
+        kernels = {}
+        for k in ("pf_embed_norm", "pf_gemm_qkv", "pf_rope", "pf_attn_combine", "pf_gemm_o", "pf_norm",
+                  "pf_gemm_gateup", "pf_gemm_down", "gemm_head", "top2"):
+            ms, cnt = tv.profile_get(k)
+            if cnt:
+                kernels[k] = {"avg_us": round(ms / cnt * 1e3, 2), "launches": cnt}
+        ms, cnt = tv.profile_get("pf_attn")
+        ms2, cnt2 = tv.profile_get("pf_attn_combine")
+        if cnt > cnt2:
+            kernels["pf_attn"] = {"avg_us": round((ms - ms2) / (cnt - cnt2) * 1e3, 2), "launches": cnt - cnt2}
+        tv.profile_enable(False)
+    # the chained prefill (32-row verify passes, each committed) once, for comparison
+    tv.set_history(0, [], 0)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tv.prefill(0, prompt)
+    torch.cuda.synchronize()
+    chain_s = time.perf_counter() - t1
+    # gate/up: 2 * rows * (2 * ffn) * hidden flops per launch; launches cover every chunk of every layer
+    chunks = []
+    pos = 0
+    while pos < n:
+        k = min(n - pos, chunk - pos % chunk)
+        chunks.append(k)
+        pos += k
+    flops = sum(2.0 * k * 2 * shape.ffn * shape.hidden for k in chunks) * len(shape.kinds)
+    k_avg_ms = k_ms / max(k_cnt, 1)
+    achieved = flops / len(chunks) / len(shape.kinds) / (k_avg_ms * 1e-3) / 1e12
+    out = {
+        "metric": "dense prefill tokens/s",
+        "value": round(n * a.steps / total, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(total / a.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{shape.name}: prefill of {n} uniform tokens in chunks of {chunk} rows",
+                   "tokens": n, "chunk": chunk},
+        "chained_prefill_tokens_per_s": round(n / chain_s, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(achieved / 2500.0, 4), "traffic": None,
+                     "kernel": "pf_gemm_gateup (k_gemm_dense<EPI_SWIGLU, 2>)", "avg_us": round(k_avg_ms * 1e3, 2),
+                     "launches": k_cnt},
     }
     if kernels:
         out["kernels"] = kernels

@@ -491,11 +491,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 // ------------------------------------------------------------ dense GEMM
 // Y[m, n] = sum_k X[m, k] W[n, k] for many activation rows (prefill
 // chunks).  The same packed weights and LDS staging as k_gemm, but a
-// workgroup covers MG groups of 32 activation rows (grid.x, fastest, so the
-// workgroups that share a weight block run together and its second and later
-// reads hit the caches) and each wave reuses its weight tile across all of
-// them: weights are read once per 32*MG rows and each k step carries MG
-// MFMAs per weight load.  No split-K: the grid has enough workgroups.
+// workgroup covers MG groups of 32 activation rows and each wave reuses its
+// weight tile across all of them: each k step carries MG MFMAs per weight
+// load.  The grid is one-dimensional and XCD-aware: workgroups are dealt to
+// the 8 XCDs in turn, so consecutive ids are renumbered to keep every
+// row-tile of a weight block on one XCD, where the block's later reads hit
+// that XCD's L2 instead of going back to memory.  No split-K: the grid has
+// enough workgroups.
 template <int EPI, int MG>
 __global__ __launch_bounds__(256) void k_gemm_dense(GemmArgs g) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
@@ -506,11 +508,16 @@ __global__ __launch_bounds__(256) void k_gemm_dense(GemmArgs g) {
     const int hf = lane >> 5, c = lane & 31;
     const int N = g.N, K = g.K;
     const int ntiles = (N + 31) >> 5;
-    const int tile = blockIdx.y * 4 + wave;
+    const int mt = (g.M + 32 * MG - 1) / (32 * MG);       // row tiles
+    const int total = gridDim.x, full = total & ~7;
+    int w = blockIdx.x;
+    if (w < full) w = (w & 7) * (full >> 3) + (w >> 3);   // XCD w%8 takes a contiguous range
+    const int wblock = w / mt, mtile = w % mt;
+    const int tile = wblock * 4 + wave;
     const bool tok = tile < ntiles;
     const int nr = tok ? min(32, N - tile * 32) : 0;
     const int nsteps = (K + 63) >> 6;
-    const int m0 = blockIdx.x * 32 * MG;
+    const int m0 = mtile * 32 * MG;
     const uint16_t *tb = g.W + (size_t)(tok ? tile : 0) * 32 * K;
     const uint16_t *tb2 = DUAL ? g.W2 + (size_t)(tok ? tile : 0) * 32 * K : nullptr;
     const uint4 z = {0u, 0u, 0u, 0u};
@@ -1502,15 +1509,14 @@ hipError_t launch_gemm_dense(hipStream_t s, int epi, const GemmArgs &a) {
     if (a.M < 1 || a.N < 1 || a.K < 8 || a.K % 8) return hipErrorInvalidValue;
     const int wblocks = ((a.N + 31) / 32 + 3) / 4;
     const dim3 block(256);
+    // single epilogues: 4 row groups (128 rows) per workgroup; SwiGLU (two
+    // weight tiles per wave): 2 groups, which keeps two waves per SIMD
+    const dim3 grid4(((a.M + 127) / 128) * wblocks), grid2(((a.M + 63) / 64) * wblocks);
     switch (epi) {
-    case EPI_BF16:
-        hipLaunchKernelGGL((k_gemm_dense<EPI_BF16, 4>), dim3((a.M + 127) / 128, wblocks), block, 0, s, a); break;
-    case EPI_RESID:
-        hipLaunchKernelGGL((k_gemm_dense<EPI_RESID, 4>), dim3((a.M + 127) / 128, wblocks), block, 0, s, a); break;
-    case EPI_F32:
-        hipLaunchKernelGGL((k_gemm_dense<EPI_F32, 4>), dim3((a.M + 127) / 128, wblocks), block, 0, s, a); break;
-    case EPI_SWIGLU:
-        hipLaunchKernelGGL((k_gemm_dense<EPI_SWIGLU, 2>), dim3((a.M + 63) / 64, wblocks), block, 0, s, a); break;
+    case EPI_BF16: hipLaunchKernelGGL((k_gemm_dense<EPI_BF16, 4>), grid4, block, 0, s, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_gemm_dense<EPI_RESID, 4>), grid4, block, 0, s, a); break;
+    case EPI_F32: hipLaunchKernelGGL((k_gemm_dense<EPI_F32, 4>), grid4, block, 0, s, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_dense<EPI_SWIGLU, 2>), grid2, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
