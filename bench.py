@@ -382,7 +382,7 @@ def main():
 
 def prefill_main(a, shape):
     """Dense prefill throughput: a prompt of --prefill uniform tokens through
-    tv_prefill_dense in chunks of --chunk rows (attention-only workloads),
+    tv_prefill_dense in chunks of --chunk rows,
     with the dense gate/up GEMM's MFMA roofline and the chained (32-row)
     prefill timed once beside it."""
     import torch
@@ -419,7 +419,8 @@ def prefill_main(a, shape):
         once()
         kernels = {}
         for k in ("pf_embed_norm", "pf_gemm_qkv", "pf_rope", "pf_attn_combine", "pf_gemm_o", "pf_norm",
-                  "pf_gemm_gateup", "pf_gemm_down", "gemm_head", "top2"):
+                  "pf_gemm_gateup", "pf_gemm_down", "pf_gemm_gate", "pf_recur", "pf_commit_state",
+                  "gemm_head", "top2"):
             ms, cnt = tv.profile_get(k)
             if cnt:
                 kernels[k] = {"avg_us": round(ms / cnt * 1e3, 2), "launches": cnt}

@@ -133,6 +133,12 @@ struct RecurArgs {
     int delta;             // gated delta rule instead of the plain gated recurrence
     int row0, n, QH;
     float eps;
+    // prefill blocks: the projection as bf16 rows instead of partials (columns
+    // below a_col from qkv_rows [rows][a_col], the rest from ab_rows [rows][ab_ld]),
+    // and the rows form a chain (node t's ancestors are 0..t-1)
+    const uint16_t *qkv_rows;
+    const uint16_t *ab_rows;
+    int ab_ld;
 };
 
 // An accepted path, passed to the commit kernels by value.

@@ -338,7 +338,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &g, int tile, int l
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
-    constexpr int U = DUAL ? 2 : 4;      // k steps per LDS stage
+    constexpr int U = (DUAL || EPI == EPI_HEAD) ? 2 : 4;   // k steps per LDS stage
     constexpr int NACC = DUAL ? 2 : 1;
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][U][32 * 64];
     __shared__ uint32_t pbits[EPI == EPI_HEAD ? kMaxRows * 4 : 1];   // head: path tokens per row
@@ -1203,7 +1203,8 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     // loads covers up to 16 nodes
     constexpr int UQ = 8, UV = kMaxRows * VW / 256, UB = 2 * UQ + UV + 2;
     static_assert(UV * 256 == kMaxRows * VW, "v elements per thread");
-    if (tid < n) ancs[tid] = r.meta->anc[r.row0 + tid];
+    const bool rows_in = r.qkv_rows != nullptr;   // a prefill block: bf16 rows, a chain
+    if (tid < n) ancs[tid] = rows_in ? (tid >= 31 ? 0xffffffffu : ((2u << tid) - 1u)) : r.meta->anc[r.row0 + tid];
     for (int base = 0; base < n * D; base += UQ * 256) {
         int mm[UB], cc[UB];
         bool ok[UB];
@@ -1228,7 +1229,16 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
         mm[UB - 2] = mm[UB - 1] = r.row0 + (tid < n ? tid : 0);
         cc[UB - 2] = r.a_col + h;
         cc[UB - 1] = r.a_col + QH + h;
-        psum_batch<UB>(r.qkv_part, r.qkv_S, mm, cc, ok, o);
+        if (rows_in) {
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                const uint16_t *src = cc[u] < r.a_col ? r.qkv_rows + (size_t)mm[u] * r.a_col + cc[u]
+                                                      : r.ab_rows + (size_t)mm[u] * r.ab_ld + (cc[u] - r.a_col);
+                o[u] = ok[u] ? bf2f(*src) : 0.f;
+            }
+        } else {
+            psum_batch<UB>(r.qkv_part, r.qkv_S, mm, cc, ok, o);
+        }
 #pragma unroll
         for (int u = 0; u < UQ; ++u) {
             const int idx = base + u * 256 + tid;

@@ -80,6 +80,7 @@ struct tv_ctx {
     // dense prefill scratch (allocated on first use, for pf_rows rows)
     int pf_rows = 0;
     uint16_t *pX = nullptr, *pXN = nullptr, *pQKV = nullptr, *pQR = nullptr, *pATT = nullptr, *pACT = nullptr;
+    uint16_t *pAB = nullptr;   // recurrent layers: gate (and write-strength) rows
     int32_t *pTok = nullptr, *h_tok = nullptr;
     float *ppo = nullptr, *ppm = nullptr, *ppl = nullptr;
     Top2 *part = nullptr;
@@ -674,7 +675,7 @@ void tv_destroy(tv_ctx *c) {
     else hipDeviceSynchronize();
     void *dev[] = {c->X, c->XN, c->QR, c->ATT, c->ACT, c->zeros, c->logits, c->part, c->po, c->pm, c->pl,
                    c->rope_cos, c->rope_sin, c->d_meta, c->gemm_partial, c->pX, c->pXN, c->pQKV, c->pQR,
-                   c->pATT, c->pACT, c->pTok, c->ppo, c->ppm, c->ppl};
+                   c->pATT, c->pACT, c->pAB, c->pTok, c->ppo, c->ppm, c->ppl};
     for (void *p : dev)
         if (p) hipFree(p);
     for (auto &q : c->reqs) {
@@ -933,11 +934,11 @@ int prefill_splits(int nz, int KVH) { return std::min(32, std::max(1, 1024 / (nz
 int ensure_prefill(tv_ctx *c, int rows) {
     if (c->pf_rows >= rows) return TV_OK;
     const tv_model_desc &m = c->m;
-    void *old[] = {c->pX, c->pXN, c->pQKV, c->pQR, c->pATT, c->pACT, c->pTok, c->ppo, c->ppm, c->ppl};
+    void *old[] = {c->pX, c->pXN, c->pQKV, c->pQR, c->pATT, c->pACT, c->pAB, c->pTok, c->ppo, c->ppm, c->ppl};
     for (void *p : old)
         if (p) hipFree(p);
     if (c->h_tok) hipHostFree(c->h_tok);
-    c->pX = c->pXN = c->pQKV = c->pQR = c->pATT = c->pACT = nullptr;
+    c->pX = c->pXN = c->pQKV = c->pQR = c->pATT = c->pACT = c->pAB = nullptr;
     c->pTok = c->h_tok = nullptr;
     c->ppo = c->ppm = c->ppl = nullptr;
     c->pf_rows = 0;
@@ -951,7 +952,8 @@ int ensure_prefill(tv_ctx *c, int rows) {
 #define ALLOC(p, bytes) if (e == hipSuccess) e = hipMalloc((void **)&(p), (bytes))
     ALLOC(c->pX, R * H * 2);
     ALLOC(c->pXN, R * H * 2);
-    ALLOC(c->pQKV, R * (QH + 2 * KVH) * D * 2);
+    ALLOC(c->pQKV, R * std::max((QH + 2 * KVH) * D, 3 * QH * D) * 2);
+    ALLOC(c->pAB, R * 2 * QH * 2);
     ALLOC(c->pQR, R * QH * D * 2);
     ALLOC(c->pATT, R * QH * D * 2);
     ALLOC(c->pACT, R * m.ffn * 2);
@@ -980,6 +982,38 @@ int prefill_chunk(tv_ctx *c, Req &q, const int32_t *tokens, int m, int pos) {
     const int nz = (m + kPrefillBlock - 1) / kPrefillBlock;
     const int target = prefill_splits(nz, KVH);
     for (int l = 0; l < md.n_layer; ++l) {
+      if (c->kinds[l] != TV_LAYER_ATTN) {
+        // a recurrent layer: q/k/v rows and gate rows on the dense GEMM, then
+        // the tree read-out on chains of 32 rows in order, each followed by
+        // the closed-form state commit of its whole chain
+        const bool delta = c->kinds[l] == TV_LAYER_DELTA;
+        const int rl = c->recur_index[l], nab = (delta ? 2 : 1) * QH;
+        GemmArgs g{};
+        g.X = c->pXN; g.ldx = H; g.W = c->wqkv[l]; g.M = m; g.N = 3 * QH * D; g.K = H;
+        g.Y = c->pQKV; g.ldy = g.N; g.zeros = c->zeros;
+        LAUNCH(c, "pf_gemm_qkv", launch_gemm_dense(s, EPI_BF16, g));
+        GemmArgs ga{};
+        ga.X = c->pXN; ga.ldx = H; ga.W = c->wa[l]; ga.M = m; ga.N = nab; ga.K = H;
+        ga.Y = c->pAB; ga.ldy = nab; ga.zeros = c->zeros;
+        LAUNCH(c, "pf_gemm_gate", launch_gemm_dense(s, EPI_BF16, ga));
+        const size_t per = (size_t)kMaxRows * QH * D;
+        for (int b0 = 0; b0 < m; b0 += kPrefillBlock) {
+            const int nb = std::min(kPrefillBlock, m - b0);
+            RecurArgs ra{};
+            ra.qkv_rows = c->pQKV; ra.ab_rows = c->pAB; ra.ab_ld = nab; ra.a_col = 3 * QH * D; ra.delta = delta;
+            ra.S0 = q.S[l]; ra.meta = c->d_meta; ra.out = c->pATT;
+            ra.save_k = q.save_k + rl * per; ra.save_v = q.save_v + rl * per;
+            ra.save_gc = q.save_gc + (size_t)rl * kMaxRows * QH;
+            ra.row0 = b0; ra.n = nb; ra.QH = QH; ra.eps = md.eps;
+            LAUNCH(c, "pf_recur", launch_recur_tree(s, D, ra));
+            RecurCommitArgs ca{};
+            ca.states = q.d_stab + rl; ca.save_k = ra.save_k; ca.save_v = ra.save_v; ca.save_gc = ra.save_gc;
+            ca.path.len = nb;
+            for (int d = 0; d < nb; ++d) ca.path.node[d] = d;
+            ca.QH = QH;
+            LAUNCH(c, "pf_commit_state", launch_recur_commit(s, D, ca, 1));
+        }
+      } else {
         GemmArgs g{};
         g.X = c->pXN; g.ldx = H; g.W = c->wqkv[l]; g.M = m; g.N = (QH + 2 * KVH) * D; g.K = H;
         g.Y = c->pQKV; g.ldy = g.N; g.zeros = c->zeros;
@@ -999,6 +1033,7 @@ int prefill_chunk(tv_ctx *c, Req &q, const int32_t *tokens, int m, int pos) {
         LAUNCH(c, "pf_attn", launch_attn(s, D, aa));
         aa.n = kPrefillBlock;
         LAUNCH(c, "pf_attn_combine", launch_attn_combine(s, D, aa, c->pATT));
+      }
         GemmArgs go{};
         go.X = c->pATT; go.ldx = QH * D; go.W = c->wo[l]; go.M = m; go.N = H; go.K = QH * D;
         go.Y = c->pX; go.ldy = H; go.zeros = c->zeros;
@@ -1028,8 +1063,6 @@ int tv_prefill_dense(tv_ctx *c, int req, const int32_t *tokens, int n, int chunk
     if (chunk < kPrefillBlock || chunk > kPrefillMaxChunk || chunk % kPrefillBlock)
         return fail(c, TV_EINVAL, "chunk %d must be a multiple of %d in [%d, %d]", chunk, kPrefillBlock,
                     kPrefillBlock, kPrefillMaxChunk);
-    if (!c->recur_layers.empty())
-        return fail(c, TV_EINVAL, "dense prefill runs attention layers only (use tv_prefill)");
     for (int i = 0; i < n; ++i)
         if (tokens[i] < 0 || tokens[i] >= m.vocab) return fail(c, TV_EINVAL, "token %d out of range", i);
     Req &q = c->reqs[req];
@@ -1039,6 +1072,8 @@ int tv_prefill_dense(tv_ctx *c, int req, const int32_t *tokens, int n, int chunk
         rc = check_bound(c, rv);
         if (rc) return rc;
     }
+    rc = upload_stab(c, q);
+    if (rc) return rc;
     rc = ensure_prefill(c, chunk);
     if (rc) return rc;
     q.pending = false;

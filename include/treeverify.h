@@ -163,9 +163,10 @@ int tv_prefill(tv_ctx *ctx, int req, const int32_t *tokens, int n, int32_t *argm
  * forwards the rest of its prompt on the same grid), so a request resumed at
  * a grid point from the cache rows a cold prefill left there computes the
  * same arithmetic, bit for bit.  `chunk` is a multiple of 32 in [32, 2048].
- * Attention layers only (TV_EINVAL for a model with recurrent layers; use
- * tv_prefill).  Rows are committed as they go: ctx_len grows by n and the
- * tokens join the history.  *argmax_last (may be NULL) gets the last row's
+ * Recurrent layers take the chunk's rows as chains of 32 in order (the tree
+ * read-out on each, then the closed-form state commit of the chain).  Rows
+ * are committed as they go: ctx_len grows by n and the tokens join the
+ * history.  *argmax_last (may be NULL) gets the last row's
  * token (with the request's modifiers and sampling), as tv_prefill. */
 int tv_prefill_dense(tv_ctx *ctx, int req, const int32_t *tokens, int n, int chunk, int32_t *argmax_last);
 

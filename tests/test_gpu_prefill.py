@@ -13,6 +13,8 @@ computes the same arithmetic as a cold prefill: bit for bit.
   that follows).
 * The dense and the chained (32-row) prefill continue with the same tokens
   up to near ties.
+* Recurrent layers (plain gated and delta rule) take the chunk as chains of
+  32 rows: the same checks, states included.
 """
 import numpy as np
 import pytest
@@ -166,16 +168,62 @@ def test_c0_dense_prefill_sampled_last_token(c0):
     assert got == a or l1 - l2 <= 2 * LOGIT_ATOL / smp.temperature
 
 
-def test_hybrid_model_rejects_dense_prefill():
+HYBS = {k: synth.scaled(synth.C0, name, n_layer=4, kinds=[k, synth.ATTN, k, k])
+        for k, name in ((synth.RECUR, "c0_hybrid_pf"), (synth.DELTA, "c0_delta_pf"))}
+
+
+@pytest.mark.parametrize("kind", [synth.RECUR, synth.DELTA], ids=["gated", "delta"])
+def test_hybrid_dense_prefill(kind):
+    """Recurrent layers in the dense prefill (chains of 32 rows through the
+    tree read-out, each committed): against the oracle's sequential decode
+    (last token, states, a following verify), and a resume on the grid equal
+    to the cold prefill bit for bit (states and cache rows)."""
     _gpu()
     import workloads
-    from greedy_draft_tree_amd import TVError, TV_EINVAL
-    shape = synth.scaled(synth.C0, "c0_hybrid_pf", n_layer=2, kinds=[synth.RECUR, synth.ATTN])
-    wl = workloads.build(shape, max_ctx=128, max_req=1, weight_device="cuda")
+    shape = HYBS[kind]
+    wl = workloads.build(shape, max_ctx=256, max_req=2, weight_device="cuda", host_copy=True)
+    orc = oracle.Oracle(shape, wl.host_weights)
+    s0 = synth.state0(shape, seed=6)
+    n, chunk = 150, 64
+    prompt = synth.uniform_ids(n + 1, shape.vocab, 21)
+    _say("hybrid dense prefill", shape.name)
+    for r in range(2):
+        for l, t in wl.states[r].items():
+            t.copy_(s0[l].cuda())
+    torch.cuda.synchronize()
     wl.tv.set_history(0, [], 0)
-    with pytest.raises(TVError) as e:
-        wl.tv.prefill_dense(0, [1, 2, 3], chunk=32)
-    assert e.value.code == TV_EINVAL
+    first = wl.tv.prefill_dense(0, prompt[:-1], chunk=chunk)
+    seq = orc.new_seq(cap=256, s0=s0)
+    last = seq.commit(prompt[:-1])
+    a, _, _, g = oracle.top2(last)
+    assert first == a or g <= 1.0, (first, a, g)
+    torch.cuda.synchronize()
+    for l, t in wl.states[0].items():
+        got = t.cpu().numpy().astype(np.float64)
+        err = np.abs(got - seq.S[l]).max()
+        print(f"[{shape.name} prefill state {l}] max|dS| {err:.3g}", flush=True)
+        assert err <= 2e-2 * max(1.0, np.abs(seq.S[l]).max()), (l, err)
+    cold_states = {l: t.clone() for l, t in wl.states[0].items()}
+    cold_kv = _kv(wl, 0, n)
+    parents = synth.c0_tree()
+    tokens = synth.tree_tokens(parents, shape.vocab, 7, root_token=int(prompt[-1]))
+    am, gap = wl.tv.verify_tree(0, parents, tokens, logits=wl.logits)
+    ol = orc.tree_scores(seq, parents, tokens)
+    gl = wl.logits[:len(parents)].cpu().numpy().astype(np.float64)
+    assert np.abs(gl - ol).max() <= LOGIT_ATOL, float(np.abs(gl - ol).max())
+    cold_logits = wl.logits[:len(parents)].clone()
+    # resumed on the grid: the first 128 rows, then the rest
+    wl.tv.set_history(1, [], 0)
+    wl.tv.prefill_dense(1, prompt[:128], chunk=chunk)
+    res_first = wl.tv.prefill_dense(1, prompt[128:n], chunk=chunk)
+    assert res_first == first
+    torch.cuda.synchronize()
+    for l, t in wl.states[1].items():
+        assert torch.equal(t, cold_states[l]), l
+    for key, t in _kv(wl, 1, n).items():
+        assert torch.equal(t, cold_kv[key]), key
+    wl.tv.verify_tree(1, parents, tokens, logits=wl.logits)
+    assert torch.equal(wl.logits[:len(parents)], cold_logits)
 
 
 def test_c1_width_dense_prefill():
