@@ -612,3 +612,77 @@ def sampled(seq: Seq, first: int, k: int, smp: Sampling, mods: Optional[Modifier
         gaps.append(g)
         t = a
     return out, gaps
+
+
+# ------------------------------------------------- residual tree sampling
+#
+# Deterministic-candidate residual sampling ("Algorithm and correctness
+# contract", Deterministic tree candidates and residual verification): at a
+# node with target distribution p (softmax of the modified scores over T),
+# the children are tried in index order; a candidate x is accepted with
+# probability r(x), r starting at p; a rejected candidate's mass is removed
+# and r renormalised; when every candidate fails, the replacement is drawn
+# from the residual r and the round ends.
+#
+# Reading taken here: a visited node consumes ONE uniform u, the uniform of
+# its depth.  Trying the candidates in order with u rescaled after each
+# rejection, then drawing the residual with the rescaled u by inverse CDF in
+# token-id order, is exactly inverse-CDF sampling of p over the order
+# (candidates in index order, then every other id ascending): the first
+# position where the running sum of the weights exceeds u times their total.
+# A leaf (no candidates) draws from p, which gives the next round its root.
+
+def residual_weights(scores: np.ndarray, temperature: float) -> np.ndarray:
+    """Unnormalised fp64 weights exp(s/T - max) of fp32 scores (-inf -> 0)."""
+    s = np.asarray(scores, dtype=np.float32).astype(np.float64) / float(temperature)
+    fin = np.isfinite(s)
+    w = np.zeros_like(s)
+    w[fin] = np.exp(s[fin] - s[fin].max())
+    return w
+
+
+def residual_decision(scores: np.ndarray, candidates: Sequence[int], temperature: float, u: float):
+    """('accept', j) for candidate j, or ('emit', token), with the margin
+    |running sum - u * total| / total at the decision (for tie checks)."""
+    w = residual_weights(scores, temperature)
+    cand = [int(c) for c in candidates]
+    rest = np.ones(w.shape[0], dtype=bool)
+    rest[cand] = False
+    order = np.concatenate([np.asarray(cand, dtype=np.int64), np.nonzero(rest)[0]])
+    cum = np.cumsum(w[order])
+    total = math.fsum(w)
+    thr = u * total
+    pos = int(np.searchsorted(cum, thr, side="right"))
+    pos = min(pos, order.shape[0] - 1)
+    while w[order[pos]] == 0.0 and pos > 0:     # never land on a zero-weight id
+        pos -= 1
+    lo = cum[pos - 1] if pos > 0 else 0.0
+    margin = min(abs(cum[pos] - thr), abs(thr - lo)) / total
+    if pos < len(cand):
+        return ("accept", pos), margin
+    return ("emit", int(order[pos])), margin
+
+
+def residual_walk(logits: np.ndarray, parents, tokens, history: Sequence[int], temperature: float,
+                  uniforms: Sequence[float], mods: Optional[Modifiers] = None):
+    """One round of residual tree sampling: (path node ids, emitted tokens,
+    the smallest decision margin).  uniforms[d] is the uniform of depth d."""
+    n = len(parents)
+    kids: List[List[int]] = [[] for _ in range(n)]
+    for i in range(1, n):
+        kids[int(parents[i])].append(i)
+    cur, d = 0, 0
+    path, emitted, margin = [0], [], 1.0
+    while True:
+        prior = list(history) + path_tokens(parents, tokens, cur)
+        scores = apply_modifiers(logits[cur], prior, mods)
+        (kind, val), mg = residual_decision(scores, [int(tokens[c]) for c in kids[cur]], temperature,
+                                            float(uniforms[d]))
+        margin = min(margin, mg)
+        if kind == "emit":
+            emitted.append(val)
+            return path, emitted, margin
+        cur = kids[cur][val]
+        path.append(cur)
+        emitted.append(int(tokens[cur]))
+        d += 1
