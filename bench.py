@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="> 0: every request samples (seeded Gumbel-max draws); 0 = greedy")
     ap.add_argument("--seed", type=int, default=42, help="sampling seed")
+    ap.add_argument("--residual", type=float, default=0.0,
+                    help="> 0: every round is a residual-sampling round at this temperature (c1/c2)")
     ap.add_argument("--prices", action="store_true",
                     help="instead of the bench line, print a verify price file (StairCut's stair tables) "
                          "for rows 1..32, chain and tree, at the --price-ctx lengths")
@@ -246,9 +248,15 @@ def main():
         trees[n] = per_req
     print("[bench] trees ready", file=sys.stderr, flush=True)
     reqs = list(range(n_req))
+    res_rng = np.random.default_rng(a.seed)
 
     def round_(n):
         per_req = trees[n]
+        if n_req == 1 and a.residual > 0:   # verify, residual walk and commit in one call
+            parents, tokens = per_req[0]
+            path, _ = tv.residual_round(0, parents, tokens, a.residual, res_rng.random(32), logits=wl.logits)
+            tv.set_history(0, hist[0], ctxs[0])
+            return [len(path)]
         if n_req == 1:   # verify, accept walk and commit in one library call
             parents, tokens = per_req[0]
             _, _, path, _ = tv.round(0, parents, tokens, logits=wl.logits)
@@ -322,7 +330,7 @@ def main():
         kernels = {}
         for k in ("embed_norm", "resid_norm", "gemm_qkv", "rope_kv", "attn", "attn_combine", "gemm_o",
                   "gemm_gateup", "splitk_finish", "gemm_down", "gemm_gate", "recur_tree", "gemm_head",
-                  "top2", "commit_kv", "commit_state"):
+                  "top2", "residual", "commit_kv", "commit_state"):
             ms, cnt = tv.profile_get(k)
             if cnt:
                 kernels[k] = {"avg_us": round(ms / cnt * 1e3, 2), "launches": cnt}
@@ -349,7 +357,8 @@ def main():
             f"SwiGLU {shape.ffn}) + fp32 head V={shape.vocab}; KV cache {'/'.join(map(str, ctxs))} rows; "
             f"one step = verify+accept+commit of trees n={','.join(map(str, ns))}"
             + (" for 2 requests in one pass, modifiers on, wrong drafter" if a.config == "c4" else "")
-            + (f"; sampled requests (temperature {a.temperature}, seed {a.seed})" if a.temperature > 0 else ""))
+            + (f"; sampled requests (temperature {a.temperature}, seed {a.seed})" if a.temperature > 0 else "")
+            + (f"; residual tree sampling at temperature {a.residual}" if a.residual > 0 else ""))
     out = {
         "metric": "ms per tree verify + achieved HBM GB/s at 8/16/24/32 nodes, 1k ctx, 1 GPU",
         "value": round(value, 2),
@@ -365,7 +374,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "ctx": ctxs[0] if n_req == 1 else ctxs, "tree_nodes": list(ns),
                    "requests": n_req, "step_bytes": step_bytes,
-                   "sampling": {"temperature": a.temperature, "seed": a.seed} if a.temperature > 0 else None},
+                   "sampling": {"temperature": a.temperature, "seed": a.seed} if a.temperature > 0 else None,
+                   "residual_temperature": a.residual if a.residual > 0 else None},
         "per_n": per,
         "ratio_16_over_8": round(ratio, 4) if ratio else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -21,7 +21,7 @@ SYMBOLS = ("tv_create", "tv_destroy", "tv_last_error", "tv_bind", "tv_set_histor
            "tv_set_modifiers", "tv_set_sampling", "tv_prefill", "tv_prefill_dense", "tv_verify_tree", "tv_verify_trees",
            "tv_accept_walk", "tv_commit", "tv_round", "tv_ctx_len", "tv_profile_enable",
            "tv_profile_reset", "tv_profile_get", "tv_linear", "tv_head_top2", "tv_pack_weight",
-           "tv_staircut")
+           "tv_staircut", "tv_residual_round")
 
 
 class TVError(RuntimeError):
@@ -74,6 +74,7 @@ def load_library():
         "tv_head_top2": ([P, P, I, P, P, P], I),
         "tv_pack_weight": ([P, P, I, I], I),
         "tv_staircut": ([P, P, P, I, P, P, F, F, P, P, P], I),
+        "tv_residual_round": ([P, I, P, P, I, P, F, P, P, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -276,6 +277,21 @@ class TreeVerifier:
             self._check(rc, "tv_round")
         return (self._am[:n].copy(), self._gap[:n].copy(), self._path[:self._lens[0]].tolist(),
                 self._emit[:self._lens[1]].tolist())
+
+    def residual_round(self, req: int, parents, tokens, temperature: float, uniforms, logits=None):
+        """tv_residual_round: (path, emitted) of one residual-sampling round;
+        uniforms[d] is the uniform of depth d."""
+        p, t = _i32(parents), _i32(tokens)
+        n = len(p)
+        u = np.ascontiguousarray(np.asarray(uniforms, dtype=np.float64))
+        if u.shape[0] < n:
+            raise TVError(-1, "tv_residual_round: one uniform per depth (at least n_nodes)")
+        lp = ctypes.c_void_p(logits.data_ptr()) if logits is not None else None
+        rc = self.lib.tv_residual_round(self.h, req, _ptr(p), _ptr(t), n, lp, float(temperature), _ptr(u),
+                                        _ptr(self._path), ctypes.addressof(self._lens), _ptr(self._emit),
+                                        ctypes.addressof(self._lens) + 4)
+        self._check(rc, "tv_residual_round")
+        return self._path[:self._lens[0]].tolist(), self._emit[:self._lens[1]].tolist()
 
     def ctx_len(self, req: int) -> int:
         rc = self.lib.tv_ctx_len(self.h, req)

@@ -729,6 +729,122 @@ __global__ __launch_bounds__(256) void k_top2_reduce(const Top2 *__restrict__ pa
     }
 }
 
+// ------------------------------------------------- residual tree sampling
+// Per verified row: the decision of deterministic-candidate residual
+// sampling ("Algorithm and correctness contract", Deterministic tree
+// candidates and residual verification) with the row's uniform u.  Its
+// candidates are the row's children in index order; the target is the
+// softmax of the row's modified scores over T.  One uniform per node: the
+// first position, over (candidates, then every other id ascending), where
+// the running sum of the weights w = exp(s/T - max) exceeds u times their
+// total; fp64 weights and sums.  The result is written to pinned host memory
+// as the argmax field of the row's record: -(j+1) to accept candidate j,
+// else the emitted token.
+
+__global__ __launch_bounds__(1024) void k_residual(const float *__restrict__ logits, int ldl, int V,
+                                                   const PassMeta *__restrict__ meta, int n, float T,
+                                                   const double *__restrict__ u_row, RowResult *res) {
+    constexpr int NT = 1024;
+    __shared__ uint32_t pathbits[(1 << 18) / 32];   // the row's path tokens (V <= 2^18)
+    __shared__ double red[NT / 64];
+    __shared__ double seg[NT];
+    __shared__ int cand[kMaxRows];
+    __shared__ int ncand_s;
+    const int i = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const float *row = logits + (size_t)i * ldl;
+    const int words = (V + 31) >> 5;
+    for (int w = t; w < words; w += NT) pathbits[w] = 0u;
+    if (t == 0) {
+        int k = 0;
+        for (int j = i + 1; j < n; ++j)   // children of row i, in index order
+            if (meta->depth[j] == meta->depth[i] + 1 && ((meta->anc[j] >> i) & 1u)) cand[k++] = meta->tok[j];
+        ncand_s = k;
+    }
+    __syncthreads();
+    const HeadMods &md = meta->mods[meta->row_req[i]];
+    if (md.rep != 1.0f && t < meta->path_len[i]) {
+        const int v = meta->path_tok[i * kMaxRows + t];
+        atomicOr(&pathbits[v >> 5], 1u << (v & 31));
+    }
+    __syncthreads();
+    const int ncand = ncand_s;
+    // modified score of id v over T (fp64), -inf for a masked id
+    auto xval = [&](int v) -> double {
+        float s = row[v];
+        if (md.rep != 1.0f) {
+            const uint32_t prior = (md.hist_bits ? md.hist_bits[v >> 5] : 0u) | pathbits[v >> 5];
+            if ((prior >> (v & 31)) & 1u) s = s > 0.f ? s / md.rep : s * md.rep;
+        }
+        if (md.bias) s = s + md.bias[v];
+        if (md.allow_bits && !((md.allow_bits[v >> 5] >> (v & 31)) & 1u)) s = -INFINITY;
+        return (double)s / (double)T;
+    };
+    // the maximum
+    double mx = -INFINITY;
+    for (int v = t; v < V; v += NT) mx = fmax(mx, xval(v));
+    for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    mx = -INFINITY;
+    for (int w = 0; w < NT / 64; ++w) mx = fmax(mx, red[w]);
+    __syncthreads();
+    // each thread sums a contiguous segment of ids; candidates count apart
+    const int per = (V + NT - 1) / NT, v0 = t * per, v1 = min(V, v0 + per);
+    auto wt = [&](int v) -> double {
+        const double x = xval(v);
+        return x == -INFINITY ? 0.0 : exp(x - mx);
+    };
+    auto is_cand = [&](int v) -> bool {
+        for (int k = 0; k < ncand; ++k)
+            if (cand[k] == v) return true;
+        return false;
+    };
+    double sum = 0.0;
+    for (int v = v0; v < v1; ++v)
+        if (!is_cand(v)) sum += wt(v);
+    seg[t] = sum;
+    __syncthreads();
+    if (t == 0) {
+        double candw[kMaxRows], csum = 0.0, rest = 0.0;
+        for (int k = 0; k < ncand; ++k) {
+            candw[k] = wt(cand[k]);
+            csum += candw[k];
+        }
+        for (int w = 0; w < NT; ++w) rest += seg[w];
+        const double thr = u_row[i] * (csum + rest);
+        int outv = -1;
+        double c = 0.0;
+        for (int k = 0; k < ncand && outv < 0; ++k) {
+            c += candw[k];
+            if (c > thr) outv = -(k + 1);
+        }
+        if (outv == -1 && ncand > 0 && c > thr) outv = -ncand;   // (not reached: handled above)
+        if (outv == -1) {
+            // the residual: the segment where the running sum crosses, then its id
+            double r = thr - c;
+            int w = 0;
+            for (; w < NT - 1; ++w) {
+                if (seg[w] > r) break;
+                r -= seg[w];
+            }
+            int last = -1;
+            for (int v = w * per; v < min(V, (w + 1) * per) && outv < 0; ++v) {
+                if (is_cand(v)) continue;
+                const double x = wt(v);
+                if (x > 0.0) last = v;
+                if (x > r) outv = v;
+                else r -= x;
+            }
+            if (outv < 0) {   // rounding at the very end: the last id with weight
+                for (int v = V - 1; v >= 0 && last < 0; --v)
+                    if (!is_cand(v) && wt(v) > 0.0) last = v;
+                outv = last;
+            }
+        }
+        *reinterpret_cast<volatile uint64_t *>(res + i) = (uint64_t)(uint32_t)outv;   // gap bits 0: done
+    }
+}
+
 // ------------------------------------------------------------- RoPE + KV
 // Rotate q and k of each tree node at position ctx + depth (rotate-half
 // pairs (i, i + D/2)); k and v go to cache slot ctx + node index ("Drafters
@@ -1593,6 +1709,13 @@ hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t
     if (D == 128) hipLaunchKernelGGL(k_attn_combine<128>, grid, dim3(128), 0, s, a, out);
     else if (D == 64) hipLaunchKernelGGL(k_attn_combine<64>, grid, dim3(64), 0, s, a, out);
     else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_residual(hipStream_t s, const float *logits, int ldl, int V, const PassMeta *meta, int n, float T,
+                           const double *u_row, RowResult *res) {
+    if (n < 1 || n > kMaxRows || V > (1 << 18) || !(T > 0.f)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_residual, dim3(n), dim3(1024), 0, s, logits, ldl, V, meta, n, T, u_row, res);
     return hipGetLastError();
 }
 

@@ -96,6 +96,8 @@ struct tv_ctx {
     // seen from the GPU)
     RowResult *h_res = nullptr;
     RowResult *hd_res = nullptr;
+    // residual tree sampling: per-row uniforms (pinned staging and device copy)
+    double *h_resu = nullptr, *d_resu = nullptr;
     int ns_max = 0;
 
     // profiling
@@ -651,6 +653,8 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     const unsigned res_flags = hipHostMallocCoherent | hipHostMallocMapped;
     if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_res, R * sizeof(RowResult), res_flags);
     if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&c->hd_res, c->h_res, 0);
+    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_resu, R * sizeof(double), hipHostMallocDefault);
+    if (e == hipSuccess) e = hipMalloc((void **)&c->d_resu, R * sizeof(double));
     if (e != hipSuccess) return cleanup(TV_EHIP);
     // RoPE table: angle pos * theta^(-2i/D) in fp64, cos and sin rounded to fp32
     {
@@ -675,7 +679,7 @@ void tv_destroy(tv_ctx *c) {
     else hipDeviceSynchronize();
     void *dev[] = {c->X, c->XN, c->QR, c->ATT, c->ACT, c->zeros, c->logits, c->part, c->po, c->pm, c->pl,
                    c->rope_cos, c->rope_sin, c->d_meta, c->gemm_partial, c->pX, c->pXN, c->pQKV, c->pQR,
-                   c->pATT, c->pACT, c->pAB, c->pTok, c->ppo, c->ppm, c->ppl};
+                   c->pATT, c->pACT, c->pAB, c->pTok, c->ppo, c->ppm, c->ppl, c->d_resu};
     for (void *p : dev)
         if (p) hipFree(p);
     for (auto &q : c->reqs) {
@@ -688,7 +692,7 @@ void tv_destroy(tv_ctx *c) {
         if (q.save_v) hipFree(q.save_v);
         if (q.save_gc) hipFree(q.save_gc);
     }
-    void *host[] = {c->h_meta, c->h_res, c->h_tok};
+    void *host[] = {c->h_meta, c->h_res, c->h_tok, c->h_resu};
     for (void *p : host)
         if (p) hipHostFree(p);
     for (auto &r : c->recs) {
@@ -918,6 +922,60 @@ int tv_round(tv_ctx *c, int req, const int32_t *parents, const int32_t *tokens, 
     rc = tv_accept_walk(parents, tokens, argmax, n_nodes, path, path_len, emitted, n_emitted);
     if (rc) return fail(c, rc, "accept walk rejected the tree");
     return tv_commit(c, req, path, *path_len);
+}
+
+int tv_residual_round(tv_ctx *c, int req, const int32_t *parents, const int32_t *tokens, int n_nodes,
+                      float *logits_dev, float temperature, const double *uniforms, int32_t *path,
+                      int *path_len, int32_t *emitted, int *n_emitted) {
+    if (!c) return TV_EINVAL;
+    if (!path || !path_len || !emitted || !n_emitted || !uniforms) return fail(c, TV_EINVAL, "null argument");
+    if (!(temperature > 0.f) || !std::isfinite(temperature))
+        return fail(c, TV_EINVAL, "temperature must be positive and finite");
+    if (n_nodes < 1 || n_nodes > TV_MAX_NODES || !parents) return fail(c, TV_EINVAL, "bad tree size");
+    int depth[TV_MAX_NODES];
+    for (int i = 0; i < n_nodes; ++i) {
+        if (i > 0 && (parents[i] < 0 || parents[i] >= i)) return fail(c, TV_EINVAL, "bad parents");
+        depth[i] = i == 0 ? 0 : depth[parents[i]] + 1;
+        if (!(uniforms[depth[i]] >= 0.0 && uniforms[depth[i]] < 1.0))
+            return fail(c, TV_EINVAL, "uniforms must lie in [0, 1)");
+    }
+    int32_t am[TV_MAX_NODES];
+    float gap[TV_MAX_NODES];
+    int rc = tv_verify_tree(c, req, parents, tokens, n_nodes, logits_dev, am, gap);
+    if (rc) return rc;
+    hipStream_t s = c->stream;
+    for (int i = 0; i < n_nodes; ++i) c->h_resu[i] = uniforms[depth[i]];
+    clear_results(c, n_nodes);
+    HIPCHECK(c, hipMemcpyAsync(c->d_resu, c->h_resu, (size_t)n_nodes * sizeof(double), hipMemcpyHostToDevice, s));
+    const float *lg = logits_dev ? logits_dev : c->logits;
+    LAUNCH(c, "residual", launch_residual(s, lg, c->m.vocab, c->m.vocab, c->d_meta, n_nodes, temperature, c->d_resu,
+                                          c->hd_res));
+    rc = wait_results(c, n_nodes);
+    if (rc) return rc;
+    // the walk: from the root, accept a child or emit and stop
+    int cur = 0, pl = 1, ne = 0;
+    path[0] = 0;
+    while (true) {
+        const int32_t d = c->h_res[cur].argmax;
+        if (d >= 0) {
+            emitted[ne++] = d;
+            break;
+        }
+        const int want = -d - 1;
+        int child = -1, k = 0;
+        for (int j = cur + 1; j < n_nodes; ++j)
+            if (parents[j] == cur && k++ == want) {
+                child = j;
+                break;
+            }
+        if (child < 0) return fail(c, TV_EHIP, "internal: residual decision names no child");
+        path[pl++] = child;
+        emitted[ne++] = tokens[child];
+        cur = child;
+    }
+    *path_len = pl;
+    *n_emitted = ne;
+    return tv_commit(c, req, path, pl);
 }
 
 // ------------------------------------------------------------ dense prefill

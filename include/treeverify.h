@@ -241,6 +241,25 @@ int tv_staircut(const int32_t *parents, const float *q, const int32_t *order, in
                 const float *price_tree_ms, const float *price_chain_ms, float draft_ms, float commit_ms,
                 int32_t *keep, int *n_keep, float *score);
 
+/* One round of deterministic-candidate residual tree sampling ("Algorithm
+ * and correctness contract", Deterministic tree candidates and residual
+ * verification): tv_verify_tree, then at each visited node the children are
+ * tried in index order against the target p = softmax(modified scores /
+ * temperature): a candidate x is accepted with probability r(x), r starting
+ * at p; a rejected candidate's mass is removed and r renormalised; when every
+ * candidate fails (or at a leaf) a replacement is drawn from the residual and
+ * the round ends; then tv_commit of the accepted path.  Each visited node
+ * consumes one uniform, uniforms[its depth] in [0, 1) (host, at least
+ * n_nodes entries): the decision is the first position, over (candidates in
+ * index order, then every other id ascending), where the running sum of
+ * p exceeds u (fp64 sums).  emitted = the accepted nodes' tokens and the
+ * final draw (the next round's root); path, as tv_round.  Errors: TV_EINVAL
+ * for a non-positive temperature or a uniform outside [0, 1), else as
+ * tv_round. */
+int tv_residual_round(tv_ctx *ctx, int req, const int32_t *parents, const int32_t *tokens, int n_nodes,
+                      float *logits_dev, float temperature, const double *uniforms, int32_t *path,
+                      int *path_len, int32_t *emitted, int *n_emitted);
+
 /* Committed context length of request `req` (negative TV_E* on error). */
 int tv_ctx_len(tv_ctx *ctx, int req);
 
