@@ -14,6 +14,13 @@
  *                   and drop the rest (step 4, Commit);
  *   tv_round        the three in one call.
  *
+ * Around it: prompts (tv_prefill through the verify path, tv_prefill_dense
+ * on the MFMA prefill kernels and the chunk grid), sampled requests
+ * (tv_set_sampling: seeded Gumbel-max draws; tv_residual_round:
+ * deterministic-candidate residual sampling), StairCut's cut of a candidate
+ * tree (tv_staircut, host only), and kernel-level calls for tests and
+ * measurement (tv_linear, tv_head_top2, tv_pack_weight, tv_profile_*).
+ *
  * Conventions shared by every call:
  *   - Every call returns TV_OK (0) or a negative TV_E* code and never throws.
  *     A failed call changes no state: validation happens before any work is
