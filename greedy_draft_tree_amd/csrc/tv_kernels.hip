@@ -498,10 +498,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 // row-tile of a weight block on one XCD, where the block's later reads hit
 // that XCD's L2 instead of going back to memory.  No split-K: the grid has
 // enough workgroups.
-template <int EPI, int MG>
+template <int EPI, int MG, int U = 2>   // U: k steps per LDS stage
 __global__ __launch_bounds__(256) void k_gemm_dense(GemmArgs g) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
-    constexpr int U = 2;   // k steps per LDS stage
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][U][MG][32 * 64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1635,14 +1634,27 @@ hipError_t launch_gemm_dense(hipStream_t s, int epi, const GemmArgs &a) {
     if (a.M < 1 || a.N < 1 || a.K < 8 || a.K % 8) return hipErrorInvalidValue;
     const int wblocks = ((a.N + 31) / 32 + 3) / 4;
     const dim3 block(256);
-    // single epilogues: 4 row groups (128 rows) per workgroup; SwiGLU (two
-    // weight tiles per wave): 2 groups, which keeps two waves per SIMD
-    const dim3 grid4(((a.M + 127) / 128) * wblocks), grid2(((a.M + 63) / 64) * wblocks);
+    // Row groups per workgroup, from a sweep at 1024 rows: single epilogues
+    // take 4 groups (128 rows) when that still gives at least 448 workgroups
+    // (about 1.75 per CU), else 2; SwiGLU (two weight tiles per wave) takes 2
+    // groups and one k step per LDS stage.  The k order of every output is
+    // the same for any choice (whole steps in order).
+    const int g4 = ((a.M + 127) / 128) * wblocks, g2 = ((a.M + 63) / 64) * wblocks;
+    const bool four = g4 >= 448;
     switch (epi) {
-    case EPI_BF16: hipLaunchKernelGGL((k_gemm_dense<EPI_BF16, 4>), grid4, block, 0, s, a); break;
-    case EPI_RESID: hipLaunchKernelGGL((k_gemm_dense<EPI_RESID, 4>), grid4, block, 0, s, a); break;
-    case EPI_F32: hipLaunchKernelGGL((k_gemm_dense<EPI_F32, 4>), grid4, block, 0, s, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_dense<EPI_SWIGLU, 2>), grid2, block, 0, s, a); break;
+    case EPI_BF16:
+        if (four) hipLaunchKernelGGL((k_gemm_dense<EPI_BF16, 4>), dim3(g4), block, 0, s, a);
+        else hipLaunchKernelGGL((k_gemm_dense<EPI_BF16, 2>), dim3(g2), block, 0, s, a);
+        break;
+    case EPI_RESID:
+        if (four) hipLaunchKernelGGL((k_gemm_dense<EPI_RESID, 4>), dim3(g4), block, 0, s, a);
+        else hipLaunchKernelGGL((k_gemm_dense<EPI_RESID, 2>), dim3(g2), block, 0, s, a);
+        break;
+    case EPI_F32:
+        if (four) hipLaunchKernelGGL((k_gemm_dense<EPI_F32, 4>), dim3(g4), block, 0, s, a);
+        else hipLaunchKernelGGL((k_gemm_dense<EPI_F32, 2>), dim3(g2), block, 0, s, a);
+        break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_dense<EPI_SWIGLU, 2, 1>), dim3(g2), block, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

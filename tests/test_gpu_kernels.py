@@ -213,16 +213,18 @@ def test_dense_linear_fp32_and_bf16(tv, M, N, K):
     assert torch.equal(yb, y.to(torch.bfloat16))
 
 
-def test_dense_linear_rows_bitwise_invariant(tv):
-    """A row's dense result does not depend on the row count or its slot."""
-    N, K = 2048, 1024
-    x, w = _operands(300, N, K, 7)
+@pytest.mark.parametrize("N,K,R", [(2048, 1024, 300), (17408, 512, 512)])
+def test_dense_linear_rows_bitwise_invariant(tv, N, K, R):
+    """A row's dense result does not depend on the row count, its slot, or
+    the tile shape the row count selects (at 17408 columns 512 rows take 4
+    row groups per workgroup, fewer rows take 2)."""
+    x, w = _operands(R, N, K, 7)
     tv.pack_weight(w)
-    full = torch.empty(300, N, dtype=torch.float32, device="cuda")
+    full = torch.empty(R, N, dtype=torch.float32, device="cuda")
     tv.linear(x, w, full)
     rng = np.random.default_rng(1)
     for M in (33, 64, 127, 129, 257):
-        perm = torch.from_numpy(rng.permutation(300)[:M]).cuda()
+        perm = torch.from_numpy(rng.permutation(R)[:M]).cuda()
         y = torch.empty(M, N, dtype=torch.float32, device="cuda")
         tv.linear(x[perm].contiguous(), w, y)
         assert torch.equal(y, full[perm]), M
