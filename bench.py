@@ -72,6 +72,8 @@ def parse():
                     help="instead of the bench line, print a verify price file (StairCut's stair tables) "
                          "for rows 1..32, chain and tree, at the --price-ctx lengths")
     ap.add_argument("--price-ctx", default="1024,8192,32768")
+    ap.add_argument("--lookup", action="store_true",
+                    help="host cost per call of the lookup drafter at the --price-ctx lengths (no GPU)")
     ap.add_argument("--prefill", type=int, default=0,
                     help="instead of the bench line, time a dense prefill of this many tokens (one JSON line)")
     ap.add_argument("--chunk", type=int, default=512, help="dense prefill chunk (rows)")
@@ -192,6 +194,8 @@ def main():
     shape = {"c1": synth.C1, "c2": synth.C2, "c3": synth.C3, "c3d": synth.C3D, "c4": synth.C2}[a.config]
     ns = {"c1": NS, "c2": NS, "c3": (16,), "c3d": (16,), "c4": (16,)}[a.config]
     ctxs = [a.ctx, a.ctx2] if a.config == "c4" else [a.ctx]
+    if a.lookup:
+        return lookup_main(a)
     if a.prices:
         return prices_main(a, shape)
     if a.prefill:
@@ -506,6 +510,52 @@ def prices_main(a, shape):
                          f"(host call to host results) on one MI355X, {time.strftime('%Y-%m-%d')}")
     table["workload"] = shape.name
     print(json.dumps(table), flush=True)
+
+
+def lookup_main(a):
+    """The lookup drafter's host cost per call (the pages give about 0.2 ms a
+    lookup): the native tv_lookup_draft (orders 2..8, depth 31, 31 nodes) at
+    each --price-ctx length on two texts, a quoting one (uniform ids that end
+    by quoting 20 tokens of an earlier span: one vote, a 31-node chain) and a
+    looping one (a 37-token cycle: a vote every cycle).  ``value`` is the
+    quoting text at the longest length; ``cpu_baseline`` the oracle's plain
+    Python on the same quoting texts."""
+    import synth
+    from greedy_draft_tree_amd.lookup import draft
+    from oracle.lookup import lookup_draft as oracle_draft
+    lens = [int(x) for x in a.price_ctx.split(",")]
+    per, texts = {}, {}
+    for L in lens:
+        ids = synth.uniform_ids(L, 151936, 5)
+        quote = np.concatenate([ids, ids[L // 3:L // 3 + 20]]).astype(np.int32)
+        loop = np.asarray((list(range(37)) * (L // 37 + 2))[:L], np.int32)
+        texts[L] = quote
+        per[str(L)] = {}
+        for name, text in (("quoting", quote), ("looping", loop)):
+            draft(text)
+            reps = max(20, 200 * 1024 // L)
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                t = draft(text)
+            ms = (time.perf_counter() - t0) / reps * 1e3
+            per[str(L)][name] = {"ms": round(ms, 4), "votes": t.votes, "nodes": len(t.parents),
+                                 "match_order": t.match_order}
+        print(f"[bench] lookup at ctx {L} done", file=sys.stderr, flush=True)
+    cpu = None
+    if not a.no_cpu_baseline:
+        t0, calls = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 5.0 or calls < len(lens):
+            oracle_draft(texts[lens[calls % len(lens)]].tolist())
+            calls += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(dt / calls * 1e3, 3), "unit": "ms per call", "cores": 1, "kind": "oracle",
+               "sample": f"{calls} calls over the quoting texts at {lens} (plain Python, one thread)"}
+    L = str(max(lens))
+    print(json.dumps({"metric": "lookup drafter ms per call (host)", "value": per[L]["quoting"]["ms"],
+                      "unit": "ms", "n_gpus": 0, "higher_is_better": False, "vs_baseline": None,
+                      "dtype": "int32", "data": "synthetic",
+                      "config": {"workload": f"lookup drafter, orders 2..8, depth 31, 31 nodes, text of {L} ids"},
+                      "per_ctx": per, "cpu_baseline": cpu}), flush=True)
 
 
 def cpu_baseline(shape, wl, kv, ctx, trees, sample, ns):

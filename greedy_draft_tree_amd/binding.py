@@ -10,6 +10,7 @@ import numpy as np
 TV_OK, TV_EINVAL, TV_ECAPACITY, TV_ESTATE, TV_EHIP = 0, -1, -2, -3, -4
 TV_MAX_NODES = 32
 TV_MAX_CANDIDATE = 256
+TV_LOOKUP_MAX_ORDER = 64
 TV_LAYER_ATTN, TV_LAYER_RECUR, TV_LAYER_DELTA = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -21,7 +22,7 @@ SYMBOLS = ("tv_create", "tv_destroy", "tv_last_error", "tv_bind", "tv_set_histor
            "tv_set_modifiers", "tv_set_sampling", "tv_prefill", "tv_prefill_dense", "tv_verify_tree", "tv_verify_trees",
            "tv_accept_walk", "tv_commit", "tv_round", "tv_ctx_len", "tv_profile_enable",
            "tv_profile_reset", "tv_profile_get", "tv_linear", "tv_head_top2", "tv_pack_weight",
-           "tv_staircut", "tv_residual_round")
+           "tv_staircut", "tv_residual_round", "tv_lookup_draft")
 
 
 class TVError(RuntimeError):
@@ -75,6 +76,7 @@ def load_library():
         "tv_pack_weight": ([P, P, I, I], I),
         "tv_staircut": ([P, P, P, I, P, P, F, F, P, P, P], I),
         "tv_residual_round": ([P, I, P, P, I, P, F, P, P, P, P, P], I),
+        "tv_lookup_draft": ([P, I, I, I, I, I, P, P, P, P, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

@@ -17,8 +17,10 @@
  * Around it: prompts (tv_prefill through the verify path, tv_prefill_dense
  * on the MFMA prefill kernels and the chunk grid), sampled requests
  * (tv_set_sampling: seeded Gumbel-max draws; tv_residual_round:
- * deterministic-candidate residual sampling), StairCut's cut of a candidate
- * tree (tv_staircut, host only), and kernel-level calls for tests and
+ * deterministic-candidate residual sampling), drafting on the host (the
+ * lookup drafter's tree from the request's own text, tv_lookup_draft, and
+ * StairCut's cut of a candidate tree, tv_staircut), and kernel-level calls
+ * for tests and
  * measurement (tv_linear, tv_head_top2, tv_pack_weight, tv_profile_*).
  *
  * Conventions shared by every call:
@@ -247,6 +249,35 @@ int tv_round(tv_ctx *ctx, int req, const int32_t *parents, const int32_t *tokens
 int tv_staircut(const int32_t *parents, const float *q, const int32_t *order, int n_nodes,
                 const float *price_tree_ms, const float *price_chain_ms, float draft_ms, float commit_ms,
                 int32_t *keep, int *n_keep, float *score);
+
+/* The lookup drafter over the request's own text ("Drafters and tree
+ * verify", The lookup drafter), host only: it copies text instead of
+ * predicting it.  An occurrence of order o is a start p with
+ * text[p .. p+o) equal to the last o tokens and p + o <= len - 1 (it is
+ * followed by at least one token).  The order used is the largest o in
+ * [min_order, max_order] with an occurrence; each of its occurrences is one
+ * vote, continuing with text[p+o .. p+o+max_depth) (shorter where the text
+ * ends).  A tree node is a token sequence that begins at least one
+ * continuation; q = (its votes) / (all votes), computed in double and
+ * rounded once to float: its vote share, the q StairCut takes.
+ *   text, len: the request's text (prompt and output so far, len >= 1); its
+ *     last token is the tree's root (the next verify's root).
+ *   1 <= min_order <= max_order <= TV_LOOKUP_MAX_ORDER (the pages use 2..8);
+ *   1 <= max_depth <= TV_MAX_CANDIDATE; 0 <= max_nodes < TV_MAX_CANDIDATE.
+ * At most max_nodes nodes are kept (the root excluded), best first by
+ * (votes descending, depth ascending, path ascending as a token sequence),
+ * an order in which ancestors come first.  Output (host arrays of at least
+ * max_nodes + 1 entries): parents, tokens, q of the kept tree in depth-first
+ * pre-order with siblings by (votes descending, token ascending), node 0 the
+ * root (q 1); order (at least max_nodes entries, may be NULL when max_nodes
+ * is 0): the kept nodes by admission, as output indices (StairCut's order);
+ * *n_nodes the nodes written, root included; *match_order the order used (0
+ * when nothing matched: the root alone) and *n_votes the vote count (either
+ * may be NULL).  TV_EINVAL for a bad argument or when memory runs out. */
+#define TV_LOOKUP_MAX_ORDER 64
+int tv_lookup_draft(const int32_t *text, int len, int min_order, int max_order, int max_depth, int max_nodes,
+                    int32_t *parents, int32_t *tokens, float *q, int32_t *order, int *n_nodes, int *match_order,
+                    int *n_votes);
 
 /* One round of deterministic-candidate residual tree sampling ("Algorithm
  * and correctness contract", Deterministic tree candidates and residual
