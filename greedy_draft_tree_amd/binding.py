@@ -76,7 +76,7 @@ def load_library():
         "tv_pack_weight": ([P, P, I, I], I),
         "tv_staircut": ([P, P, P, I, P, P, F, F, P, P, P], I),
         "tv_residual_round": ([P, I, P, P, I, P, F, P, P, P, P, P], I),
-        "tv_lookup_draft": ([P, I, I, I, I, I, P, P, P, P, P, P, P], I),
+        "tv_lookup_draft": ([P, I, I, I, I, I, F, P, P, P, P, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

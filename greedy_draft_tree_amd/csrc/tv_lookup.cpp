@@ -84,12 +84,13 @@ struct Tree {
 }  // namespace
 
 extern "C" int tv_lookup_draft(const int32_t *text, int len, int min_order, int max_order, int max_depth,
-                               int max_nodes, int32_t *parents, int32_t *tokens, float *q, int32_t *order,
-                               int *n_nodes, int *match_order, int *n_votes) {
+                               int max_nodes, float rho, int32_t *parents, int32_t *tokens, float *q,
+                               int32_t *order, int *n_nodes, int *match_order, int *n_votes) {
     if (!text || len < 1 || !parents || !tokens || !q || !n_nodes) return TV_EINVAL;
     if (min_order < 1 || max_order < min_order || max_order > TV_LOOKUP_MAX_ORDER) return TV_EINVAL;
     if (max_depth < 1 || max_depth > TV_MAX_CANDIDATE) return TV_EINVAL;
     if (max_nodes < 0 || max_nodes > TV_MAX_CANDIDATE - 1 || (max_nodes > 0 && !order)) return TV_EINVAL;
+    if (!(rho > 0.f && rho <= 1.f)) return TV_EINVAL;
     try {
         // match length of every earlier end position against the text's end
         int o = 0;
@@ -135,7 +136,9 @@ extern "C" int tv_lookup_draft(const int32_t *text, int len, int min_order, int 
             x.out = n;
             parents[n] = par;
             tokens[n] = x.token;
-            q[n] = id == 0 ? 1.0f : (float)((double)x.count / (double)V);
+            double decay = 1.0;   // rho^depth as depth products, in the oracle's order
+            for (int d = 0; d < x.depth; ++d) decay *= (double)rho;
+            q[n] = id == 0 ? 1.0f : (float)((double)x.count / (double)V * decay);
             ++n;
             std::sort(x.kids.begin(), x.kids.end(), [&t](int a, int b) {
                 const Node &u = t.nodes[a], &v = t.nodes[b];

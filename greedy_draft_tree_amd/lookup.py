@@ -4,7 +4,7 @@ drafter): a draft tree copied from the request's own text.
 ``draft`` calls ``tv_lookup_draft``: the longest match (orders min..max) of
 the text's last tokens among earlier occurrences, one vote per occurrence,
 and the best ``max_nodes`` nodes of the votes' continuation tree with their
-vote shares as q.  The result plugs into StairCut (``staircut.cut``): q and
+vote shares as q (times rho^depth: StairCut's continuation rate a level).  The result plugs into StairCut (``staircut.cut``): q and
 the admission order are what it takes.
 """
 from __future__ import annotations
@@ -26,8 +26,13 @@ class LookupTree(NamedTuple):
     votes: int
 
 
+STAIR_DECAY = 1.0 / 1.6   # StairCut's fixed continuation rate a level for lookup nodes
+
+
 def draft(text: Sequence[int], min_order: int = 2, max_order: int = 8, max_depth: int = 31,
-          max_nodes: int = 31) -> LookupTree:
+          max_nodes: int = 31, rho: float = 1.0) -> LookupTree:
+    """tv_lookup_draft.  q = vote share * rho^depth: rho = 1 gives the plain
+    shares, STAIR_DECAY the q StairCut takes with its fixed decay."""
     lib = load_library()
     t = _i32(text)
     if t.ndim != 1 or t.shape[0] < 1:
@@ -40,7 +45,9 @@ def draft(text: Sequence[int], min_order: int = 2, max_order: int = 8, max_depth
     q = np.empty(cap, np.float32)
     order = np.empty(max(max_nodes, 1), np.int32)
     n, o, v = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
-    rc = lib.tv_lookup_draft(_ptr(t), int(t.shape[0]), min_order, max_order, max_depth, max_nodes,
+    if not (0.0 < rho <= 1.0):
+        raise TVError(-1, "tv_lookup_draft: rho must lie in (0, 1]")
+    rc = lib.tv_lookup_draft(_ptr(t), int(t.shape[0]), min_order, max_order, max_depth, max_nodes, rho,
                              _ptr(parents), _ptr(tokens), _ptr(q), _ptr(order),
                              ctypes.byref(n), ctypes.byref(o), ctypes.byref(v))
     if rc != 0:

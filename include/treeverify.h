@@ -258,8 +258,11 @@ int tv_staircut(const int32_t *parents, const float *q, const int32_t *order, in
  * [min_order, max_order] with an occurrence; each of its occurrences is one
  * vote, continuing with text[p+o .. p+o+max_depth) (shorter where the text
  * ends).  A tree node is a token sequence that begins at least one
- * continuation; q = (its votes) / (all votes), computed in double and
- * rounded once to float: its vote share, the q StairCut takes.
+ * continuation; q = (its votes) / (all votes) * rho^depth, computed in
+ * double (rho^depth as depth products) and rounded once to float: its vote
+ * share times StairCut's continuation rate a level ("Drafters and tree
+ * verify", StairCut: a fixed decay of 1/1.6 a level, or a learned rate;
+ * 0 < rho <= 1, rho = 1 for the plain vote shares).
  *   text, len: the request's text (prompt and output so far, len >= 1); its
  *     last token is the tree's root (the next verify's root).
  *   1 <= min_order <= max_order <= TV_LOOKUP_MAX_ORDER (the pages use 2..8);
@@ -276,8 +279,8 @@ int tv_staircut(const int32_t *parents, const float *q, const int32_t *order, in
  * may be NULL).  TV_EINVAL for a bad argument or when memory runs out. */
 #define TV_LOOKUP_MAX_ORDER 64
 int tv_lookup_draft(const int32_t *text, int len, int min_order, int max_order, int max_depth, int max_nodes,
-                    int32_t *parents, int32_t *tokens, float *q, int32_t *order, int *n_nodes, int *match_order,
-                    int *n_votes);
+                    float rho, int32_t *parents, int32_t *tokens, float *q, int32_t *order, int *n_nodes,
+                    int *match_order, int *n_votes);
 
 /* One round of deterministic-candidate residual tree sampling ("Algorithm
  * and correctness contract", Deterministic tree candidates and residual

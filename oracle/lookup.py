@@ -26,7 +26,12 @@ Readings taken here (the pages leave them open):
 * output: node 0 is the root, the text's last token (the next verify's
   root), q = 1; then the kept nodes in depth-first pre-order with siblings by
   (count descending, token ascending); ``order`` lists the kept nodes by
-  admission (the best-first order above) as output indices.
+  admission (the best-first order above) as output indices;
+* ``rho`` is the continuation rate a level that StairCut's q multiplies in
+  ("Drafters and tree verify", StairCut: a fixed decay of 1/1.6 a level, or a
+  learned rate that lets a long verbatim copy keep its whole line): a node at
+  depth d gets q = (count / votes) * rho^d, rho^d taken as d products in fp64,
+  rounded once to fp32; rho = 1 gives the plain vote shares.
 """
 from typing import Dict, List, Sequence, Tuple
 
@@ -57,9 +62,9 @@ def node_counts(text: Sequence[int], starts: Sequence[int], o: int, max_depth: i
 
 
 def lookup_draft(text: Sequence[int], min_order: int = 2, max_order: int = 8, max_depth: int = 31,
-                 max_nodes: int = 31):
+                 max_nodes: int = 31, rho: float = 1.0):
     """(parents, tokens, q, order, o, votes) of the lookup tree; q as fp32
-    values (count / votes divided in fp64, rounded once)."""
+    values (count / votes * rho^depth in fp64, rounded once)."""
     import numpy as np
     text = [int(t) for t in text]
     o, starts = match_order(text, min_order, max_order)
@@ -86,7 +91,10 @@ def lookup_draft(text: Sequence[int], min_order: int = 2, max_order: int = 8, ma
             index[ch] = len(tokens)
             parents.append(index[path])
             tokens.append(ch[-1])
-            q.append(float(np.float32(counts[ch] / V)))
+            decay = 1.0
+            for _ in range(len(ch)):
+                decay *= float(np.float32(rho))
+            q.append(float(np.float32(counts[ch] / V * decay)))
             visit(ch)
 
     visit(())

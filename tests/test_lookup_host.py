@@ -44,7 +44,8 @@ def test_random_texts_bit_exact():
         text = _quoted(rng, L, vocab) if i % 2 else [int(x) for x in rng.integers(0, vocab, L)]
         mn = int(rng.integers(1, 4))
         mx = int(rng.integers(mn, 12))
-        _same(text, mn, mx, int(rng.integers(1, 40)), int(rng.integers(0, 64)))
+        rho = 1.0 if i % 3 else float(rng.choice([1 / 1.6, 0.9, 0.3]))
+        _same(text, mn, mx, int(rng.integers(1, 40)), int(rng.integers(0, 64)), rho)
 
 
 def test_long_texts_bit_exact():
@@ -53,6 +54,7 @@ def test_long_texts_bit_exact():
         text = _quoted(rng, L, vocab)
         for nodes in (31, 255):
             _same(text, 2, 8, 31, nodes)
+            _same(text, 2, 8, 31, nodes, 1 / 1.6)
 
 
 def test_edges():
@@ -87,14 +89,17 @@ def test_native_rejects_bad_pointers_and_sizes():
     qf = np.zeros(40, np.float32)
     n = ctypes.c_int(0)
     addr = lambda a: a.__array_interface__["data"][0]
-    assert lib.tv_lookup_draft(None, 4, 2, 8, 31, 31, addr(out), addr(out), addr(qf), addr(out), ctypes.byref(n),
+    assert lib.tv_lookup_draft(None, 4, 2, 8, 31, 31, 1.0, addr(out), addr(out), addr(qf), addr(out), ctypes.byref(n),
                                None, None) == -1
-    assert lib.tv_lookup_draft(addr(t), 0, 2, 8, 31, 31, addr(out), addr(out), addr(qf), addr(out), ctypes.byref(n),
+    assert lib.tv_lookup_draft(addr(t), 0, 2, 8, 31, 31, 1.0, addr(out), addr(out), addr(qf), addr(out), ctypes.byref(n),
                                None, None) == -1
-    assert lib.tv_lookup_draft(addr(t), 4, 2, 8, 31, 5, addr(out), addr(out), addr(qf), None, ctypes.byref(n),
+    assert lib.tv_lookup_draft(addr(t), 4, 2, 8, 31, 5, 1.0, addr(out), addr(out), addr(qf), None, ctypes.byref(n),
                                None, None) == -1
-    assert lib.tv_lookup_draft(addr(t), 4, 2, 8, 31, 0, addr(out), addr(out), addr(qf), None, ctypes.byref(n),
+    assert lib.tv_lookup_draft(addr(t), 4, 2, 8, 31, 0, 1.0, addr(out), addr(out), addr(qf), None, ctypes.byref(n),
                                None, None) == 0 and n.value == 1
+    for rho in (0.0, -0.5, 1.5, float("nan")):
+        assert lib.tv_lookup_draft(addr(t), 4, 2, 8, 31, 5, rho, addr(out), addr(out), addr(qf), addr(out),
+                                   ctypes.byref(n), None, None) == -1
 
 
 def test_lookup_tree_feeds_staircut():
@@ -112,3 +117,28 @@ def test_lookup_tree_feeds_staircut():
     steep = [0.0] + [10.0 + (40.0 if r > 8 else 0.0) for r in range(1, 33)]
     keep2, _ = cut(t.parents, t.q, t.order, steep, steep, 1.0, 0.5)
     assert keep2 == list(range(8))
+
+
+def test_decay_keeps_or_cuts_a_copied_line():
+    """StairCut on the MI355X price shape (a verify costs little more at 32
+    rows than at 8): with the fixed decay of 1/1.6 a level a copied line is cut
+    back, with a continuation rate of 1 it is kept whole, as the pages say of
+    their learned rate for long verbatim copies."""
+    from greedy_draft_tree_amd.lookup import STAIR_DECAY
+    line = synth.uniform_ids(40, 151936, 14).tolist()
+    text = synth.uniform_ids(60, 151936, 15).tolist() + line + line[:10]
+    prices = [0.0] + [10.0 + 0.03 * r for r in range(1, 33)]
+    whole = draft(text, 2, 8, 31, 31)
+    decayed = draft(text, 2, 8, 31, 31, STAIR_DECAY)
+    assert decayed.parents == whole.parents and decayed.order == whole.order
+    for d in range(1, 32):
+        r = 1.0
+        for _ in range(d):
+            r *= float(np.float32(STAIR_DECAY))
+        assert decayed.q[d] == float(np.float32(r))
+    keep, _ = cut(whole.parents, whole.q, whole.order, prices, prices, 1.0, 0.5)
+    assert len(keep) == 32
+    # decayed: sum q = (1 - 0.625^n) / 0.6 for n nodes; at 7 / 15 / 31 nodes the
+    # score is 2.6043 / 11.74, 2.6652 / 11.98, 2.6667 / 12.46 ms: 15 nodes win
+    keep, _ = cut(decayed.parents, decayed.q, decayed.order, prices, prices, 1.0, 0.5)
+    assert len(keep) == 16

@@ -55,6 +55,11 @@ def test_periodic_text_closed_form(P, L, o, depth, nodes):
     want = [1.0] + [float(np.float32((V - math.ceil(d / P) + 1) / V)) for d in range(1, n + 1)]
     assert q == want
     assert order == list(range(1, n + 1))
+    # with a continuation rate a level: the same tree, q(d) times rho^d
+    rho = 0.625
+    p2, t2, q2, o2, _, _ = lookup_draft(text, 2, o, depth, nodes, rho)
+    assert (p2, t2, o2) == (parents, tokens, order)
+    assert q2 == [1.0] + [float(np.float32((V - math.ceil(d / P) + 1) / V * rho ** d)) for d in range(1, n + 1)]
 
 
 def _path(parents, tokens, i):
