@@ -80,6 +80,48 @@ def test_c0_dense_prefill_against_oracle(c0, n, chunk):
         assert am[i] == oam[i] or ogap[i] <= 1.0
 
 
+def test_c0_dense_prefill_largest_chunk():
+    """The largest chunk the library takes (2048 rows) and a ragged second
+    chunk, against the oracle's sequential decode of 2100 tokens; a resume at
+    the grid point 2048 equals the cold prefill bit for bit."""
+    _gpu()
+    import workloads
+    wl = workloads.build(synth.C0, max_ctx=2200, max_req=2, weight_device="cuda", host_copy=True)
+    orc = oracle.Oracle(synth.C0, wl.host_weights)
+    n, chunk = 2100, 2048
+    prompt = synth.uniform_ids(n + 1, synth.C0.vocab, 91)
+    _say("c0 dense prefill", n, chunk)
+    wl.tv.set_history(0, [], 0)
+    first = wl.tv.prefill_dense(0, prompt[:-1], chunk=chunk)
+    seq = orc.new_seq(cap=2200)
+    last = seq.commit(prompt[:-1])
+    a, _, _, g = oracle.top2(last)
+    assert first == a or g <= 1.0, (first, a, g)
+    for (l, nm), t in wl.kv[0].items():
+        got = t[:, :n].float().cpu().numpy().astype(np.float64)
+        want = (seq.K if nm == "k" else seq.V)[l][:, :n]
+        err = np.abs(got - want)
+        tol = 2.0 ** -6 * np.maximum(1.0, np.abs(want))
+        assert (err <= tol).mean() > 0.999 and err.max() < 0.1, (l, nm, float(err.max()))
+    parents = synth.random_tree(32, 5)
+    tokens = synth.tree_tokens(parents, synth.C0.vocab, 8, root_token=int(prompt[-1]))
+    am, gap = wl.tv.verify_tree(0, parents, tokens, logits=wl.logits)
+    ol = orc.tree_scores(seq, parents, tokens)
+    gl = wl.logits[:len(parents)].cpu().numpy().astype(np.float64)
+    assert np.abs(gl - ol).max() <= LOGIT_ATOL, float(np.abs(gl - ol).max())
+    oam, ogap = oracle.tree_decisions(ol, parents, tokens, seq.history)
+    for i in range(len(parents)):
+        assert am[i] == oam[i] or ogap[i] <= 1.0
+    # resumed at the grid point from the cold rows
+    for key, t in wl.kv[1].items():
+        t.zero_()
+        t[:, :chunk].copy_(wl.kv[0][key][:, :chunk])
+    wl.tv.set_history(1, prompt[:chunk].tolist(), chunk)
+    assert wl.tv.prefill_dense(1, prompt[chunk:n], chunk=chunk) == first
+    for key, t in wl.kv[1].items():
+        assert torch.equal(t[:, :n], wl.kv[0][key][:, :n]), key
+
+
 def test_c0_resume_on_the_grid_is_bitwise_cold(c0):
     wl, _ = c0
     chunk, n = 64, 230
