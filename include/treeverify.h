@@ -50,6 +50,11 @@
  *   - A verify writes the tree's KV rows at cache slots ctx_len + i but does
  *     not move ctx_len; only tv_commit does.  Verifying again without a commit
  *     discards the previous tree.
+ *   - A context is used by one thread at a time: calls on the same tv_ctx
+ *     must not overlap (it owns activation scratch, pinned staging and the
+ *     last error message).  Separate contexts may run on separate threads,
+ *     each on its own stream.  tv_accept_walk, tv_staircut and
+ *     tv_lookup_draft keep no state and may be called from any thread.
  */
 #ifndef TREEVERIFY_H
 #define TREEVERIFY_H
