@@ -99,14 +99,18 @@ struct AttnArgs {
     int ztarget;        // prefill: splits of the cache keys per block (about)
 };
 
-// Cache keys per attention split for about `splits` splits, in whole LDS
-// chunks.  A verify takes 32 (a function of the context length only).
+// Cache keys per attention split for at most `splits` splits, in whole LDS
+// chunks.  A verify takes at most 31 cache splits (a function of the
+// context length only): with the tree's own split that is 32 workgroups a KV
+// head, 256 for 8 KV heads, one per CU (a workgroup fills its CU's register
+// file), so no workgroup waits for a second round.
+constexpr int kVerifyCacheSplits = 31;
 __host__ __device__ inline int attn_span_n(int ctx, int splits) {
     const int chunks = (ctx + kAttnChunk - 1) / kAttnChunk;
     const int per = (chunks + splits - 1) / splits;
     return (per < 1 ? 1 : per) * kAttnChunk;
 }
-__host__ __device__ inline int attn_span(int ctx) { return attn_span_n(ctx, 32); }
+__host__ __device__ inline int attn_span(int ctx) { return attn_span_n(ctx, kVerifyCacheSplits); }
 
 struct RopeArgs {
     const float *part;   // QKV projection partial sums (row-contiguous split-K layout)

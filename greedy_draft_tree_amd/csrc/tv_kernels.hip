@@ -1014,34 +1014,49 @@ __global__ __launch_bounds__(64 * (kAttnComputeWaves + kAttnLoaderWaves)) void k
     const uint16_t *Kb = a.Kc + (size_t)kvh * a.cap * D;
     const uint16_t *Vb = a.Vc + (size_t)kvh * a.cap * D;
     // stage the chunk of keys starting at c0 into buffer buf, by threads
-    // [0, nt) of a group (tg = this thread's index in it); every load of a
-    // pass (SB pieces of K and of V per thread) is issued before any store
-    constexpr int SB = 4;
+    // [0, nt) of a group (tg = this thread's index in it).  Task j loads
+    // pieces 2j and 2j+1 of K (consecutive tasks read consecutive 32 bytes)
+    // and piece j / NPAIR of the key pair j % NPAIR of V: the key pair runs
+    // fastest, so each transposed V store is one dword holding two keys of
+    // one dimension and a half-wave's stores fall in distinct banks.  Every
+    // load of a pass (TB tasks per thread) is issued before any store.
+    constexpr int NPAIR = CH / 2;
+    constexpr int NTASK = NPAIR * KC;
+    constexpr int TB = 2;
     auto stage = [&](int c0, int buf, int tg, int nt) {
         const int cn = min(CH, nkeys - c0);
-        for (int base = 0; base < CH * KC; base += SB * nt) {
-            uint4 kv[SB], vv[SB];
+        for (int base = 0; base < NTASK; base += TB * nt) {
+            uint4 kv[TB][2], vv[TB][2];
 #pragma unroll
-            for (int i = 0; i < SB; ++i) {
-                const int idx = base + i * nt + tg;
-                const int kk = idx / KC, p = idx % KC;
-                kv[i] = uint4{0u, 0u, 0u, 0u};
-                vv[i] = uint4{0u, 0u, 0u, 0u};
-                if (idx < CH * KC && kk < cn) {
+            for (int i = 0; i < TB; ++i) {
+                const int j = base + i * nt + tg;
+                const int kk = (2 * j) / KC, p = (2 * j) % KC;
+                const int kp = j % NPAIR, pv = j / NPAIR;
+                const bool in = j < NTASK;
+                kv[i][0] = kv[i][1] = vv[i][0] = vv[i][1] = uint4{0u, 0u, 0u, 0u};
+                if (in && kk < cn) {
                     const size_t off = (size_t)(key0 + c0 + kk) * D + p * 8;
-                    kv[i] = ld16(Kb + off);
-                    vv[i] = ld16(Vb + off);
+                    kv[i][0] = ld16(Kb + off);
+                    kv[i][1] = ld16(Kb + off + 8);
                 }
+                if (in && 2 * kp < cn) vv[i][0] = ld16(Vb + (size_t)(key0 + c0 + 2 * kp) * D + pv * 8);
+                if (in && 2 * kp + 1 < cn) vv[i][1] = ld16(Vb + (size_t)(key0 + c0 + 2 * kp + 1) * D + pv * 8);
             }
 #pragma unroll
-            for (int i = 0; i < SB; ++i) {
-                const int idx = base + i * nt + tg;
-                if (idx < CH * KC) {
-                    const int kk = idx / KC, p = idx % KC;
-                    *reinterpret_cast<uint4 *>(Ks[buf] + kk * D + ((p ^ (kk & (KC - 1))) << 3)) = kv[i];
-                    const uint16_t *ve = reinterpret_cast<const uint16_t *>(&vv[i]);
+            for (int i = 0; i < TB; ++i) {
+                const int j = base + i * nt + tg;
+                if (j < NTASK) {
+                    const int kk = (2 * j) / KC, p = (2 * j) % KC;
+                    const int kp = j % NPAIR, pv = j / NPAIR;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) Vt[buf][(p * 8 + e) * VSTR + kk] = ve[e];
+                    for (int h = 0; h < 2; ++h)
+                        *reinterpret_cast<uint4 *>(Ks[buf] + kk * D + (((p + h) ^ (kk & (KC - 1))) << 3)) = kv[i][h];
+                    const uint16_t *v0 = reinterpret_cast<const uint16_t *>(&vv[i][0]);
+                    const uint16_t *v1 = reinterpret_cast<const uint16_t *>(&vv[i][1]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        *reinterpret_cast<uint32_t *>(Vt[buf] + (pv * 8 + e) * VSTR + 2 * kp) =
+                            (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
                 }
             }
         }

@@ -609,7 +609,7 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     auto cleanup = [&](int rc) { tv_destroy(c); return rc; };
     const int R = kMaxRows;
     const int H = m.hidden, D = m.head_dim;
-    c->ns_max = 32 + 1;  // at most 32 cache splits (attn_span) plus the tree split
+    c->ns_max = 32 + 1;  // at most 32 cache splits (attn_span's 31; a prefill block's 32) plus the tree split
     const size_t RP = (size_t)kMaxRows * kMaxGroup;
     hipError_t e = hipSuccess;
 #define ALLOC(p, bytes) if (e == hipSuccess) e = hipMalloc((void **)&(p), (bytes))
