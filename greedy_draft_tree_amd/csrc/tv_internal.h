@@ -162,8 +162,8 @@ struct RecurCommitArgs {
 
 // launch wrappers (tv_kernels.hip); each returns hipGetLastError()
 // X = embedding rows of the pass's tokens, Y = RMSNorm(X) with weights w
-hipError_t launch_embed_norm(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H,
-                             const uint16_t *w, float eps, uint16_t *X, uint16_t *Y);
+hipError_t launch_embed_norm(hipStream_t s, const uint16_t *emb, const PassMeta *meta, PassMeta *meta_out, int M,
+                             int H, const uint16_t *w, float eps, uint16_t *X, uint16_t *Y);
 // X = bf16(X + bf16(sum of the S split-K partials P)), Y = RMSNorm(X) with weights w
 hipError_t launch_resid_norm(hipStream_t s, const float *P, int S, int M, int H, const uint16_t *w, float eps,
                              uint16_t *X, uint16_t *Y);

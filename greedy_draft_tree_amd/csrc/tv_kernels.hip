@@ -194,14 +194,27 @@ enum RowMode { ROW_EMBED = 0, ROW_RESID = 1 };
 
 __device__ __forceinline__ float4 ld_f4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 
+// ROW_EMBED reads the pass metadata where the host wrote it (coherent pinned
+// memory, read over the bus): each row takes its token, and workgroup 0 also
+// copies the whole record to meta_out in device memory for the later kernels
+// of the pass, which replaces a separate copy before the pass.
 template <int MODE>
 __global__ __launch_bounds__(kRowThreads) void k_row_norm(const uint16_t *__restrict__ emb,
                                                           const PassMeta *__restrict__ meta,
+                                                          PassMeta *__restrict__ meta_out,
                                                           const float *__restrict__ P, int S, int H,
                                                           const uint16_t *__restrict__ w, float eps,
                                                           uint16_t *__restrict__ X, uint16_t *__restrict__ Y) {
     __shared__ float red[kRowThreads / 64];
     const int m = blockIdx.x, t = threadIdx.x;
+    if constexpr (MODE == ROW_EMBED) {
+        if (m == 0 && meta_out) {
+            static_assert(sizeof(PassMeta) % 4 == 0, "the metadata record is copied in words");
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(meta);
+            uint32_t *dst = reinterpret_cast<uint32_t *>(meta_out);
+            for (int i = t; i < (int)(sizeof(PassMeta) / 4); i += blockDim.x) dst[i] = src[i];
+        }
+    }
     const int n0 = 8 * t;
     const bool ok = n0 < H;
     const uint4 z = {0u, 0u, 0u, 0u};
@@ -1615,19 +1628,19 @@ __global__ __launch_bounds__(256) void k_commit_kv(uint16_t *const *__restrict__
 
 static int row_threads(int H) { return ((H / 8 + 63) / 64) * 64; }
 
-hipError_t launch_embed_norm(hipStream_t s, const uint16_t *emb, const PassMeta *meta, int M, int H,
-                             const uint16_t *w, float eps, uint16_t *X, uint16_t *Y) {
+hipError_t launch_embed_norm(hipStream_t s, const uint16_t *emb, const PassMeta *meta, PassMeta *meta_out, int M,
+                             int H, const uint16_t *w, float eps, uint16_t *X, uint16_t *Y) {
     if (H % 8 || H > 8 * kRowThreads) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_row_norm<ROW_EMBED>, dim3(M), dim3(row_threads(H)), 0, s, emb, meta, nullptr, 0, H, w,
-                       eps, X, Y);
+    hipLaunchKernelGGL(k_row_norm<ROW_EMBED>, dim3(M), dim3(row_threads(H)), 0, s, emb, meta, meta_out, nullptr, 0,
+                       H, w, eps, X, Y);
     return hipGetLastError();
 }
 
 hipError_t launch_resid_norm(hipStream_t s, const float *P, int S, int M, int H, const uint16_t *w, float eps,
                              uint16_t *X, uint16_t *Y) {
     if (H % 8 || H > 8 * kRowThreads || S < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_row_norm<ROW_RESID>, dim3(M), dim3(row_threads(H)), 0, s, nullptr, nullptr, P, S, H, w,
-                       eps, X, Y);
+    hipLaunchKernelGGL(k_row_norm<ROW_RESID>, dim3(M), dim3(row_threads(H)), 0, s, nullptr, nullptr, nullptr, P, S,
+                       H, w, eps, X, Y);
     return hipGetLastError();
 }
 

@@ -90,7 +90,10 @@ struct tv_ctx {
     float *gemm_partial = nullptr;   // split-K partial tiles
     size_t gemm_partial_floats = 0;
     // pinned host staging
-    PassMeta *h_meta = nullptr;
+    // pass metadata: written by the host into coherent pinned memory (h_meta;
+    // hd_meta the same memory seen from the GPU); the pass's first kernel
+    // copies it to d_meta
+    PassMeta *h_meta = nullptr, *hd_meta = nullptr;
     // per-row results of a pass (RowResult), written by the top-2 kernel
     // straight into coherent pinned host memory (hd_res: the same memory
     // seen from the GPU)
@@ -435,14 +438,13 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
     }
     const int M = total;
     hipStream_t s = c->stream;
-    clear_results(c, M);
-    HIPCHECK(c, hipMemcpyAsync(c->d_meta, c->h_meta, sizeof(PassMeta), hipMemcpyHostToDevice, s));
+    clear_results(c, M);   // its release fence also publishes the metadata, which the GPU reads where it lies
 
     const int H = m.hidden, D = m.head_dim, QH = m.n_qhead, KVH = m.n_kvhead;
     // X: residual stream; XN = RMSNorm(X) with the weights of the next
     // projection that reads it (xn_w), written by the kernel that updates X.
     const uint16_t *xn_w = c->attn_norm[0];
-    LAUNCH(c, "embed_norm", launch_embed_norm(s, c->emb, c->d_meta, M, H, xn_w, m.eps, c->X, c->XN));
+    LAUNCH(c, "embed_norm", launch_embed_norm(s, c->emb, c->hd_meta, c->d_meta, M, H, xn_w, m.eps, c->X, c->XN));
     auto normed = [&](GemmArgs &g, const uint16_t *w) -> int {
         if (xn_w != w) return fail(c, TV_ESTATE, "internal: normalised rows hold another norm");
         g.X = c->XN; g.ldx = H;
@@ -649,8 +651,9 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     }
     ALLOC(c->gemm_partial, c->gemm_partial_floats * 4);
 #undef ALLOC
-    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_meta, sizeof(PassMeta), hipHostMallocDefault);
     const unsigned res_flags = hipHostMallocCoherent | hipHostMallocMapped;
+    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_meta, sizeof(PassMeta), res_flags);
+    if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&c->hd_meta, c->h_meta, 0);
     if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_res, R * sizeof(RowResult), res_flags);
     if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&c->hd_res, c->h_res, 0);
     if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_resu, R * sizeof(double), hipHostMallocDefault);
