@@ -192,10 +192,12 @@ struct RowResult {
 constexpr uint32_t kGapEmpty = 0x7fc0deadu;   // a NaN pattern no gap takes
 hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M, RowResult *res);
 // residual tree sampling decisions of the pass's n rows (logits [n][ldl]
-// fp32, the pass's metadata, u_row[n] device doubles): res[i].argmax = -(j+1)
-// to accept candidate j of row i, else the emitted token; gap bits 0
+// fp32, the pass's metadata, u_row[n] device doubles, parts device scratch
+// of kResidualPartBytes per row): res[i].argmax = -(j+1) to accept candidate
+// j of row i, else the emitted token; gap bits 0
+constexpr size_t kResidualPartBytes = 64 * 16;   // per row: at most 64 chunks of (max, sum) doubles
 hipError_t launch_residual(hipStream_t s, const float *logits, int ldl, int V, const PassMeta *meta, int n, float T,
-                           const double *u_row, RowResult *res);
+                           const double *u_row, void *parts, RowResult *res);
 hipError_t launch_recur_tree(hipStream_t s, int D, const RecurArgs &a);
 hipError_t launch_recur_commit(hipStream_t s, int D, const RecurCommitArgs &a, int n_layers);
 hipError_t launch_commit_kv(hipStream_t s, uint16_t *const *kv_ptrs, int n_layers, int KVH,

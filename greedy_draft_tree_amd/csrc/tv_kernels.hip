@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <climits>
 
 #include "tv_internal.h"
 
@@ -752,108 +753,249 @@ __global__ __launch_bounds__(256) void k_top2_reduce(const Top2 *__restrict__ pa
 // total; fp64 weights and sums.  The result is written to pinned host memory
 // as the argmax field of the row's record: -(j+1) to accept candidate j,
 // else the emitted token.
+//
+// Two kernels.  k_residual_chunks spreads each row over chunks of
+// kResChunk ids (one workgroup each, 16 consecutive ids a thread): the
+// chunk's maximum m_c and the sum s_c of exp(x - m_c) over its non-candidate
+// ids.  k_residual_decide (one workgroup a row) takes the row's maximum M,
+// weighs the chunks by s_c exp(m_c - M), walks the candidates, then the
+// chunks, then the crossing chunk's per-thread sums and ids.
 
-__global__ __launch_bounds__(1024) void k_residual(const float *__restrict__ logits, int ldl, int V,
-                                                   const PassMeta *__restrict__ meta, int n, float T,
-                                                   const double *__restrict__ u_row, RowResult *res) {
-    constexpr int NT = 1024;
-    __shared__ uint32_t pathbits[(1 << 18) / 32];   // the row's path tokens (V <= 2^18)
-    __shared__ double red[NT / 64];
-    __shared__ double seg[NT];
-    __shared__ int cand[kMaxRows];
-    __shared__ int ncand_s;
-    const int i = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const float *row = logits + (size_t)i * ldl;
-    const int words = (V + 31) >> 5;
-    for (int w = t; w < words; w += NT) pathbits[w] = 0u;
-    if (t == 0) {
-        int k = 0;
-        for (int j = i + 1; j < n; ++j)   // children of row i, in index order
-            if (meta->depth[j] == meta->depth[i] + 1 && ((meta->anc[j] >> i) & 1u)) cand[k++] = meta->tok[j];
-        ncand_s = k;
-    }
+constexpr int kResChunk = 4096, kResThreads = 256, kResPer = kResChunk / kResThreads;
+constexpr int kResMaxChunks = 64;   // V <= 2^18
+
+struct ResPart {
+    double m, s;
+};
+
+// The chunk's path tokens (the repetition penalty's prior ids besides the
+// history) and the row's candidate tokens as bit masks over the chunk's ids.
+__device__ __forceinline__ void res_masks(const PassMeta *meta, int i, int n, int c0, uint32_t *pmask,
+                                          uint32_t *cmask) {
+    const int t = threadIdx.x;
+    if (t < kResChunk / 32) pmask[t] = cmask[t] = 0u;
     __syncthreads();
     const HeadMods &md = meta->mods[meta->row_req[i]];
     if (md.rep != 1.0f && t < meta->path_len[i]) {
-        const int v = meta->path_tok[i * kMaxRows + t];
-        atomicOr(&pathbits[v >> 5], 1u << (v & 31));
+        const unsigned v = (unsigned)(meta->path_tok[i * kMaxRows + t] - c0);
+        if (v < (unsigned)kResChunk) atomicOr(&pmask[v >> 5], 1u << (v & 31));
+    }
+    if (t > i && t < n && meta->depth[t] == meta->depth[i] + 1 && ((meta->anc[t] >> i) & 1u)) {
+        const unsigned v = (unsigned)(meta->tok[t] - c0);
+        if (v < (unsigned)kResChunk) atomicOr(&cmask[v >> 5], 1u << (v & 31));
     }
     __syncthreads();
-    const int ncand = ncand_s;
-    // modified score of id v over T (fp64), -inf for a masked id
-    auto xval = [&](int v) -> double {
-        float s = row[v];
-        if (md.rep != 1.0f) {
-            const uint32_t prior = (md.hist_bits ? md.hist_bits[v >> 5] : 0u) | pathbits[v >> 5];
-            if ((prior >> (v & 31)) & 1u) s = s > 0.f ? s / md.rep : s * md.rep;
-        }
-        if (md.bias) s = s + md.bias[v];
-        if (md.allow_bits && !((md.allow_bits[v >> 5] >> (v & 31)) & 1u)) s = -INFINITY;
-        return (double)s / (double)T;
-    };
-    // the maximum
+}
+
+// modified score over T (fp64: times 1/T, within an ulp of the quotient) of
+// id v with its raw logit s; -inf if masked
+__device__ __forceinline__ double res_score(float s, int v, const HeadMods &md, bool in_path, double invT) {
+    if (md.rep != 1.0f) {
+        const bool prior = in_path || (md.hist_bits && ((md.hist_bits[v >> 5] >> (v & 31)) & 1u));
+        if (prior) s = s > 0.f ? s / md.rep : s * md.rep;
+    }
+    if (md.bias) s = s + md.bias[v];
+    if (md.allow_bits && !((md.allow_bits[v >> 5] >> (v & 31)) & 1u)) s = -INFINITY;
+    return (double)s * invT;
+}
+
+__global__ __launch_bounds__(kResThreads) void k_residual_chunks(const float *__restrict__ logits, int ldl, int V,
+                                                                 const PassMeta *__restrict__ meta, int n, float T,
+                                                                 ResPart *__restrict__ parts) {
+    __shared__ uint32_t pmask[kResChunk / 32], cmask[kResChunk / 32];
+    __shared__ double red[kResThreads / 64];
+    const int c = blockIdx.x, i = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int c0 = c * kResChunk;
+    const double invT = 1.0 / (double)T;
+    res_masks(meta, i, n, c0, pmask, cmask);
+    const HeadMods &md = meta->mods[meta->row_req[i]];
+    const float *row = logits + (size_t)i * ldl;
+    double x[kResPer];
     double mx = -INFINITY;
-    for (int v = t; v < V; v += NT) mx = fmax(mx, xval(v));
+#pragma unroll
+    for (int k = 0; k < kResPer; ++k) {
+        const int o = t * kResPer + k, v = c0 + o;
+        x[k] = v < V ? res_score(row[v], v, md, (pmask[o >> 5] >> (o & 31)) & 1u, invT) : -INFINITY;
+        mx = fmax(mx, x[k]);
+    }
+#pragma unroll
     for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
     if (lane == 0) red[wave] = mx;
     __syncthreads();
-    mx = -INFINITY;
-    for (int w = 0; w < NT / 64; ++w) mx = fmax(mx, red[w]);
+    mx = red[0];
+#pragma unroll
+    for (int w = 1; w < kResThreads / 64; ++w) mx = fmax(mx, red[w]);
     __syncthreads();
-    // each thread sums a contiguous segment of ids; candidates count apart
-    const int per = (V + NT - 1) / NT, v0 = t * per, v1 = min(V, v0 + per);
-    auto wt = [&](int v) -> double {
-        const double x = xval(v);
-        return x == -INFINITY ? 0.0 : exp(x - mx);
-    };
-    auto is_cand = [&](int v) -> bool {
-        for (int k = 0; k < ncand; ++k)
-            if (cand[k] == v) return true;
-        return false;
-    };
-    double sum = 0.0;
-    for (int v = v0; v < v1; ++v)
-        if (!is_cand(v)) sum += wt(v);
-    seg[t] = sum;
+    double sum = 0.0;   // ascending ids, candidates apart
+#pragma unroll
+    for (int k = 0; k < kResPer; ++k) {
+        const int o = t * kResPer + k;
+        if (x[k] != -INFINITY && !((cmask[o >> 5] >> (o & 31)) & 1u)) sum += exp(x[k] - mx);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    if (lane == 0) red[wave] = sum;
     __syncthreads();
     if (t == 0) {
-        double candw[kMaxRows], csum = 0.0, rest = 0.0;
-        for (int k = 0; k < ncand; ++k) {
-            candw[k] = wt(cand[k]);
-            csum += candw[k];
-        }
-        for (int w = 0; w < NT; ++w) rest += seg[w];
+        double tot = 0.0;
+        for (int w = 0; w < kResThreads / 64; ++w) tot += red[w];
+        parts[(size_t)i * gridDim.x + c] = ResPart{mx, tot};
+    }
+}
+
+// inclusive prefix sum over the 64 lanes of a wave (a fixed order of adds)
+__device__ __forceinline__ double wave_prefix(double x, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+__global__ __launch_bounds__(kResThreads) void k_residual_decide(const float *__restrict__ logits, int ldl, int V,
+                                                                 const PassMeta *__restrict__ meta, int n, float T,
+                                                                 const double *__restrict__ u_row,
+                                                                 const ResPart *__restrict__ parts, int nchunks,
+                                                                 RowResult *res) {
+    __shared__ uint32_t pmask[kResChunk / 32], cmask[kResChunk / 32];
+    __shared__ double seg[kResThreads];
+    __shared__ int lastv[kResThreads];
+    __shared__ double wts[kResChunk];   // the crossing chunk's weights (0 for candidates and masked ids)
+    __shared__ double W[kResMaxChunks], mc[kResMaxChunks], candw[kMaxRows];   // chunk and candidate weights
+    __shared__ double sh_M, sh_r;
+    __shared__ int sh_chunk, sh_out;
+    const int i = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const HeadMods &md = meta->mods[meta->row_req[i]];
+    const float *row = logits + (size_t)i * ldl;
+    const ResPart *pr = parts + (size_t)i * nchunks;
+    const double invT = 1.0 / (double)T;
+    // candidates: node t is a child of row i (children in index order)
+    const bool is_cand = t > i && t < n && meta->depth[t] == meta->depth[i] + 1 && ((meta->anc[t] >> i) & 1u);
+    if (wave == 0) {   // the row's maximum over its chunks
+        double m = lane < nchunks ? pr[lane].m : -INFINITY;
+        if (lane < nchunks) mc[lane] = m;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
+        if (lane == 0) sh_M = m;
+    }
+    __syncthreads();
+    const double M = sh_M;
+    if (t < nchunks) W[t] = mc[t] == -INFINITY ? 0.0 : pr[t].s * exp(mc[t] - M);
+    if (t < kMaxRows) candw[t] = 0.0;
+    if (is_cand) {
+        const int v = meta->tok[t];
+        bool in_path = false;
+        if (md.rep != 1.0f)
+            for (int q = 0; q < meta->path_len[i]; ++q) in_path |= meta->path_tok[i * kMaxRows + q] == v;
+        const double xv = res_score(row[v], v, md, in_path, invT);
+        candw[t] = xv == -INFINITY ? 0.0 : exp(xv - M);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // running sums over the candidates (lane j: node j) and the chunks (lane c)
+        const uint64_t cmaskl = __ballot(is_cand);   // wave 0 holds nodes 0..63: every candidate
+        const double pc = wave_prefix(lane < kMaxRows ? candw[lane] : 0.0, lane);
+        const double pw = wave_prefix(lane < nchunks ? W[lane] : 0.0, lane);
+        const double csum = __shfl(pc, 63), rest = __shfl(pw, 63);
         const double thr = u_row[i] * (csum + rest);
-        int outv = -1;
-        double c = 0.0;
-        for (int k = 0; k < ncand && outv < 0; ++k) {
-            c += candw[k];
-            if (c > thr) outv = -(k + 1);
-        }
-        if (outv == -1 && ncand > 0 && c > thr) outv = -ncand;   // (not reached: handled above)
-        if (outv == -1) {
-            // the residual: the segment where the running sum crosses, then its id
-            double r = thr - c;
-            int w = 0;
-            for (; w < NT - 1; ++w) {
-                if (seg[w] > r) break;
-                r -= seg[w];
-            }
-            int last = -1;
-            for (int v = w * per; v < min(V, (w + 1) * per) && outv < 0; ++v) {
-                if (is_cand(v)) continue;
-                const double x = wt(v);
-                if (x > 0.0) last = v;
-                if (x > r) outv = v;
-                else r -= x;
-            }
-            if (outv < 0) {   // rounding at the very end: the last id with weight
-                for (int v = V - 1; v >= 0 && last < 0; --v)
-                    if (!is_cand(v) && wt(v) > 0.0) last = v;
-                outv = last;
+        int out = INT_MIN, chunk = -1;
+        double r = 0.0;
+        const uint64_t hitc = __ballot(pc > thr);   // the first crossing lane is a candidate's
+        if (hitc) {
+            const int j = __ffsll((unsigned long long)hitc) - 1;
+            out = -(__popcll(cmaskl & ((1ull << j) - 1ull)) + 1);
+        } else {
+            r = thr - csum;
+            const uint64_t hitw = __ballot(lane < nchunks && pw > r);
+            if (hitw) {
+                chunk = __ffsll((unsigned long long)hitw) - 1;
+                const double before = __shfl(pw, chunk > 0 ? chunk - 1 : 0);
+                r -= chunk > 0 ? before : 0.0;
+            } else {   // rounding at the very end: the last chunk with weight, past its end
+                const uint64_t pos = __ballot(lane < nchunks && W[lane] > 0.0);
+                chunk = pos ? 63 - __clzll((unsigned long long)pos) : -1;
+                r = INFINITY;
             }
         }
-        *reinterpret_cast<volatile uint64_t *>(res + i) = (uint64_t)(uint32_t)outv;   // gap bits 0: done
+        if (lane == 0) {
+            sh_r = r;
+            sh_chunk = chunk;
+            sh_out = out;
+        }
+    }
+    __syncthreads();
+    const int chunk = sh_chunk;
+    if (sh_out == INT_MIN && chunk >= 0) {
+        const int c0 = chunk * kResChunk;
+        res_masks(meta, i, n, c0, pmask, cmask);
+        double sum = 0.0;
+        int last = -1;
+#pragma unroll
+        for (int k = 0; k < kResPer; ++k) {
+            const int o = t * kResPer + k, v = c0 + o;
+            double w = 0.0;
+            if (v < V && !((cmask[o >> 5] >> (o & 31)) & 1u)) {
+                const double xv = res_score(row[v], v, md, (pmask[o >> 5] >> (o & 31)) & 1u, invT);
+                if (xv != -INFINITY) w = exp(xv - M);
+            }
+            wts[o] = w;
+            sum += w;
+            if (w > 0.0) last = v;
+        }
+        seg[t] = sum;
+        lastv[t] = last;
+        __syncthreads();
+        if (wave == 0) {
+            // lane l takes the sums of threads 4l..4l+3 (in order); the first
+            // lane whose running sum exceeds r holds the crossing thread
+            const double r = sh_r;
+            double a[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) a[k] = seg[4 * lane + k];
+            const double loc = ((a[0] + a[1]) + a[2]) + a[3];
+            const double pre = wave_prefix(loc, lane);
+            const double up = __shfl_up(pre, 1);   // every lane takes part in the shuffle
+            const double excl = lane > 0 ? up : 0.0;
+            const uint64_t hit = __ballot(pre > r);
+            int out = -1;
+            if (hit) {
+                const int L = __ffsll((unsigned long long)hit) - 1;
+                if (lane == L) {
+                    double rr = r - excl;
+                    for (int k = 0; k < 4 && out < 0; ++k) {
+                        if (a[k] > rr) {
+                            const int tt = 4 * lane + k;   // the crossing thread: walk its ids
+                            for (int q = 0; q < kResPer && out < 0; ++q) {
+                                const double w = wts[tt * kResPer + q];
+                                if (w == 0.0) continue;   // candidates, masked ids, ids past V
+                                if (w > rr) out = c0 + tt * kResPer + q;
+                                else rr -= w;
+                            }
+                            if (out < 0) out = lastv[tt];   // rounding inside the thread's ids
+                        } else {
+                            rr -= a[k];
+                        }
+                    }
+                }
+                out = __shfl(out, L);
+            }
+            if (out < 0) {   // rounding: the chunk's last id with weight
+                int lv = -1;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) lv = lastv[4 * lane + k] >= 0 ? lastv[4 * lane + k] : lv;
+                const uint64_t has = __ballot(lv >= 0);
+                out = has ? __shfl(lv, 63 - __clzll((unsigned long long)has)) : -1;
+            }
+            if (lane == 0) sh_out = out;
+        }
+        __syncthreads();
+    }
+    if (t == 0) {
+        int out = sh_out;
+        if (out == INT_MIN) out = -1;   // nothing carries weight (every id masked): the first candidate's slot
+        // one 8-byte store: the decision, and gap bits 0 (not the empty pattern) to mark the record done
+        *reinterpret_cast<volatile uint64_t *>(res + i) = (uint64_t)(uint32_t)out;
     }
 }
 
@@ -1753,9 +1895,13 @@ hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t
 }
 
 hipError_t launch_residual(hipStream_t s, const float *logits, int ldl, int V, const PassMeta *meta, int n, float T,
-                           const double *u_row, RowResult *res) {
-    if (n < 1 || n > kMaxRows || V > (1 << 18) || !(T > 0.f)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_residual, dim3(n), dim3(1024), 0, s, logits, ldl, V, meta, n, T, u_row, res);
+                           const double *u_row, void *parts, RowResult *res) {
+    const int nchunks = (V + kResChunk - 1) / kResChunk;
+    if (n < 1 || n > kMaxRows || V < 1 || nchunks > kResMaxChunks || !(T > 0.f)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_residual_chunks, dim3(nchunks, n), dim3(kResThreads), 0, s, logits, ldl, V, meta, n, T,
+                       static_cast<ResPart *>(parts));
+    hipLaunchKernelGGL(k_residual_decide, dim3(n), dim3(kResThreads), 0, s, logits, ldl, V, meta, n, T, u_row,
+                       static_cast<const ResPart *>(parts), nchunks, res);
     return hipGetLastError();
 }
 

@@ -101,6 +101,7 @@ struct tv_ctx {
     RowResult *hd_res = nullptr;
     // residual tree sampling: per-row uniforms (pinned staging and device copy)
     double *h_resu = nullptr, *d_resu = nullptr;
+    void *d_resparts = nullptr;   // per-row chunk maxima and sums of the residual decision
     int ns_max = 0;
 
     // profiling
@@ -184,8 +185,11 @@ void clear_results(tv_ctx *c, int M) {
     std::atomic_thread_fence(std::memory_order_release);
 }
 
-// Wait until the top-2 kernel has filled every row's record: spin on the
-// pinned host copy (lower wake-up latency than a stream synchronisation),
+// Wait until the kernel that decides the rows has filled every row's record
+// (one 8-byte store each, so a gap field other than the empty pattern means
+// the whole record has landed; the argmax field may hold any value, -1
+// included): spin on the pinned host copy (lower wake-up latency than a
+// stream synchronisation),
 // polling the stream now and then so that a failed or drained stream ends
 // the wait.  With event profiling on, synchronise the stream so the events
 // can be read.
@@ -197,12 +201,12 @@ int wait_results(tv_ctx *c, int M) {
     volatile RowResult *r = c->h_res;
     int m = 0;
     for (long it = 1;; ++it) {
-        while (m < M && r[m].argmax != -1 && r[m].gap_bits != kGapEmpty) ++m;
+        while (m < M && r[m].gap_bits != kGapEmpty) ++m;
         if (m == M) break;
         if ((it & 4095) == 0) {
             const hipError_t q = hipStreamQuery(c->stream);
             if (q == hipSuccess) {
-                while (m < M && r[m].argmax != -1 && r[m].gap_bits != kGapEmpty) ++m;
+                while (m < M && r[m].gap_bits != kGapEmpty) ++m;
                 if (m == M) break;
                 return fail(c, TV_EHIP, "pass finished without the result of row %d", m);
             }
@@ -658,6 +662,7 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&c->hd_res, c->h_res, 0);
     if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_resu, R * sizeof(double), hipHostMallocDefault);
     if (e == hipSuccess) e = hipMalloc((void **)&c->d_resu, R * sizeof(double));
+    if (e == hipSuccess) e = hipMalloc(&c->d_resparts, R * kResidualPartBytes);
     if (e != hipSuccess) return cleanup(TV_EHIP);
     // RoPE table: angle pos * theta^(-2i/D) in fp64, cos and sin rounded to fp32
     {
@@ -682,7 +687,7 @@ void tv_destroy(tv_ctx *c) {
     else hipDeviceSynchronize();
     void *dev[] = {c->X, c->XN, c->QR, c->ATT, c->ACT, c->zeros, c->logits, c->part, c->po, c->pm, c->pl,
                    c->rope_cos, c->rope_sin, c->d_meta, c->gemm_partial, c->pX, c->pXN, c->pQKV, c->pQR,
-                   c->pATT, c->pACT, c->pAB, c->pTok, c->ppo, c->ppm, c->ppl, c->d_resu};
+                   c->pATT, c->pACT, c->pAB, c->pTok, c->ppo, c->ppm, c->ppl, c->d_resu, c->d_resparts};
     for (void *p : dev)
         if (p) hipFree(p);
     for (auto &q : c->reqs) {
@@ -952,7 +957,7 @@ int tv_residual_round(tv_ctx *c, int req, const int32_t *parents, const int32_t 
     HIPCHECK(c, hipMemcpyAsync(c->d_resu, c->h_resu, (size_t)n_nodes * sizeof(double), hipMemcpyHostToDevice, s));
     const float *lg = logits_dev ? logits_dev : c->logits;
     LAUNCH(c, "residual", launch_residual(s, lg, c->m.vocab, c->m.vocab, c->d_meta, n_nodes, temperature, c->d_resu,
-                                          c->hd_res));
+                                          c->d_resparts, c->hd_res));
     rc = wait_results(c, n_nodes);
     if (rc) return rc;
     // the walk: from the root, accept a child or emit and stop

@@ -68,6 +68,29 @@ def test_c0_residual_rounds(c0, T):
     assert same_as_oracle >= 8
 
 
+def test_c0_residual_accepts_the_first_child(c0):
+    """A round whose first candidate is the model's near-certain token (a low
+    temperature) accepts it: the decision that names candidate 0 is encoded
+    as -1 in the row's record, the same value that marks a record empty, so
+    completion must be read from the record's other field."""
+    wl, orc = c0
+    prompt = synth.uniform_ids(30, synth.C0.vocab, 12)
+    wl.tv.set_history(0, [], 0)
+    wl.tv.prefill(0, prompt[:-1])
+    seq = orc.new_seq(cap=512)
+    seq.commit(prompt[:-1])
+    root = int(prompt[-1])
+    g = int(wl.tv.verify_tree(0, [-1], [root], logits=wl.logits)[0][0])
+    other = (g + 1) % synth.C0.vocab
+    parents, tokens = [-1, 0, 0], [root, g, other]
+    u = np.full(32, 0.01)   # accepted whenever p(g) > 0.01, certain for the argmax at T = 0.05
+    _say("c0 residual accepts candidate 0")
+    path, emitted = wl.tv.residual_round(0, parents, tokens, 0.05, u, logits=wl.logits)
+    gl = wl.logits[:3].cpu().numpy()
+    opath, oemit, margin = oracle.residual_walk(gl, parents, tokens, seq.history, 0.05, u)
+    assert path[:2] == [0, 1] and (path, emitted) == (opath, oemit), (path, emitted, opath, oemit, margin)
+
+
 def test_c0_residual_errors_leave_state(c0):
     from greedy_draft_tree_amd import TVError, TV_EINVAL
     wl, _ = c0
