@@ -268,6 +268,53 @@ def test_hybrid_dense_prefill(kind):
     assert torch.equal(wl.logits[:len(parents)], cold_logits)
 
 
+HYBW = {k: synth.scaled(synth.C1, name, n_layer=4, kinds=[k, synth.ATTN, k, k])
+        for k, name in ((synth.RECUR, "c3_layers4_pf"), (synth.DELTA, "c3d_layers4_pf"))}
+
+
+@pytest.mark.parametrize("kind", [synth.RECUR, synth.DELTA], ids=["gated", "delta"])
+def test_hybrid_full_width_dense_prefill(kind):
+    """Recurrent layers at full width (40 heads x 128 x 128 fp32 states,
+    hidden 5120) in the dense prefill: 70 prompt rows in chunks of 64 (chains
+    of 32, 32 and 6 rows) against the oracle's sequential decode (states, last
+    token, a following verify at the oracle's bf16-drift tolerance)."""
+    _gpu()
+    import workloads
+    from test_gpu_parity import check_rows
+    shape = HYBW[kind]
+    wl = workloads.build(shape, max_ctx=128, max_req=1, weight_device="cuda", host_copy=True)
+    orc = oracle.Oracle(shape, wl.host_weights)
+    s0 = synth.state0(shape, seed=6)
+    for l, t in wl.states[0].items():
+        t.copy_(s0[l].cuda())
+    torch.cuda.synchronize()
+    n = 70
+    prompt = synth.uniform_ids(n + 1, shape.vocab, 23)
+    _say("full-width hybrid dense prefill", shape.name, n)
+    wl.tv.set_history(0, [], 0)
+    first = wl.tv.prefill_dense(0, prompt[:-1], chunk=64)
+    seq = orc.new_seq(cap=128, s0=s0)
+    last = seq.commit(prompt[:-1])
+    a, _, _, g = oracle.top2(last)
+    assert first == a or g <= 2.0, (first, a, g)
+    torch.cuda.synchronize()
+    for l, t in wl.states[0].items():
+        got = t.cpu().numpy().astype(np.float64)
+        err = np.abs(got - seq.S[l]).max()
+        print(f"[{shape.name} prefill state {l}] max|dS| {err:.3g}", flush=True)
+        assert err <= 2e-2 * max(1.0, np.abs(seq.S[l]).max()), (l, err)
+    parents = synth.spine_tree(8, 2)
+    tokens = synth.tree_tokens(parents, shape.vocab, 3, root_token=int(prompt[-1]))
+    am, gap = wl.tv.verify_tree(0, parents, tokens, logits=wl.logits)
+    ol = orc.tree_scores(seq, parents, tokens)
+    ex = oracle.Oracle(shape, wl.host_weights, exact=True)
+    es = ex.new_seq(cap=128, s0=s0)
+    es.commit(prompt[:-1])
+    oe = ex.tree_scores(es, parents, tokens)
+    check_rows(wl.logits[:8].cpu().numpy(), am, gap, ol, parents, tokens, seq.history,
+               what=f"{shape.name} after dense prefill", orc_exact=oe)
+
+
 def test_c1_width_dense_prefill():
     """Full width (hidden 5120, 40 q heads, ffn 17408, the fp32 head): 96
     prompt rows in chunks of 64 against the oracle, then a verify."""
