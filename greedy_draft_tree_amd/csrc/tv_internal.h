@@ -79,12 +79,20 @@ inline int gemm_splits(int N, int K) {
     return s < 1 ? 1 : s;
 }
 
+// One request of a verify pass: its rows [row0, row0 + n) of the pass, this
+// layer's cache, its committed context and its attention cache splits.
+struct PassReq {
+    uint16_t *Kc, *Vc;  // cache [n_kvhead][cap][D]
+    int row0, n, ctx;
+    int span, nsplit;   // cache keys per split and cache splits (the tree's own split follows them)
+};
+
 struct AttnArgs {
     const uint16_t *Q;  // rotated queries, rows row0.., [rows, n_qhead*D]
-    const uint16_t *Kc; // cache [n_kvhead][cap][D]
+    const uint16_t *Kc; // cache [n_kvhead][cap][D] (prefill)
     const uint16_t *Vc;
     const PassMeta *meta;
-    float *po;          // partials [n_kvhead][ns][kMaxRows*kMaxGroup][D]
+    float *po;          // partials [n_kvhead][ns][kMaxRows*kMaxGroup][D] (prefill: one such block per z)
     float *pm;          // [n_kvhead][ns][kMaxRows*kMaxGroup]
     float *pl;
     int row0, n, ctx, cap, G, n_qhead, ns, n_ctx_split;
@@ -97,6 +105,12 @@ struct AttnArgs {
     // any block has, plus one)
     int zrows, M;
     int ztarget;        // prefill: splits of the cache keys per block (about)
+    // verify (nreq > 0): grid.z runs over the pass's requests, each with its
+    // own cache, context and splits; n, span and ns are the largest of any
+    // request (they size the launch), and the partials of a query row sit at
+    // its pass row, so requests never share a slot
+    int nreq;
+    PassReq rq[kMaxRows];
 };
 
 // Cache keys per attention split for at most `splits` splits, in whole LDS
@@ -116,10 +130,11 @@ struct RopeArgs {
     const float *part;   // QKV projection partial sums (row-contiguous split-K layout)
     int S;               // its k-range splits
     uint16_t *q_out;     // [rows, QH*D]
-    uint16_t *Kc, *Vc;   // cache [KVH][cap][D]
     const float *cosT, *sinT; // [max_pos][D/2]
     const PassMeta *meta;
-    int row0, n, ctx, cap, QH, KVH, D;
+    int M, cap, QH, KVH, D;   // M: rows of the pass
+    int nreq;            // requests of the pass, in row order
+    PassReq rq[kMaxRows];
 };
 
 struct RecurArgs {

@@ -1005,19 +1005,24 @@ __global__ __launch_bounds__(kResThreads) void k_residual_decide(const float *__
 // and tree verify", Tree verify through recurrent layers: position = depth,
 // every node at its depth-first slot).
 
-// Grid (node, slice): thread u of a node handles one q pair, one k pair or
-// one v element: units [0, QH*D/2) q, then KVH*D/2 k, then KVH*D v.
+// Grid (row of the pass, slice): thread u of a row handles one q pair, one
+// k pair or one v element: units [0, QH*D/2) q, then KVH*D/2 k, then KVH*D
+// v.  Every request of the pass is served by the one launch: a row finds its
+// request (rows are in request order) and writes that request's cache.
 __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
-    const int i = blockIdx.x;
-    const int m = a.row0 + i;
+    const int m = blockIdx.x;
+    int r = 0;
+    while (r + 1 < a.nreq && m >= a.rq[r + 1].row0) ++r;
+    const PassReq &rq = a.rq[r];
+    const int i = m - rq.row0;   // node index within its request
     const int D = a.D, half = D / 2;
     const int u = blockIdx.y * 256 + threadIdx.x;
     const int nq = a.QH * half, nk = a.KVH * half, nv = a.KVH * D;
     if (u >= nq + nk + nv) return;
-    const int pos = a.ctx + a.meta->depth[m];
+    const int pos = rq.ctx + a.meta->depth[m];
     // projection outputs: bf16 of the partial sums (the QKV projection's rounding point)
     auto qkv = [&](int n) { return bfround(psum(a.part, a.S, 1, 0, m, n)); };
-    const size_t slot = (size_t)(a.ctx + i);
+    const size_t slot = (size_t)(rq.ctx + i);
     if (u < nq + nk) {
         const bool isq = u < nq;
         const int uu = isq ? u : u - nq;
@@ -1025,12 +1030,12 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
         const int col = (isq ? 0 : a.QH * D) + h * D + p;
         const float x0 = qkv(col), x1 = qkv(col + half);
         const float c = a.cosT[(size_t)pos * half + p], s = a.sinT[(size_t)pos * half + p];
-        uint16_t *o = isq ? a.q_out + (size_t)m * a.QH * D + h * D : a.Kc + ((size_t)h * a.cap + slot) * D;
+        uint16_t *o = isq ? a.q_out + (size_t)m * a.QH * D + h * D : rq.Kc + ((size_t)h * a.cap + slot) * D;
         o[p] = f2bf(x0 * c - x1 * s);
         o[p + half] = f2bf(x1 * c + x0 * s);
     } else {
         const int uu = u - nq - nk, h = uu / D, d = uu % D;
-        a.Vc[((size_t)h * a.cap + slot) * D + d] = f2bf(qkv((a.QH + a.KVH) * D + h * D + d));
+        rq.Vc[((size_t)h * a.cap + slot) * D + d] = f2bf(qkv((a.QH + a.KVH) * D + h * D + d));
     }
 }
 
@@ -1142,9 +1147,21 @@ __global__ __launch_bounds__(64 * (kAttnComputeWaves + kAttnLoaderWaves)) void k
     const int lane = tid & 63, wave = tid >> 6;
     const int hf = lane >> 5, c = lane & 31;
     const int G = a.G;
-    // this block's rows, context and splits (a prefill block of a chain, or the pass's tree)
+    // this block's rows, context, splits and cache (a prefill block of a
+    // chain, or one request's tree in a verify pass)
     int n = a.n, row0 = a.row0, ctx = a.ctx, span = a.span, nsplit = a.n_ctx_split;
-    if (a.zrows > 0) {
+    const uint16_t *Kc = a.Kc, *Vc = a.Vc;
+    if (a.nreq > 0) {
+        const PassReq &rq = a.rq[z];
+        n = rq.n;
+        row0 = rq.row0;
+        ctx = rq.ctx;
+        span = rq.span;
+        nsplit = rq.nsplit;
+        Kc = rq.Kc;
+        Vc = rq.Vc;
+        if (split > nsplit) return;            // a request with fewer splits: the whole workgroup leaves
+    } else if (a.zrows > 0) {
         row0 = z * a.zrows;
         n = min(a.zrows, a.M - row0);
         ctx = a.ctx + row0;
@@ -1164,10 +1181,10 @@ __global__ __launch_bounds__(64 * (kAttnComputeWaves + kAttnLoaderWaves)) void k
     const int t = rowok ? row / G : 0, hh = rowok ? row % G : 0;
     // keys of the block's own rows visible to row t: its ancestors and itself
     // (a prefill chain: rows 0..t)
-    const uint32_t anc = a.zrows > 0 ? (t >= 31 ? 0xffffffffu : ((2u << t) - 1u)) : a.meta->anc[a.row0 + t];
+    const uint32_t anc = a.zrows > 0 ? (t >= 31 ? 0xffffffffu : ((2u << t) - 1u)) : a.meta->anc[row0 + t];
 
-    const uint16_t *Kb = a.Kc + (size_t)kvh * a.cap * D;
-    const uint16_t *Vb = a.Vc + (size_t)kvh * a.cap * D;
+    const uint16_t *Kb = Kc + (size_t)kvh * a.cap * D;
+    const uint16_t *Vb = Vc + (size_t)kvh * a.cap * D;
     // stage the chunk of keys starting at c0 into buffer buf, by threads
     // [0, nt) of a group (tg = this thread's index in it).  Task j loads
     // pieces 2j and 2j+1 of K (consecutive tasks read consecutive 32 bytes)
@@ -1329,7 +1346,9 @@ __global__ __launch_bounds__(64 * (kAttnComputeWaves + kAttnLoaderWaves)) void k
 
     if (!rowok || hf > 1) return;
     const int RP = kMaxRows * kMaxGroup;
-    const size_t pb = (((size_t)z * gridDim.y + kvh) * a.ns + split) * RP + row;
+    // a prefill block's partials at its z; a verify row's at its pass row
+    const size_t pb = a.nreq > 0 ? ((size_t)kvh * a.ns + split) * RP + row0 * G + row
+                                 : (((size_t)z * gridDim.y + kvh) * a.ns + split) * RP + row;
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
 #pragma unroll
@@ -1348,13 +1367,19 @@ __global__ __launch_bounds__(D) void k_attn_combine(AttnArgs a, uint16_t *__rest
     const int G = a.G, kvh = h / G, row = t * G + (h % G);
     const int RP = kMaxRows * kMaxGroup;
     int ns = a.ns, row0 = a.row0;
-    if (a.zrows > 0) {   // a prefill block: its own split count
+    if (a.nreq > 0) {    // request z of a verify pass: its own rows and split count
+        const PassReq &rq = a.rq[z];
+        if (t >= rq.n) return;
+        row0 = rq.row0;
+        ns = rq.nsplit + 1;
+    } else if (a.zrows > 0) {   // a prefill block: its own split count
         row0 = z * a.zrows;
         if (row0 + t >= a.M) return;
         const int ctx = a.ctx + row0, span = attn_span_n(ctx, a.ztarget);
         ns = (ctx + span - 1) / span + 1;
     }
-    const size_t b0 = (((size_t)z * (a.n_qhead / G) + kvh) * a.ns) * RP + row;
+    const size_t b0 = a.nreq > 0 ? ((size_t)kvh * a.ns) * RP + row0 * G + row
+                                 : (((size_t)z * (a.n_qhead / G) + kvh) * a.ns) * RP + row;
     if (d < ns) {
         ms[d] = a.pm[b0 + (size_t)d * RP];
         wl[d] = a.pl[b0 + (size_t)d * RP];
@@ -1850,8 +1875,11 @@ hipError_t launch_pack(hipStream_t s, const uint16_t *src, uint16_t *dst, int N,
 }
 
 hipError_t launch_rope_kv(hipStream_t s, const RopeArgs &a) {
+    if (a.nreq < 1 || a.nreq > kMaxRows || a.M < 1 || a.M > kMaxRows || a.rq[0].row0 != 0 ||
+        a.rq[a.nreq - 1].row0 + a.rq[a.nreq - 1].n != a.M)
+        return hipErrorInvalidValue;
     const int units = a.QH * a.D / 2 + a.KVH * a.D / 2 + a.KVH * a.D;
-    hipLaunchKernelGGL(k_rope_kv, dim3(a.n, (units + 255) / 256), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_rope_kv, dim3(a.M, (units + 255) / 256), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1877,8 +1905,13 @@ hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a) {
     if (rb > kAttnComputeWaves) return hipErrorInvalidValue;
     // loader waves only when a split spans more than one chunk of keys
     const int lw = a.span > kAttnChunk ? kAttnLoaderWaves : 0;
-    const int nz = a.zrows > 0 ? (a.M + a.zrows - 1) / a.zrows : 1;
+    const int nz = a.nreq > 0 ? a.nreq : a.zrows > 0 ? (a.M + a.zrows - 1) / a.zrows : 1;
     if (a.zrows > 0 && (a.zrows > kMaxRows || a.M < 1)) return hipErrorInvalidValue;
+    if (a.nreq > kMaxRows || (a.nreq > 0 && a.zrows > 0)) return hipErrorInvalidValue;
+    for (int r = 0; r < a.nreq; ++r)   // the launch is sized by the largest request
+        if (a.rq[r].n > a.n || a.rq[r].nsplit + 1 > a.ns || a.rq[r].span > a.span ||
+            (a.rq[r].row0 + a.rq[r].n) * a.G > kMaxRows * kMaxGroup)
+            return hipErrorInvalidValue;
     const dim3 grid(a.ns, a.n_qhead / a.G, nz), block(64 * (rb + lw));
     if (D == 128) hipLaunchKernelGGL(k_attn<128>, grid, block, 0, s, a);
     else if (D == 64) hipLaunchKernelGGL(k_attn<64>, grid, block, 0, s, a);
@@ -1887,7 +1920,7 @@ hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a) {
 }
 
 hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t *out) {
-    const dim3 grid(a.n, a.n_qhead, a.zrows > 0 ? (a.M + a.zrows - 1) / a.zrows : 1);
+    const dim3 grid(a.n, a.n_qhead, a.nreq > 0 ? a.nreq : a.zrows > 0 ? (a.M + a.zrows - 1) / a.zrows : 1);
     if (D == 128) hipLaunchKernelGGL(k_attn_combine<128>, grid, dim3(128), 0, s, a, out);
     else if (D == 64) hipLaunchKernelGGL(k_attn_combine<64>, grid, dim3(64), 0, s, a, out);
     else return hipErrorInvalidValue;

@@ -466,29 +466,36 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
             g.W = c->wqkv[l]; g.M = M; g.N = (QH + 2 * KVH) * D; g.K = H;
             int S = 0;
             GEMMP(c, "gemm_qkv", g, S);
+            // one launch of each kernel serves every request of the pass
+            RopeArgs ra{};
+            ra.part = c->gemm_partial; ra.S = S; ra.q_out = c->QR;
+            ra.cosT = c->rope_cos; ra.sinT = c->rope_sin; ra.meta = c->d_meta;
+            ra.M = M; ra.cap = m.max_ctx; ra.QH = QH; ra.KVH = KVH; ra.D = D; ra.nreq = n_req;
+            AttnArgs aa{};
+            aa.Q = c->QR; aa.meta = c->d_meta; aa.po = c->po; aa.pm = c->pm; aa.pl = c->pl;
+            aa.cap = m.max_ctx; aa.G = c->G; aa.n_qhead = QH;
+            aa.scale = (float)(1.0 / std::sqrt((double)D));
+            aa.nreq = n_req;
             for (int r = 0; r < n_req; ++r) {
                 Req &q = c->reqs[reqs[r]];
-                RopeArgs ra{};
-                ra.part = c->gemm_partial; ra.S = S; ra.q_out = c->QR; ra.Kc = q.K[l]; ra.Vc = q.V[l];
-                ra.cosT = c->rope_cos; ra.sinT = c->rope_sin; ra.meta = c->d_meta;
-                ra.row0 = row0s[r]; ra.n = n_nodes[r]; ra.ctx = q.ctx_len; ra.cap = m.max_ctx;
-                ra.QH = QH; ra.KVH = KVH; ra.D = D;
-                LAUNCH(c, "rope_kv", launch_rope_kv(s, ra));
+                PassReq &p = ra.rq[r];
+                p.Kc = q.K[l]; p.Vc = q.V[l];
+                p.row0 = row0s[r]; p.n = n_nodes[r]; p.ctx = q.ctx_len;
+                p.span = attn_span(q.ctx_len);
+                p.nsplit = (q.ctx_len + p.span - 1) / p.span;
+                aa.rq[r] = p;
+                aa.n = std::max(aa.n, p.n);
+                aa.span = std::max(aa.span, p.span);
+                aa.ns = std::max(aa.ns, p.nsplit + 1);
             }
-            for (int r = 0; r < n_req; ++r) {
-                Req &q = c->reqs[reqs[r]];
-                AttnArgs aa{};
-                aa.Q = c->QR; aa.Kc = q.K[l]; aa.Vc = q.V[l]; aa.meta = c->d_meta;
-                aa.po = c->po; aa.pm = c->pm; aa.pl = c->pl;
-                aa.row0 = row0s[r]; aa.n = n_nodes[r]; aa.ctx = q.ctx_len; aa.cap = m.max_ctx;
-                aa.G = c->G; aa.n_qhead = QH;
-                aa.span = attn_span(q.ctx_len);
-                aa.n_ctx_split = (q.ctx_len + aa.span - 1) / aa.span;
-                aa.ns = aa.n_ctx_split + 1;
-                aa.scale = (float)(1.0 / std::sqrt((double)D));
-                LAUNCH(c, "attn", launch_attn(s, D, aa));
-                LAUNCH(c, "attn_combine", launch_attn_combine(s, D, aa, c->ATT));
-            }
+            // attention takes the longest contexts first: the grid is dispatched
+            // in request order, and a short request's workgroups then fill the
+            // CUs the long ones leave rather than holding them back (partials sit
+            // at pass rows, so the order changes no result)
+            std::stable_sort(aa.rq, aa.rq + n_req, [](const PassReq &x, const PassReq &y) { return x.ctx > y.ctx; });
+            LAUNCH(c, "rope_kv", launch_rope_kv(s, ra));
+            LAUNCH(c, "attn", launch_attn(s, D, aa));
+            LAUNCH(c, "attn_combine", launch_attn_combine(s, D, aa, c->ATT));
         } else {
             const int rl = c->recur_index[l];
             // one projection over the q/k/v rows stacked on the gate rows
