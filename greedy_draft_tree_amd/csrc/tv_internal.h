@@ -10,7 +10,8 @@ constexpr int kMaxRows = 32;   // rows of one pass
 constexpr int kMaxGroup = 8;   // query heads per KV head
 constexpr int kAttnChunk = 64;  // keys staged in LDS at a time
 constexpr int kAttnComputeWaves = 5;  // query rows G*n <= 160: one wave per 32
-constexpr int kAttnLoaderWaves = 2;   // waves that stage the next chunk while the others compute
+constexpr int kAttnWaves = 8;         // waves of an attention workgroup that stages chunks: the register file
+                                       // holds 2 waves a SIMD, and every wave beyond the compute waves loads
 constexpr int kRecurSlices = 4; // value-column slices per head in the recurrent read-out
 
 // Candidate pair of a top-2 search: best (v1, i1) and runner-up (v2, i2),

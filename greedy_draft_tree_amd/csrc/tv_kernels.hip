@@ -1123,15 +1123,16 @@ __global__ __launch_bounds__(1024) void k_norm_dense(const int32_t *__restrict__
 // lane already holds, and V^T is staged in LDS with the same order.  P is
 // split into bf16 high and low parts (two MFMAs) so P.V keeps ~16 bits of P.
 // The softmax runs in base 2 (scores times scale * log2 e, exp2).  When a
-// split spans several 64-key chunks, two extra loader waves stage the next
-// chunk into the second LDS buffer while the compute waves use the first.
+// split spans several 64-key chunks, the workgroup's other waves (up to 8 in
+// all) stage the next chunk into the second LDS buffer while the compute
+// waves use the first.
 // Each workgroup writes its unnormalised partial (max in base-2 units, sum,
 // output); the combine kernel merges splits in index order.  Split
 // boundaries depend only on ctx, so a row's result does not depend on the
 // other rows.
 
 template <int D>
-__global__ __launch_bounds__(64 * (kAttnComputeWaves + kAttnLoaderWaves)) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
     constexpr int CH = kAttnChunk;     // keys per LDS stage
     constexpr int KC = D / 8;          // 16-byte chunks per key row
     constexpr int VSTR = CH + 4;       // bf16 stride of a transposed V row
@@ -1903,8 +1904,11 @@ hipError_t launch_norm_dense(hipStream_t s, const int32_t *tok, const uint16_t *
 hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a) {
     const int rb = (a.G * a.n + 31) / 32;   // compute waves
     if (rb > kAttnComputeWaves) return hipErrorInvalidValue;
-    // loader waves only when a split spans more than one chunk of keys
-    const int lw = a.span > kAttnChunk ? kAttnLoaderWaves : 0;
+    // loader waves only when a split spans more than one chunk of keys: all
+    // the waves the CU holds beyond the compute waves, so that a chunk is
+    // staged in one pass of loads for up to 24 rows (two passes with two
+    // loader waves cost 10 % at 8k context)
+    const int lw = a.span > kAttnChunk ? kAttnWaves - rb : 0;
     const int nz = a.nreq > 0 ? a.nreq : a.zrows > 0 ? (a.M + a.zrows - 1) / a.zrows : 1;
     if (a.zrows > 0 && (a.zrows > kMaxRows || a.M < 1)) return hipErrorInvalidValue;
     if (a.nreq > kMaxRows || (a.nreq > 0 && a.zrows > 0)) return hipErrorInvalidValue;
