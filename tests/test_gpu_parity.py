@@ -502,6 +502,58 @@ def test_c4_joint_modifiers_wrong_drafter(c1):
             roots[r] = emitted[0]
 
 
+
+def test_c1_width_four_requests_one_pass_equal_alone():
+    """Four requests in one pass of 32 rows (1, 7, 8 and 16 nodes at
+    contexts 0, 100, 1024 and 5000).  One RoPE, attention and combine launch
+    serves them all, each with its own cache splits: none (the tree alone),
+    short splits of one chunk, and 320-key splits staged by loader waves.
+    Each request's logits, argmax and gap equal its alone verify bit for bit
+    ("Exactness", Parallel requests), and the 100-context request's rows
+    match the oracle."""
+    _gpu()
+    import workloads
+    ctxs, ns = (0, 100, 1024, 5000), (1, 7, 8, 16)
+    _say("c1-width four-request build")
+    wl = workloads.build(synth.C1, max_ctx=max(ctxs) + 64, max_req=4, weight_device="cuda", host_copy=True)
+    kv1, hist1, trees = None, None, []
+    for r, (ctx, n) in enumerate(zip(ctxs, ns)):
+        hist = synth.uniform_ids(ctx, synth.C1.vocab, 80 + r) if ctx else []
+        kv = synth.kv_cache(synth.C1, ctx, seed=90 + r, cap=ctx) if ctx else None
+        workloads.load_context(wl, r, ctx, 0, history=hist,
+                               src_kv={k: v.cuda() for k, v in kv.items()} if kv else None)
+        if r == 1:
+            kv1, hist1 = kv, list(hist)
+        parents = synth.spine_tree(n, 100 + r)
+        root = int(hist[-1]) if ctx else 7
+        trees.append((parents, synth.tree_tokens(parents, synth.C1.vocab, 110 + r, root_token=root)))
+    _say("c1-width four-request joint verify")
+    am_j, gap_j = wl.tv.verify_trees([0, 1, 2, 3], [t[0] for t in trees], [t[1] for t in trees], logits=wl.logits)
+    joint = wl.logits[:32].clone()
+    row0 = 0
+    for r, (parents, tokens) in enumerate(trees):
+        n = len(parents)
+        _say("c1-width alone", r, "ctx", ctxs[r], "n", n)
+        am_a, gap_a = wl.tv.verify_tree(r, parents, tokens, logits=wl.logits)
+        assert torch.equal(wl.logits[:n], joint[row0:row0 + n]), f"request {r}: joint != alone"
+        np.testing.assert_array_equal(am_a, am_j[row0:row0 + n])
+        np.testing.assert_array_equal(gap_a, gap_j[row0:row0 + n])
+        if r == 1:
+            gl = joint[row0:row0 + n].cpu().numpy().astype(np.float64)
+            orc = oracle.Oracle(synth.C1, wl.host_weights)
+            rows = orc.tree_scores(orc.new_seq(cap=ctxs[1] + 40, kv=kv1, ctx_len=ctxs[1], history=hist1),
+                                   parents, tokens, rows_wanted=[0, 3, n - 1])
+            ex = oracle.Oracle(synth.C1, wl.host_weights, exact=True)
+            rows_ex = ex.tree_scores(ex.new_seq(cap=ctxs[1] + 40, kv=kv1, ctx_len=ctxs[1], history=hist1),
+                                     parents, tokens, rows_wanted=[0, 3, n - 1])
+            need = sorted(i for i in range(n) if not np.isnan(rows[i, 0]))
+            idx = {i: j for j, i in enumerate(need)}
+            sub_parents = [-1 if parents[i] < 0 else idx[int(parents[i])] for i in need]
+            check_rows(gl[need], am_a[need], gap_a[need], rows[need], sub_parents,
+                       [int(tokens[i]) for i in need], hist1, what="four requests, ctx 100", orc_exact=rows_ex[need])
+        row0 += n
+    assert row0 == 32
+
 # ------------------------------------------------------------- edge cases
 
 def test_c0_edges_capacity_single_row_three_requests(c0):
