@@ -120,6 +120,7 @@ struct AttnArgs {
 // head, 256 for 8 KV heads, one per CU (a workgroup fills its CU's register
 // file), so no workgroup waits for a second round.
 constexpr int kVerifyCacheSplits = 31;
+constexpr int kAttnMaxSplits = 33;   // partial splits of a query row: 32 cache splits at most (a prefill block's) + the tree's
 __host__ __device__ inline int attn_span_n(int ctx, int splits) {
     const int chunks = (ctx + kAttnChunk - 1) / kAttnChunk;
     const int per = (chunks + splits - 1) / splits;

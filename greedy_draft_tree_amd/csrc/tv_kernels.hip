@@ -166,20 +166,30 @@ __device__ __forceinline__ void score_quad(const PassMeta *meta, int m, int n0, 
 // partials of an element in k-range order, so every element's sum order is
 // fixed by the weight shape.
 
-__device__ __forceinline__ float psum(const float *__restrict__ P, int S, int nacc, int j, int m, int n) {
-    const float *p = P + ((size_t)(n >> 7) * S * nacc + j) * 4096 + (size_t)m * 128 + (n & 127);
-    const size_t st = (size_t)nacc * 4096;
-    float s = 0.f;
-    int k = 0;
-    for (; k + 4 <= S; k += 4) {   // four loads in flight, adds kept in k order
-        const float a0 = p[k * st], a1 = p[(k + 1) * st], a2 = p[(k + 2) * st], a3 = p[(k + 3) * st];
-        s += a0;
-        s += a1;
-        s += a2;
-        s += a3;
+
+// Split-K sums of U elements (element u's partials start at p[u], one split
+// every st floats), with the loads of 16 splits of every element issued
+// before any add: one round trip to memory for up to 16 splits.  Each
+// element's adds stay in k-range order.
+template <int U>
+__device__ __forceinline__ void psum_multi(const float *const (&p)[U], size_t st, int S, float (&out)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) out[u] = 0.f;
+    for (int k0 = 0; k0 < S; k0 += 16) {
+        float l[U][16];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) l[u][j] = k0 + j < S ? p[u][(size_t)(k0 + j) * st] : 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (k0 + j < S) out[u] += l[u][j];
     }
-    for (; k < S; ++k) s += p[k * st];
-    return s;
+}
+__device__ __forceinline__ const float *pptr(const float *P, int S, int nacc, int j, int m, int n) {
+    return P + ((size_t)(n >> 7) * S * nacc + j) * 4096 + (size_t)m * 128 + (n & 127);
 }
 
 // --------------------------------------------- residual stream + RMSNorm
@@ -653,14 +663,22 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g, int S) {
     const int nl = (int)(idx & 127), m = (int)((idx >> 7) & 31);
     const int n = (int)((idx >> 12) * 128) + nl;
     if (m >= g.M || n >= g.N) return;
-    const float acc = psum(g.partial, S, NACC, 0, m, n);
+    float sums[NACC];
+    if constexpr (NACC == 2) {
+        const float *const pp[2] = {pptr(g.partial, S, 2, 0, m, n), pptr(g.partial, S, 2, 1, m, n)};
+        psum_multi<2>(pp, 2 * 4096, S, sums);
+    } else {
+        const float *const pp[1] = {pptr(g.partial, S, 1, 0, m, n)};
+        psum_multi<1>(pp, 4096, S, sums);
+    }
+    const float acc = sums[0];
     uint16_t *y = g.Y + (size_t)m * g.ldy + n;
     if constexpr (EPI == EPI_BF16) {
         *y = f2bf(acc);
     } else if constexpr (EPI == EPI_RESID) {
         *y = f2bf(bf2f(*y) + bfround(acc));
     } else if constexpr (EPI == EPI_SWIGLU) {
-        const float gt = bfround(acc), up = bfround(psum(g.partial, S, NACC, 1, m, n));
+        const float gt = bfround(acc), up = bfround(sums[NACC - 1]);
         *y = f2bf(gt / (1.0f + expf(-gt)) * up);
     }
 }
@@ -1021,21 +1039,26 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
     if (u >= nq + nk + nv) return;
     const int pos = rq.ctx + a.meta->depth[m];
     // projection outputs: bf16 of the partial sums (the QKV projection's rounding point)
-    auto qkv = [&](int n) { return bfround(psum(a.part, a.S, 1, 0, m, n)); };
     const size_t slot = (size_t)(rq.ctx + i);
     if (u < nq + nk) {
         const bool isq = u < nq;
         const int uu = isq ? u : u - nq;
         const int h = uu / half, p = uu % half;
         const int col = (isq ? 0 : a.QH * D) + h * D + p;
-        const float x0 = qkv(col), x1 = qkv(col + half);
+        const float *const pp[2] = {pptr(a.part, a.S, 1, 0, m, col), pptr(a.part, a.S, 1, 0, m, col + half)};
+        float xs[2];
+        psum_multi<2>(pp, 4096, a.S, xs);
+        const float x0 = bfround(xs[0]), x1 = bfround(xs[1]);
         const float c = a.cosT[(size_t)pos * half + p], s = a.sinT[(size_t)pos * half + p];
         uint16_t *o = isq ? a.q_out + (size_t)m * a.QH * D + h * D : rq.Kc + ((size_t)h * a.cap + slot) * D;
         o[p] = f2bf(x0 * c - x1 * s);
         o[p + half] = f2bf(x1 * c + x0 * s);
     } else {
         const int uu = u - nq - nk, h = uu / D, d = uu % D;
-        rq.Vc[((size_t)h * a.cap + slot) * D + d] = f2bf(qkv((a.QH + a.KVH) * D + h * D + d));
+        const float *const pp[1] = {pptr(a.part, a.S, 1, 0, m, (a.QH + a.KVH) * D + h * D + d)};
+        float xs[1];
+        psum_multi<1>(pp, 4096, a.S, xs);
+        rq.Vc[((size_t)h * a.cap + slot) * D + d] = f2bf(bfround(xs[0]));
     }
 }
 
@@ -1381,6 +1404,11 @@ __global__ __launch_bounds__(D) void k_attn_combine(AttnArgs a, uint16_t *__rest
     }
     const size_t b0 = a.nreq > 0 ? ((size_t)kvh * a.ns) * RP + row0 * G + row
                                  : (((size_t)z * (a.n_qhead / G) + kvh) * a.ns) * RP + row;
+    // every split's output of this dim and (thread d) split d's maximum and
+    // sum: all loads in flight at once
+    float pv[kAttnMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kAttnMaxSplits; ++s) pv[s] = s < ns ? a.po[(b0 + (size_t)s * RP) * D + d] : 0.f;
     if (d < ns) {
         ms[d] = a.pm[b0 + (size_t)d * RP];
         wl[d] = a.pl[b0 + (size_t)d * RP];
@@ -1392,16 +1420,11 @@ __global__ __launch_bounds__(D) void k_attn_combine(AttnArgs a, uint16_t *__rest
     if (d < ns) ws[d] = (ms[d] == -INFINITY) ? 0.f : exp2f(ms[d] - M);
     __syncthreads();
     float L = 0.f, O = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += 8) {   // eight splits' loads in flight, adds in split order
-        float pv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pv[i] = s0 + i < ns ? a.po[(b0 + (size_t)(s0 + i) * RP) * D + d] : 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (s0 + i < ns) {
-                L += ws[s0 + i] * wl[s0 + i];
-                O += ws[s0 + i] * pv[i];
-            }
+    for (int s = 0; s < kAttnMaxSplits; ++s) {   // adds in split order
+        if (s < ns) {
+            L += ws[s] * wl[s];
+            O += ws[s] * pv[s];
         }
     }
     out[(size_t)(row0 + t) * a.n_qhead * D + h * D + d] = f2bf(O / L);
@@ -1924,6 +1947,7 @@ hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a) {
 }
 
 hipError_t launch_attn_combine(hipStream_t s, int D, const AttnArgs &a, uint16_t *out) {
+    if (a.ns > kAttnMaxSplits || D < kAttnMaxSplits) return hipErrorInvalidValue;
     const dim3 grid(a.n, a.n_qhead, a.nreq > 0 ? a.nreq : a.zrows > 0 ? (a.M + a.zrows - 1) / a.zrows : 1);
     if (D == 128) hipLaunchKernelGGL(k_attn_combine<128>, grid, dim3(128), 0, s, a, out);
     else if (D == 64) hipLaunchKernelGGL(k_attn_combine<64>, grid, dim3(64), 0, s, a, out);
