@@ -220,10 +220,11 @@ __global__ __launch_bounds__(kRowThreads) void k_row_norm(const uint16_t *__rest
     const int m = blockIdx.x, t = threadIdx.x;
     if constexpr (MODE == ROW_EMBED) {
         if (m == 0 && meta_out) {
-            static_assert(sizeof(PassMeta) % 4 == 0, "the metadata record is copied in words");
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(meta);
-            uint32_t *dst = reinterpret_cast<uint32_t *>(meta_out);
-            for (int i = t; i < (int)(sizeof(PassMeta) / 4); i += blockDim.x) dst[i] = src[i];
+            // 16-byte pieces: one load per thread, one trip over the bus
+            static_assert(sizeof(PassMeta) % 16 == 0, "the metadata record is copied in 16-byte pieces");
+            const uint4 *src = reinterpret_cast<const uint4 *>(meta);
+            uint4 *dst = reinterpret_cast<uint4 *>(meta_out);
+            for (int i = t; i < (int)(sizeof(PassMeta) / 16); i += blockDim.x) dst[i] = src[i];
         }
     }
     const int n0 = 8 * t;
