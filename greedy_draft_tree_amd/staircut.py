@@ -5,12 +5,16 @@
 * ``PriceModel``: verify prices by context class, kind (chain or tree) and row
   count, in the pages' price-file format
   ``{"<context class>": {"<kind>": {"<rows>": ms, ...}, ...}, ..., "step_ms": x, "measured": "..."}``,
-  with the pages' lookup rules: a class not in the file takes the nearest
-  lower one, rows between two measured counts interpolate, rows past the
-  last add ``step_ms`` a row (else the last two counts' slope), live prices
-  are followed by an exponential moving average (0.1 a count, unmeasured
-  counts shifted by the learned offset), and a price never falls with more
-  rows.  Without a file every count starts at 1 ms.
+  and the rules the pages give for reading it ("Drafters and tree verify",
+  StairCut on Flash-Next, and the shared price files): an unlisted context
+  class falls back to the largest listed one below it; a row count between
+  two measured ones is a linear blend of them; beyond the last measured
+  count the price grows by ``step_ms`` per row, or by the slope of the last
+  two counts when the file has no ``step_ms``; measured round times update
+  the prices online with an exponential moving average of weight 0.1 per
+  count, shifting the unmeasured counts by the mean learned offset; prices
+  are made non-decreasing in the row count.  With no file, every count
+  costs 1 ms.
 * ``measure_prices``: a price file for a bound model on this GPU.
 """
 from __future__ import annotations

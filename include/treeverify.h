@@ -173,10 +173,10 @@ int tv_prefill(tv_ctx *ctx, int req, const int32_t *tokens, int n, int32_t *argm
  * the MFMA-bound prefill kernels (one GEMM over all of a chunk's rows per
  * projection, attention in blocks of 32 rows).  The chunk grid is fixed by
  * absolute position: chunks end at multiples of `chunk` ("Exactness",
- * Caches: snapshots lie on the prefill chunk grid and a resumed request
- * forwards the rest of its prompt on the same grid), so a request resumed at
- * a grid point from the cache rows a cold prefill left there computes the
- * same arithmetic, bit for bit.  `chunk` is a multiple of 32 in [32, 2048].
+ * Caches: snapshots are taken at chunk-grid boundaries and a restored
+ * request continues on those boundaries), so a request resumed at a grid
+ * point from the cache rows a cold prefill left there computes the same
+ * arithmetic, bit for bit.  `chunk` is a multiple of 32 in [32, 2048].
  * Recurrent layers take the chunk's rows as chains of 32 in order (the tree
  * read-out on each, then the closed-form state commit of the chain).  Rows
  * are committed as they go: ctx_len grows by n and the tokens join the

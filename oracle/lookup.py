@@ -1,13 +1,14 @@
 """The lookup drafter over the request's own text, written plainly
 (TEST INFRASTRUCTURE: only tests may import it).
 
-"Drafters and tree verify", The lookup drafter: the drafter copies text
-instead of predicting it.  It finds the longest match of the last few tokens
-in the request itself (prompt and output so far, orders 2 to 8); every
-continuation found is a vote, and the votes form a tree whose node scores are
-path probabilities.  The tree then goes to StairCut, which admits nodes in
-the drafter's score order ("Drafters and tree verify", StairCut: a lookup
-node's q is its vote share).
+"Drafters and tree verify", The lookup drafter: this drafter proposes
+tokens by reuse, not by a model.  The request's most recent tokens (a suffix
+of 2 to 8 ids) are searched for earlier in its own prompt and output; each
+earlier place where the longest such suffix occurs contributes the tokens
+that followed it, and merging those continuations gives a tree in which a
+node's score is the fraction of continuations that pass through it.
+StairCut then takes the tree, using that fraction as the node's q
+("Drafters and tree verify", StairCut).
 
 Readings taken here (the pages leave them open):
 * an occurrence of order o is a start p with text[p:p+o] equal to the last o

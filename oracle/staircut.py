@@ -1,15 +1,14 @@
 """StairCut, written plainly (TEST INFRASTRUCTURE: only tests may import it).
 
-"Drafters and tree verify", StairCut: each round a candidate tree is cut to
-the node count that maximises expected committed tokens per millisecond,
+"Drafters and tree verify", StairCut: before each verify, the candidate
+tree is trimmed to the size with the best ratio of expected tokens to cost,
 
-    (1 + sum of q over the kept nodes) / (verify(rows) + draft + commit),
+    (1 + min(sum of q over the kept nodes, their number)) / (verify(rows) + draft + commit),
 
-where a node's q is its path probability (capped at 1 by the caller), the
-gain counts at most one token per kept node (min(sum q, n)), nodes are
-admitted in the order of the drafter's own score, each with the ancestors it
-needs, and a cut ends at 7, 15, 23 or 31 nodes (8, 16, 24 or 32 rows) or at
-the whole candidate.
+q being a node's path probability (the caller caps it at 1).  Candidates
+enter in descending drafter score, and a node that enters brings along any
+of its ancestors not yet kept; the sizes considered stop at 7, 15, 23 or 31
+nodes (8, 16, 24 or 32 rows) and at the full candidate.
 
 Readings taken here (the pages leave them open):
 * a cut "ends at" P nodes means: the longest admission prefix whose kept set

@@ -1,8 +1,9 @@
 """Dense (MFMA) prefill on the chunk grid (MI355X only).
 
-"Exactness", Caches: snapshots are taken on the prefill chunk grid and a
-resumed request forwards the rest of its prompt on the same grid, so it
-computes the same arithmetic as a cold prefill: bit for bit.
+"Exactness", Caches: cache snapshots sit on chunk-grid boundaries, and a
+request restored from one continues its prompt on those same boundaries, so
+its arithmetic, and hence every bit of its output, matches a prefill that
+started from nothing.
 
 * The last row's token and the cache rows a dense prefill leaves agree with
   the oracle's sequential decode of the prompt (tokens up to near ties; the
