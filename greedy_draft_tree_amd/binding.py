@@ -102,6 +102,38 @@ def _ptr(a: np.ndarray) -> int:
     return a.__array_interface__["data"][0]
 
 
+def _dtype_name(t) -> str:
+    return str(getattr(t, "dtype", None)).replace("torch.", "")
+
+
+def check_device_tensor(t, what: str, dtype: Optional[str] = None, min_numel: int = 0,
+                        shape: Optional[Tuple[int, ...]] = None) -> None:
+    """Raise ValueError unless ``t`` is a contiguous device tensor of ``dtype``
+    ("float32", "bfloat16") with at least ``min_numel`` elements (or exactly
+    ``shape``).  The library writes through the raw pointer, so a tensor of
+    the wrong element size, on the host or too small would be written past
+    its end on the device; every entry point checks before the call."""
+    if dtype is not None and _dtype_name(t) != dtype:
+        raise ValueError(f"{what}: dtype {_dtype_name(t)}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: tensor must be contiguous")
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{what}: tensor must be on the GPU")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{what}: {t.numel()} elements, at least {min_numel} needed")
+
+
+def _logits_ptr(logits, rows: int, vocab: int, what: str):
+    """Device address of an fp32 logits buffer with room for [rows, vocab]
+    (None passes NULL: the library's own scratch)."""
+    if logits is None:
+        return None
+    check_device_tensor(logits, f"{what}: logits", "float32", rows * vocab)
+    return logits.data_ptr()
+
+
 # output buffers of accept_walk, reused across calls (results are copied out)
 _walk_path = np.zeros(TV_MAX_NODES, np.int32)
 _walk_emit = np.zeros(TV_MAX_NODES, np.int32)
@@ -136,6 +168,7 @@ class TreeVerifier:
         d = _Desc(n_layer, hidden, n_qhead, n_kvhead, head_dim, ffn, vocab, self._kinds,
                   eps, rope_theta, max_ctx, max_req)
         self.vocab, self.max_ctx, self.max_req = vocab, max_ctx, max_req
+        self.hidden = hidden
         # per-call result buffers of tv_verify_tree (copied out on return)
         self._am = np.zeros(TV_MAX_NODES, np.int32)
         self._gap = np.zeros(TV_MAX_NODES, np.float32)
@@ -177,8 +210,7 @@ class TreeVerifier:
 
     def bind(self, name: str, tensor) -> None:
         """tv_bind with a contiguous device tensor."""
-        if not tensor.is_contiguous():
-            raise ValueError(f"{name}: tensor must be contiguous")
+        check_device_tensor(tensor, name)
         nbytes = tensor.numel() * tensor.element_size()
         self._check(self.lib.tv_bind(self.h, name.encode(), ctypes.c_void_p(tensor.data_ptr()),
                                      nbytes), f"tv_bind({name})")
@@ -225,11 +257,7 @@ class TreeVerifier:
         ``logits``: optional device fp32 tensor with room for [n, vocab]."""
         p, t = _i32(parents), _i32(tokens)
         n = int(p.size)
-        lp = None
-        if logits is not None:
-            if logits.numel() < n * self.vocab or not logits.is_contiguous():
-                raise ValueError("logits tensor too small or not contiguous")
-            lp = logits.data_ptr()
+        lp = _logits_ptr(logits, n, self.vocab, "verify_tree")
         rc = self.lib.tv_verify_tree(self.h, req, _ptr(p), _ptr(t), n, lp, self._am_ptr, self._gap_ptr)
         if rc != TV_OK:
             self._check(rc, "tv_verify_tree")
@@ -247,11 +275,7 @@ class TreeVerifier:
         tp = (ctypes.c_void_p * k)(*[t.ctypes.data for t in ts])
         am = np.zeros(max(total, 1), np.int32)
         gap = np.zeros(max(total, 1), np.float32)
-        lp = None
-        if logits is not None:
-            if logits.numel() < total * self.vocab or not logits.is_contiguous():
-                raise ValueError("logits tensor too small or not contiguous")
-            lp = ctypes.c_void_p(logits.data_ptr())
+        lp = _logits_ptr(logits, total, self.vocab, "verify_trees")
         self._check(self.lib.tv_verify_trees(self.h, k, _ptr(rq), ctypes.cast(pp, ctypes.c_void_p),
                                              ctypes.cast(tp, ctypes.c_void_p), _ptr(ns), lp,
                                              _ptr(am), _ptr(gap)), "tv_verify_trees")
@@ -268,11 +292,7 @@ class TreeVerifier:
         (argmax, gap, path, emitted)."""
         p, t = _i32(parents), _i32(tokens)
         n = int(p.size)
-        lp = None
-        if logits is not None:
-            if logits.numel() < n * self.vocab or not logits.is_contiguous():
-                raise ValueError("logits tensor too small or not contiguous")
-            lp = logits.data_ptr()
+        lp = _logits_ptr(logits, n, self.vocab, "round")
         rc = self.lib.tv_round(self.h, req, _ptr(p), _ptr(t), n, lp, self._am_ptr, self._gap_ptr,
                                self._path_ptr, self._lens_ptr, self._emit_ptr, self._lens_ptr + 4)
         if rc != TV_OK:
@@ -288,7 +308,7 @@ class TreeVerifier:
         u = np.ascontiguousarray(np.asarray(uniforms, dtype=np.float64))
         if u.shape[0] < n:
             raise TVError(-1, "tv_residual_round: one uniform per depth (at least n_nodes)")
-        lp = ctypes.c_void_p(logits.data_ptr()) if logits is not None else None
+        lp = _logits_ptr(logits, n, self.vocab, "residual_round")
         rc = self.lib.tv_residual_round(self.h, req, _ptr(p), _ptr(t), n, lp, float(temperature), _ptr(u),
                                         _ptr(self._path), ctypes.addressof(self._lens), _ptr(self._emit),
                                         ctypes.addressof(self._lens) + 4)
@@ -304,28 +324,36 @@ class TreeVerifier:
     def linear(self, x, w, y) -> None:
         """tv_linear: y = x w^T (bf16 out if y is bf16, fp32 sums if y is fp32);
         w must have been packed with pack_weight."""
+        if x.dim() != 2 or w.dim() != 2:
+            raise ValueError("linear: x and w must be matrices")
         M, K = x.shape
         N = w.shape[0]
-        assert w.shape[1] == K and tuple(y.shape) == (M, N)
-        for t in (x, w, y):
-            if not t.is_contiguous():
-                raise ValueError("operands must be contiguous")
-        fp32 = 1 if y.element_size() == 4 else 0
+        check_device_tensor(x, "linear: x", "bfloat16")
+        check_device_tensor(w, "linear: w", "bfloat16", shape=(N, K))
+        if _dtype_name(y) not in ("bfloat16", "float32"):
+            raise ValueError(f"linear: y dtype {_dtype_name(y)}, expected bfloat16 or float32")
+        check_device_tensor(y, "linear: y", shape=(M, N))
+        fp32 = 1 if _dtype_name(y) == "float32" else 0
         self._check(self.lib.tv_linear(self.h, ctypes.c_void_p(x.data_ptr()),
                                        ctypes.c_void_p(w.data_ptr()), M, N, K,
                                        ctypes.c_void_p(y.data_ptr()), fp32), "tv_linear")
 
     def pack_weight(self, w) -> None:
         """tv_pack_weight: rearrange a row-major [N, K] bf16 tensor in place."""
+        if w.dim() != 2:
+            raise ValueError("pack_weight: w must be a matrix")
+        check_device_tensor(w, "pack_weight: w", "bfloat16")
         N, K = w.shape
         self._check(self.lib.tv_pack_weight(self.h, ctypes.c_void_p(w.data_ptr()), N, K),
                     "tv_pack_weight")
 
     def head_top2(self, x, logits):
         """tv_head_top2 on x [M, hidden] bf16 -> (argmax, gap)."""
+        if x.dim() != 2 or not (1 <= x.shape[0] <= TV_MAX_NODES):
+            raise ValueError("head_top2: x must be [M, hidden] with 1 <= M <= 32")
         M = x.shape[0]
-        if logits.numel() < M * self.vocab:
-            raise ValueError("logits tensor too small")
+        check_device_tensor(x, "head_top2: x", "bfloat16", shape=(M, self.hidden))
+        check_device_tensor(logits, "head_top2: logits", "float32", M * self.vocab)
         am = np.zeros(M, np.int32)
         gap = np.zeros(M, np.float32)
         self._check(self.lib.tv_head_top2(self.h, ctypes.c_void_p(x.data_ptr()), M,

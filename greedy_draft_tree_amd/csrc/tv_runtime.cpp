@@ -226,6 +226,19 @@ void read_results(tv_ctx *c, int M, int32_t *argmax, float *gap) {
     }
 }
 
+// A call that fails after it has enqueued work returns only once that work
+// has drained: otherwise a kernel of the failed call could still be reading
+// the pinned pass metadata (or scratch) that the next call rewrites.
+struct DrainOnError {
+    tv_ctx *c;
+    bool armed = true;
+    explicit DrainOnError(tv_ctx *ctx) : c(ctx) {}
+    ~DrainOnError() {
+        if (armed) hipStreamSynchronize(c->stream);
+    }
+    void done() { armed = false; }
+};
+
 #define LAUNCH(c, nm, call)                                                                  \
     do {                                                                                     \
         Launch L_(c, nm);                                                                    \
@@ -448,6 +461,7 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
     // X: residual stream; XN = RMSNorm(X) with the weights of the next
     // projection that reads it (xn_w), written by the kernel that updates X.
     const uint16_t *xn_w = c->attn_norm[0];
+    DrainOnError drain(c);
     LAUNCH(c, "embed_norm", launch_embed_norm(s, c->emb, c->hd_meta, c->d_meta, M, H, xn_w, m.eps, c->X, c->XN));
     auto normed = [&](GemmArgs &g, const uint16_t *w) -> int {
         if (xn_w != w) return fail(c, TV_ESTATE, "internal: normalised rows hold another norm");
@@ -559,6 +573,7 @@ int run_pass(tv_ctx *c, int n_req, const int *reqs, const int32_t *const *parent
         const int rc = wait_results(c, M);
         if (rc) return rc;
     }
+    drain.done();
     read_results(c, M, argmax, gap);
 
     for (int r = 0; r < n_req; ++r) {
@@ -963,10 +978,12 @@ int tv_residual_round(tv_ctx *c, int req, const int32_t *parents, const int32_t 
     clear_results(c, n_nodes);
     HIPCHECK(c, hipMemcpyAsync(c->d_resu, c->h_resu, (size_t)n_nodes * sizeof(double), hipMemcpyHostToDevice, s));
     const float *lg = logits_dev ? logits_dev : c->logits;
+    DrainOnError drain(c);
     LAUNCH(c, "residual", launch_residual(s, lg, c->m.vocab, c->m.vocab, c->d_meta, n_nodes, temperature, c->d_resu,
                                           c->d_resparts, c->hd_res));
     rc = wait_results(c, n_nodes);
     if (rc) return rc;
+    drain.done();
     // the walk: from the root, accept a child or emit and stop
     int cur = 0, pl = 1, ne = 0;
     path[0] = 0;
@@ -1150,6 +1167,7 @@ int tv_prefill_dense(tv_ctx *c, int req, const int32_t *tokens, int n, int chunk
     rc = ensure_prefill(c, chunk);
     if (rc) return rc;
     q.pending = false;
+    DrainOnError drain(c);
     int done = 0;
     while (done < n) {
         // the chunk grid: chunks end at multiples of `chunk` positions
@@ -1197,6 +1215,7 @@ int tv_prefill_dense(tv_ctx *c, int req, const int32_t *tokens, int n, int chunk
         }
     }
     if (!argmax_last) HIPCHECK(c, hipStreamSynchronize(c->stream));
+    drain.done();
     return TV_OK;
 }
 
@@ -1232,6 +1251,7 @@ int tv_linear(tv_ctx *c, const void *x, const void *w, int M, int N, int K, void
     g.X = (const uint16_t *)x; g.ldx = K; g.W = (const uint16_t *)w; g.M = M; g.N = N; g.K = K;
     g.zeros = c->zeros;
     hipStream_t s = c->stream;
+    DrainOnError drain(c);
     if (M > kMaxRows) {   // many rows: the dense (prefill) GEMM
         if (y_fp32) { g.Yf = (float *)y; g.ldyf = N; }
         else { g.Y = (uint16_t *)y; g.ldy = N; }
@@ -1244,6 +1264,7 @@ int tv_linear(tv_ctx *c, const void *x, const void *w, int M, int N, int K, void
         GEMM(c, "gemm_linear", EPI_BF16, g);
     }
     HIPCHECK(c, hipStreamSynchronize(s));
+    drain.done();
     if (c->prof) harvest(c);
     return TV_OK;
 }
@@ -1265,12 +1286,14 @@ int tv_head_top2(tv_ctx *c, const void *x, int M, float *logits_dev, int32_t *ar
     g.X = (const uint16_t *)x; g.ldx = m.hidden; g.W = c->head; g.M = M; g.N = m.vocab; g.K = m.hidden;
     g.Yf = logits_dev; g.ldyf = m.vocab; g.part = c->part;
     clear_results(c, M);
+    DrainOnError drain(c);
     GEMM(c, "gemm_head", EPI_HEAD, g);
     LAUNCH(c, "top2", launch_top2_reduce(s, c->part, ((m.vocab + 31) / 32 + 3) / 4, M, c->hd_res));
     {
         const int rc2 = wait_results(c, M);
         if (rc2) return rc2;
     }
+    drain.done();
     read_results(c, M, argmax, gap);
     return TV_OK;
 }

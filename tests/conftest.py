@@ -11,3 +11,8 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (runs through the HIP library)")
     config.addinivalue_line("markers", "slow: large CPU oracle case")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    import parity_log
+    parity_log.write()

@@ -37,7 +37,17 @@ def check_rows(gpu_logits, gpu_argmax, gpu_gap, orc_logits, parents, tokens, his
     activation rounding itself puts on that row (max |rounded - exact|): a
     tiny fp32 difference that lands on a bf16 rounding boundary is carried
     forward ("Exactness", The one exception: near ties), so two correct
-    bf16 computations differ by about the rounding's own effect."""
+    bf16 computations differ by about the rounding's own effect.
+
+    Token differences ("Exactness", The one exception: near ties): a row
+    whose GPU argmax differs from the oracle's passes when the oracle's
+    top-1/top-2 gap is at most one bf16 ulp.  A larger gap passes only with
+    the evidence that the two rounded computations merely broke a tie of the
+    exact one: the GPU's token is the oracle's runner-up, and in the
+    oracle's unrounded run those two tokens are within one bf16 ulp of each
+    other or already in the GPU's order.  Every such case is counted and
+    logged (tests/parity_log.py)."""
+    import parity_log
     n = len(parents)
     diff = np.abs(gpu_logits[:n].astype(np.float64) - orc_logits[:n])
     tol = np.full(n, LOGIT_ATOL)
@@ -55,22 +65,31 @@ def check_rows(gpu_logits, gpu_argmax, gpu_gap, orc_logits, parents, tokens, his
     am, gap = oracle.tree_decisions(orc_logits, parents, tokens, history, mods)
     ties, drift = 0, 0
     for i in range(n):
-        if gpu_argmax[i] != am[i]:
-            if gap[i] <= 1.0:
-                ties += 1
-                continue
-            # Beyond one ulp a flip is accepted only where the row's measured
-            # bf16 drift (the oracle's own rounded-vs-exact spread, not the
-            # GPU) can explain it: two results within tol of each other can
-            # order two scores differently only when they are within 2*tol.
-            scores = oracle.apply_modifiers(orc_logits[i], list(history) +
-                                            oracle.path_tokens(parents, tokens, i), mods)
-            a, l1, l2, _ = oracle.top2(scores)
-            assert orc_exact is not None and l1 - l2 <= 2 * tol[i], \
-                f"{what}: row {i} argmax {gpu_argmax[i]} vs {am[i]} at gap {gap[i]:.3f} ulp"
-            drift += 1
-    if drift:
-        print(f"[{what}] argmax flips beyond 1 ulp within the row's bf16 drift: {drift}", flush=True)
+        if gpu_argmax[i] == am[i]:
+            continue
+        if gap[i] <= 1.0:
+            ties += 1
+            continue
+        prior = list(history) + oracle.path_tokens(parents, tokens, i)
+        scores = oracle.apply_modifiers(orc_logits[i], prior, mods)
+        a, l1, l2, _ = oracle.top2(scores)
+        b = int(gpu_argmax[i])
+        runner_up = int(np.argmax(np.where(np.arange(scores.shape[0]) == a, -np.inf, scores)))
+        assert b == runner_up, \
+            f"{what}: row {i} argmax {b} is not the oracle's runner-up {runner_up} (gap {gap[i]:.3f} ulp)"
+        assert orc_exact is not None, \
+            f"{what}: row {i} argmax {b} vs {a} at gap {gap[i]:.3f} ulp with no unrounded run"
+        ex = oracle.apply_modifiers(orc_exact[i], prior, mods).astype(np.float64)
+        in_gpu_order = ex[b] > ex[a] or (ex[b] == ex[a] and b < a)
+        within_ulp = abs(ex[a] - ex[b]) <= float(oracle.ulp_bf16(max(ex[a], ex[b])))
+        assert in_gpu_order or within_ulp, \
+            f"{what}: row {i} argmax {b} vs {a} at gap {gap[i]:.3f} ulp; unrounded scores " \
+            f"{ex[b]:.6g} vs {ex[a]:.6g} do not support the GPU's order"
+        drift += 1
+    parity_log.record(what, n, ties, drift, float(diff.max()), float(tol.min()), float(tol.max()))
+    if ties or drift:
+        print(f"[{what}] near ties (<= 1 ulp): {ties}; wider flips backed by the unrounded run: {drift}",
+              flush=True)
     return am, gap, ties + drift
 
 
