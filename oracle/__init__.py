@@ -226,6 +226,36 @@ class Oracle:
         o = np.einsum("hkv,hk->hv", S, q)
         return o, S
 
+    def recurrent_token(self, kind: int, qkv: np.ndarray, a: np.ndarray, S_prev: np.ndarray):
+        """The token mixing of a recurrent layer from its projections (both
+        already at their rounding point): ``qkv`` stacks q, k and v heads
+        (QH*D values each), ``a`` the gate pre-activations and, for a delta
+        layer, the write-strength pre-activations after them.  q and k are
+        L2-normalised per head; the log-decay is log sigmoid(gate) and the
+        write strength sigmoid(.).  Returns (read-out [QH*D] at its rounding
+        point, the new state held in fp32)."""
+        s, r = self.s, self.r
+        QH, D = s.n_qhead, s.head_dim
+        q = r(self.l2norm(qkv[:QH * D].reshape(QH, D)))
+        k = r(self.l2norm(qkv[QH * D:2 * QH * D].reshape(QH, D)))
+        v = qkv[2 * QH * D:3 * QH * D].reshape(QH, D)
+        if kind == RECUR:
+            o, S = self.recur_mix(q, k, v, log_sigmoid(a[:QH]), S_prev)
+        else:
+            o, S = self.delta_mix(q, k, v, log_sigmoid(a[:QH]), sigmoid(a[QH:2 * QH]), S_prev)
+        # the state is held in fp32 between tokens
+        return r(o.reshape(-1)), (S if self.exact else f32(S))
+
+    def recurrent_layer(self, l: int, xn: np.ndarray, S_prev: np.ndarray):
+        """Recurrent layer l on its normalised input row ``xn``: the stacked
+        q/k/v projection (wqkv) and the gate projection (wa: gate rows, then a
+        delta layer's write-strength rows), each rounded, then
+        ``recurrent_token``."""
+        p = f"layers.{l}."
+        qkv = self.r(self.matvec(p + "wqkv", xn))
+        a = self.r(self.matvec(p + "wa", xn))
+        return self.recurrent_token(self.s.kinds[l], qkv, a, S_prev)
+
     def l2norm(self, x: np.ndarray) -> np.ndarray:
         return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + self.s.eps)
 
@@ -259,19 +289,7 @@ class Oracle:
                 o = r(self.attention(q, Ka, Va).reshape(-1))
                 rows[l] = (k, v)
             else:
-                qkv = r(self.matvec(p + "wqkv", xn))
-                q = r(self.l2norm(qkv[:QH * D].reshape(QH, D)))
-                k = r(self.l2norm(qkv[QH * D:2 * QH * D].reshape(QH, D)))
-                v = qkv[2 * QH * D:].reshape(QH, D)
-                a = r(self.matvec(p + "wa", xn))
-                if kind == RECUR:
-                    o, S = self.recur_mix(q, k, v, log_sigmoid(a), states[l])
-                else:
-                    # gate rows, then write-strength rows
-                    o, S = self.delta_mix(q, k, v, log_sigmoid(a[:QH]), sigmoid(a[QH:]), states[l])
-                o = r(o.reshape(-1))
-                # the state is held in fp32 between tokens
-                new_states[l] = S if self.exact else f32(S)
+                o, new_states[l] = self.recurrent_layer(l, xn, states[l])
             x = r(x + r(self.matvec(p + "wo", o)))
             hn = r(self.rmsnorm(x, p + "ffn_norm"))
             gt = r(self.matvec(p + "wg", hn))
