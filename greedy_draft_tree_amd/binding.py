@@ -22,7 +22,8 @@ SYMBOLS = ("tv_create", "tv_destroy", "tv_last_error", "tv_bind", "tv_set_histor
            "tv_set_modifiers", "tv_set_sampling", "tv_prefill", "tv_prefill_dense", "tv_verify_tree", "tv_verify_trees",
            "tv_accept_walk", "tv_commit", "tv_round", "tv_ctx_len", "tv_profile_enable",
            "tv_profile_reset", "tv_profile_get", "tv_linear", "tv_head_top2", "tv_pack_weight",
-           "tv_staircut", "tv_residual_round", "tv_lookup_draft")
+           "tv_staircut", "tv_residual_round", "tv_lookup_draft", "tv_attention", "tv_rope_kv",
+           "tv_resid_norm", "tv_recur_tree", "tv_recur_commit", "tv_gather_kv")
 
 
 class TVError(RuntimeError):
@@ -77,6 +78,12 @@ def load_library():
         "tv_staircut": ([P, P, P, I, P, P, F, F, P, P, P], I),
         "tv_residual_round": ([P, I, P, P, I, P, F, P, P, P, P, P], I),
         "tv_lookup_draft": ([P, I, I, I, I, I, F, P, P, P, P, P, P, P], I),
+        "tv_attention": ([P, P, P, P, I, I, P, I, P], I),
+        "tv_rope_kv": ([P, P, I, I, P, I, P, P, P, I], I),
+        "tv_resid_norm": ([P, P, I, I, P, P, P], I),
+        "tv_recur_tree": ([P, I, P, I, P, I, P, P, P, P, P], I),
+        "tv_recur_commit": ([P, P, P, P, P, P, I], I),
+        "tv_gather_kv": ([P, P, P, I, I, P, I], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -169,6 +176,7 @@ class TreeVerifier:
                   eps, rope_theta, max_ctx, max_req)
         self.vocab, self.max_ctx, self.max_req = vocab, max_ctx, max_req
         self.hidden = hidden
+        self.n_qhead, self.n_kvhead, self.head_dim = n_qhead, n_kvhead, head_dim
         # per-call result buffers of tv_verify_tree (copied out on return)
         self._am = np.zeros(TV_MAX_NODES, np.int32)
         self._gap = np.zeros(TV_MAX_NODES, np.float32)
@@ -360,6 +368,94 @@ class TreeVerifier:
                                           ctypes.c_void_p(logits.data_ptr()), _ptr(am), _ptr(gap)),
                     "tv_head_top2")
         return am, gap
+
+    # ------------------------------------------------ kernel-level calls
+
+    def _partials(self, part, splits: int, rows: int, cols: int, what: str) -> int:
+        """Device address of split-K partials for `rows` rows and `cols`
+        columns in the library's layout (128-column blocks of 32 rows)."""
+        need = ((cols + 127) // 128) * int(splits) * 4096
+        if not (1 <= rows <= TV_MAX_NODES):
+            raise ValueError(f"{what}: {rows} rows, 1..32 supported")
+        check_device_tensor(part, f"{what}: partials", "float32", need)
+        return part.data_ptr()
+
+    def attention(self, q, k_cache, v_cache, ctx_len: int, parents, out) -> None:
+        """tv_attention: tree-masked attention of the tree's rows."""
+        p = _i32(parents)
+        n, QD = int(p.size), self.n_qhead * self.head_dim
+        check_device_tensor(q, "attention: q", "bfloat16", shape=(n, QD))
+        check_device_tensor(out, "attention: out", "bfloat16", shape=(n, QD))
+        check_device_tensor(k_cache, "attention: k_cache", "bfloat16")
+        check_device_tensor(v_cache, "attention: v_cache", "bfloat16", shape=tuple(k_cache.shape))
+        kvh, cap, d = k_cache.shape
+        if (kvh, d) != (self.n_kvhead, self.head_dim):
+            raise ValueError("attention: cache shape does not match the model")
+        self._check(self.lib.tv_attention(self.h, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), int(cap),
+                                          int(ctx_len), _ptr(p), n, out.data_ptr()), "tv_attention")
+
+    def rope_kv(self, part, splits: int, depth, ctx_len: int, q_out, k_cache, v_cache) -> None:
+        """tv_rope_kv: finish the QKV partials, rotate q and k, write the cache."""
+        dep = _i32(depth)
+        n = int(dep.size)
+        cols = (self.n_qhead + 2 * self.n_kvhead) * self.head_dim
+        pp = self._partials(part, splits, n, cols, "rope_kv")
+        check_device_tensor(q_out, "rope_kv: q_out", "bfloat16", shape=(n, self.n_qhead * self.head_dim))
+        check_device_tensor(k_cache, "rope_kv: k_cache", "bfloat16")
+        check_device_tensor(v_cache, "rope_kv: v_cache", "bfloat16", shape=tuple(k_cache.shape))
+        kvh, cap, d = k_cache.shape
+        if (kvh, d) != (self.n_kvhead, self.head_dim):
+            raise ValueError("rope_kv: cache shape does not match the model")
+        self._check(self.lib.tv_rope_kv(self.h, pp, int(splits), n, _ptr(dep), int(ctx_len), q_out.data_ptr(),
+                                        k_cache.data_ptr(), v_cache.data_ptr(), int(cap)), "tv_rope_kv")
+
+    def resid_norm(self, part, splits: int, x, w, y) -> None:
+        """tv_resid_norm: x += bf16(partial sums); y = RMSNorm(x) * w."""
+        n = int(x.shape[0])
+        pp = self._partials(part, splits, n, self.hidden, "resid_norm")
+        check_device_tensor(x, "resid_norm: x", "bfloat16", shape=(n, self.hidden))
+        check_device_tensor(y, "resid_norm: y", "bfloat16", shape=(n, self.hidden))
+        check_device_tensor(w, "resid_norm: w", "bfloat16", shape=(self.hidden,))
+        self._check(self.lib.tv_resid_norm(self.h, pp, int(splits), n, x.data_ptr(), w.data_ptr(), y.data_ptr()),
+                    "tv_resid_norm")
+
+    def recur_tree(self, kind: int, part, splits: int, parents, state, out, save_k, save_v, save_gc) -> None:
+        """tv_recur_tree: recurrent read-out of a tree and the saves for a commit."""
+        p = _i32(parents)
+        n = int(p.size)
+        QH, D = self.n_qhead, self.head_dim
+        cols = 3 * QH * D + (2 if kind == TV_LAYER_DELTA else 1) * QH
+        pp = self._partials(part, splits, n, cols, "recur_tree")
+        check_device_tensor(state, "recur_tree: state", "float32", shape=(QH, D, D))
+        check_device_tensor(out, "recur_tree: out", "bfloat16", shape=(n, QH * D))
+        check_device_tensor(save_k, "recur_tree: save_k", "bfloat16", shape=(TV_MAX_NODES, QH, D))
+        check_device_tensor(save_v, "recur_tree: save_v", "float32", shape=(TV_MAX_NODES, QH, D))
+        check_device_tensor(save_gc, "recur_tree: save_gc", "float32", shape=(TV_MAX_NODES, QH))
+        self._check(self.lib.tv_recur_tree(self.h, int(kind), pp, int(splits), _ptr(p), n, state.data_ptr(),
+                                           out.data_ptr(), save_k.data_ptr(), save_v.data_ptr(),
+                                           save_gc.data_ptr()), "tv_recur_tree")
+
+    def recur_commit(self, state, save_k, save_v, save_gc, path) -> None:
+        """tv_recur_commit: the state after `path` from tv_recur_tree's saves."""
+        pa = _i32(path)
+        QH, D = self.n_qhead, self.head_dim
+        check_device_tensor(state, "recur_commit: state", "float32", shape=(QH, D, D))
+        check_device_tensor(save_k, "recur_commit: save_k", "bfloat16", shape=(TV_MAX_NODES, QH, D))
+        check_device_tensor(save_v, "recur_commit: save_v", "float32", shape=(TV_MAX_NODES, QH, D))
+        check_device_tensor(save_gc, "recur_commit: save_gc", "float32", shape=(TV_MAX_NODES, QH))
+        self._check(self.lib.tv_recur_commit(self.h, state.data_ptr(), save_k.data_ptr(), save_v.data_ptr(),
+                                             save_gc.data_ptr(), _ptr(pa), int(pa.size)), "tv_recur_commit")
+
+    def gather_kv(self, k_cache, v_cache, ctx_len: int, path) -> None:
+        """tv_gather_kv: cache slot ctx_len + path[d] -> ctx_len + d."""
+        pa = _i32(path)
+        check_device_tensor(k_cache, "gather_kv: k_cache", "bfloat16")
+        check_device_tensor(v_cache, "gather_kv: v_cache", "bfloat16", shape=tuple(k_cache.shape))
+        kvh, cap, d = k_cache.shape
+        if (kvh, d) != (self.n_kvhead, self.head_dim):
+            raise ValueError("gather_kv: cache shape does not match the model")
+        self._check(self.lib.tv_gather_kv(self.h, k_cache.data_ptr(), v_cache.data_ptr(), int(cap), int(ctx_len),
+                                          _ptr(pa), int(pa.size)), "tv_gather_kv")
 
     def profile_enable(self, on: bool = True, only_prefix: str = "") -> None:
         self._check(self.lib.tv_profile_enable(self.h, int(on), only_prefix.encode()),

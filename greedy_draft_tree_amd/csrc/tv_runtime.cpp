@@ -102,6 +102,8 @@ struct tv_ctx {
     // residual tree sampling: per-row uniforms (pinned staging and device copy)
     double *h_resu = nullptr, *d_resu = nullptr;
     void *d_resparts = nullptr;   // per-row chunk maxima and sums of the residual decision
+    // device pointer table for the kernel-level calls (pinned staging and device copy)
+    void **h_tab = nullptr, **d_tab = nullptr;
     int ns_max = 0;
 
     // profiling
@@ -685,6 +687,8 @@ int tv_create(const tv_model_desc *md, void *stream, tv_ctx **out) {
     if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_resu, R * sizeof(double), hipHostMallocDefault);
     if (e == hipSuccess) e = hipMalloc((void **)&c->d_resu, R * sizeof(double));
     if (e == hipSuccess) e = hipMalloc(&c->d_resparts, R * kResidualPartBytes);
+    if (e == hipSuccess) e = hipHostMalloc((void **)&c->h_tab, 16 * sizeof(void *), hipHostMallocDefault);
+    if (e == hipSuccess) e = hipMalloc((void **)&c->d_tab, 16 * sizeof(void *));
     if (e != hipSuccess) return cleanup(TV_EHIP);
     // RoPE table: angle pos * theta^(-2i/D) in fp64, cos and sin rounded to fp32
     {
@@ -709,7 +713,8 @@ void tv_destroy(tv_ctx *c) {
     else hipDeviceSynchronize();
     void *dev[] = {c->X, c->XN, c->QR, c->ATT, c->ACT, c->zeros, c->logits, c->part, c->po, c->pm, c->pl,
                    c->rope_cos, c->rope_sin, c->d_meta, c->gemm_partial, c->pX, c->pXN, c->pQKV, c->pQR,
-                   c->pATT, c->pACT, c->pAB, c->pTok, c->ppo, c->ppm, c->ppl, c->d_resu, c->d_resparts};
+                   c->pATT, c->pACT, c->pAB, c->pTok, c->ppo, c->ppm, c->ppl, c->d_resu, c->d_resparts,
+                   c->d_tab};
     for (void *p : dev)
         if (p) hipFree(p);
     for (auto &q : c->reqs) {
@@ -722,7 +727,7 @@ void tv_destroy(tv_ctx *c) {
         if (q.save_v) hipFree(q.save_v);
         if (q.save_gc) hipFree(q.save_gc);
     }
-    void *host[] = {c->h_meta, c->h_res, c->h_tok, c->h_resu};
+    void *host[] = {c->h_meta, c->h_res, c->h_tok, c->h_resu, c->h_tab};
     for (void *p : host)
         if (p) hipHostFree(p);
     for (auto &r : c->recs) {
@@ -1333,6 +1338,184 @@ int tv_profile_get(tv_ctx *c, const char *prefix, double *total_ms, int *count) 
         }
     *total_ms = ms;
     *count = n;
+    return TV_OK;
+}
+
+} // extern "C"
+
+// ------------------------------------------------------- kernel-level calls
+namespace {
+
+// Tree metadata of one request's n-node tree (validated) for a kernel-level
+// call: depth and ancestor-or-self bits, copied to the device copy of the
+// pass record that the kernels read.
+int upload_tree_meta(tv_ctx *c, const int32_t *parents, int n) {
+    if (!parents || n < 1 || n > TV_MAX_NODES || parents[0] != -1)
+        return fail(c, TV_EINVAL, "tree of %d nodes: parents[0] must be -1", n);
+    for (int i = 1; i < n; ++i)
+        if (parents[i] < 0 || parents[i] >= i) return fail(c, TV_EINVAL, "parents[%d] = %d not in [0, %d)", i, parents[i], i);
+    PassMeta &pm = *c->h_meta;
+    memset(&pm, 0, sizeof pm);
+    for (int i = 0; i < n; ++i) {
+        const int p = parents[i];
+        pm.depth[i] = p < 0 ? 0 : pm.depth[p] + 1;
+        pm.anc[i] = (p < 0 ? 0u : pm.anc[p]) | (1u << i);
+        pm.row_req[i] = 0;
+        pm.path_len[i] = pm.depth[i] + 1;
+    }
+    HIPCHECK(c, hipMemcpyAsync(c->d_meta, c->h_meta, sizeof(PassMeta), hipMemcpyHostToDevice, c->stream));
+    return TV_OK;
+}
+
+int finish_call(tv_ctx *c) {
+    HIPCHECK(c, hipStreamSynchronize(c->stream));
+    if (c->prof) harvest(c);
+    return TV_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int tv_attention(tv_ctx *c, const void *q, const void *k_cache, const void *v_cache, int cap, int ctx_len,
+                 const int32_t *parents, int n_nodes, void *out) {
+    if (!c) return TV_EINVAL;
+    const tv_model_desc &m = c->m;
+    if (!q || !k_cache || !v_cache || !out) return fail(c, TV_EINVAL, "null operand");
+    if (ctx_len < 0 || cap < 1 || n_nodes < 1 || ctx_len + n_nodes > cap)
+        return fail(c, TV_ECAPACITY, "ctx_len %d + %d rows does not fit a cache of %d rows", ctx_len, n_nodes, cap);
+    const int D = m.head_dim;
+    DrainOnError drain(c);
+    int rc = upload_tree_meta(c, parents, n_nodes);
+    if (rc) return rc;
+    AttnArgs aa{};
+    aa.Q = (const uint16_t *)q; aa.meta = c->d_meta; aa.po = c->po; aa.pm = c->pm; aa.pl = c->pl;
+    aa.cap = cap; aa.G = c->G; aa.n_qhead = m.n_qhead;
+    aa.scale = (float)(1.0 / std::sqrt((double)D));
+    aa.nreq = 1;
+    PassReq &p = aa.rq[0];
+    p.Kc = (uint16_t *)k_cache; p.Vc = (uint16_t *)v_cache;
+    p.row0 = 0; p.n = n_nodes; p.ctx = ctx_len;
+    p.span = attn_span(ctx_len);
+    p.nsplit = (ctx_len + p.span - 1) / p.span;
+    aa.n = p.n; aa.span = p.span; aa.ns = p.nsplit + 1;
+    LAUNCH(c, "attn", launch_attn(c->stream, D, aa));
+    LAUNCH(c, "attn_combine", launch_attn_combine(c->stream, D, aa, (uint16_t *)out));
+    rc = finish_call(c);
+    if (rc) return rc;
+    drain.done();
+    return TV_OK;
+}
+
+int tv_rope_kv(tv_ctx *c, const float *qkv_part, int splits, int n_rows, const int32_t *depth, int ctx_len,
+               void *q_out, void *k_cache, void *v_cache, int cap) {
+    if (!c) return TV_EINVAL;
+    const tv_model_desc &m = c->m;
+    if (!qkv_part || !depth || !q_out || !k_cache || !v_cache) return fail(c, TV_EINVAL, "null operand");
+    if (n_rows < 1 || n_rows > kMaxRows) return fail(c, TV_EINVAL, "n_rows %d not in [1, %d]", n_rows, kMaxRows);
+    if (splits < 1 || splits > 4096) return fail(c, TV_EINVAL, "splits %d out of range", splits);
+    if (ctx_len < 0 || ctx_len + n_rows > cap) return fail(c, TV_ECAPACITY, "rows do not fit the cache");
+    for (int i = 0; i < n_rows; ++i)
+        if (depth[i] < 0 || ctx_len + depth[i] >= m.max_ctx)
+            return fail(c, TV_EINVAL, "row %d: position %d outside the rotation table", i, ctx_len + depth[i]);
+    DrainOnError drain(c);
+    PassMeta &pm = *c->h_meta;
+    memset(&pm, 0, sizeof pm);
+    for (int i = 0; i < n_rows; ++i) pm.depth[i] = depth[i];
+    HIPCHECK(c, hipMemcpyAsync(c->d_meta, c->h_meta, sizeof(PassMeta), hipMemcpyHostToDevice, c->stream));
+    RopeArgs ra{};
+    ra.part = qkv_part; ra.S = splits; ra.q_out = (uint16_t *)q_out;
+    ra.cosT = c->rope_cos; ra.sinT = c->rope_sin; ra.meta = c->d_meta;
+    ra.M = n_rows; ra.cap = cap; ra.QH = m.n_qhead; ra.KVH = m.n_kvhead; ra.D = m.head_dim; ra.nreq = 1;
+    ra.rq[0].Kc = (uint16_t *)k_cache; ra.rq[0].Vc = (uint16_t *)v_cache;
+    ra.rq[0].row0 = 0; ra.rq[0].n = n_rows; ra.rq[0].ctx = ctx_len;
+    LAUNCH(c, "rope_kv", launch_rope_kv(c->stream, ra));
+    int rc = finish_call(c);
+    if (rc) return rc;
+    drain.done();
+    return TV_OK;
+}
+
+int tv_resid_norm(tv_ctx *c, const float *part, int splits, int n_rows, void *x, const void *w, void *y) {
+    if (!c) return TV_EINVAL;
+    if (!part || !x || !w || !y) return fail(c, TV_EINVAL, "null operand");
+    if (n_rows < 1 || n_rows > kMaxRows) return fail(c, TV_EINVAL, "n_rows %d not in [1, %d]", n_rows, kMaxRows);
+    if (splits < 1 || splits > 4096) return fail(c, TV_EINVAL, "splits %d out of range", splits);
+    DrainOnError drain(c);
+    LAUNCH(c, "resid_norm", launch_resid_norm(c->stream, part, splits, n_rows, c->m.hidden, (const uint16_t *)w,
+                                              c->m.eps, (uint16_t *)x, (uint16_t *)y));
+    int rc = finish_call(c);
+    if (rc) return rc;
+    drain.done();
+    return TV_OK;
+}
+
+int tv_recur_tree(tv_ctx *c, int kind, const float *part, int splits, const int32_t *parents, int n_nodes,
+                  const float *state, void *out, void *save_k, float *save_v, float *save_gc) {
+    if (!c) return TV_EINVAL;
+    const tv_model_desc &m = c->m;
+    if (kind != TV_LAYER_RECUR && kind != TV_LAYER_DELTA) return fail(c, TV_EINVAL, "kind %d is not recurrent", kind);
+    if (!part || !state || !out || !save_k || !save_v || !save_gc) return fail(c, TV_EINVAL, "null operand");
+    if (splits < 1 || splits > 4096) return fail(c, TV_EINVAL, "splits %d out of range", splits);
+    DrainOnError drain(c);
+    int rc = upload_tree_meta(c, parents, n_nodes);
+    if (rc) return rc;
+    RecurArgs ra{};
+    ra.qkv_part = part; ra.qkv_S = splits;
+    ra.a_col = 3 * m.n_qhead * m.head_dim; ra.delta = kind == TV_LAYER_DELTA;
+    ra.S0 = state; ra.meta = c->d_meta; ra.out = (uint16_t *)out;
+    ra.save_k = (uint16_t *)save_k; ra.save_v = save_v; ra.save_gc = save_gc;
+    ra.row0 = 0; ra.n = n_nodes; ra.QH = m.n_qhead; ra.eps = m.eps;
+    LAUNCH(c, "recur_tree", launch_recur_tree(c->stream, m.head_dim, ra));
+    rc = finish_call(c);
+    if (rc) return rc;
+    drain.done();
+    return TV_OK;
+}
+
+int tv_recur_commit(tv_ctx *c, float *state, const void *save_k, const float *save_v, const float *save_gc,
+                    const int32_t *path, int path_len) {
+    if (!c) return TV_EINVAL;
+    if (!state || !save_k || !save_v || !save_gc || !path) return fail(c, TV_EINVAL, "null operand");
+    if (path_len < 1 || path_len > kMaxRows) return fail(c, TV_EINVAL, "path_len %d not in [1, %d]", path_len, kMaxRows);
+    for (int d = 0; d < path_len; ++d)
+        if (path[d] < 0 || path[d] >= kMaxRows) return fail(c, TV_EINVAL, "path[%d] = %d out of range", d, path[d]);
+    DrainOnError drain(c);
+    c->h_tab[0] = state;
+    HIPCHECK(c, hipMemcpyAsync(c->d_tab, c->h_tab, sizeof(void *), hipMemcpyHostToDevice, c->stream));
+    RecurCommitArgs ra{};
+    ra.states = (float *const *)c->d_tab;
+    ra.save_k = (const uint16_t *)save_k; ra.save_v = save_v; ra.save_gc = save_gc;
+    ra.path.len = path_len;
+    for (int d = 0; d < path_len; ++d) ra.path.node[d] = path[d];
+    ra.QH = c->m.n_qhead;
+    LAUNCH(c, "commit_state", launch_recur_commit(c->stream, c->m.head_dim, ra, 1));
+    int rc = finish_call(c);
+    if (rc) return rc;
+    drain.done();
+    return TV_OK;
+}
+
+int tv_gather_kv(tv_ctx *c, void *k_cache, void *v_cache, int cap, int ctx_len, const int32_t *path, int path_len) {
+    if (!c) return TV_EINVAL;
+    if (!k_cache || !v_cache || !path) return fail(c, TV_EINVAL, "null operand");
+    if (path_len < 1 || path_len > kMaxRows) return fail(c, TV_EINVAL, "path_len %d not in [1, %d]", path_len, kMaxRows);
+    for (int d = 0; d < path_len; ++d)
+        if (path[d] < d || path[d] >= kMaxRows || (d > 0 && path[d] <= path[d - 1]))
+            return fail(c, TV_EINVAL, "path[%d] = %d: a path's nodes increase and path[d] >= d", d, path[d]);
+    if (ctx_len < 0 || ctx_len + path[path_len - 1] >= cap) return fail(c, TV_ECAPACITY, "path rows outside the cache");
+    DrainOnError drain(c);
+    c->h_tab[0] = k_cache;
+    c->h_tab[1] = v_cache;
+    HIPCHECK(c, hipMemcpyAsync(c->d_tab, c->h_tab, 2 * sizeof(void *), hipMemcpyHostToDevice, c->stream));
+    PathArg pa{};
+    pa.len = path_len;
+    for (int d = 0; d < path_len; ++d) pa.node[d] = path[d];
+    LAUNCH(c, "commit_kv", launch_commit_kv(c->stream, (uint16_t *const *)c->d_tab, 1, c->m.n_kvhead, cap,
+                                            c->m.head_dim, ctx_len, pa));
+    int rc = finish_call(c);
+    if (rc) return rc;
+    drain.done();
     return TV_OK;
 }
 

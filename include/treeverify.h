@@ -20,8 +20,9 @@
  * deterministic-candidate residual sampling), drafting on the host (the
  * lookup drafter's tree from the request's own text, tv_lookup_draft, and
  * StairCut's cut of a candidate tree, tv_staircut), and kernel-level calls
- * for tests and
- * measurement (tv_linear, tv_head_top2, tv_pack_weight, tv_profile_*).
+ * for tests and measurement (tv_linear, tv_head_top2, tv_pack_weight,
+ * tv_attention, tv_rope_kv, tv_resid_norm, tv_recur_tree, tv_recur_commit,
+ * tv_gather_kv, tv_profile_*).
  *
  * Conventions shared by every call:
  *   - Every call returns TV_OK (0) or a negative TV_E* code and never throws.
@@ -333,6 +334,72 @@ int tv_linear(tv_ctx *ctx, const void *x, const void *w, int M, int N, int K, vo
  * packs (packing twice scrambles the matrix).  Synchronises the stream. */
 int tv_pack_weight(tv_ctx *ctx, void *w, int N, int K);
 int tv_head_top2(tv_ctx *ctx, const void *x, int M, float *logits_dev, int32_t *argmax, float *gap_ulps);
+
+/* Kernel-level calls of the pass's other kernels, on caller-given device
+ * operands, for per-kernel parity tests and measurement.  Shapes come from
+ * the context's model; each call validates its arguments, runs its kernels
+ * on the context's stream and synchronises it.  None reads bound weights.
+ *
+ * Split-K partial layout (the projections' output that the consumers
+ * finish): for `splits` k-ranges S, column n of row m (m < 32) of k-range s
+ * is the float at index ((n / 128) * S + s) * 4096 + m * 128 + n % 128.
+ * A consumer adds the S partials of an element in k-range order in fp32 and
+ * rounds the sum to bf16 (the projection's rounding point).
+ *
+ * tv_attention ("Drafters and tree verify", Tree verify through recurrent
+ *   layers: each node attends to the cached context and to its ancestors
+ *   and itself): grouped-query attention of the n_nodes rows of a tree.
+ *   q: [n_nodes, n_qhead * head_dim] bf16, already rotated; k_cache,
+ *   v_cache: [n_kvhead, cap, head_dim] bf16 whose slots [0, ctx_len) hold
+ *   the context and slot ctx_len + i node i's key and value; parents: host
+ *   [n_nodes], tree rules as tv_verify_tree.  Query head h uses KV head
+ *   h / (n_qhead / n_kvhead); scores are scaled by 1/sqrt(head_dim) and
+ *   normalised by an fp32 softmax.  out: [n_nodes, n_qhead * head_dim] bf16.
+ *   TV_ECAPACITY when ctx_len + n_nodes > cap.
+ * tv_rope_kv (same section: a node sits at position ctx_len + its depth and
+ *   in cache slot ctx_len + its index): finishes the QKV projection's
+ *   partials (columns: n_qhead, then n_kvhead, then n_kvhead heads of
+ *   head_dim) for n_rows <= 32 rows, rotates q and k of row i by position
+ *   ctx_len + depth[i] (host array; rotate-half pairs (j, j + head_dim/2),
+ *   angle pos * rope_theta^(-2j/head_dim)), writes the rotated q to q_out
+ *   [n_rows, n_qhead * head_dim] bf16 and k, v to cache slot ctx_len + i of
+ *   k_cache, v_cache [n_kvhead, cap, head_dim] bf16.  Positions must lie
+ *   below the model's max_ctx.
+ * tv_resid_norm: for n_rows <= 32 rows of x [n_rows, hidden] bf16 (in
+ *   place), x = bf16(x + bf16(sum of the `splits` partials)), then
+ *   y = bf16(x / sqrt(mean(x^2) + eps) * w) with w [hidden] bf16, y
+ *   [n_rows, hidden] bf16: the residual add and the next RMSNorm.
+ * tv_recur_tree (same section: the state along each root-to-node path,
+ *   never overwriting a parent's): the read-out of a recurrent layer of
+ *   `kind` TV_LAYER_RECUR or TV_LAYER_DELTA for an n_nodes tree.  part: the
+ *   stacked projection's partials, columns q, k and v (n_qhead heads of
+ *   head_dim each), then the n_qhead gate pre-activations, then for a delta
+ *   layer the n_qhead write-strength pre-activations; state: [n_qhead,
+ *   head_dim, head_dim] fp32, the state before the tree (key index first).
+ *   out: [n_nodes, n_qhead * head_dim] bf16 read-outs.  save_k [32, n_qhead,
+ *   head_dim] bf16, save_v [32, n_qhead, head_dim] fp32 and save_gc [32,
+ *   n_qhead] fp32 receive, per node, the normalised key, the value (a delta
+ *   layer: the pseudo-value) and the cumulative log-gate that
+ *   tv_recur_commit takes.
+ * tv_recur_commit (same section: the closed form of the state after the
+ *   accepted path): state = e^{gc_last} state + sum over the path of
+ *   e^{gc_last - gc_t} k_t u_t^T, in place, from tv_recur_tree's saves;
+ *   path: host node ids (path_len <= 32, each < 32), root first.
+ * tv_gather_kv (same section: the commit gathers the accepted rows): slot
+ *   ctx_len + path[d] -> ctx_len + d of k_cache and v_cache [n_kvhead, cap,
+ *   head_dim], in place; path: host, strictly increasing, path[d] >= d.
+ * Errors: TV_EINVAL for a null operand or a bad size, tree or path. */
+int tv_attention(tv_ctx *ctx, const void *q, const void *k_cache, const void *v_cache, int cap, int ctx_len,
+                 const int32_t *parents, int n_nodes, void *out);
+int tv_rope_kv(tv_ctx *ctx, const float *qkv_part, int splits, int n_rows, const int32_t *depth, int ctx_len,
+               void *q_out, void *k_cache, void *v_cache, int cap);
+int tv_resid_norm(tv_ctx *ctx, const float *part, int splits, int n_rows, void *x, const void *w, void *y);
+int tv_recur_tree(tv_ctx *ctx, int kind, const float *part, int splits, const int32_t *parents, int n_nodes,
+                  const float *state, void *out, void *save_k, float *save_v, float *save_gc);
+int tv_recur_commit(tv_ctx *ctx, float *state, const void *save_k, const float *save_v, const float *save_gc,
+                    const int32_t *path, int path_len);
+int tv_gather_kv(tv_ctx *ctx, void *k_cache, void *v_cache, int cap, int ctx_len, const int32_t *path,
+                 int path_len);
 
 /* Kernel timing: with `on` != 0, launches whose kernel name starts with
  * `only_prefix` (all launches when it is NULL or "") are bracketed by HIP

@@ -119,6 +119,12 @@ def ulp_bf16(x):
     return np.ldexp(1.0, e - 7)
 
 
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of one row in fp64: x / sqrt(mean(x^2) + eps) * w."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / math.sqrt(float(np.mean(x * x)) + eps) * np.asarray(w, dtype=np.float64)
+
+
 def log_sigmoid(a):
     return -np.logaddexp(0.0, -np.asarray(a, dtype=np.float64))
 
@@ -179,8 +185,7 @@ class Oracle:
         return y
 
     def rmsnorm(self, x: np.ndarray, wname: str) -> np.ndarray:
-        w = bf16_bits_to_f64(self.W[wname])
-        return x / math.sqrt(float(np.mean(x * x)) + self.s.eps) * w
+        return rms_norm(x, bf16_bits_to_f64(self.W[wname]), self.s.eps)
 
     def rope(self, x: np.ndarray, pos: int) -> np.ndarray:
         """Rotate each head [h, D] by angle pos*inv_freq[i] on pairs (i, i+D/2)."""
@@ -226,14 +231,16 @@ class Oracle:
         o = np.einsum("hkv,hk->hv", S, q)
         return o, S
 
-    def recurrent_token(self, kind: int, qkv: np.ndarray, a: np.ndarray, S_prev: np.ndarray):
+    def recurrent_token(self, kind: int, qkv: np.ndarray, a: np.ndarray, S_prev: np.ndarray,
+                        round_out: bool = True):
         """The token mixing of a recurrent layer from its projections (both
         already at their rounding point): ``qkv`` stacks q, k and v heads
         (QH*D values each), ``a`` the gate pre-activations and, for a delta
         layer, the write-strength pre-activations after them.  q and k are
         L2-normalised per head; the log-decay is log sigmoid(gate) and the
         write strength sigmoid(.).  Returns (read-out [QH*D] at its rounding
-        point, the new state held in fp32)."""
+        point, or unrounded with ``round_out=False``; the new state held in
+        fp32)."""
         s, r = self.s, self.r
         QH, D = s.n_qhead, s.head_dim
         q = r(self.l2norm(qkv[:QH * D].reshape(QH, D)))
@@ -244,7 +251,8 @@ class Oracle:
         else:
             o, S = self.delta_mix(q, k, v, log_sigmoid(a[:QH]), sigmoid(a[QH:2 * QH]), S_prev)
         # the state is held in fp32 between tokens
-        return r(o.reshape(-1)), (S if self.exact else f32(S))
+        o = o.reshape(-1)
+        return (r(o) if round_out else o), (S if self.exact else f32(S))
 
     def recurrent_layer(self, l: int, xn: np.ndarray, S_prev: np.ndarray):
         """Recurrent layer l on its normalised input row ``xn``: the stacked

@@ -325,3 +325,35 @@ def modifiers(vocab: int, seed: int, n_bias: int = 64, bias: float = 5.0,
         np.bitwise_or.at(words, idx // 32, (np.uint32(1) << (idx % 32).astype(np.uint32)))
         bits = words
     return Modifiers(float(penalty), ids, vals, bits)
+
+
+# ---------------------------------------------------- kernel-level inputs
+
+def bf16_normal(shape, seed: int, std: float = 1.0, device="cpu") -> torch.Tensor:
+    """N(0, std) drawn in fp32 and rounded to bf16 (one tensor)."""
+    return _normal_bf16(tuple(shape), seed, std, device)
+
+
+def dyadic_partials(splits: int, rows: int, cols: int, seed: int, std: float = 1.0) -> np.ndarray:
+    """[splits, rows, cols] float32 split-K partials whose values are
+    multiples of 2**-12 below 2**8 in magnitude, drawn around N(0, std/sqrt
+    (splits)) per split: any order of fp32 additions of one element's
+    partials is exact, so the sum has one value on every side."""
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0.0, std / math.sqrt(splits), size=(splits, rows, cols))
+    x = np.clip(np.round(x * 4096.0), -(2 ** 20 - 1), 2 ** 20 - 1) / 4096.0
+    return x.astype(np.float32)
+
+
+def splitk_layout(parts: np.ndarray) -> np.ndarray:
+    """Lay [S, rows <= 32, cols] partials out in the library's split-K layout:
+    column n of row m of k-range s at ((n // 128) * S + s) * 4096 + m * 128
+    + n % 128 (a flat float32 array; unused places are zero)."""
+    S, rows, cols = parts.shape
+    assert rows <= 32
+    nb = (cols + 127) // 128
+    out = np.zeros((nb, S, 32, 128), dtype=np.float32)
+    padded = np.zeros((S, rows, nb * 128), dtype=np.float32)
+    padded[:, :, :cols] = parts
+    out[:, :, :rows, :] = padded.reshape(S, rows, nb, 128).transpose(2, 0, 1, 3)
+    return out.reshape(-1)

@@ -228,3 +228,33 @@ def test_dense_linear_rows_bitwise_invariant(tv, N, K, R):
         y = torch.empty(M, N, dtype=torch.float32, device="cuda")
         tv.linear(x[perm].contiguous(), w, y)
         assert torch.equal(y, full[perm]), M
+
+
+def test_head_top2_exact_ties_go_to_the_lowest_id():
+    """Planted exact ties: head rows 5, 700 and 1000 are identical, so their
+    fp32 logits are bitwise equal; they are the largest of the row, so the
+    top-2 reduce must return the lowest of them with a gap of 0, and a
+    second planted pair (rows 2 and 3, the only rows above the rest in row
+    1's input) the same.  Ties are decided under a strict order, so this
+    holds for any merge order of the candidates."""
+    _gpu()
+    from greedy_draft_tree_amd import TreeVerifier
+    shape = synth.C0
+    s = torch.cuda.current_stream().cuda_stream
+    t = TreeVerifier.for_shape(shape, max_ctx=64, max_req=1, stream=s)
+    H, V = shape.hidden, shape.vocab
+    g = torch.Generator(device="cpu").manual_seed(3)
+    w = (torch.randn(V, H, generator=g) * 0.02).to(torch.bfloat16)
+    w[5] = w[700] = w[1000] = 0.05
+    w[2] = w[3] = torch.linspace(-0.06, 0.06, H).to(torch.bfloat16)
+    t.bind("head", w.cuda())
+    x = torch.ones(2, H, dtype=torch.bfloat16)
+    x[1] = torch.linspace(-1, 1, H).to(torch.bfloat16)
+    logits = torch.empty(2, V, dtype=torch.float32, device="cuda")
+    am, gap = t.head_top2(x.cuda(), logits)
+    lg = logits.cpu()
+    assert lg[0, 5] == lg[0, 700] == lg[0, 1000] and int(lg[0].argmax()) in (5, 700, 1000)
+    assert am[0] == 5 and gap[0] == 0.0
+    assert lg[1, 2] == lg[1, 3] and float(lg[1, 2]) > float(lg[1, 4:].max())
+    assert am[1] == 2 and gap[1] == 0.0
+    t.close()
