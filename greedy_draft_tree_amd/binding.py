@@ -23,7 +23,7 @@ SYMBOLS = ("tv_create", "tv_destroy", "tv_last_error", "tv_bind", "tv_set_histor
            "tv_accept_walk", "tv_commit", "tv_round", "tv_ctx_len", "tv_profile_enable",
            "tv_profile_reset", "tv_profile_get", "tv_linear", "tv_head_top2", "tv_pack_weight",
            "tv_staircut", "tv_residual_round", "tv_lookup_draft", "tv_attention", "tv_rope_kv",
-           "tv_resid_norm", "tv_recur_tree", "tv_recur_commit", "tv_gather_kv")
+           "tv_resid_norm", "tv_recur_tree", "tv_recur_commit", "tv_gather_kv", "tv_linear_noalloc")
 
 
 class TVError(RuntimeError):
@@ -84,6 +84,7 @@ def load_library():
         "tv_recur_tree": ([P, I, P, I, P, I, P, P, P, P, P], I),
         "tv_recur_commit": ([P, P, P, P, P, P, I], I),
         "tv_gather_kv": ([P, P, P, I, I, P, I], I),
+        "tv_linear_noalloc": ([P, P, I, I, I, P, I, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -139,6 +140,27 @@ def _logits_ptr(logits, rows: int, vocab: int, what: str):
         return None
     check_device_tensor(logits, f"{what}: logits", "float32", rows * vocab)
     return logits.data_ptr()
+
+
+def linear_noalloc(x, w, y, stream: Optional[int] = None) -> None:
+    """tv_linear_noalloc: y = x w^T on static library scratch, no context and
+    no allocation; only enqueues on ``stream`` (default: torch's current
+    stream, passed by the caller as an int handle)."""
+    lib = _lib if _lib is not None else load_library()
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("linear_noalloc: x and w must be matrices")
+    M, K = x.shape
+    N = w.shape[0]
+    check_device_tensor(x, "linear_noalloc: x", "bfloat16")
+    check_device_tensor(w, "linear_noalloc: w", "bfloat16", shape=(N, K))
+    if _dtype_name(y) not in ("bfloat16", "float32"):
+        raise ValueError(f"linear_noalloc: y dtype {_dtype_name(y)}, expected bfloat16 or float32")
+    check_device_tensor(y, "linear_noalloc: y", shape=(M, N))
+    rc = lib.tv_linear_noalloc(x.data_ptr(), w.data_ptr(), M, N, K, y.data_ptr(),
+                               1 if _dtype_name(y) == "float32" else 0, ctypes.c_void_p(stream or 0))
+    if rc != TV_OK:
+        msg = lib.tv_last_error(None)
+        raise TVError(rc, f"tv_linear_noalloc: {msg.decode() if msg else ''}")
 
 
 # output buffers of accept_walk, reused across calls (results are copied out)

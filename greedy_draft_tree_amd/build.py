@@ -5,7 +5,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libtreeverify.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("tv_kernels.hip", "tv_runtime.cpp", "tv_staircut.cpp", "tv_lookup.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("tv_kernels.hip", "tv_runtime.cpp", "tv_staircut.cpp", "tv_lookup.cpp",
+                                                         "tv_noalloc.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          # packed fp32 arithmetic stays off: scalar fp32 only

@@ -220,4 +220,7 @@ hipError_t launch_recur_commit(hipStream_t s, int D, const RecurCommitArgs &a, i
 hipError_t launch_commit_kv(hipStream_t s, uint16_t *const *kv_ptrs, int n_layers, int KVH,
                             int cap, int D, int ctx, const PathArg &path);
 
+// message of the last failed context-free call on this thread (tv_noalloc.hip)
+const char *noalloc_last_error();
+
 } // namespace tv

@@ -737,7 +737,7 @@ void tv_destroy(tv_ctx *c) {
     delete c;
 }
 
-const char *tv_last_error(tv_ctx *c) { return c ? c->err.c_str() : "null context"; }
+const char *tv_last_error(tv_ctx *c) { return c ? c->err.c_str() : noalloc_last_error(); }
 
 int tv_bind(tv_ctx *c, const char *name, void *ptr, size_t bytes) {
     if (!c || !name) return TV_EINVAL;

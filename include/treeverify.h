@@ -110,6 +110,8 @@ typedef struct tv_ctx tv_ctx;
 /* Create a context; `stream` is a hipStream_t (NULL = the null stream). */
 int tv_create(const tv_model_desc *m, void *stream, tv_ctx **out);
 void tv_destroy(tv_ctx *ctx);
+/* The message of the last failed call on `ctx`; with ctx == NULL, of the
+ * last failed context-free call on the calling thread. */
 const char *tv_last_error(tv_ctx *ctx);
 
 /* Bind a caller-owned device buffer by name.  `bytes` must equal the
@@ -400,6 +402,21 @@ int tv_recur_commit(tv_ctx *ctx, float *state, const void *save_k, const float *
                     const int32_t *path, int path_len);
 int tv_gather_kv(tv_ctx *ctx, void *k_cache, void *v_cache, int cap, int ctx_len, const int32_t *path,
                  int path_len);
+
+/* tv_linear_noalloc: tv_linear for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same operands, kernels and results as tv_linear (bit
+ * for bit), but it takes no context and allocates nothing: its scratch (a
+ * zero block, split-K partials and top-2 candidates) is one static device
+ * array of 12 MiB + 256 B per GPU, which the library holds until the
+ * process ends.  It only enqueues work on `stream` (a hipStream_t, NULL =
+ * the null stream) and does not synchronise it.  Every call on one GPU
+ * shares that GPU's array, so calls that overlap on a GPU (other streams,
+ * other threads) race; calls on one stream are ordered.  TV_EINVAL for a
+ * shape whose scratch exceeds the array (fp32 output with M * ceil(N/128)
+ * * 16 bytes above 4 MiB); the message is tv_last_error(NULL) on the
+ * calling thread. */
+int tv_linear_noalloc(const void *x, const void *w, int M, int N, int K, void *y, int y_fp32, void *stream);
 
 /* Kernel timing: with `on` != 0, launches whose kernel name starts with
  * `only_prefix` (all launches when it is NULL or "") are bracketed by HIP
