@@ -10,10 +10,14 @@ the model's own greedy tokens along their spine (learned in warm-up), so the
 accept walk takes the spine and the commit moves real rows; branches are
 uniform ids.
 
-Configurations (``--config``; the default c1 is the headline workload):
+Configurations (``--config``; the default c2 is the headline workload):
 
+* c2: 64 decoder layers of width 5120 + fp32 head (about 27B parameters),
+  trees n = 8/16/24/32 at ``ctx`` (1024); with no ``--no-extras`` the same
+  stack is also timed at the ``--extra-ctx`` contexts (8192), reported as
+  extra keys ``ctx<N>``, and one such layer + the head (c1) as the extra key
+  ``c1_layer``.
 * c1: one 5120-wide decoder layer + fp32 head, trees n = 8/16/24/32.
-* c2: 64 such layers.
 * c3: the 64-layer hybrid (48 gated-recurrence + 16 attention layers), n = 16.
 * c3d: c3 with gated delta-rule (Gated DeltaNet) layers in place of the plain
   gated recurrence, n = 16.
@@ -35,8 +39,12 @@ KV and state reads, tree KV written, logits written, committed rows and
 states moved) divided by its wall time.  ``roofline`` reports the dominant
 kernel (the fp32 head for c1; the gate/up projection, which takes the most
 time summed over layers, for the stacks) timed with HIP events on the
-library's stream during the timed region.  ``cpu_baseline`` times the CPU
-oracle on the same trees (c1 and c2).
+library's stream during the timed region; ``traffic`` is the kernel's HBM
+bytes per launch from the committed rocprofv3 counter summary in profiles/,
+reported only while the kernel source matches the one counted.
+``cpu_baseline`` times the CPU oracle on one 8-node tree of the same
+workload (``--cpu-sample full``: the four trees), repeated for at least 10 s
+(c1 and c2).
 """
 from __future__ import annotations
 
@@ -60,7 +68,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c1", choices=["c1", "c2", "c3", "c3d", "c4"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c3d", "c4"])
     ap.add_argument("--ctx", type=int, default=1024)
     ap.add_argument("--ctx2", type=int, default=8192, help="second request's context (c4)")
     ap.add_argument("--temperature", type=float, default=0.0,
@@ -79,7 +87,11 @@ def parse():
     ap.add_argument("--chunk", type=int, default=512, help="dense prefill chunk (rows)")
     ap.add_argument("--price-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", default="full",
+    ap.add_argument("--extra-ctx", default="8192",
+                    help="c2: the same stack also timed at these contexts (extra keys ctx<N>)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="c2: skip the extra contexts and the one-layer (c1) extra keys")
+    ap.add_argument("--cpu-sample", default="n8",
                     help="'full' = the same four trees; 'n8' = one 8-node tree")
     ap.add_argument("--kernel-breakdown", action="store_true",
                     help="add per-kernel event timings (an extra untimed pass)")
@@ -118,11 +130,12 @@ def model_bytes(shape, n, ctxs, path_lens, mods=False):
     return b
 
 
-def committed_traffic():
-    """Per-launch HBM bytes of the head kernel from the committed rocprofv3
-    counter summary, if the kernel source it was taken on is unchanged."""
+def committed_traffic(summary):
+    """Per-launch HBM bytes of a kernel from its committed rocprofv3 counter
+    summary (profiles/<summary>), if the kernel source it was taken on is
+    unchanged."""
     here = os.path.dirname(os.path.abspath(__file__))
-    summ = os.path.join(here, "profiles", "gemm_head_c1_layer_ctx1024_counters.md")
+    summ = os.path.join(here, "profiles", summary)
     src = os.path.join(here, "greedy_draft_tree_amd", "csrc", "tv_kernels.hip")
     if not os.path.exists(summ):
         return None
@@ -180,16 +193,193 @@ def make_wrong(parents, tokens, argmax, vocab):
     return tokens
 
 
+def build_workload(a, shape, max_ctx, n_req, want_cpu):
+    import torch
+    import workloads
+    print(f"[bench] building {shape.name} (max ctx {max_ctx})", file=sys.stderr, flush=True)
+    wl = workloads.build(shape, max_ctx=max_ctx, max_req=n_req, weight_device="cuda", host_copy=want_cpu)
+    torch.cuda.synchronize()
+    return wl
+
+
+def setup(a, wl, shape, ns, ctxs, mods_on):
+    """Load the contexts (synthetic caches and states), modifiers and
+    sampling, and make the trees: the spine carries the model's own tokens
+    (learned here), or for the joint config a drafter wrong at every node."""
+    import synth
+    import workloads
+    tv = wl.tv
+    n_req = len(ctxs)
+    hist, kv = [], None
+    for r, ctx in enumerate(ctxs):
+        h = synth.uniform_ids(ctx, shape.vocab, 40 + r) if mods_on else []
+        kvr = workloads.load_context(wl, r, ctx, seed=3 + r, history=h, state_seed=6)
+        if r == 0:
+            kv = kvr
+        hist.append(h)
+    for r in range(n_req):
+        if mods_on:
+            md = synth.modifiers(shape.vocab, 7 + r)
+            tv.set_modifiers(r, md.rep_penalty, md.bias_ids, md.bias_vals, md.allow_bits)
+        else:
+            tv.set_modifiers(r, 1.0)
+        tv.set_sampling(r, a.temperature if a.temperature > 0 else 0.0, a.seed + r)
+    trees = {}
+    for n in ns:
+        per_req = []
+        for r in range(n_req):
+            parents = synth.spine_tree(n, 4)
+            tokens = synth.tree_tokens(parents, shape.vocab, 5 + n + 100 * r, root_token=17 + r)
+            if mods_on:
+                for _ in range(4):   # a changed token changes its subtree's rows: repeat until stable
+                    am, _ = tv.verify_tree(r, parents, tokens)
+                    fixed = make_wrong(parents, tokens, am, shape.vocab)
+                    if np.array_equal(fixed, tokens):
+                        break
+                    tokens = fixed
+            else:
+                tokens = learn_spine(tv, parents, tokens, r)
+            per_req.append((parents, tokens))
+        trees[n] = per_req
+    print(f"[bench] {shape.name} ctx {ctxs}: trees ready", file=sys.stderr, flush=True)
+    return hist, kv, trees
+
+
+def time_rounds(a, wl, shape, ns, ctxs, hist, trees, kern, mods_on):
+    """Warm-up, then exactly a.steps steps (every tree size once per step),
+    bracketed by device synchronisations; the dominant kernel `kern` is
+    timed by HIP events on the library's stream during the timed steps."""
+    import torch
+    from greedy_draft_tree_amd import accept_walk
+    tv = wl.tv
+    n_req = len(ctxs)
+    reqs = list(range(n_req))
+    res_rng = np.random.default_rng(a.seed)
+
+    def round_(n):
+        per_req = trees[n]
+        if n_req == 1 and a.residual > 0:   # verify, residual walk and commit in one call
+            parents, tokens = per_req[0]
+            path, _ = tv.residual_round(0, parents, tokens, a.residual, res_rng.random(32), logits=wl.logits)
+            tv.set_history(0, hist[0], ctxs[0])
+            return [len(path)]
+        if n_req == 1:   # verify, accept walk and commit in one library call
+            parents, tokens = per_req[0]
+            _, _, path, _ = tv.round(0, parents, tokens, logits=wl.logits)
+            tv.set_history(0, hist[0], ctxs[0])
+            return [len(path)]
+        am, _ = tv.verify_trees(reqs, [p for p, _ in per_req], [t for _, t in per_req], logits=wl.logits)
+        lens = []
+        for r in range(n_req):
+            parents, tokens = per_req[r]
+            path, _ = accept_walk(parents, tokens, am[r * n:(r + 1) * n])
+            tv.commit(r, path)
+            tv.set_history(r, hist[r], ctxs[r])
+            lens.append(len(path))
+        return lens
+
+    for _ in range(a.warmup):
+        for n in ns:
+            round_(n)
+    tv.profile_reset()
+    tv.profile_enable(True, kern)
+    per_n = {n: [] for n in ns}
+    lens_seen = {n: [] for n in ns}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        for n in ns:
+            s = time.perf_counter()
+            lens = round_(n)
+            per_n[n].append(time.perf_counter() - s)
+            lens_seen[n].append(lens)
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    k_ms, k_cnt = tv.profile_get(kern)
+    tv.profile_enable(False)
+    print(f"[bench] {shape.name} ctx {ctxs}: {a.steps} steps in {total:.3f} s", file=sys.stderr, flush=True)
+
+    all_bytes = sum(model_bytes(shape, n, ctxs, lens, mods_on) for n in ns for lens in lens_seen[n])
+    per = {}
+    for n in ns:
+        ms = float(np.median(per_n[n]) * 1e3)
+        plen = [float(np.mean([l[r] for l in lens_seen[n]])) for r in range(n_req)]
+        by = model_bytes(shape, n, ctxs, [int(round(x)) for x in plen], mods_on)
+        key = str(n) if n_req == 1 else "+".join([str(n)] * n_req)
+        per[key] = {"ms_median": round(ms, 4), "ms_min": round(float(np.min(per_n[n]) * 1e3), 4),
+                    "GBps": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / HBM_PEAK_GBS, 4),
+                    "rows_per_s": round(n * n_req / ms * 1e3, 1), "bytes": by,
+                    "path_len": plen[0] if n_req == 1 else plen}
+    ratio = per["16"]["ms_median"] / per["8"]["ms_median"] if "8" in per and "16" in per else None
+    k_avg_ms = k_ms / max(k_cnt, 1)
+    if kern == "gemm_head":
+        kb = float(np.mean([head_bytes(shape, n * n_req) for n in ns]))
+        kname = "gemm_head (k_gemm<EPI_HEAD>)"
+        summary = "gemm_head_c1_layer_ctx1024_counters.md"
+    else:
+        kb = float(np.mean([gateup_bytes(shape, n * n_req) for n in ns]))
+        kname = "gemm_gateup (k_gemm<EPI_SWIGLU>, split-K partials)"
+        summary = "gemm_gateup_c2_stack64_ctx1024_counters.md"
+    achieved = kb / (k_avg_ms * 1e-3) / 1e9
+    counted = shape.name in ("c1_layer", "c2_stack64") and ctxs == [1024] and not mods_on
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": committed_traffic(summary) if counted else None,
+            "kernel": kname, "avg_us": round(k_avg_ms * 1e3, 2), "bytes_per_launch": int(kb), "launches": k_cnt}
+    return {"value": round(all_bytes / total / 1e9, 2), "ms_per_step": round(total / a.steps * 1e3, 4),
+            "step_bytes": all_bytes // a.steps, "per_n": per,
+            "ratio_16_over_8": round(ratio, 4) if ratio else None, "roofline": roof,
+            "round_": round_}
+
+
+def kernel_breakdown(tv, round_, ns):
+    tv.profile_reset()
+    tv.profile_enable(True, "")
+    for _ in range(5):
+        for n in ns:
+            round_(n)
+    kernels = {}
+    for k in ("embed_norm", "resid_norm", "gemm_qkv", "rope_kv", "attn", "attn_combine", "gemm_o",
+              "gemm_gateup", "splitk_finish", "gemm_down", "gemm_gate", "recur_tree", "gemm_head",
+              "top2", "residual", "commit_kv", "commit_state"):
+        ms, cnt = tv.profile_get(k)
+        if cnt:
+            kernels[k] = {"avg_us": round(ms / cnt * 1e3, 2), "launches": cnt}
+    # prefix counts: "attn" also matches "attn_combine", "gemm_gate" also "gemm_gateup"
+    for k, sub in (("attn", "attn_combine"), ("gemm_gate", "gemm_gateup")):
+        if k in kernels and sub in kernels:
+            ms, cnt = tv.profile_get(k)
+            ms2, cnt2 = tv.profile_get(sub)
+            if cnt > cnt2:
+                kernels[k] = {"avg_us": round((ms - ms2) / (cnt - cnt2) * 1e3, 2), "launches": cnt - cnt2}
+            else:
+                del kernels[k]
+    tv.profile_enable(False)
+    return kernels
+
+
+def describe(config, shape, ctxs, ns, a):
+    wname = {"c1": "c1_layer: 1 x", "c2": "c2_stack64: 64 x",
+             "c3": "c3_hybrid64: 48 recurrent + 16 attention layers x",
+             "c3d": "c3d_delta64: 48 gated delta-rule + 16 attention layers x",
+             "c4": "c4 on c2_stack64: 64 x"}[config]
+    return (f"{wname} (hidden {shape.hidden}, {shape.n_qhead}q/{shape.n_kvhead}kv heads x {shape.head_dim}, "
+            f"SwiGLU {shape.ffn}) + fp32 head V={shape.vocab}; KV cache {'/'.join(map(str, ctxs))} rows; "
+            f"one step = verify+accept+commit of trees n={','.join(map(str, ns))}"
+            + (" for 2 requests in one pass, modifiers on, wrong drafter" if config == "c4" else "")
+            + (f"; sampled requests (temperature {a.temperature}, seed {a.seed})" if a.temperature > 0 else "")
+            + (f"; residual tree sampling at temperature {a.residual}" if a.residual > 0 else ""))
+
+
 def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
               "(a verify does not shard: see the design notes on multi-GPU)", file=sys.stderr)
         sys.exit(2)
+    import gc
     import torch
     import synth
-    import workloads
-    from greedy_draft_tree_amd import accept_walk
 
     shape = {"c1": synth.C1, "c2": synth.C2, "c3": synth.C3, "c3d": synth.C3D, "c4": synth.C2}[a.config]
     ns = {"c1": NS, "c2": NS, "c3": (16,), "c3d": (16,), "c4": (16,)}[a.config]
@@ -209,186 +399,63 @@ def main():
         dst_t.copy_(src_t)
         torch.cuda.synchronize()
         del src_t, dst_t
-    print(f"[bench] building {shape.name} ctx={ctxs}", file=sys.stderr, flush=True)
+    extra_ctx = [int(x) for x in a.extra_ctx.split(",") if x] if (a.config == "c2" and not a.no_extras) else []
     want_cpu = (not a.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0
                 and a.config in ("c1", "c2"))
-    wl = workloads.build(shape, max_ctx=max(ctxs) + 64, max_req=n_req, weight_device="cuda",
-                         host_copy=want_cpu)
-    hist = []
-    kv = None
-    for r, ctx in enumerate(ctxs):
-        h = synth.uniform_ids(ctx, shape.vocab, 40 + r) if mods_on else []
-        kvr = workloads.load_context(wl, r, ctx, seed=3 + r, history=h, state_seed=6)
-        if r == 0:
-            kv = kvr
-        hist.append(h)
-    tv = wl.tv
-    if mods_on:
-        for r in range(n_req):
-            md = synth.modifiers(shape.vocab, 7 + r)
-            tv.set_modifiers(r, md.rep_penalty, md.bias_ids, md.bias_vals, md.allow_bits)
-    if a.temperature > 0:
-        for r in range(n_req):
-            tv.set_sampling(r, a.temperature, a.seed + r)
-
-    # trees: spine carries the model's own greedy tokens (learned in warm-up);
-    # c4's drafter is wrong at every node instead
-    trees = {}
-    for n in ns:
-        per_req = []
-        for r in range(n_req):
-            parents = synth.spine_tree(n, 4)
-            tokens = synth.tree_tokens(parents, shape.vocab, 5 + n + 100 * r, root_token=17 + r)
-            if mods_on:
-                for _ in range(4):   # a changed token changes its subtree's rows: repeat until stable
-                    am, _ = tv.verify_tree(r, parents, tokens)
-                    fixed = make_wrong(parents, tokens, am, shape.vocab)
-                    if np.array_equal(fixed, tokens):
-                        break
-                    tokens = fixed
-            else:
-                tokens = learn_spine(tv, parents, tokens, r)
-            per_req.append((parents, tokens))
-        trees[n] = per_req
-    print("[bench] trees ready", file=sys.stderr, flush=True)
-    reqs = list(range(n_req))
-    res_rng = np.random.default_rng(a.seed)
-
-    def round_(n):
-        per_req = trees[n]
-        if n_req == 1 and a.residual > 0:   # verify, residual walk and commit in one call
-            parents, tokens = per_req[0]
-            path, _ = tv.residual_round(0, parents, tokens, a.residual, res_rng.random(32), logits=wl.logits)
-            tv.set_history(0, hist[0], ctxs[0])
-            return [len(path)]
-        if n_req == 1:   # verify, accept walk and commit in one library call
-            parents, tokens = per_req[0]
-            _, _, path, _ = tv.round(0, parents, tokens, logits=wl.logits)
-            tv.set_history(0, hist[0], ctxs[0])
-            return [len(path)]
-        else:
-            am, _ = tv.verify_trees(reqs, [p for p, _ in per_req], [t for _, t in per_req],
-                                    logits=wl.logits)
-            ams = [am[r * n:(r + 1) * n] for r in range(n_req)]
-        lens = []
-        for r in range(n_req):
-            parents, tokens = per_req[r]
-            path, _ = accept_walk(parents, tokens, ams[r])
-            tv.commit(r, path)
-            tv.set_history(r, hist[r], ctxs[r])
-            lens.append(len(path))
-        return lens
-
-    for _ in range(a.warmup):
-        for n in ns:
-            round_(n)
-
+    wl = build_workload(a, shape, max(ctxs + extra_ctx) + 64, n_req, want_cpu)
+    hist, kv, trees = setup(a, wl, shape, ns, ctxs, mods_on)
     kern = "gemm_head" if a.config == "c1" else "gemm_gateup"
-    tv.profile_reset()
-    tv.profile_enable(True, kern)
-    per_n = {n: [] for n in ns}
-    lens_seen = {n: [] for n in ns}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(a.steps):
-        for n in ns:
-            s = time.perf_counter()
-            lens = round_(n)
-            per_n[n].append(time.perf_counter() - s)
-            lens_seen[n].append(lens)
-    torch.cuda.synchronize()
-    total = time.perf_counter() - t0
-    k_ms, k_cnt = tv.profile_get(kern)
-    tv.profile_enable(False)
+    res = time_rounds(a, wl, shape, ns, ctxs, hist, trees, kern, mods_on)
 
-    all_bytes = sum(model_bytes(shape, n, ctxs, lens, mods_on) for n in ns for lens in lens_seen[n])
-    step_bytes = all_bytes // a.steps
-    value = all_bytes / total / 1e9
-    per = {}
-    for n in ns:
-        ms = float(np.median(per_n[n]) * 1e3)
-        plen = [float(np.mean([l[r] for l in lens_seen[n]])) for r in range(n_req)]
-        by = model_bytes(shape, n, ctxs, [int(round(x)) for x in plen], mods_on)
-        key = str(n) if n_req == 1 else "+".join([str(n)] * n_req)
-        per[key] = {"ms_median": round(ms, 4), "ms_min": round(float(np.min(per_n[n]) * 1e3), 4),
-                    "GBps": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / HBM_PEAK_GBS, 4),
-                    "rows_per_s": round(n * n_req / ms * 1e3, 1), "bytes": by,
-                    "path_len": plen[0] if n_req == 1 else plen}
-    ratio = per["16"]["ms_median"] / per["8"]["ms_median"] if "8" in per and "16" in per else None
-    k_avg_ms = k_ms / max(k_cnt, 1)
-    if kern == "gemm_head":
-        kb = float(np.mean([head_bytes(shape, n * n_req) for n in ns]))
-        kname = "gemm_head (k_gemm<EPI_HEAD>)"
-    else:
-        kb = float(np.mean([gateup_bytes(shape, n * n_req) for n in ns]))
-        kname = "gemm_gateup (k_gemm<EPI_SWIGLU>, split-K partials)"
-    achieved = kb / (k_avg_ms * 1e-3) / 1e9
-
-    kernels = None
-    if a.kernel_breakdown:
-        tv.profile_reset()
-        tv.profile_enable(True, "")
-        for _ in range(5):
-            for n in ns:
-                round_(n)
-        kernels = {}
-        for k in ("embed_norm", "resid_norm", "gemm_qkv", "rope_kv", "attn", "attn_combine", "gemm_o",
-                  "gemm_gateup", "splitk_finish", "gemm_down", "gemm_gate", "recur_tree", "gemm_head",
-                  "top2", "residual", "commit_kv", "commit_state"):
-            ms, cnt = tv.profile_get(k)
-            if cnt:
-                kernels[k] = {"avg_us": round(ms / cnt * 1e3, 2), "launches": cnt}
-        # prefix counts: "attn" also matches "attn_combine", "gemm_gate" also "gemm_gateup"
-        for k, sub in (("attn", "attn_combine"), ("gemm_gate", "gemm_gateup")):
-            if k in kernels and sub in kernels:
-                ms, cnt = tv.profile_get(k)
-                ms2, cnt2 = tv.profile_get(sub)
-                if cnt > cnt2:
-                    kernels[k] = {"avg_us": round((ms - ms2) / (cnt - cnt2) * 1e3, 2), "launches": cnt - cnt2}
-                else:
-                    del kernels[k]
-        tv.profile_enable(False)
-
+    kernels = kernel_breakdown(wl.tv, res["round_"], ns) if a.kernel_breakdown else None
     cpu = None
     if want_cpu:
         cpu = cpu_baseline(shape, wl, kv, ctxs[0], {n: trees[n][0] for n in ns}, a.cpu_sample, ns)
+        wl.host_weights = None
+        gc.collect()
 
-    wname = {"c1": "c1_layer: 1 x", "c2": "c2_stack64: 64 x",
-             "c3": "c3_hybrid64: 48 recurrent + 16 attention layers x",
-             "c3d": "c3d_delta64: 48 gated delta-rule + 16 attention layers x",
-             "c4": "c4 on c2_stack64: 64 x"}[a.config]
-    desc = (f"{wname} (hidden {shape.hidden}, {shape.n_qhead}q/{shape.n_kvhead}kv heads x {shape.head_dim}, "
-            f"SwiGLU {shape.ffn}) + fp32 head V={shape.vocab}; KV cache {'/'.join(map(str, ctxs))} rows; "
-            f"one step = verify+accept+commit of trees n={','.join(map(str, ns))}"
-            + (" for 2 requests in one pass, modifiers on, wrong drafter" if a.config == "c4" else "")
-            + (f"; sampled requests (temperature {a.temperature}, seed {a.seed})" if a.temperature > 0 else "")
-            + (f"; residual tree sampling at temperature {a.residual}" if a.residual > 0 else ""))
     out = {
         "metric": "ms per tree verify + achieved HBM GB/s at 8/16/24/32 nodes, 1k ctx, 1 GPU",
-        "value": round(value, 2),
+        "value": res["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(total / a.steps * 1e3, 4),
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": desc, "ctx": ctxs[0] if n_req == 1 else ctxs, "tree_nodes": list(ns),
-                   "requests": n_req, "step_bytes": step_bytes,
+        "config": {"workload": describe(a.config, shape, ctxs, ns, a), "ctx": ctxs[0] if n_req == 1 else ctxs,
+                   "tree_nodes": list(ns), "requests": n_req, "step_bytes": res["step_bytes"],
                    "sampling": {"temperature": a.temperature, "seed": a.seed} if a.temperature > 0 else None,
                    "residual_temperature": a.residual if a.residual > 0 else None},
-        "per_n": per,
-        "ratio_16_over_8": round(ratio, 4) if ratio else None,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": committed_traffic() if (a.config == "c1" and a.ctx == 1024) else None,
-                     "kernel": kname, "avg_us": round(k_avg_ms * 1e3, 2),
-                     "bytes_per_launch": int(kb), "launches": k_cnt},
+        "per_n": res["per_n"],
+        "ratio_16_over_8": res["ratio_16_over_8"],
+        "roofline": res["roofline"],
         "cpu_baseline": cpu,
     }
+    # the same stack at the longer contexts (its own bytes: the caches read grow)
+    for ctx in extra_ctx:
+        h, _, tr = setup(a, wl, shape, ns, [ctx], False)
+        r = time_rounds(a, wl, shape, ns, [ctx], h, tr, kern, False)
+        out[f"ctx{ctx}"] = {"value": r["value"], "ms_per_step": r["ms_per_step"], "per_n": r["per_n"],
+                            "ratio_16_over_8": r["ratio_16_over_8"],
+                            "gateup_us": r["roofline"]["avg_us"], "gateup_frac": r["roofline"]["frac"]}
+    if a.config == "c2" and not a.no_extras:
+        # one layer + the head (the c1 workload): where the head's 1.56 GB dominates
+        wl.tv.close()
+        del wl
+        gc.collect()
+        torch.cuda.empty_cache()
+        wl1 = build_workload(a, synth.C1, a.ctx + 64, 1, False)
+        h, _, tr = setup(a, wl1, synth.C1, NS, [a.ctx], False)
+        r = time_rounds(a, wl1, synth.C1, NS, [a.ctx], h, tr, "gemm_head", False)
+        out["c1_layer"] = {"workload": describe("c1", synth.C1, [a.ctx], NS, a), "value": r["value"],
+                           "ms_per_step": r["ms_per_step"], "per_n": r["per_n"],
+                           "ratio_16_over_8": r["ratio_16_over_8"], "roofline": r["roofline"]}
+        wl1.tv.close()
     if kernels:
         out["kernels"] = kernels
     print(json.dumps(out), flush=True)
