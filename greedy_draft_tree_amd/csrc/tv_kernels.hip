@@ -1457,34 +1457,53 @@ __device__ __forceinline__ float log_sigmoid(float a) {
     return a >= 0.f ? -log1pf(expf(-a)) : a - log1pf(expf(a));
 }
 
-// Split-K sums of U elements at once: every split's load of the U elements
-// is issued before any add (4 splits per round), and each element's adds stay
-// in k-range order, as in psum.
-template <int U>
-__device__ __forceinline__ void psum_batch(const float *__restrict__ P, int S, const int (&m)[U],
-                                           const int (&col)[U], const bool (&ok)[U], float (&out)[U]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) out[u] = 0.f;
-    for (int k0 = 0; k0 < S; k0 += 4) {
-        float l[U][4];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float *p = P + ((size_t)(col[u] >> 7) * S + k0) * 4096 + (size_t)m[u] * 128 + (col[u] & 127);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) l[u][j] = (ok[u] && k0 + j < S) ? p[(size_t)j * 4096] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (k0 + j < S) out[u] += l[u][j];
-        }
-    }
+// Sum over groups of W consecutive lanes (W = 8 or 16, inside one 16-lane
+// DPP row), every lane of a group getting the same total: adds with lanes
+// xor 1 and xor 2 (quad permutes), then the mirror inside each half-row and
+// inside the row.  A fixed tree: the result depends only on the values.
+template <int W>
+__device__ __forceinline__ float row_sum(float x) {
+    static_assert(W == 8 || W == 16, "one or two half rows");
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)); // row_half_mirror
+    if constexpr (W == 16)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // row_mirror
+    return x;
 }
 
 // Eight consecutive fp32 values as bf16 (exact when they are bf16 values).
 __device__ __forceinline__ uint4 pack_bf8(const float *x) {
     return uint4{f2bf2(x[0], x[1]), f2bf2(x[2], x[3]), f2bf2(x[4], x[5]), f2bf2(x[6], x[7])};
+}
+
+// Forward substitution for value column c, held in registers, of the delta
+// rule's unit lower-triangular system (n <= NN nodes; ancestors have lower
+// indices, so node order is a topological order): once u_s is final it is
+// taken out of every later node's right-hand side, so node t's sum runs over
+// s = 0, 1, ..., t - 1 in order.  u[t] for t >= n is never stored.
+template <int NN, int VW>
+__device__ __forceinline__ void delta_solve(float (*vsm)[VW], const float (*akt)[kMaxRows + 4], int n, int c) {
+    float u[NN];
+#pragma unroll
+    for (int t = 0; t < NN; ++t) u[t] = t < n ? vsm[t][c] : 0.f;
+#pragma unroll
+    for (int s = 0; s < NN - 1; ++s) {
+        if (s + 1 >= n) break;
+        const float us = u[s];
+#pragma unroll
+        for (int q = (s + 1) / 4; q < NN / 4; ++q) {
+            if (4 * q >= n) break;
+            const float4 a = *reinterpret_cast<const float4 *>(&akt[s][4 * q]);
+            const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * q + e > s) u[4 * q + e] -= av[e] * us;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NN; ++t)
+        if (t < n) vsm[t][c] = u[t];
 }
 
 template <int D, bool DELTA>
@@ -1499,21 +1518,20 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     // (|S0 - hi - lo| <= 2^-17 |S0|).
     constexpr int VS = kRecurSlices;
     constexpr int VW = D / VS;             // value columns per workgroup (<= 32)
-    constexpr int DP = D + 1;              // padded fp32 row stride
     constexpr int BP = D + 8;              // padded bf16 row stride (16-byte rows, spread banks)
     constexpr int KB = D / 16;             // MFMA k blocks
     static_assert(VW <= 32 && D % 16 == 0, "slice shape");
-    __shared__ float qs[kMaxRows][DP], ks[kMaxRows][DP];            // raw projections
     __shared__ __attribute__((aligned(16))) uint16_t qb[kMaxRows][BP], kb[kMaxRows][BP];   // normalised, bf16
     __shared__ __attribute__((aligned(16))) uint16_t s0h[VW][BP], s0l[VW][BP];  // S0 slice, transposed, hi/lo
     __shared__ float vsm[kMaxRows][VW];    // v, then (delta) the right-hand side and u
     __shared__ float accq[kMaxRows][VW + 1], acck[DELTA ? kMaxRows : 1][VW + 1];   // S0^T q_t, S0^T k_t
-    __shared__ float gsh[kMaxRows], gcs[kMaxRows], scale[2][kMaxRows];
+    __shared__ float gsh[kMaxRows], gcs[kMaxRows];
     __shared__ uint32_t ancs[kMaxRows];    // ancestor-or-self bits of each node
     __shared__ float coef[kMaxRows][kMaxRows + 1];
-    // delta rule: write strengths and b_t e^{gc_t - gc_s} (k_t . k_s) for strict ancestors s
+    // delta rule: write strengths, and akt[s][t] = b_t e^{gc_t - gc_s} (k_t . k_s)
+    // for strict ancestors s of t (zero otherwise; rows padded to 36 floats)
     __shared__ float bsh[DELTA ? kMaxRows : 1];
-    __shared__ __attribute__((aligned(16))) float akk[DELTA ? kMaxRows : 1][kMaxRows];
+    __shared__ __attribute__((aligned(16))) float akt[DELTA ? kMaxRows : 1][kMaxRows + 4];
     const int h = blockIdx.x, v0 = blockIdx.y * VW, tid = threadIdx.x, n = r.n, QH = r.QH;
     const int lane = tid & 63, wave = tid >> 6, hf = lane >> 5, l32 = lane & 31;
 
@@ -1531,69 +1549,106 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
                              : float4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    // projection outputs: split-K partials summed in k-range order, rounded
-    // to bf16 (the projection's output rounding).  Each batch sums 8 q and 8
-    // k elements per thread; the first also this slice's v columns (up to 4
-    // per thread) and the node's gate (and write strength), so one round of
-    // loads covers up to 16 nodes
-    constexpr int UQ = 8, UV = kMaxRows * VW / 256, UB = 2 * UQ + UV + 2;
-    static_assert(UV * 256 == kMaxRows * VW, "v elements per thread");
+    // Projection outputs: split-K partials summed in k-range order (or, for
+    // a prefill block, bf16 rows), rounded to bf16 (the projection's output
+    // rounding).  Each thread takes eight consecutive columns of q and of k
+    // for rows qr0, qr0 + RPP, ... (TPR threads a row), four of this slice's
+    // v columns for row vr, and a node's gate (and write strength): every
+    // load of every split (four splits a round) is in flight before the
+    // first add.
+    constexpr int TPR = D / 8;             // threads per q or k row (16 or 8: one DPP row)
+    constexpr int RPP = 256 / TPR;         // rows per pass
+    constexpr int NP = kMaxRows / RPP;     // passes cover every row slot (rows >= n are zero)
+    constexpr int VT = VW / 4;             // threads per v row
+    static_assert(NP * RPP == kMaxRows && (256 / VT) >= kMaxRows, "load mapping");
     const bool rows_in = r.qkv_rows != nullptr;   // a prefill block: bf16 rows, a chain
     if (tid < n) ancs[tid] = rows_in ? (tid >= 31 ? 0xffffffffu : ((2u << tid) - 1u)) : r.meta->anc[r.row0 + tid];
-    for (int base = 0; base < n * D; base += UQ * 256) {
-        int mm[UB], cc[UB];
-        bool ok[UB];
-        float o[UB];
+    const int qr0 = tid / TPR, qc = (tid % TPR) * 8;
+    const int vr = tid / VT, vc = (tid % VT) * 4;
+    const bool vok = vr < n, gok = tid < n;
+    float qx[NP][8], kx[NP][8], ga = 0.f, gb = 0.f;
+    float4 vx = {0.f, 0.f, 0.f, 0.f};
+    if (rows_in) {
+        auto row4 = [&](bool ok, int m, int col) -> uint2 {   // four bf16 values of row m
+            return ok ? *reinterpret_cast<const uint2 *>(r.qkv_rows + (size_t)m * r.a_col + col) : uint2{0u, 0u};
+        };
 #pragma unroll
-        for (int u = 0; u < UQ; ++u) {
-            const int idx = base + u * 256 + tid;
-            ok[u] = ok[UQ + u] = idx < n * D;
-            mm[u] = mm[UQ + u] = r.row0 + (idx < n * D ? idx / D : 0);
-            cc[u] = h * D + idx % D;
-            cc[UQ + u] = (QH + h) * D + idx % D;
-        }
+        for (int i = 0; i < NP; ++i) {
+            const int m = qr0 + i * RPP;
 #pragma unroll
-        for (int u = 0; u < UV; ++u) {
-            const int idx = u * 256 + tid;
-            ok[2 * UQ + u] = base == 0 && idx < n * VW;
-            mm[2 * UQ + u] = r.row0 + (idx < n * VW ? idx / VW : 0);
-            cc[2 * UQ + u] = (2 * QH + h) * D + v0 + idx % VW;
-        }
-        ok[UB - 2] = base == 0 && tid < n;
-        ok[UB - 1] = DELTA && base == 0 && tid < n;
-        mm[UB - 2] = mm[UB - 1] = r.row0 + (tid < n ? tid : 0);
-        cc[UB - 2] = r.a_col + h;
-        cc[UB - 1] = r.a_col + QH + h;
-        if (rows_in) {
-#pragma unroll
-            for (int u = 0; u < UB; ++u) {
-                const uint16_t *src = cc[u] < r.a_col ? r.qkv_rows + (size_t)mm[u] * r.a_col + cc[u]
-                                                      : r.ab_rows + (size_t)mm[u] * r.ab_ld + (cc[u] - r.a_col);
-                o[u] = ok[u] ? bf2f(*src) : 0.f;
-            }
-        } else {
-            psum_batch<UB>(r.qkv_part, r.qkv_S, mm, cc, ok, o);
-        }
-#pragma unroll
-        for (int u = 0; u < UQ; ++u) {
-            const int idx = base + u * 256 + tid;
-            if (idx < n * D) {
-                qs[idx / D][idx % D] = bfround(o[u]);
-                ks[idx / D][idx % D] = bfround(o[UQ + u]);
+            for (int hh = 0; hh < 2; ++hh) {
+                const uint2 wq = row4(m < n, r.row0 + m, h * D + qc + 4 * hh);
+                const uint2 wk = row4(m < n, r.row0 + m, (QH + h) * D + qc + 4 * hh);
+                qx[i][4 * hh + 0] = __uint_as_float(wq.x << 16); qx[i][4 * hh + 1] = __uint_as_float(wq.x & 0xffff0000u);
+                qx[i][4 * hh + 2] = __uint_as_float(wq.y << 16); qx[i][4 * hh + 3] = __uint_as_float(wq.y & 0xffff0000u);
+                kx[i][4 * hh + 0] = __uint_as_float(wk.x << 16); kx[i][4 * hh + 1] = __uint_as_float(wk.x & 0xffff0000u);
+                kx[i][4 * hh + 2] = __uint_as_float(wk.y << 16); kx[i][4 * hh + 3] = __uint_as_float(wk.y & 0xffff0000u);
             }
         }
-        if (base == 0) {
+        const uint2 wv = row4(vok, r.row0 + vr, (2 * QH + h) * D + v0 + vc);
+        vx = float4{__uint_as_float(wv.x << 16), __uint_as_float(wv.x & 0xffff0000u),
+                    __uint_as_float(wv.y << 16), __uint_as_float(wv.y & 0xffff0000u)};
+        if (gok) {
+            ga = bf2f(r.ab_rows[(size_t)(r.row0 + tid) * r.ab_ld + h]);
+            if (DELTA) gb = bf2f(r.ab_rows[(size_t)(r.row0 + tid) * r.ab_ld + QH + h]);
+        }
+    } else {
+        const float *P = r.qkv_part;
+        const int S = r.qkv_S;
+        auto pp = [&](int m, int col, int sp) {   // partial of split sp, row m, column col
+            return P + ((size_t)(col >> 7) * S + sp) * 4096 + (size_t)m * 128 + (col & 127);
+        };
 #pragma unroll
-            for (int u = 0; u < UV; ++u) {
-                const int idx = u * 256 + tid;
-                if (idx < n * VW) vsm[idx / VW][idx % VW] = bfround(o[2 * UQ + u]);
+        for (int i = 0; i < NP; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qx[i][e] = kx[i][e] = 0.f;
+        for (int k0 = 0; k0 < S; k0 += 4) {
+            float4 lq[NP][4][2], lk[NP][4][2], lv[4];
+            float4 lga, lgb;   // gate (and write-strength) partials of four splits
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool sj = k0 + j < S;
+#pragma unroll
+                for (int i = 0; i < NP; ++i) {
+                    const int m = qr0 + i * RPP;
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        lq[i][j][hh] = lk[i][j][hh] = float4{0.f, 0.f, 0.f, 0.f};
+                        if (sj && m < n) {
+                            lq[i][j][hh] = *reinterpret_cast<const float4 *>(pp(r.row0 + m, h * D + qc + 4 * hh, k0 + j));
+                            lk[i][j][hh] = *reinterpret_cast<const float4 *>(pp(r.row0 + m, (QH + h) * D + qc + 4 * hh, k0 + j));
+                        }
+                    }
+                }
+                lv[j] = float4{0.f, 0.f, 0.f, 0.f};
+                if (sj && vok) lv[j] = *reinterpret_cast<const float4 *>(pp(r.row0 + vr, (2 * QH + h) * D + v0 + vc, k0 + j));
+                const float g1 = (sj && gok) ? *pp(r.row0 + tid, r.a_col + h, k0 + j) : 0.f;
+                const float g2 = (DELTA && sj && gok) ? *pp(r.row0 + tid, r.a_col + QH + h, k0 + j) : 0.f;
+                if (j == 0) { lga.x = g1; lgb.x = g2; }
+                else if (j == 1) { lga.y = g1; lgb.y = g2; }
+                else if (j == 2) { lga.z = g1; lgb.z = g2; }
+                else { lga.w = g1; lgb.w = g2; }
             }
-            if (tid < n) {
-                gsh[tid] = log_sigmoid(bfround(o[UB - 2]));
-                if constexpr (DELTA) bsh[tid] = 1.0f / (1.0f + expf(-bfround(o[UB - 1])));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (k0 + j < S) {
+#pragma unroll
+                    for (int i = 0; i < NP; ++i)
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            qx[i][4 * hh + 0] += lq[i][j][hh].x; qx[i][4 * hh + 1] += lq[i][j][hh].y;
+                            qx[i][4 * hh + 2] += lq[i][j][hh].z; qx[i][4 * hh + 3] += lq[i][j][hh].w;
+                            kx[i][4 * hh + 0] += lk[i][j][hh].x; kx[i][4 * hh + 1] += lk[i][j][hh].y;
+                            kx[i][4 * hh + 2] += lk[i][j][hh].z; kx[i][4 * hh + 3] += lk[i][j][hh].w;
+                        }
+                    vx.x += lv[j].x; vx.y += lv[j].y; vx.z += lv[j].z; vx.w += lv[j].w;
+                    ga += j == 0 ? lga.x : j == 1 ? lga.y : j == 2 ? lga.z : lga.w;
+                    gb += j == 0 ? lgb.x : j == 1 ? lgb.y : j == 2 ? lgb.z : lgb.w;
+                }
             }
         }
     }
+    // the state slice, transposed into bf16 hi + lo parts
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int idx = tid + i * 256;
@@ -1608,47 +1663,54 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
             }
         }
     }
-    __syncthreads();
-    // L2 norms of q and k rows: 8 lanes per vector (lane p takes elements
-    // p, p + 8, ...), then a fixed xor-shuffle tree over the 8
-    for (int base = 0; base < 2 * n * 8; base += 256) {
-        const int vec = (base + tid) >> 3, p = tid & 7;
-        float ss = 0.f;
-        if (vec < 2 * n) {
-            const float *x = (vec & 1) ? ks[vec >> 1] : qs[vec >> 1];
+    // q and k: round the sums, then each row's sum of squares over its TPR
+    // lanes (consecutive lanes of one DPP row; a fixed tree of DPP
+    // exchanges), then the normalised row rounded to bf16 (rows >= n are
+    // zero: the matrix-core padding); the first slice also saves the keys
 #pragma unroll
-            for (int d = p; d < D; d += 8) ss += x[d] * x[d];
+    for (int i = 0; i < NP; ++i) {
+        const int m = qr0 + i * RPP;
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            qx[i][e] = bfround(qx[i][e]);
+            kx[i][e] = bfround(kx[i][e]);
+            sq += qx[i][e] * qx[i][e];
+            sk += kx[i][e] * kx[i][e];
         }
+        sq = row_sum<TPR>(sq);
+        sk = row_sum<TPR>(sk);
+        const float fq = 1.0f / sqrtf(sq + r.eps), fk = 1.0f / sqrtf(sk + r.eps);
+        float nq[8], nk[8];
 #pragma unroll
-        for (int o = 4; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-        if (p == 0 && vec < 2 * n) scale[vec & 1][vec >> 1] = 1.0f / sqrtf(ss + r.eps);
+        for (int e = 0; e < 8; ++e) {
+            nq[e] = qx[i][e] * fq;
+            nk[e] = kx[i][e] * fk;
+        }
+        const uint4 wq = pack_bf8(nq), wk = pack_bf8(nk);
+        *reinterpret_cast<uint4 *>(&qb[m][qc]) = m < n ? wq : uint4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<uint4 *>(&kb[m][qc]) = m < n ? wk : uint4{0u, 0u, 0u, 0u};
+        if (blockIdx.y == 0 && m < n) *reinterpret_cast<uint4 *>(r.save_k + ((size_t)m * QH + h) * D + qc) = wk;
     }
+    if (vok) {
+        vsm[vr][vc] = bfround(vx.x);
+        vsm[vr][vc + 1] = bfround(vx.y);
+        vsm[vr][vc + 2] = bfround(vx.z);
+        vsm[vr][vc + 3] = bfround(vx.w);
+    }
+    if (gok) {
+        gsh[tid] = log_sigmoid(bfround(ga));
+        if constexpr (DELTA) bsh[tid] = 1.0f / (1.0f + expf(-bfround(gb)));
+    }
+    __syncthreads();
     if (tid < n) {
         // cumulative gate over the ancestors, root first (ancestors have lower indices)
         const uint32_t anc = ancs[tid];
         float gc = 0.f;
 #pragma unroll
-        for (int s = 0; s < kMaxRows; ++s)
-            if (s <= tid && ((anc >> s) & 1u)) gc += gsh[s];
+        for (int s2 = 0; s2 < kMaxRows; ++s2)
+            if (s2 <= tid && ((anc >> s2) & 1u)) gc += gsh[s2];
         gcs[tid] = gc;
-    }
-    __syncthreads();
-    // normalised q and k, rounded to bf16; rows beyond n are zero (MFMA padding)
-    for (int idx = tid; idx < kMaxRows * (D / 8); idx += 256) {
-        const int t = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
-        uint4 wq = {0u, 0u, 0u, 0u}, wk = {0u, 0u, 0u, 0u};
-        if (t < n) {
-            float xq[8], xk[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                xq[e] = qs[t][d0 + e] * scale[0][t];
-                xk[e] = ks[t][d0 + e] * scale[1][t];
-            }
-            wq = pack_bf8(xq);
-            wk = pack_bf8(xk);
-        }
-        *reinterpret_cast<uint4 *>(&qb[t][d0]) = wq;
-        *reinterpret_cast<uint4 *>(&kb[t][d0]) = wk;
     }
     __syncthreads();
     // the small products, one wave each: lane (hf, j = lane % 32) supplies k
@@ -1657,7 +1719,7 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     const uint4 z = {0u, 0u, 0u, 0u};
     if (wave == 0 || (DELTA && wave == 1)) {
         // coef (wave 0): e^{gc_t - gc_s} (q_t . k_s) over ancestors-or-self s;
-        // akk (wave 1): b_t e^{gc_t - gc_s} (k_t . k_s) over strict ancestors
+        // akt (wave 1, transposed): b_t e^{gc_t - gc_s} (k_t . k_s) over strict ancestors
         const uint16_t(*A)[BP] = wave == 0 ? qb : kb;
         f32x16 acc = {};
 #pragma unroll
@@ -1677,7 +1739,7 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
                 if (wave == 0) {
                     coef[t][s] = anc ? decay * acc[rr] : 0.f;
                 } else if constexpr (DELTA) {
-                    akk[t][s] = (anc && s != t) ? bsh[t] * decay * acc[rr] : 0.f;
+                    akt[s][t] = (anc && s != t) ? bsh[t] * decay * acc[rr] : 0.f;
                 }
             }
         }
@@ -1713,25 +1775,10 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
             vsm[t][c] = bsh[t] * (vsm[t][c] - expf(gcs[t]) * acck[t][c]);
         }
         __syncthreads();
-        // forward substitution, one lane per value column, u in registers
-        // (ancestors have lower indices, so u_s is final when node t needs it)
+        // forward substitution, one thread a value column (the column in registers)
         if (tid < VW) {
-            float u[kMaxRows];
-#pragma unroll
-            for (int t = 0; t < kMaxRows; ++t) {
-                if (t >= n) break;
-                float x = vsm[t][tid];
-#pragma unroll
-                for (int s4 = 0; s4 < t; s4 += 4) {
-                    const float4 a4 = *reinterpret_cast<const float4 *>(&akk[t][s4]);
-                    x -= a4.x * u[s4];
-                    if (s4 + 1 < t) x -= a4.y * u[s4 + 1];
-                    if (s4 + 2 < t) x -= a4.z * u[s4 + 2];
-                    if (s4 + 3 < t) x -= a4.w * u[s4 + 3];
-                }
-                u[t] = x;
-                vsm[t][tid] = x;
-            }
+            if (n <= 16) delta_solve<16, VW>(vsm, akt, n, tid);
+            else delta_solve<kMaxRows, VW>(vsm, akt, n, tid);
         }
         __syncthreads();
     }
@@ -1744,13 +1791,7 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
         r.out[(size_t)(r.row0 + t) * QH * D + h * D + v0 + c] = f2bf(o);
         r.save_v[((size_t)t * QH + h) * D + v0 + c] = vsm[t][c];
     }
-    if (blockIdx.y == 0) {
-        for (int idx = tid; idx < n * D; idx += 256) {
-            const int t = idx / D, d = idx % D;
-            r.save_k[((size_t)t * QH + h) * D + d] = kb[t][d];
-        }
-        if (tid < n) r.save_gc[(size_t)tid * QH + h] = gcs[tid];
-    }
+    if (blockIdx.y == 0 && tid < n) r.save_gc[(size_t)tid * QH + h] = gcs[tid];
 }
 
 // State commit: the state after the accepted path from the quantities the
