@@ -300,6 +300,14 @@ __global__ __launch_bounds__(kRowThreads) void k_row_norm(const uint16_t *__rest
     *reinterpret_cast<uint4 *>(Y + (size_t)m * H + n0) = uint4{yw[0], yw[1], yw[2], yw[3]};
 }
 
+// XOR swizzle of the 16-byte chunks of a staged activation row (128 bytes
+// of k): row r keeps chunk x in slot x ^ bswz(r).  A B-operand read takes
+// chunk ch of rows c = lane % 32; the LDS serves a 16-byte read for 16
+// lanes at a time over its 64 banks, and with bswz(c) = (c / 2) % 8 those
+// 16 lanes (8 even rows on one half of the banks, 8 odd rows on the other)
+// hit 16 distinct groups of 4 banks.
+__device__ __forceinline__ int bswz(int row) { return (row >> 1) & 7; }
+
 // ------------------------------------------------------------ skinny GEMM
 // Y[m, n] = sum_k X[m, k] W[n, k] for M <= 32 activation rows.
 //
@@ -387,12 +395,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 
     // Activation staging with direct global->LDS loads: thread t fills bytes
     // [16t, 16t+16) of a step's 4 KB block, i.e. row br = t/8, slot sw = t%8,
-    // with the row's 16-byte chunk sw ^ (br & 7) (the XOR swizzle that makes
+    // with the row's 16-byte chunk sw ^ bswz(br) (the XOR swizzle that makes
     // the B-operand reads conflict-free); rows beyond M and k beyond K read a
     // zero block.  The next group's loads are issued first in each group (the
     // buffer they fill was released by the previous group's barrier), ahead
     // of the weight loads, and waited for at the group's barrier.
-    const int br = tid >> 3, bsw = (tid & 7) ^ (br & 7);
+    const int br = tid >> 3, bsw = (tid & 7) ^ bswz(br);
     const uint16_t *xrow = g.X + (size_t)(br < g.M ? br : 0) * g.ldx;
     typedef __attribute__((address_space(3))) uint8_t lds_byte;
     auto bissue = [&](int buf, int sf) {
@@ -434,7 +442,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int ch = 4 * hf + q;
-                const uint4 b = *reinterpret_cast<const uint4 *>(&Bs[buf][u][c * 64 + ((ch ^ (c & 7)) << 3)]);
+                const uint4 b = *reinterpret_cast<const uint4 *>(&Bs[buf][u][c * 64 + ((ch ^ bswz(c)) << 3)]);
                 acc = mfma32(a[u][q], b, acc);
                 if constexpr (DUAL) acc2 = mfma32(a2[u][q], b, acc2);
             }
@@ -546,7 +554,7 @@ __global__ __launch_bounds__(256) void k_gemm_dense(GemmArgs g) {
     const uint16_t *tb2 = DUAL ? g.W2 + (size_t)(tok ? tile : 0) * 32 * K : nullptr;
     const uint4 z = {0u, 0u, 0u, 0u};
 
-    const int br = tid >> 3, bsw = (tid & 7) ^ (br & 7);
+    const int br = tid >> 3, bsw = (tid & 7) ^ bswz(br);
     typedef __attribute__((address_space(3))) uint8_t lds_byte;
     auto bissue = [&](int buf, int sf) {
 #pragma unroll
@@ -598,7 +606,7 @@ __global__ __launch_bounds__(256) void k_gemm_dense(GemmArgs g) {
                 const int ch = 4 * hf + q;
 #pragma unroll
                 for (int gi = 0; gi < MG; ++gi) {
-                    const uint4 b = *reinterpret_cast<const uint4 *>(&Bs[buf][u][gi][c * 64 + ((ch ^ (c & 7)) << 3)]);
+                    const uint4 b = *reinterpret_cast<const uint4 *>(&Bs[buf][u][gi][c * 64 + ((ch ^ bswz(c)) << 3)]);
                     acc[gi] = mfma32(a[u][q], b, acc[gi]);
                     if constexpr (DUAL) acc2[gi] = mfma32(a2[u][q], b, acc2[gi]);
                 }
