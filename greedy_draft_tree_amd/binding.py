@@ -23,7 +23,8 @@ SYMBOLS = ("tv_create", "tv_destroy", "tv_last_error", "tv_bind", "tv_set_histor
            "tv_accept_walk", "tv_commit", "tv_round", "tv_ctx_len", "tv_profile_enable",
            "tv_profile_reset", "tv_profile_get", "tv_linear", "tv_head_top2", "tv_pack_weight",
            "tv_staircut", "tv_residual_round", "tv_lookup_draft", "tv_attention", "tv_rope_kv",
-           "tv_resid_norm", "tv_recur_tree", "tv_recur_commit", "tv_gather_kv", "tv_linear_noalloc")
+           "tv_resid_norm", "tv_recur_tree", "tv_recur_commit", "tv_gather_kv", "tv_linear_noalloc",
+           "tv_prices_create", "tv_prices_destroy", "tv_prices_class", "tv_prices_table", "tv_prices_observe")
 
 
 class TVError(RuntimeError):
@@ -85,6 +86,11 @@ def load_library():
         "tv_recur_commit": ([P, P, P, P, P, P, I], I),
         "tv_gather_kv": ([P, P, P, I, I, P, I], I),
         "tv_linear_noalloc": ([P, P, I, I, I, P, I, P], I),
+        "tv_prices_create": ([P, P, P, P, I, I, ctypes.c_double, ctypes.c_double, ctypes.POINTER(P)], I),
+        "tv_prices_destroy": ([P], None),
+        "tv_prices_class": ([P, I, P, P], I),
+        "tv_prices_table": ([P, I, I, P], I),
+        "tv_prices_observe": ([P, I, I, I, ctypes.c_double], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

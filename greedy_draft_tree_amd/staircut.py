@@ -2,8 +2,9 @@
 
 * ``cut``: the native cut (``tv_staircut``) of a candidate tree to the node
   count that maximises expected committed tokens per millisecond.
-* ``PriceModel``: verify prices by context class, kind (chain or tree) and row
-  count, in the pages' price-file format
+* ``PriceModel``: the library's verify prices (``tv_prices_*``) by context
+  class, kind (chain or tree) and row count, from a price file in the pages'
+  format
   ``{"<context class>": {"<kind>": {"<rows>": ms, ...}, ...}, ..., "step_ms": x, "measured": "..."}``,
   and the rules the pages give for reading it ("Drafters and tree verify",
   StairCut on Flash-Next, and the shared price files): an unlisted context
@@ -56,18 +57,43 @@ def cut(parents: Sequence[int], q: Sequence[float], order: Sequence[int], price_
 
 
 class PriceModel:
-    """Verify prices in ms by (context class, kind, rows); see the module doc."""
+    """Verify prices in ms by (context class, kind, rows): the library's
+    price model (``tv_prices_*``) built from a price file in the format of
+    the module doc; this class only marshals."""
 
     def __init__(self, table: Optional[dict] = None, ema: float = 0.1):
         self.table = table or {}
         self.ema = ema
-        self.step_ms = self.table.get("step_ms")
-        self.file: Dict[int, Dict[str, Dict[int, float]]] = {}
+        step = self.table.get("step_ms")
+        cls, kind, rows, ms = [], [], [], []
         for key, kinds in self.table.items():
             if not str(key).lstrip("-").isdigit() or not isinstance(kinds, dict):
                 continue
-            self.file[int(key)] = {k: {int(r): float(ms) for r, ms in v.items()} for k, v in kinds.items()}
-        self.live: Dict[Tuple[int, str], Dict[int, float]] = {}
+            for k, v in kinds.items():
+                if k not in KINDS:
+                    continue
+                for r, p in v.items():
+                    cls.append(int(key))
+                    kind.append(KINDS.index(k))
+                    rows.append(int(r))
+                    ms.append(float(p))
+        self._lib = load_library()
+        c, kd, rw = _i32(cls), _i32(kind), _i32(rows)
+        m = np.ascontiguousarray(np.asarray(ms, dtype=np.float64))
+        h = ctypes.c_void_p()
+        rc = self._lib.tv_prices_create(_ptr(c) if len(cls) else None, _ptr(kd) if len(cls) else None,
+                                        _ptr(rw) if len(cls) else None, _ptr(m) if len(cls) else None, len(cls),
+                                        int(step is not None), float(step) if step is not None else 0.0,
+                                        float(ema), ctypes.byref(h))
+        if rc != 0:
+            raise TVError(rc, "tv_prices_create: invalid price file or weight")
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.tv_prices_destroy(h)
+            self._h = None
 
     @classmethod
     def load(cls, path: str, ema: float = 0.1) -> "PriceModel":
@@ -75,41 +101,19 @@ class PriceModel:
             return cls(json.load(f), ema)
 
     def class_of(self, ctx: int) -> Optional[int]:
-        if not self.file:
-            return None
-        lower = [c for c in self.file if c <= ctx]
-        return max(lower) if lower else min(self.file)
-
-    def _file_price(self, cls: Optional[int], kind: str, rows: int) -> float:
-        if cls is None or kind not in self.file[cls] or not self.file[cls][kind]:
-            return 1.0
-        pts = sorted(self.file[cls][kind].items())
-        rs = [r for r, _ in pts]
-        ps = [p for _, p in pts]
-        if rows <= rs[0]:
-            return ps[0]
-        if rows <= rs[-1]:
-            return float(np.interp(rows, rs, ps))
-        if self.step_ms is not None:
-            step = float(self.step_ms)
-        elif len(rs) >= 2:
-            step = (ps[-1] - ps[-2]) / (rs[-1] - rs[-2])
-        else:
-            step = 0.0
-        return ps[-1] + step * (rows - rs[-1])
+        c, has = ctypes.c_int32(0), ctypes.c_int(0)
+        rc = self._lib.tv_prices_class(self._h, int(ctx), ctypes.byref(c), ctypes.byref(has))
+        if rc != 0:
+            raise TVError(rc, "tv_prices_class")
+        return int(c.value) if has.value else None
 
     def prices(self, ctx: int, kind: str) -> np.ndarray:
         """Prices for rows 0..32 (index 0 unused), non-decreasing in rows."""
-        cls = self.class_of(ctx)
-        live = self.live.get((cls, kind), {})
-        base = np.array([self._file_price(cls, kind, r) for r in range(TV_MAX_NODES + 1)])
-        offs = [ms - base[r] for r, ms in live.items()]
-        shift = float(np.mean(offs)) if offs else 0.0
-        out = base + shift
-        for r, ms in live.items():
-            out[r] = ms
-        out[0] = out[1]
-        return np.maximum.accumulate(out)
+        out = np.zeros(TV_MAX_NODES + 1, np.float64)
+        rc = self._lib.tv_prices_table(self._h, int(ctx), KINDS.index(kind), _ptr(out))
+        if rc != 0:
+            raise TVError(rc, "tv_prices_table")
+        return out
 
     def price(self, ctx: int, kind: str, rows: int) -> float:
         return float(self.prices(ctx, kind)[rows])
@@ -117,10 +121,9 @@ class PriceModel:
     def observe(self, ctx: int, kind: str, rows: int, ms: float) -> None:
         """Follow a live price: an EMA of the counts seen (started at the
         model's current price for that count)."""
-        cls = self.class_of(ctx)
-        live = self.live.setdefault((cls, kind), {})
-        cur = live.get(rows, self.price(ctx, kind, rows))
-        live[rows] = cur + self.ema * (ms - cur)
+        rc = self._lib.tv_prices_observe(self._h, int(ctx), KINDS.index(kind), int(rows), float(ms))
+        if rc != 0:
+            raise TVError(rc, "tv_prices_observe: bad kind, count or time")
 
 
 def _tree_shape(rows: int, kind: str) -> List[int]:

@@ -258,6 +258,42 @@ int tv_staircut(const int32_t *parents, const float *q, const int32_t *order, in
                 const float *price_tree_ms, const float *price_chain_ms, float draft_ms, float commit_ms,
                 int32_t *keep, int *n_keep, float *score);
 
+/* StairCut's verify prices by row count ("Drafters and tree verify",
+ * StairCut on Flash-Next, and the shared price files), host only: a model
+ * built from a price file's points and updated online with measured round
+ * times, whose table feeds tv_staircut's price arguments.
+ *   tv_prices_create: n_points points (ctx_class[i], kind[i], rows[i],
+ *     ms[i]) of a price file, kind TV_PRICE_CHAIN or TV_PRICE_TREE, rows
+ *     >= 1, each (class, kind, rows) at most once (n_points may be 0: no
+ *     file); has_step says whether the file gives step_ms; ema in (0, 1] is
+ *     the weight of a measured round.  *out receives the model (free it with
+ *     tv_prices_destroy).
+ *   tv_prices_class: the context class of ctx: the largest listed class
+ *     <= ctx, else the smallest listed one; *has_class = 0 when there is no
+ *     file.
+ *   tv_prices_table: out[0..TV_MAX_NODES] (host doubles) = the prices in ms
+ *     for the class of ctx and the kind: the file's price of each count (the
+ *     first listed price below the first listed count; linear between two
+ *     listed counts; past the last, step_ms a row, else the last two counts'
+ *     slope, else flat; 1 ms for every count with no file or no entry for
+ *     the kind), shifted by the mean offset of the measured counts from the
+ *     file, each measured count at its live price, out[0] = out[1], then
+ *     made non-decreasing in rows.
+ *   tv_prices_observe: a measured round of `rows` rows (1..TV_MAX_NODES)
+ *     at ctx took ms: that count's live price (started at its current table
+ *     price) moves by ema * (ms - live).
+ * Errors: TV_EINVAL for a null pointer, a bad kind, count, weight or
+ * non-finite value, a count listed twice, or when memory runs out. */
+#define TV_PRICE_CHAIN 0
+#define TV_PRICE_TREE 1
+typedef struct tv_prices tv_prices;
+int tv_prices_create(const int32_t *ctx_class, const int32_t *kind, const int32_t *rows, const double *ms,
+                     int n_points, int has_step, double step_ms, double ema, tv_prices **out);
+void tv_prices_destroy(tv_prices *p);
+int tv_prices_class(const tv_prices *p, int ctx, int32_t *cls, int *has_class);
+int tv_prices_table(const tv_prices *p, int ctx, int kind, double *out);
+int tv_prices_observe(tv_prices *p, int ctx, int kind, int rows, double ms);
+
 /* The lookup drafter over the request's own text ("Drafters and tree
  * verify", The lookup drafter), host only: it copies text instead of
  * predicting it.  An occurrence of order o is a start p with

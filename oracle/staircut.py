@@ -71,3 +71,79 @@ def staircut(parents: Sequence[int], q: Sequence[float], order: Sequence[int],
         if best is None or score > best:
             best, best_k = score, k
     return sorted(prefixes[best_k]), best
+
+
+class Prices:
+    """Verify prices by row count, plainly ("Drafters and tree verify",
+    StairCut on Flash-Next, and the shared price files): a price file lists
+    prices by context class and kind (chain or tree); a context without its
+    own class takes the nearest lower one; counts between two listed ones
+    interpolate; past the last listed count the price grows step_ms a row,
+    or by the last two counts' slope; measured rounds update a count's price
+    online (an EMA of weight `ema` a count) and shift the counts not measured
+    by the learned offset; a price never falls with more rows; with no file
+    every count costs 1 ms.
+
+    Readings taken here: a context below every listed class takes the
+    smallest one; a count below the first listed one takes the first listed
+    price; the learned offset is the mean of (live price - file price) over
+    the measured counts of that class and kind; a count's live price starts
+    at its current price; the table is made non-decreasing by a running
+    maximum from one row upward, and row 0 copies row 1.
+
+    points: (context class, kind, rows, ms) tuples, kind "chain" or "tree".
+    """
+
+    ROWS = 32
+
+    def __init__(self, points, step_ms=None, ema=0.1):
+        self.curves = {}
+        for c, k, r, m in points:
+            self.curves.setdefault((c, k), {})[r] = m
+        self.classes = sorted({c for c, _, _, _ in points})
+        self.step_ms = step_ms
+        self.ema = ema
+        self.live = {}   # (class, kind) -> {rows: ms}, in the order first measured
+
+    def context_class(self, ctx):
+        if not self.classes:
+            return None
+        lower = [c for c in self.classes if c <= ctx]
+        return max(lower) if lower else self.classes[0]
+
+    def file_price(self, cls, kind, rows):
+        pts = sorted(self.curves.get((cls, kind), {}).items())
+        if cls is None or not pts:
+            return 1.0
+        if rows <= pts[0][0]:
+            return pts[0][1]
+        for (r0, p0), (r1, p1) in zip(pts, pts[1:]):
+            if r0 <= rows <= r1:
+                return p0 + (p1 - p0) * (rows - r0) / (r1 - r0)
+        r_last, p_last = pts[-1]
+        if self.step_ms is not None:
+            step = self.step_ms
+        elif len(pts) >= 2:
+            step = (p_last - pts[-2][1]) / (r_last - pts[-2][0])
+        else:
+            step = 0.0
+        return p_last + step * (rows - r_last)
+
+    def table(self, ctx, kind):
+        cls = self.context_class(ctx)
+        base = [self.file_price(cls, kind, r) for r in range(self.ROWS + 1)]
+        live = self.live.get((cls, kind), {})
+        shift = sum(ms - base[r] for r, ms in live.items()) / len(live) if live else 0.0
+        out = [b + shift for b in base]
+        for r, ms in live.items():
+            out[r] = ms
+        out[0] = out[1]
+        for r in range(1, self.ROWS + 1):
+            out[r] = max(out[r], out[r - 1])
+        return out
+
+    def observe(self, ctx, kind, rows, ms):
+        cls = self.context_class(ctx)
+        live = self.live.setdefault((cls, kind), {})
+        cur = live[rows] if rows in live else self.table(ctx, kind)[rows]
+        live[rows] = cur + self.ema * (ms - cur)
