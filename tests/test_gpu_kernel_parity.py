@@ -262,6 +262,30 @@ def test_resid_norm_identical_inputs(tvs, shape, n, splits):
                   f"resid_norm {shape.name} n={n}")
 
 
+def test_resid_norm_repeated_calls(tvs):
+    """Calls in a row on one context with different row counts: each row's
+    residual stream and normalised row have the same bits in every call
+    (no state carried from one call to the next, a fixed reduction order)."""
+    shape = FULL
+    H = shape.hidden
+    _say("resid_norm repeated", shape.name)
+    outs = []
+    for n in (32, 5, 32, 17, 32):
+        parts = synth.dyadic_partials(4, 32, H, 310, std=0.3)[:, :n]
+        x0 = synth.bf16_normal((32, H), 311, 1.0)[:n]
+        w = synth.bf16_normal((H,), 312, 1.0)
+        x = x0.cuda()
+        y = torch.empty_like(x)
+        tvs[shape.name].resid_norm(torch.from_numpy(synth.splitk_layout(np.ascontiguousarray(parts))).cuda(), 4,
+                                   x, w.cuda(), y)
+        torch.cuda.synchronize()
+        outs.append((bf16_bits(x.cpu()), bf16_bits(y.cpu())))
+    for i, (xb, yb) in enumerate(outs):
+        n = xb.shape[0]
+        assert np.array_equal(xb, outs[0][0][:n]), f"call {i}: residual stream differs"
+        assert np.array_equal(yb, outs[0][1][:n]), f"call {i}: normalised rows differ"
+
+
 # ------------------------------------------------------- recurrent layer
 
 def _condition_norms(parts, orc):
