@@ -1303,36 +1303,47 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
                     s[kb] = mfma32(ka, q[kk], s[kb]);
                 }
             }
-            // visible keys of the chunk as a bit mask: inside the range, and
-            // for the tree's own keys an ancestor-or-self of this row
-            uint64_t vis = cn >= 64 ? ~0ull : ((1ull << cn) - 1ull);
-            if (tree) vis &= (uint64_t)anc;   // the tree's keys are one chunk (c0 = 0)
-            if (!rowok) vis = 0ull;
-            // scores in base-2 units: softmax(x * scale) = 2^(x * scale * log2 e - max)
+            // scores in base-2 units: softmax(x * scale) = 2^(x * scale * log2 e - max).
+            // The maximum is taken over the raw scores and scaled once (a
+            // product by a positive constant, correctly rounded, keeps the
+            // order); a full chunk of cache keys needs no mask, otherwise
+            // keys outside the range, and for the tree's own keys those not
+            // an ancestor-or-self of this row, become -inf
             float mx = -INFINITY;
+            if (cn >= CH && !tree) {
 #pragma unroll
-            for (int kb = 0; kb < CH / 32; ++kb)
+                for (int kb = 0; kb < CH / 32; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int j = kb * 32 + acc_row(r, hf);   // key within the chunk
-                    const float v = ((vis >> j) & 1ull) ? s[kb][r] * scale2 : -INFINITY;
-                    s[kb][r] = v;
-                    mx = fmaxf(mx, v);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(mrun, mx);
-            float alpha;
-            if (mnew == -INFINITY) {
-                alpha = 1.f;
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
             } else {
-                alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mnew);
+                uint64_t vis = cn >= 64 ? ~0ull : ((1ull << cn) - 1ull);
+                if (tree) vis &= (uint64_t)anc;   // the tree's keys are one chunk (c0 = 0)
+                if (!rowok) vis = 0ull;
+#pragma unroll
+                for (int kb = 0; kb < CH / 32; ++kb) {
+                    const uint32_t vb = (uint32_t)(vis >> (32 * kb));
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float v = ((vb >> acc_row(r, hf)) & 1u) ? s[kb][r] : -INFINITY;
+                        s[kb][r] = v;
+                        mx = fmaxf(mx, v);
+                    }
+                }
             }
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale2;
+            const float mnew = fmaxf(mrun, mx);
+            // with no visible key yet every score here is -inf: subtract 0
+            const float msub = mnew == -INFINITY ? 0.f : mnew;
+            const float alpha = mrun == -INFINITY ? (mnew == -INFINITY ? 1.f : 0.f)
+                                                  : __builtin_amdgcn_exp2f(mrun - mnew);
+            // p = 2^(score * scale2 - max) with one rounding before the
+            // exponential; a masked score gives 2^-inf = 0
             float ls = 0.f;
 #pragma unroll
             for (int kb = 0; kb < CH / 32; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = (s[kb][r] == -INFINITY) ? 0.f : exp2f(s[kb][r] - mnew);
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale2, -msub));
                     s[kb][r] = p;
                     ls += p;
                 }
