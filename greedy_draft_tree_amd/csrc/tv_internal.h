@@ -9,6 +9,7 @@ namespace tv {
 constexpr int kMaxRows = 32;   // rows of one pass
 constexpr int kMaxGroup = 8;   // query heads per KV head
 constexpr int kAttnChunk = 64;  // keys staged in LDS at a time
+constexpr int kAttnLoadTasks = 3;  // staging tasks (64 bytes of K and of V) a loader thread holds per chunk
 constexpr int kAttnComputeWaves = 5;  // query rows G*n <= 160: one wave per 32
 constexpr int kAttnWaves = 8;         // waves of an attention workgroup that stages chunks: the register file
                                        // holds 2 waves a SIMD, and every wave beyond the compute waves loads

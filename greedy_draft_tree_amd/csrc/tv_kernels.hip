@@ -1140,6 +1140,14 @@ __global__ __launch_bounds__(1024) void k_norm_dense(const int32_t *__restrict__
 }
 
 // ---------------------------------------------------------- tree attention
+// Workgroup barrier that orders LDS only: global loads a wave has in flight
+// stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Grid (split, kv head); one wave per block of 32 query rows, where row
 // r = node*G + head-in-group.  Splits 0..n_ctx_split-1 each take `span`
 // cache keys (visible to every row); the last split takes the tree's own
@@ -1158,17 +1166,22 @@ __global__ __launch_bounds__(1024) void k_norm_dense(const int32_t *__restrict__
 // split spans several 64-key chunks, the workgroup's other waves (up to 8 in
 // all) stage the next chunk into the second LDS buffer while the compute
 // waves use the first.
+// With DS = 2 two waves share a block of 32 rows, each forming the scores
+// and probabilities of all the block's keys but only half of the output
+// dims (the products of P with V are the largest share of a chunk's work);
+// every output value takes the same operations in the same order either way.
 // Each workgroup writes its unnormalised partial (max in base-2 units, sum,
 // output); the combine kernel merges splits in index order.  Split
 // boundaries depend only on ctx, so a row's result does not depend on the
 // other rows.
 
-template <int D>
+template <int D, int DS>
 __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
     constexpr int CH = kAttnChunk;     // keys per LDS stage
     constexpr int KC = D / 8;          // 16-byte chunks per key row
     constexpr int VSTR = CH + 4;       // bf16 stride of a transposed V row
-    constexpr int NDB = D / 32;        // output dim blocks
+    constexpr int NDB = D / 32 / DS;   // output dim blocks of one wave
+    static_assert(DS == 1 || DS == 2, "one or two waves per block of rows");
     constexpr int NKK = D / 16;        // dim steps of the score MFMA
     // two LDS stages: while the compute waves use one, the loader waves fill
     // the other with the next chunk of keys
@@ -1203,13 +1216,15 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
         if (split > nsplit) return;            // a block with fewer splits: the whole workgroup leaves
     }
     const int R = G * n;
-    const int cw = (R + 31) >> 5;              // compute waves; any further waves only load
+    const int cw = ((R + 31) >> 5) * DS;       // compute waves; any further waves only load
+    const int rbi = wave / DS;                 // the wave's block of 32 rows
+    const int db0 = (wave % DS) * NDB;         // and its first output dim block
     const bool loaders = nthr > cw * 64;
     const bool tree = split >= nsplit;
     const int key0 = tree ? ctx : split * span;
     const int nkeys = tree ? n : min(span, ctx - key0);
     const int nch = (nkeys + CH - 1) / CH;
-    const int row = wave * 32 + c;             // this lane's query row (compute waves)
+    const int row = rbi * 32 + c;              // this lane's query row (compute waves)
     const bool rowok = wave < cw && row < R;
     const int t = rowok ? row / G : 0, hh = rowok ? row % G : 0;
     // keys of the block's own rows visible to row t: its ancestors and itself
@@ -1228,42 +1243,66 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
     constexpr int NPAIR = CH / 2;
     constexpr int NTASK = NPAIR * KC;
     constexpr int TB = 2;
-    auto stage = [&](int c0, int buf, int tg, int nt) {
-        const int cn = min(CH, nkeys - c0);
-        for (int base = 0; base < NTASK; base += TB * nt) {
-            uint4 kv[TB][2], vv[TB][2];
+    // A pass is split in two: the loads of up to T tasks per thread (tasks
+    // base + i * nt + tg) into registers, then their stores.  The loads are
+    // unconditional (a task or key past the end reads the last valid one)
+    // so that the compiler's count of loads in flight stays exact; the
+    // stores write zeros for keys past the end.
+    auto load_pass = [&](int c0, int base, int tg, int nt, auto &kv, auto &vv) {
+        constexpr int T = sizeof(kv) / sizeof(kv[0]);
+        // a chunk past the split's end (a loader's idle slot) reads the
+        // split's first key over and over: cache hits, and the same count
+        // of loads in flight on every path
+        if (c0 >= nkeys) c0 = 0;
+        const int cn = c0 == 0 && nkeys <= 0 ? 1 : min(CH, nkeys - c0);
+        const uint16_t *kb = Kb + (size_t)(key0 + c0) * D, *vb = Vb + (size_t)(key0 + c0) * D;
 #pragma unroll
-            for (int i = 0; i < TB; ++i) {
-                const int j = base + i * nt + tg;
+        for (int i = 0; i < T; ++i) {
+            const int j = min(base + i * nt + tg, NTASK - 1);
+            const int kk = min((2 * j) / KC, cn - 1), p = (2 * j) % KC;
+            const int kp = j % NPAIR, pv = j / NPAIR;
+            kv[i][0] = ld16(kb + (size_t)kk * D + p * 8);
+            kv[i][1] = ld16(kb + (size_t)kk * D + p * 8 + 8);
+            vv[i][0] = ld16(vb + (size_t)min(2 * kp, cn - 1) * D + pv * 8);
+            vv[i][1] = ld16(vb + (size_t)min(2 * kp + 1, cn - 1) * D + pv * 8);
+        }
+    };
+    auto store_pass = [&](int c0, int buf, int base, int tg, int nt, const auto &kv, const auto &vv) {
+        constexpr int T = sizeof(kv) / sizeof(kv[0]);
+        const int cn = min(CH, nkeys - c0);
+#pragma unroll
+        for (int i = 0; i < T; ++i) {
+            const int j = base + i * nt + tg;
+            if (j < NTASK) {
                 const int kk = (2 * j) / KC, p = (2 * j) % KC;
                 const int kp = j % NPAIR, pv = j / NPAIR;
-                const bool in = j < NTASK;
-                kv[i][0] = kv[i][1] = vv[i][0] = vv[i][1] = uint4{0u, 0u, 0u, 0u};
-                if (in && kk < cn) {
-                    const size_t off = (size_t)(key0 + c0 + kk) * D + p * 8;
-                    kv[i][0] = ld16(Kb + off);
-                    kv[i][1] = ld16(Kb + off + 8);
+                // keys past the end are stored as zeros (masks on the values)
+                const uint32_t mk = kk < cn ? ~0u : 0u, m0 = 2 * kp < cn ? ~0u : 0u, m1 = 2 * kp + 1 < cn ? ~0u : 0u;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint4 k4 = kv[i][h];
+                    *reinterpret_cast<uint4 *>(Ks[buf] + kk * D + (((p + h) ^ (kk & (KC - 1))) << 3)) =
+                        uint4{k4.x & mk, k4.y & mk, k4.z & mk, k4.w & mk};
                 }
-                if (in && 2 * kp < cn) vv[i][0] = ld16(Vb + (size_t)(key0 + c0 + 2 * kp) * D + pv * 8);
-                if (in && 2 * kp + 1 < cn) vv[i][1] = ld16(Vb + (size_t)(key0 + c0 + 2 * kp + 1) * D + pv * 8);
-            }
+                // dim pv*8 + e of keys 2kp and 2kp+1 as one dword
+                const uint4 w0 = vv[i][0], w1 = vv[i][1];
+                const uint32_t a0[4] = {w0.x & m0, w0.y & m0, w0.z & m0, w0.w & m0},
+                               a1[4] = {w1.x & m1, w1.y & m1, w1.z & m1, w1.w & m1};
 #pragma unroll
-            for (int i = 0; i < TB; ++i) {
-                const int j = base + i * nt + tg;
-                if (j < NTASK) {
-                    const int kk = (2 * j) / KC, p = (2 * j) % KC;
-                    const int kp = j % NPAIR, pv = j / NPAIR;
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-                        *reinterpret_cast<uint4 *>(Ks[buf] + kk * D + (((p + h) ^ (kk & (KC - 1))) << 3)) = kv[i][h];
-                    const uint16_t *v0 = reinterpret_cast<const uint16_t *>(&vv[i][0]);
-                    const uint16_t *v1 = reinterpret_cast<const uint16_t *>(&vv[i][1]);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        *reinterpret_cast<uint32_t *>(Vt[buf] + (pv * 8 + e) * VSTR + 2 * kp) =
-                            (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
+                for (int e = 0; e < 4; ++e) {
+                    *reinterpret_cast<uint32_t *>(Vt[buf] + (pv * 8 + 2 * e) * VSTR + 2 * kp) =
+                        (a0[e] & 0xffffu) | (a1[e] << 16);
+                    *reinterpret_cast<uint32_t *>(Vt[buf] + (pv * 8 + 2 * e + 1) * VSTR + 2 * kp) =
+                        (a0[e] >> 16) | (a1[e] & 0xffff0000u);
                 }
             }
+        }
+    };
+    auto stage = [&](int c0, int buf, int tg, int nt) {
+        for (int base = 0; base < NTASK; base += TB * nt) {
+            uint4 kv[TB][2], vv[TB][2];
+            load_pass(c0, base, tg, nt, kv, vv);
+            store_pass(c0, buf, base, tg, nt, kv, vv);
         }
     };
 
@@ -1281,13 +1320,29 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
     float mrun = -INFINITY, lrun = 0.f;   // running max (base-2 units) and sum
     const float scale2 = a.scale * 1.4426950408889634f;
 
-    if (nch > 0) stage(0, 0, tid, nthr);      // the first chunk: every thread
-    __syncthreads();
+    // the first chunk: every thread
+    if (nch > 0) stage(0, 0, tid, nthr);
+    if (wave >= cw) {
+        // loader waves: the loads of chunk c+2 are issued during chunk c and
+        // stay in flight across the barrier that ends it; their stores fill
+        // the free buffer at the start of chunk c+1 (at most kAttnLoadTasks
+        // tasks a thread: one pass)
+        const int tg = tid - cw * 64, nt = nthr - cw * 64;
+        uint4 lk[kAttnLoadTasks][2], lv[kAttnLoadTasks][2];
+        __builtin_amdgcn_sched_barrier(0);   // after the first chunk's stores, not before them
+        load_pass(CH, 0, tg, nt, lk, lv);
+        lds_barrier();
+        for (int ci = 0; ci < nch; ++ci) {
+            if (ci + 1 < nch) store_pass((ci + 1) * CH, (ci & 1) ^ 1, 0, tg, nt, lk, lv);
+            load_pass((ci + 2) * CH, 0, tg, nt, lk, lv);
+            lds_barrier();
+        }
+        return;
+    }
+    lds_barrier();
     for (int ci = 0; ci < nch; ++ci) {
         const int buf = ci & 1, c0 = ci * CH;
-        if (wave >= cw) {
-            if (ci + 1 < nch) stage(c0 + CH, buf ^ 1, tid - cw * 64, nthr - cw * 64);   // loader waves
-        } else if (wave * 32 < R) {
+        {
             const int cn = min(CH, nkeys - c0);
             const uint16_t *Kl = Ks[buf];
             const uint16_t *Vl = Vt[buf];
@@ -1372,7 +1427,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
                     const int k0 = kb * 32 + 16 * h + 4 * hf;
 #pragma unroll
                     for (int d = 0; d < NDB; ++d) {
-                        const uint16_t *vr = Vl + (d * 32 + c) * VSTR;
+                        const uint16_t *vr = Vl + ((db0 + d) * 32 + c) * VSTR;
                         const uint2 v0 = *reinterpret_cast<const uint2 *>(vr + k0);
                         const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + k0 + 8);
                         const uint4 va = {v0.x, v0.y, v1.x, v1.y};
@@ -1381,10 +1436,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
                     }
                 }
         }
-        __syncthreads();
+        lds_barrier();
         if (!loaders && ci + 1 < nch) {   // no loader waves: stage the next chunk in turn
             stage(c0 + CH, buf ^ 1, tid, nthr);
-            __syncthreads();
+            lds_barrier();
         }
     }
 
@@ -1396,8 +1451,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) a.po[pb * D + d * 32 + acc_row(r, hf)] = o[d][r];
-    if (hf == 0) {
+        for (int r = 0; r < 16; ++r) a.po[pb * D + (db0 + d) * 32 + acc_row(r, hf)] = o[d][r];
+    if (hf == 0 && db0 == 0) {
         a.pm[pb] = mrun;
         a.pl[pb] = lrun;
     }
@@ -1992,7 +2047,13 @@ hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a) {
     // the waves the CU holds beyond the compute waves, so that a chunk is
     // staged in one pass of loads for up to 24 rows (two passes with two
     // loader waves cost 10 % at 8k context)
-    const int lw = a.span > kAttnChunk ? kAttnWaves - rb : 0;
+    // two waves per block of rows (half the output dims each) when the CU
+    // has the waves for them and, with loaders, at least four loader waves
+    const bool multi = a.span > kAttnChunk;
+    const int ds = 2 * rb + (multi ? 4 : 0) <= kAttnWaves ? 2 : 1;
+    const int lw = multi ? kAttnWaves - rb * ds : 0;
+    // the loader waves stage a chunk in one pass of kAttnLoadTasks tasks a thread
+    if (multi && lw * 64 * kAttnLoadTasks < kAttnChunk / 2 * (D / 8)) return hipErrorInvalidValue;
     const int nz = a.nreq > 0 ? a.nreq : a.zrows > 0 ? (a.M + a.zrows - 1) / a.zrows : 1;
     if (a.zrows > 0 && (a.zrows > kMaxRows || a.M < 1)) return hipErrorInvalidValue;
     if (a.nreq > kMaxRows || (a.nreq > 0 && a.zrows > 0)) return hipErrorInvalidValue;
@@ -2000,9 +2061,11 @@ hipError_t launch_attn(hipStream_t s, int D, const AttnArgs &a) {
         if (a.rq[r].n > a.n || a.rq[r].nsplit + 1 > a.ns || a.rq[r].span > a.span ||
             (a.rq[r].row0 + a.rq[r].n) * a.G > kMaxRows * kMaxGroup)
             return hipErrorInvalidValue;
-    const dim3 grid(a.ns, a.n_qhead / a.G, nz), block(64 * (rb + lw));
-    if (D == 128) hipLaunchKernelGGL(k_attn<128>, grid, block, 0, s, a);
-    else if (D == 64) hipLaunchKernelGGL(k_attn<64>, grid, block, 0, s, a);
+    const dim3 grid(a.ns, a.n_qhead / a.G, nz), block(64 * (rb * ds + lw));
+    if (D == 128 && ds == 2) hipLaunchKernelGGL((k_attn<128, 2>), grid, block, 0, s, a);
+    else if (D == 128) hipLaunchKernelGGL((k_attn<128, 1>), grid, block, 0, s, a);
+    else if (D == 64 && ds == 2) hipLaunchKernelGGL((k_attn<64, 2>), grid, block, 0, s, a);
+    else if (D == 64) hipLaunchKernelGGL((k_attn<64, 1>), grid, block, 0, s, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
