@@ -1253,8 +1253,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
         // a chunk past the split's end (a loader's idle slot) reads the
         // split's first key over and over: cache hits, and the same count
         // of loads in flight on every path
-        if (c0 >= nkeys) c0 = 0;
-        const int cn = c0 == 0 && nkeys <= 0 ? 1 : min(CH, nkeys - c0);
+        const bool live = c0 < nkeys;
+        const int cn = live ? min(CH, nkeys - c0) : 1;
+        if (!live) c0 = 0;
         const uint16_t *kb = Kb + (size_t)(key0 + c0) * D, *vb = Vb + (size_t)(key0 + c0) * D;
 #pragma unroll
         for (int i = 0; i < T; ++i) {

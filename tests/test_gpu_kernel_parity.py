@@ -171,6 +171,29 @@ def test_attention_identical_inputs(tvs, shape, ctx, tree, qstd):
     check_rounded(gpu, exact, delta, f"attention {shape.name} ctx={ctx} {kind}{n}")
 
 
+@pytest.mark.parametrize("ctx", [1024, 3000, 8192])
+def test_attention_rows_independent_of_tree_size(tvs, ctx):
+    """A node's attention output has the same bits whatever the size of the
+    tree around it: the first rows of chains of 4, 8, 24 and 32 nodes (the
+    launch gives each block of 32 query rows one wave or, when the CU has
+    the waves, two waves that take half of the output dims each) agree
+    bit for bit with the same rows of the longest chain."""
+    shape = FULL
+    QH, KVH, D = shape.n_qhead, shape.n_kvhead, shape.head_dim
+    _say("attention rows vs tree size", ctx)
+    q = synth.bf16_normal((32, QH * D), 121, 1.0).cuda()
+    K = synth.bf16_normal((KVH, ctx + 40, D), 122).cuda()
+    V = synth.bf16_normal((KVH, ctx + 40, D), 123).cuda()
+    outs = {}
+    for n in (32, 24, 8, 4):
+        out = torch.empty((n, QH * D), dtype=torch.bfloat16, device="cuda")
+        tvs[shape.name].attention(q[:n].contiguous(), K, V, ctx, synth.chain_tree(n), out)
+        torch.cuda.synchronize()
+        outs[n] = out.cpu()
+    for n in (24, 8, 4):
+        assert torch.equal(outs[n], outs[32][:n]), f"ctx {ctx}: rows of a {n}-node chain differ"
+
+
 def test_attention_masks_non_ancestors(tvs):
     """A row does not move when keys and values of nodes off its path change."""
     shape, ctx, n = FULL, 300, 12
