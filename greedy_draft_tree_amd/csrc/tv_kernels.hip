@@ -1390,16 +1390,20 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(AttnArgs a) {
             const float mnew = fmaxf(mrun, mx);
             // with no visible key yet every score here is -inf: subtract 0
             const float msub = mnew == -INFINITY ? 0.f : mnew;
-            const float alpha = mrun == -INFINITY ? (mnew == -INFINITY ? 1.f : 0.f)
-                                                  : __builtin_amdgcn_exp2f(mrun - mnew);
-            // p = 2^(score * scale2 - max) with one rounding before the
-            // exponential; a masked score gives 2^-inf = 0
+            const float alpha = mrun == -INFINITY ? (mnew == -INFINITY ? 1.f : 0.f) : exp2f(mrun - mnew);
+            // p = 2^(round(score * scale2) - max): the product and the
+            // difference each rounded (no fused multiply-add, so every
+            // probability has the bits of the plain two-step form), then
+            // the exponential instruction (a probability below 2^-126, which
+            // it flushes, moves no sum or product it enters); a masked score
+            // gives 2^-inf = 0
             float ls = 0.f;
 #pragma unroll
             for (int kb = 0; kb < CH / 32; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale2, -msub));
+#pragma clang fp contract(off)
+                    const float p = __builtin_amdgcn_exp2f(s[kb][r] * scale2 - msub);
                     s[kb][r] = p;
                     ls += p;
                 }
