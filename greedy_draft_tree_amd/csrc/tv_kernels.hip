@@ -1556,33 +1556,44 @@ __device__ __forceinline__ uint4 pack_bf8(const float *x) {
     return uint4{f2bf2(x[0], x[1]), f2bf2(x[2], x[3]), f2bf2(x[4], x[5]), f2bf2(x[6], x[7])};
 }
 
-// Forward substitution for value column c, held in registers, of the delta
-// rule's unit lower-triangular system (n <= NN nodes; ancestors have lower
-// indices, so node order is a topological order): once u_s is final it is
-// taken out of every later node's right-hand side, so node t's sum runs over
-// s = 0, 1, ..., t - 1 in order.  u[t] for t >= n is never stored.
+// Forward substitution for value column c of the delta rule's unit
+// lower-triangular system (n <= NN nodes; ancestors have lower indices, so
+// node order is a topological order), by the four lanes of a quad: lane j
+// holds in registers the nodes t = j, j + 4, ... of the column.  Once u_s is
+// final its owner (lane s % 4) hands it to the quad (a DPP broadcast) and it
+// is taken out of every later node's right-hand side, so node t's sum runs
+// over s = 0, 1, ..., t - 1 in order.  akq[s][j][i] is the coefficient of
+// node 4i + j in row s.  u[t] for t >= n is never stored.
+// Lane k's x for every lane of its quad (quad_perm [k, k, k, k]); k is a
+// constant once the caller's loop is unrolled.
+__device__ __forceinline__ float quad_bcast(float x, int k) {
+    const int v = __float_as_int(x);
+    switch (k & 3) {
+    case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x00, 0xF, 0xF, false));
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x55, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xAA, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xFF, 0xF, 0xF, false));
+    }
+}
+
 template <int NN, int VW>
-__device__ __forceinline__ void delta_solve(float (*vsm)[VW], const float (*akt)[kMaxRows + 4], int n, int c) {
-    float u[NN];
+__device__ __forceinline__ void delta_solve(float (*vsm)[VW], const float (*akq)[kMaxRows + 4], int n, int c, int j) {
+    constexpr int NI = NN / 4;
+    float u[NI];
 #pragma unroll
-    for (int t = 0; t < NN; ++t) u[t] = t < n ? vsm[t][c] : 0.f;
+    for (int i = 0; i < NI; ++i) u[i] = 4 * i + j < n ? vsm[4 * i + j][c] : 0.f;
 #pragma unroll
     for (int s = 0; s < NN - 1; ++s) {
         if (s + 1 >= n) break;
-        const float us = u[s];
+        const float us = quad_bcast(u[s / 4], s);   // u_s from lane s % 4 of the quad
+        const float *a = akq[s] + j * NI;
 #pragma unroll
-        for (int q = (s + 1) / 4; q < NN / 4; ++q) {
-            if (4 * q >= n) break;
-            const float4 a = *reinterpret_cast<const float4 *>(&akt[s][4 * q]);
-            const float av[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (4 * q + e > s) u[4 * q + e] -= av[e] * us;
-        }
+        for (int i = s / 4; i < NI; ++i)
+            if (4 * i + j > s) u[i] -= a[i] * us;
     }
 #pragma unroll
-    for (int t = 0; t < NN; ++t)
-        if (t < n) vsm[t][c] = u[t];
+    for (int i = 0; i < NI; ++i)
+        if (4 * i + j < n) vsm[4 * i + j][c] = u[i];
 }
 
 template <int D, bool DELTA>
@@ -1607,26 +1618,27 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     __shared__ float gsh[kMaxRows], gcs[kMaxRows];
     __shared__ uint32_t ancs[kMaxRows];    // ancestor-or-self bits of each node
     __shared__ float coef[kMaxRows][kMaxRows + 1];
-    // delta rule: write strengths, and akt[s][t] = b_t e^{gc_t - gc_s} (k_t . k_s)
-    // for strict ancestors s of t (zero otherwise; rows padded to 36 floats)
+    // delta rule: write strengths, and the coefficient b_t e^{gc_t - gc_s}
+    // (k_t . k_s) of node t in row s, for strict ancestors s of t (zero
+    // otherwise), at akq[s][(t % 4) * NI + t / 4] with NI = (n <= 16 ? 4 : 8)
+    // (node t's solver lane is t % 4; rows padded to 36 floats)
     __shared__ float bsh[DELTA ? kMaxRows : 1];
-    __shared__ __attribute__((aligned(16))) float akt[DELTA ? kMaxRows : 1][kMaxRows + 4];
+    __shared__ __attribute__((aligned(16))) float akq[DELTA ? kMaxRows : 1][kMaxRows + 4];
     const int h = blockIdx.x, v0 = blockIdx.y * VW, tid = threadIdx.x, n = r.n, QH = r.QH;
     const int lane = tid & 63, wave = tid >> 6, hf = lane >> 5, l32 = lane & 31;
 
-    // state slice (every load in flight first); stored transposed as bf16
-    // hi + lo after the projection loads below are issued
-    constexpr int NV = D * VW / 4;         // float4 pieces
-    constexpr int PER = (NV + 255) / 256;
-    float4 st[PER];
+    // state slice (every load in flight first), read already transposed: a
+    // thread takes KPT consecutive keys of one value column (one 4-byte load
+    // per key, a wave's loads coalesced along the columns) and later writes
+    // them as bf16 hi + lo runs of its column's row
+    constexpr int KPT = D * VW / 256;      // keys per thread
+    static_assert(256 % VW == 0 && KPT % 4 == 0, "state slice mapping");
+    const int sc = tid % VW, sk0 = (tid / VW) * KPT;
+    float st[KPT];
     {
-        const float *S0 = r.S0 + (size_t)h * D * D + v0;
+        const float *S0 = r.S0 + (size_t)h * D * D + (size_t)sk0 * D + v0 + sc;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int idx = tid + i * 256;
-            st[i] = idx < NV ? *reinterpret_cast<const float4 *>(S0 + (size_t)(idx / (VW / 4)) * D + 4 * (idx % (VW / 4)))
-                             : float4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int i = 0; i < KPT; ++i) st[i] = S0[(size_t)i * D];
     }
     // Projection outputs: split-K partials summed in k-range order (or, for
     // a prefill block, bf16 rows), rounded to bf16 (the projection's output
@@ -1727,20 +1739,18 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
             }
         }
     }
-    // the state slice, transposed into bf16 hi + lo parts
+    // the state slice as bf16 hi + lo parts, KPT keys of column sc at a time
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int idx = tid + i * 256;
-        if (idx < NV) {
-            const int k = idx / (VW / 4), c0 = 4 * (idx % (VW / 4));
-            const float x[4] = {st[i].x, st[i].y, st[i].z, st[i].w};
+    for (int i = 0; i < KPT; i += 4) {
+        uint32_t wh[2], wl[2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint16_t hi = f2bf(x[e]);
-                s0h[c0 + e][k] = hi;
-                s0l[c0 + e][k] = f2bf(x[e] - bf2f(hi));
-            }
+        for (int e = 0; e < 2; ++e) {
+            const float x0 = st[i + 2 * e], x1 = st[i + 2 * e + 1];
+            wh[e] = f2bf2(x0, x1);
+            wl[e] = f2bf2(x0 - __uint_as_float(wh[e] << 16), x1 - __uint_as_float(wh[e] & 0xffff0000u));
         }
+        *reinterpret_cast<uint2 *>(&s0h[sc][sk0 + i]) = uint2{wh[0], wh[1]};
+        *reinterpret_cast<uint2 *>(&s0l[sc][sk0 + i]) = uint2{wl[0], wl[1]};
     }
     // q and k: round the sums, then each row's sum of squares over its TPR
     // lanes (consecutive lanes of one DPP row; a fixed tree of DPP
@@ -1787,8 +1797,10 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
         const uint32_t anc = ancs[tid];
         float gc = 0.f;
 #pragma unroll
-        for (int s2 = 0; s2 < kMaxRows; ++s2)
-            if (s2 <= tid && ((anc >> s2) & 1u)) gc += gsh[s2];
+        for (int s2 = 0; s2 < kMaxRows; ++s2) {   // every read issued; a non-ancestor adds an exact zero
+            const float g = gsh[s2];
+            gc += (s2 <= tid && ((anc >> s2) & 1u)) ? g : 0.f;
+        }
         gcs[tid] = gc;
     }
     __syncthreads();
@@ -1798,7 +1810,7 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     const uint4 z = {0u, 0u, 0u, 0u};
     if (wave == 0 || (DELTA && wave == 1)) {
         // coef (wave 0): e^{gc_t - gc_s} (q_t . k_s) over ancestors-or-self s;
-        // akt (wave 1, transposed): b_t e^{gc_t - gc_s} (k_t . k_s) over strict ancestors
+        // akq (wave 1, by solver lane): b_t e^{gc_t - gc_s} (k_t . k_s) over strict ancestors
         const uint16_t(*A)[BP] = wave == 0 ? qb : kb;
         f32x16 acc = {};
 #pragma unroll
@@ -1818,7 +1830,7 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
                 if (wave == 0) {
                     coef[t][s] = anc ? decay * acc[rr] : 0.f;
                 } else if constexpr (DELTA) {
-                    akt[s][t] = (anc && s != t) ? bsh[t] * decay * acc[rr] : 0.f;
+                    akq[s][(t & 3) * (n <= 16 ? 4 : 8) + (t >> 2)] = (anc && s != t) ? bsh[t] * decay * acc[rr] : 0.f;
                 }
             }
         }
@@ -1854,10 +1866,10 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
             vsm[t][c] = bsh[t] * (vsm[t][c] - expf(gcs[t]) * acck[t][c]);
         }
         __syncthreads();
-        // forward substitution, one thread a value column (the column in registers)
-        if (tid < VW) {
-            if (n <= 16) delta_solve<16, VW>(vsm, akt, n, tid);
-            else delta_solve<kMaxRows, VW>(vsm, akt, n, tid);
+        // forward substitution, a quad of lanes a value column (the column in registers)
+        if (tid < 4 * VW) {
+            if (n <= 16) delta_solve<16, VW>(vsm, akq, n, tid >> 2, tid & 3);
+            else delta_solve<kMaxRows, VW>(vsm, akq, n, tid >> 2, tid & 3);
         }
         __syncthreads();
     }
