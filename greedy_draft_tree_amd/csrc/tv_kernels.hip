@@ -1582,14 +1582,21 @@ __device__ __forceinline__ void delta_solve(float (*vsm)[VW], const float (*akq)
     float u[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) u[i] = 4 * i + j < n ? vsm[4 * i + j][c] : 0.f;
+    // row s + 1's coefficients are read while step s runs
+    float a[NI], an[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) a[i] = akq[0][j * NI + i];
 #pragma unroll
     for (int s = 0; s < NN - 1; ++s) {
         if (s + 1 >= n) break;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) an[i] = akq[s + 1][j * NI + i];
         const float us = quad_bcast(u[s / 4], s);   // u_s from lane s % 4 of the quad
-        const float *a = akq[s] + j * NI;
 #pragma unroll
         for (int i = s / 4; i < NI; ++i)
             if (4 * i + j > s) u[i] -= a[i] * us;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) a[i] = an[i];
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i)
@@ -1759,6 +1766,11 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         const int m = qr0 + i * RPP;
+        if ((wave * 64) / TPR + i * RPP >= n) {   // every row of this wave's pass is padding
+            *reinterpret_cast<uint4 *>(&qb[m][qc]) = uint4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<uint4 *>(&kb[m][qc]) = uint4{0u, 0u, 0u, 0u};
+            continue;
+        }
         float sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -1821,9 +1833,11 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
         }
         const int s = l32;
         if (s < n) {
+            const int rrn = n <= 16 ? 8 : 16;   // accumulators rr >= 8 hold nodes >= 16
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
                 const int t = acc_row(rr, hf);
+                if (rr >= rrn) break;
                 if (t >= n) continue;
                 const bool anc = (ancs[t] >> s) & 1u;
                 const float decay = expf(gcs[t] - gcs[s]);
