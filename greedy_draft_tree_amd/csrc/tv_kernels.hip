@@ -1834,17 +1834,28 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
         const int s = l32;
         if (s < n) {
             const int rrn = n <= 16 ? 8 : 16;   // accumulators rr >= 8 hold nodes >= 16
+            // every node-indexed read issued first (slots past n are read and not used)
+            float gt[16], bt[16];
+            uint32_t at[16];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int t = acc_row(rr, hf);
+                gt[rr] = gcs[t];
+                at[rr] = ancs[t];
+                bt[rr] = DELTA ? bsh[DELTA ? t : 0] : 0.f;
+            }
+            const float gs = gcs[s];
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
                 const int t = acc_row(rr, hf);
                 if (rr >= rrn) break;
                 if (t >= n) continue;
-                const bool anc = (ancs[t] >> s) & 1u;
-                const float decay = expf(gcs[t] - gcs[s]);
+                const bool anc = (at[rr] >> s) & 1u;
+                const float decay = expf(gt[rr] - gs);
                 if (wave == 0) {
                     coef[t][s] = anc ? decay * acc[rr] : 0.f;
                 } else if constexpr (DELTA) {
-                    akq[s][(t & 3) * (n <= 16 ? 4 : 8) + (t >> 2)] = (anc && s != t) ? bsh[t] * decay * acc[rr] : 0.f;
+                    akq[s][(t & 3) * (n <= 16 ? 4 : 8) + (t >> 2)] = (anc && s != t) ? bt[rr] * decay * acc[rr] : 0.f;
                 }
             }
         }
