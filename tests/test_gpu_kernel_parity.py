@@ -138,6 +138,9 @@ def _attention_delta(q, Kk, Vv, D, chunks_per_split, n_splits):
     (FULL, 3000, ("random", 29), 1.0),     # ragged: two chunks a split, a short last split
     (FULL, 0, ("bush", 17), 1.0),          # no context: the tree's keys only
     (FULL, 100, ("chain", 1), 3.0),        # one row, one short split
+    (FULL, 2500, ("random", 8), 2.0),      # two chunks a split: one load ahead, then an idle slot
+    (FULL, 8100, ("spine", 32), 1.0),      # five chunks a split, a ragged last split
+    (FULL, 6000, ("bush", 16), 1.0),
     (TINY, 777, ("spine", 32), 1.0),       # heads of 64
     (TINY, 64, ("random", 24), 2.0),
 ])
@@ -376,6 +379,12 @@ def _oracle_tree(orc, kind, x, parents, S0):
     (FULL, synth.DELTA, 1, 3, "chain"),
     (TINY, synth.DELTA, 24, 2, "random"),
     (TINY, synth.RECUR, 9, 1, "bush"),
+    # node counts that leave the solver's lanes uneven (nodes t = j, j + 4, ...)
+    # and the 16 / 32 coefficient layouts at their edges
+    (FULL, synth.DELTA, 5, 4, "random"),
+    (FULL, synth.DELTA, 17, 4, "spine"),
+    (FULL, synth.DELTA, 31, 4, "random"),
+    (TINY, synth.DELTA, 13, 4, "chain"),
 ])
 def test_recur_tree_and_commit_identical_inputs(tvs, shape, kind, n, splits, tree):
     QH, D = shape.n_qhead, shape.head_dim
