@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 #include "tv_internal.h"
 
@@ -657,6 +658,186 @@ __global__ __launch_bounds__(256) void k_gemm_dense(GemmArgs g) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         if (n0 + e < N) y[e] = o[e];
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------ dense GEMM, 256 x 256 tiles
+// For prefill chunks with enough rows that 256 x 256 tiles give every CU a
+// workgroup: a workgroup of 8 waves (two a SIMD) computes a 256 x 256 tile
+// (256 activation rows by 256 weight rows; with SwiGLU 128 gate and 128 up
+// rows of the same 128 output columns), each wave 128 rows by two weight
+// tiles in 8 accumulator tiles, so every weight fragment a wave reads from
+// LDS feeds 4 MFMAs and every activation fragment 2 (the 32-row-group
+// kernel above re-reads each weight tile from the caches for every 64
+// rows).  Both operands reach LDS by direct global-to-LDS loads in stages
+// of 32 k (half of a packed 64-k step: its 1 KB q-blocks 0-1, then 2-3),
+// three stages in flight ahead of the one in use, each stage in its own LDS
+// array so that the compiler can tell a load into one stage from a read of
+// another and holds no read back for loads it does not depend on.  Each
+// wave waits for its own loads of the next stage before the barrier that
+// publishes it.  Every output takes its MFMAs in the same order as in the
+// kernel above (steps in order, q-blocks 0..3 within a step, the same
+// operand layout), so the two kernels give the same bits.
+constexpr int kBigTile = 256;
+
+template <int EPI>
+__global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    // a stage: weight blocks [8 tiles][2 q-blocks], then activation blocks
+    // [8 groups of 32 rows][2 q-blocks], 1 KB (64 x 16 bytes) each
+    __shared__ __attribute__((aligned(16))) uint4 L0[2048];
+    __shared__ __attribute__((aligned(16))) uint4 L1[2048];
+    __shared__ __attribute__((aligned(16))) uint4 L2[2048];
+    __shared__ __attribute__((aligned(16))) uint4 L3[2048];
+    typedef __attribute__((address_space(3))) uint8_t lds_byte;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hf = lane >> 5, c = lane & 31;
+    const int K = g.K, M = g.M;
+    const int nst = K >> 5;                       // stages of 32 k
+    const int mt = (M + kBigTile - 1) / kBigTile;
+    const int total = gridDim.x, full = total & ~7;
+    int w = blockIdx.x;
+    if (w < full) w = (w & 7) * (full >> 3) + (w >> 3);   // XCD w%8 takes a contiguous range
+    const int nb = w / mt, m0 = (w % mt) * kBigTile;
+    // 8 waves, two a SIMD: wave (wm, wn) takes 128 activation rows (row
+    // groups 4wm..4wm+3) and two weight tiles: single weights tiles 2wn and
+    // 2wn+1; SwiGLU the gate and the up tile of output columns 32wn..+31
+    const int wm = wave & 1, wn = wave >> 1;
+
+    // This wave's loads: blocks wave + 8i.  i < 2: weight blocks of tile
+    // (wave + 8i) / 2; i >= 2: activation blocks of row group
+    // (wave + 8i - 16) / 2; q-block half wave % 2.  Stage st reads bytes
+    // 2 KB * st on of a weight tile's packed rows, and k = 64 (st / 2) +
+    // 16 (st % 2) on of an activation row (lanes 32-63 four 16-byte chunks
+    // further).
+    const int qh = wave & 1;
+    const uint16_t *wsrc[2];
+    const uint16_t *xsrc[2];
+    bool xok[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int t = (wave + 8 * i) >> 1;
+        const uint16_t *tb;
+        if constexpr (DUAL) tb = t < 4 ? g.W + (size_t)(4 * nb + t) * 32 * K : g.W2 + (size_t)(4 * nb + t - 4) * 32 * K;
+        else tb = g.W + (size_t)(8 * nb + t) * 32 * K;
+        wsrc[i] = tb + qh * 512 + lane * 8;
+        const int row = m0 + ((wave + 8 * i) >> 1) * 32 + c;
+        xok[i] = row < M;
+        xsrc[i] = g.X + (size_t)(xok[i] ? row : 0) * g.ldx + hf * 32 + qh * 8;
+    }
+    auto issue = [&](int st, uint4 *buf) {
+        const bool live = st < nst;   // past the end: zeros into a free stage, so every wait count holds
+        const size_t wo = (size_t)st * 1024;   // step st/2, q-blocks 2(st%2) + half: st KB of the tile
+        const int xo = (st >> 1) * 64 + (st & 1) * 16;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds(live ? static_cast<const void *>(wsrc[i] + wo) : g.zeros,
+                                             (lds_byte *)buf + (wave + 8 * i) * 1024, 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds(live && xok[i] ? static_cast<const void *>(xsrc[i] + xo) : g.zeros,
+                                             (lds_byte *)buf + 16384 + (wave + 8 * i) * 1024, 16, 0, 0);
+    };
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] = f32x16{};
+    // the wave's two weight tiles among the 8 staged
+    auto wtile = [&](int j) { return DUAL ? 4 * j + wn : 2 * wn + j; };
+    auto compute = [&](const uint4 *buf) {
+        // every operand of the stage is read first (12 reads in flight), so
+        // the products start as soon as the first ones land
+        uint4 a[2][2], b[2][4];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) a[q][j] = buf[(wtile(j) * 2 + q) * 64 + lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) b[q][r] = buf[1024 + ((4 * wm + r) * 2 + q) * 64 + lane];
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[j][r] = mfma32(a[q][j], b[q][r], acc[j][r]);
+    };
+    // wait until at most n of this wave's loads are in flight (vmcnt only)
+    auto wait_loads = [&](auto n) {
+        constexpr int v = decltype(n)::value;
+        __builtin_amdgcn_s_waitcnt((v & 15) | ((v >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+    };
+    auto publish = [&]() {
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto body = [&](int st, const uint4 *cur, uint4 *nxt) {
+        issue(st + 3, nxt);
+        compute(cur);
+        wait_loads(std::integral_constant<int, 8>{});   // stage st+1 landed; st+2, st+3 in flight
+        publish();
+    };
+    issue(0, L0);
+    issue(1, L1);
+    issue(2, L2);
+    wait_loads(std::integral_constant<int, 8>{});
+    publish();
+    for (int st = 0; st < nst; st += 4) {   // nst is a multiple of 4
+        body(st, L0, L3);
+        body(st + 1, L1, L0);
+        body(st + 2, L2, L1);
+        body(st + 3, L3, L2);
+    }
+    wait_loads(std::integral_constant<int, 0>{});
+
+    // epilogue: accumulators r = 4jj..4jj+3 of tile (j, rg) hold 4
+    // consecutive output columns of activation row m
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+        const int m = m0 + (4 * wm + rg) * 32 + c;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < (DUAL ? 1 : 2); ++j) {
+            const int tile = DUAL ? 4 * nb + wn : 8 * nb + 2 * wn + j;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int n0 = tile * 32 + 8 * jj + 4 * hf;
+                float v[4], v2[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = acc[j][rg][4 * jj + e];
+                    v2[e] = DUAL ? acc[1][rg][4 * jj + e] : 0.f;
+                }
+                if constexpr (EPI == EPI_F32) {
+                    *reinterpret_cast<float4 *>(g.Yf + (size_t)m * g.ldyf + n0) = float4{v[0], v[1], v[2], v[3]};
+                } else {
+                    uint16_t *y = g.Y + (size_t)m * g.ldy + n0;
+                    uint16_t o[4];
+                    if constexpr (EPI == EPI_RESID) {
+                        const uint2 old = *reinterpret_cast<const uint2 *>(y);
+                        const uint16_t yo[4] = {(uint16_t)(old.x & 0xffffu), (uint16_t)(old.x >> 16),
+                                                (uint16_t)(old.y & 0xffffu), (uint16_t)(old.y >> 16)};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o[e] = f2bf(bf2f(yo[e]) + bfround(v[e]));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if constexpr (EPI == EPI_BF16) {
+                                o[e] = f2bf(v[e]);
+                            } else {
+                                const float gt = bfround(v[e]), up = bfround(v2[e]);
+                                o[e] = f2bf(gt / (1.0f + expf(-gt)) * up);
+                            }
+                        }
+                    }
+                    *reinterpret_cast<uint2 *>(y) = uint2{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                                                          (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
                 }
             }
         }
@@ -2007,7 +2188,8 @@ hipError_t launch_gemm(hipStream_t s, int epi, const GemmArgs &a, int splits) {
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_dense(hipStream_t s, int epi, const GemmArgs &a) {
+// The 32-row-group kernel over the whole shape.
+static hipError_t launch_gemm_groups(hipStream_t s, int epi, const GemmArgs &a) {
     if (a.M < 1 || a.N < 1 || a.K < 8 || a.K % 8) return hipErrorInvalidValue;
     const int wblocks = ((a.N + 31) / 32 + 3) / 4;
     const dim3 block(256);
@@ -2016,25 +2198,72 @@ hipError_t launch_gemm_dense(hipStream_t s, int epi, const GemmArgs &a) {
     // (about 1.75 per CU), else 2; SwiGLU (two weight tiles per wave) takes 2
     // groups and one k step per LDS stage.  The k order of every output is
     // the same for any choice (whole steps in order).
-    const int g4 = ((a.M + 127) / 128) * wblocks, g2 = ((a.M + 63) / 64) * wblocks;
-    const bool four = g4 >= 448;
+    // One group (32 rows) when two would leave CUs idle (the last weight
+    // blocks of a shape whose bulk ran on the 256 x 256 tiles).
+    const int g4 = ((a.M + 127) / 128) * wblocks, g2 = ((a.M + 63) / 64) * wblocks, g1 = ((a.M + 31) / 32) * wblocks;
+    const bool four = g4 >= 448, one = g2 < 256;
     switch (epi) {
     case EPI_BF16:
         if (four) hipLaunchKernelGGL((k_gemm_dense<EPI_BF16, 4>), dim3(g4), block, 0, s, a);
+        else if (one) hipLaunchKernelGGL((k_gemm_dense<EPI_BF16, 1>), dim3(g1), block, 0, s, a);
         else hipLaunchKernelGGL((k_gemm_dense<EPI_BF16, 2>), dim3(g2), block, 0, s, a);
         break;
     case EPI_RESID:
         if (four) hipLaunchKernelGGL((k_gemm_dense<EPI_RESID, 4>), dim3(g4), block, 0, s, a);
+        else if (one) hipLaunchKernelGGL((k_gemm_dense<EPI_RESID, 1>), dim3(g1), block, 0, s, a);
         else hipLaunchKernelGGL((k_gemm_dense<EPI_RESID, 2>), dim3(g2), block, 0, s, a);
         break;
     case EPI_F32:
         if (four) hipLaunchKernelGGL((k_gemm_dense<EPI_F32, 4>), dim3(g4), block, 0, s, a);
+        else if (one) hipLaunchKernelGGL((k_gemm_dense<EPI_F32, 1>), dim3(g1), block, 0, s, a);
         else hipLaunchKernelGGL((k_gemm_dense<EPI_F32, 2>), dim3(g2), block, 0, s, a);
         break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_dense<EPI_SWIGLU, 2, 1>), dim3(g2), block, 0, s, a); break;
+    case EPI_SWIGLU:
+        if (one) hipLaunchKernelGGL((k_gemm_dense<EPI_SWIGLU, 1, 1>), dim3(g1), block, 0, s, a);
+        else hipLaunchKernelGGL((k_gemm_dense<EPI_SWIGLU, 2, 1>), dim3(g2), block, 0, s, a);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+
+hipError_t launch_gemm_dense(hipStream_t s, int epi, const GemmArgs &a) {
+    if (a.M < 1 || a.N < 1 || a.K < 8 || a.K % 8) return hipErrorInvalidValue;
+    // 256 x 256 tiles (same bits) for 256 rows and more when the shape is
+    // whole (k a multiple of 128, whole weight blocks, 16-byte aligned rows)
+    // and the tiles fill every CU at least once.  Only whole rounds of 256
+    // tiles (one workgroup a CU) run on them: the weight blocks of a last,
+    // partial round go to the 32-row-group kernel in a second launch, whose
+    // smaller tiles spread them over more CUs (the two kernels give the
+    // same bits, so where the cut falls changes no output).
+    const bool dual = epi == EPI_SWIGLU;
+    const int bw = dual ? 128 : 256;                 // output columns of a weight block
+    const int nblk = a.N / bw, mt = (a.M + kBigTile - 1) / kBigTile;
+    const bool whole = a.M >= kBigTile && a.K % 128 == 0 && a.N % bw == 0 && a.ldx % 8 == 0 &&
+                       (epi == EPI_F32 ? a.ldyf % 4 == 0 : a.ldy % 4 == 0);
+    const int rem = (nblk * mt) % 256 ? ((nblk * mt) % 256 + mt - 1) / mt : 0;   // blocks of the partial round
+    const int nbig = (nblk - rem) * mt;
+    if (!whole || nbig < 256) return launch_gemm_groups(s, epi, a);
+    const dim3 grid(nbig), block8(512);
+    switch (epi) {
+    case EPI_BF16: hipLaunchKernelGGL(k_gemm_big<EPI_BF16>, grid, block8, 0, s, a); break;
+    case EPI_RESID: hipLaunchKernelGGL(k_gemm_big<EPI_RESID>, grid, block8, 0, s, a); break;
+    case EPI_F32: hipLaunchKernelGGL(k_gemm_big<EPI_F32>, grid, block8, 0, s, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_big<EPI_SWIGLU>, grid, block8, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || rem == 0) return e;
+    // the last rem weight blocks: output columns c0.. of the same rows
+    const int c0 = (nblk - rem) * bw;
+    GemmArgs r = a;
+    r.N = rem * bw;
+    r.W = a.W + (size_t)c0 * a.K;                    // whole 32-row tiles of the packed weights
+    if (dual) r.W2 = a.W2 + (size_t)c0 * a.K;
+    if (epi == EPI_F32) r.Yf = a.Yf + c0;
+    else r.Y = a.Y + c0;
+    return launch_gemm_groups(s, epi, r);
 }
 
 hipError_t launch_splitk_reduce(hipStream_t s, int epi, const GemmArgs &a, int splits) {

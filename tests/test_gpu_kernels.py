@@ -189,7 +189,8 @@ def test_head_rows_bitwise_invariant(tv, head):
 
 # ------------------------------------------------------------ dense (prefill) GEMM
 
-@pytest.mark.parametrize("M,N,K", [(33, 512, 256), (130, 1056, 1024), (300, 5120, 5120), (97, 17408, 512)])
+@pytest.mark.parametrize("M,N,K", [(33, 512, 256), (130, 1056, 1024), (300, 5120, 5120), (97, 17408, 512),
+                                   (1000, 17408, 512)])   # 256 x 256 tiles, a ragged last row tile
 def test_dense_linear_fp32_and_bf16(tv, M, N, K):
     """More than 32 rows run the dense kernel: fp32 sums within Higham's
     bound, bf16 outputs correctly rounded up to that bound."""
@@ -213,11 +214,12 @@ def test_dense_linear_fp32_and_bf16(tv, M, N, K):
     assert torch.equal(yb, y.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("N,K,R", [(2048, 1024, 300), (17408, 512, 512)])
+@pytest.mark.parametrize("N,K,R", [(2048, 1024, 300), (17408, 512, 512), (17408, 1280, 1024)])
 def test_dense_linear_rows_bitwise_invariant(tv, N, K, R):
     """A row's dense result does not depend on the row count, its slot, or
     the tile shape the row count selects (at 17408 columns 512 rows take 4
-    row groups per workgroup, fewer rows take 2)."""
+    row groups per workgroup, fewer rows take 2; 1024 rows take the 256 x
+    256 tiles, the subsets below the 32-row-group kernel)."""
     x, w = _operands(R, N, K, 7)
     tv.pack_weight(w)
     full = torch.empty(R, N, dtype=torch.float32, device="cuda")

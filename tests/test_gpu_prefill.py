@@ -340,3 +340,32 @@ def test_c1_width_dense_prefill():
     err = np.abs(gl - ol).max()
     print(f"[c1 dense prefill] verify max|dlogit| {err:.4g}", flush=True)
     assert err <= 0.1, err
+
+
+def test_full_width_prefill_chunk_size_is_bitwise():
+    """A one-layer full-width gated-recurrence model (hidden 5120, ffn 17408)
+    prefilled with chunks of 2048 rows (the stacked q/k/v projection and
+    gate/up with SwiGLU on the 256 x 256 tiles) and with chunks of 64 (every
+    projection on the 32-row-group kernel): recurrent layers take their rows
+    as chains of 32 in order whatever the chunk, so the last token and the
+    state after the prompt agree bit for bit."""
+    _gpu()
+    import workloads
+    shape = synth.scaled(synth.C1, "c3_layer1_pf", n_layer=1, kinds=[synth.RECUR])
+    wl = workloads.build(shape, max_ctx=2112, max_req=2, weight_device="cuda", host_copy=False)
+    s0 = synth.state0(shape, seed=8)
+    for r in (0, 1):
+        for l, t in wl.states[r].items():
+            t.copy_(s0[l].cuda())
+    torch.cuda.synchronize()
+    n = 2100
+    prompt = synth.uniform_ids(n, shape.vocab, 29)
+    _say("full-width prefill, chunk 2048 vs 64", n)
+    firsts = []
+    for r, chunk in ((0, 2048), (1, 64)):
+        wl.tv.set_history(r, [], 0)
+        firsts.append(wl.tv.prefill_dense(r, prompt, chunk=chunk))
+    torch.cuda.synchronize()
+    assert firsts[0] == firsts[1], firsts
+    for l in wl.states[0]:
+        assert torch.equal(wl.states[0][l], wl.states[1][l]), l
