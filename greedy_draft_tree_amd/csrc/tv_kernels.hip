@@ -683,9 +683,13 @@ __global__ __launch_bounds__(256) void k_gemm_dense(GemmArgs g) {
 // operand layout), so the two kernels give the same bits.
 constexpr int kBigTile = 256;
 
-template <int EPI>
-__global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
+template <int EPI, int TR>   // TR: activation rows of a workgroup tile (256, 128 or 64)
+__device__ __forceinline__ void gemm_big(const GemmArgs &g) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    static_assert(TR == 256 || TR == 128 || TR == 64, "row tile");
+    constexpr int RG = TR / 64;           // row groups of 32 a wave
+    constexpr int XB = TR / 128 > 0 ? TR / 128 : 1;   // activation loads a wave issues a stage (some fill nothing)
+    constexpr int WAIT = 2 * (2 + XB);    // loads of two stages in flight
     // a stage: weight blocks [8 tiles][2 q-blocks], then activation blocks
     // [8 groups of 32 rows][2 q-blocks], 1 KB (64 x 16 bytes) each
     __shared__ __attribute__((aligned(16))) uint4 L0[2048];
@@ -698,26 +702,29 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     const int hf = lane >> 5, c = lane & 31;
     const int K = g.K, M = g.M;
     const int nst = K >> 5;                       // stages of 32 k
-    const int mt = (M + kBigTile - 1) / kBigTile;
+    const int mt = (M + TR - 1) / TR;
     const int total = gridDim.x, full = total & ~7;
     int w = blockIdx.x;
     if (w < full) w = (w & 7) * (full >> 3) + (w >> 3);   // XCD w%8 takes a contiguous range
-    const int nb = w / mt, m0 = (w % mt) * kBigTile;
-    // 8 waves, two a SIMD: wave (wm, wn) takes 128 activation rows (row
-    // groups 4wm..4wm+3) and two weight tiles: single weights tiles 2wn and
-    // 2wn+1; SwiGLU the gate and the up tile of output columns 32wn..+31
+    const int nb = w / mt, m0 = (w % mt) * TR;
+    // 8 waves, two a SIMD: wave (wm, wn) takes TR/2 activation rows (row
+    // groups RG wm .. RG wm + RG - 1) and two weight tiles: single weights
+    // tiles 2wn and 2wn+1; SwiGLU the gate and the up tile of output
+    // columns 32wn..+31
     const int wm = wave & 1, wn = wave >> 1;
 
-    // This wave's loads: blocks wave + 8i.  i < 2: weight blocks of tile
-    // (wave + 8i) / 2; i >= 2: activation blocks of row group
-    // (wave + 8i - 16) / 2; q-block half wave % 2.  Stage st reads bytes
+    // This wave's loads: weight blocks wave + 8i (i < 2) of tile
+    // (wave + 8i) / 2, and activation blocks wave + 8i (i < XB) of row group
+    // (wave + 8i) / 2 (with TR = 64 the waves past its 4 blocks load zeros
+    // into the unused rest of the stage, so every wave issues the same
+    // count); q-block half wave % 2.  Stage st reads bytes
     // 2 KB * st on of a weight tile's packed rows, and k = 64 (st / 2) +
     // 16 (st % 2) on of an activation row (lanes 32-63 four 16-byte chunks
     // further).
     const int qh = wave & 1;
     const uint16_t *wsrc[2];
-    const uint16_t *xsrc[2];
-    bool xok[2];
+    const uint16_t *xsrc[XB];
+    bool xok[XB];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int t = (wave + 8 * i) >> 1;
@@ -725,8 +732,12 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
         if constexpr (DUAL) tb = t < 4 ? g.W + (size_t)(4 * nb + t) * 32 * K : g.W2 + (size_t)(4 * nb + t - 4) * 32 * K;
         else tb = g.W + (size_t)(8 * nb + t) * 32 * K;
         wsrc[i] = tb + qh * 512 + lane * 8;
-        const int row = m0 + ((wave + 8 * i) >> 1) * 32 + c;
-        xok[i] = row < M;
+    }
+#pragma unroll
+    for (int i = 0; i < XB; ++i) {
+        const int grp = (wave + 8 * i) >> 1;
+        const int row = m0 + grp * 32 + c;
+        xok[i] = grp < TR / 32 && row < M;
         xsrc[i] = g.X + (size_t)(xok[i] ? row : 0) * g.ldx + hf * 32 + qh * 8;
     }
     auto issue = [&](int st, uint4 *buf) {
@@ -738,35 +749,35 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
             __builtin_amdgcn_global_load_lds(live ? static_cast<const void *>(wsrc[i] + wo) : g.zeros,
                                              (lds_byte *)buf + (wave + 8 * i) * 1024, 16, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < XB; ++i)
             __builtin_amdgcn_global_load_lds(live && xok[i] ? static_cast<const void *>(xsrc[i] + xo) : g.zeros,
                                              (lds_byte *)buf + 16384 + (wave + 8 * i) * 1024, 16, 0, 0);
     };
 
-    f32x16 acc[2][4];
+    f32x16 acc[2][RG];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[j][r] = f32x16{};
+        for (int r = 0; r < RG; ++r) acc[j][r] = f32x16{};
     // the wave's two weight tiles among the 8 staged
     auto wtile = [&](int j) { return DUAL ? 4 * j + wn : 2 * wn + j; };
     auto compute = [&](const uint4 *buf) {
         // every operand of the stage is read first (12 reads in flight), so
         // the products start as soon as the first ones land
-        uint4 a[2][2], b[2][4];
+        uint4 a[2][2], b[2][RG];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) a[q][j] = buf[(wtile(j) * 2 + q) * 64 + lane];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) b[q][r] = buf[1024 + ((4 * wm + r) * 2 + q) * 64 + lane];
+            for (int r = 0; r < RG; ++r) b[q][r] = buf[1024 + ((RG * wm + r) * 2 + q) * 64 + lane];
         }
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[j][r] = mfma32(a[q][j], b[q][r], acc[j][r]);
+                for (int r = 0; r < RG; ++r) acc[j][r] = mfma32(a[q][j], b[q][r], acc[j][r]);
     };
     // wait until at most n of this wave's loads are in flight (vmcnt only)
     auto wait_loads = [&](auto n) {
@@ -780,13 +791,13 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     auto body = [&](int st, const uint4 *cur, uint4 *nxt) {
         issue(st + 3, nxt);
         compute(cur);
-        wait_loads(std::integral_constant<int, 8>{});   // stage st+1 landed; st+2, st+3 in flight
+        wait_loads(std::integral_constant<int, WAIT>{});   // stage st+1 landed; st+2, st+3 in flight
         publish();
     };
     issue(0, L0);
     issue(1, L1);
     issue(2, L2);
-    wait_loads(std::integral_constant<int, 8>{});
+    wait_loads(std::integral_constant<int, WAIT>{});
     publish();
     for (int st = 0; st < nst; st += 4) {   // nst is a multiple of 4
         body(st, L0, L3);
@@ -799,8 +810,8 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     // epilogue: accumulators r = 4jj..4jj+3 of tile (j, rg) hold 4
     // consecutive output columns of activation row m
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-        const int m = m0 + (4 * wm + rg) * 32 + c;
+    for (int rg = 0; rg < RG; ++rg) {
+        const int m = m0 + (RG * wm + rg) * 32 + c;
         if (m >= M) continue;
 #pragma unroll
         for (int j = 0; j < (DUAL ? 1 : 2); ++j) {
@@ -843,6 +854,14 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
         }
     }
 }
+
+// One kernel per row-tile height (the body above, instantiated three ways).
+template <int EPI>
+__global__ __launch_bounds__(512) void k_gemm_big256(GemmArgs g) { gemm_big<EPI, 256>(g); }
+template <int EPI>
+__global__ __launch_bounds__(512) void k_gemm_big128(GemmArgs g) { gemm_big<EPI, 128>(g); }
+template <int EPI>
+__global__ __launch_bounds__(512) void k_gemm_big64(GemmArgs g) { gemm_big<EPI, 64>(g); }
 
 // Split-K finish: one thread per output element adds its S partials in
 // k-range order and applies the element's epilogue.
@@ -2228,32 +2247,49 @@ static hipError_t launch_gemm_groups(hipStream_t s, int epi, const GemmArgs &a) 
 }
 
 
+// k_gemm_big of row tile mt_rows (256, 128 or 64) over nblk weight blocks.
+static hipError_t launch_gemm_big(hipStream_t s, int epi, const GemmArgs &a, int nblk, int mt_rows) {
+    const dim3 grid(nblk * ((a.M + mt_rows - 1) / mt_rows)), block(512);
+#define TV_BIG(K)                                                                                             \
+    switch (epi) {                                                                                            \
+    case EPI_BF16: hipLaunchKernelGGL(K<EPI_BF16>, grid, block, 0, s, a); break;                              \
+    case EPI_RESID: hipLaunchKernelGGL(K<EPI_RESID>, grid, block, 0, s, a); break;                            \
+    case EPI_F32: hipLaunchKernelGGL(K<EPI_F32>, grid, block, 0, s, a); break;                                \
+    case EPI_SWIGLU: hipLaunchKernelGGL(K<EPI_SWIGLU>, grid, block, 0, s, a); break;                          \
+    default: return hipErrorInvalidValue;                                                                     \
+    }
+    if (mt_rows == 256) { TV_BIG(k_gemm_big256) }
+    else if (mt_rows == 128) { TV_BIG(k_gemm_big128) }
+    else if (mt_rows == 64) { TV_BIG(k_gemm_big64) }
+    else return hipErrorInvalidValue;
+#undef TV_BIG
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_dense(hipStream_t s, int epi, const GemmArgs &a) {
     if (a.M < 1 || a.N < 1 || a.K < 8 || a.K % 8) return hipErrorInvalidValue;
     // 256 x 256 tiles (same bits) for 256 rows and more when the shape is
     // whole (k a multiple of 128, whole weight blocks, 16-byte aligned rows)
     // and the tiles fill every CU at least once.  Only whole rounds of 256
     // tiles (one workgroup a CU) run on them: the weight blocks of a last,
-    // partial round go to the 32-row-group kernel in a second launch, whose
-    // smaller tiles spread them over more CUs (the two kernels give the
-    // same bits, so where the cut falls changes no output).
+    // partial round take tiles of 128 or 64 rows in a second launch, which
+    // spreads them over more CUs (every tile height gives the same bits, so
+    // where the cut falls changes no output).  Measured at 1024 and 2048
+    // rows on the 5120-wide layer's shapes.
     const bool dual = epi == EPI_SWIGLU;
     const int bw = dual ? 128 : 256;                 // output columns of a weight block
     const int nblk = a.N / bw, mt = (a.M + kBigTile - 1) / kBigTile;
     const bool whole = a.M >= kBigTile && a.K % 128 == 0 && a.N % bw == 0 && a.ldx % 8 == 0 &&
                        (epi == EPI_F32 ? a.ldyf % 4 == 0 : a.ldy % 4 == 0);
     const int rem = (nblk * mt) % 256 ? ((nblk * mt) % 256 + mt - 1) / mt : 0;   // blocks of the partial round
-    const int nbig = (nblk - rem) * mt;
-    if (!whole || nbig < 256) return launch_gemm_groups(s, epi, a);
-    const dim3 grid(nbig), block8(512);
-    switch (epi) {
-    case EPI_BF16: hipLaunchKernelGGL(k_gemm_big<EPI_BF16>, grid, block8, 0, s, a); break;
-    case EPI_RESID: hipLaunchKernelGGL(k_gemm_big<EPI_RESID>, grid, block8, 0, s, a); break;
-    case EPI_F32: hipLaunchKernelGGL(k_gemm_big<EPI_F32>, grid, block8, 0, s, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_big<EPI_SWIGLU>, grid, block8, 0, s, a); break;
-    default: return hipErrorInvalidValue;
+    if (!whole) return launch_gemm_groups(s, epi, a);
+    if ((nblk - rem) * mt < 256) {
+        // too few 256-row tiles for a round: 128-row tiles when they fill
+        // the CUs (the 32-row-group kernel is faster below that)
+        if (nblk * ((a.M + 127) / 128) >= 256) return launch_gemm_big(s, epi, a, nblk, 128);
+        return launch_gemm_groups(s, epi, a);
     }
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_gemm_big(s, epi, a, nblk - rem, kBigTile);
     if (e != hipSuccess || rem == 0) return e;
     // the last rem weight blocks: output columns c0.. of the same rows
     const int c0 = (nblk - rem) * bw;
@@ -2263,7 +2299,7 @@ hipError_t launch_gemm_dense(hipStream_t s, int epi, const GemmArgs &a) {
     if (dual) r.W2 = a.W2 + (size_t)c0 * a.K;
     if (epi == EPI_F32) r.Yf = a.Yf + c0;
     else r.Y = a.Y + c0;
-    return launch_gemm_groups(s, epi, r);
+    return launch_gemm_big(s, epi, r, rem, rem * ((a.M + 127) / 128) >= 256 ? 128 : 64);
 }
 
 hipError_t launch_splitk_reduce(hipStream_t s, int epi, const GemmArgs &a, int splits) {

@@ -214,12 +214,13 @@ def test_dense_linear_fp32_and_bf16(tv, M, N, K):
     assert torch.equal(yb, y.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("N,K,R", [(2048, 1024, 300), (17408, 512, 512), (17408, 1280, 1024)])
+@pytest.mark.parametrize("N,K,R", [(2048, 1024, 300), (17408, 512, 512), (17408, 1280, 1024), (7168, 1280, 2048)])
 def test_dense_linear_rows_bitwise_invariant(tv, N, K, R):
     """A row's dense result does not depend on the row count, its slot, or
     the tile shape the row count selects (at 17408 columns 512 rows take 4
     row groups per workgroup, fewer rows take 2; 1024 rows take the 256 x
-    256 tiles, the subsets below the 32-row-group kernel)."""
+    256 tiles with the last weight blocks on 64-row tiles, 2048 rows at 7168
+    columns 128-row tiles, and the subsets below the 32-row-group kernel)."""
     x, w = _operands(R, N, K, 7)
     tv.pack_weight(w)
     full = torch.empty(R, N, dtype=torch.float32, device="cuda")
