@@ -2280,7 +2280,9 @@ hipError_t launch_gemm_dense(hipStream_t s, int epi, const GemmArgs &a) {
     const int bw = dual ? 128 : 256;                 // output columns of a weight block
     const int nblk = a.N / bw, mt = (a.M + kBigTile - 1) / kBigTile;
     const bool whole = a.M >= kBigTile && a.K % 128 == 0 && a.N % bw == 0 && a.ldx % 8 == 0 &&
-                       (epi == EPI_F32 ? a.ldyf % 4 == 0 : a.ldy % 4 == 0);
+                       ((uintptr_t)a.X & 15) == 0 &&
+                       (epi == EPI_F32 ? a.ldyf % 4 == 0 && ((uintptr_t)a.Yf & 15) == 0
+                                       : a.ldy % 4 == 0 && ((uintptr_t)a.Y & 7) == 0);
     const int rem = (nblk * mt) % 256 ? ((nblk * mt) % 256 + mt - 1) / mt : 0;   // blocks of the partial round
     if (!whole) return launch_gemm_groups(s, epi, a);
     if ((nblk - rem) * mt < 256) {
