@@ -27,3 +27,23 @@ def write():
     tot = {k: sum(r[k] for r in RECORDS) for k in ("rows", "ties", "flips")}
     with open(path, "w") as f:
         json.dump({"total": tot, "records": RECORDS}, f, indent=1)
+
+
+def render(path, commit, passed):
+    """Markdown table of a written log: ``python tests/parity_log.py LOG COMMIT PASSED``."""
+    d = json.load(open(path))
+    tot = d["total"]
+    out = ["| case | rows | ties | flips | max abs logit error | tolerance (min .. max over rows) |",
+           "|---|---:|---:|---:|---:|---|"]
+    for r in d["records"]:
+        out.append(f"| {r['case']} | {r['rows']} | {r['ties']} | {r['flips']} | {r['max_abs_dlogit']:.4g} | "
+                   f"{r['tol_min']:.4g} .. {r['tol_max']:.4g} |")
+    head = (f"on MI355X at commit `{commit}` ({passed} GPU tests passed).",
+            f"**Total: {tot['rows']} rows compared, {tot['ties']} ties, {tot['flips']} flips.**")
+    return head, "\n".join(out)
+
+
+if __name__ == "__main__":
+    import sys
+    head, table = render(sys.argv[1], sys.argv[2], sys.argv[3])
+    print(head[0]); print(head[1]); print(); print(table)
