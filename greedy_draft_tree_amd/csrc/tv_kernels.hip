@@ -1733,7 +1733,9 @@ __global__ __launch_bounds__(D) void k_attn_combine(AttnArgs a, uint16_t *__rest
 // in what the commit saves.
 
 __device__ __forceinline__ float log_sigmoid(float a) {
-    return a >= 0.f ? -log1pf(expf(-a)) : a - log1pf(expf(a));
+    // -log(1 + e^{-a}) for a >= 0, a - log(1 + e^{a}) below: both take e^{-|a|}
+    const float l = log1pf(expf(-fabsf(a)));
+    return a >= 0.f ? -l : a - l;
 }
 
 // Sum over groups of W consecutive lanes (W = 8 or 16, inside one 16-lane
@@ -1756,14 +1758,6 @@ __device__ __forceinline__ uint4 pack_bf8(const float *x) {
     return uint4{f2bf2(x[0], x[1]), f2bf2(x[2], x[3]), f2bf2(x[4], x[5]), f2bf2(x[6], x[7])};
 }
 
-// Forward substitution for value column c of the delta rule's unit
-// lower-triangular system (n <= NN nodes; ancestors have lower indices, so
-// node order is a topological order), by the four lanes of a quad: lane j
-// holds in registers the nodes t = j, j + 4, ... of the column.  Once u_s is
-// final its owner (lane s % 4) hands it to the quad (a DPP broadcast) and it
-// is taken out of every later node's right-hand side, so node t's sum runs
-// over s = 0, 1, ..., t - 1 in order.  akq[s][j][i] is the coefficient of
-// node 4i + j in row s.  u[t] for t >= n is never stored.
 // Lane k's x for every lane of its quad (quad_perm [k, k, k, k]); k is a
 // constant once the caller's loop is unrolled.
 __device__ __forceinline__ float quad_bcast(float x, int k) {
@@ -1776,35 +1770,53 @@ __device__ __forceinline__ float quad_bcast(float x, int k) {
     }
 }
 
+// Forward substitution for value column c of the delta rule's unit
+// lower-triangular system (n <= NN nodes; ancestors have lower indices, so
+// node order is a topological order), by the four lanes of a quad: lane j
+// holds in registers the nodes t = j, j + 4, ... of the column.  Once u_s is
+// final its owner (lane s % 4) hands it to the quad (a DPP broadcast) and it
+// is taken out of every later node's right-hand side, so node t's sum runs
+// over s = 0, 1, ..., t - 1 in order.  akq[s][j][i] is the coefficient of
+// node 4i + j in row s.  u[t] for t >= n is never stored.
 template <int NN, int VW>
-__device__ __forceinline__ void delta_solve(float (*vsm)[VW], const float (*akq)[kMaxRows + 4], int n, int c, int j) {
+__device__ __forceinline__ void delta_solve(float (*vsm)[VW + 1], const float (*akq)[kMaxRows + 4], int n, int c, int j) {
     constexpr int NI = NN / 4;
+    constexpr int PD = 4;   // coefficient rows in flight ahead of the step that uses them
     float u[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) u[i] = 4 * i + j < n ? vsm[4 * i + j][c] : 0.f;
-    // row s + 1's coefficients are read while step s runs
-    float a[NI], an[NI];
+    // ring of the next PD rows' coefficients: row s sits in a[s % PD] and is
+    // replaced by row s + PD once step s has used it (rows past n are read,
+    // never used: akq has kMaxRows rows)
+    float a[PD][NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) a[i] = akq[0][j * NI + i];
+    for (int q = 0; q < PD; ++q)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) a[q][i] = akq[q][j * NI + i];
 #pragma unroll
     for (int s = 0; s < NN - 1; ++s) {
         if (s + 1 >= n) break;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) an[i] = akq[s + 1][j * NI + i];
         const float us = quad_bcast(u[s / 4], s);   // u_s from lane s % 4 of the quad
 #pragma unroll
         for (int i = s / 4; i < NI; ++i)
-            if (4 * i + j > s) u[i] -= a[i] * us;
+            if (4 * i + j > s) u[i] -= a[s % PD][i] * us;
+        if (s + PD < NN - 1) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) a[i] = an[i];
+            for (int i = 0; i < NI; ++i) a[s % PD][i] = akq[s + PD][j * NI + i];
+        }
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i)
         if (4 * i + j < n) vsm[4 * i + j][c] = u[i];
 }
 
+// Threads of a read-out workgroup: 8 waves at head size 128 (two a SIMD, so
+// each wave's loads, norms and sums are half as long and a SIMD has a
+// second wave to switch to), 4 at 64 (the state-slice mapping's limit).
+constexpr int recur_threads(int D) { return D >= 128 ? 512 : 256; }
+
 template <int D, bool DELTA>
-__global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
+__global__ __launch_bounds__(recur_threads(D)) void k_recur_tree(RecurArgs r) {
     // grid (head, value slice): a workgroup produces value columns
     // [v0, v0 + VW) of its head for every node; the small per-head setup
     // (norms, cumulative gates, the node-node coefficients) is repeated by
@@ -1814,15 +1826,17 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     // S0^T Q, S0^T K with the fp32 state split into bf16 hi + lo parts
     // (|S0 - hi - lo| <= 2^-17 |S0|).
     constexpr int VS = kRecurSlices;
+    constexpr int NT = recur_threads(D);
     constexpr int VW = D / VS;             // value columns per workgroup (<= 32)
     constexpr int BP = D + 8;              // padded bf16 row stride (16-byte rows, spread banks)
     constexpr int KB = D / 16;             // MFMA k blocks
     static_assert(VW <= 32 && D % 16 == 0, "slice shape");
     __shared__ __attribute__((aligned(16))) uint16_t qb[kMaxRows][BP], kb[kMaxRows][BP];   // normalised, bf16
     __shared__ __attribute__((aligned(16))) uint16_t s0h[VW][BP], s0l[VW][BP];  // S0 slice, transposed, hi/lo
-    __shared__ float vsm[kMaxRows][VW];    // v, then (delta) the right-hand side and u
-    __shared__ float accq[kMaxRows][VW + 1], acck[DELTA ? kMaxRows : 1][VW + 1];   // S0^T q_t, S0^T k_t
-    __shared__ float gsh[kMaxRows], gcs[kMaxRows];
+    __shared__ float vsm[kMaxRows][VW + 1];   // v, then (delta) the right-hand side and u (odd stride: a
+                                              // wave of nodes at one column hits distinct banks)
+    __shared__ float accq[kMaxRows][VW + 1];   // e^{gc_t} S0^T q_t
+    __shared__ float gcs[kMaxRows];
     __shared__ uint32_t ancs[kMaxRows];    // ancestor-or-self bits of each node
     __shared__ float coef[kMaxRows][kMaxRows + 1];
     // delta rule: write strengths, and the coefficient b_t e^{gc_t - gc_s}
@@ -1838,8 +1852,8 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     // thread takes KPT consecutive keys of one value column (one 4-byte load
     // per key, a wave's loads coalesced along the columns) and later writes
     // them as bf16 hi + lo runs of its column's row
-    constexpr int KPT = D * VW / 256;      // keys per thread
-    static_assert(256 % VW == 0 && KPT % 4 == 0, "state slice mapping");
+    constexpr int KPT = D * VW / NT;       // keys per thread
+    static_assert(NT % VW == 0 && KPT % 4 == 0, "state slice mapping");
     const int sc = tid % VW, sk0 = (tid / VW) * KPT;
     float st[KPT];
     {
@@ -1855,15 +1869,19 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     // load of every split (four splits a round) is in flight before the
     // first add.
     constexpr int TPR = D / 8;             // threads per q or k row (16 or 8: one DPP row)
-    constexpr int RPP = 256 / TPR;         // rows per pass
+    constexpr int RPP = NT / TPR;          // rows per pass
     constexpr int NP = kMaxRows / RPP;     // passes cover every row slot (rows >= n are zero)
     constexpr int VT = VW / 4;             // threads per v row
-    static_assert(NP * RPP == kMaxRows && (256 / VT) >= kMaxRows, "load mapping");
+    static_assert(NP * RPP == kMaxRows && (NT / VT) >= kMaxRows, "load mapping");
     const bool rows_in = r.qkv_rows != nullptr;   // a prefill block: bf16 rows, a chain
     if (tid < n) ancs[tid] = rows_in ? (tid >= 31 ? 0xffffffffu : ((2u << tid) - 1u)) : r.meta->anc[r.row0 + tid];
     const int qr0 = tid / TPR, qc = (tid % TPR) * 8;
     const int vr = tid / VT, vc = (tid % VT) * 4;
-    const bool vok = vr < n, gok = tid < n;
+    // gates: lane t of the last wave takes node t (its rows of q and k are
+    // padding up to 28 nodes at head size 128, 24 at 64)
+    const int gl = tid - (NT - 64);
+    const bool vok = vr < n, gok = gl >= 0 && gl < n;
+    const uint32_t ganc = !gok ? 0u : rows_in ? (gl >= 31 ? 0xffffffffu : ((2u << gl) - 1u)) : r.meta->anc[r.row0 + gl];
     float qx[NP][8], kx[NP][8], ga = 0.f, gb = 0.f;
     float4 vx = {0.f, 0.f, 0.f, 0.f};
     if (rows_in) {
@@ -1887,8 +1905,8 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
         vx = float4{__uint_as_float(wv.x << 16), __uint_as_float(wv.x & 0xffff0000u),
                     __uint_as_float(wv.y << 16), __uint_as_float(wv.y & 0xffff0000u)};
         if (gok) {
-            ga = bf2f(r.ab_rows[(size_t)(r.row0 + tid) * r.ab_ld + h]);
-            if (DELTA) gb = bf2f(r.ab_rows[(size_t)(r.row0 + tid) * r.ab_ld + QH + h]);
+            ga = bf2f(r.ab_rows[(size_t)(r.row0 + gl) * r.ab_ld + h]);
+            if (DELTA) gb = bf2f(r.ab_rows[(size_t)(r.row0 + gl) * r.ab_ld + QH + h]);
         }
     } else {
         const float *P = r.qkv_part;
@@ -1920,8 +1938,8 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
                 }
                 lv[j] = float4{0.f, 0.f, 0.f, 0.f};
                 if (sj && vok) lv[j] = *reinterpret_cast<const float4 *>(pp(r.row0 + vr, (2 * QH + h) * D + v0 + vc, k0 + j));
-                const float g1 = (sj && gok) ? *pp(r.row0 + tid, r.a_col + h, k0 + j) : 0.f;
-                const float g2 = (DELTA && sj && gok) ? *pp(r.row0 + tid, r.a_col + QH + h, k0 + j) : 0.f;
+                const float g1 = (sj && gok) ? *pp(r.row0 + gl, r.a_col + h, k0 + j) : 0.f;
+                const float g2 = (DELTA && sj && gok) ? *pp(r.row0 + gl, r.a_col + QH + h, k0 + j) : 0.f;
                 if (j == 0) { lga.x = g1; lgb.x = g2; }
                 else if (j == 1) { lga.y = g1; lgb.y = g2; }
                 else if (j == 2) { lga.z = g1; lgb.z = g2; }
@@ -1999,21 +2017,22 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
         vsm[vr][vc + 2] = bfround(vx.z);
         vsm[vr][vc + 3] = bfround(vx.w);
     }
-    if (gok) {
-        gsh[tid] = log_sigmoid(bfround(ga));
-        if constexpr (DELTA) bsh[tid] = 1.0f / (1.0f + expf(-bfround(gb)));
-    }
-    __syncthreads();
-    if (tid < n) {
-        // cumulative gate over the ancestors, root first (ancestors have lower indices)
-        const uint32_t anc = ancs[tid];
-        float gc = 0.f;
+    if (wave == NT / 64 - 1) {
+        // lane t's gate g_t (every lane computes one; lanes >= n are never
+        // added), then the cumulative gate over the ancestors-or-self in
+        // index order, root first (ancestors have lower indices), each g_s
+        // broadcast from lane s; a non-ancestor adds an exact zero
+        const float g = log_sigmoid(bfround(ga));
+        if constexpr (DELTA)
+            if (gok) bsh[gl] = 1.0f / (1.0f + expf(-bfround(gb)));
+        float gc = 0.f;   // stopping at n drops only exact zeros (gc is never -0)
 #pragma unroll
-        for (int s2 = 0; s2 < kMaxRows; ++s2) {   // every read issued; a non-ancestor adds an exact zero
-            const float g = gsh[s2];
-            gc += (s2 <= tid && ((anc >> s2) & 1u)) ? g : 0.f;
+        for (int s2 = 0; s2 < kMaxRows; ++s2) {
+            if (s2 >= n) break;
+            const float gs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), s2));
+            gc += (s2 <= gl && ((ganc >> s2) & 1u)) ? gs : 0.f;
         }
-        gcs[tid] = gc;
+        if (gok) gcs[gl] = gc;
     }
     __syncthreads();
     // the small products, one wave each: lane (hf, j = lane % 32) supplies k
@@ -2072,25 +2091,23 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
             acc = mfma32(ah, b, acc);
             acc = mfma32(al, b, acc);
         }
+        // wave 2 keeps e^{gc_t} S0^T q_t for the read-out; wave 3 (delta)
+        // turns v into the right-hand side b_t (v_t - e^{gc_t} S0^T k_t) in
+        // place (no other wave touches v in this phase)
         const int t = l32;
         if (t < n) {
+            const float eg = expf(gcs[t]), bt = DELTA ? bsh[DELTA ? t : 0] : 0.f;
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
                 const int c = acc_row(rr, hf);
                 if (c >= VW) continue;
-                if (wave == 2) accq[t][c] = acc[rr];
-                else if constexpr (DELTA) acck[t][c] = acc[rr];
+                if (wave == 2) accq[t][c] = eg * acc[rr];
+                else if constexpr (DELTA) vsm[t][c] = bt * (vsm[t][c] - eg * acc[rr]);
             }
         }
     }
     __syncthreads();
     if constexpr (DELTA) {
-        // right-hand side b_t (v_t - e^{gc_t} S0^T k_t), in place of v
-        for (int idx = tid; idx < n * VW; idx += 256) {
-            const int t = idx / VW, c = idx % VW;
-            vsm[t][c] = bsh[t] * (vsm[t][c] - expf(gcs[t]) * acck[t][c]);
-        }
-        __syncthreads();
         // forward substitution, a quad of lanes a value column (the column in registers)
         if (tid < 4 * VW) {
             if (n <= 16) delta_solve<16, VW>(vsm, akq, n, tid >> 2, tid & 3);
@@ -2100,9 +2117,9 @@ __global__ __launch_bounds__(256) void k_recur_tree(RecurArgs r) {
     }
     // read-out o_t = e^{gc_t} S0^T q_t + sum over ancestors-or-self s of
     // coef[t][s] u_s (u = v for the plain recurrence)
-    for (int idx = tid; idx < n * VW; idx += 256) {
+    for (int idx = tid; idx < n * VW; idx += NT) {
         const int t = idx / VW, c = idx % VW;
-        float o = expf(gcs[t]) * accq[t][c];
+        float o = accq[t][c];
         for (int s = 0; s <= t; ++s) o += coef[t][s] * vsm[s][c];
         r.out[(size_t)(r.row0 + t) * QH * D + h * D + v0 + c] = f2bf(o);
         r.save_v[((size_t)t * QH + h) * D + v0 + c] = vsm[t][c];
@@ -2406,7 +2423,7 @@ hipError_t launch_top2_reduce(hipStream_t s, const Top2 *part, int ntiles, int M
 
 hipError_t launch_recur_tree(hipStream_t s, int D, const RecurArgs &a) {
     if (a.n < 1 || a.n > kMaxRows) return hipErrorInvalidValue;
-    const dim3 grid(a.QH, kRecurSlices), block(256);
+    const dim3 grid(a.QH, kRecurSlices), block(recur_threads(D));
     if (D == 128 && a.delta) hipLaunchKernelGGL((k_recur_tree<128, true>), grid, block, 0, s, a);
     else if (D == 128) hipLaunchKernelGGL((k_recur_tree<128, false>), grid, block, 0, s, a);
     else if (D == 64 && a.delta) hipLaunchKernelGGL((k_recur_tree<64, true>), grid, block, 0, s, a);
