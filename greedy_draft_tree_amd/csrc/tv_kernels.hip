@@ -1770,6 +1770,22 @@ __device__ __forceinline__ float quad_bcast(float x, int k) {
     }
 }
 
+// Cumulative gate of lane t's node: the sum of g_s over its ancestors-or-self
+// s (bits of anc) in index order, root first, each g_s broadcast from lane s
+// of the wave; a non-ancestor adds an exact zero.  NN >= n: the slots from n
+// on are non-ancestors, and since the sum starts at +0 and is never -0,
+// dropping them leaves it unchanged.
+template <int NN>
+__device__ __forceinline__ float cum_gate(float g, int t, uint32_t anc) {
+    float gc = 0.f;
+#pragma unroll
+    for (int s = 0; s < NN; ++s) {
+        const float gs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), s));
+        gc += (s <= t && ((anc >> s) & 1u)) ? gs : 0.f;
+    }
+    return gc;
+}
+
 // Forward substitution for value column c of the delta rule's unit
 // lower-triangular system (n <= NN nodes; ancestors have lower indices, so
 // node order is a topological order), by the four lanes of a quad: lane j
@@ -2025,13 +2041,7 @@ __global__ __launch_bounds__(recur_threads(D)) void k_recur_tree(RecurArgs r) {
         const float g = log_sigmoid(bfround(ga));
         if constexpr (DELTA)
             if (gok) bsh[gl] = 1.0f / (1.0f + expf(-bfround(gb)));
-        float gc = 0.f;   // stopping at n drops only exact zeros (gc is never -0)
-#pragma unroll
-        for (int s2 = 0; s2 < kMaxRows; ++s2) {
-            if (s2 >= n) break;
-            const float gs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), s2));
-            gc += (s2 <= gl && ((ganc >> s2) & 1u)) ? gs : 0.f;
-        }
+        const float gc = n <= 16 ? cum_gate<16>(g, gl, ganc) : cum_gate<kMaxRows>(g, gl, ganc);
         if (gok) gcs[gl] = gc;
     }
     __syncthreads();
