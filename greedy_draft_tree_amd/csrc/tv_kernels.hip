@@ -1771,17 +1771,18 @@ __device__ __forceinline__ float quad_bcast(float x, int k) {
 }
 
 // Cumulative gate of lane t's node: the sum of g_s over its ancestors-or-self
-// s (bits of anc) in index order, root first, each g_s broadcast from lane s
-// of the wave; a non-ancestor adds an exact zero.  NN >= n: the slots from n
-// on are non-ancestors, and since the sum starts at +0 and is never -0,
-// dropping them leaves it unchanged.
+// s (bits of anc; ancestors have lower indices, so no bit lies above t) in
+// index order, root first, each g_s broadcast from lane s of the wave; a
+// non-ancestor adds an exact zero.  NN >= n: the slots from n on are
+// non-ancestors, and since the sum starts at +0 and is never -0, dropping
+// them leaves it unchanged.
 template <int NN>
-__device__ __forceinline__ float cum_gate(float g, int t, uint32_t anc) {
+__device__ __forceinline__ float cum_gate(float g, uint32_t anc) {
     float gc = 0.f;
 #pragma unroll
     for (int s = 0; s < NN; ++s) {
         const float gs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), s));
-        gc += (s <= t && ((anc >> s) & 1u)) ? gs : 0.f;
+        gc += ((anc >> s) & 1u) ? gs : 0.f;
     }
     return gc;
 }
@@ -2033,33 +2034,54 @@ __global__ __launch_bounds__(recur_threads(D)) void k_recur_tree(RecurArgs r) {
         vsm[vr][vc + 2] = bfround(vx.z);
         vsm[vr][vc + 3] = bfround(vx.w);
     }
+    float gate_g = 0.f;   // the gate wave's lane t: g_t, summed over ancestors after the barrier
     if (wave == NT / 64 - 1) {
         // lane t's gate g_t (every lane computes one; lanes >= n are never
-        // added), then the cumulative gate over the ancestors-or-self in
-        // index order, root first (ancestors have lower indices), each g_s
-        // broadcast from lane s; a non-ancestor adds an exact zero
-        const float g = log_sigmoid(bfround(ga));
+        // added) and, for a delta layer, its write strength b_t
+        gate_g = log_sigmoid(bfround(ga));
         if constexpr (DELTA)
             if (gok) bsh[gl] = 1.0f / (1.0f + expf(-bfround(gb)));
-        const float gc = n <= 16 ? cum_gate<16>(g, gl, ganc) : cum_gate<kMaxRows>(g, gl, ganc);
-        if (gok) gcs[gl] = gc;
     }
     __syncthreads();
     // the small products, one wave each: lane (hf, j = lane % 32) supplies k
     // slots 16*kk + 8*hf + 0..7 of A row j and of B column j; accumulator r
-    // holds row acc_row(r, hf) of column j
+    // holds row acc_row(r, hf) of column j.  Their MFMA chains run while the
+    // gate wave forms the cumulative gates, which the epilogues read after a
+    // barrier.
     const uint4 z = {0u, 0u, 0u, 0u};
-    if (wave == 0 || (DELTA && wave == 1)) {
-        // coef (wave 0): e^{gc_t - gc_s} (q_t . k_s) over ancestors-or-self s;
-        // akq (wave 1, by solver lane): b_t e^{gc_t - gc_s} (k_t . k_s) over strict ancestors
+    const bool pw_qk = wave == 0 || (DELTA && wave == 1);   // Q K^T (coef) and K K^T (akq)
+    const bool pw_s0 = wave == 2 || (DELTA && wave == 3);   // S0^T Q and S0^T K
+    if (wave == NT / 64 - 1) {
+        // the cumulative gate over the ancestors-or-self in index order, root
+        // first (ancestors have lower indices)
+        const float gc = n <= 16 ? cum_gate<16>(gate_g, ganc) : cum_gate<kMaxRows>(gate_g, ganc);
+        if (gok) gcs[gl] = gc;
+    }
+    f32x16 acc = {};
+    if (pw_qk) {
         const uint16_t(*A)[BP] = wave == 0 ? qb : kb;
-        f32x16 acc = {};
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) {
             const uint4 a = *reinterpret_cast<const uint4 *>(&A[l32][16 * kk + 8 * hf]);
             const uint4 b = *reinterpret_cast<const uint4 *>(&kb[l32][16 * kk + 8 * hf]);
             acc = mfma32(a, b, acc);
         }
+    } else if (pw_s0) {
+        // A row = value column (S0 transposed), B column = node
+        const uint16_t(*B)[BP] = wave == 2 ? qb : kb;
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+            const uint4 b = *reinterpret_cast<const uint4 *>(&B[l32][16 * kk + 8 * hf]);
+            const uint4 ah = l32 < VW ? *reinterpret_cast<const uint4 *>(&s0h[l32][16 * kk + 8 * hf]) : z;
+            const uint4 al = l32 < VW ? *reinterpret_cast<const uint4 *>(&s0l[l32][16 * kk + 8 * hf]) : z;
+            acc = mfma32(ah, b, acc);
+            acc = mfma32(al, b, acc);
+        }
+    }
+    __syncthreads();
+    if (pw_qk) {
+        // coef (wave 0): e^{gc_t - gc_s} (q_t . k_s) over ancestors-or-self s;
+        // akq (wave 1, by solver lane): b_t e^{gc_t - gc_s} (k_t . k_s) over strict ancestors
         const int s = l32;
         if (s < n) {
             const int rrn = n <= 16 ? 8 : 16;   // accumulators rr >= 8 hold nodes >= 16
@@ -2088,19 +2110,7 @@ __global__ __launch_bounds__(recur_threads(D)) void k_recur_tree(RecurArgs r) {
                 }
             }
         }
-    } else if (wave == 2 || (DELTA && wave == 3)) {
-        // S0^T q_t (wave 2) and S0^T k_t (wave 3) for this slice's columns:
-        // A row = value column (S0 transposed), B column = node
-        const uint16_t(*B)[BP] = wave == 2 ? qb : kb;
-        f32x16 acc = {};
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk) {
-            const uint4 b = *reinterpret_cast<const uint4 *>(&B[l32][16 * kk + 8 * hf]);
-            const uint4 ah = l32 < VW ? *reinterpret_cast<const uint4 *>(&s0h[l32][16 * kk + 8 * hf]) : z;
-            const uint4 al = l32 < VW ? *reinterpret_cast<const uint4 *>(&s0l[l32][16 * kk + 8 * hf]) : z;
-            acc = mfma32(ah, b, acc);
-            acc = mfma32(al, b, acc);
-        }
+    } else if (pw_s0) {
         // wave 2 keeps e^{gc_t} S0^T q_t for the read-out; wave 3 (delta)
         // turns v into the right-hand side b_t (v_t - e^{gc_t} S0^T k_t) in
         // place (no other wave touches v in this phase)
