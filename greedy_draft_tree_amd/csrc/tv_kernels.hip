@@ -617,11 +617,22 @@ __global__ __launch_bounds__(256) void k_gemm_dense(GemmArgs g) {
         __syncthreads();
     }
     if (!tok) return;
-    // epilogue: accumulators r = 4j..4j+3 hold 4 consecutive output columns
+    // epilogue: accumulators r = 4j..4j+3 hold 4 consecutive output columns;
+    // a residual epilogue reads the row group's old values before its first
+    // store (else each load waits for the store before it)
 #pragma unroll
     for (int gi = 0; gi < MG; ++gi) {
         const int m = m0 + gi * 32 + c;
         if (m >= g.M) continue;
+        uint16_t yold[EPI == EPI_RESID ? 4 : 1][4];
+        if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n0 = tile * 32 + 8 * j + 4 * hf;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) yold[j][e] = n0 + e < N ? g.Y[(size_t)m * g.ldy + n0 + e] : (uint16_t)0;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int n0 = tile * 32 + 8 * j + 4 * hf;
@@ -645,7 +656,7 @@ __global__ __launch_bounds__(256) void k_gemm_dense(GemmArgs g) {
                     if constexpr (EPI == EPI_BF16) {
                         o[e] = f2bf(v[e]);
                     } else if constexpr (EPI == EPI_RESID) {
-                        o[e] = f2bf(bf2f(y[e]) + bfround(v[e]));
+                        o[e] = f2bf(bf2f(yold[j][e]) + bfround(v[e]));
                     } else {
                         const float gt = bfround(v[e]), up = bfround(v2[e]);
                         o[e] = f2bf(gt / (1.0f + expf(-gt)) * up);
@@ -808,11 +819,24 @@ __device__ __forceinline__ void gemm_big(const GemmArgs &g) {
     wait_loads(std::integral_constant<int, 0>{});
 
     // epilogue: accumulators r = 4jj..4jj+3 of tile (j, rg) hold 4
-    // consecutive output columns of activation row m
+    // consecutive output columns of activation row m.  A residual epilogue
+    // reads the row group's old values before its first store (in program
+    // order a store could alias the next load, so the compiler would wait
+    // out each load in turn)
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
         const int m = m0 + (RG * wm + rg) * 32 + c;
         if (m >= M) continue;
+        uint2 oldv[DUAL ? 1 : 2][4];
+        if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int tile = 8 * nb + 2 * wn + j;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    oldv[j][jj] = *reinterpret_cast<const uint2 *>(g.Y + (size_t)m * g.ldy + tile * 32 + 8 * jj + 4 * hf);
+            }
+        }
 #pragma unroll
         for (int j = 0; j < (DUAL ? 1 : 2); ++j) {
             const int tile = DUAL ? 4 * nb + wn : 8 * nb + 2 * wn + j;
@@ -831,7 +855,7 @@ __device__ __forceinline__ void gemm_big(const GemmArgs &g) {
                     uint16_t *y = g.Y + (size_t)m * g.ldy + n0;
                     uint16_t o[4];
                     if constexpr (EPI == EPI_RESID) {
-                        const uint2 old = *reinterpret_cast<const uint2 *>(y);
+                        const uint2 old = oldv[DUAL ? 0 : j][jj];
                         const uint16_t yo[4] = {(uint16_t)(old.x & 0xffffu), (uint16_t)(old.x >> 16),
                                                 (uint16_t)(old.y & 0xffffu), (uint16_t)(old.y >> 16)};
 #pragma unroll
@@ -2323,9 +2347,12 @@ hipError_t launch_gemm_dense(hipStream_t s, int epi, const GemmArgs &a) {
     const int rem = (nblk * mt) % 256 ? ((nblk * mt) % 256 + mt - 1) / mt : 0;   // blocks of the partial round
     if (!whole) return launch_gemm_groups(s, epi, a);
     if ((nblk - rem) * mt < 256) {
-        // too few 256-row tiles for a round: 128-row tiles when they fill
-        // the CUs (the 32-row-group kernel is faster below that)
-        if (nblk * ((a.M + 127) / 128) >= 256) return launch_gemm_big(s, epi, a, nblk, 128);
+        // too few 256-row tiles for a round: 128-row tiles when they cover
+        // at least half the CUs, else 64-row tiles on the same terms (at
+        // 512-1024 rows of the 5120-wide layer's QKV, O and down shapes 10-20 %
+        // faster than the 32-row-group kernel, which stays below that)
+        if (nblk * ((a.M + 127) / 128) >= 128) return launch_gemm_big(s, epi, a, nblk, 128);
+        if (nblk * ((a.M + 63) / 64) >= 128) return launch_gemm_big(s, epi, a, nblk, 64);
         return launch_gemm_groups(s, epi, a);
     }
     hipError_t e = launch_gemm_big(s, epi, a, nblk - rem, kBigTile);

@@ -190,7 +190,8 @@ def test_head_rows_bitwise_invariant(tv, head):
 # ------------------------------------------------------------ dense (prefill) GEMM
 
 @pytest.mark.parametrize("M,N,K", [(33, 512, 256), (130, 1056, 1024), (300, 5120, 5120), (97, 17408, 512),
-                                   (1000, 17408, 512)])   # 256 x 256 tiles, a ragged last row tile
+                                   (1000, 17408, 512),    # 256 x 256 tiles, a ragged last row tile
+                                   (500, 5120, 1280)])    # 64-row tiles, a ragged last row tile
 def test_dense_linear_fp32_and_bf16(tv, M, N, K):
     """More than 32 rows run the dense kernel: fp32 sums within Higham's
     bound, bf16 outputs correctly rounded up to that bound."""
@@ -214,13 +215,15 @@ def test_dense_linear_fp32_and_bf16(tv, M, N, K):
     assert torch.equal(yb, y.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("N,K,R", [(2048, 1024, 300), (17408, 512, 512), (17408, 1280, 1024), (7168, 1280, 2048)])
+@pytest.mark.parametrize("N,K,R", [(2048, 1024, 300), (17408, 512, 512), (17408, 1280, 1024), (7168, 1280, 2048),
+                                   (7168, 1280, 1024), (5120, 1280, 768), (5120, 1280, 512)])
 def test_dense_linear_rows_bitwise_invariant(tv, N, K, R):
     """A row's dense result does not depend on the row count, its slot, or
     the tile shape the row count selects (at 17408 columns 512 rows take 4
     row groups per workgroup, fewer rows take 2; 1024 rows take the 256 x
-    256 tiles with the last weight blocks on 64-row tiles, 2048 rows at 7168
-    columns 128-row tiles, and the subsets below the 32-row-group kernel)."""
+    256 tiles with the last weight blocks on 64-row tiles; 128-row tiles at
+    7168 columns for 1024 and 2048 rows, 64-row tiles at 5120 columns for 512
+    and 768 rows; the subsets below on the 32-row-group kernel)."""
     x, w = _operands(R, N, K, 7)
     tv.pack_weight(w)
     full = torch.empty(R, N, dtype=torch.float32, device="cuda")
