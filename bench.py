@@ -545,7 +545,7 @@ def prefill_main(a, shape):
         "chained_prefill_tokens_per_s": round(n / chain_s, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(achieved / 2500.0, 4), "traffic": None,
-                     "kernel": "pf_gemm_gateup (SwiGLU: k_gemm_big when its tiles fill the CUs, else k_gemm_dense<EPI_SWIGLU, 2>)", "avg_us": round(k_avg_ms * 1e3, 2),
+                     "kernel": "pf_gemm_gateup (SwiGLU: k_gemm_big when its tiles cover at least half the CUs, else k_gemm_dense<EPI_SWIGLU, 2>)", "avg_us": round(k_avg_ms * 1e3, 2),
                      "launches": k_cnt},
     }
     if kernels:
