@@ -2164,7 +2164,16 @@ __global__ __launch_bounds__(recur_threads(D)) void k_recur_tree(RecurArgs r) {
     for (int idx = tid; idx < n * VW; idx += NT) {
         const int t = idx / VW, c = idx % VW;
         float o = accq[t][c];
-        for (int s = 0; s <= t; ++s) o += coef[t][s] * vsm[s][c];
+        int s = 0;
+        for (; s + 3 <= t; s += 4) {   // four terms' reads in flight, then their adds in order
+            const float c0 = coef[t][s], c1 = coef[t][s + 1], c2 = coef[t][s + 2], c3 = coef[t][s + 3];
+            const float u0 = vsm[s][c], u1 = vsm[s + 1][c], u2 = vsm[s + 2][c], u3 = vsm[s + 3][c];
+            o += c0 * u0;
+            o += c1 * u1;
+            o += c2 * u2;
+            o += c3 * u3;
+        }
+        for (; s <= t; ++s) o += coef[t][s] * vsm[s][c];
         r.out[(size_t)(r.row0 + t) * QH * D + h * D + v0 + c] = f2bf(o);
         r.save_v[((size_t)t * QH + h) * D + v0 + c] = vsm[t][c];
     }
