@@ -1906,9 +1906,9 @@ __global__ __launch_bounds__(recur_threads(D)) void k_recur_tree(RecurArgs r) {
     // a prefill block, bf16 rows), rounded to bf16 (the projection's output
     // rounding).  Each thread takes eight consecutive columns of q and of k
     // for rows qr0, qr0 + RPP, ... (TPR threads a row), four of this slice's
-    // v columns for row vr, and a node's gate (and write strength): every
-    // load of every split (four splits a round) is in flight before the
-    // first add.
+    // v columns for row vr, and lane t of the last wave node t's gate (and
+    // write strength): every load of every split (four splits a round) is
+    // in flight before the first add.
     constexpr int TPR = D / 8;             // threads per q or k row (16 or 8: one DPP row)
     constexpr int RPP = NT / TPR;          // rows per pass
     constexpr int NP = kMaxRows / RPP;     // passes cover every row slot (rows >= n are zero)
